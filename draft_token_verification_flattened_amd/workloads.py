@@ -1,0 +1,239 @@
+"""Seeded synthetic inputs for the speculative verification path.
+
+This module only draws random numbers and lays them out. It holds none of the
+method's arithmetic: no softmax, no acceptance test, no schedule. Both the HIP
+path (through the tests and bench.py) and the CPU oracle (through the tests)
+consume what it returns; neither imports the other.
+
+Five workloads are defined, sized after the DSpark pages' serving setting
+(maximum draft length 5; a Qwen3-like vocabulary of 151936 entries; math, code
+and chat traffic with decreasing acceptance). The pages measure on public
+math/code/chat suites; those are not used here. The three "domain" profiles of
+the saturated workload stand in for them, keeping the pages' ordering of
+accepted length (math > code > chat).
+
+Every array comes from numpy's Philox bit generator keyed by the workload seed,
+drawn in the order written below, so a workload is reproducible bit for bit on
+any host. bf16 arrays are the round-to-nearest-even encoding of fp32 samples and
+are stored as their uint16 bit patterns.
+
+Random numbers the method itself consumes (the acceptance uniforms, the
+resampling uniform, the Markov head's sampling uniforms) are drawn here as
+inputs, float32 values k * 2**-24 in [0, 1).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["CONFIGS", "Workload", "make", "f32_to_bf16_bits", "bf16_bits_to_f32",
+           "step_time_table"]
+
+
+# ---------------------------------------------------------------------------
+# encoding helpers (storage only)
+# ---------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 samples to bfloat16 (nearest, ties to even); uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# workload definitions
+# ---------------------------------------------------------------------------
+
+def _table(points, step_time):
+    b = np.asarray(points, dtype=np.int32)
+    thr = np.array([float(p) / float(step_time(float(p))) for p in points], dtype=np.float64)
+    return b, thr
+
+
+def step_time_table(name: str):
+    """Engine throughput table (batch tokens B_j, tokens per unit time thr_j)."""
+    if name == "c0":       # concave: step time 1 + 0.08 B
+        return _table([4 * j for j in range(1, 9)], lambda b: 1.0 + 0.08 * b)
+    if name == "c1":       # flat step time up to 512 tokens
+        return _table([64 * j for j in range(1, 9)], lambda b: 1.0)
+    if name == "c2":       # soft knee at 256 tokens
+        pts = [32, 64, 128, 192, 256, 384, 512, 768, 1024, 1280, 1536, 2048]
+        return _table(pts, lambda b: 1.0 if b <= 256 else 1.0 + 0.5 * (b - 256) / 256)
+    if name == "c3":       # 16 points up to 4096 tokens
+        return _table([256 * j for j in range(1, 17)], lambda b: 1.0 + b / 1024.0)
+    if name == "c4":
+        pts = [128, 256, 512, 768, 1024, 1536, 2048, 2560, 3072]
+        return _table(pts, lambda b: 1.0 if b <= 1024 else 1.0 + 0.5 * (b - 1024) / 1024)
+    raise KeyError(name)
+
+
+CONFIGS = {
+    "c0": dict(name="c0", desc="tiny CPU-checkable step: R=4, k=5, V=32, fp32, Markov head rank 4",
+               seed=0, R=4, k=5, V=32, dtype="f32", markov=True, d_m=4, tau=1.0,
+               modes=("greedy", "sample")),
+    "c1": dict(name="c1", desc="light load: R=64, k=5, V=151936, bf16, flat step time to 512 tokens",
+               seed=1, R=64, k=5, V=151936, dtype="bf16", markov=False, tau=1.0,
+               modes=("greedy", "sample")),
+    "c2": dict(name="c2", desc="saturated load: R=256, k=5, V=151936, bf16, knee at 256 batch tokens, "
+                                "math/code/chat profiles",
+               seed=2, R=256, k=5, V=151936, dtype="bf16", markov=False, tau=1.0,
+               modes=("greedy", "sample")),
+    "c3": dict(name="c3", desc="long parallel blocks: R=128, k=16, V=129280, bf16, suffix decay, tau=0.7",
+               seed=3, R=128, k=16, V=129280, dtype="bf16", markov=False, tau=0.7,
+               modes=("sample",)),
+    "c4": dict(name="c4", desc="full semi-autoregressive step: R=512, k=5, V=151936, d_m=256, bf16",
+               seed=7, R=512, k=5, V=151936, dtype="bf16", markov=True, d_m=256, tau=1.0,
+               modes=("sample",)),
+}
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    R: int
+    k: int
+    V: int
+    dtype: str                      # "bf16" (uint16 bit arrays) or "f32"
+    tau: float
+    conf_logit: np.ndarray          # f32 [R,k]   raw confidence-head logits z
+    pos_temp: np.ndarray            # f32 [k]     per-position temperatures
+    tbl_tokens: np.ndarray          # i32 [n]
+    tbl_thr: np.ndarray             # f64 [n]
+    target: np.ndarray              # [R,k+1,V]
+    u_verify: np.ndarray            # f32 [R,k+1]  j<k: acceptance; k: resample
+    draft: Optional[np.ndarray] = None          # [R,k,V]  (absent for Markov workloads)
+    tokens_sample: Optional[np.ndarray] = None  # i32 [R,k] drafts drawn from q at tau
+    tokens_greedy: Optional[np.ndarray] = None  # i32 [R,k] argmax of the draft logits
+    backbone: Optional[np.ndarray] = None       # [R,k,V]   parallel backbone logits
+    emb: Optional[np.ndarray] = None            # [V,d_m]   previous-token embedding
+    proj: Optional[np.ndarray] = None           # [V,d_m]   projection, one d_m row per vocab entry
+    prev_token: Optional[np.ndarray] = None     # i32 [R]
+    u_draft: Optional[np.ndarray] = None        # f32 [R,k]
+    d_m: int = 0
+
+
+def _enc(x32: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x32)
+    return np.ascontiguousarray(x32, dtype=np.float32)
+
+
+def _dec(x: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits_to_f32(x) if dtype == "bf16" else x
+
+
+def _sample_rows(g: np.random.Generator, logits32: np.ndarray, tau: float) -> np.ndarray:
+    """Draw one index per row with probability proportional to exp(logit / tau).
+
+    Gumbel-max: argmax(logit / tau + G), G standard Gumbel. Rows are processed
+    in blocks to bound memory.
+    """
+    rows = logits32.reshape(-1, logits32.shape[-1])
+    out = np.empty(rows.shape[0], dtype=np.int32)
+    inv_tau = np.float32(1.0 / tau)
+    blk = max(1, (1 << 24) // rows.shape[1])
+    for s in range(0, rows.shape[0], blk):
+        e = min(rows.shape[0], s + blk)
+        u = g.random((e - s, rows.shape[1]), dtype=np.float64)
+        gum = -np.log(-np.log(np.maximum(u, 1e-300)))
+        out[s:e] = np.argmax(rows[s:e].astype(np.float64) * float(inv_tau) + gum, axis=1)
+    return out.reshape(logits32.shape[:-1])
+
+
+def _uniform24(g: np.random.Generator, shape) -> np.ndarray:
+    # float32 multiples of 2**-24 in [0, 1)
+    return (g.integers(0, 1 << 24, size=shape, dtype=np.int64).astype(np.float64) * 2.0 ** -24).astype(np.float32)
+
+
+def make(name: str, *, R: Optional[int] = None, V: Optional[int] = None) -> Workload:
+    """Build workload `name` ("c0".."c4"). R and V may be shrunk for quick tests;
+    the recipe is otherwise unchanged."""
+    cfg = dict(CONFIGS[name])
+    if R is not None:
+        cfg["R"] = R
+    if V is not None:
+        cfg["V"] = V
+    R_, k, V_, dt, tau = cfg["R"], cfg["k"], cfg["V"], cfg["dtype"], cfg["tau"]
+    g = np.random.Generator(np.random.Philox(cfg["seed"]))
+    tbl_b, tbl_thr = step_time_table(name)
+    pos_temp = np.linspace(1.0, 2.0, k).astype(np.float32)
+    w = dict(name=name, R=R_, k=k, V=V_, dtype=dt, tau=tau, tbl_tokens=tbl_b, tbl_thr=tbl_thr,
+             pos_temp=pos_temp)
+
+    if name == "c0":
+        tl32 = (2.0 * g.standard_normal((R_, k + 1, V_), dtype=np.float32)).astype(np.float32)
+        bk32 = (tl32[:, :k] + g.standard_normal((R_, k, V_), dtype=np.float32)).astype(np.float32)
+        sd = np.float32(np.sqrt(0.1))        # N(0, 0.1): variance 0.1
+        emb = (sd * g.standard_normal((V_, cfg["d_m"]), dtype=np.float32)).astype(np.float32)
+        proj = (sd * g.standard_normal((V_, cfg["d_m"]), dtype=np.float32)).astype(np.float32)
+        prev = g.integers(0, V_, size=R_, dtype=np.int64).astype(np.int32)
+        z = (1.0 + g.standard_normal((R_, k), dtype=np.float32)).astype(np.float32)
+        w.update(target=_enc(tl32, dt), backbone=_enc(bk32, dt), emb=emb, proj=proj,
+                 prev_token=prev, conf_logit=z, d_m=cfg["d_m"])
+    elif name in ("c1", "c2"):
+        tl32 = (3.0 * g.standard_normal((R_, k + 1, V_), dtype=np.float32)).astype(np.float32)
+        target = _enc(tl32, dt)
+        d32 = tl32[:, :k] + np.float32(1.5) * g.standard_normal((R_, k, V_), dtype=np.float32)
+        del tl32
+        draft = _enc(d32, dt)
+        del d32
+        dd = _dec(draft, dt)
+        tok_g = np.argmax(dd, axis=-1).astype(np.int32)
+        tok_s = _sample_rows(g, dd, tau)
+        del dd
+        if name == "c1":
+            m = 0.9 * 0.85 ** np.arange(k)
+            m = np.broadcast_to(m, (R_, k))
+        else:
+            # math / code / chat thirds of the requests
+            dom = np.minimum((np.arange(R_) * 3) // max(R_, 1), 2)
+            means = np.array([0.92, 0.88, 0.75])[dom]
+            m = np.broadcast_to(means[:, None], (R_, k))
+        raw = g.beta(20.0 * m, 20.0 * (1.0 - m))
+        raw = np.clip(raw, 1e-12, 1.0 - 1e-12)
+        z = np.log(raw / (1.0 - raw)).astype(np.float32)
+        w.update(target=target, draft=draft, tokens_greedy=tok_g, tokens_sample=tok_s, conf_logit=z)
+    elif name == "c3":
+        tl32 = (3.0 * g.standard_normal((R_, k + 1, V_), dtype=np.float32)).astype(np.float32)
+        target = _enc(tl32, dt)
+        sig = (0.5 + 3.5 * np.arange(k) / (k - 1)).astype(np.float32)
+        d32 = tl32[:, :k] + sig[None, :, None] * g.standard_normal((R_, k, V_), dtype=np.float32)
+        del tl32
+        draft = _enc(d32, dt)
+        del d32
+        dd = _dec(draft, dt)
+        tok_s = _sample_rows(g, dd, tau)
+        tok_g = np.argmax(dd, axis=-1).astype(np.int32)
+        del dd
+        mu = np.linspace(1.5, -2.5, k)
+        z = (mu[None, :] + 0.5 * g.standard_normal((R_, k))).astype(np.float32)
+        w.update(target=target, draft=draft, tokens_greedy=tok_g, tokens_sample=tok_s, conf_logit=z)
+    elif name == "c4":
+        d_m = cfg["d_m"]
+        tl32 = (3.0 * g.standard_normal((R_, k + 1, V_), dtype=np.float32)).astype(np.float32)
+        target = _enc(tl32, dt)
+        bk32 = tl32[:, :k] + np.float32(1.5) * g.standard_normal((R_, k, V_), dtype=np.float32)
+        del tl32
+        backbone = _enc(bk32, dt)
+        del bk32
+        emb = _enc(g.standard_normal((V_, d_m), dtype=np.float32), dt)
+        proj = _enc(np.float32(0.5 / 16) * g.standard_normal((V_, d_m), dtype=np.float32), dt)
+        prev = g.integers(0, V_, size=R_, dtype=np.int64).astype(np.int32)
+        z = (1.0 + g.standard_normal((R_, k), dtype=np.float32)).astype(np.float32)
+        w.update(target=target, backbone=backbone, emb=emb, proj=proj, prev_token=prev,
+                 conf_logit=z, d_m=d_m)
+    else:
+        raise KeyError(name)
+
+    w["u_verify"] = _uniform24(g, (R_, k + 1))
+    w["u_draft"] = _uniform24(g, (R_, k))
+    return Workload(**w)
+

@@ -1,0 +1,209 @@
+"""The acceptance rule over a flattened varlen batch, float64.
+
+TEST INFRASTRUCTURE (see the package docstring).
+
+Every selected draft token of every request is one element of a single batch;
+a tag (request id, position) per element carries the in-sequence dependency
+([P1] engineering table, row "内核利用率暴跌": all tokens are flattened into
+independent elements and a tag tensor passes the dependencies). For request r
+with scheduled length L_r the batch holds rows (r, 0) .. (r, L_r); rows j < L_r
+verify draft token x_j, row L_r only supplies the bonus token.
+
+Per verified row (the rule itself is oracle.rule):
+  greedy    g = first argmax of the target logits; keep iff g == x_j.
+  sampling  p = softmax(target / tau), q = softmax(draft / tau);
+            keep iff u[r, j] < min(1, p(x_j) / q(x_j)).
+Per request: a_r = first j < L_r not kept, else L_r ([P2] section 一: resample
+after the first divergence). Emitted: x_0 .. x_{a_r - 1}, then
+  greedy    the target argmax of row a_r;
+  sampling  a draw with u[r, k] from max(0, p - q) at row a_r when a_r < L_r
+            (from p when that residual has no mass), else from p of row L_r.
+
+The scalar definition in oracle.rule and this vectorised form must agree
+element for element on the same uniforms (tests/test_oracle_verify.py); the
+vectorisation runs over requests, one position at a time, with no other
+reordering. Pins: agreement with oracle.rule; a chi-square test on 10**7
+seeded trials that emitted tokens follow the target distribution; negative
+controls that a planted mistake fails it.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import numerics
+
+
+def _first_false(acc: np.ndarray, L: np.ndarray) -> np.ndarray:
+    """a_r = smallest j < L_r with acc[r, j] False, else L_r."""
+    R, k = acc.shape
+    a = np.array(L, dtype=np.int64, copy=True)
+    for j in range(k - 1, -1, -1):
+        rej = (~acc[:, j]) & (j < L)
+        a = np.where(rej, j, a)
+    return a
+
+
+def decide(px: np.ndarray, qx: np.ndarray, u_acc: np.ndarray, L: np.ndarray):
+    """Keep flags and accepted lengths from p(x_j), q(x_j) [R,k] and uniforms.
+
+    keep probability = min(1, p/q), 1 where q == 0; keep iff u < that.
+    Entries j >= L_r are ignored (False).
+    """
+    px = np.asarray(px, dtype=np.float64)
+    qx = np.asarray(qx, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(qx > 0, px / np.where(qx > 0, qx, 1.0), np.inf)
+    keep = np.minimum(1.0, ratio)
+    acc = np.asarray(u_acc, dtype=np.float64) < keep
+    k = px.shape[1]
+    acc &= np.arange(k)[None, :] < np.asarray(L)[:, None]
+    return acc, _first_false(acc, np.asarray(L)), ratio
+
+
+def draw_rows(w: np.ndarray, u: np.ndarray):
+    """Inverse-CDF draw per row of weights w [n,V] with uniforms u [n].
+
+    Returns (index [n], margin [n]) where margin is the distance of t = u * W to
+    the nearest CDF boundary, divided by W: how far the draw is from flipping.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    c = np.cumsum(w, axis=1)
+    W = c[:, -1]
+    t = np.asarray(u, dtype=np.float64) * W
+    above = c > t[:, None]
+    y = np.argmax(above, axis=1)
+    none = ~above.any(axis=1)
+    if none.any():
+        for i in np.nonzero(none)[0]:
+            y[i] = np.nonzero(w[i] > 0)[0][-1]
+    n = w.shape[0]
+    hi = c[np.arange(n), y]
+    lo = np.where(y > 0, c[np.arange(n), np.maximum(y - 1, 0)], 0.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        margin = np.minimum(np.abs(hi - t), np.abs(t - lo)) / W
+    return y.astype(np.int64), margin
+
+
+def residual_rows(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """max(0, p - q) per row; p itself for rows where that has no mass."""
+    w = np.maximum(p - q, 0.0)
+    empty = ~(w.sum(axis=1) > 0)
+    w[empty] = p[empty]
+    return w
+
+
+def verify_probs(P: np.ndarray, Qd: np.ndarray, x: np.ndarray, L: np.ndarray, u: np.ndarray):
+    """Sampling-mode rule on explicit distributions.
+
+    P [R,k+1,V] target distributions, Qd [R,k,V] draft distributions, x [R,k]
+    draft tokens, L [R] lengths, u [R,k+1] uniforms (j < k keep, k resample).
+    Returns (a [R], out [R,k+1] padded with -1).
+    """
+    R, k1, V = P.shape
+    k = k1 - 1
+    rr = np.arange(R)[:, None]
+    jj = np.arange(k)[None, :]
+    px = P[rr, jj, x]
+    qx = Qd[rr, jj, x]
+    _, a, _ = decide(px, qx, u[:, :k], L)
+    pa = P[np.arange(R), a]
+    qa = Qd[np.arange(R), np.minimum(a, k - 1)]
+    w = np.where((a < L)[:, None], residual_rows(pa, qa), pa)
+    y, _ = draw_rows(w, u[:, k])
+    return a, _emit(a, x, y, k)
+
+
+def _emit(a, x, y, k):
+    R = len(a)
+    out = np.full((R, k + 1), -1, dtype=np.int64)
+    for j in range(k):
+        out[:, j] = np.where(j < a, x[:, j], out[:, j])
+    out[np.arange(R), a] = y
+    return out
+
+
+def lengths_from_cu(cu_rows: np.ndarray) -> np.ndarray:
+    cu = np.asarray(cu_rows, dtype=np.int64)
+    return cu[1:] - cu[:-1] - 1
+
+
+def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
+           tags: np.ndarray, cu_rows: np.ndarray, tau: float, u_verify: np.ndarray,
+           block_rows: int = 64) -> dict:
+    """Verify a flattened batch. Shapes: target [R,k+1,V], draft [R,k,V] (sampling
+    only), tokens [R,k], tags [B,2], cu_rows [R+1], u_verify [R,k+1].
+
+    Returns a dict with accepted_len [R], out_tokens [R,k+1] (-1 after the last
+    emitted token) and per-row and per-request diagnostics for parity tests.
+    """
+    R, k1, V = target.shape
+    k = k1 - 1
+    L = lengths_from_cu(cu_rows)
+    tags = np.asarray(tags, dtype=np.int64)
+    B = int(cu_rows[-1])
+    assert tags.shape[0] >= B
+    x = np.asarray(tokens, dtype=np.int64)
+    res = dict(L=L)
+
+    if mode == "greedy":
+        g_row = np.zeros(B, dtype=np.int64)
+        for s in range(0, B, block_rows):
+            e = min(B, s + block_rows)
+            rows = numerics.decode(target[tags[s:e, 0], tags[s:e, 1]], dtype)
+            g_row[s:e] = numerics.argmax_first(rows)
+        g = np.full((R, k + 1), -1, dtype=np.int64)
+        g[tags[:B, 0], tags[:B, 1]] = g_row
+        acc = np.zeros((R, k), dtype=bool)
+        for j in range(k):
+            acc[:, j] = (j < L) & (g[:, j] == x[:, j])
+        a = _first_false(acc, L)
+        y = g[np.arange(R), a]
+        res.update(accepted_len=a, out_tokens=_emit(a, x, y, k), row_argmax=g_row,
+                   accept=acc)
+        return res
+
+    if mode != "sample":
+        raise ValueError(mode)
+    px = np.zeros((R, k), dtype=np.float64)
+    qx = np.ones((R, k), dtype=np.float64)
+    row_p = np.full(B, np.nan)
+    row_q = np.full(B, np.nan)
+    ver = tags[:B, 1] < L[tags[:B, 0]]
+    vidx = np.nonzero(ver)[0]
+    for s in range(0, len(vidx), block_rows):
+        t = vidx[s:s + block_rows]
+        r, j = tags[t, 0], tags[t, 1]
+        xt = x[r, j]
+        p = numerics.softmax(numerics.decode(target[r, j], dtype), tau)
+        q = numerics.softmax(numerics.decode(draft[r, j], dtype), tau)
+        n = np.arange(len(t))
+        px[r, j] = p[n, xt]
+        qx[r, j] = q[n, xt]
+        row_p[t] = p[n, xt]
+        row_q[t] = q[n, xt]
+    acc, a, ratio = decide(px, qx, u_verify[:, :k], L)
+    # resample / bonus rows, recomputed one block at a time
+    y = np.zeros(R, dtype=np.int64)
+    margin = np.zeros(R, dtype=np.float64)
+    res_mass = np.zeros(R, dtype=np.float64)
+    for s in range(0, R, block_rows):
+        rs = np.arange(s, min(R, s + block_rows))
+        ar = a[rs]
+        p = numerics.softmax(numerics.decode(target[rs, ar], dtype), tau)
+        w = p.copy()
+        rej = ar < L[rs]
+        if rej.any():
+            q = numerics.softmax(numerics.decode(draft[rs[rej], ar[rej]], dtype), tau)
+            wr = np.maximum(p[rej] - q, 0.0)
+            res_mass[rs[rej]] = wr.sum(axis=1)
+            wr = residual_rows(p[rej], q)
+            w[rej] = wr
+        y[rs], margin[rs] = draw_rows(w, u_verify[rs, k])
+    row_ratio = np.full(B, np.nan)
+    row_acc = np.zeros(B, dtype=bool)
+    row_ratio[vidx] = ratio[tags[vidx, 0], tags[vidx, 1]]
+    row_acc[vidx] = acc[tags[vidx, 0], tags[vidx, 1]]
+    res.update(accepted_len=a, out_tokens=_emit(a, x, y, k), row_p=row_p, row_q=row_q,
+               row_ratio=row_ratio, row_accept=row_acc, accept=acc, draw_margin=margin,
+               residual_mass=res_mass, row_verified=ver)
+    return res

@@ -1,0 +1,236 @@
+"""Pins of the float64 batch verifier (oracle.verify).
+
+1. It agrees element for element with the scalar rule (oracle.rule) when both
+   take the same uniforms: accept flags, accepted lengths and emitted tokens.
+2. Chi-square on 10**7 Philox-seeded trials: the first n = k+1 tokens emitted
+   over repeated steps follow the target's autoregressive distribution
+   (V = 8, k = 3, 4096 cells). Pre-registered threshold: p > 1e-4.
+3. The same test with a planted mistake gives p < 1e-9.
+4. Greedy mode on logits equals the scalar greedy rule.
+"""
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle import numerics, rule, schedule, verify
+
+
+def _rand_dists(g, shape, V, zeros=0.0):
+    a = g.gamma(1.0, size=shape + (V,))
+    if zeros:
+        a = np.where(g.random(a.shape) < zeros, 0.0, a)
+        a[..., 0] += 1e-3
+    return a / a.sum(axis=-1, keepdims=True)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_batch_equals_scalar_rule(seed):
+    g = np.random.Generator(np.random.Philox(100 + seed))
+    R, k, V = 300, 4, 6
+    P = _rand_dists(g, (R, k + 1), V)
+    Qd = _rand_dists(g, (R, k), V, zeros=0.2 if seed % 2 else 0.0)
+    if seed == 3:
+        Qd[:50] = P[:50, :k]                   # p == q rows: empty residual
+    x = np.zeros((R, k), dtype=np.int64)
+    for j in range(k):
+        c = np.cumsum(Qd[:, j], axis=1)
+        x[:, j] = np.minimum((c < g.random(R)[:, None]).sum(axis=1), V - 1)
+    L = g.integers(0, k + 1, size=R)
+    u = (g.integers(0, 1 << 24, size=(R, k + 1)) * 2.0 ** -24)
+    a, out = verify.verify_probs(P, Qd, x, L, u)
+    for r in range(R):
+        def coin(j, prob, r=r):
+            return u[r, j] < prob
+
+        def draw(w, r=r):
+            return numerics.inv_cdf(np.array(w, dtype=np.float64), u[r, k])
+
+        ar, em = rule.speculative_step(list(P[r]), list(Qd[r]), list(x[r]), int(L[r]), coin, draw)
+        assert ar == a[r]
+        assert list(out[r, :ar + 1]) == em
+        assert (out[r, ar + 1:] == -1).all()
+
+
+def test_greedy_batch_equals_scalar_rule():
+    g = np.random.Generator(np.random.Philox(7))
+    R, k, V = 200, 5, 16
+    target = g.integers(-3, 3, size=(R, k + 1, V)).astype(np.float32)    # many ties
+    x = g.integers(0, V, size=(R, k)).astype(np.int64)
+    agree = g.random((R, k)) < 0.7
+    x = np.where(agree, numerics.argmax_first(target[:, :k].astype(np.float64)), x)
+    L = g.integers(0, k + 1, size=R)
+    tags, cu = schedule.flatten(L)
+    res = verify.verify("greedy", "f32", target, None, x, tags, cu, 1.0,
+                        np.zeros((R, k + 1), dtype=np.float32))
+    for r in range(R):
+        ar, em = rule.greedy_step([list(target[r, j]) for j in range(k + 1)], list(x[r]), int(L[r]))
+        assert ar == res["accepted_len"][r]
+        assert list(res["out_tokens"][r, :ar + 1]) == em
+
+
+def test_sampling_batch_on_logits_matches_probability_form():
+    """verify() on stored logits equals verify_probs() on their float64 softmax."""
+    g = np.random.Generator(np.random.Philox(9))
+    R, k, V = 64, 3, 40
+    tl = (2 * g.standard_normal((R, k + 1, V))).astype(np.float32)
+    dl = (tl[:, :k] + g.standard_normal((R, k, V))).astype(np.float32)
+    tau = 0.8
+    P = numerics.softmax(tl.astype(np.float64), tau)
+    Qd = numerics.softmax(dl.astype(np.float64), tau)
+    x = np.array([[numerics.inv_cdf(Qd[r, j], g.random()) for j in range(k)] for r in range(R)])
+    L = g.integers(0, k + 1, size=R)
+    u = (g.integers(0, 1 << 24, size=(R, k + 1)) * 2.0 ** -24).astype(np.float32)
+    tags, cu = schedule.flatten(L)
+    res = verify.verify("sample", "f32", tl, dl, x, tags, cu, tau, u)
+    a, out = verify.verify_probs(P, Qd, x, L, u.astype(np.float64))
+    assert (res["accepted_len"] == a).all()
+    assert (res["out_tokens"] == out).all()
+
+
+# ---------------------------------------------------------------------------
+# chi-square over repeated steps
+# ---------------------------------------------------------------------------
+
+class LogitModel:
+    """Prefix-dependent target and draft logits for V = 8; prefixes longer than
+    3 share one row (they cannot affect the first 4 emitted tokens)."""
+
+    def __init__(self, V=8, depth=3, seed=0):
+        g = np.random.Generator(np.random.Philox(seed))
+        self.V, self.depth = V, depth
+        self.offsets = [0]
+        for l in range(depth):
+            self.offsets.append(self.offsets[-1] + V ** l)
+        n_rows = self.offsets[-1] + V ** depth + 1
+        self.tl = (1.2 * g.standard_normal((n_rows, V))).astype(np.float32)
+        self.dl = (self.tl + 0.9 * g.standard_normal((n_rows, V))).astype(np.float32)
+        self.shared = n_rows - 1
+
+    def code(self, toks, lens):
+        """Row of each prefix toks[i, :lens[i]]."""
+        V = self.V
+        code = np.full(len(lens), self.shared, dtype=np.int64)
+        for l in range(self.depth + 1):
+            sel = lens == l
+            if not sel.any():
+                continue
+            c = np.zeros(sel.sum(), dtype=np.int64)
+            for t in range(l):
+                c = c * V + toks[sel, t]
+            code[sel] = self.offsets[l] + c
+        return code
+
+    def target_probs(self, n):
+        """Exact (float64) probability of every length-n sequence."""
+        P = numerics.softmax(self.tl.astype(np.float64), 1.0)
+        seqs = np.array(np.meshgrid(*[np.arange(self.V)] * n, indexing="ij")).reshape(n, -1).T
+        pr = np.ones(len(seqs))
+        for t in range(n):
+            rows = self.code(seqs, np.full(len(seqs), t))
+            pr *= P[rows, seqs[:, t]]
+        return seqs, pr
+
+
+def run_trials(model, n_trials, k, seed, verify_fn, batch=1_000_000):
+    """Draft from q, verify, repeat until n = k+1 tokens are emitted; count the
+    first n emitted tokens of every trial. verify_fn(P, Qd, x, L, u) -> (a, out)."""
+    V, n = model.V, k + 1
+    g = np.random.Generator(np.random.Philox(seed))
+    Pt = numerics.softmax(model.tl.astype(np.float64), 1.0)
+    Qt = numerics.softmax(model.dl.astype(np.float64), 1.0)
+    counts = np.zeros(V ** n, dtype=np.int64)
+    for s in range(0, n_trials, batch):
+        T = min(batch, n_trials - s)
+        ctx = np.zeros((T, n + k + 1), dtype=np.int64)
+        lens = np.zeros(T, dtype=np.int64)
+        active = np.arange(T)
+        while len(active):
+            A = len(active)
+            toks = np.zeros((A, n + k + 1), dtype=np.int64)
+            toks[:] = ctx[active]
+            ln = lens[active].copy()
+            x = np.zeros((A, k), dtype=np.int64)
+            rows_p = np.zeros((A, k + 1), dtype=np.int64)
+            for j in range(k + 1):
+                code = model.code(toks, ln + j)
+                rows_p[:, j] = code
+                if j < k:
+                    c = np.cumsum(Qt[code], axis=1)
+                    x[:, j] = np.minimum((c <= g.random(A)[:, None]).sum(axis=1), V - 1)
+                    toks[np.arange(A), ln + j] = x[:, j]
+            L = g.integers(0, k + 1, size=A)
+            u = (g.integers(0, 1 << 24, size=(A, k + 1)) * 2.0 ** -24)
+            a, out = verify_fn(Pt[rows_p], Qt[rows_p[:, :k]], x, L, u)
+            for j in range(k + 1):
+                put = (j <= a) & (lens[active] + j < n + k + 1)
+                idx = active[put]
+                ctx[idx, lens[idx] + j] = out[put, j]
+            lens[active] += a + 1
+            active = active[lens[active] < n]
+        code = np.zeros(T, dtype=np.int64)
+        for t in range(n):
+            code = code * V + ctx[:, t]
+        counts += np.bincount(code, minlength=V ** n)
+    return counts
+
+
+def chi2_pvalue(counts, probs, min_expected=5.0):
+    """Pearson chi-square p-value; cells expected below min_expected are pooled."""
+    exp = probs / probs.sum() * counts.sum()
+    small = exp < min_expected
+    obs = np.concatenate([counts[~small], [counts[small].sum()]])
+    ex = np.concatenate([exp[~small], [exp[small].sum()]])
+    if ex[-1] == 0:
+        obs, ex = obs[:-1], ex[:-1]
+    return stats.chisquare(obs, ex).pvalue
+
+
+@pytest.fixture(scope="module")
+def logit_model():
+    return LogitModel(seed=5)
+
+
+def test_chisquare_1e7_trials(logit_model):
+    k = 3
+    seqs, pr = logit_model.target_probs(k + 1)
+    counts = run_trials(logit_model, 10_000_000, k, seed=2026, verify_fn=verify.verify_probs)
+    assert counts.sum() == 10_000_000
+    p = chi2_pvalue(counts, pr)
+    assert p > 1e-4, p
+
+
+def _planted_resample_from_p(P, Qd, x, L, u):
+    orig = verify.residual_rows
+    try:
+        verify.residual_rows = lambda p, q: p.copy()
+        return verify.verify_probs(P, Qd, x, L, u)
+    finally:
+        verify.residual_rows = orig
+
+
+def _planted_inverted_ratio(P, Qd, x, L, u):
+    return verify.verify_probs(Qd_pad(Qd, P), P[:, :-1], x, L, u)
+
+
+def Qd_pad(Qd, P):
+    # target rows replaced by draft rows (bonus row kept): keep prob becomes min(1, q/p)
+    out = P.copy()
+    out[:, :-1] = Qd
+    return out
+
+
+def _planted_no_min(P, Qd, x, L, u):
+    # accept iff u < p (the draft probability is ignored)
+    R, k1, V = P.shape
+    Q1 = np.ones_like(Qd)
+    a, _ = verify.verify_probs(P, Q1, x, L, u)
+    _, out = verify.verify_probs(P, Qd, x, np.minimum(L, a), u)
+    return np.minimum(L, a), out
+
+
+@pytest.mark.parametrize("bad", [_planted_resample_from_p, _planted_inverted_ratio, _planted_no_min])
+def test_chisquare_planted_mistakes_fail(logit_model, bad):
+    k = 3
+    seqs, pr = logit_model.target_probs(k + 1)
+    counts = run_trials(logit_model, 1_000_000, k, seed=77, verify_fn=bad)
+    assert chi2_pvalue(counts, pr) < 1e-9
