@@ -1,0 +1,258 @@
+"""Benchmark of the confidence-scheduled, flattened verification step on one GPU.
+
+One step = one pass of the hot path over one batch of synthetic input:
+  (Markov head, for the Markov workloads) -> calibration, survival, prefix
+  schedule and flatten -> verification pass, first-reject, resample and emit.
+
+Default workload: R = 256 requests, k = 5, V = 151936, bf16 logits, sampling at
+tau = 1, throughput table with a knee at 256 batch tokens (the scheduler
+truncates), math/code/chat confidence profiles. The metric is verified draft
+tokens per second (N = sum of scheduled lengths per step, divided by the step
+time) and the HBM bandwidth the verification kernel achieves against the
+8 TB/s peak of MI355X.
+
+  python bench.py [--steps K] [--warmup W] [--config c2] [--mode sample]
+                  [--max-len k|-1] [--no-cpu] [--variants]
+
+Prints one JSON line. Inputs are resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft tokens/s at V=151936, k=5, 256 req; achieved HBM GB/s % peak"
+HBM_PEAK = 8.0e12
+DOMINANT = "verify_partials"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_partials_c2_traffic.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--mode", default="sample", choices=["sample", "greedy"])
+    ap.add_argument("--max-len", default="k")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time greedy and verify-all variants of the workload")
+    ap.add_argument("--copy-probe", type=float, default=0.0,
+                    help="only run a device copy of this many GiB (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("common.h", "verify.hip"):
+        h.update(open(os.path.join(ROOT, "draft_token_verification_flattened_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the current kernel source."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None, None
+    vals = {}
+    for line in open(PROFILE_TRAFFIC):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash():
+        return None, vals.get("source_hash")
+    try:
+        return float(vals["hbm_bytes_per_launch"]), vals.get("source_hash")
+    except (KeyError, ValueError):
+        return None, None
+
+
+def algorithmic_bytes(w, mode, N, R):
+    """Logit bytes the verification pass must read once: every target row of
+    the flattened batch (N verified + R bonus), plus the N draft rows when
+    sampling."""
+    esize = 2 if w.dtype == "bf16" else 4
+    rows = (2 * N + R) if mode == "sample" else (N + R)
+    return rows * w.V * esize
+
+
+def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        d.step(mode_c, max_len)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        d.step(mode_c, max_len)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    # per-kernel durations: HIP events recorded by the library on the launch
+    # stream around each kernel, over a second pass of the same steps
+    B.timing_reset()
+    B.timing_enable(True)
+    for _ in range(steps):
+        d.step(mode_c, max_len)
+    torch.cuda.synchronize()
+    kern = {}
+    for name in ("markov_logits", "markov_pick", "schedule", "verify_partials", "verify_finalize",
+                 "resample_mass", "resample_pick"):
+        n, tot = B.timing_read(name)
+        if n:
+            kern[name] = dict(launches_per_step=n / steps, avg_us=1000.0 * tot / n)
+    B.timing_enable(False)
+    B.timing_reset()
+    L = d.host("lengths")
+    N = int(L.sum())
+    R = w.R
+    nbytes = algorithmic_bytes(w, mode, N, R)
+    dom = kern.get(DOMINANT)
+    achieved = nbytes / (dom["avg_us"] * 1e-6) if dom else None
+    verify_us = sum(kern[k]["avg_us"] * kern[k]["launches_per_step"]
+                    for k in ("verify_partials", "verify_finalize", "resample_mass", "resample_pick") if k in kern)
+    return dict(mode=mode, max_len=max_len, ms_per_step=ms_step, N=N, rows=int(d.host("n_rows")[0]),
+                tokens_per_s=N / (ms_step * 1e-3), verify_us=verify_us,
+                verify_tokens_per_s=N / (verify_us * 1e-6) if verify_us else None,
+                algorithmic_bytes=nbytes, dominant_gbps=achieved / 1e9 if achieved else None,
+                dominant_frac=achieved / HBM_PEAK if achieved else None, kernels=kern)
+
+
+def cpu_baseline(w, mode, max_len):
+    """The oracle, as it stands, on one full step of the same workload."""
+    import numpy as np
+    from oracle import markov as omarkov
+    from oracle import schedule as osched
+    from oracle import verify as overify
+    t = time.perf_counter()
+    if w.backbone is not None:
+        m = omarkov.markov_draft(mode, w.dtype, w.backbone, w.emb, w.proj, w.prev_token, w.tau, w.u_draft)
+        dl, tok = m["logits"], m["tokens"]
+    else:
+        dl, tok = w.draft, (w.tokens_sample if mode == "sample" else w.tokens_greedy)
+    s = osched.schedule(w.conf_logit, w.pos_temp, w.tbl_tokens, w.tbl_thr, max_len)
+    tags, cu = osched.flatten(s["L"])
+    overify.verify(mode, w.dtype, w.target, dl if mode == "sample" else None, tok, tags, cu, w.tau, w.u_verify)
+    dt = time.perf_counter() - t
+    N = int(np.sum(s["L"]))
+    threads = 1
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        if w.backbone is not None and info:
+            threads = max(i.get("num_threads", 1) for i in info)
+    except Exception:
+        pass
+    return dict(value=N / dt, unit="verified draft tokens/s", cores=threads, kind="oracle",
+                sample=f"one full step of the workload (R={w.R}, N={N} verified drafts), "
+                       f"single process, {dt:.2f} s")
+
+
+def copy_probe(gib):
+    import torch
+    n = int(gib * (1 << 30))
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py runs on one GPU only: the verification step is measured on a single MI355X; "
+              "multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+
+    import numpy as np  # noqa: F401
+    import torch
+    from draft_token_verification_flattened_amd import binding as B
+    from draft_token_verification_flattened_amd import workloads
+    from draft_token_verification_flattened_amd.pipeline import DeviceStep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.lib()   # fail loudly if the HIP library is missing
+    w = workloads.make(args.config)
+    max_len = w.k if args.max_len == "k" else int(args.max_len)
+    d = DeviceStep(w)
+    mode_c = B.SAMPLE if args.mode == "sample" else B.GREEDY
+    main_res = run_variant(d, w, mode_c, args.mode, max_len, args.steps, args.warmup, B, torch)
+
+    extra = {}
+    if args.variants:
+        for mode in (["sample", "greedy"] if w.backbone is None else ["sample"]):
+            for ml in (w.k, -1):
+                if mode == args.mode and ml == max_len:
+                    continue
+                mc = B.SAMPLE if mode == "sample" else B.GREEDY
+                r = run_variant(d, w, mc, mode, ml, args.steps, args.warmup, B, torch)
+                extra[f"{mode}_{'scheduled' if ml == w.k else 'verify_all'}"] = r
+
+    traffic, thash = committed_traffic()
+    dom = main_res["kernels"].get(DOMINANT, {})
+    roofline = {
+        "bound": "hbm",
+        "achieved": main_res["dominant_gbps"],
+        "peak": HBM_PEAK / 1e9,
+        "unit": "GB/s",
+        "frac": main_res["dominant_frac"],
+        "traffic": traffic,
+        "kernel": DOMINANT,
+        "avg_launch_us": dom.get("avg_us"),
+        "algorithmic_bytes_per_launch": main_res["algorithmic_bytes"],
+    }
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, args.mode, max_len)
+    out = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.config}: {workloads.CONFIGS[args.config]['desc']}",
+            "R": w.R, "k": w.k, "V": w.V, "storage": w.dtype, "mode": args.mode,
+            "tau": w.tau, "max_len": max_len, "verified_drafts_per_step": main_res["N"],
+            "flattened_rows_per_step": main_res["rows"], "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "verify_only": {"us_per_step": main_res["verify_us"], "tokens_per_s": main_res["verify_tokens_per_s"]},
+        "kernels": main_res["kernels"],
+        "variants": {k: {kk: v[kk] for kk in ("ms_per_step", "N", "rows", "tokens_per_s", "verify_us",
+                                                "verify_tokens_per_s", "dominant_gbps", "dominant_frac")}
+                     for k, v in extra.items()},
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+"""ctypes binding of libspecv (include/specv.h).
+
+Argument marshalling only: each wrapper checks that torch tensors have the
+dtype, shape and device the C ABI expects, passes their device pointers and the
+current HIP stream, and raises on a non-zero status. Every step of the
+computation runs in the library's kernels. There is no fallback: if the
+library is not built, loading fails with an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecv.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "specv.h")
+
+OK, EINVAL, EUNSUPPORTED, EDEVICE = 0, -1, -2, -3
+BF16, F32 = 0, 1
+GREEDY, SAMPLE = 0, 1
+STATUS_BAD_TOKEN, STATUS_BAD_TAG = 1, 2
+MAX_K, MAX_SCHED_ITEMS = 32, 16384
+
+_c_int, _c_size, _c_ptr = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGS = {
+    "spec_schedule": (_c_int, [_c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
+                               _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+    "spec_flatten": (_c_int, [_c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+    "spec_verify_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
+    "spec_verify": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                             _c_ptr, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                             _c_size, _c_ptr]),
+    "markov_draft_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
+    "markov_draft": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
+                              _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+    "specv_last_error": (ctypes.c_char_p, []),
+    "specv_read_status": (_c_int, [_c_ptr, _c_ptr, ctypes.POINTER(ctypes.c_uint32)]),
+    "specv_timing_enable": (_c_int, [_c_int]),
+    "specv_timing_reset": (_c_int, []),
+    "specv_timing_read": (_c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int),
+                                   ctypes.POINTER(ctypes.c_double)]),
+}
+
+_lib = None
+
+
+class SpecvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"specv error {code}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libspecv.so (built by draft_token_verification_flattened_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run python -m draft_token_verification_flattened_amd.build")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/specv.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)))
+
+
+def last_error() -> str:
+    return lib().specv_last_error().decode()
+
+
+def _check(code: int):
+    if code != OK:
+        raise SpecvError(code, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+
+
+_LOGIT_TYPES = {torch.bfloat16: BF16, torch.int16: BF16, torch.uint16: BF16, torch.float32: F32}
+
+
+def logit_dtype(t: torch.Tensor) -> int:
+    return _LOGIT_TYPES[t.dtype]
+
+
+def spec_schedule(conf_logit, pos_temp, tbl_tokens, tbl_thr, max_len, len_out, tags_out, cu_rows_out,
+                  n_rows_out, survival_out=None, stream=None):
+    R, k = conf_logit.shape
+    _dev(conf_logit, "conf_logit", (torch.float32,))
+    _dev(pos_temp, "pos_temp", (torch.float32,), (k,))
+    _dev(tbl_tokens, "tbl_tokens", (torch.int32,))
+    _dev(tbl_thr, "tbl_thr", (torch.float64,), tuple(tbl_tokens.shape))
+    _dev(len_out, "len_out", (torch.int32,), (R,))
+    _dev(tags_out, "tags_out", (torch.int32,), (R * (k + 1), 2))
+    _dev(cu_rows_out, "cu_rows_out", (torch.int32,), (R + 1,))
+    _dev(n_rows_out, "n_rows_out", (torch.int32,), (1,))
+    if survival_out is not None:
+        _dev(survival_out, "survival_out", (torch.float64,), (R, k))
+    _check(lib().spec_schedule(R, k, _ptr(conf_logit), _ptr(pos_temp), _ptr(tbl_tokens), _ptr(tbl_thr),
+                               tbl_tokens.numel(), int(max_len), _ptr(len_out), _ptr(tags_out),
+                               _ptr(cu_rows_out), _ptr(n_rows_out), _ptr(survival_out), _stream(stream)))
+
+
+def spec_flatten(len_in, k, tags_out, cu_rows_out, n_rows_out, stream=None):
+    R = len_in.numel()
+    _dev(len_in, "len_in", (torch.int32,))
+    _dev(tags_out, "tags_out", (torch.int32,), (R * (k + 1), 2))
+    _dev(cu_rows_out, "cu_rows_out", (torch.int32,), (R + 1,))
+    _dev(n_rows_out, "n_rows_out", (torch.int32,), (1,))
+    _check(lib().spec_flatten(R, int(k), _ptr(len_in), _ptr(tags_out), _ptr(cu_rows_out), _ptr(n_rows_out),
+                              _stream(stream)))
+
+
+def verify_workspace_bytes(mode: int, R: int, k: int, V: int) -> int:
+    return int(lib().spec_verify_workspace_bytes(mode, R, k, V))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A device byte buffer for the ws argument (torch allocations are 256-byte aligned)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def spec_verify(mode, target, draft, tokens, tags, cu_rows, n_rows, temperature, uniforms, accepted_len_out,
+                out_tokens, ws, row_diag=None, stream=None):
+    R, k1, V = target.shape
+    k = k1 - 1
+    dt = logit_dtype(target)
+    _dev(target, "target", tuple(_LOGIT_TYPES))
+    if mode == SAMPLE:
+        _dev(draft, "draft", (target.dtype,), (R, k, V))
+        _dev(uniforms, "uniforms", (torch.float32,), (R, k + 1))
+    _dev(tokens, "tokens", (torch.int32,), (R, k))
+    _dev(tags, "tags", (torch.int32,), (R * (k + 1), 2))
+    _dev(cu_rows, "cu_rows", (torch.int32,), (R + 1,))
+    _dev(n_rows, "n_rows", (torch.int32,), (1,))
+    _dev(accepted_len_out, "accepted_len_out", (torch.int32,), (R,))
+    _dev(out_tokens, "out_tokens", (torch.int32,), (R, k + 1))
+    _dev(ws, "ws", (torch.uint8,))
+    if row_diag is not None:
+        _dev(row_diag, "row_diag", (torch.float32,), (R * (k + 1), 4))
+    _check(lib().spec_verify(int(mode), dt, R, k, V, _ptr(target), _ptr(draft) if mode == SAMPLE else None,
+                             _ptr(tokens), _ptr(tags), _ptr(cu_rows), _ptr(n_rows), float(temperature),
+                             _ptr(uniforms) if mode == SAMPLE else None, _ptr(accepted_len_out),
+                             _ptr(out_tokens), _ptr(row_diag), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def markov_workspace_bytes(R: int, k: int, V: int, d_m: int) -> int:
+    return int(lib().markov_draft_workspace_bytes(R, k, V, d_m))
+
+
+def markov_draft(mode, backbone, emb, proj, prev_token, temperature, uniforms, tokens_out, logits_out, ws,
+                 stream=None):
+    R, k, V = backbone.shape
+    d_m = emb.shape[1]
+    dt = logit_dtype(backbone)
+    _dev(backbone, "backbone", tuple(_LOGIT_TYPES))
+    _dev(emb, "emb", (backbone.dtype,), (V, d_m))
+    _dev(proj, "proj", (backbone.dtype,), (V, d_m))
+    _dev(prev_token, "prev_token", (torch.int32,), (R,))
+    _dev(tokens_out, "tokens_out", (torch.int32,), (R, k))
+    _dev(logits_out, "logits_out", (backbone.dtype,), (R, k, V))
+    _dev(ws, "ws", (torch.uint8,))
+    if mode == SAMPLE:
+        _dev(uniforms, "uniforms", (torch.float32,), (R, k))
+    _check(lib().markov_draft(int(mode), dt, R, k, V, d_m, _ptr(backbone), _ptr(emb), _ptr(proj),
+                              _ptr(prev_token), float(temperature), _ptr(uniforms) if mode == SAMPLE else None,
+                              _ptr(tokens_out), _ptr(logits_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def read_status(ws, stream=None) -> int:
+    v = ctypes.c_uint32(0)
+    _check(lib().specv_read_status(_ptr(ws), _stream(stream), ctypes.byref(v)))
+    return int(v.value)
+
+
+def timing_enable(on: bool):
+    _check(lib().specv_timing_enable(1 if on else 0))
+
+
+def timing_reset():
+    _check(lib().specv_timing_reset())
+
+
+def timing_read(prefix: str):
+    n = ctypes.c_int(0)
+    t = ctypes.c_double(0.0)
+    _check(lib().specv_timing_read(prefix.encode(), ctypes.byref(n), ctypes.byref(t)))
+    return int(n.value), float(t.value)

@@ -1,0 +1,129 @@
+// libspecv host utilities: last-error message, status readback, kernel timing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "host.h"
+
+namespace specv {
+
+namespace {
+thread_local char g_err[512] = "";
+
+struct Pending {
+    std::string name;
+    hipEvent_t a, b;
+};
+
+bool g_timing = false;
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_free;
+std::map<std::string, std::pair<int, double>> g_done;
+std::string g_cur;
+hipEvent_t g_cur_a = nullptr;
+
+hipEvent_t take_event() {
+    if (!g_free.empty()) {
+        hipEvent_t e = g_free.back();
+        g_free.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+void timing_before(const char* name, hipStream_t s) {
+    if (!g_timing) return;
+    g_cur = name;
+    g_cur_a = take_event();
+    if (g_cur_a) (void)hipEventRecord(g_cur_a, s);
+}
+
+void timing_after(hipStream_t s) {
+    if (!g_timing || !g_cur_a) return;
+    hipEvent_t b = take_event();
+    if (!b) return;
+    (void)hipEventRecord(b, s);
+    g_pending.push_back({g_cur, g_cur_a, b});
+    g_cur_a = nullptr;
+}
+
+}  // namespace specv
+
+extern "C" {
+
+const char* specv_last_error(void) { return specv::g_err; }
+
+int specv_read_status(const void* ws, specv_stream stream, uint32_t* status_out) {
+    if (!ws || !status_out) return specv::fail(SPECV_EINVAL, "specv_read_status: NULL pointer");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(s) != hipSuccess)
+        return specv::fail(SPECV_EDEVICE, "specv_read_status: stream synchronisation failed");
+    if (hipMemcpy(status_out, ws, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+        return specv::fail(SPECV_EDEVICE, "specv_read_status: copy failed");
+    return SPECV_OK;
+}
+
+int specv_timing_enable(int on) {
+    specv::g_timing = on != 0;
+    return SPECV_OK;
+}
+
+int specv_timing_reset(void) {
+    for (auto& p : specv::g_pending) {
+        (void)hipEventSynchronize(p.b);
+        specv::g_free.push_back(p.a);
+        specv::g_free.push_back(p.b);
+    }
+    specv::g_pending.clear();
+    specv::g_done.clear();
+    return SPECV_OK;
+}
+
+int specv_timing_read(const char* prefix, int* launches, double* total_ms) {
+    if (!prefix || !launches || !total_ms)
+        return specv::fail(SPECV_EINVAL, "specv_timing_read: NULL pointer");
+    for (auto& p : specv::g_pending) {
+        if (hipEventSynchronize(p.b) != hipSuccess)
+            return specv::fail(SPECV_EDEVICE, "specv_timing_read: event synchronisation failed");
+        float ms = 0.f;
+        (void)hipEventElapsedTime(&ms, p.a, p.b);
+        auto& d = specv::g_done[p.name];
+        d.first += 1;
+        d.second += ms;
+        specv::g_free.push_back(p.a);
+        specv::g_free.push_back(p.b);
+    }
+    specv::g_pending.clear();
+    int n = 0;
+    double t = 0.0;
+    size_t lp = strlen(prefix);
+    for (auto& kv : specv::g_done) {
+        if (kv.first.compare(0, lp, prefix) == 0) {
+            n += kv.second.first;
+            t += kv.second.second;
+        }
+    }
+    *launches = n;
+    *total_ms = t;
+    return SPECV_OK;
+}
+
+}  // extern "C"

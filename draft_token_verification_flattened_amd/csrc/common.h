@@ -1,0 +1,174 @@
+// Device helpers shared by the gfx950 kernels of libspecv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "specv.h"
+
+namespace specv {
+
+constexpr int kWave = 64;   // CDNA wavefront width
+
+// Workspace header: one status word, padded to 256 bytes.
+struct WsHeader {
+    uint32_t status;
+    uint32_t pad[63];
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Storage traits: 16-byte vector of logits, widened to float.
+template <int DT> struct Logit;
+
+template <> struct Logit<SPECV_BF16> {
+    using T = uint16_t;
+    static constexpr int kVec = 8;                 // elements per 16-byte load
+    __device__ static __forceinline__ float load1(const T* p) {
+        return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+    }
+    __device__ static __forceinline__ void unpack(const uint4& v, float (&x)[8]) {
+        x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+        x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+        x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+        x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+    }
+};
+
+template <> struct Logit<SPECV_F32> {
+    using T = float;
+    static constexpr int kVec = 4;
+    __device__ static __forceinline__ float load1(const T* p) { return *p; }
+    __device__ static __forceinline__ void unpack(const uint4& v, float (&x)[4]) {
+        x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+        x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+    }
+};
+
+// ---- wavefront reductions (xor butterflies: every lane ends with the result) ----
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// (value, index) maximum: larger value wins, equal values go to the lower index.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float v2 = __shfl_xor(v, o, kWave);
+        int i2 = __shfl_xor(i, o, kWave);
+        argmax_merge(v, i, v2, i2);
+    }
+}
+
+// Online log-sum-exp state in base 2: the sum of exp2(a - m) over the elements
+// seen, a = logit * log2(e) / tau. An empty state is (-inf, 0).
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+    float mm = fmaxf(m, m2);
+    if (mm == -INFINITY) return;
+    float e1 = (m == -INFINITY) ? 0.f : exp2f(m - mm);
+    float e2 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mm);
+    s = s * e1 + s2 * e2;
+    m = mm;
+}
+
+__device__ __forceinline__ void wave_lse(float& m, float& s) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float m2 = __shfl_xor(m, o, kWave);
+        float s2 = __shfl_xor(s, o, kWave);
+        lse_merge(m, s, m2, s2);
+    }
+}
+
+// Inclusive prefix sum across the wave in lane order.
+__device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        float t = __shfl_up(v, o, kWave);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Two-level inverse-CDF draw by one wavefront: the smallest index e with
+// w_0 + ... + w_e > thr, where the weights come in chunks of `chunk_len`.
+// chunk_mass(ch) must return the chunk's total weight and weight(e) one
+// element's; the chunk totals select the chunk, an in-order scan of its
+// elements selects the index. When rounding leaves no crossing, the last index
+// with positive weight (in the last chunk with mass) is returned.
+template <class ChunkMass, class Weight>
+__device__ int inv_cdf_pick(int C, int V, int chunk_len, float thr, ChunkMass chunk_mass, Weight weight,
+                            int lane) {
+    float carry = 0.f, base = 0.f;
+    int sel = -1, last_pos = -1;
+    for (int ch0 = 0; ch0 < C && sel < 0; ch0 += kWave) {
+        const int ch = ch0 + lane;
+        const float mch = ch < C ? chunk_mass(ch) : 0.f;
+        const float inc = wave_inclusive_scan(mch, lane) + carry;
+        int cand = (ch < C && inc > thr) ? ch : 0x7fffffff;
+        const int pos = (ch < C && mch > 0.f) ? ch : -1;
+        cand = wave_min_int(cand);
+        last_pos = max(last_pos, -wave_min_int(-pos));
+        if (cand != 0x7fffffff) {
+            sel = cand;
+            base = __shfl(inc - mch, cand - ch0, kWave);
+        }
+        carry = __shfl(inc, kWave - 1, kWave);
+    }
+    if (sel < 0) {
+        sel = last_pos < 0 ? 0 : last_pos;
+        base = -INFINITY;                      // no crossing: fall back to the last positive weight
+    }
+    const int beg = sel * chunk_len, end = min(V, beg + chunk_len);
+    float run = base;
+    int found = 0x7fffffff, lastw = -1;
+    for (int e0 = beg; e0 < end && found == 0x7fffffff; e0 += kWave * 8) {
+        float w[8];
+        float lsum = 0.f;
+        const int my = e0 + lane * 8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            w[q] = (my + q < end) ? weight(my + q) : 0.f;
+            lsum += w[q];
+            if (w[q] > 0.f) lastw = max(lastw, my + q);
+        }
+        const float incl = wave_inclusive_scan(lsum, lane);
+        float cum = run + (incl - lsum);
+        int hit = 0x7fffffff;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            cum += w[q];
+            if (hit == 0x7fffffff && my + q < end && cum > thr) hit = my + q;
+        }
+        found = wave_min_int(hit);
+        run += __shfl(incl, kWave - 1, kWave);
+    }
+    lastw = -wave_min_int(-lastw);
+    return found != 0x7fffffff ? found : (lastw >= 0 ? lastw : beg);
+}
+
+__device__ __forceinline__ void set_status(WsHeader* h, uint32_t bits) {
+    atomicOr(&h->status, bits);
+}
+
+}  // namespace specv

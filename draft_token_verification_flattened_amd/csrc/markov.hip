@@ -1,0 +1,357 @@
+// markov_draft: the Markov head of the semi-autoregressive drafter.
+//
+// Pages: the drafter keeps a parallel backbone that proposes the whole block in
+// one pass and adds a light sequential module that injects prefix information
+// token by token; the default is a Markov head that looks only at the previous
+// token ("刚融完500亿创始人亲自下场写代码…", section "1. 半自回归生成";
+// "DSpark 的 661% 提速…", section 3.1). The head is read here as a low-rank
+// additive correction: dl_i = backbone_i + E[x_{i-1}] . P^T.
+//
+// Per position i (sequential: x_i feeds position i+1):
+//   markov_logits_mfma (bf16)  one workgroup per 64-entry vocabulary slice:
+//       the slice of P (64 x d_m) is staged in LDS; four wavefronts sweep the
+//       requests in blocks of 64, multiplying gathered embedding rows E[x_{i-1}]
+//       by the slice with v_mfma_f32_16x16x32_bf16 (fp32 accumulation). The
+//       epilogue adds the backbone logits, rounds to bf16 (nearest-even),
+//       stores the draft logits and emits per-(request, slice) softmax or
+//       argmax partials of the rounded values.
+//   markov_logits_fma (fp32)   the same with one lane per output and plain FMA.
+//   markov_pick                one wavefront per request: merges the partials;
+//       greedy argmax, or the two-level inverse-CDF draw over softmax(dl / tau).
+#include <climits>
+
+#include "common.h"
+#include "host.h"
+
+namespace specv {
+
+constexpr int kSlice = 64;          // vocabulary entries per workgroup / partial
+
+struct MarkovArgs {
+    int R, k, V, d_m, S;            // S = slices per row
+    int pos;                        // current position i
+    int mode;
+    float c;                        // log2(e) / tau
+    const void* bk;                 // [R,k,V]
+    const void* emb;                // [V,d_m]
+    const void* proj;               // [V,d_m]
+    const int32_t* prev;            // [R]
+    const float* uniforms;          // [R,k]
+    int32_t* tokens;                // [R,k]
+    void* dl;                       // [R,k,V]
+    float2* part;                   // [R * S]
+    WsHeader* hdr;
+};
+
+__device__ __forceinline__ int prev_token(const MarkovArgs& a, int m) {
+    int p = a.pos == 0 ? a.prev[m] : a.tokens[long(m) * a.k + a.pos - 1];
+    return p;
+}
+
+// round-to-nearest-even float -> bf16 bits (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Partial of one (request, slice): argmax (greedy) or base-2 online softmax.
+struct Part {
+    float a;
+    float b;   // greedy: index bits; sampling: sum
+};
+
+__device__ __forceinline__ void part_add(int mode, Part& p, float x, int idx, float c) {
+    if (mode == SPECV_GREEDY) {
+        if (__float_as_int(p.b) == INT_MAX || x > p.a || (x == p.a && idx < __float_as_int(p.b))) {
+            p.a = x;
+            p.b = __int_as_float(idx);
+        }
+    } else {
+        const float am = x * c;
+        if (am > p.a) { p.b *= __builtin_amdgcn_exp2f(p.a - am); p.a = am; }
+        p.b += __builtin_amdgcn_exp2f(fmaf(x, c, -p.a));
+    }
+}
+
+__device__ __forceinline__ void part_merge(int mode, Part& p, Part q) {
+    if (mode == SPECV_GREEDY) {
+        int i1 = __float_as_int(p.b), i2 = __float_as_int(q.b);
+        if (q.a > p.a || (q.a == p.a && i2 < i1) || i1 == INT_MAX) {
+            if (i2 != INT_MAX) { p.a = q.a; p.b = q.b; }
+        }
+    } else {
+        lse_merge(p.a, p.b, q.a, q.b);
+    }
+}
+
+__device__ __forceinline__ Part part_empty(int mode) {
+    Part p;
+    if (mode == SPECV_GREEDY) { p.a = -INFINITY; p.b = __int_as_float(INT_MAX); }
+    else { p.a = -INFINITY; p.b = 0.f; }
+    return p;
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// bf16: MFMA projection
+// ---------------------------------------------------------------------------
+
+template <bool VEC4>
+__global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * kSlice;
+    const int dm = a.d_m;
+    if (a.pos == 0 && blockIdx.x == 0 && tid == 0) a.hdr->status = 0u;   // this kernel sets no bits
+    const int row_bytes = dm * 2 + 16;              // padded LDS row (bank spread)
+    const uint16_t* P = static_cast<const uint16_t*>(a.proj);
+    const uint16_t* E = static_cast<const uint16_t*>(a.emb);
+
+    // stage P[n0 .. n0+63, :] in LDS (zeros past V)
+    const int vec_per_row = dm / 8;
+    for (int q = tid; q < kSlice * vec_per_row; q += blockDim.x) {
+        const int rr = q / vec_per_row, cc = q % vec_per_row;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (n0 + rr < a.V) v = reinterpret_cast<const uint4*>(P + long(n0 + rr) * dm)[cc];
+        *reinterpret_cast<uint4*>(lds_raw + rr * row_bytes + cc * 16) = v;
+    }
+    __syncthreads();
+
+    const uint16_t* bk = static_cast<const uint16_t*>(a.bk);
+    uint16_t* dl = static_cast<uint16_t*>(a.dl);
+    const int g = lane >> 4, l16 = lane & 15;
+
+    for (int mb = wave * 64; mb < a.R; mb += 4 * 64) {
+        f32x4 acc[4][4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // gathered embedding rows of this lane's four request columns
+        const uint16_t* erow[4];
+        bool mok[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int m = mb + 16 * b + l16;
+            mok[b] = m < a.R;
+            int p = mok[b] ? prev_token(a, m) : 0;
+            if (p < 0 || p >= a.V) p = 0;             // reported by markov_pick
+            erow[b] = E + long(p) * dm;
+        }
+        for (int k0 = 0; k0 < dm; k0 += 32) {
+            bf16x8 bfr[4], afr[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                uint4 v = mok[b] ? *reinterpret_cast<const uint4*>(erow[b] + k0 + 8 * g) : make_uint4(0, 0, 0, 0);
+                bfr[b] = __builtin_bit_cast(bf16x8, v);
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                uint4 v = *reinterpret_cast<const uint4*>(lds_raw + (16 * x + l16) * row_bytes + (k0 + 8 * g) * 2);
+                afr[x] = __builtin_bit_cast(bf16x8, v);
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[x][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[x], bfr[b], acc[x][b], 0, 0, 0);
+        }
+        // epilogue: lane holds vocab n0 + 16x + 4g + {0..3} of request mb + 16b + l16
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int m = mb + 16 * b + l16;
+            Part pp = part_empty(a.mode);
+            if (m < a.R) {
+                const long rowoff = (long(m) * a.k + a.pos) * long(a.V);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int n = n0 + 16 * x + 4 * g;
+                    float bkv[4];
+                    if (VEC4 && n + 3 < a.V) {
+                        uint2 w = *reinterpret_cast<const uint2*>(bk + rowoff + n);
+                        bkv[0] = bf16_lo(w.x); bkv[1] = bf16_hi(w.x);
+                        bkv[2] = bf16_lo(w.y); bkv[3] = bf16_hi(w.y);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            bkv[e] = n + e < a.V ? __uint_as_float(uint32_t(bk[rowoff + n + e]) << 16) : 0.f;
+                    }
+                    uint32_t hb[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        hb[e] = f32_to_bf16_rne(acc[x][b][e] + bkv[e]);
+                        if (n + e < a.V) part_add(a.mode, pp, __uint_as_float(hb[e] << 16), n + e, a.c);
+                    }
+                    if (VEC4 && n + 3 < a.V) {
+                        *reinterpret_cast<uint2*>(dl + rowoff + n) =
+                            make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < a.V) dl[rowoff + n + e] = uint16_t(hb[e]);
+                    }
+                }
+            }
+            // merge the four lanes that share this request (lane ^ 16, lane ^ 32)
+#pragma unroll
+            for (int o = 16; o <= 32; o <<= 1) {
+                Part q;
+                q.a = __shfl_xor(pp.a, o, 64);
+                q.b = __shfl_xor(pp.b, o, 64);
+                part_merge(a.mode, pp, q);
+            }
+            if (g == 0 && m < a.R) a.part[long(m) * a.S + blockIdx.x] = make_float2(pp.a, pp.b);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32: plain FMA projection, one wavefront per (request, slice)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void markov_logits_fma(MarkovArgs a) {
+    const int lane = threadIdx.x & 63;
+    const long item = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (item >= long(a.R) * a.S) return;
+    const int m = int(item / a.S), sl = int(item % a.S);
+    const int n = sl * kSlice + lane;
+    const float* E = static_cast<const float*>(a.emb);
+    const float* P = static_cast<const float*>(a.proj);
+    const float* bk = static_cast<const float*>(a.bk);
+    float* dl = static_cast<float*>(a.dl);
+    if (a.pos == 0 && item == 0 && lane == 0) a.hdr->status = 0u;   // this kernel sets no bits
+    int p = prev_token(a, m);
+    if (p < 0 || p >= a.V) p = 0;                 // reported by markov_pick
+    Part pp = part_empty(a.mode);
+    if (n < a.V) {
+        float acc = 0.f;
+        for (int d = 0; d < a.d_m; ++d) acc = fmaf(E[long(p) * a.d_m + d], P[long(n) * a.d_m + d], acc);
+        const long off = (long(m) * a.k + a.pos) * long(a.V) + n;
+        const float v = acc + bk[off];
+        dl[off] = v;
+        part_add(a.mode, pp, v, n, a.c);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        Part q;
+        q.a = __shfl_xor(pp.a, o, 64);
+        q.b = __shfl_xor(pp.b, o, 64);
+        part_merge(a.mode, pp, q);
+    }
+    if (lane == 0) a.part[long(m) * a.S + sl] = make_float2(pp.a, pp.b);
+}
+
+// ---------------------------------------------------------------------------
+// next token per request
+// ---------------------------------------------------------------------------
+
+template <int DT>
+__global__ __launch_bounds__(256) void markov_pick(MarkovArgs a) {
+    using LT = Logit<DT>;
+    using T = typename LT::T;
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= a.R) return;
+    if (a.pos == 0 && lane == 0 && (a.prev[m] < 0 || a.prev[m] >= a.V)) set_status(a.hdr, SPECV_STATUS_BAD_TOKEN);
+    const float2* pr = a.part + long(m) * a.S;
+    Part tot = part_empty(a.mode);
+    for (int s = lane; s < a.S; s += 64) {
+        Part q;
+        q.a = pr[s].x;
+        q.b = pr[s].y;
+        part_merge(a.mode, tot, q);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        Part q;
+        q.a = __shfl_xor(tot.a, o, 64);
+        q.b = __shfl_xor(tot.b, o, 64);
+        part_merge(a.mode, tot, q);
+    }
+    int y;
+    if (a.mode == SPECV_GREEDY) {
+        y = __float_as_int(tot.b);
+    } else {
+        const float M = tot.a;
+        const float thr = a.uniforms[long(m) * a.k + a.pos] * tot.b;
+        const T* row = static_cast<const T*>(a.dl) + (long(m) * a.k + a.pos) * long(a.V);
+        const float c = a.c;
+        y = inv_cdf_pick(
+            a.S, a.V, kSlice, thr,
+            [&](int s) { float2 q = pr[s]; return q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - M); },
+            [&](int e) { return exp2f(fmaf(LT::load1(row + e), c, -M)); }, lane);
+    }
+    if (lane == 0) a.tokens[long(m) * a.k + a.pos] = y;
+}
+
+}  // namespace specv
+
+extern "C" size_t markov_draft_workspace_bytes(int R, int k, int V, int d_m) {
+    if (R < 1 || k < 1 || k > SPECV_MAX_K || V < 1 || d_m < 1) return 0;
+    const size_t S = (size_t(V) + specv::kSlice - 1) / specv::kSlice;
+    return 256 + ((size_t(R) * S * sizeof(float2) + 255) & ~size_t(255));
+}
+
+extern "C" int markov_draft(int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
+                            const void* emb, const void* proj, const int32_t* prev_token,
+                            float temperature, const float* uniforms, int32_t* draft_tokens_out,
+                            void* draft_logits_out, void* ws, size_t ws_bytes, specv_stream stream) {
+    using namespace specv;
+    clear_error();
+    if (mode != SPECV_GREEDY && mode != SPECV_SAMPLE)
+        return fail(SPECV_EINVAL, "markov_draft: mode %d is neither greedy (0) nor sample (1)", mode);
+    if (dtype != SPECV_BF16 && dtype != SPECV_F32)
+        return fail(SPECV_EUNSUPPORTED, "markov_draft: dtype %d unsupported", dtype);
+    if (R < 1 || k < 1 || k > SPECV_MAX_K || V < 1 || d_m < 1)
+        return fail(SPECV_EINVAL, "markov_draft: need R >= 1, 1 <= k <= %d, V >= 1, d_m >= 1", SPECV_MAX_K);
+    if (dtype == SPECV_BF16 && (d_m % 32 != 0 || d_m > 480))
+        return fail(SPECV_EUNSUPPORTED, "markov_draft: bf16 needs d_m %% 32 == 0 and d_m <= 480 (got %d)", d_m);
+    if (!backbone_logits || !emb || !proj || !prev_token || !draft_tokens_out || !draft_logits_out || !ws)
+        return fail(SPECV_EINVAL, "markov_draft: NULL required pointer");
+    if (mode == SPECV_SAMPLE) {
+        if (!uniforms) return fail(SPECV_EINVAL, "markov_draft: sampling needs uniforms");
+        if (!(temperature > 0.f) || !(temperature < INFINITY))
+            return fail(SPECV_EINVAL, "markov_draft: temperature must be finite and > 0");
+    }
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return fail(SPECV_EINVAL, "markov_draft: workspace must be 256-byte aligned");
+    const size_t need = markov_draft_workspace_bytes(R, k, V, d_m);
+    if (ws_bytes < need)
+        return fail(SPECV_EINVAL, "markov_draft: workspace of %zu bytes, need %zu", ws_bytes, need);
+    if (dtype == SPECV_BF16 && (!aligned16(emb) || !aligned16(proj)))
+        return fail(SPECV_EINVAL, "markov_draft: emb and proj must be 16-byte aligned");
+
+    MarkovArgs a;
+    a.R = R; a.k = k; a.V = V; a.d_m = d_m;
+    a.S = (V + kSlice - 1) / kSlice;
+    a.mode = mode;
+    a.c = mode == SPECV_SAMPLE ? float(1.4426950408889634 / double(temperature)) : 1.f;
+    a.bk = backbone_logits; a.emb = emb; a.proj = proj; a.prev = prev_token;
+    a.uniforms = uniforms; a.tokens = draft_tokens_out; a.dl = draft_logits_out;
+    a.hdr = static_cast<WsHeader*>(ws);
+    a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + 256);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool vec4 = (V % 4) == 0 && (reinterpret_cast<uintptr_t>(backbone_logits) & 7u) == 0 &&
+                      (reinterpret_cast<uintptr_t>(draft_logits_out) & 7u) == 0;
+    const size_t lds = size_t(kSlice) * size_t(d_m * 2 + 16);
+    // The status word is cleared by position 0's logits kernel (which sets no
+    // bits) and set by position 0's pick kernel, which checks prev_token.
+    for (int i = 0; i < k; ++i) {
+        a.pos = i;
+        if (dtype == SPECV_BF16) {
+            if (vec4)
+                SPECV_LAUNCH("markov_logits", s, markov_logits_mfma<true><<<a.S, 256, lds, s>>>(a));
+            else
+                SPECV_LAUNCH("markov_logits", s, markov_logits_mfma<false><<<a.S, 256, lds, s>>>(a));
+            SPECV_LAUNCH("markov_pick", s, markov_pick<SPECV_BF16><<<(R + 3) / 4, 256, 0, s>>>(a));
+        } else {
+            const long items = long(R) * a.S;
+            SPECV_LAUNCH("markov_logits", s, markov_logits_fma<<<(items + 3) / 4, 256, 0, s>>>(a));
+            SPECV_LAUNCH("markov_pick", s, markov_pick<SPECV_F32><<<(R + 3) / 4, 256, 0, s>>>(a));
+        }
+    }
+    return SPECV_OK;
+}

@@ -1,0 +1,93 @@
+"""Device buffers for one workload and the calls of one speculative step.
+
+Holds the inputs of a workload in HBM and the outputs of each call, and strings
+the library calls together: (Markov draft) -> schedule -> verify. Marshalling
+only; all computation happens in libspecv's kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .workloads import Workload
+
+
+def to_device(a: np.ndarray, device) -> torch.Tensor:
+    if a.dtype == np.uint16:                         # bf16 bit patterns
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class DeviceStep:
+    def __init__(self, w: Workload, device="cuda"):
+        self.w = w
+        self.device = device
+        R, k, V = w.R, w.k, w.V
+        dev = lambda a: None if a is None else to_device(a, device)   # noqa: E731
+        self.target = dev(w.target)
+        self.draft_in = dev(w.draft)
+        self.tok_greedy = dev(w.tokens_greedy)
+        self.tok_sample = dev(w.tokens_sample)
+        self.z = dev(w.conf_logit)
+        self.T = dev(w.pos_temp)
+        self.tbl_b = dev(w.tbl_tokens)
+        self.tbl_t = dev(w.tbl_thr)
+        self.u_verify = dev(w.u_verify)
+        self.u_draft = dev(w.u_draft)
+        self.backbone = dev(w.backbone)
+        self.emb = dev(w.emb)
+        self.proj = dev(w.proj)
+        self.prev = dev(w.prev_token)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.lengths = torch.zeros(R, **i32)
+        self.tags = torch.zeros(R * (k + 1), 2, **i32)
+        self.cu_rows = torch.zeros(R + 1, **i32)
+        self.n_rows = torch.zeros(1, **i32)
+        self.survival = torch.zeros(R, k, dtype=torch.float64, device=device)
+        self.acc_len = torch.zeros(R, **i32)
+        self.out_tokens = torch.zeros(R, k + 1, **i32)
+        self.diag = torch.zeros(R * (k + 1), 4, dtype=torch.float32, device=device)
+        self.ws_verify = B.workspace(B.verify_workspace_bytes(B.SAMPLE, R, k, V), device)
+        if w.backbone is not None:
+            self.draft_tokens = torch.zeros(R, k, **i32)
+            self.draft_logits = torch.zeros(R, k, V, dtype=self.backbone.dtype, device=device)
+            self.ws_markov = B.workspace(B.markov_workspace_bytes(R, k, V, w.d_m), device)
+
+    # -- calls ---------------------------------------------------------------
+    def schedule(self, max_len=None, stream=None):
+        max_len = self.w.k if max_len is None else max_len
+        B.spec_schedule(self.z, self.T, self.tbl_b, self.tbl_t, max_len, self.lengths, self.tags, self.cu_rows,
+                        self.n_rows, self.survival, stream=stream)
+
+    def flatten(self, lengths: torch.Tensor, stream=None):
+        B.spec_flatten(lengths, self.w.k, self.tags, self.cu_rows, self.n_rows, stream=stream)
+
+    def markov(self, mode, stream=None):
+        B.markov_draft(mode, self.backbone, self.emb, self.proj, self.prev, self.w.tau, self.u_draft,
+                       self.draft_tokens, self.draft_logits, self.ws_markov, stream=stream)
+
+    def drafts(self, mode):
+        """(draft logits, draft tokens) the verifier uses for this workload and mode."""
+        if self.w.backbone is not None:
+            return self.draft_logits, self.draft_tokens
+        return self.draft_in, (self.tok_sample if mode == B.SAMPLE else self.tok_greedy)
+
+    def verify(self, mode, draft=None, tokens=None, diag=True, stream=None):
+        d, t = self.drafts(mode)
+        d = d if draft is None else draft
+        t = t if tokens is None else tokens
+        B.spec_verify(mode, self.target, d, t, self.tags, self.cu_rows, self.n_rows, self.w.tau, self.u_verify,
+                      self.acc_len, self.out_tokens, self.ws_verify, row_diag=self.diag if diag else None,
+                      stream=stream)
+
+    def step(self, mode, max_len=None, diag=False, stream=None):
+        """One pass of the hot path: (Markov draft,) schedule + flatten, verify."""
+        if self.w.backbone is not None:
+            self.markov(mode, stream=stream)
+        self.schedule(max_len, stream=stream)
+        self.verify(mode, diag=diag, stream=stream)
+
+    # -- readback ------------------------------------------------------------
+    def host(self, name) -> np.ndarray:
+        return getattr(self, name).cpu().numpy()

@@ -12,9 +12,10 @@ math/code/chat suites; those are not used here. The three "domain" profiles of
 the saturated workload stand in for them, keeping the pages' ordering of
 accepted length (math > code > chat).
 
-Every array comes from numpy's Philox bit generator keyed by the workload seed,
-drawn in the order written below, so a workload is reproducible bit for bit on
-any host. bf16 arrays are the round-to-nearest-even encoding of fp32 samples and
+Every array comes from numpy's Philox bit generator keyed by the workload seed:
+small arrays from one stream in the order written below, the large logit and
+weight arrays in blocks of rows, each block from its own stream keyed by
+(seed, array, block). A workload is reproducible bit for bit on any host. bf16 arrays are the round-to-nearest-even encoding of fp32 samples and
 are stored as their uint16 bit patterns.
 
 Random numbers the method itself consumes (the acceptance uniforms, the
@@ -23,7 +24,9 @@ inputs, float32 values k * 2**-24 in [0, 1).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
@@ -133,24 +136,42 @@ def _dec(x: np.ndarray, dtype: str) -> np.ndarray:
 def _sample_rows(g: np.random.Generator, logits32: np.ndarray, tau: float) -> np.ndarray:
     """Draw one index per row with probability proportional to exp(logit / tau).
 
-    Gumbel-max: argmax(logit / tau + G), G standard Gumbel. Rows are processed
-    in blocks to bound memory.
+    Gumbel-max: argmax(logit / tau + G), G standard Gumbel.
     """
     rows = logits32.reshape(-1, logits32.shape[-1])
     out = np.empty(rows.shape[0], dtype=np.int32)
-    inv_tau = np.float32(1.0 / tau)
-    blk = max(1, (1 << 24) // rows.shape[1])
-    for s in range(0, rows.shape[0], blk):
-        e = min(rows.shape[0], s + blk)
-        u = g.random((e - s, rows.shape[1]), dtype=np.float64)
+    inv_tau = 1.0 / tau
+    for i in range(rows.shape[0]):
+        u = g.random(rows.shape[1], dtype=np.float64)
         gum = -np.log(-np.log(np.maximum(u, 1e-300)))
-        out[s:e] = np.argmax(rows[s:e].astype(np.float64) * float(inv_tau) + gum, axis=1)
+        out[i] = np.argmax(rows[i].astype(np.float64) * inv_tau + gum)
     return out.reshape(logits32.shape[:-1])
 
 
 def _uniform24(g: np.random.Generator, shape) -> np.ndarray:
     # float32 multiples of 2**-24 in [0, 1)
     return (g.integers(0, 1 << 24, size=shape, dtype=np.int64).astype(np.float64) * 2.0 ** -24).astype(np.float32)
+
+
+# Large arrays are drawn in blocks of rows, each block from its own Philox
+# stream keyed by (workload seed, array id, block index), so the result does not
+# depend on how many threads fill it.
+_BLOCK = 4
+
+
+def _stream(seed: int, array_id: int, block: int) -> np.random.Generator:
+    return np.random.Generator(np.random.Philox(key=(int(seed) << 64) | (int(array_id) << 32) | int(block)))
+
+
+def _parallel_blocks(n: int, fn):
+    blocks = [(b, b * _BLOCK, min(n, (b + 1) * _BLOCK)) for b in range((n + _BLOCK - 1) // _BLOCK)]
+    workers = max(1, min(16, os.cpu_count() or 1, len(blocks)))
+    if workers == 1:
+        for blk in blocks:
+            fn(*blk)
+        return
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda blk: fn(*blk), blocks))
 
 
 def make(name: str, *, R: Optional[int] = None, V: Optional[int] = None) -> Workload:
@@ -161,12 +182,13 @@ def make(name: str, *, R: Optional[int] = None, V: Optional[int] = None) -> Work
         cfg["R"] = R
     if V is not None:
         cfg["V"] = V
-    R_, k, V_, dt, tau = cfg["R"], cfg["k"], cfg["V"], cfg["dtype"], cfg["tau"]
-    g = np.random.Generator(np.random.Philox(cfg["seed"]))
+    R_, k, V_, dt, tau, seed = cfg["R"], cfg["k"], cfg["V"], cfg["dtype"], cfg["tau"], cfg["seed"]
+    g = np.random.Generator(np.random.Philox(seed))
     tbl_b, tbl_thr = step_time_table(name)
     pos_temp = np.linspace(1.0, 2.0, k).astype(np.float32)
     w = dict(name=name, R=R_, k=k, V=V_, dtype=dt, tau=tau, tbl_tokens=tbl_b, tbl_thr=tbl_thr,
              pos_temp=pos_temp)
+    st = np.uint16 if dt == "bf16" else np.float32
 
     if name == "c0":
         tl32 = (2.0 * g.standard_normal((R_, k + 1, V_), dtype=np.float32)).astype(np.float32)
@@ -178,54 +200,62 @@ def make(name: str, *, R: Optional[int] = None, V: Optional[int] = None) -> Work
         z = (1.0 + g.standard_normal((R_, k), dtype=np.float32)).astype(np.float32)
         w.update(target=_enc(tl32, dt), backbone=_enc(bk32, dt), emb=emb, proj=proj,
                  prev_token=prev, conf_logit=z, d_m=cfg["d_m"])
-    elif name in ("c1", "c2"):
-        tl32 = (3.0 * g.standard_normal((R_, k + 1, V_), dtype=np.float32)).astype(np.float32)
-        target = _enc(tl32, dt)
-        d32 = tl32[:, :k] + np.float32(1.5) * g.standard_normal((R_, k, V_), dtype=np.float32)
-        del tl32
-        draft = _enc(d32, dt)
-        del d32
-        dd = _dec(draft, dt)
-        tok_g = np.argmax(dd, axis=-1).astype(np.int32)
-        tok_s = _sample_rows(g, dd, tau)
-        del dd
-        if name == "c1":
-            m = 0.9 * 0.85 ** np.arange(k)
-            m = np.broadcast_to(m, (R_, k))
+    elif name in ("c1", "c2", "c3"):
+        target = np.empty((R_, k + 1, V_), dtype=st)
+        draft = np.empty((R_, k, V_), dtype=st)
+        tok_g = np.empty((R_, k), dtype=np.int32)
+        tok_s = np.empty((R_, k), dtype=np.int32)
+        if name == "c3":
+            sig = (0.5 + 3.5 * np.arange(k) / (k - 1)).astype(np.float32)   # suffix decay
         else:
-            # math / code / chat thirds of the requests
-            dom = np.minimum((np.arange(R_) * 3) // max(R_, 1), 2)
-            means = np.array([0.92, 0.88, 0.75])[dom]
-            m = np.broadcast_to(means[:, None], (R_, k))
-        raw = g.beta(20.0 * m, 20.0 * (1.0 - m))
-        raw = np.clip(raw, 1e-12, 1.0 - 1e-12)
-        z = np.log(raw / (1.0 - raw)).astype(np.float32)
-        w.update(target=target, draft=draft, tokens_greedy=tok_g, tokens_sample=tok_s, conf_logit=z)
-    elif name == "c3":
-        tl32 = (3.0 * g.standard_normal((R_, k + 1, V_), dtype=np.float32)).astype(np.float32)
-        target = _enc(tl32, dt)
-        sig = (0.5 + 3.5 * np.arange(k) / (k - 1)).astype(np.float32)
-        d32 = tl32[:, :k] + sig[None, :, None] * g.standard_normal((R_, k, V_), dtype=np.float32)
-        del tl32
-        draft = _enc(d32, dt)
-        del d32
-        dd = _dec(draft, dt)
-        tok_s = _sample_rows(g, dd, tau)
-        tok_g = np.argmax(dd, axis=-1).astype(np.int32)
-        del dd
-        mu = np.linspace(1.5, -2.5, k)
-        z = (mu[None, :] + 0.5 * g.standard_normal((R_, k))).astype(np.float32)
+            sig = np.full(k, 1.5, dtype=np.float32)
+
+        def fill(b, lo, hi):
+            gb = _stream(seed, 1, b)
+            tl32 = np.float32(3.0) * gb.standard_normal((hi - lo, k + 1, V_), dtype=np.float32)
+            target[lo:hi] = _enc(tl32, dt)
+            d32 = tl32[:, :k] + sig[None, :, None] * gb.standard_normal((hi - lo, k, V_), dtype=np.float32)
+            draft[lo:hi] = _enc(d32, dt)
+            dd = _dec(draft[lo:hi], dt)
+            tok_g[lo:hi] = np.argmax(dd, axis=-1)
+            tok_s[lo:hi] = _sample_rows(gb, dd, tau)
+
+        _parallel_blocks(R_, fill)
+        if name == "c3":
+            mu = np.linspace(1.5, -2.5, k)
+            z = (mu[None, :] + 0.5 * g.standard_normal((R_, k))).astype(np.float32)
+        else:
+            if name == "c1":
+                m = np.broadcast_to(0.9 * 0.85 ** np.arange(k), (R_, k))
+            else:
+                # math / code / chat thirds of the requests
+                dom = np.minimum((np.arange(R_) * 3) // max(R_, 1), 2)
+                m = np.broadcast_to(np.array([0.92, 0.88, 0.75])[dom][:, None], (R_, k))
+            raw = np.clip(g.beta(20.0 * m, 20.0 * (1.0 - m)), 1e-12, 1.0 - 1e-12)
+            z = np.log(raw / (1.0 - raw)).astype(np.float32)
         w.update(target=target, draft=draft, tokens_greedy=tok_g, tokens_sample=tok_s, conf_logit=z)
     elif name == "c4":
         d_m = cfg["d_m"]
-        tl32 = (3.0 * g.standard_normal((R_, k + 1, V_), dtype=np.float32)).astype(np.float32)
-        target = _enc(tl32, dt)
-        bk32 = tl32[:, :k] + np.float32(1.5) * g.standard_normal((R_, k, V_), dtype=np.float32)
-        del tl32
-        backbone = _enc(bk32, dt)
-        del bk32
-        emb = _enc(g.standard_normal((V_, d_m), dtype=np.float32), dt)
-        proj = _enc(np.float32(0.5 / 16) * g.standard_normal((V_, d_m), dtype=np.float32), dt)
+        target = np.empty((R_, k + 1, V_), dtype=st)
+        backbone = np.empty((R_, k, V_), dtype=st)
+        emb = np.empty((V_, d_m), dtype=st)
+        proj = np.empty((V_, d_m), dtype=st)
+
+        def fill_rows(b, lo, hi):
+            gb = _stream(seed, 1, b)
+            tl32 = np.float32(3.0) * gb.standard_normal((hi - lo, k + 1, V_), dtype=np.float32)
+            target[lo:hi] = _enc(tl32, dt)
+            bk32 = tl32[:, :k] + np.float32(1.5) * gb.standard_normal((hi - lo, k, V_), dtype=np.float32)
+            backbone[lo:hi] = _enc(bk32, dt)
+
+        def fill_vocab(b, lo, hi):
+            lo, hi = lo * 1024, min(V_, hi * 1024)
+            gb = _stream(seed, 2, b)
+            emb[lo:hi] = _enc(gb.standard_normal((hi - lo, d_m), dtype=np.float32), dt)
+            proj[lo:hi] = _enc(np.float32(0.5 / 16) * gb.standard_normal((hi - lo, d_m), dtype=np.float32), dt)
+
+        _parallel_blocks(R_, fill_rows)
+        _parallel_blocks((V_ + 1023) // 1024, fill_vocab)
         prev = g.integers(0, V_, size=R_, dtype=np.int64).astype(np.int32)
         z = (1.0 + g.standard_normal((R_, k), dtype=np.float32)).astype(np.float32)
         w.update(target=target, backbone=backbone, emb=emb, proj=proj, prev_token=prev,
@@ -236,4 +266,3 @@ def make(name: str, *, R: Optional[int] = None, V: Optional[int] = None) -> Work
     w["u_verify"] = _uniform24(g, (R_, k + 1))
     w["u_draft"] = _uniform24(g, (R_, k))
     return Workload(**w)
-

@@ -1,0 +1,238 @@
+/*
+ * specv.h -- C ABI of the MI355X (gfx950) library for confidence-scheduled,
+ * flattened speculative verification (DSpark).
+ *
+ * The operations follow the DSpark pages, cited by title and section:
+ *   [P1] "刚融完500亿创始人亲自下场写代码DeepSeek不卷参数专治AI“嘴慢”"
+ *        (mooersco.com), sections "1. 半自回归生成", "2. 置信度调度验证" and the
+ *        engineering table under "不止是算法更是“工业级”的系统魔改".
+ *   [P2] "DSpark 的 661% 提速，是真突破还是数字游戏？" (new-universe.cn),
+ *        sections 一, 3.1 and 3.2.
+ *   [P3] "DeepSeek服务器不再卡顿！DSpark加速60% - 80%，推理成本降40%"
+ *        (qwbw.cn), section "DSpark的神奇之处".
+ *   [P4] aibuzzwire.news, "deepseek-dspark-speculative-decoding-85-percent-
+ *        faster-llm-inference", section "置信度计划、负载感知验证".
+ *
+ * Conventions for every call
+ *   - Array arguments are DEVICE pointers owned by the caller; the library
+ *     never keeps them after the call returns.
+ *   - A call validates its scalar arguments and pointers on the host, then
+ *     only enqueues kernels on `stream` (a hipStream_t; NULL is the null
+ *     stream) and returns. It never allocates, frees or synchronises.
+ *   - Return value: SPECV_OK, or a negative code; on SPECV_EINVAL and
+ *     SPECV_EUNSUPPORTED nothing was enqueued. specv_last_error() gives a
+ *     message (per host thread).
+ *   - Data errors found on the device (a draft token outside [0, V), a tag that
+ *     disagrees with cu_rows) never fault: the offending row is treated as
+ *     rejected and a bit is set in the workspace status word, readable with
+ *     specv_read_status().
+ *   - Calls that share a workspace must not run concurrently.
+ *   - Row-major layouts throughout. "bf16" arrays hold IEEE bfloat16 values
+ *     (2 bytes each); "f32" arrays hold float.
+ */
+#ifndef SPECV_H
+#define SPECV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* specv_stream; /* a hipStream_t */
+
+enum {
+    SPECV_OK = 0,
+    SPECV_EINVAL = -1,        /* bad argument; nothing enqueued */
+    SPECV_EUNSUPPORTED = -2,  /* valid but not supported (dtype, sizes); nothing enqueued */
+    SPECV_EDEVICE = -3        /* a HIP launch or runtime call failed */
+};
+
+enum { SPECV_BF16 = 0, SPECV_F32 = 1 };       /* logit storage type */
+enum { SPECV_GREEDY = 0, SPECV_SAMPLE = 1 };  /* acceptance mode */
+
+/* status-word bits (specv_read_status) */
+enum {
+    SPECV_STATUS_BAD_TOKEN = 1u, /* a draft token outside [0, V) */
+    SPECV_STATUS_BAD_TAG = 2u    /* tags[] disagrees with cu_rows[] */
+};
+
+/* Limits of the scheduler: all candidate keys of one call are sorted in the
+ * local data share of one workgroup. */
+#define SPECV_MAX_K 32
+#define SPECV_MAX_SCHED_ITEMS 16384 /* R * k */
+
+/* ------------------------------------------------------------------------ */
+/* spec_schedule                                                             */
+/* ------------------------------------------------------------------------ */
+/*
+ * Calibrate confidences, turn them into survival probabilities, choose each
+ * request's verification length with the hardware-aware prefix scheduler, and
+ * flatten the chosen rows ([P1] "2. 置信度调度验证"; [P2] 3.2; [P3] "DSpark的神奇之处";
+ * [P4] "置信度计划、负载感知验证"; flattening: [P1] engineering table, row
+ * "内核利用率暴跌").
+ *
+ *   c[r,i] = 1 / (1 + exp(-z[r,i] / T[i]))          temporal temperature scaling
+ *   S[r,i] = c[r,0] * ... * c[r,i]                    survival (float64)
+ *   Q[r,i] = floor(S[r,i] * 2^32 + 0.5)               integer key
+ *   Candidates (r,i), i < min(k, max_len), sorted by Q descending, then i, then r.
+ *   For M = 0 .. #candidates, with P(M) the sum of the first M keys and Bt = R + M:
+ *     G(M) = (R * 2^32 + P(M)) * thr(Bt) / Bt        (float64, no fused ops)
+ *   thr(Bt) interpolates the table linearly; below tbl_tokens[0] it is
+ *   tbl_thr[0] * Bt / tbl_tokens[0]; at or above the last point it is the last
+ *   value. M* = the smallest M with the largest G; L_r = the number of request
+ *   r's candidates among the first M*. max_len < 0 forces L_r = k.
+ *   Flatten: rows (r, j), j = 0..L_r, request-major; cu_rows[r] = first row of r;
+ *   n_rows = cu_rows[R] = sum(L_r + 1). Row (r, L_r) carries the bonus token.
+ *
+ * Arguments (device pointers unless noted)
+ *   R, k          requests and draft block size (host ints): 1 <= k <= 32,
+ *                 R >= 1, R*k <= 16384
+ *   conf_logit    f32 [R,k]   raw confidence-head logits z
+ *   pos_temp      f32 [k]     temperatures T_i > 0 (not checked on the device)
+ *   tbl_tokens    i32 [n_tbl] batch tokens, strictly increasing, > 0
+ *   tbl_thr       f64 [n_tbl] throughput at those batch sizes, > 0
+ *   n_tbl         host int, 1..64
+ *   max_len       host int, -1 (verify all k) or 0..k
+ *   len_out       i32 [R]           L_r
+ *   tags_out      i32 [R*(k+1),2]   (request, position) per flattened row;
+ *                                   rows >= n_rows are left untouched
+ *   cu_rows_out   i32 [R+1]
+ *   n_rows_out    i32 [1]
+ *   survival_out  f64 [R,k] or NULL
+ * Errors: SPECV_EINVAL for NULL required pointers or out-of-range sizes.
+ */
+int spec_schedule(int R, int k, const float* conf_logit, const float* pos_temp,
+                  const int32_t* tbl_tokens, const double* tbl_thr, int n_tbl, int max_len,
+                  int32_t* len_out, int32_t* tags_out, int32_t* cu_rows_out,
+                  int32_t* n_rows_out, double* survival_out, specv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* spec_flatten                                                              */
+/* ------------------------------------------------------------------------ */
+/*
+ * Flatten given verification lengths (e.g. decided by the caller one or two
+ * rounds ahead) into the tagged varlen batch that spec_verify consumes
+ * ([P1] engineering table, row "内核利用率暴跌"). Same outputs as the
+ * flattening part of spec_schedule. Lengths outside [0, k] are clamped.
+ *   R >= 1, 1 <= k <= 32 (host ints); len_in i32 [R]; tags_out i32 [R*(k+1),2];
+ *   cu_rows_out i32 [R+1]; n_rows_out i32 [1].
+ */
+int spec_flatten(int R, int k, const int32_t* len_in, int32_t* tags_out,
+                 int32_t* cu_rows_out, int32_t* n_rows_out, specv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* spec_verify                                                               */
+/* ------------------------------------------------------------------------ */
+/*
+ * The exact acceptance rule over the flattened batch ([P2] 一: verified tokens
+ * are kept and the first divergence is resampled; [P3] "DSpark的神奇之处":
+ * rejection sampling keeps the target's distribution; [P4] opening: the longest
+ * correct prefix is accepted).
+ *
+ * For request r with L_r = cu_rows[r+1] - cu_rows[r] - 1, verified rows
+ * j < L_r and the bonus row j = L_r:
+ *   greedy:   g_j = argmax_v target[r,j,v] (lowest index on ties);
+ *             keep x_j iff g_j == x_j.
+ *   sampling: p_j = softmax(target[r,j,:] / tau), q_j = softmax(draft[r,j,:] / tau);
+ *             keep x_j iff u[r,j] < min(1, p_j(x_j) / q_j(x_j)).
+ *   a_r = first j < L_r not kept, else L_r.
+ *   out_tokens[r,0..a_r-1] = x[r,0..a_r-1]; out_tokens[r,a_r] =
+ *     greedy:   g_{a_r};
+ *     sampling: inverse-CDF draw with u[r,k] from max(0, p - q) at row a_r when
+ *               a_r < L_r (from p when that residual has no mass), else from
+ *               p_{L_r}: the smallest v with w_0 + .. + w_v > u * sum(w).
+ *   out_tokens[r, a_r+1 .. k] = -1; accepted_len[r] = a_r.
+ * Arithmetic is float32 (softmax statistics in base 2 with a pre-scaled
+ * log2(e)/tau); greedy decisions are exact comparisons.
+ *
+ * Arguments (device pointers unless noted)
+ *   mode, dtype     SPECV_GREEDY / SPECV_SAMPLE, SPECV_BF16 / SPECV_F32
+ *   R, k, V         host ints: R >= 1, 1 <= k <= 32, V >= 1
+ *   target_logits   [R,k+1,V] in dtype
+ *   draft_logits    [R,k,V] in dtype (sampling); ignored and may be NULL in greedy
+ *   draft_tokens    i32 [R,k]
+ *   tags, cu_rows, n_rows   the flattened batch (spec_schedule / spec_flatten)
+ *   temperature     host float tau > 0 (sampling); ignored in greedy
+ *   uniforms        f32 [R,k+1] in [0,1): column j < k decides row j, column k
+ *                   drives the resample / bonus draw (sampling; may be NULL in greedy)
+ *   accepted_len_out i32 [R]
+ *   out_tokens       i32 [R,k+1]
+ *   row_diag         f32 [R*(k+1),4] or NULL. Verified rows: sampling
+ *                    {p(x), q(x), p(x)/q(x), kept}, greedy {argmax, max logit, 0,
+ *                    kept}. Bonus rows: sampling {0,0,0,-1}, greedy {argmax,
+ *                    max logit, 0, -1}.
+ *   ws, ws_bytes     workspace of at least spec_verify_workspace_bytes(mode,R,k,V)
+ *                    bytes, 256-byte aligned; contents need no initialisation
+ * Errors: SPECV_EINVAL (NULL pointers, sizes, tau, small workspace),
+ *         SPECV_EUNSUPPORTED (dtype), SPECV_EDEVICE (launch failure).
+ */
+size_t spec_verify_workspace_bytes(int mode, int R, int k, int V);
+int spec_verify(int mode, int dtype, int R, int k, int V, const void* target_logits,
+                const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
+                const int32_t* cu_rows, const int32_t* n_rows, float temperature,
+                const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
+                float* row_diag, void* ws, size_t ws_bytes, specv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* markov_draft                                                              */
+/* ------------------------------------------------------------------------ */
+/*
+ * The Markov head of the semi-autoregressive drafter ([P1] "1. 半自回归生成":
+ * a parallel backbone plus a light sequential module injecting prefix
+ * information token by token, by default a Markov head that depends only on the
+ * previous token; [P2] 3.1). For i = 0..k-1, with x_{-1} = prev_token[r]:
+ *   dl[r,i,:] = round(backbone[r,i,:] + emb[x_{i-1},:] . proj^T)  (float32
+ *               accumulation; one round-to-nearest-even to dtype)
+ *   x_i = argmax dl[r,i,:] (greedy, lowest index) or the inverse-CDF draw from
+ *         softmax(dl[r,i,:] / tau) with uniforms[r,i] (sampling).
+ * The rounded logits are written out: they are the draft distribution the
+ * verifier must use.
+ *
+ * Arguments (device pointers unless noted)
+ *   mode, dtype     as spec_verify
+ *   R, k, V, d_m    host ints: R >= 1, 1 <= k <= 32, V >= 1, d_m >= 1
+ *                   (bf16: d_m % 32 == 0 and d_m <= 480)
+ *   backbone_logits [R,k,V] dtype
+ *   emb             [V,d_m] dtype   previous-token embedding
+ *   proj            [V,d_m] dtype   projection, one d_m row per vocabulary entry
+ *   prev_token      i32 [R]          last committed token
+ *   temperature     host float > 0 (sampling)
+ *   uniforms        f32 [R,k] (sampling; may be NULL in greedy)
+ *   draft_tokens_out i32 [R,k];  draft_logits_out [R,k,V] dtype
+ *   ws, ws_bytes    at least markov_draft_workspace_bytes(R,k,V,d_m)
+ * Errors: as spec_verify.
+ */
+size_t markov_draft_workspace_bytes(int R, int k, int V, int d_m);
+int markov_draft(int mode, int dtype, int R, int k, int V, int d_m,
+                 const void* backbone_logits, const void* emb, const void* proj,
+                 const int32_t* prev_token, float temperature, const float* uniforms,
+                 int32_t* draft_tokens_out, void* draft_logits_out, void* ws, size_t ws_bytes,
+                 specv_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* diagnostics                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* specv_last_error(void);
+
+/* Read the workspace status word of the last spec_verify / markov_draft call
+ * that used `ws` (synchronises `stream`). */
+int specv_read_status(const void* ws, specv_stream stream, uint32_t* status_out);
+
+/* Per-kernel timing with HIP events recorded on the launch stream around each
+ * kernel the library enqueues. Off by default; meant for benchmarks. Not
+ * thread-safe. specv_timing_read synchronises the recorded events and returns
+ * the number of launches and their summed duration for kernels whose name
+ * starts with `prefix`. */
+int specv_timing_enable(int on);
+int specv_timing_reset(void);
+int specv_timing_read(const char* prefix, int* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECV_H */
