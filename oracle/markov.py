@@ -29,12 +29,18 @@ import numpy as np
 from . import numerics
 
 
+def head_exact(bk_row: np.ndarray, emb: np.ndarray, proj: np.ndarray, prev: np.ndarray,
+               dtype: str) -> np.ndarray:
+    """bk + E[prev] . P^T for one position, in float64 before any rounding."""
+    e = numerics.decode(emb, dtype)[np.asarray(prev, dtype=np.int64)]      # [R, d_m]
+    p = numerics.decode(proj, dtype)                                       # [V, d_m]
+    return numerics.decode(bk_row, dtype) + e @ p.T
+
+
 def head_logits(bk_row: np.ndarray, emb: np.ndarray, proj: np.ndarray, prev: np.ndarray,
                 dtype: str) -> np.ndarray:
     """Rounded draft logits for one position: round(bk + E[prev] . P^T); stored type."""
-    e = numerics.decode(emb, dtype)[np.asarray(prev, dtype=np.int64)]      # [R, d_m]
-    p = numerics.decode(proj, dtype)                                       # [V, d_m]
-    exact = numerics.decode(bk_row, dtype) + e @ p.T                       # float64
+    exact = head_exact(bk_row, emb, proj, prev, dtype)
     if dtype == "bf16":
         return numerics.round_bf16(exact)
     return numerics.round_f32(exact)
