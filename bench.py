@@ -30,8 +30,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified draft tokens/s at V=151936, k=5, 256 req; achieved HBM GB/s % peak"
 HBM_PEAK = 8.0e12
-DOMINANT = "verify_partials"
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_partials_c2_traffic.txt")
+DOMINANT = "verify_stream"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_stream_c2_traffic.txt")
 
 
 def parse():
@@ -105,8 +105,7 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
         d.step(mode_c, max_len)
     torch.cuda.synchronize()
     kern = {}
-    for name in ("markov_logits", "markov_pick", "schedule", "verify_partials", "verify_finalize",
-                 "resample_mass", "resample_pick"):
+    for name in ("markov_logits", "markov_pick", "schedule", "verify_stream", "verify_decide", "verify_residual"):
         n, tot = B.timing_read(name)
         if n:
             kern[name] = dict(launches_per_step=n / steps, avg_us=1000.0 * tot / n)
@@ -119,7 +118,7 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
     dom = kern.get(DOMINANT)
     achieved = nbytes / (dom["avg_us"] * 1e-6) if dom else None
     verify_us = sum(kern[k]["avg_us"] * kern[k]["launches_per_step"]
-                    for k in ("verify_partials", "verify_finalize", "resample_mass", "resample_pick") if k in kern)
+                    for k in ("verify_stream", "verify_decide", "verify_residual") if k in kern)
     return dict(mode=mode, max_len=max_len, ms_per_step=ms_step, N=N, rows=int(d.host("n_rows")[0]),
                 tokens_per_s=N / (ms_step * 1e-3), verify_us=verify_us,
                 verify_tokens_per_s=N / (verify_us * 1e-6) if verify_us else None,

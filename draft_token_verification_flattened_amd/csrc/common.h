@@ -10,10 +10,14 @@ namespace specv {
 
 constexpr int kWave = 64;   // CDNA wavefront width
 
-// Workspace header: one status word, padded to 256 bytes.
+// Workspace header, padded to 256 bytes. `status` holds the data-error bits of
+// the last completed call (specv_read_status reads this first word); `pending`
+// and `done` are scratch of a running call and are zero between calls.
 struct WsHeader {
     uint32_t status;
-    uint32_t pad[63];
+    uint32_t pending;
+    uint32_t done;
+    uint32_t pad[61];
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -98,6 +102,61 @@ __device__ __forceinline__ void wave_lse(float& m, float& s) {
         float s2 = __shfl_xor(s, o, kWave);
         lse_merge(m, s, m2, s2);
     }
+}
+
+// ---- DPP wavefront reductions: quad permutes, row mirrors and the two row
+// broadcasts leave the reduction of all 64 lanes in lane 63, which is then read
+// into a scalar. Every lane of the wave must be active.
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+    return __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(old), __float_as_int(v)));
+}
+__device__ __forceinline__ float lane63(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Sum over the wave (fixed order, identical on every call with the same data).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_f<0xb1>(0.f, v);          // quad_perm [1,0,3,2]
+    v += dpp_f<0x4e>(0.f, v);          // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(0.f, v);         // row_half_mirror
+    v += dpp_f<0x140>(0.f, v);         // row_mirror
+    v += dpp_f<0x142, 0xa>(0.f, v);    // row_bcast:15 into rows 1 and 3
+    v += dpp_f<0x143, 0xc>(0.f, v);    // row_bcast:31 into rows 2 and 3
+    return lane63(v);
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmaxf(v, dpp_f<0xb1>(v, v));
+    v = fmaxf(v, dpp_f<0x4e>(v, v));
+    v = fmaxf(v, dpp_f<0x141>(v, v));
+    v = fmaxf(v, dpp_f<0x140>(v, v));
+    v = fmaxf(v, dpp_f<0x142, 0xa>(v, v));
+    v = fmaxf(v, dpp_f<0x143, 0xc>(v, v));
+    return lane63(v);
+}
+
+// (value, index) maximum over the wave, larger value first, then lower index.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ void argmax_dpp_step(float& v, int& i) {
+    const float v2 = dpp_f<CTRL, ROW_MASK>(v, v);
+    const int i2 = dpp_i<CTRL, ROW_MASK>(i, i);
+    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+__device__ __forceinline__ void wave_argmax_dpp(float& v, int& i) {
+    argmax_dpp_step<0xb1>(v, i);
+    argmax_dpp_step<0x4e>(v, i);
+    argmax_dpp_step<0x141>(v, i);
+    argmax_dpp_step<0x140>(v, i);
+    argmax_dpp_step<0x142, 0xa>(v, i);
+    argmax_dpp_step<0x143, 0xc>(v, i);
+    v = lane63(v);
+    i = __builtin_amdgcn_readlane(i, 63);
 }
 
 // Inclusive prefix sum across the wave in lane order.

@@ -7,19 +7,28 @@
 // 还是数字游戏？", section 一); rejection sampling keeps the target's distribution
 // ("DeepSeek服务器不再卡顿！…", section "DSpark的神奇之处").
 //
-// Four kernels on one stream:
-//   verify_partials   one wavefront per (row slot, vocabulary chunk): streams a
-//                     2048-logit chunk of a target (or draft) row with 16-byte
-//                     loads and writes a partial: (max, index) in greedy mode,
-//                     the base-2 online softmax state (m, s) in sampling mode.
-//                     All HBM traffic of the step is here.
-//   verify_finalize   one wavefront per request: merges chunk partials per row,
-//                     decides every verified row, finds the first rejection
-//                     a_r, writes accepted lengths and tokens (greedy: final).
-//   resample_mass     sampling only; one wavefront per (request, chunk) of the
-//                     rejected row: chunk mass of max(0, p - q).
-//   resample_pick     sampling only; one wavefront per request: chunk prefix
-//                     sums, then an in-chunk scan for the inverse-CDF draw.
+// Kernels, in stream order:
+//   verify_stream    the HBM stream. Work item = (flattened row t, chunk of
+//                    64 * kNV 16-byte vectors); the n_rows * C items are split
+//                    into one contiguous range per wavefront of a persistent
+//                    grid. Each wavefront loads item i+1 (target and, for a
+//                    verified row in sampling mode, draft) while it reduces item
+//                    i to the chunk's partial: (max, lowest index) in greedy
+//                    mode; in sampling mode the base-2 softmax state (M, S) of p
+//                    and of q, with M the chunk maximum of logit * log2(e) / tau
+//                    and S the sum of exp2(logit * log2(e) / tau - M). Wave
+//                    reductions use DPP. No atomics and no waits: all of the
+//                    step's logit traffic is here.
+//   verify_decide    one workgroup per request: merges each row's chunk
+//                    partials, decides every verified row, finds the first
+//                    rejection a_r and writes the accepted length and tokens.
+//                    Greedy: complete. Sampling with every row kept: draws the
+//                    bonus token from p of row L_r (chunk masses from the
+//                    partials, then an in-order scan of one chunk).
+//   verify_residual  sampling, requests with a_r < L_r: re-reads the rejected
+//                    row pair chunk by chunk for the masses of max(0, p - q); the
+//                    last chunk of a request to finish (device-scope counter)
+//                    draws the token by the inverse CDF.
 #include <climits>
 
 #include "common.h"
@@ -27,12 +36,20 @@
 
 namespace specv {
 
-constexpr int kChunk = 2048;        // logits per (row, chunk) work item
-constexpr int kWavesPerBlock = 4;   // 256-thread workgroups
+constexpr int kThreads = 256;               // 4 wavefronts per workgroup
+constexpr int kWaves = kThreads / kWave;
+constexpr int kNV = 4;                      // 16-byte vectors per lane per tensor per item
+constexpr int kChunkVecs = kWave * kNV;     // vectors per chunk
+
+__host__ __device__ constexpr int chunk_elems(int vec) { return kChunkVecs * vec; }
+static int chunk_len(int dtype) { return chunk_elems(dtype == SPECV_BF16 ? 8 : 4); }
+
+struct RowRec {                             // one per flattened row (sampling)
+    float ax, bx;                           // target / draft logit at the draft token
+};
 
 struct VerifyArgs {
-    int R, k, V, C;                 // C = chunks per row
-    int Bmax;                       // R * (k + 1)
+    int R, k, V, C, CH, Bmax;               // C chunks of CH logits per row
     const void* target;
     const void* draft;
     const int32_t* tokens;
@@ -40,405 +57,595 @@ struct VerifyArgs {
     const int32_t* cu_rows;
     const int32_t* n_rows;
     const float* uniforms;
-    float c;                        // log2(e) / tau
+    float c;                                // log2(e) / tau
     int32_t* acc_len;
     int32_t* out_tokens;
     float* diag;
     WsHeader* hdr;
-    float2* part;                   // [slots * C]; slot = t (greedy) or 2t + tensor
-    float4* rs_stat;                // [R] {m_p, s_p, m_q, s_q} of the resample row
-    int4* rs_row;                   // [R] {row t, a_r, kind (0 residual, 1 bonus), 0}
-    float* mass;                    // [R * C]
+    float4* part;                           // [Bmax * C] sampling (m_p, s_p, m_q, s_q); greedy (v, idx, -, -)
+    RowRec* rec;                            // [Bmax]
+    float4* rs_stat;                        // [R] (Mp, Zp, Mq, Zq) of the resample row
+    int4* rs_row;                           // [R] (row t, a_r, kind: 0 residual / 1 done, 0)
+    float* mass;                            // [R * C] residual chunk masses
+    int* rctr;                              // [R] residual chunks finished (zero between calls)
 };
 
 struct Layout {
-    size_t part, rs_stat, rs_row, mass, total;
+    size_t part, rec, rs_stat, rs_row, mass, rctr, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-static Layout ws_layout(int mode, int R, int k, int V) {
+static Layout ws_layout(int R, int k, int V) {
     Layout l;
-    size_t C = (size_t(V) + kChunk - 1) / kChunk;
-    size_t slots = size_t(mode == SPECV_SAMPLE ? 2 : 1) * size_t(R) * size_t(k + 1);
+    const size_t C = (size_t(V) + chunk_elems(4) - 1) / chunk_elems(4);   // fp32 has the most chunks
+    const size_t B = size_t(R) * size_t(k + 1);
     size_t off = align256(sizeof(WsHeader));
-    l.part = off;
-    off = align256(off + slots * C * sizeof(float2));
-    l.rs_stat = off;
-    off = align256(off + size_t(R) * sizeof(float4));
-    l.rs_row = off;
-    off = align256(off + size_t(R) * sizeof(int4));
-    l.mass = off;
-    off = align256(off + size_t(R) * C * sizeof(float));
+    l.part = off;    off = align256(off + B * C * sizeof(float4));
+    l.rec = off;     off = align256(off + B * sizeof(RowRec));
+    l.rs_stat = off; off = align256(off + size_t(R) * sizeof(float4));
+    l.rs_row = off;  off = align256(off + size_t(R) * sizeof(int4));
+    l.mass = off;    off = align256(off + size_t(R) * C * sizeof(float));
+    l.rctr = off;    off = align256(off + size_t(R) * sizeof(int));
     l.total = off;
     return l;
 }
 
 // ---------------------------------------------------------------------------
-// pass 1: per (row slot, chunk) partials
+// Device-coherent exchange of the residual chunk masses inside verify_residual:
+// relaxed device-scope atomics, which gfx950 performs at the device-coherent
+// level (stores write through, loads bypass the per-XCD L2). A writer waits
+// for its stores to complete before it bumps the request's counter; the reader
+// loads only after the counter says every chunk is in.
 // ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void put(float* p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get(const float* p) {
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)),
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void publish() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ int bump(int* p) {
+    const int old = __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return old;
+}
+
+// ---------------------------------------------------------------------------
+// verify_stream
+// ---------------------------------------------------------------------------
+
+// Raw logits of one item for one lane: kNV 16-byte vectors (VEC) or kNV * kVec
+// scalars (unaligned rows, or V not a multiple of the vector width).
+template <int DT, bool VEC>
+struct Raw {
+    using LT = Logit<DT>;
+    using T = typename LT::T;
+    static constexpr int kVec = LT::kVec;
+    static constexpr int kE = kNV * kVec;           // logits per lane per item
+    uint4 v[VEC ? kNV : 1];
+    float s[VEC ? 1 : kE];
+
+    // Lane's element q of a chunk sits at chunk offset
+    // (q / kVec * 64 + lane) * kVec + q % kVec in both layouts; for fixed q the
+    // offsets increase with the lane, for a fixed lane they increase with q.
+    __device__ __forceinline__ static int offset(int q, int lane) {
+        return ((q / kVec) * kWave + lane) * kVec + q % kVec;
+    }
+
+    __device__ __forceinline__ void load(const T* row, int beg, int V, int lane) {
+        if constexpr (VEC) {
+            const uint4* vr = reinterpret_cast<const uint4*>(row);
+            const int nv = V / kVec, b = beg / kVec;
+#pragma unroll
+            for (int u = 0; u < kNV; ++u) {
+                const int i = b + u * kWave + lane;
+                v[u] = i < nv ? vr[i] : make_uint4(0u, 0u, 0u, 0u);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < kE; ++q) {
+                const int e = beg + offset(q, lane);
+                s[q] = e < V ? LT::load1(row + e) : -INFINITY;
+            }
+        }
+    }
+
+    // Widen to float; elements past the end of the row become -inf.
+    __device__ __forceinline__ void widen(int beg, int V, int lane, float (&x)[kE]) const {
+        if constexpr (VEC) {
+            const int nv = V / kVec, b = beg / kVec;
+#pragma unroll
+            for (int u = 0; u < kNV; ++u) {
+                float t[kVec];
+                LT::unpack(v[u], t);
+                const bool ok = b + u * kWave + lane < nv;
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) x[u * kVec + e] = ok ? t[e] : -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < kE; ++q) x[q] = s[q];
+        }
+    }
+};
+
+// Base-2 softmax state of one chunk of x * c over the wave: M = max, S = sum
+// of exp2(x * c - M); (-inf, 0) for a chunk of padding only.
+template <int E>
+__device__ __forceinline__ float2 chunk_softmax(const float (&x)[E], float c) {
+    float mx = x[0];
+#pragma unroll
+    for (int q = 1; q < E; ++q) mx = fmaxf(mx, x[q]);
+    const float M = wave_max_dpp(mx) * c;
+    if (M == -INFINITY) return make_float2(-INFINITY, 0.f);
+    float acc = 0.f;
+#pragma unroll
+    for (int q = 0; q < E; ++q) acc += __builtin_amdgcn_exp2f(fmaf(x[q], c, -M));
+    return make_float2(M, wave_sum_dpp(acc));
+}
+
+struct RowInfo {
+    int t, r, j;
+    bool ok, verified;
+    int x;
+};
+
+__device__ __forceinline__ RowInfo row_info(const VerifyArgs& a, int t, bool need_x) {
+    RowInfo ri;
+    ri.t = t;
+    ri.r = a.tags[2 * t];
+    ri.j = a.tags[2 * t + 1];
+    ri.ok = ri.r >= 0 && ri.r < a.R && ri.j >= 0 && ri.j <= a.k;
+    ri.verified = false;
+    ri.x = -1;
+    if (ri.ok && need_x) {
+        const int L = a.cu_rows[ri.r + 1] - a.cu_rows[ri.r] - 1;
+        ri.verified = ri.j < L && ri.j < a.k;
+        if (ri.verified) ri.x = a.tokens[long(ri.r) * a.k + ri.j];
+    }
+    return ri;
+}
 
 template <int DT, int MODE, bool VEC>
-__global__ __launch_bounds__(256) void verify_partials(VerifyArgs a) {
-    using LT = Logit<DT>;
-    using T = typename LT::T;
-    constexpr int kV = LT::kVec;
-    constexpr int kU = kChunk / (kWave * kV);      // 16-byte loads per lane
-
+__global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
+    using RW = Raw<DT, VEC>;
+    using T = typename RW::T;
+    constexpr int E = RW::kE;
+    constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
     const int lane = threadIdx.x & (kWave - 1);
-    const long item = long(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr->status = 0u;   // this kernel sets no bits
-    const int chunk = int(item % a.C);
-    const long slot = item / a.C;
-    const int t = MODE == SPECV_SAMPLE ? int(slot >> 1) : int(slot);
-    const int tensor = MODE == SPECV_SAMPLE ? int(slot & 1) : 0;
-    if (t >= a.Bmax || t >= *a.n_rows) return;
-    const int r = a.tags[2 * t], j = a.tags[2 * t + 1];
-    if (r < 0 || r >= a.R || j < 0 || j > a.k) return;            // reported by finalize
-    if (tensor == 1) {
-        const int L = a.cu_rows[r + 1] - a.cu_rows[r] - 1;
-        if (j >= L || j >= a.k) return;                            // bonus rows have no draft
-    }
-    const T* row = tensor == 0
-        ? static_cast<const T*>(a.target) + (long(r) * (a.k + 1) + j) * long(a.V)
-        : static_cast<const T*>(a.draft) + (long(r) * a.k + j) * long(a.V);
-    const int beg = chunk * kChunk;
-    const int end = min(a.V, beg + kChunk);
+    const long nw = long(gridDim.x) * kWaves;
+    const long w = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr->status = 0u;   // later kernels of this call set bits
+    const int nrows = min(*a.n_rows, a.Bmax);
+    const long items = long(max(nrows, 0)) * a.C;
+    long i = items * w / nw;
+    const long iend = items * (w + 1) / nw;
+    if (i >= iend) return;
 
-    float2 res;
-    if (MODE == SPECV_GREEDY) {
-        float bv = -INFINITY;
-        int bi = INT_MAX;
-        if (VEC) {
-            const uint4* vrow = reinterpret_cast<const uint4*>(row);
-            uint4 buf[kU];
-            const int v0 = beg / kV, v1 = end / kV;
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                int v = v0 + u * kWave + lane;
-                if (v < v1) buf[u] = vrow[v];
-            }
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                int v = v0 + u * kWave + lane;
-                if (v < v1) {
-                    float x[kV];
-                    LT::unpack(buf[u], x);
-#pragma unroll
-                    for (int e = 0; e < kV; ++e)
-                        if (bi == INT_MAX || x[e] > bv) { bv = x[e]; bi = v * kV + e; }
+    const float c = a.c;
+    auto trow_of = [&](const RowInfo& q) {
+        return static_cast<const T*>(a.target) + (long(q.r) * (a.k + 1) + q.j) * long(a.V);
+    };
+    auto drow_of = [&](const RowInfo& q) {
+        return static_cast<const T*>(a.draft) + (long(q.r) * a.k + q.j) * long(a.V);
+    };
+    auto issue = [&](RW& bt, RW& bd, const RowInfo& q, long it) {
+        if (!q.ok) return;
+        const int beg = int(it % a.C) * a.CH;
+        bt.load(trow_of(q), beg, a.V, lane);
+        if (SAMPLE && q.verified) bd.load(drow_of(q), beg, a.V, lane);
+    };
+
+    RowInfo ri = row_info(a, int(i / a.C), SAMPLE);
+
+    // Item i from (bt, bd) while item i+1 is loaded into (nt, nd).
+    auto step = [&](RW& bt, RW& bd, RW& nt, RW& nd) {
+        const long nx = i + 1;
+        const bool more = nx < iend;
+        RowInfo rn = ri;
+        if (more && nx % a.C == 0) rn = row_info(a, int(nx / a.C), SAMPLE);
+        if (more) issue(nt, nd, rn, nx);
+
+        const int ch = int(i % a.C);
+        const int beg = ch * a.CH;
+        float4 outp = SAMPLE ? make_float4(-INFINITY, 0.f, -INFINITY, 0.f)
+                             : make_float4(-INFINITY, __int_as_float(INT_MAX), 0.f, 0.f);
+        if (ri.ok) {
+            float x[E];
+            bt.widen(beg, a.V, lane, x);
+            if (SAMPLE) {
+                const float2 P = chunk_softmax(x, c);
+                outp.x = P.x; outp.y = P.y;
+                if (ri.verified) {
+                    float y[E];
+                    bd.widen(beg, a.V, lane, y);
+                    const float2 Q = chunk_softmax(y, c);
+                    outp.z = Q.x; outp.w = Q.y;
+                    if (lane == 0 && ri.x >= beg && ri.x < beg + a.CH && ri.x < a.V) {
+                        a.rec[ri.t].ax = Logit<DT>::load1(trow_of(ri) + ri.x);
+                        a.rec[ri.t].bx = Logit<DT>::load1(drow_of(ri) + ri.x);
+                    }
                 }
-            }
-        } else {
-            for (int e = beg + lane; e < end; e += kWave) {
-                float x = LT::load1(row + e);
-                if (bi == INT_MAX || x > bv) { bv = x; bi = e; }
-            }
-        }
-        wave_argmax(bv, bi);
-        res = make_float2(bv, __int_as_float(bi));
-    } else {
-        const float c = a.c;
-        float m = -INFINITY, s = 0.f;
-        if (VEC) {
-            const uint4* vrow = reinterpret_cast<const uint4*>(row);
-            uint4 buf[kU];
-            const int v0 = beg / kV, v1 = end / kV;
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                int v = v0 + u * kWave + lane;
-                if (v < v1) buf[u] = vrow[v];
-            }
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                int v = v0 + u * kWave + lane;
-                if (v < v1) {
-                    float x[kV];
-                    LT::unpack(buf[u], x);
-                    float vm = x[0];
-#pragma unroll
-                    for (int e = 1; e < kV; ++e) vm = fmaxf(vm, x[e]);
-                    const float am = vm * c;
-                    if (am > m) { s *= __builtin_amdgcn_exp2f(m - am); m = am; }
-#pragma unroll
-                    for (int e = 0; e < kV; ++e) s += __builtin_amdgcn_exp2f(fmaf(x[e], c, -m));
-                }
-            }
-        } else {
-            for (int e = beg + lane; e < end; e += kWave) {
-                float x = LT::load1(row + e);
-                const float am = x * c;
-                if (am > m) { s *= __builtin_amdgcn_exp2f(m - am); m = am; }
-                s += __builtin_amdgcn_exp2f(fmaf(x, c, -m));
-            }
-        }
-        wave_lse(m, s);
-        res = make_float2(m, s);
-    }
-    if (lane == 0) a.part[slot * a.C + chunk] = res;
-}
-
-// ---------------------------------------------------------------------------
-// per-request decisions
-// ---------------------------------------------------------------------------
-
-template <int DT, int MODE>
-__global__ __launch_bounds__(256) void verify_finalize(VerifyArgs a) {
-    using LT = Logit<DT>;
-    using T = typename LT::T;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int r = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (r >= a.R) return;
-    const int k = a.k;
-    const int base = a.cu_rows[r];
-    const int L = a.cu_rows[r + 1] - base - 1;
-    int32_t* out = a.out_tokens + long(r) * (k + 1);
-
-    bool bad = L < 0 || L > k || base < 0 || base + L >= a.Bmax;
-    if (!bad && lane <= L) {
-        const int t = base + lane;
-        bad = a.tags[2 * t] != r || a.tags[2 * t + 1] != lane;
-    }
-    bad = __any(bad);
-    if (bad) {
-        if (lane == 0) {
-            set_status(a.hdr, SPECV_STATUS_BAD_TAG);
-            a.acc_len[r] = 0;
-            if (MODE == SPECV_SAMPLE) a.rs_row[r] = make_int4(-1, 0, 2, 0);
-        }
-        if (lane <= k) out[lane] = -1;
-        return;
-    }
-
-    int acc = L;              // first rejected position (L if none)
-    int y = -1;               // greedy: token emitted at position acc
-    float4 stat = make_float4(0.f, 0.f, 0.f, 0.f);
-    int rs_t = base + L;
-
-    for (int j = 0; j <= L; ++j) {
-        const int t = base + j;
-        const bool verified = j < L;
-        int x = -1;
-        bool xok = true;
-        if (verified) {
-            x = a.tokens[long(r) * k + j];
-            xok = x >= 0 && x < a.V;
-        }
-        if (MODE == SPECV_GREEDY) {
-            float bv = -INFINITY;
-            int bi = INT_MAX;
-            for (int ch = lane; ch < a.C; ch += kWave) {
-                float2 p = a.part[long(t) * a.C + ch];
-                argmax_merge(bv, bi, p.x, __float_as_int(p.y));
-            }
-            wave_argmax(bv, bi);
-            bool keep = false;
-            if (verified) {
-                keep = xok && bi == x;
-                if (!keep && acc == L) { acc = j; y = bi; }
-            } else if (acc == L) {
-                y = bi;
-            }
-            if (a.diag && lane == 0)
-                reinterpret_cast<float4*>(a.diag)[t] =
-                    make_float4(float(bi), bv, 0.f, verified ? (keep ? 1.f : 0.f) : -1.f);
-        } else {
-            float mp = -INFINITY, sp = 0.f, mq = -INFINITY, sq = 0.f;
-            for (int ch = lane; ch < a.C; ch += kWave) {
-                float2 p = a.part[long(2 * t) * a.C + ch];
-                lse_merge(mp, sp, p.x, p.y);
-                if (verified) {
-                    float2 q = a.part[long(2 * t + 1) * a.C + ch];
-                    lse_merge(mq, sq, q.x, q.y);
-                }
-            }
-            wave_lse(mp, sp);
-            if (verified) wave_lse(mq, sq);
-            if (verified) {
-                float px = 0.f, qx = 0.f, ratio = 0.f;
-                bool keep = false;
-                if (xok) {
-                    const T* trow = static_cast<const T*>(a.target) + (long(r) * (k + 1) + j) * long(a.V);
-                    const T* drow = static_cast<const T*>(a.draft) + (long(r) * k + j) * long(a.V);
-                    const float tx = LT::load1(trow + x);
-                    const float dx = LT::load1(drow + x);
-                    px = exp2f(fmaf(tx, a.c, -mp)) / sp;
-                    qx = exp2f(fmaf(dx, a.c, -mq)) / sq;
-                    ratio = qx > 0.f ? px / qx : INFINITY;
-                    const float u = a.uniforms[long(r) * (k + 1) + j];
-                    keep = u < fminf(1.f, ratio);
-                }
-                if (!keep && acc == L) {
-                    acc = j;
-                    stat = make_float4(mp, sp, mq, sq);
-                    rs_t = t;
-                }
-                if (a.diag && lane == 0)
-                    reinterpret_cast<float4*>(a.diag)[t] = make_float4(px, qx, ratio, keep ? 1.f : 0.f);
             } else {
-                if (acc == L) stat = make_float4(mp, sp, 0.f, 0.f);
-                if (a.diag && lane == 0)
-                    reinterpret_cast<float4*>(a.diag)[t] = make_float4(0.f, 0.f, 0.f, -1.f);
+                float bv = -INFINITY;
+                int bi = INT_MAX;
+#pragma unroll
+                for (int q = 0; q < E; ++q)           // a lane's offsets increase with q
+                    if (x[q] > bv) { bv = x[q]; bi = beg + RW::offset(q, lane); }
+                wave_argmax_dpp(bv, bi);
+                outp.x = bv; outp.y = __int_as_float(bi);
             }
         }
-        if (verified && !xok && lane == 0) set_status(a.hdr, SPECV_STATUS_BAD_TOKEN);
-    }
+        if (lane == 0) a.part[long(ri.t) * a.C + ch] = outp;
+        ri = rn;
+    };
 
-    if (lane <= k) {
-        int v = -1;
-        if (lane < acc) v = a.tokens[long(r) * k + lane];
-        else if (lane == acc && MODE == SPECV_GREEDY) v = y;
-        out[lane] = v;
-    }
-    if (lane == 0) {
-        a.acc_len[r] = acc;
-        if (MODE == SPECV_SAMPLE) {
-            a.rs_stat[r] = stat;
-            a.rs_row[r] = make_int4(rs_t, acc, acc < L ? 0 : 1, 0);
-        }
+    RW t0, d0, t1, d1;                          // two named buffers: no dynamic indexing
+    issue(t0, d0, ri, i);
+    for (;;) {
+        step(t0, d0, t1, d1);
+        if (++i >= iend) break;
+        step(t1, d1, t0, d0);
+        if (++i >= iend) break;
     }
 }
 
 // ---------------------------------------------------------------------------
-// resample: chunk masses of the residual max(0, p - q)
+// verify_decide
 // ---------------------------------------------------------------------------
 
-template <int DT, bool VEC>
-__device__ __forceinline__ float residual_weight(float tx, float dx, float c, float4 st,
-                                                 float inv_sp, float inv_sq) {
-    const float p = exp2f(fmaf(tx, c, -st.x)) * inv_sp;
-    const float q = exp2f(fmaf(dx, c, -st.z)) * inv_sq;
+// In-chunk inverse CDF by one wavefront. The chunk of CH logits starting at
+// `beg` of the target row (and, for PAIR, of the draft row) is loaded in the
+// stream layout; wt(xt, xd) is an element's weight. Returns the first element
+// whose running sum from `base`, in index order, exceeds thr; else the last
+// element with positive weight (beg if none).
+template <int DT, bool VEC, bool PAIR, class Wf>
+__device__ int chunk_pick(const typename Logit<DT>::T* trow, const typename Logit<DT>::T* drow, int beg,
+                          int V, float base, float thr, Wf wt) {
+    using RW = Raw<DT, VEC>;
+    constexpr int E = RW::kE, GW = RW::kVec;
+    const int lane = threadIdx.x & (kWave - 1);
+    RW rt, rd;
+    rt.load(trow, beg, V, lane);
+    if constexpr (PAIR) rd.load(drow, beg, V, lane);
+    float xt[E], xd[E];
+    rt.widen(beg, V, lane, xt);
+    if constexpr (PAIR) {
+        rd.widen(beg, V, lane, xd);
+    } else {
+#pragma unroll
+        for (int q = 0; q < E; ++q) xd[q] = 0.f;
+    }
+    float w[E];
+#pragma unroll
+    for (int q = 0; q < E; ++q) w[q] = xt[q] == -INFINITY ? 0.f : wt(xt[q], xd[q]);
+    float run = base;
+    int lastw = -1;
+#pragma unroll
+    for (int u = 0; u < kNV; ++u) {                 // groups of 64 * GW elements, in index order
+        float ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < GW; ++e) ls += w[u * GW + e];
+        const float incl = wave_inclusive_scan(ls, lane);
+        float cum = run + (incl - ls);
+        int hit = INT_MAX;
+#pragma unroll
+        for (int e = 0; e < GW; ++e) {
+            const float we = w[u * GW + e];
+            const int off = beg + RW::offset(u * GW + e, lane);
+            cum += we;
+            if (we > 0.f) lastw = max(lastw, off);
+            if (hit == INT_MAX && cum > thr) hit = off;
+        }
+        const int f = wave_min_int(hit);
+        if (f != INT_MAX) return f;
+        run += __shfl(incl, kWave - 1, kWave);
+    }
+    const int lw = -wave_min_int(-lastw);
+    return lw >= 0 ? lw : beg;
+}
+
+// max(0, p - q) of one element, given the resample row's (Mp, Zp, Mq, Zq)
+// through st and the reciprocals ip = 1/Zp, iq = 1/Zq.
+__device__ __forceinline__ float residual_weight(float xt, float xd, float c, float4 st, float ip, float iq) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(xt, c, -st.x)) * ip;
+    const float q = __builtin_amdgcn_exp2f(fmaf(xd, c, -st.z)) * iq;
     return fmaxf(p - q, 0.f);
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(256) void resample_mass(VerifyArgs a) {
+// Chunk holding the draw among C chunk masses, by one wavefront in chunk
+// order: the first chunk whose inclusive prefix exceeds thr = u * total, with
+// the prefix before it in `base`; without a crossing (rounding), the last
+// chunk with positive mass and an in-chunk threshold of +inf.
+template <class Mf>
+__device__ int wave_find_chunk(int C, float u, Mf mass_of, float& base, float& cthr) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float total = 0.f;
+    for (int c0 = 0; c0 < C; c0 += kWave) {
+        const int cc = c0 + lane;
+        total += __shfl(wave_inclusive_scan(cc < C ? mass_of(cc) : 0.f, lane), kWave - 1, kWave);
+    }
+    const float thr = u * total;
+    float carry = 0.f;
+    int last_pos = -1;
+    for (int c0 = 0; c0 < C; c0 += kWave) {
+        const int cc = c0 + lane;
+        const float mc = cc < C ? mass_of(cc) : 0.f;
+        const float inc = wave_inclusive_scan(mc, lane) + carry;
+        const int cand = wave_min_int(cc < C && inc > thr ? cc : INT_MAX);
+        last_pos = max(last_pos, -wave_min_int(cc < C && mc > 0.f ? -cc : 1));
+        if (cand != INT_MAX) {
+            base = __shfl(inc - mc, cand - c0, kWave);
+            cthr = thr;
+            return cand;
+        }
+        carry = __shfl(inc, kWave - 1, kWave);
+    }
+    base = 0.f;
+    cthr = INFINITY;
+    return last_pos < 0 ? 0 : last_pos;
+}
+
+template <int DT, int MODE, bool VEC>
+__global__ __launch_bounds__(kThreads) void verify_decide(VerifyArgs a) {
     using LT = Logit<DT>;
     using T = typename LT::T;
-    constexpr int kV = LT::kVec;
-    constexpr int kU = kChunk / (kWave * kV);
-    const int lane = threadIdx.x & (kWave - 1);
-    const long item = long(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    if (item >= long(a.R) * a.C) return;
-    const int r = int(item / a.C), chunk = int(item % a.C);
-    const int4 rw = a.rs_row[r];
-    if (rw.z != 0) return;                               // bonus / invalid: no residual
-    const float4 st = a.rs_stat[r];
-    const int j = rw.y;
-    const T* trow = static_cast<const T*>(a.target) + (long(r) * (a.k + 1) + j) * long(a.V);
-    const T* drow = static_cast<const T*>(a.draft) + (long(r) * a.k + j) * long(a.V);
-    const float c = a.c, inv_sp = 1.f / st.y, inv_sq = 1.f / st.w;
-    const int beg = chunk * kChunk, end = min(a.V, beg + kChunk);
-    float s = 0.f;
-    if (VEC) {
-        const uint4* vt = reinterpret_cast<const uint4*>(trow);
-        const uint4* vd = reinterpret_cast<const uint4*>(drow);
-        const int v0 = beg / kV, v1 = end / kV;
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            int v = v0 + u * kWave + lane;
-            if (v < v1) {
-                float xt[kV], xd[kV];
-                LT::unpack(vt[v], xt);
-                LT::unpack(vd[v], xd);
-#pragma unroll
-                for (int e = 0; e < kV; ++e) s += residual_weight<DT, VEC>(xt[e], xd[e], c, st, inv_sp, inv_sq);
+    constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
+    __shared__ int keep_s[SPECV_MAX_K + 1];
+    __shared__ int g_s[SPECV_MAX_K + 1];
+    __shared__ float4 st_s[SPECV_MAX_K + 1];
+    __shared__ int bad_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = blockIdx.x;
+    const int k = a.k, C = a.C;
+    const int base = a.cu_rows[r];
+    const int L = a.cu_rows[r + 1] - base - 1;
+    const int nrows = min(*a.n_rows, a.Bmax);
+    int32_t* out = a.out_tokens + long(r) * (k + 1);
+    if (tid == 0) bad_s = L < 0 || L > k || base < 0 || base + L >= nrows;
+    __syncthreads();
+
+    if (!bad_s) {
+        for (int j = wave; j <= L; j += kWaves) {
+            const int t = base + j;
+            if (lane == 0 && (a.tags[2 * t] != r || a.tags[2 * t + 1] != j)) bad_s = 1;
+            const bool verified = j < L;
+            if (!SAMPLE) {
+                float gv = -INFINITY;
+                int gi = INT_MAX;
+                for (int cc = lane; cc < C; cc += kWave) {
+                    const float4 p = a.part[long(t) * C + cc];
+                    argmax_merge(gv, gi, p.x, __float_as_int(p.y));
+                }
+                wave_argmax(gv, gi);
+                if (lane == 0) {
+                    const int y = gi == INT_MAX ? 0 : gi;
+                    bool keep = false;
+                    if (verified) {
+                        const int x = a.tokens[long(r) * k + j];
+                        if (x < 0 || x >= a.V) atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TOKEN);
+                        keep = x == y;
+                    }
+                    keep_s[j] = keep;
+                    g_s[j] = y;
+                    if (a.diag)
+                        reinterpret_cast<float4*>(a.diag)[t] =
+                            make_float4(float(y), gv, 0.f, verified ? (keep ? 1.f : 0.f) : -1.f);
+                }
+            } else {
+                float mp = -INFINITY, zp = 0.f, mq = -INFINITY, zq = 0.f;
+                for (int cc = lane; cc < C; cc += kWave) {
+                    const float4 p = a.part[long(t) * C + cc];
+                    lse_merge(mp, zp, p.x, p.y);
+                    lse_merge(mq, zq, p.z, p.w);
+                }
+                wave_lse(mp, zp);
+                wave_lse(mq, zq);
+                if (lane == 0) {
+                    st_s[j] = make_float4(mp, zp, mq, zq);
+                    bool keep = false;
+                    if (verified) {
+                        const int x = a.tokens[long(r) * k + j];
+                        const bool xok = x >= 0 && x < a.V;
+                        float px = 0.f, qx = 0.f, ratio = 0.f;
+                        if (xok) {
+                            const RowRec rc = a.rec[t];
+                            px = exp2f(fmaf(rc.ax, a.c, -mp)) / zp;
+                            qx = exp2f(fmaf(rc.bx, a.c, -mq)) / zq;
+                            ratio = qx > 0.f ? px / qx : INFINITY;
+                            keep = a.uniforms[long(r) * (k + 1) + j] < fminf(1.f, ratio);
+                        } else {
+                            atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TOKEN);
+                        }
+                        if (a.diag)
+                            reinterpret_cast<float4*>(a.diag)[t] = make_float4(px, qx, ratio, keep ? 1.f : 0.f);
+                    } else if (a.diag) {
+                        reinterpret_cast<float4*>(a.diag)[t] = make_float4(0.f, 0.f, 0.f, -1.f);
+                    }
+                    keep_s[j] = keep;
+                }
             }
         }
-    } else {
-        for (int e = beg + lane; e < end; e += kWave)
-            s += residual_weight<DT, VEC>(LT::load1(trow + e), LT::load1(drow + e), c, st, inv_sp, inv_sq);
     }
-    s = wave_sum(s);
-    if (lane == 0) a.mass[item] = s;
+    __syncthreads();
+    if (bad_s) {
+        if (tid == 0) {
+            atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TAG);
+            a.acc_len[r] = 0;
+            if (SAMPLE) a.rs_row[r] = make_int4(-1, 0, 1, 0);
+        }
+        if (tid <= k) out[tid] = -1;
+        return;
+    }
+    int acc = L;
+    for (int j = 0; j < L; ++j)
+        if (!keep_s[j]) { acc = j; break; }
+    if (tid <= k) {
+        int v = -1;
+        if (tid < acc) v = a.tokens[long(r) * k + tid];
+        else if (tid == acc && !SAMPLE) v = g_s[acc];
+        out[tid] = v;
+    }
+    if (tid == 0) a.acc_len[r] = acc;
+    if (!SAMPLE) return;
+
+    const int t = base + acc;
+    const float4 st = st_s[acc];
+    if (acc < L) {                                 // residual draw in verify_residual
+        if (tid == 0) {
+            a.rs_stat[r] = st;
+            a.rs_row[r] = make_int4(t, acc, 0, 0);
+        }
+        return;
+    }
+    // every row kept: bonus token from p of row L (masses relative to Mp)
+    if (tid == 0) a.rs_row[r] = make_int4(t, acc, 1, 0);
+    if (wave != 0) return;
+    const float u = a.uniforms[long(r) * (k + 1) + k];
+    float cbase, cthr;
+    const int cs = wave_find_chunk(C, u, [&](int cc) {
+        const float4 p = a.part[long(t) * C + cc];
+        return p.x == -INFINITY ? 0.f : p.y * exp2f(p.x - st.x);
+    }, cbase, cthr);
+    const T* trow = static_cast<const T*>(a.target) + (long(r) * (k + 1) + acc) * long(a.V);
+    const float cc_ = a.c, Mp = st.x;
+    const int y = chunk_pick<DT, VEC, false>(trow, nullptr, cs * a.CH, a.V, cbase, cthr, [&](float xt, float) {
+        return __builtin_amdgcn_exp2f(fmaf(xt, cc_, -Mp));
+    });
+    if (lane == 0) out[acc] = y;
 }
 
 // ---------------------------------------------------------------------------
-// resample: inverse-CDF pick
+// verify_residual
 // ---------------------------------------------------------------------------
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(256) void resample_pick(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) void verify_residual(VerifyArgs a) {
+    using RW = Raw<DT, VEC>;
     using LT = Logit<DT>;
-    using T = typename LT::T;
+    using T = typename RW::T;
+    constexpr int E = RW::kE;
     const int lane = threadIdx.x & (kWave - 1);
-    const int r = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (r >= a.R) return;
-    const int4 rw = a.rs_row[r];
-    if (rw.z == 2) return;
-    const float4 st = a.rs_stat[r];
-    const int t = rw.x, j = rw.y;
-    bool residual = rw.z == 0;
+    const long nw = long(gridDim.x) * kWaves;
+    const long w = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
     const int C = a.C;
+    const long items = long(a.R) * C;
     const float c = a.c;
-
-    // chunk masses: the residual's, or the target row's own (unnormalised,
-    // relative to its maximum) from the pass-1 partials
-    auto chunk_mass = [&](int ch, bool res) -> float {
-        if (res) return a.mass[long(r) * C + ch];
-        float2 p = a.part[long(2 * t) * C + ch];
-        return p.x == -INFINITY ? 0.f : p.y * exp2f(p.x - st.x);
-    };
-    float W = 0.f;
-    if (residual) {
-        for (int ch0 = 0; ch0 < C; ch0 += kWave) {
-            int ch = ch0 + lane;
-            W += wave_sum(ch < C ? chunk_mass(ch, true) : 0.f);
+    for (long i = items * w / nw, iend = items * (w + 1) / nw; i < iend; ++i) {
+        const int r = int(i / C), ch = int(i % C);
+        const int4 rw = a.rs_row[r];
+        if (rw.z != 0) continue;                       // no residual draw for this request
+        const float4 st = a.rs_stat[r];
+        const int j = rw.y;
+        const T* trow = static_cast<const T*>(a.target) + (long(r) * (a.k + 1) + j) * long(a.V);
+        const T* drow = static_cast<const T*>(a.draft) + (long(r) * a.k + j) * long(a.V);
+        const float ip = 1.f / st.y, iq = 1.f / st.w;
+        const int beg = ch * a.CH;
+        RW rt, rd;
+        rt.load(trow, beg, a.V, lane);
+        rd.load(drow, beg, a.V, lane);
+        float xt[E], xd[E];
+        rt.widen(beg, a.V, lane, xt);
+        rd.widen(beg, a.V, lane, xd);
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < E; ++q) s += xt[q] == -INFINITY ? 0.f : residual_weight(xt[q], xd[q], c, st, ip, iq);
+        s = wave_sum_dpp(s);
+        int last = 0;
+        if (lane == 0) {
+            put(&a.mass[long(r) * C + ch], s);
+            publish();
+            last = bump(&a.rctr[r]) == C - 1;
         }
-        if (!(W > 0.f)) residual = false;                 // empty residual: draw from p
-    }
-    if (!residual) {
-        W = 0.f;
-        for (int ch0 = 0; ch0 < C; ch0 += kWave) {
-            int ch = ch0 + lane;
-            W += wave_sum(ch < C ? chunk_mass(ch, false) : 0.f);
+        last = __shfl(last, 0, kWave);
+        if (!last) continue;
+        // last chunk of this request: draw from the residual (from p when the
+        // residual has no mass), then reset the counter for the next call
+        auto mass_of = [&](int cc) { return get(&a.mass[long(r) * C + cc]); };
+        float total = 0.f;
+        for (int c0 = 0; c0 < C; c0 += kWave) total += wave_sum(c0 + lane < C ? mass_of(c0 + lane) : 0.f);
+        const bool residual = total > 0.f;
+        const float u = a.uniforms[long(r) * (a.k + 1) + a.k];
+        float cbase, cthr;
+        int cs;
+        if (residual) {
+            cs = wave_find_chunk(C, u, mass_of, cbase, cthr);
+        } else {
+            const int t = rw.x;
+            cs = wave_find_chunk(C, u, [&](int cc) {
+                const float4 p = a.part[long(t) * C + cc];
+                return p.x == -INFINITY ? 0.f : p.y * exp2f(p.x - st.x);
+            }, cbase, cthr);
+        }
+        const int b2 = cs * a.CH;
+        int y;
+        if (residual)
+            y = chunk_pick<DT, VEC, true>(trow, drow, b2, a.V, cbase, cthr, [&](float xt_, float xd_) {
+                return residual_weight(xt_, xd_, c, st, ip, iq);
+            });
+        else
+            y = chunk_pick<DT, VEC, false>(trow, nullptr, b2, a.V, cbase, cthr, [&](float xt_, float) {
+                return __builtin_amdgcn_exp2f(fmaf(xt_, c, -st.x));
+            });
+        if (lane == 0) {
+            a.out_tokens[long(r) * (a.k + 1) + j] = y;
+            __hip_atomic_store(&a.rctr[r], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    const float thr = a.uniforms[long(r) * (a.k + 1) + a.k] * W;
-    const T* trow = static_cast<const T*>(a.target) + (long(r) * (a.k + 1) + j) * long(a.V);
-    const T* drow = residual ? static_cast<const T*>(a.draft) + (long(r) * a.k + j) * long(a.V) : nullptr;
-    const float inv_sp = 1.f / st.y, inv_sq = residual ? 1.f / st.w : 0.f;
-    auto weight = [&](int e) -> float {
-        const float tx = LT::load1(trow + e);
-        if (residual) return residual_weight<DT, VEC>(tx, LT::load1(drow + e), c, st, inv_sp, inv_sq);
-        return exp2f(fmaf(tx, c, -st.x));
-    };
-    const int yv = inv_cdf_pick(C, a.V, kChunk, thr, [&](int ch) { return chunk_mass(ch, residual); },
-                                weight, lane);
-    if (lane == 0) a.out_tokens[long(r) * (a.k + 1) + rw.y] = yv;
 }
 
 // ---------------------------------------------------------------------------
 // host entry
 // ---------------------------------------------------------------------------
 
-template <int DT>
-static int launch_verify(int mode, bool vec, const VerifyArgs& a, hipStream_t s) {
-    const long slots = long(mode == SPECV_SAMPLE ? 2 : 1) * a.Bmax;
-    const long items = slots * a.C;
-    const dim3 blk(kWave * kWavesPerBlock);
-    const dim3 g1((items + kWavesPerBlock - 1) / kWavesPerBlock);
-    const dim3 gR((a.R + kWavesPerBlock - 1) / kWavesPerBlock);
-    const dim3 gRC((long(a.R) * a.C + kWavesPerBlock - 1) / kWavesPerBlock);
+static int device_cus(int& cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return fail(SPECV_EDEVICE, "spec_verify: cannot query the device");
+    return SPECV_OK;
+}
+
+// Workgroups for a persistent kernel over `items` wave-sized work items: as
+// many as are resident at once, but no more than one wave per item.
+template <class K>
+static int persistent_grid(K kernel, long items, int cus, int& G) {
+    int per = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess || per < 1)
+        return fail(SPECV_EDEVICE, "spec_verify: cannot query the occupancy");
+    const long waves_needed = std::max<long>(1, items);
+    G = int(std::min<long>(long(cus) * per, (waves_needed + kWaves - 1) / kWaves));
+    return SPECV_OK;
+}
+
+template <int DT, bool VEC>
+static int launch_verify(int mode, VerifyArgs& a, hipStream_t s) {
+    int cus = 0;
+    if (int e = device_cus(cus)) return e;
+    const long max_items = long(a.Bmax) * a.C;
+    int G = 0;
     if (mode == SPECV_GREEDY) {
-        if (vec)
-            SPECV_LAUNCH("verify_partials", s, verify_partials<DT, SPECV_GREEDY, true><<<g1, blk, 0, s>>>(a));
-        else
-            SPECV_LAUNCH("verify_partials", s, verify_partials<DT, SPECV_GREEDY, false><<<g1, blk, 0, s>>>(a));
-        SPECV_LAUNCH("verify_finalize", s, verify_finalize<DT, SPECV_GREEDY><<<gR, blk, 0, s>>>(a));
+        auto ks = verify_stream<DT, SPECV_GREEDY, VEC>;
+        if (int e = persistent_grid(ks, max_items, cus, G)) return e;
+        SPECV_LAUNCH("verify_stream", s, ks<<<G, kThreads, 0, s>>>(a));
+        SPECV_LAUNCH("verify_decide", s, verify_decide<DT, SPECV_GREEDY, VEC><<<a.R, kThreads, 0, s>>>(a));
         return SPECV_OK;
     }
-    if (vec) {
-        SPECV_LAUNCH("verify_partials", s, verify_partials<DT, SPECV_SAMPLE, true><<<g1, blk, 0, s>>>(a));
-        SPECV_LAUNCH("verify_finalize", s, verify_finalize<DT, SPECV_SAMPLE><<<gR, blk, 0, s>>>(a));
-        SPECV_LAUNCH("resample_mass", s, resample_mass<DT, true><<<gRC, blk, 0, s>>>(a));
-        SPECV_LAUNCH("resample_pick", s, resample_pick<DT, true><<<gR, blk, 0, s>>>(a));
-    } else {
-        SPECV_LAUNCH("verify_partials", s, verify_partials<DT, SPECV_SAMPLE, false><<<g1, blk, 0, s>>>(a));
-        SPECV_LAUNCH("verify_finalize", s, verify_finalize<DT, SPECV_SAMPLE><<<gR, blk, 0, s>>>(a));
-        SPECV_LAUNCH("resample_mass", s, resample_mass<DT, false><<<gRC, blk, 0, s>>>(a));
-        SPECV_LAUNCH("resample_pick", s, resample_pick<DT, false><<<gR, blk, 0, s>>>(a));
-    }
+    auto ks = verify_stream<DT, SPECV_SAMPLE, VEC>;
+    if (int e = persistent_grid(ks, max_items, cus, G)) return e;
+    SPECV_LAUNCH("verify_stream", s, ks<<<G, kThreads, 0, s>>>(a));
+    SPECV_LAUNCH("verify_decide", s, verify_decide<DT, SPECV_SAMPLE, VEC><<<a.R, kThreads, 0, s>>>(a));
+    auto kr = verify_residual<DT, VEC>;
+    if (int e = persistent_grid(kr, long(a.R) * a.C, cus, G)) return e;
+    SPECV_LAUNCH("verify_residual", s, kr<<<G, kThreads, 0, s>>>(a));
     return SPECV_OK;
 }
 
@@ -447,7 +654,7 @@ static int launch_verify(int mode, bool vec, const VerifyArgs& a, hipStream_t s)
 extern "C" size_t spec_verify_workspace_bytes(int mode, int R, int k, int V) {
     if (R < 1 || k < 1 || k > SPECV_MAX_K || V < 1 || (mode != SPECV_GREEDY && mode != SPECV_SAMPLE))
         return 0;
-    return specv::ws_layout(mode, R, k, V).total;
+    return specv::ws_layout(R, k, V).total;
 }
 
 extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void* target_logits,
@@ -464,8 +671,8 @@ extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void*
     if (R < 1 || k < 1 || k > SPECV_MAX_K || V < 1)
         return fail(SPECV_EINVAL, "spec_verify: need R >= 1, 1 <= k <= %d, V >= 1 (got R=%d k=%d V=%d)",
                     SPECV_MAX_K, R, k, V);
-    if (long(R) * (k + 1) > INT_MAX / 2)
-        return fail(SPECV_EINVAL, "spec_verify: R*(k+1) too large");
+    if (long(R) * (k + 1) > INT_MAX / 2 || V > INT_MAX - chunk_elems(8))
+        return fail(SPECV_EINVAL, "spec_verify: R*(k+1) or V too large");
     if (!target_logits || !draft_tokens || !tags || !cu_rows || !n_rows || !accepted_len_out ||
         !out_tokens || !ws)
         return fail(SPECV_EINVAL, "spec_verify: NULL required pointer");
@@ -478,18 +685,19 @@ extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void*
     }
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
         return fail(SPECV_EINVAL, "spec_verify: workspace must be 256-byte aligned");
-    const Layout lay = ws_layout(mode, R, k, V);
+    const Layout lay = ws_layout(R, k, V);
     if (ws_bytes < lay.total)
         return fail(SPECV_EINVAL, "spec_verify: workspace of %zu bytes, need %zu", ws_bytes, lay.total);
 
     const int esize = dtype == SPECV_BF16 ? 2 : 4;
     const int vecw = 16 / esize;
-    bool vec = (V % vecw) == 0 && aligned16(target_logits) &&
-               (mode == SPECV_GREEDY || aligned16(draft_logits));
+    const bool vec = (V % vecw) == 0 && aligned16(target_logits) &&
+                     (mode == SPECV_GREEDY || aligned16(draft_logits));
 
     VerifyArgs a;
     a.R = R; a.k = k; a.V = V;
-    a.C = (V + kChunk - 1) / kChunk;
+    a.CH = chunk_len(dtype);
+    a.C = (V + a.CH - 1) / a.CH;
     a.Bmax = R * (k + 1);
     a.target = target_logits;
     a.draft = draft_logits;
@@ -504,11 +712,14 @@ extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void*
     a.diag = row_diag;
     char* w = static_cast<char*>(ws);
     a.hdr = reinterpret_cast<WsHeader*>(w);
-    a.part = reinterpret_cast<float2*>(w + lay.part);
+    a.part = reinterpret_cast<float4*>(w + lay.part);
+    a.rec = reinterpret_cast<RowRec*>(w + lay.rec);
     a.rs_stat = reinterpret_cast<float4*>(w + lay.rs_stat);
     a.rs_row = reinterpret_cast<int4*>(w + lay.rs_row);
     a.mass = reinterpret_cast<float*>(w + lay.mass);
+    a.rctr = reinterpret_cast<int*>(w + lay.rctr);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return dtype == SPECV_BF16 ? launch_verify<SPECV_BF16>(mode, vec, a, s)
-                               : launch_verify<SPECV_F32>(mode, vec, a, s);
+    if (dtype == SPECV_BF16)
+        return vec ? launch_verify<SPECV_BF16, true>(mode, a, s) : launch_verify<SPECV_BF16, false>(mode, a, s);
+    return vec ? launch_verify<SPECV_F32, true>(mode, a, s) : launch_verify<SPECV_F32, false>(mode, a, s);
 }
