@@ -28,8 +28,9 @@ MAX_K, MAX_SCHED_ITEMS = 32, 16384
 _c_int, _c_size, _c_ptr = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
 _SIGS = {
+    "spec_schedule_workspace_bytes": (_c_size, [_c_int, _c_int]),
     "spec_schedule": (_c_int, [_c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
-                               _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+                               _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
     "spec_flatten": (_c_int, [_c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "spec_verify_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "spec_verify": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
@@ -114,8 +115,12 @@ def logit_dtype(t: torch.Tensor) -> int:
     return _LOGIT_TYPES[t.dtype]
 
 
+def schedule_workspace_bytes(R: int, k: int) -> int:
+    return int(lib().spec_schedule_workspace_bytes(R, k))
+
+
 def spec_schedule(conf_logit, pos_temp, tbl_tokens, tbl_thr, max_len, len_out, tags_out, cu_rows_out,
-                  n_rows_out, survival_out=None, stream=None):
+                  n_rows_out, ws, survival_out=None, stream=None):
     R, k = conf_logit.shape
     _dev(conf_logit, "conf_logit", (torch.float32,))
     _dev(pos_temp, "pos_temp", (torch.float32,), (k,))
@@ -125,11 +130,13 @@ def spec_schedule(conf_logit, pos_temp, tbl_tokens, tbl_thr, max_len, len_out, t
     _dev(tags_out, "tags_out", (torch.int32,), (R * (k + 1), 2))
     _dev(cu_rows_out, "cu_rows_out", (torch.int32,), (R + 1,))
     _dev(n_rows_out, "n_rows_out", (torch.int32,), (1,))
+    _dev(ws, "ws", (torch.uint8,))
     if survival_out is not None:
         _dev(survival_out, "survival_out", (torch.float64,), (R, k))
     _check(lib().spec_schedule(R, k, _ptr(conf_logit), _ptr(pos_temp), _ptr(tbl_tokens), _ptr(tbl_thr),
                                tbl_tokens.numel(), int(max_len), _ptr(len_out), _ptr(tags_out),
-                               _ptr(cu_rows_out), _ptr(n_rows_out), _ptr(survival_out), _stream(stream)))
+                               _ptr(cu_rows_out), _ptr(n_rows_out), _ptr(survival_out), _ptr(ws), ws.numel(),
+                               _stream(stream)))
 
 
 def spec_flatten(len_in, k, tags_out, cu_rows_out, n_rows_out, stream=None):

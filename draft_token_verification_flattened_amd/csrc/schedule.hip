@@ -13,13 +13,19 @@
 // the choice is a global throughput maximisation (aibuzzwire.news article,
 // section "置信度计划、负载感知验证").
 //
-// One workgroup of 1024 threads does everything: the candidate count is at most
-// 16384, small enough for the keys to sit in the local data share, and the
-// whole call is a few microseconds of latency-bound work.
+// The scheduler needs, for every prefix length M of the candidates sorted by
+// key, the key sum P(M), and then the M with the largest gain. It does not sort:
+// candidate x sits at sorted position rank(x) = #{keys < x}, so the prefix that
+// ends at x has M = rank(x) + 1 and P(M) = (sum of Q over keys < x) + Q(x).
+// schedule_rank spreads those all-pairs counts over up to 256 workgroups (each
+// recomputes all keys into its LDS, then counts for its slice of keys), each
+// workgroup posts its best (G, M, key), and the last one to finish picks the
+// overall best and flattens. On one compute unit a sort of a few thousand
+// 64-bit keys costs ~10-20 us; the spread count costs ~1-2 us.
 //
 // Bit-exactness: survival is float64, quantised to an integer key
-// Q = floor(S * 2^32 + 0.5); prefix sums of keys are integers (order-free); the
-// gain G(M) uses one fixed float64 formula with contraction disabled, so a host
+// Q = floor(S * 2^32 + 0.5); sums of keys are integers (order-free); the gain
+// G(M) uses one fixed float64 formula with contraction disabled, so a host
 // reference computing the same formula gets the same bits.
 #pragma clang fp contract(off)
 
@@ -49,16 +55,18 @@ __device__ __forceinline__ uint64_t quantise(double S) {
     return uint64_t(floor(S * 4294967296.0 + 0.5));
 }
 
+// Table lookup: linear interpolation on the segment [B_j, B_j+1) holding bt
+// (found by binary search; the batch tokens are strictly increasing).
 __device__ double throughput(int bt, const int* tb, const double* tt, int n) {
     if (bt < tb[0]) return (tt[0] * double(bt)) / double(tb[0]);
     if (bt >= tb[n - 1]) return tt[n - 1];
-    for (int j = 0; j + 1 < n; ++j) {
-        if (tb[j] <= bt && bt < tb[j + 1]) {
-            const double frac = double(bt - tb[j]) / double(tb[j + 1] - tb[j]);
-            return tt[j] + (tt[j + 1] - tt[j]) * frac;
-        }
+    int lo = 0, hi = n - 1;                 // tb[lo] <= bt < tb[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tb[mid] <= bt) lo = mid; else hi = mid;
     }
-    return tt[n - 1];
+    const double frac = double(bt - tb[lo]) / double(tb[hi] - tb[lo]);
+    return tt[lo] + (tt[hi] - tt[lo]) * frac;
 }
 
 // Block-wide exclusive scan of one 64-bit value per thread; returns the total too.
@@ -103,19 +111,24 @@ struct SchedArgs {
     int32_t* cu_rows;
     int32_t* n_rows;
     double* survival;
+    struct SchedWs* ws;
 };
 
-// Verification length of request r for selection threshold `kstar` (a key;
-// candidates with smaller keys are selected).
-__device__ int request_length(const SchedArgs& a, int r, uint64_t kstar) {
-    double S = 1.0;
-    int L = 0;
-    for (int i = 0; i < a.kk; ++i) {
-        S = S * survival_step(a.z[long(r) * a.k + i], a.T[i]);
-        if (make_key(quantise(S), i, r) < kstar) ++L;
-    }
-    return L;
-}
+// Workspace of spec_schedule: a finish counter (zero between calls) and one
+// best-prefix record per workgroup.
+constexpr int kMaxSchedGroups = 256;
+struct SchedBest {
+    long long g;
+    int m;
+    int pad;
+    uint64_t key;
+    uint64_t pad2;
+};
+struct SchedWs {
+    int done;
+    int pad[63];
+    SchedBest best[kMaxSchedGroups];
+};
 
 // Write cu_rows, tags, n_rows (and len_out) for this thread's contiguous
 // request range [r0, r1) given lengths computed by `len_of`.
@@ -141,109 +154,166 @@ __device__ void flatten_block(const SchedArgs& a, int r0, int r1, F len_of, uint
     }
 }
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(SchedArgs a) {
-    __shared__ uint64_t keys[SPECV_MAX_SCHED_ITEMS];
-    __shared__ uint64_t sh[64];
-    __shared__ int tb[kMaxTbl];
-    __shared__ double tt[kMaxTbl];
-    __shared__ double red_g[kSchedThreads / 64];
-    __shared__ int red_m[kSchedThreads / 64];
-    __shared__ uint64_t kstar_sh;
-
-    const int tid = threadIdx.x, nt = blockDim.x;
-    const int per = (a.R + nt - 1) / nt;
-    const int r0 = min(a.R, tid * per), r1 = min(a.R, r0 + per);
-
-    if (a.max_len < 0 || a.kk == 0) {
-        // verify all k (max_len < 0) or nothing (max_len == 0)
-        const int Lfix = a.max_len < 0 ? a.k : 0;
-        if (a.survival) {
-            for (int r = r0; r < r1; ++r) {
-                double S = 1.0;
-                for (int i = 0; i < a.k; ++i) {
-                    S = S * survival_step(a.z[long(r) * a.k + i], a.T[i]);
-                    a.survival[long(r) * a.k + i] = S;
-                }
-            }
-        }
-        flatten_block(a, r0, r1, [&](int) { return Lfix; }, sh);
-        return;
-    }
-
-    for (int i = tid; i < a.n_tbl; i += nt) { tb[i] = a.tbl_b[i]; tt[i] = a.tbl_t[i]; }
-
-    // 1. calibrated survival, quantised keys
-    const int n = a.R * a.kk;
-    int n2 = 1;
-    while (n2 < n) n2 <<= 1;
-    for (int r = r0; r < r1; ++r) {
+// Keys of all candidates into LDS, request-major (keys[r * kk + i]); the
+// survival of every (r, i < k) to `survival` when it is not NULL.
+__device__ void compute_keys(const SchedArgs& a, uint64_t* keys, bool write_survival) {
+    for (int r = threadIdx.x; r < a.R; r += blockDim.x) {
         double S = 1.0;
         for (int i = 0; i < a.k; ++i) {
+            if (i >= a.kk && !write_survival) break;
             S = S * survival_step(a.z[long(r) * a.k + i], a.T[i]);
-            if (a.survival) a.survival[long(r) * a.k + i] = S;
+            if (write_survival) a.survival[long(r) * a.k + i] = S;
             if (i < a.kk) keys[r * a.kk + i] = make_key(quantise(S), i, r);
         }
     }
-    for (int i = n + tid; i < n2; i += nt) keys[i] = ~0ull;
-    __syncthreads();
+}
 
-    // 2. bitonic sort, ascending
-    for (int size = 2; size <= n2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int idx = tid; idx < (n2 >> 1); idx += nt) {
-                const int pos = 2 * idx - (idx & (stride - 1));
-                const int par = pos + stride;
-                const bool asc = (pos & size) == 0;
-                const uint64_t x = keys[pos], y = keys[par];
-                if ((x > y) == asc) { keys[pos] = y; keys[par] = x; }
+// All lengths fixed (max_len < 0: all k; max_len == 0: none): survival and flatten.
+__global__ __launch_bounds__(kSchedThreads) void schedule_fixed(SchedArgs a) {
+    __shared__ uint64_t sh[64];
+    const int tid = threadIdx.x, nt = blockDim.x;
+    if (a.survival) {
+        for (int r = tid; r < a.R; r += nt) {
+            double S = 1.0;
+            for (int i = 0; i < a.k; ++i) {
+                S = S * survival_step(a.z[long(r) * a.k + i], a.T[i]);
+                a.survival[long(r) * a.k + i] = S;
             }
-            __syncthreads();
         }
     }
+    const int Lfix = a.max_len < 0 ? a.k : 0;
+    const int per = (a.R + nt - 1) / nt;
+    const int r0 = min(a.R, tid * per), r1 = min(a.R, r0 + per);
+    flatten_block(a, r0, r1, [&](int) { return Lfix; }, sh);
+}
 
-    // 3. prefix sums of keys in sorted order; gain of every prefix length M
-    const uint64_t R32 = uint64_t(a.R) << 32;
-    const int seg = (n + nt - 1) / nt;
-    const int m0 = min(n, tid * seg), m1 = min(n, m0 + seg);
-    uint64_t local = 0;
-    for (int m = m0; m < m1; ++m) local += key_q(keys[m]);
-    uint64_t total;
-    uint64_t P = block_exclusive_scan_u64(local, sh, total);
-    double best = -1.0;
-    int bestM = INT_MAX;
-    if (tid == 0) {
-        const int bt = a.R;
-        best = (double(R32) * throughput(bt, tb, tt, a.n_tbl)) / double(bt);
-        bestM = 0;
-    }
-    for (int m = m0; m < m1; ++m) {
-        P += key_q(keys[m]);
-        const int M = m + 1, bt = a.R + M;
-        const double G = (double(R32 + P) * throughput(bt, tb, tt, a.n_tbl)) / double(bt);
-        if (G > best) { best = G; bestM = M; }     // increasing M: strict keeps the first
-    }
-    // block arg-max: larger G, then smaller M
-    const int lane = tid & 63, w = tid >> 6;
+__device__ __forceinline__ void put64(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long get64(unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One workgroup's best prefix, or the winner of a merge: larger G first, then
+// smaller M. G >= 0, so its bits order like its value as signed integers; an
+// empty candidate carries G bits LLONG_MIN.
+struct Best {
+    long long g;
+    int m;
+    uint64_t key;
+};
+
+__device__ __forceinline__ void best_merge(Best& x, long long g, int m, uint64_t key) {
+    if (g > x.g || (g == x.g && m < x.m)) { x.g = g; x.m = m; x.key = key; }
+}
+
+__device__ __forceinline__ void wave_best(Best& b) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        const double g2 = __shfl_xor(best, o, 64);
-        const int m2 = __shfl_xor(bestM, o, 64);
-        if (g2 > best || (g2 == best && m2 < bestM)) { best = g2; bestM = m2; }
+        const long long g2 = __shfl_xor(b.g, o, 64);
+        const int m2 = __shfl_xor(b.m, o, 64);
+        const uint64_t k2 = __shfl_xor(b.key, o, 64);
+        best_merge(b, g2, m2, k2);
     }
-    if (lane == 0) { red_g[w] = best; red_m[w] = bestM; }
-    __syncthreads();
-    if (tid == 0) {
-        double bg = red_g[0];
-        int bm = red_m[0];
-        for (int q = 1; q < (nt >> 6); ++q)
-            if (red_g[q] > bg || (red_g[q] == bg && red_m[q] < bm)) { bg = red_g[q]; bm = red_m[q]; }
-        kstar_sh = bm < n ? keys[bm] : ~0ull;
-    }
-    __syncthreads();
-    const uint64_t kstar = kstar_sh;
+}
 
-    // 4. lengths and flatten
-    flatten_block(a, r0, r1, [&](int r) { return request_length(a, r, kstar); }, sh);
+__global__ __launch_bounds__(kSchedThreads) void schedule_rank(SchedArgs a, int kw) {
+    extern __shared__ __align__(16) uint64_t keys[];          // [R * kk]
+    __shared__ int tb[kMaxTbl];
+    __shared__ double tt[kMaxTbl];
+    __shared__ unsigned long long cnt_sh[64];                  // per local key (kw <= 64)
+    __shared__ unsigned long long sum_sh[64];
+    __shared__ uint64_t sh[64];
+    __shared__ int last_sh;
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
+    const int n = a.R * a.kk;
+
+    // 1. table and all keys
+    for (int i = tid; i < a.n_tbl; i += nt) { tb[i] = a.tbl_b[i]; tt[i] = a.tbl_t[i]; }
+    if (tid < kw) { cnt_sh[tid] = 0ull; sum_sh[tid] = 0ull; }
+    compute_keys(a, keys, blockIdx.x == 0 && a.survival != nullptr);
+    __syncthreads();
+
+    // 2. rank and prefix sum of this workgroup's keys [j0, j0 + kw): thread
+    //    (key a_, segment b_) counts over its share of all n keys
+    const int j0 = blockIdx.x * kw;
+    const int a_ = tid % kw, b_ = tid / kw, nseg = nt / kw;
+    const int j = j0 + a_;
+    if (j < n) {
+        const uint64_t x = keys[j];
+        const int s0 = int(long(n) * b_ / nseg), s1 = int(long(n) * (b_ + 1) / nseg);
+        unsigned cnt = 0;
+        unsigned long long sum = 0;
+        for (int y = s0; y < s1; ++y) {
+            const uint64_t ky = keys[y];
+            if (ky < x) { ++cnt; sum += key_q(ky); }
+        }
+        atomicAdd(&cnt_sh[a_], (unsigned long long)cnt);
+        atomicAdd(&sum_sh[a_], sum);
+    }
+    __syncthreads();
+
+    // 3. this workgroup's best prefix; post it; the last workgroup continues
+    const uint64_t R32 = uint64_t(a.R) << 32;
+    if (tid < 64) {
+        Best b{LLONG_MIN, INT_MAX, 0ull};
+        for (int q = tid; q < kw && j0 + q < n; q += 64) {
+            const uint64_t x = keys[j0 + q];
+            const int M = int(cnt_sh[q]) + 1, bt = a.R + M;
+            const uint64_t P = sum_sh[q] + key_q(x);
+            const double G = (double(R32 + P) * throughput(bt, tb, tt, a.n_tbl)) / double(bt);
+            best_merge(b, __double_as_longlong(G), M, x);
+        }
+        if (blockIdx.x == 0 && tid == 0) {                   // the empty prefix, M = 0
+            const double G0 = (double(R32) * throughput(a.R, tb, tt, a.n_tbl)) / double(a.R);
+            best_merge(b, __double_as_longlong(G0), 0, 0ull);
+        }
+        wave_best(b);
+        if (tid == 0) {
+            SchedWs* w = a.ws;
+            put64(reinterpret_cast<unsigned long long*>(&w->best[blockIdx.x].g), (unsigned long long)b.g);
+            __hip_atomic_store(&w->best[blockIdx.x].m, b.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            put64(reinterpret_cast<unsigned long long*>(&w->best[blockIdx.x].key), b.key);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            last_sh = __hip_atomic_fetch_add(&w->done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                      int(gridDim.x) - 1;
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        }
+    }
+    __syncthreads();
+    if (!last_sh) return;
+
+    // 4. overall best: the selected candidates are the keys <= its key (none if M = 0)
+    if (tid < 64) {
+        SchedWs* w = a.ws;
+        Best b{LLONG_MIN, INT_MAX, 0ull};
+        for (int q = tid; q < int(gridDim.x); q += 64)
+            best_merge(b, (long long)get64(reinterpret_cast<unsigned long long*>(&w->best[q].g)),
+                       __hip_atomic_load(&w->best[q].m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                       get64(reinterpret_cast<unsigned long long*>(&w->best[q].key)));
+        wave_best(b);
+        if (tid == 0) {
+            sh[62] = b.key;
+            sh[63] = uint64_t(b.m);
+            __hip_atomic_store(&w->done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __syncthreads();
+    const uint64_t kt = sh[62];
+    const bool any = sh[63] > 0;
+    __syncthreads();
+    // a request's keys increase with the position, so its selection is a prefix
+    auto len_of = [&](int r) {
+        int L = 0;
+        if (any)
+            while (L < a.kk && keys[r * a.kk + L] <= kt) ++L;
+        return L;
+    };
+    const int per = (a.R + nt - 1) / nt;
+    const int r0 = min(a.R, tid * per), r1 = min(a.R, r0 + per);
+    flatten_block(a, r0, r1, len_of, sh);
 }
 
 // spec_flatten, part 1: offsets (single workgroup, contiguous request ranges).
@@ -280,10 +350,16 @@ __global__ __launch_bounds__(256) void flatten_tags_kernel(SchedArgs a) {
 
 }  // namespace specv
 
+extern "C" size_t spec_schedule_workspace_bytes(int R, int k) {
+    if (R < 1 || k < 1 || k > SPECV_MAX_K || long(R) * k > SPECV_MAX_SCHED_ITEMS) return 0;
+    return sizeof(specv::SchedWs);
+}
+
 extern "C" int spec_schedule(int R, int k, const float* conf_logit, const float* pos_temp,
                              const int32_t* tbl_tokens, const double* tbl_thr, int n_tbl, int max_len,
                              int32_t* len_out, int32_t* tags_out, int32_t* cu_rows_out,
-                             int32_t* n_rows_out, double* survival_out, specv_stream stream) {
+                             int32_t* n_rows_out, double* survival_out, void* ws, size_t ws_bytes,
+                             specv_stream stream) {
     using namespace specv;
     clear_error();
     if (R < 1 || k < 1 || k > SPECV_MAX_K || long(R) * k > SPECV_MAX_SCHED_ITEMS)
@@ -293,10 +369,14 @@ extern "C" int spec_schedule(int R, int k, const float* conf_logit, const float*
         return fail(SPECV_EINVAL, "spec_schedule: max_len must be -1 or in [0, k] (got %d)", max_len);
     if (max_len != -1 && max_len != 0 && (n_tbl < 1 || n_tbl > kMaxTbl))
         return fail(SPECV_EINVAL, "spec_schedule: n_tbl must be in [1, %d] (got %d)", kMaxTbl, n_tbl);
-    if (!conf_logit || !pos_temp || !len_out || !tags_out || !cu_rows_out || !n_rows_out)
+    if (!conf_logit || !pos_temp || !len_out || !tags_out || !cu_rows_out || !n_rows_out || !ws)
         return fail(SPECV_EINVAL, "spec_schedule: NULL required pointer");
     if (max_len > 0 && (!tbl_tokens || !tbl_thr))
         return fail(SPECV_EINVAL, "spec_schedule: NULL throughput table");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return fail(SPECV_EINVAL, "spec_schedule: workspace must be 256-byte aligned");
+    if (ws_bytes < sizeof(SchedWs))
+        return fail(SPECV_EINVAL, "spec_schedule: workspace of %zu bytes, need %zu", ws_bytes, sizeof(SchedWs));
     SchedArgs a;
     a.R = R; a.k = k;
     a.max_len = max_len;
@@ -307,8 +387,23 @@ extern "C" int spec_schedule(int R, int k, const float* conf_logit, const float*
     a.len_in = nullptr;
     a.len_out = len_out; a.tags = tags_out; a.cu_rows = cu_rows_out; a.n_rows = n_rows_out;
     a.survival = survival_out;
+    a.ws = static_cast<SchedWs*>(ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    SPECV_LAUNCH("schedule", s, schedule_kernel<<<1, kSchedThreads, 0, s>>>(a));
+    if (max_len < 0 || max_len == 0) {
+        SPECV_LAUNCH("schedule", s, schedule_fixed<<<1, kSchedThreads, 0, s>>>(a));
+        return SPECV_OK;
+    }
+    // keys per workgroup: a power of two >= 16, enough for at most 256 workgroups
+    const int n = R * a.kk;
+    int kw = 16;
+    while (long(kw) * kMaxSchedGroups < n) kw <<= 1;
+    const int groups = (n + kw - 1) / kw;
+    const size_t lds = size_t(n) * sizeof(uint64_t);
+    if (lds > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(schedule_rank),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
+        return fail(SPECV_EDEVICE, "spec_schedule: cannot reserve %zu bytes of LDS", lds);
+    SPECV_LAUNCH("schedule", s, schedule_rank<<<groups, kSchedThreads, lds, s>>>(a, kw));
     return SPECV_OK;
 }
 

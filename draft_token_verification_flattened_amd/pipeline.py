@@ -49,6 +49,7 @@ class DeviceStep:
         self.out_tokens = torch.zeros(R, k + 1, **i32)
         self.diag = torch.zeros(R * (k + 1), 4, dtype=torch.float32, device=device)
         self.ws_verify = B.workspace(B.verify_workspace_bytes(B.SAMPLE, R, k, V), device)
+        self.ws_sched = B.workspace(B.schedule_workspace_bytes(R, k), device)
         if w.backbone is not None:
             self.draft_tokens = torch.zeros(R, k, **i32)
             self.draft_logits = torch.zeros(R, k, V, dtype=self.backbone.dtype, device=device)
@@ -58,7 +59,7 @@ class DeviceStep:
     def schedule(self, max_len=None, stream=None):
         max_len = self.w.k if max_len is None else max_len
         B.spec_schedule(self.z, self.T, self.tbl_b, self.tbl_t, max_len, self.lengths, self.tags, self.cu_rows,
-                        self.n_rows, self.survival, stream=stream)
+                        self.n_rows, self.ws_sched, self.survival, stream=stream)
 
     def flatten(self, lengths: torch.Tensor, stream=None):
         B.spec_flatten(lengths, self.w.k, self.tags, self.cu_rows, self.n_rows, stream=stream)

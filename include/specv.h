@@ -59,8 +59,8 @@ enum {
     SPECV_STATUS_TIMEOUT = 4u    /* a bounded wait between workgroups expired */
 };
 
-/* Limits of the scheduler: all candidate keys of one call are sorted in the
- * local data share of one workgroup. */
+/* Limits of the scheduler: all candidate keys of one call are held in the
+ * local data share of each of its workgroups. */
 #define SPECV_MAX_K 32
 #define SPECV_MAX_SCHED_ITEMS 16384 /* R * k */
 
@@ -102,12 +102,21 @@ enum {
  *   cu_rows_out   i32 [R+1]
  *   n_rows_out    i32 [1]
  *   survival_out  f64 [R,k] or NULL
- * Errors: SPECV_EINVAL for NULL required pointers or out-of-range sizes.
+ *   ws, ws_bytes  workspace of at least spec_schedule_workspace_bytes(R, k)
+ *                 bytes, 256-byte aligned, zero-filled before its first use
+ *                 (every call leaves it zeroed again)
+ * Execution: up to 256 workgroups; each computes every key, counts for its
+ *   share of keys how many keys are smaller (and their sum), and posts its best
+ *   prefix; the last to finish picks the overall best and flattens. No sort.
+ * Errors: SPECV_EINVAL for NULL required pointers, out-of-range sizes or a small
+ *   workspace; SPECV_EDEVICE if the launch fails.
  */
+size_t spec_schedule_workspace_bytes(int R, int k);
 int spec_schedule(int R, int k, const float* conf_logit, const float* pos_temp,
                   const int32_t* tbl_tokens, const double* tbl_thr, int n_tbl, int max_len,
                   int32_t* len_out, int32_t* tags_out, int32_t* cu_rows_out,
-                  int32_t* n_rows_out, double* survival_out, specv_stream stream);
+                  int32_t* n_rows_out, double* survival_out, void* ws, size_t ws_bytes,
+                  specv_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* spec_flatten                                                              */

@@ -70,10 +70,10 @@ def test_greedy_needs_no_draft_or_uniforms_but_checks_rest():
 
 def _sched(**kw):
     a = dict(R=4, k=5, z=FAKE, T=FAKE, tb=FAKE, tt=FAKE, n=8, max_len=5, L=FAKE, tags=FAKE, cu=FAKE,
-             nrows=FAKE, surv=None)
+             nrows=FAKE, surv=None, ws=FAKE, wsb=1 << 20)
     a.update(kw)
     return B.lib().spec_schedule(a["R"], a["k"], a["z"], a["T"], a["tb"], a["tt"], a["n"], a["max_len"],
-                                 a["L"], a["tags"], a["cu"], a["nrows"], a["surv"], None)
+                                 a["L"], a["tags"], a["cu"], a["nrows"], a["surv"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,msg", [
@@ -86,6 +86,9 @@ def _sched(**kw):
     (dict(n=65), "n_tbl"),
     (dict(z=None), "NULL"),
     (dict(tb=None), "table"),
+    (dict(ws=None), "NULL"),
+    (dict(ws=FAKE + 8), "aligned"),
+    (dict(wsb=64), "workspace"),
 ])
 def test_schedule_rejects(kw, msg):
     assert _sched(**kw) == B.EINVAL

@@ -110,7 +110,8 @@ def test_schedule_limits(R, k):
     tags = torch.zeros(R * (k + 1), 2, dtype=torch.int32, device="cuda")
     cu = torch.zeros(R + 1, dtype=torch.int32, device="cuda")
     nr = torch.zeros(1, dtype=torch.int32, device="cuda")
-    B.spec_schedule(dev(z), dev(T), dev(pts), dev(thr), k, L, tags, cu, nr)
+    ws = B.workspace(B.schedule_workspace_bytes(R, k), "cuda")
+    B.spec_schedule(dev(z), dev(T), dev(pts), dev(thr), k, L, tags, cu, nr, ws)
     torch.cuda.synchronize()
     ref = osched.schedule(z, T, pts, thr, k)
     assert np.array_equal(L.cpu().numpy(), ref["L"])
