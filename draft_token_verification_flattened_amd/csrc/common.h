@@ -141,6 +141,17 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
     return lane63(v);
 }
 
+// Minimum of an int over the wave (all lanes active), as a scalar.
+__device__ __forceinline__ int wave_min_int_dpp(int v) {
+    v = min(v, dpp_i<0xb1>(v, v));
+    v = min(v, dpp_i<0x4e>(v, v));
+    v = min(v, dpp_i<0x141>(v, v));
+    v = min(v, dpp_i<0x140>(v, v));
+    v = min(v, dpp_i<0x142, 0xa>(v, v));
+    v = min(v, dpp_i<0x143, 0xc>(v, v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 // (value, index) maximum over the wave, larger value first, then lower index.
 template <int CTRL, int ROW_MASK = 0xf>
 __device__ __forceinline__ void argmax_dpp_step(float& v, int& i) {

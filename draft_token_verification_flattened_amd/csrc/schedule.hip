@@ -130,27 +130,32 @@ struct SchedWs {
     SchedBest best[kMaxSchedGroups];
 };
 
-// Write cu_rows, tags, n_rows (and len_out) for this thread's contiguous
-// request range [r0, r1) given lengths computed by `len_of`.
+// Flattened batch for the lengths given by `len_of`, this thread's contiguous
+// request range [r0, r1): verified rows first, request-major (request r's at
+// cu_rows[r] .. cu_rows[r+1]-1, tags (r, 0) .. (r, L_r - 1)), then one bonus row
+// per request at N + r with tag (r, L_r); N = cu_rows[R], n_rows = N + R.
 template <typename F>
 __device__ void flatten_block(const SchedArgs& a, int r0, int r1, F len_of, uint64_t* sh) {
     uint64_t local = 0;
-    for (int r = r0; r < r1; ++r) local += uint64_t(len_of(r) + 1);
+    for (int r = r0; r < r1; ++r) local += uint64_t(len_of(r));
     uint64_t total;
     uint64_t off = block_exclusive_scan_u64(local, sh, total);
+    const int N = int(total);
     for (int r = r0; r < r1; ++r) {
         const int L = len_of(r);
         a.cu_rows[r] = int32_t(off);
         if (a.len_out) a.len_out[r] = L;
-        for (int j = 0; j <= L; ++j) {
+        for (int j = 0; j < L; ++j) {
             a.tags[2 * (off + j)] = r;
             a.tags[2 * (off + j) + 1] = j;
         }
-        off += uint64_t(L + 1);
+        a.tags[2 * (N + r)] = r;
+        a.tags[2 * (N + r) + 1] = L;
+        off += uint64_t(L);
     }
     if (threadIdx.x == 0) {
-        a.cu_rows[a.R] = int32_t(total);
-        *a.n_rows = int32_t(total);
+        a.cu_rows[a.R] = N;
+        *a.n_rows = N + a.R;
     }
 }
 
@@ -323,16 +328,16 @@ __global__ __launch_bounds__(kSchedThreads) void flatten_offsets_kernel(SchedArg
     const int per = (a.R + nt - 1) / nt;
     const int r0 = min(a.R, tid * per), r1 = min(a.R, r0 + per);
     uint64_t local = 0;
-    for (int r = r0; r < r1; ++r) local += uint64_t(min(max(a.len_in[r], 0), a.k) + 1);
+    for (int r = r0; r < r1; ++r) local += uint64_t(min(max(a.len_in[r], 0), a.k));
     uint64_t total;
     uint64_t off = block_exclusive_scan_u64(local, sh, total);
     for (int r = r0; r < r1; ++r) {
         a.cu_rows[r] = int32_t(off);
-        off += uint64_t(min(max(a.len_in[r], 0), a.k) + 1);
+        off += uint64_t(min(max(a.len_in[r], 0), a.k));
     }
     if (tid == 0) {
         a.cu_rows[a.R] = int32_t(total);
-        *a.n_rows = int32_t(total);
+        *a.n_rows = int32_t(total) + a.R;
     }
 }
 
@@ -342,10 +347,13 @@ __global__ __launch_bounds__(256) void flatten_tags_kernel(SchedArgs a) {
     if (r >= a.R) return;
     const int L = min(max(a.len_in[r], 0), a.k);
     const int off = a.cu_rows[r];
-    for (int j = 0; j <= L; ++j) {
+    const int N = a.cu_rows[a.R];
+    for (int j = 0; j < L; ++j) {
         a.tags[2 * (off + j)] = r;
         a.tags[2 * (off + j) + 1] = j;
     }
+    a.tags[2 * (N + r)] = r;
+    a.tags[2 * (N + r) + 1] = L;
 }
 
 }  // namespace specv

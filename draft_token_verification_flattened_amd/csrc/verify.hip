@@ -7,27 +7,30 @@
 // 还是数字游戏？", section 一); rejection sampling keeps the target's distribution
 // ("DeepSeek服务器不再卡顿！…", section "DSpark的神奇之处").
 //
+// Batch layout (spec_schedule / spec_flatten): rows [0, N) are the verified rows,
+// request-major, request r's at [cu_rows[r], cu_rows[r+1]); rows [N, N + R) are
+// the bonus rows, request r's at N + r. N = cu_rows[R]; n_rows = N + R.
+//
 // Kernels, in stream order:
-//   verify_stream    the HBM stream. Work item = (flattened row t, chunk of
-//                    64 * kNV 16-byte vectors); the n_rows * C items are split
-//                    into one contiguous range per wavefront of a persistent
-//                    grid. Each wavefront loads item i+1 (target and, for a
-//                    verified row in sampling mode, draft) while it reduces item
-//                    i to the chunk's partial: (max, lowest index) in greedy
-//                    mode; in sampling mode the base-2 softmax state (M, S) of p
-//                    and of q, with M the chunk maximum of logit * log2(e) / tau
-//                    and S the sum of exp2(logit * log2(e) / tau - M). Wave
-//                    reductions use DPP. No atomics and no waits: all of the
-//                    step's logit traffic is here.
+//   verify_stream    the HBM stream. Work item = one chunk of 64 * kNV 16-byte
+//                    vectors of one logit row. Items: the target chunks of all
+//                    rows, then (sampling) the draft chunks of the verified rows,
+//                    so every item costs the same; the item range is split into
+//                    one contiguous share per wavefront of a persistent grid.
+//                    Each wavefront loads item i+1 while it reduces item i to a
+//                    partial: (max, lowest index) in greedy mode, the base-2
+//                    softmax state (M, S) of the chunk in sampling mode (M = max
+//                    of logit * log2(e) / tau, S = sum of exp2(that - M)). No
+//                    atomics, no waits: all of the step's logit traffic is here.
 //   verify_decide    one workgroup per request: merges each row's chunk
 //                    partials, decides every verified row, finds the first
 //                    rejection a_r and writes the accepted length and tokens.
 //                    Greedy: complete. Sampling with every row kept: draws the
-//                    bonus token from p of row L_r (chunk masses from the
+//                    bonus token from p of the bonus row (chunk masses from the
 //                    partials, then an in-order scan of one chunk).
 //   verify_residual  sampling, requests with a_r < L_r: re-reads the rejected
-//                    row pair chunk by chunk for the masses of max(0, p - q); the
-//                    last chunk of a request to finish (device-scope counter)
+//                    row pair for the chunk masses of max(0, p - q); the last
+//                    wavefront of a request to finish (device-scope counter)
 //                    draws the token by the inverse CDF.
 #include <climits>
 
@@ -38,7 +41,8 @@ namespace specv {
 
 constexpr int kThreads = 256;               // 4 wavefronts per workgroup
 constexpr int kWaves = kThreads / kWave;
-constexpr int kNV = 4;                      // 16-byte vectors per lane per tensor per item
+constexpr int kDecideThreads = 512;         // verify_decide: 8 rows of a request at a time
+constexpr int kNV = 4;                      // 16-byte vectors per lane per item
 constexpr int kChunkVecs = kWave * kNV;     // vectors per chunk
 
 __host__ __device__ constexpr int chunk_elems(int vec) { return kChunkVecs * vec; }
@@ -62,7 +66,8 @@ struct VerifyArgs {
     int32_t* out_tokens;
     float* diag;
     WsHeader* hdr;
-    float4* part;                           // [Bmax * C] sampling (m_p, s_p, m_q, s_q); greedy (v, idx, -, -)
+    float2* part_p;                         // [Bmax * C] target chunk partials
+    float2* part_q;                         // [Bmax * C] draft chunk partials (sampling)
     RowRec* rec;                            // [Bmax]
     float4* rs_stat;                        // [R] (Mp, Zp, Mq, Zq) of the resample row
     int4* rs_row;                           // [R] (row t, a_r, kind: 0 residual / 1 done, 0)
@@ -71,7 +76,7 @@ struct VerifyArgs {
 };
 
 struct Layout {
-    size_t part, rec, rs_stat, rs_row, mass, rctr, total;
+    size_t part_p, part_q, rec, rs_stat, rs_row, mass, rctr, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -81,7 +86,8 @@ static Layout ws_layout(int R, int k, int V) {
     const size_t C = (size_t(V) + chunk_elems(4) - 1) / chunk_elems(4);   // fp32 has the most chunks
     const size_t B = size_t(R) * size_t(k + 1);
     size_t off = align256(sizeof(WsHeader));
-    l.part = off;    off = align256(off + B * C * sizeof(float4));
+    l.part_p = off;  off = align256(off + B * C * sizeof(float2));
+    l.part_q = off;  off = align256(off + B * C * sizeof(float2));
     l.rec = off;     off = align256(off + B * sizeof(RowRec));
     l.rs_stat = off; off = align256(off + size_t(R) * sizeof(float4));
     l.rs_row = off;  off = align256(off + size_t(R) * sizeof(int4));
@@ -112,24 +118,24 @@ __device__ __forceinline__ void publish() {
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
-__device__ __forceinline__ int bump(int* p) {
-    const int old = __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ int bump(int* p, int v) {
+    const int old = __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     return old;
 }
 
 // ---------------------------------------------------------------------------
-// verify_stream
+// chunk loads
 // ---------------------------------------------------------------------------
 
-// Raw logits of one item for one lane: kNV 16-byte vectors (VEC) or kNV * kVec
+// Raw logits of one chunk for one lane: kNV 16-byte vectors (VEC) or kNV * kVec
 // scalars (unaligned rows, or V not a multiple of the vector width).
 template <int DT, bool VEC>
 struct Raw {
     using LT = Logit<DT>;
     using T = typename LT::T;
     static constexpr int kVec = LT::kVec;
-    static constexpr int kE = kNV * kVec;           // logits per lane per item
+    static constexpr int kE = kNV * kVec;           // logits per lane per chunk
     uint4 v[VEC ? kNV : 1];
     float s[VEC ? 1 : kE];
 
@@ -140,14 +146,18 @@ struct Raw {
         return ((q / kVec) * kWave + lane) * kVec + q % kVec;
     }
 
-    __device__ __forceinline__ void load(const T* row, int beg, int V, int lane) {
+    // Load the chunk starting at element `beg`; `full` = the whole chunk lies
+    // inside the row (else the elements past V are not read).
+    __device__ __forceinline__ void load(const T* row, int beg, int V, int lane, bool full) {
         if constexpr (VEC) {
-            const uint4* vr = reinterpret_cast<const uint4*>(row);
-            const int nv = V / kVec, b = beg / kVec;
+            const uint4* vr = reinterpret_cast<const uint4*>(row) + beg / kVec + lane;
+            if (full) {
 #pragma unroll
-            for (int u = 0; u < kNV; ++u) {
-                const int i = b + u * kWave + lane;
-                v[u] = i < nv ? vr[i] : make_uint4(0u, 0u, 0u, 0u);
+                for (int u = 0; u < kNV; ++u) v[u] = vr[u * kWave];
+            } else {
+                const int nv = V / kVec - beg / kVec - lane;
+#pragma unroll
+                for (int u = 0; u < kNV; ++u) v[u] = u * kWave < nv ? vr[u * kWave] : make_uint4(0u, 0u, 0u, 0u);
             }
         } else {
 #pragma unroll
@@ -158,17 +168,24 @@ struct Raw {
         }
     }
 
-    // Widen to float; elements past the end of the row become -inf.
-    __device__ __forceinline__ void widen(int beg, int V, int lane, float (&x)[kE]) const {
+    // Widen to float; with !full the elements past the end of the row are -inf.
+    __device__ __forceinline__ void widen(int beg, int V, int lane, bool full, float (&x)[kE]) const {
         if constexpr (VEC) {
-            const int nv = V / kVec, b = beg / kVec;
 #pragma unroll
             for (int u = 0; u < kNV; ++u) {
                 float t[kVec];
                 LT::unpack(v[u], t);
-                const bool ok = b + u * kWave + lane < nv;
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) x[u * kVec + e] = ok ? t[e] : -INFINITY;
+                for (int e = 0; e < kVec; ++e) x[u * kVec + e] = t[e];
+            }
+            if (!full) {
+                const int nv = V / kVec - beg / kVec - lane;
+#pragma unroll
+                for (int u = 0; u < kNV; ++u)
+                    if (u * kWave >= nv) {
+#pragma unroll
+                        for (int e = 0; e < kVec; ++e) x[u * kVec + e] = -INFINITY;
+                    }
             }
         } else {
 #pragma unroll
@@ -177,14 +194,21 @@ struct Raw {
     }
 };
 
+// Largest of a lane's values (pairs folded with three-input max).
+template <int E>
+__device__ __forceinline__ float lane_max(const float (&x)[E]) {
+    float m = fmaxf(x[0], x[1]);
+#pragma unroll
+    for (int q = 2; q + 1 < E; q += 2) m = fmaxf(m, fmaxf(x[q], x[q + 1]));
+    if (E % 2) m = fmaxf(m, x[E - 1]);
+    return m;
+}
+
 // Base-2 softmax state of one chunk of x * c over the wave: M = max, S = sum
 // of exp2(x * c - M); (-inf, 0) for a chunk of padding only.
 template <int E>
 __device__ __forceinline__ float2 chunk_softmax(const float (&x)[E], float c) {
-    float mx = x[0];
-#pragma unroll
-    for (int q = 1; q < E; ++q) mx = fmaxf(mx, x[q]);
-    const float M = wave_max_dpp(mx) * c;
+    const float M = wave_max_dpp(lane_max(x)) * c;
     if (M == -INFINITY) return make_float2(-INFINITY, 0.f);
     float acc = 0.f;
 #pragma unroll
@@ -192,27 +216,31 @@ __device__ __forceinline__ float2 chunk_softmax(const float (&x)[E], float c) {
     return make_float2(M, wave_sum_dpp(acc));
 }
 
-struct RowInfo {
-    int t, r, j;
-    bool ok, verified;
-    int x;
-};
-
-__device__ __forceinline__ RowInfo row_info(const VerifyArgs& a, int t, bool need_x) {
-    RowInfo ri;
-    ri.t = t;
-    ri.r = a.tags[2 * t];
-    ri.j = a.tags[2 * t + 1];
-    ri.ok = ri.r >= 0 && ri.r < a.R && ri.j >= 0 && ri.j <= a.k;
-    ri.verified = false;
-    ri.x = -1;
-    if (ri.ok && need_x) {
-        const int L = a.cu_rows[ri.r + 1] - a.cu_rows[ri.r] - 1;
-        ri.verified = ri.j < L && ri.j < a.k;
-        if (ri.verified) ri.x = a.tokens[long(ri.r) * a.k + ri.j];
+// (max, lowest index) of one chunk over the wave.
+template <class RW, int E>
+__device__ __forceinline__ float2 chunk_argmax(const float (&x)[E], int beg, int lane) {
+    const float lm = lane_max(x);
+    const float M = wave_max_dpp(lm);
+    int idx = INT_MAX;
+    if (lm == M && M != -INFINITY) {
+#pragma unroll
+        for (int q = E - 1; q >= 0; --q)               // offsets increase with q: keep the first
+            if (x[q] == M) idx = beg + RW::offset(q, lane);
     }
-    return ri;
+    return make_float2(M, __int_as_float(wave_min_int_dpp(idx)));
 }
+
+// ---------------------------------------------------------------------------
+// verify_stream
+// ---------------------------------------------------------------------------
+
+template <class T>
+struct RowMeta {
+    const T* row;
+    int t;                                  // flattened row
+    int x;                                  // draft token to capture, or -1
+    bool ok;                                // tag in range
+};
 
 template <int DT, int MODE, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
@@ -224,102 +252,117 @@ __global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
     const long nw = long(gridDim.x) * kWaves;
     const long w = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
     if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr->status = 0u;   // later kernels of this call set bits
-    const int nrows = min(*a.n_rows, a.Bmax);
-    const long items = long(max(nrows, 0)) * a.C;
-    long i = items * w / nw;
-    const long iend = items * (w + 1) / nw;
-    if (i >= iend) return;
+    const int nrows = min(max(*a.n_rows, 0), a.Bmax);
+    const int nver = min(max(a.cu_rows[a.R], 0), nrows);
+    const int C = a.C, CH = a.CH, V = a.V;
+    const long it_t = long(nrows) * C;                              // target items, then draft items
+    const long items = it_t + (SAMPLE ? long(nver) * C : 0);
+    const long i0 = items * w / nw, i1 = items * (w + 1) / nw;
+    if (i0 >= i1) return;
+
+    // tensor 0 = target row t, 1 = draft row t (t < nver)
+    auto meta = [&](int t, int tensor) {
+        RowMeta<T> m;
+        const int r = a.tags[2 * t], j = a.tags[2 * t + 1];
+        m.t = t;
+        m.ok = r >= 0 && r < a.R && j >= 0 && j <= a.k && (tensor == 0 || j < a.k);
+        m.x = -1;
+        m.row = nullptr;
+        if (m.ok) {
+            m.row = tensor == 0 ? static_cast<const T*>(a.target) + (long(r) * (a.k + 1) + j) * long(V)
+                                : static_cast<const T*>(a.draft) + (long(r) * a.k + j) * long(V);
+            if (SAMPLE && t < nver && j < a.k) m.x = a.tokens[long(r) * a.k + j];
+        }
+        return m;
+    };
+
+    int tensor = i0 >= it_t ? 1 : 0;
+    const long rel = tensor ? i0 - it_t : i0;
+    int t = int(rel / C), ch = int(rel % C);
+    int left = int(i1 - i0);
+    // metadata of this row and of the row after it (loaded one run ahead)
+    auto next_row = [&](int& tt, int& tens) {
+        if (++tt == nrows && tens == 0) { tt = 0; tens = 1; }
+    };
+    RowMeta<T> cur = meta(t, tensor);
+    int tn = t, tensn = tensor;
+    next_row(tn, tensn);
+    RowMeta<T> nxt{};
+    if (left > C - ch) nxt = meta(tn, tensn);
 
     const float c = a.c;
-    auto trow_of = [&](const RowInfo& q) {
-        return static_cast<const T*>(a.target) + (long(q.r) * (a.k + 1) + q.j) * long(a.V);
+    auto issue = [&](RW& b, const RowMeta<T>& m, int chunk) {
+        if (!m.ok) return;
+        const int beg = chunk * CH;
+        b.load(m.row, beg, V, lane, beg + CH <= V);
     };
-    auto drow_of = [&](const RowInfo& q) {
-        return static_cast<const T*>(a.draft) + (long(q.r) * a.k + q.j) * long(a.V);
-    };
-    auto issue = [&](RW& bt, RW& bd, const RowInfo& q, long it) {
-        if (!q.ok) return;
-        const int beg = int(it % a.C) * a.CH;
-        bt.load(trow_of(q), beg, a.V, lane);
-        if (SAMPLE && q.verified) bd.load(drow_of(q), beg, a.V, lane);
-    };
-
-    RowInfo ri = row_info(a, int(i / a.C), SAMPLE);
-
-    // Item i from (bt, bd) while item i+1 is loaded into (nt, nd).
-    auto step = [&](RW& bt, RW& bd, RW& nt, RW& nd) {
-        const long nx = i + 1;
-        const bool more = nx < iend;
-        RowInfo rn = ri;
-        if (more && nx % a.C == 0) rn = row_info(a, int(nx / a.C), SAMPLE);
-        if (more) issue(nt, nd, rn, nx);
-
-        const int ch = int(i % a.C);
-        const int beg = ch * a.CH;
-        float4 outp = SAMPLE ? make_float4(-INFINITY, 0.f, -INFINITY, 0.f)
-                             : make_float4(-INFINITY, __int_as_float(INT_MAX), 0.f, 0.f);
-        if (ri.ok) {
+    auto process = [&](const RW& b) {
+        const int beg = ch * CH;
+        const bool full = beg + CH <= V;
+        float2 P = SAMPLE ? make_float2(-INFINITY, 0.f) : make_float2(-INFINITY, __int_as_float(INT_MAX));
+        if (cur.ok) {
             float x[E];
-            bt.widen(beg, a.V, lane, x);
-            if (SAMPLE) {
-                const float2 P = chunk_softmax(x, c);
-                outp.x = P.x; outp.y = P.y;
-                if (ri.verified) {
-                    float y[E];
-                    bd.widen(beg, a.V, lane, y);
-                    const float2 Q = chunk_softmax(y, c);
-                    outp.z = Q.x; outp.w = Q.y;
-                    if (lane == 0 && ri.x >= beg && ri.x < beg + a.CH && ri.x < a.V) {
-                        a.rec[ri.t].ax = Logit<DT>::load1(trow_of(ri) + ri.x);
-                        a.rec[ri.t].bx = Logit<DT>::load1(drow_of(ri) + ri.x);
-                    }
-                }
-            } else {
-                float bv = -INFINITY;
-                int bi = INT_MAX;
-#pragma unroll
-                for (int q = 0; q < E; ++q)           // a lane's offsets increase with q
-                    if (x[q] > bv) { bv = x[q]; bi = beg + RW::offset(q, lane); }
-                wave_argmax_dpp(bv, bi);
-                outp.x = bv; outp.y = __int_as_float(bi);
+            b.widen(beg, V, lane, full, x);
+            P = SAMPLE ? chunk_softmax(x, c) : chunk_argmax<RW>(x, beg, lane);
+            if (SAMPLE && lane == 0 && cur.x >= beg && cur.x < beg + CH && cur.x < V) {
+                const float lx = Logit<DT>::load1(cur.row + cur.x);
+                if (tensor == 0) a.rec[cur.t].ax = lx; else a.rec[cur.t].bx = lx;
             }
         }
-        if (lane == 0) a.part[long(ri.t) * a.C + ch] = outp;
-        ri = rn;
+        if (lane == 0) (tensor == 0 ? a.part_p : a.part_q)[long(cur.t) * C + ch] = P;
+    };
+    // item (cur, ch) from b while the next item is loaded into nb
+    auto step = [&](RW& b, RW& nb) {
+        const bool row_end = ch + 1 == C;
+        if (left > 1) issue(nb, row_end ? nxt : cur, row_end ? 0 : ch + 1);
+        process(b);
+        --left;
+        if (row_end) {
+            ch = 0;
+            t = tn;
+            tensor = tensn;
+            cur = nxt;
+            next_row(tn, tensn);
+            if (left > C) nxt = meta(tn, tensn);
+        } else {
+            ++ch;
+        }
     };
 
-    RW t0, d0, t1, d1;                          // two named buffers: no dynamic indexing
-    issue(t0, d0, ri, i);
+    RW b0, b1;                                    // two named buffers: no dynamic indexing
+    issue(b0, cur, ch);
     for (;;) {
-        step(t0, d0, t1, d1);
-        if (++i >= iend) break;
-        step(t1, d1, t0, d0);
-        if (++i >= iend) break;
+        step(b0, b1);
+        if (left == 0) break;
+        step(b1, b0);
+        if (left == 0) break;
     }
 }
 
 // ---------------------------------------------------------------------------
-// verify_decide
+// inverse-CDF helpers (one wavefront)
 // ---------------------------------------------------------------------------
 
-// In-chunk inverse CDF by one wavefront. The chunk of CH logits starting at
-// `beg` of the target row (and, for PAIR, of the draft row) is loaded in the
-// stream layout; wt(xt, xd) is an element's weight. Returns the first element
-// whose running sum from `base`, in index order, exceeds thr; else the last
-// element with positive weight (beg if none).
+// In-chunk inverse CDF. The chunk of CH logits starting at `beg` of the target
+// row (and, for PAIR, of the draft row) is loaded in the stream layout; wt(xt,
+// xd) is an element's weight. Returns the first element whose running sum from
+// `base`, in index order, exceeds thr; else the last element with positive
+// weight (beg if none).
 template <int DT, bool VEC, bool PAIR, class Wf>
 __device__ int chunk_pick(const typename Logit<DT>::T* trow, const typename Logit<DT>::T* drow, int beg,
                           int V, float base, float thr, Wf wt) {
     using RW = Raw<DT, VEC>;
     constexpr int E = RW::kE, GW = RW::kVec;
     const int lane = threadIdx.x & (kWave - 1);
+    const int CH = chunk_elems(GW);
+    const bool full = beg + CH <= V;
     RW rt, rd;
-    rt.load(trow, beg, V, lane);
-    if constexpr (PAIR) rd.load(drow, beg, V, lane);
+    rt.load(trow, beg, V, lane, full);
+    if constexpr (PAIR) rd.load(drow, beg, V, lane, full);
     float xt[E], xd[E];
-    rt.widen(beg, V, lane, xt);
+    rt.widen(beg, V, lane, full, xt);
     if constexpr (PAIR) {
-        rd.widen(beg, V, lane, xd);
+        rd.widen(beg, V, lane, full, xd);
     } else {
 #pragma unroll
         for (int q = 0; q < E; ++q) xd[q] = 0.f;
@@ -353,18 +396,10 @@ __device__ int chunk_pick(const typename Logit<DT>::T* trow, const typename Logi
     return lw >= 0 ? lw : beg;
 }
 
-// max(0, p - q) of one element, given the resample row's (Mp, Zp, Mq, Zq)
-// through st and the reciprocals ip = 1/Zp, iq = 1/Zq.
-__device__ __forceinline__ float residual_weight(float xt, float xd, float c, float4 st, float ip, float iq) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(xt, c, -st.x)) * ip;
-    const float q = __builtin_amdgcn_exp2f(fmaf(xd, c, -st.z)) * iq;
-    return fmaxf(p - q, 0.f);
-}
-
-// Chunk holding the draw among C chunk masses, by one wavefront in chunk
-// order: the first chunk whose inclusive prefix exceeds thr = u * total, with
-// the prefix before it in `base`; without a crossing (rounding), the last
-// chunk with positive mass and an in-chunk threshold of +inf.
+// Chunk holding the draw among C chunk masses, in chunk order: the first chunk
+// whose inclusive prefix exceeds thr = u * total, with the prefix before it in
+// `base`; without a crossing (rounding), the last chunk with positive mass and
+// an in-chunk threshold of +inf.
 template <class Mf>
 __device__ int wave_find_chunk(int C, float u, Mf mass_of, float& base, float& cthr) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -394,11 +429,24 @@ __device__ int wave_find_chunk(int C, float u, Mf mass_of, float& base, float& c
     return last_pos < 0 ? 0 : last_pos;
 }
 
+// max(0, p - q) of one element, given the resample row's (Mp, Zp, Mq, Zq) in
+// st and the reciprocals ip = 1/Zp, iq = 1/Zq.
+__device__ __forceinline__ float residual_weight(float xt, float xd, float c, float4 st, float ip, float iq) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(xt, c, -st.x)) * ip;
+    const float q = __builtin_amdgcn_exp2f(fmaf(xd, c, -st.z)) * iq;
+    return fmaxf(p - q, 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// verify_decide
+// ---------------------------------------------------------------------------
+
 template <int DT, int MODE, bool VEC>
-__global__ __launch_bounds__(kThreads) void verify_decide(VerifyArgs a) {
+__global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
     using LT = Logit<DT>;
     using T = typename LT::T;
     constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
+    constexpr int kW = kDecideThreads / kWave;
     __shared__ int keep_s[SPECV_MAX_K + 1];
     __shared__ int g_s[SPECV_MAX_K + 1];
     __shared__ float4 st_s[SPECV_MAX_K + 1];
@@ -406,23 +454,24 @@ __global__ __launch_bounds__(kThreads) void verify_decide(VerifyArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = blockIdx.x;
     const int k = a.k, C = a.C;
+    const int nrows = min(max(*a.n_rows, 0), a.Bmax);
+    const int N = a.cu_rows[a.R];
     const int base = a.cu_rows[r];
-    const int L = a.cu_rows[r + 1] - base - 1;
-    const int nrows = min(*a.n_rows, a.Bmax);
+    const int L = a.cu_rows[r + 1] - base;
     int32_t* out = a.out_tokens + long(r) * (k + 1);
-    if (tid == 0) bad_s = L < 0 || L > k || base < 0 || base + L >= nrows;
+    if (tid == 0) bad_s = L < 0 || L > k || base < 0 || base + L > N || N < 0 || N + r >= nrows;
     __syncthreads();
 
     if (!bad_s) {
-        for (int j = wave; j <= L; j += kWaves) {
-            const int t = base + j;
-            if (lane == 0 && (a.tags[2 * t] != r || a.tags[2 * t + 1] != j)) bad_s = 1;
+        for (int j = wave; j <= L; j += kW) {
             const bool verified = j < L;
+            const int t = verified ? base + j : N + r;
+            if (lane == 0 && (a.tags[2 * t] != r || a.tags[2 * t + 1] != j)) bad_s = 1;
             if (!SAMPLE) {
                 float gv = -INFINITY;
                 int gi = INT_MAX;
                 for (int cc = lane; cc < C; cc += kWave) {
-                    const float4 p = a.part[long(t) * C + cc];
+                    const float2 p = a.part_p[long(t) * C + cc];
                     argmax_merge(gv, gi, p.x, __float_as_int(p.y));
                 }
                 wave_argmax(gv, gi);
@@ -443,12 +492,15 @@ __global__ __launch_bounds__(kThreads) void verify_decide(VerifyArgs a) {
             } else {
                 float mp = -INFINITY, zp = 0.f, mq = -INFINITY, zq = 0.f;
                 for (int cc = lane; cc < C; cc += kWave) {
-                    const float4 p = a.part[long(t) * C + cc];
+                    const float2 p = a.part_p[long(t) * C + cc];
                     lse_merge(mp, zp, p.x, p.y);
-                    lse_merge(mq, zq, p.z, p.w);
+                    if (verified) {
+                        const float2 q = a.part_q[long(t) * C + cc];
+                        lse_merge(mq, zq, q.x, q.y);
+                    }
                 }
                 wave_lse(mp, zp);
-                wave_lse(mq, zq);
+                if (verified) wave_lse(mq, zq);
                 if (lane == 0) {
                     st_s[j] = make_float4(mp, zp, mq, zq);
                     bool keep = false;
@@ -497,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void verify_decide(VerifyArgs a) {
     if (tid == 0) a.acc_len[r] = acc;
     if (!SAMPLE) return;
 
-    const int t = base + acc;
+    const int t = acc < L ? base + acc : N + r;
     const float4 st = st_s[acc];
     if (acc < L) {                                 // residual draw in verify_residual
         if (tid == 0) {
@@ -506,13 +558,13 @@ __global__ __launch_bounds__(kThreads) void verify_decide(VerifyArgs a) {
         }
         return;
     }
-    // every row kept: bonus token from p of row L (masses relative to Mp)
+    // every row kept: bonus token from p of the bonus row (masses relative to Mp)
     if (tid == 0) a.rs_row[r] = make_int4(t, acc, 1, 0);
     if (wave != 0) return;
     const float u = a.uniforms[long(r) * (k + 1) + k];
     float cbase, cthr;
     const int cs = wave_find_chunk(C, u, [&](int cc) {
-        const float4 p = a.part[long(t) * C + cc];
+        const float2 p = a.part_p[long(t) * C + cc];
         return p.x == -INFINITY ? 0.f : p.y * exp2f(p.x - st.x);
     }, cbase, cthr);
     const T* trow = static_cast<const T*>(a.target) + (long(r) * (k + 1) + acc) * long(a.V);
@@ -530,45 +582,66 @@ __global__ __launch_bounds__(kThreads) void verify_decide(VerifyArgs a) {
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_residual(VerifyArgs a) {
     using RW = Raw<DT, VEC>;
-    using LT = Logit<DT>;
     using T = typename RW::T;
     constexpr int E = RW::kE;
     const int lane = threadIdx.x & (kWave - 1);
     const long nw = long(gridDim.x) * kWaves;
     const long w = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    const int C = a.C;
+    const int C = a.C, CH = a.CH, V = a.V;
     const long items = long(a.R) * C;
     const float c = a.c;
-    for (long i = items * w / nw, iend = items * (w + 1) / nw; i < iend; ++i) {
-        const int r = int(i / C), ch = int(i % C);
+    long i = items * w / nw;
+    const long iend = items * (w + 1) / nw;
+    while (i < iend) {
+        // one run: the chunks of request r in this wavefront's share
+        const int r = int(i / C);
+        const int ch0 = int(i % C);
+        const int n = int(min<long>(iend - i, C - ch0));
+        i += n;
         const int4 rw = a.rs_row[r];
         if (rw.z != 0) continue;                       // no residual draw for this request
         const float4 st = a.rs_stat[r];
         const int j = rw.y;
-        const T* trow = static_cast<const T*>(a.target) + (long(r) * (a.k + 1) + j) * long(a.V);
-        const T* drow = static_cast<const T*>(a.draft) + (long(r) * a.k + j) * long(a.V);
+        const T* trow = static_cast<const T*>(a.target) + (long(r) * (a.k + 1) + j) * long(V);
+        const T* drow = static_cast<const T*>(a.draft) + (long(r) * a.k + j) * long(V);
         const float ip = 1.f / st.y, iq = 1.f / st.w;
-        const int beg = ch * a.CH;
-        RW rt, rd;
-        rt.load(trow, beg, a.V, lane);
-        rd.load(drow, beg, a.V, lane);
-        float xt[E], xd[E];
-        rt.widen(beg, a.V, lane, xt);
-        rd.widen(beg, a.V, lane, xd);
-        float s = 0.f;
+        auto mass_of_chunk = [&](const RW& rt, const RW& rd, int ch) {
+            const int beg = ch * CH;
+            const bool full = beg + CH <= V;
+            float xt[E], xd[E];
+            rt.widen(beg, V, lane, full, xt);
+            rd.widen(beg, V, lane, full, xd);
+            float s = 0.f;
 #pragma unroll
-        for (int q = 0; q < E; ++q) s += xt[q] == -INFINITY ? 0.f : residual_weight(xt[q], xd[q], c, st, ip, iq);
-        s = wave_sum_dpp(s);
+            for (int q = 0; q < E; ++q) s += xt[q] == -INFINITY ? 0.f : residual_weight(xt[q], xd[q], c, st, ip, iq);
+            return wave_sum_dpp(s);
+        };
+        auto issue = [&](RW& rt, RW& rd, int ch) {
+            const int beg = ch * CH;
+            const bool full = beg + CH <= V;
+            rt.load(trow, beg, V, lane, full);
+            rd.load(drow, beg, V, lane, full);
+        };
+        RW t0, d0, t1, d1;
+        issue(t0, d0, ch0);
+        for (int q = 0; q < n; q += 2) {
+            if (q + 1 < n) issue(t1, d1, ch0 + q + 1);
+            const float m0 = mass_of_chunk(t0, d0, ch0 + q);
+            if (lane == 0) put(&a.mass[long(r) * C + ch0 + q], m0);
+            if (q + 1 >= n) break;
+            if (q + 2 < n) issue(t0, d0, ch0 + q + 2);
+            const float m1 = mass_of_chunk(t1, d1, ch0 + q + 1);
+            if (lane == 0) put(&a.mass[long(r) * C + ch0 + q + 1], m1);
+        }
         int last = 0;
         if (lane == 0) {
-            put(&a.mass[long(r) * C + ch], s);
             publish();
-            last = bump(&a.rctr[r]) == C - 1;
+            last = bump(&a.rctr[r], n) + n == C;
         }
         last = __shfl(last, 0, kWave);
         if (!last) continue;
-        // last chunk of this request: draw from the residual (from p when the
-        // residual has no mass), then reset the counter for the next call
+        // every chunk of this request is in: draw from the residual (from p when
+        // the residual has no mass), then reset the counter for the next call
         auto mass_of = [&](int cc) { return get(&a.mass[long(r) * C + cc]); };
         float total = 0.f;
         for (int c0 = 0; c0 < C; c0 += kWave) total += wave_sum(c0 + lane < C ? mass_of(c0 + lane) : 0.f);
@@ -581,18 +654,18 @@ __global__ __launch_bounds__(kThreads) void verify_residual(VerifyArgs a) {
         } else {
             const int t = rw.x;
             cs = wave_find_chunk(C, u, [&](int cc) {
-                const float4 p = a.part[long(t) * C + cc];
+                const float2 p = a.part_p[long(t) * C + cc];
                 return p.x == -INFINITY ? 0.f : p.y * exp2f(p.x - st.x);
             }, cbase, cthr);
         }
-        const int b2 = cs * a.CH;
+        const int b2 = cs * CH;
         int y;
         if (residual)
-            y = chunk_pick<DT, VEC, true>(trow, drow, b2, a.V, cbase, cthr, [&](float xt_, float xd_) {
+            y = chunk_pick<DT, VEC, true>(trow, drow, b2, V, cbase, cthr, [&](float xt_, float xd_) {
                 return residual_weight(xt_, xd_, c, st, ip, iq);
             });
         else
-            y = chunk_pick<DT, VEC, false>(trow, nullptr, b2, a.V, cbase, cthr, [&](float xt_, float) {
+            y = chunk_pick<DT, VEC, false>(trow, nullptr, b2, V, cbase, cthr, [&](float xt_, float) {
                 return __builtin_amdgcn_exp2f(fmaf(xt_, c, -st.x));
             });
         if (lane == 0) {
@@ -630,19 +703,18 @@ template <int DT, bool VEC>
 static int launch_verify(int mode, VerifyArgs& a, hipStream_t s) {
     int cus = 0;
     if (int e = device_cus(cus)) return e;
-    const long max_items = long(a.Bmax) * a.C;
     int G = 0;
     if (mode == SPECV_GREEDY) {
         auto ks = verify_stream<DT, SPECV_GREEDY, VEC>;
-        if (int e = persistent_grid(ks, max_items, cus, G)) return e;
+        if (int e = persistent_grid(ks, long(a.Bmax) * a.C, cus, G)) return e;
         SPECV_LAUNCH("verify_stream", s, ks<<<G, kThreads, 0, s>>>(a));
-        SPECV_LAUNCH("verify_decide", s, verify_decide<DT, SPECV_GREEDY, VEC><<<a.R, kThreads, 0, s>>>(a));
+        SPECV_LAUNCH("verify_decide", s, verify_decide<DT, SPECV_GREEDY, VEC><<<a.R, kDecideThreads, 0, s>>>(a));
         return SPECV_OK;
     }
     auto ks = verify_stream<DT, SPECV_SAMPLE, VEC>;
-    if (int e = persistent_grid(ks, max_items, cus, G)) return e;
+    if (int e = persistent_grid(ks, 2L * a.Bmax * a.C, cus, G)) return e;
     SPECV_LAUNCH("verify_stream", s, ks<<<G, kThreads, 0, s>>>(a));
-    SPECV_LAUNCH("verify_decide", s, verify_decide<DT, SPECV_SAMPLE, VEC><<<a.R, kThreads, 0, s>>>(a));
+    SPECV_LAUNCH("verify_decide", s, verify_decide<DT, SPECV_SAMPLE, VEC><<<a.R, kDecideThreads, 0, s>>>(a));
     auto kr = verify_residual<DT, VEC>;
     if (int e = persistent_grid(kr, long(a.R) * a.C, cus, G)) return e;
     SPECV_LAUNCH("verify_residual", s, kr<<<G, kThreads, 0, s>>>(a));
@@ -671,7 +743,7 @@ extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void*
     if (R < 1 || k < 1 || k > SPECV_MAX_K || V < 1)
         return fail(SPECV_EINVAL, "spec_verify: need R >= 1, 1 <= k <= %d, V >= 1 (got R=%d k=%d V=%d)",
                     SPECV_MAX_K, R, k, V);
-    if (long(R) * (k + 1) > INT_MAX / 2 || V > INT_MAX - chunk_elems(8))
+    if (long(R) * (k + 1) > INT_MAX / 4 || V > INT_MAX - chunk_elems(8))
         return fail(SPECV_EINVAL, "spec_verify: R*(k+1) or V too large");
     if (!target_logits || !draft_tokens || !tags || !cu_rows || !n_rows || !accepted_len_out ||
         !out_tokens || !ws)
@@ -712,7 +784,8 @@ extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void*
     a.diag = row_diag;
     char* w = static_cast<char*>(ws);
     a.hdr = reinterpret_cast<WsHeader*>(w);
-    a.part = reinterpret_cast<float4*>(w + lay.part);
+    a.part_p = reinterpret_cast<float2*>(w + lay.part_p);
+    a.part_q = reinterpret_cast<float2*>(w + lay.part_q);
     a.rec = reinterpret_cast<RowRec*>(w + lay.rec);
     a.rs_stat = reinterpret_cast<float4*>(w + lay.rs_stat);
     a.rs_row = reinterpret_cast<int4*>(w + lay.rs_row);

@@ -84,8 +84,12 @@ enum {
  *   tbl_thr[0] * Bt / tbl_tokens[0]; at or above the last point it is the last
  *   value. M* = the smallest M with the largest G; L_r = the number of request
  *   r's candidates among the first M*. max_len < 0 forces L_r = k.
- *   Flatten: rows (r, j), j = 0..L_r, request-major; cu_rows[r] = first row of r;
- *   n_rows = cu_rows[R] = sum(L_r + 1). Row (r, L_r) carries the bonus token.
+ *   Flatten (one element per row, tagged (r, j)): the verified rows first,
+ *   request-major: request r's rows cu_rows[r] .. cu_rows[r+1]-1 carry
+ *   (r, 0) .. (r, L_r - 1), cu_rows = exclusive prefix sum of L, N = cu_rows[R];
+ *   then one bonus row per request: row N + r carries (r, L_r).
+ *   n_rows = N + R. (The pages fix no order; this one keeps the rows that need
+ *   draft logits in one block.)
  *
  * Arguments (device pointers unless noted)
  *   R, k          requests and draft block size (host ints): 1 <= k <= 32,
@@ -99,7 +103,7 @@ enum {
  *   len_out       i32 [R]           L_r
  *   tags_out      i32 [R*(k+1),2]   (request, position) per flattened row;
  *                                   rows >= n_rows are left untouched
- *   cu_rows_out   i32 [R+1]
+ *   cu_rows_out   i32 [R+1]         verified-row offsets (see Flatten)
  *   n_rows_out    i32 [1]
  *   survival_out  f64 [R,k] or NULL
  *   ws, ws_bytes  workspace of at least spec_schedule_workspace_bytes(R, k)
@@ -141,8 +145,9 @@ int spec_flatten(int R, int k, const int32_t* len_in, int32_t* tags_out,
  * rejection sampling keeps the target's distribution; [P4] opening: the longest
  * correct prefix is accepted).
  *
- * For request r with L_r = cu_rows[r+1] - cu_rows[r] - 1, verified rows
- * j < L_r and the bonus row j = L_r:
+ * The batch is spec_schedule's / spec_flatten's: request r has L_r =
+ * cu_rows[r+1] - cu_rows[r] verified rows at cu_rows[r] + j (j < L_r) and its
+ * bonus row at cu_rows[R] + r (j = L_r); tags must agree with that layout.
  *   greedy:   g_j = argmax_v target[r,j,v] (lowest index on ties);
  *             keep x_j iff g_j == x_j.
  *   sampling: p_j = softmax(target[r,j,:] / tau), q_j = softmax(draft[r,j,:] / tau);

@@ -14,7 +14,7 @@ What the pages fix:
     confidence, add them batch by batch while the extra step time per extra
     correct token pays ([P3] section "DSpark的神奇之处").
   * The selected tokens are flattened with a (request, position) tag ([P1]
-    engineering table, row "内核利用率暴跌").
+    engineering table, row "内核利用率暴跌"); the row order is free (see flatten).
 
 Readings where the pages are silent (each listed with its reason in the design
 notes):
@@ -120,12 +120,29 @@ def schedule(z, T, tbl_tokens, tbl_thr, max_len: int, k: int = None) -> dict:
 
 
 def flatten(L: np.ndarray):
-    """Request-major flattened rows: tags [B,2] = (r, j) for j = 0..L_r, cu_rows [R+1]."""
+    """The flattened varlen batch for lengths L [R].
+
+    Every row is one element with its tag (r, j). Verified rows come first,
+    request-major: rows cu[r] .. cu[r+1]-1 carry (r, 0) .. (r, L_r - 1), with
+    cu the exclusive prefix sum of L (cu [R+1], cu[R] = N = sum L). Then one bonus
+    row per request: row N + r carries (r, L_r). n_rows = N + R.
+    The pages fix no row order (the tag carries the dependency); this one puts
+    the rows that need both target and draft logits in one contiguous block.
+    """
     L = np.asarray(L, dtype=np.int64)
+    R = len(L)
     cu = [0]
     tags = []
-    for r in range(len(L)):
-        for j in range(int(L[r]) + 1):
+    for r in range(R):
+        for j in range(int(L[r])):
             tags.append((r, j))
-        cu.append(cu[-1] + int(L[r]) + 1)
+        cu.append(cu[-1] + int(L[r]))
+    for r in range(R):
+        tags.append((r, int(L[r])))
     return np.array(tags, dtype=np.int64).reshape(-1, 2), np.array(cu, dtype=np.int64)
+
+
+def n_rows(cu_rows) -> int:
+    """Rows of the flattened batch: the verified rows plus one bonus row per request."""
+    cu = np.asarray(cu_rows, dtype=np.int64)
+    return int(cu[-1]) + len(cu) - 1

@@ -6,8 +6,9 @@ Every selected draft token of every request is one element of a single batch;
 a tag (request id, position) per element carries the in-sequence dependency
 ([P1] engineering table, row "内核利用率暴跌": all tokens are flattened into
 independent elements and a tag tensor passes the dependencies). For request r
-with scheduled length L_r the batch holds rows (r, 0) .. (r, L_r); rows j < L_r
-verify draft token x_j, row L_r only supplies the bonus token.
+with scheduled length L_r the batch holds rows tagged (r, 0) .. (r, L_r); rows
+j < L_r verify draft token x_j, row L_r only supplies the bonus token. The row
+order is schedule.flatten's; everything here is keyed by the tags.
 
 Per verified row (the rule itself is oracle.rule):
   greedy    g = first argmax of the target logits; keep iff g == x_j.
@@ -123,15 +124,17 @@ def _emit(a, x, y, k):
 
 
 def lengths_from_cu(cu_rows: np.ndarray) -> np.ndarray:
+    """L_r from the verified-row offsets of the flattened batch (schedule.flatten)."""
     cu = np.asarray(cu_rows, dtype=np.int64)
-    return cu[1:] - cu[:-1] - 1
+    return cu[1:] - cu[:-1]
 
 
 def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
            tags: np.ndarray, cu_rows: np.ndarray, tau: float, u_verify: np.ndarray,
            block_rows: int = 64) -> dict:
     """Verify a flattened batch. Shapes: target [R,k+1,V], draft [R,k,V] (sampling
-    only), tokens [R,k], tags [B,2], cu_rows [R+1], u_verify [R,k+1].
+    only), tokens [R,k], tags [B,2] with B = cu_rows[R] + R, cu_rows [R+1]
+    (schedule.flatten), u_verify [R,k+1].
 
     Returns a dict with accepted_len [R], out_tokens [R,k+1] (-1 after the last
     emitted token) and per-row and per-request diagnostics for parity tests.
@@ -140,7 +143,7 @@ def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
     k = k1 - 1
     L = lengths_from_cu(cu_rows)
     tags = np.asarray(tags, dtype=np.int64)
-    B = int(cu_rows[-1])
+    B = int(cu_rows[-1]) + R
     assert tags.shape[0] >= B
     x = np.asarray(tokens, dtype=np.int64)
     res = dict(L=L)

@@ -91,8 +91,8 @@ def test_schedule_bit_exact(name, max_len):
     assert np.array_equal(L, ref["L"]), (L, ref["L"])
     tags, cu = osched.flatten(ref["L"])
     assert np.array_equal(d.host("cu_rows"), cu)
-    assert int(d.host("n_rows")[0]) == cu[-1]
-    assert np.array_equal(d.host("tags")[:cu[-1]], tags)
+    assert int(d.host("n_rows")[0]) == osched.n_rows(cu)
+    assert np.array_equal(d.host("tags")[:osched.n_rows(cu)], tags)
     S = d.host("survival")
     assert np.max(np.abs(S - ref["S"]) / ref["S"]) < 1e-14
 
@@ -117,7 +117,7 @@ def test_schedule_limits(R, k):
     assert np.array_equal(L.cpu().numpy(), ref["L"])
     rt, rc = osched.flatten(ref["L"])
     assert np.array_equal(cu.cpu().numpy(), rc)
-    assert np.array_equal(tags.cpu().numpy()[:rc[-1]], rt)
+    assert np.array_equal(tags.cpu().numpy()[:osched.n_rows(rc)], rt)
 
 
 def test_flatten_matches_oracle():
@@ -132,8 +132,8 @@ def test_flatten_matches_oracle():
         torch.cuda.synchronize()
         rt, rc = osched.flatten(np.clip(Ls, 0, k))
         assert np.array_equal(cu.cpu().numpy(), rc)
-        assert int(nr.item()) == rc[-1]
-        assert np.array_equal(tags.cpu().numpy()[:rc[-1]], rt)
+        assert int(nr.item()) == osched.n_rows(rc)
+        assert np.array_equal(tags.cpu().numpy()[:osched.n_rows(rc)], rt)
 
 
 # ---------------------------------------------------------------------------
@@ -148,7 +148,7 @@ def _run_verify(name, mode, max_len):
     tags, cu = osched.flatten(ref_s["L"])
     dl_host, tok_host = drafts_for(name, mode)
     mode_c = B.SAMPLE if mode == "sample" else B.GREEDY
-    say("verify", name, mode, "max_len", max_len, "rows", cu[-1])
+    say("verify", name, mode, "max_len", max_len, "rows", osched.n_rows(cu))
     d.flatten(to_device(ref_s["L"].astype(np.int32), "cuda"))
     d.verify(mode_c, draft=to_device(dl_host, "cuda") if mode == "sample" else None,
              tokens=to_device(tok_host.astype(np.int32), "cuda"))
@@ -166,7 +166,7 @@ GREEDY_CASES = [("c0", 5), ("c0", -1), ("c1", 5), ("c2", 5), ("c2", -1), ("c3", 
 @pytest.mark.parametrize("name,max_len", GREEDY_CASES)
 def test_verify_greedy_bit_exact(name, max_len):
     d, ref, tags, cu = _run_verify(name, "greedy", max_len)
-    Bn = cu[-1]
+    Bn = osched.n_rows(cu)
     assert np.array_equal(d.host("acc_len"), ref["accepted_len"])
     assert np.array_equal(d.host("out_tokens"), ref["out_tokens"])
     diag = d.host("diag")[:Bn]
@@ -175,7 +175,7 @@ def test_verify_greedy_bit_exact(name, max_len):
 
 def check_sampling(d, ref, tags, cu, u, tol=1e-5):
     """Sampling-mode parity with near-tie accounting; returns counts."""
-    Bn = cu[-1]
+    Bn = osched.n_rows(cu)
     diag = d.host("diag")[:Bn].astype(np.float64)
     ver = ref["row_verified"]
     for col, key in [(0, "row_p"), (1, "row_q"), (2, "row_ratio")]:
@@ -320,7 +320,7 @@ def test_verify_edges(R, k, V, dtype, ties, offset, tau, mode):
     if mode == "greedy":
         assert np.array_equal(acc, ref["accepted_len"])
         assert np.array_equal(out, ref["out_tokens"])
-        assert np.array_equal(diag[:cu[-1], 0].astype(np.int64), ref["row_argmax"])
+        assert np.array_equal(diag[:osched.n_rows(cu), 0].astype(np.int64), ref["row_argmax"])
     else:
         check_sampling(_Res(acc, out, diag), ref, tags, cu, u)
 

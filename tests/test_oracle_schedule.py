@@ -171,5 +171,8 @@ def test_load_adaptive_lengths_match_pages():
 
 def test_flatten_layout():
     tags, cu = schedule.flatten(np.array([2, 0, 3]))
-    assert list(cu) == [0, 3, 4, 8]
-    assert tags.tolist() == [[0, 0], [0, 1], [0, 2], [1, 0], [2, 0], [2, 1], [2, 2], [2, 3]]
+    assert list(cu) == [0, 2, 2, 5]
+    assert tags.tolist() == [[0, 0], [0, 1], [2, 0], [2, 1], [2, 2], [0, 2], [1, 0], [2, 3]]
+    assert schedule.n_rows(cu) == 8
+    # every (r, j <= L_r) appears exactly once
+    assert sorted(map(tuple, tags.tolist())) == [(0, 0), (0, 1), (0, 2), (1, 0), (2, 0), (2, 1), (2, 2), (2, 3)]
