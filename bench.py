@@ -85,32 +85,37 @@ def algorithmic_bytes(w, mode, N, R):
 
 
 def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
+    """Warm up, then run `steps` steps twice: first with the library recording
+    start/stop events from each kernel's own dispatch (per-kernel durations;
+    the events cost the step some time), then uninstrumented (the step time
+    and the throughput)."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         d.step(mode_c, max_len)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    B.timing_reset()
+    B.timing_enable(True)
     t0.record(stream)
     for _ in range(steps):
         d.step(mode_c, max_len)
     t1.record(stream)
     torch.cuda.synchronize()
+    B.timing_enable(False)
     ms_step = t0.elapsed_time(t1) / steps
-    # per-kernel durations: HIP events recorded by the library on the launch
-    # stream around each kernel, over a second pass of the same steps
-    B.timing_reset()
-    B.timing_enable(True)
-    for _ in range(steps):
-        d.step(mode_c, max_len)
-    torch.cuda.synchronize()
     kern = {}
     for name in ("markov_logits", "markov_pick", "schedule", "verify_stream", "verify_decide", "verify_residual"):
         n, tot = B.timing_read(name)
         if n:
             kern[name] = dict(launches_per_step=n / steps, avg_us=1000.0 * tot / n)
-    B.timing_enable(False)
     B.timing_reset()
+    t0.record(stream)
+    for _ in range(steps):
+        d.step(mode_c, max_len)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_plain = t0.elapsed_time(t1) / steps
     L = d.host("lengths")
     N = int(L.sum())
     R = w.R
@@ -119,41 +124,52 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
     achieved = nbytes / (dom["avg_us"] * 1e-6) if dom else None
     verify_us = sum(kern[k]["avg_us"] * kern[k]["launches_per_step"]
                     for k in ("verify_stream", "verify_decide", "verify_residual") if k in kern)
-    return dict(mode=mode, max_len=max_len, ms_per_step=ms_step, N=N, rows=int(d.host("n_rows")[0]),
-                tokens_per_s=N / (ms_step * 1e-3), verify_us=verify_us,
+    return dict(mode=mode, max_len=max_len, ms_per_step=ms_plain, ms_per_step_instrumented=ms_step, N=N,
+                rows=int(d.host("n_rows")[0]), tokens_per_s=N / (ms_plain * 1e-3), verify_us=verify_us,
                 verify_tokens_per_s=N / (verify_us * 1e-6) if verify_us else None,
                 algorithmic_bytes=nbytes, dominant_gbps=achieved / 1e9 if achieved else None,
                 dominant_frac=achieved / HBM_PEAK if achieved else None, kernels=kern)
 
 
-def cpu_baseline(w, mode, max_len):
-    """The oracle, as it stands, on one full step of the same workload."""
+def cpu_baseline(w, mode, max_len, min_seconds=10.0):
+    """The oracle, as it stands, on the same workload: whole steps repeated until
+    at least `min_seconds` of CPU time have passed."""
     import numpy as np
     from oracle import markov as omarkov
     from oracle import schedule as osched
     from oracle import verify as overify
-    t = time.perf_counter()
-    if w.backbone is not None:
-        m = omarkov.markov_draft(mode, w.dtype, w.backbone, w.emb, w.proj, w.prev_token, w.tau, w.u_draft)
-        dl, tok = m["logits"], m["tokens"]
-    else:
-        dl, tok = w.draft, (w.tokens_sample if mode == "sample" else w.tokens_greedy)
-    s = osched.schedule(w.conf_logit, w.pos_temp, w.tbl_tokens, w.tbl_thr, max_len)
-    tags, cu = osched.flatten(s["L"])
-    overify.verify(mode, w.dtype, w.target, dl if mode == "sample" else None, tok, tags, cu, w.tau, w.u_verify)
-    dt = time.perf_counter() - t
-    N = int(np.sum(s["L"]))
+
+    def one_step():
+        if w.backbone is not None:
+            m = omarkov.markov_draft(mode, w.dtype, w.backbone, w.emb, w.proj, w.prev_token, w.tau, w.u_draft)
+            dl, tok = m["logits"], m["tokens"]
+        else:
+            dl, tok = w.draft, (w.tokens_sample if mode == "sample" else w.tokens_greedy)
+        s = osched.schedule(w.conf_logit, w.pos_temp, w.tbl_tokens, w.tbl_thr, max_len)
+        tags, cu = osched.flatten(s["L"])
+        overify.verify(mode, w.dtype, w.target, dl if mode == "sample" else None, tok, tags, cu, w.tau,
+                       w.u_verify)
+        return int(np.sum(s["L"]))
+
     threads = 1
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
-        if w.backbone is not None and info:
+        if w.backbone is not None and info:        # only the Markov head calls BLAS
             threads = max(i.get("num_threads", 1) for i in info)
     except Exception:
         pass
-    return dict(value=N / dt, unit="verified draft tokens/s", cores=threads, kind="oracle",
-                sample=f"one full step of the workload (R={w.R}, N={N} verified drafts), "
-                       f"single process, {dt:.2f} s")
+    reps, N = 0, 0
+    t = time.perf_counter()
+    while True:
+        N = one_step()
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds:
+            break
+    return dict(value=N * reps / dt, unit="verified draft tokens/s", cores=threads, kind="oracle",
+                sample=f"{reps} full steps of the workload (R={w.R}, N={N} verified drafts per step), "
+                       f"{dt:.1f} s, one process")
 
 
 def copy_probe(gib):
@@ -245,8 +261,10 @@ def main():
         "cpu_baseline": cpu,
         "verify_only": {"us_per_step": main_res["verify_us"], "tokens_per_s": main_res["verify_tokens_per_s"]},
         "kernels": main_res["kernels"],
-        "variants": {k: {kk: v[kk] for kk in ("ms_per_step", "N", "rows", "tokens_per_s", "verify_us",
-                                                "verify_tokens_per_s", "dominant_gbps", "dominant_frac")}
+        "ms_per_step_instrumented": main_res["ms_per_step_instrumented"],
+        "variants": {k: {kk: v[kk] for kk in ("ms_per_step", "ms_per_step_instrumented", "N", "rows",
+                                                "tokens_per_s", "verify_us", "verify_tokens_per_s",
+                                                "dominant_gbps", "dominant_frac")}
                      for k, v in extra.items()},
         "source_hash": source_hash(),
     }

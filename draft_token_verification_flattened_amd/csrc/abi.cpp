@@ -24,8 +24,6 @@ bool g_timing = false;
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_free;
 std::map<std::string, std::pair<int, double>> g_done;
-std::string g_cur;
-hipEvent_t g_cur_a = nullptr;
 
 hipEvent_t take_event() {
     if (!g_free.empty()) {
@@ -49,20 +47,19 @@ int fail(int code, const char* fmt, ...) {
 
 void clear_error() { g_err[0] = 0; }
 
-void timing_before(const char* name, hipStream_t s) {
-    if (!g_timing) return;
-    g_cur = name;
-    g_cur_a = take_event();
-    if (g_cur_a) (void)hipEventRecord(g_cur_a, s);
+bool timing_on() { return g_timing; }
+
+void timing_events(hipEvent_t& start, hipEvent_t& stop) {
+    start = take_event();
+    stop = start ? take_event() : nullptr;
+    if (start && !stop) {
+        g_free.push_back(start);
+        start = nullptr;
+    }
 }
 
-void timing_after(hipStream_t s) {
-    if (!g_timing || !g_cur_a) return;
-    hipEvent_t b = take_event();
-    if (!b) return;
-    (void)hipEventRecord(b, s);
-    g_pending.push_back({g_cur, g_cur_a, b});
-    g_cur_a = nullptr;
+void timing_record(const char* name, hipEvent_t start, hipEvent_t stop) {
+    g_pending.push_back({name, start, stop});
 }
 
 }  // namespace specv

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "specv.h"
@@ -13,23 +14,32 @@ namespace specv {
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 
-// Timing hooks around one kernel launch (no-ops unless timing is enabled).
-void timing_before(const char* name, hipStream_t s);
-void timing_after(hipStream_t s);
+// Timing of launches (off unless enabled): start/stop events taken from the
+// kernel's own dispatch (hipExtLaunchKernel), so they bracket the kernel alone.
+bool timing_on();
+void timing_events(hipEvent_t& start, hipEvent_t& stop);
+void timing_record(const char* name, hipEvent_t start, hipEvent_t stop);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Launch `kernel` on `s` (with timing events when enabled) and check the launch.
+template <typename... KArgs, typename... Args>
+int launch_kernel(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                  hipStream_t s, Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (timing_on()) timing_events(e0, e1);
+    hipExtLaunchKernelGGL(kernel, grid, block, static_cast<std::uint32_t>(shmem), s, e0, e1, 0u, args...);
+    const hipError_t e = hipGetLastError();
+    if (e0 && e1) timing_record(name, e0, e1);
+    if (e != hipSuccess) return fail(SPECV_EDEVICE, "%s: launch failed: %s", name, hipGetErrorString(e));
+    return SPECV_OK;
+}
+
 }  // namespace specv
 
-// Launch a kernel, with timing and an error check. Returns SPECV_EDEVICE from
-// the enclosing function when the launch fails.
-#define SPECV_LAUNCH(name, stream, ...)                                              \
-    do {                                                                             \
-        ::specv::timing_before(name, stream);                                        \
-        __VA_ARGS__;                                                                 \
-        hipError_t e_ = hipGetLastError();                                           \
-        ::specv::timing_after(stream);                                               \
-        if (e_ != hipSuccess)                                                        \
-            return ::specv::fail(SPECV_EDEVICE, "%s: launch failed: %s", name,       \
-                                 hipGetErrorString(e_));                             \
+// Launch a kernel; returns the error code from the enclosing function on failure.
+#define SPECV_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                                  \
+    do {                                                                                            \
+        if (int e_ = ::specv::launch_kernel(name, kernel, grid, block, shmem, stream, __VA_ARGS__)) \
+            return e_;                                                                              \
     } while (0)

@@ -343,14 +343,14 @@ extern "C" int markov_draft(int mode, int dtype, int R, int k, int V, int d_m, c
         a.pos = i;
         if (dtype == SPECV_BF16) {
             if (vec4)
-                SPECV_LAUNCH("markov_logits", s, markov_logits_mfma<true><<<a.S, 256, lds, s>>>(a));
+                SPECV_LAUNCH("markov_logits", markov_logits_mfma<true>, a.S, 256, lds, s, a);
             else
-                SPECV_LAUNCH("markov_logits", s, markov_logits_mfma<false><<<a.S, 256, lds, s>>>(a));
-            SPECV_LAUNCH("markov_pick", s, markov_pick<SPECV_BF16><<<(R + 3) / 4, 256, 0, s>>>(a));
+                SPECV_LAUNCH("markov_logits", markov_logits_mfma<false>, a.S, 256, lds, s, a);
+            SPECV_LAUNCH("markov_pick", markov_pick<SPECV_BF16>, (R + 3) / 4, 256, 0, s, a);
         } else {
             const long items = long(R) * a.S;
-            SPECV_LAUNCH("markov_logits", s, markov_logits_fma<<<(items + 3) / 4, 256, 0, s>>>(a));
-            SPECV_LAUNCH("markov_pick", s, markov_pick<SPECV_F32><<<(R + 3) / 4, 256, 0, s>>>(a));
+            SPECV_LAUNCH("markov_logits", markov_logits_fma, (items + 3) / 4, 256, 0, s, a);
+            SPECV_LAUNCH("markov_pick", markov_pick<SPECV_F32>, (R + 3) / 4, 256, 0, s, a);
         }
     }
     return SPECV_OK;

@@ -398,7 +398,7 @@ extern "C" int spec_schedule(int R, int k, const float* conf_logit, const float*
     a.ws = static_cast<SchedWs*>(ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (max_len < 0 || max_len == 0) {
-        SPECV_LAUNCH("schedule", s, schedule_fixed<<<1, kSchedThreads, 0, s>>>(a));
+        SPECV_LAUNCH("schedule", schedule_fixed, 1, kSchedThreads, 0, s, a);
         return SPECV_OK;
     }
     // keys per workgroup: a power of two >= 16, enough for at most 256 workgroups
@@ -411,7 +411,7 @@ extern "C" int spec_schedule(int R, int k, const float* conf_logit, const float*
         hipFuncSetAttribute(reinterpret_cast<const void*>(schedule_rank),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
         return fail(SPECV_EDEVICE, "spec_schedule: cannot reserve %zu bytes of LDS", lds);
-    SPECV_LAUNCH("schedule", s, schedule_rank<<<groups, kSchedThreads, lds, s>>>(a, kw));
+    SPECV_LAUNCH("schedule", schedule_rank, groups, kSchedThreads, lds, s, a, kw);
     return SPECV_OK;
 }
 
@@ -427,7 +427,7 @@ extern "C" int spec_flatten(int R, int k, const int32_t* len_in, int32_t* tags_o
     a.R = R; a.k = k;
     a.len_in = len_in; a.tags = tags_out; a.cu_rows = cu_rows_out; a.n_rows = n_rows_out;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    SPECV_LAUNCH("flatten_offsets", s, flatten_offsets_kernel<<<1, kSchedThreads, 0, s>>>(a));
-    SPECV_LAUNCH("flatten_tags", s, flatten_tags_kernel<<<(R + 255) / 256, 256, 0, s>>>(a));
+    SPECV_LAUNCH("flatten_offsets", flatten_offsets_kernel, 1, kSchedThreads, 0, s, a);
+    SPECV_LAUNCH("flatten_tags", flatten_tags_kernel, (R + 255) / 256, 256, 0, s, a);
     return SPECV_OK;
 }

@@ -210,10 +210,12 @@ template <int E>
 __device__ __forceinline__ float2 chunk_softmax(const float (&x)[E], float c) {
     const float M = wave_max_dpp(lane_max(x)) * c;
     if (M == -INFINITY) return make_float2(-INFINITY, 0.f);
-    float acc = 0.f;
+    float acc[4];                                       // four chains for latency
 #pragma unroll
-    for (int q = 0; q < E; ++q) acc += __builtin_amdgcn_exp2f(fmaf(x[q], c, -M));
-    return make_float2(M, wave_sum_dpp(acc));
+    for (int q = 0; q < 4; ++q) acc[q] = __builtin_amdgcn_exp2f(fmaf(x[q], c, -M));
+#pragma unroll
+    for (int q = 4; q < E; ++q) acc[q % 4] += __builtin_amdgcn_exp2f(fmaf(x[q], c, -M));
+    return make_float2(M, wave_sum_dpp((acc[0] + acc[1]) + (acc[2] + acc[3])));
 }
 
 // (max, lowest index) of one chunk over the wave.
@@ -707,17 +709,17 @@ static int launch_verify(int mode, VerifyArgs& a, hipStream_t s) {
     if (mode == SPECV_GREEDY) {
         auto ks = verify_stream<DT, SPECV_GREEDY, VEC>;
         if (int e = persistent_grid(ks, long(a.Bmax) * a.C, cus, G)) return e;
-        SPECV_LAUNCH("verify_stream", s, ks<<<G, kThreads, 0, s>>>(a));
-        SPECV_LAUNCH("verify_decide", s, verify_decide<DT, SPECV_GREEDY, VEC><<<a.R, kDecideThreads, 0, s>>>(a));
+        SPECV_LAUNCH("verify_stream", ks, G, kThreads, 0, s, a);
+        SPECV_LAUNCH("verify_decide", verify_decide<DT, SPECV_GREEDY, VEC>, a.R, kDecideThreads, 0, s, a);
         return SPECV_OK;
     }
     auto ks = verify_stream<DT, SPECV_SAMPLE, VEC>;
     if (int e = persistent_grid(ks, 2L * a.Bmax * a.C, cus, G)) return e;
-    SPECV_LAUNCH("verify_stream", s, ks<<<G, kThreads, 0, s>>>(a));
-    SPECV_LAUNCH("verify_decide", s, verify_decide<DT, SPECV_SAMPLE, VEC><<<a.R, kDecideThreads, 0, s>>>(a));
+    SPECV_LAUNCH("verify_stream", ks, G, kThreads, 0, s, a);
+    SPECV_LAUNCH("verify_decide", verify_decide<DT, SPECV_SAMPLE, VEC>, a.R, kDecideThreads, 0, s, a);
     auto kr = verify_residual<DT, VEC>;
     if (int e = persistent_grid(kr, long(a.R) * a.C, cus, G)) return e;
-    SPECV_LAUNCH("verify_residual", s, kr<<<G, kThreads, 0, s>>>(a));
+    SPECV_LAUNCH("verify_residual", kr, G, kThreads, 0, s, a);
     return SPECV_OK;
 }
 
