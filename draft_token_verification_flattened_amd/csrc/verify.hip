@@ -71,12 +71,13 @@ struct VerifyArgs {
     RowRec* rec;                            // [Bmax]
     float4* rs_stat;                        // [R] (Mp, Zp, Mq, Zq) of the resample row
     int4* rs_row;                           // [R] (row t, a_r, kind: 0 residual / 1 done, 0)
+    int* rs_list;                           // [R] requests with a residual draw (hdr->count of them)
     float* mass;                            // [R * C] residual chunk masses
     int* rctr;                              // [R] residual chunks finished (zero between calls)
 };
 
 struct Layout {
-    size_t part_p, part_q, rec, rs_stat, rs_row, mass, rctr, total;
+    size_t part_p, part_q, rec, rs_stat, rs_row, rs_list, mass, rctr, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -91,6 +92,7 @@ static Layout ws_layout(int R, int k, int V) {
     l.rec = off;     off = align256(off + B * sizeof(RowRec));
     l.rs_stat = off; off = align256(off + size_t(R) * sizeof(float4));
     l.rs_row = off;  off = align256(off + size_t(R) * sizeof(int4));
+    l.rs_list = off; off = align256(off + size_t(R) * sizeof(int));
     l.mass = off;    off = align256(off + size_t(R) * C * sizeof(float));
     l.rctr = off;    off = align256(off + size_t(R) * sizeof(int));
     l.total = off;
@@ -253,7 +255,10 @@ __global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const long nw = long(gridDim.x) * kWaves;
     const long w = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr->status = 0u;   // later kernels of this call set bits
+    if (blockIdx.x == 0 && threadIdx.x == 0) {     // later kernels of this call update both
+        a.hdr->status = 0u;
+        a.hdr->count = 0u;
+    }
     const int nrows = min(max(*a.n_rows, 0), a.Bmax);
     const int nver = min(max(a.cu_rows[a.R], 0), nrows);
     const int C = a.C, CH = a.CH, V = a.V;
@@ -354,40 +359,43 @@ template <int DT, bool VEC, bool PAIR, class Wf>
 __device__ int chunk_pick(const typename Logit<DT>::T* trow, const typename Logit<DT>::T* drow, int beg,
                           int V, float base, float thr, Wf wt) {
     using RW = Raw<DT, VEC>;
-    constexpr int E = RW::kE, GW = RW::kVec;
+    constexpr int GW = RW::kVec;
     const int lane = threadIdx.x & (kWave - 1);
-    const int CH = chunk_elems(GW);
-    const bool full = beg + CH <= V;
+    const bool full = beg + chunk_elems(GW) <= V;
+    const int nv = VEC ? V / GW - beg / GW - lane : 0;
     RW rt, rd;
     rt.load(trow, beg, V, lane, full);
     if constexpr (PAIR) rd.load(drow, beg, V, lane, full);
-    float xt[E], xd[E];
-    rt.widen(beg, V, lane, full, xt);
-    if constexpr (PAIR) {
-        rd.widen(beg, V, lane, full, xd);
-    } else {
-#pragma unroll
-        for (int q = 0; q < E; ++q) xd[q] = 0.f;
-    }
-    float w[E];
-#pragma unroll
-    for (int q = 0; q < E; ++q) w[q] = xt[q] == -INFINITY ? 0.f : wt(xt[q], xd[q]);
     float run = base;
     int lastw = -1;
 #pragma unroll
     for (int u = 0; u < kNV; ++u) {                 // groups of 64 * GW elements, in index order
+        float xt[GW], xd[GW], w[GW];
+        if constexpr (VEC) {
+            RW::LT::unpack(rt.v[u], xt);
+            if constexpr (PAIR) RW::LT::unpack(rd.v[u], xd);
+        } else {
+#pragma unroll
+            for (int e = 0; e < GW; ++e) {
+                xt[e] = rt.s[u * GW + e];
+                if constexpr (PAIR) xd[e] = rd.s[u * GW + e];
+            }
+        }
+        const bool ok = !VEC || full || u * kWave < nv;
         float ls = 0.f;
 #pragma unroll
-        for (int e = 0; e < GW; ++e) ls += w[u * GW + e];
+        for (int e = 0; e < GW; ++e) {
+            w[e] = ok && xt[e] != -INFINITY ? wt(xt[e], PAIR ? xd[e] : 0.f) : 0.f;
+            ls += w[e];
+        }
         const float incl = wave_inclusive_scan(ls, lane);
         float cum = run + (incl - ls);
         int hit = INT_MAX;
 #pragma unroll
         for (int e = 0; e < GW; ++e) {
-            const float we = w[u * GW + e];
             const int off = beg + RW::offset(u * GW + e, lane);
-            cum += we;
-            if (we > 0.f) lastw = max(lastw, off);
+            cum += w[e];
+            if (w[e] > 0.f) lastw = max(lastw, off);
             if (hit == INT_MAX && cum > thr) hit = off;
         }
         const int f = wave_min_int(hit);
@@ -557,6 +565,7 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
         if (tid == 0) {
             a.rs_stat[r] = st;
             a.rs_row[r] = make_int4(t, acc, 0, 0);
+            a.rs_list[atomicAdd(&a.hdr->count, 1u)] = r;
         }
         return;
     }
@@ -581,43 +590,62 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
 // verify_residual
 // ---------------------------------------------------------------------------
 
+// Residual mass of one chunk of a row pair, one 16-byte vector (or group of
+// scalars) at a time so that few values are live at once.
+template <int DT, bool VEC>
+__device__ __forceinline__ float chunk_residual_mass(const Raw<DT, VEC>& rt, const Raw<DT, VEC>& rd, int beg, int V,
+                                                     int lane, float c, float4 st, float ip, float iq) {
+    using RW = Raw<DT, VEC>;
+    constexpr int GW = RW::kVec;
+    const bool full = beg + chunk_elems(GW) <= V;
+    const int nv = VEC ? V / GW - beg / GW - lane : 0;
+    float s[2] = {0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kNV; ++u) {
+        float xt[GW], xd[GW];
+        if constexpr (VEC) {
+            RW::LT::unpack(rt.v[u], xt);
+            RW::LT::unpack(rd.v[u], xd);
+        } else {
+#pragma unroll
+            for (int e = 0; e < GW; ++e) { xt[e] = rt.s[u * GW + e]; xd[e] = rd.s[u * GW + e]; }
+        }
+        const bool ok = !VEC || full || u * kWave < nv;
+        if (ok) {
+#pragma unroll
+            for (int e = 0; e < GW; ++e)
+                s[e & 1] += xt[e] == -INFINITY ? 0.f : residual_weight(xt[e], xd[e], c, st, ip, iq);
+        }
+    }
+    return wave_sum_dpp(s[0] + s[1]);
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_residual(VerifyArgs a) {
     using RW = Raw<DT, VEC>;
     using T = typename RW::T;
-    constexpr int E = RW::kE;
     const int lane = threadIdx.x & (kWave - 1);
     const long nw = long(gridDim.x) * kWaves;
     const long w = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
     const int C = a.C, CH = a.CH, V = a.V;
-    const long items = long(a.R) * C;
+    const int nres = min(int(a.hdr->count), a.R);
+    const long items = long(nres) * C;             // (residual request, chunk)
     const float c = a.c;
     long i = items * w / nw;
     const long iend = items * (w + 1) / nw;
     while (i < iend) {
-        // one run: the chunks of request r in this wavefront's share
-        const int r = int(i / C);
+        // one run: the chunks of one residual request in this wavefront's share
+        const int q = int(i / C);
         const int ch0 = int(i % C);
         const int n = int(min<long>(iend - i, C - ch0));
         i += n;
+        const int r = a.rs_list[q];
         const int4 rw = a.rs_row[r];
-        if (rw.z != 0) continue;                       // no residual draw for this request
         const float4 st = a.rs_stat[r];
         const int j = rw.y;
         const T* trow = static_cast<const T*>(a.target) + (long(r) * (a.k + 1) + j) * long(V);
         const T* drow = static_cast<const T*>(a.draft) + (long(r) * a.k + j) * long(V);
         const float ip = 1.f / st.y, iq = 1.f / st.w;
-        auto mass_of_chunk = [&](const RW& rt, const RW& rd, int ch) {
-            const int beg = ch * CH;
-            const bool full = beg + CH <= V;
-            float xt[E], xd[E];
-            rt.widen(beg, V, lane, full, xt);
-            rd.widen(beg, V, lane, full, xd);
-            float s = 0.f;
-#pragma unroll
-            for (int q = 0; q < E; ++q) s += xt[q] == -INFINITY ? 0.f : residual_weight(xt[q], xd[q], c, st, ip, iq);
-            return wave_sum_dpp(s);
-        };
         auto issue = [&](RW& rt, RW& rd, int ch) {
             const int beg = ch * CH;
             const bool full = beg + CH <= V;
@@ -626,14 +654,14 @@ __global__ __launch_bounds__(kThreads) void verify_residual(VerifyArgs a) {
         };
         RW t0, d0, t1, d1;
         issue(t0, d0, ch0);
-        for (int q = 0; q < n; q += 2) {
-            if (q + 1 < n) issue(t1, d1, ch0 + q + 1);
-            const float m0 = mass_of_chunk(t0, d0, ch0 + q);
-            if (lane == 0) put(&a.mass[long(r) * C + ch0 + q], m0);
-            if (q + 1 >= n) break;
-            if (q + 2 < n) issue(t0, d0, ch0 + q + 2);
-            const float m1 = mass_of_chunk(t1, d1, ch0 + q + 1);
-            if (lane == 0) put(&a.mass[long(r) * C + ch0 + q + 1], m1);
+        for (int m = 0; m < n; m += 2) {
+            if (m + 1 < n) issue(t1, d1, ch0 + m + 1);
+            const float m0 = chunk_residual_mass(t0, d0, (ch0 + m) * CH, V, lane, c, st, ip, iq);
+            if (lane == 0) put(&a.mass[long(r) * C + ch0 + m], m0);
+            if (m + 1 >= n) break;
+            if (m + 2 < n) issue(t0, d0, ch0 + m + 2);
+            const float m1 = chunk_residual_mass(t1, d1, (ch0 + m + 1) * CH, V, lane, c, st, ip, iq);
+            if (lane == 0) put(&a.mass[long(r) * C + ch0 + m + 1], m1);
         }
         int last = 0;
         if (lane == 0) {
@@ -763,6 +791,8 @@ extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void*
     if (ws_bytes < lay.total)
         return fail(SPECV_EINVAL, "spec_verify: workspace of %zu bytes, need %zu", ws_bytes, lay.total);
 
+    if (long(R) * (k + 1) * 2 * ((V + chunk_elems(4) - 1) / chunk_elems(4)) > INT_MAX)
+        return fail(SPECV_EUNSUPPORTED, "spec_verify: R*(k+1)*V too large for one call");
     const int esize = dtype == SPECV_BF16 ? 2 : 4;
     const int vecw = 16 / esize;
     const bool vec = (V % vecw) == 0 && aligned16(target_logits) &&
@@ -791,6 +821,7 @@ extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void*
     a.rec = reinterpret_cast<RowRec*>(w + lay.rec);
     a.rs_stat = reinterpret_cast<float4*>(w + lay.rs_stat);
     a.rs_row = reinterpret_cast<int4*>(w + lay.rs_row);
+    a.rs_list = reinterpret_cast<int*>(w + lay.rs_list);
     a.mass = reinterpret_cast<float*>(w + lay.mass);
     a.rctr = reinterpret_cast<int*>(w + lay.rctr);
     hipStream_t s = static_cast<hipStream_t>(stream);
