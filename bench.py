@@ -105,7 +105,7 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
     B.timing_enable(False)
     ms_step = t0.elapsed_time(t1) / steps
     kern = {}
-    for name in ("markov_logits", "markov_pick", "schedule", "verify_stream", "verify_decide", "verify_residual"):
+    for name in ("markov_logits", "markov_pick", "schedule", "verify_stream", "verify_decide"):
         n, tot = B.timing_read(name)
         if n:
             kern[name] = dict(launches_per_step=n / steps, avg_us=1000.0 * tot / n)
@@ -123,7 +123,7 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
     dom = kern.get(DOMINANT)
     achieved = nbytes / (dom["avg_us"] * 1e-6) if dom else None
     verify_us = sum(kern[k]["avg_us"] * kern[k]["launches_per_step"]
-                    for k in ("verify_stream", "verify_decide", "verify_residual") if k in kern)
+                    for k in ("verify_stream", "verify_decide") if k in kern)
     return dict(mode=mode, max_len=max_len, ms_per_step=ms_plain, ms_per_step_instrumented=ms_step, N=N,
                 rows=int(d.host("n_rows")[0]), tokens_per_s=N / (ms_plain * 1e-3), verify_us=verify_us,
                 verify_tokens_per_s=N / (verify_us * 1e-6) if verify_us else None,

@@ -22,7 +22,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "specv.h")
 OK, EINVAL, EUNSUPPORTED, EDEVICE = 0, -1, -2, -3
 BF16, F32 = 0, 1
 GREEDY, SAMPLE = 0, 1
-STATUS_BAD_TOKEN, STATUS_BAD_TAG, STATUS_TIMEOUT = 1, 2, 4
+STATUS_BAD_TOKEN, STATUS_BAD_TAG = 1, 2
 MAX_K, MAX_SCHED_ITEMS = 32, 16384
 
 _c_int, _c_size, _c_ptr = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
@@ -154,8 +154,9 @@ def verify_workspace_bytes(mode: int, R: int, k: int, V: int) -> int:
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A zero-filled device byte buffer for the ws argument (torch allocations
-    are 256-byte aligned; the library keeps it zeroed between calls)."""
+    """A zero-filled device byte buffer for a ws argument (torch allocations
+    are 256-byte aligned). spec_schedule needs its workspace zeroed before the
+    first call and leaves it zeroed; the other calls need no initialisation."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 

@@ -11,13 +11,10 @@ namespace specv {
 constexpr int kWave = 64;   // CDNA wavefront width
 
 // Workspace header, padded to 256 bytes. `status` holds the data-error bits of
-// the last completed call (specv_read_status reads this first word); `count`
-// is scratch of a running call (spec_verify: the number of requests that need
-// a residual draw).
+// the last completed call (specv_read_status reads this first word).
 struct WsHeader {
     uint32_t status;
-    uint32_t count;
-    uint32_t pad[62];
+    uint32_t pad[63];
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

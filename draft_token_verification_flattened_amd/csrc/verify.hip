@@ -22,16 +22,16 @@
 //                    softmax state (M, S) of the chunk in sampling mode (M = max
 //                    of logit * log2(e) / tau, S = sum of exp2(that - M)). No
 //                    atomics, no waits: all of the step's logit traffic is here.
-//   verify_decide    one workgroup per request: merges each row's chunk
-//                    partials, decides every verified row, finds the first
-//                    rejection a_r and writes the accepted length and tokens.
-//                    Greedy: complete. Sampling with every row kept: draws the
-//                    bonus token from p of the bonus row (chunk masses from the
-//                    partials, then an in-order scan of one chunk).
-//   verify_residual  sampling, requests with a_r < L_r: re-reads the rejected
-//                    row pair for the chunk masses of max(0, p - q); the last
-//                    wavefront of a request to finish (device-scope counter)
-//                    draws the token by the inverse CDF.
+//   verify_decide    one 1024-thread workgroup per request: merges each row's
+//                    chunk partials, decides every verified row, finds the
+//                    first rejection a_r and writes the accepted length and
+//                    tokens. Greedy: complete. Sampling: a request with
+//                    a_r < L_r re-reads its rejected row pair with all 16
+//                    wavefronts for the chunk masses of max(0, p - q) (kept in
+//                    LDS) and draws the token by the inverse CDF; with every
+//                    row kept it draws the bonus token from p of the bonus row
+//                    (chunk masses from the partials). No cross-workgroup
+//                    exchange anywhere.
 #include <climits>
 
 #include "common.h"
@@ -41,7 +41,8 @@ namespace specv {
 
 constexpr int kThreads = 256;               // 4 wavefronts per workgroup
 constexpr int kWaves = kThreads / kWave;
-constexpr int kDecideThreads = 512;         // verify_decide: 8 rows of a request at a time
+constexpr int kDecideThreads = 1024;        // verify_decide: 16 wavefronts per request
+constexpr int kMaxChunks = 4096;            // sampling: chunks per row (residual masses live in LDS)
 constexpr int kNV = 4;                      // 16-byte vectors per lane per item
 constexpr int kChunkVecs = kWave * kNV;     // vectors per chunk
 
@@ -69,15 +70,10 @@ struct VerifyArgs {
     float2* part_p;                         // [Bmax * C] target chunk partials
     float2* part_q;                         // [Bmax * C] draft chunk partials (sampling)
     RowRec* rec;                            // [Bmax]
-    float4* rs_stat;                        // [R] (Mp, Zp, Mq, Zq) of the resample row
-    int4* rs_row;                           // [R] (row t, a_r, kind: 0 residual / 1 done, 0)
-    int* rs_list;                           // [R] requests with a residual draw (hdr->count of them)
-    float* mass;                            // [R * C] residual chunk masses
-    int* rctr;                              // [R] residual chunks finished (zero between calls)
 };
 
 struct Layout {
-    size_t part_p, part_q, rec, rs_stat, rs_row, rs_list, mass, rctr, total;
+    size_t part_p, part_q, rec, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -90,40 +86,8 @@ static Layout ws_layout(int R, int k, int V) {
     l.part_p = off;  off = align256(off + B * C * sizeof(float2));
     l.part_q = off;  off = align256(off + B * C * sizeof(float2));
     l.rec = off;     off = align256(off + B * sizeof(RowRec));
-    l.rs_stat = off; off = align256(off + size_t(R) * sizeof(float4));
-    l.rs_row = off;  off = align256(off + size_t(R) * sizeof(int4));
-    l.rs_list = off; off = align256(off + size_t(R) * sizeof(int));
-    l.mass = off;    off = align256(off + size_t(R) * C * sizeof(float));
-    l.rctr = off;    off = align256(off + size_t(R) * sizeof(int));
     l.total = off;
     return l;
-}
-
-// ---------------------------------------------------------------------------
-// Device-coherent exchange of the residual chunk masses inside verify_residual:
-// relaxed device-scope atomics, which gfx950 performs at the device-coherent
-// level (stores write through, loads bypass the per-XCD L2). A writer waits
-// for its stores to complete before it bumps the request's counter; the reader
-// loads only after the counter says every chunk is in.
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ void put(float* p, float v) {
-    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float get(const float* p) {
-    return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)),
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ void publish() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-__device__ __forceinline__ int bump(int* p, int v) {
-    const int old = __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    return old;
 }
 
 // ---------------------------------------------------------------------------
@@ -255,10 +219,7 @@ __global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const long nw = long(gridDim.x) * kWaves;
     const long w = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {     // later kernels of this call update both
-        a.hdr->status = 0u;
-        a.hdr->count = 0u;
-    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr->status = 0u;   // verify_decide sets bits later
     const int nrows = min(max(*a.n_rows, 0), a.Bmax);
     const int nver = min(max(a.cu_rows[a.R], 0), nrows);
     const int C = a.C, CH = a.CH, V = a.V;
@@ -356,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
 // `base`, in index order, exceeds thr; else the last element with positive
 // weight (beg if none).
 template <int DT, bool VEC, bool PAIR, class Wf>
-__device__ int chunk_pick(const typename Logit<DT>::T* trow, const typename Logit<DT>::T* drow, int beg,
+__device__ __forceinline__ int chunk_pick(const typename Logit<DT>::T* trow, const typename Logit<DT>::T* drow, int beg,
                           int V, float base, float thr, Wf wt) {
     using RW = Raw<DT, VEC>;
     constexpr int GW = RW::kVec;
@@ -364,8 +325,10 @@ __device__ int chunk_pick(const typename Logit<DT>::T* trow, const typename Logi
     const bool full = beg + chunk_elems(GW) <= V;
     const int nv = VEC ? V / GW - beg / GW - lane : 0;
     RW rt, rd;
-    rt.load(trow, beg, V, lane, full);
-    if constexpr (PAIR) rd.load(drow, beg, V, lane, full);
+    if constexpr (VEC) {                            // scalar rows load group by group below
+        rt.load(trow, beg, V, lane, full);
+        if constexpr (PAIR) rd.load(drow, beg, V, lane, full);
+    }
     float run = base;
     int lastw = -1;
 #pragma unroll
@@ -377,8 +340,9 @@ __device__ int chunk_pick(const typename Logit<DT>::T* trow, const typename Logi
         } else {
 #pragma unroll
             for (int e = 0; e < GW; ++e) {
-                xt[e] = rt.s[u * GW + e];
-                if constexpr (PAIR) xd[e] = rd.s[u * GW + e];
+                const int x = beg + RW::offset(u * GW + e, lane);
+                xt[e] = x < V ? RW::LT::load1(trow + x) : -INFINITY;
+                if constexpr (PAIR) xd[e] = x < V ? RW::LT::load1(drow + x) : -INFINITY;
             }
         }
         const bool ok = !VEC || full || u * kWave < nv;
@@ -411,7 +375,7 @@ __device__ int chunk_pick(const typename Logit<DT>::T* trow, const typename Logi
 // `base`; without a crossing (rounding), the last chunk with positive mass and
 // an in-chunk threshold of +inf.
 template <class Mf>
-__device__ int wave_find_chunk(int C, float u, Mf mass_of, float& base, float& cthr) {
+__device__ __forceinline__ int wave_find_chunk(int C, float u, Mf mass_of, float& base, float& cthr) {
     const int lane = threadIdx.x & (kWave - 1);
     float total = 0.f;
     for (int c0 = 0; c0 < C; c0 += kWave) {
@@ -439,162 +403,22 @@ __device__ int wave_find_chunk(int C, float u, Mf mass_of, float& base, float& c
     return last_pos < 0 ? 0 : last_pos;
 }
 
-// max(0, p - q) of one element, given the resample row's (Mp, Zp, Mq, Zq) in
-// st and the reciprocals ip = 1/Zp, iq = 1/Zq.
-__device__ __forceinline__ float residual_weight(float xt, float xd, float c, float4 st, float ip, float iq) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(xt, c, -st.x)) * ip;
-    const float q = __builtin_amdgcn_exp2f(fmaf(xd, c, -st.z)) * iq;
-    return fmaxf(p - q, 0.f);
+// max(0, p - q) of one element. lp = Mp + log2 Zp and lq = Mq + log2 Zq are
+// the base-2 log-normalisers of the row pair, so p = exp2(xt * c - lp) with the
+// normaliser folded into the exponent. A -inf logit gives probability 0.
+__device__ __forceinline__ float residual_weight(float xt, float xd, float c, float lp, float lq) {
+    return fmaxf(__builtin_amdgcn_exp2f(fmaf(xt, c, -lp)) - __builtin_amdgcn_exp2f(fmaf(xd, c, -lq)), 0.f);
 }
 
 // ---------------------------------------------------------------------------
 // verify_decide
 // ---------------------------------------------------------------------------
 
-template <int DT, int MODE, bool VEC>
-__global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
-    using LT = Logit<DT>;
-    using T = typename LT::T;
-    constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
-    constexpr int kW = kDecideThreads / kWave;
-    __shared__ int keep_s[SPECV_MAX_K + 1];
-    __shared__ int g_s[SPECV_MAX_K + 1];
-    __shared__ float4 st_s[SPECV_MAX_K + 1];
-    __shared__ int bad_s;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = blockIdx.x;
-    const int k = a.k, C = a.C;
-    const int nrows = min(max(*a.n_rows, 0), a.Bmax);
-    const int N = a.cu_rows[a.R];
-    const int base = a.cu_rows[r];
-    const int L = a.cu_rows[r + 1] - base;
-    int32_t* out = a.out_tokens + long(r) * (k + 1);
-    if (tid == 0) bad_s = L < 0 || L > k || base < 0 || base + L > N || N < 0 || N + r >= nrows;
-    __syncthreads();
-
-    if (!bad_s) {
-        for (int j = wave; j <= L; j += kW) {
-            const bool verified = j < L;
-            const int t = verified ? base + j : N + r;
-            if (lane == 0 && (a.tags[2 * t] != r || a.tags[2 * t + 1] != j)) bad_s = 1;
-            if (!SAMPLE) {
-                float gv = -INFINITY;
-                int gi = INT_MAX;
-                for (int cc = lane; cc < C; cc += kWave) {
-                    const float2 p = a.part_p[long(t) * C + cc];
-                    argmax_merge(gv, gi, p.x, __float_as_int(p.y));
-                }
-                wave_argmax(gv, gi);
-                if (lane == 0) {
-                    const int y = gi == INT_MAX ? 0 : gi;
-                    bool keep = false;
-                    if (verified) {
-                        const int x = a.tokens[long(r) * k + j];
-                        if (x < 0 || x >= a.V) atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TOKEN);
-                        keep = x == y;
-                    }
-                    keep_s[j] = keep;
-                    g_s[j] = y;
-                    if (a.diag)
-                        reinterpret_cast<float4*>(a.diag)[t] =
-                            make_float4(float(y), gv, 0.f, verified ? (keep ? 1.f : 0.f) : -1.f);
-                }
-            } else {
-                float mp = -INFINITY, zp = 0.f, mq = -INFINITY, zq = 0.f;
-                for (int cc = lane; cc < C; cc += kWave) {
-                    const float2 p = a.part_p[long(t) * C + cc];
-                    lse_merge(mp, zp, p.x, p.y);
-                    if (verified) {
-                        const float2 q = a.part_q[long(t) * C + cc];
-                        lse_merge(mq, zq, q.x, q.y);
-                    }
-                }
-                wave_lse(mp, zp);
-                if (verified) wave_lse(mq, zq);
-                if (lane == 0) {
-                    st_s[j] = make_float4(mp, zp, mq, zq);
-                    bool keep = false;
-                    if (verified) {
-                        const int x = a.tokens[long(r) * k + j];
-                        const bool xok = x >= 0 && x < a.V;
-                        float px = 0.f, qx = 0.f, ratio = 0.f;
-                        if (xok) {
-                            const RowRec rc = a.rec[t];
-                            px = exp2f(fmaf(rc.ax, a.c, -mp)) / zp;
-                            qx = exp2f(fmaf(rc.bx, a.c, -mq)) / zq;
-                            ratio = qx > 0.f ? px / qx : INFINITY;
-                            keep = a.uniforms[long(r) * (k + 1) + j] < fminf(1.f, ratio);
-                        } else {
-                            atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TOKEN);
-                        }
-                        if (a.diag)
-                            reinterpret_cast<float4*>(a.diag)[t] = make_float4(px, qx, ratio, keep ? 1.f : 0.f);
-                    } else if (a.diag) {
-                        reinterpret_cast<float4*>(a.diag)[t] = make_float4(0.f, 0.f, 0.f, -1.f);
-                    }
-                    keep_s[j] = keep;
-                }
-            }
-        }
-    }
-    __syncthreads();
-    if (bad_s) {
-        if (tid == 0) {
-            atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TAG);
-            a.acc_len[r] = 0;
-            if (SAMPLE) a.rs_row[r] = make_int4(-1, 0, 1, 0);
-        }
-        if (tid <= k) out[tid] = -1;
-        return;
-    }
-    int acc = L;
-    for (int j = 0; j < L; ++j)
-        if (!keep_s[j]) { acc = j; break; }
-    if (tid <= k) {
-        int v = -1;
-        if (tid < acc) v = a.tokens[long(r) * k + tid];
-        else if (tid == acc && !SAMPLE) v = g_s[acc];
-        out[tid] = v;
-    }
-    if (tid == 0) a.acc_len[r] = acc;
-    if (!SAMPLE) return;
-
-    const int t = acc < L ? base + acc : N + r;
-    const float4 st = st_s[acc];
-    if (acc < L) {                                 // residual draw in verify_residual
-        if (tid == 0) {
-            a.rs_stat[r] = st;
-            a.rs_row[r] = make_int4(t, acc, 0, 0);
-            a.rs_list[atomicAdd(&a.hdr->count, 1u)] = r;
-        }
-        return;
-    }
-    // every row kept: bonus token from p of the bonus row (masses relative to Mp)
-    if (tid == 0) a.rs_row[r] = make_int4(t, acc, 1, 0);
-    if (wave != 0) return;
-    const float u = a.uniforms[long(r) * (k + 1) + k];
-    float cbase, cthr;
-    const int cs = wave_find_chunk(C, u, [&](int cc) {
-        const float2 p = a.part_p[long(t) * C + cc];
-        return p.x == -INFINITY ? 0.f : p.y * exp2f(p.x - st.x);
-    }, cbase, cthr);
-    const T* trow = static_cast<const T*>(a.target) + (long(r) * (k + 1) + acc) * long(a.V);
-    const float cc_ = a.c, Mp = st.x;
-    const int y = chunk_pick<DT, VEC, false>(trow, nullptr, cs * a.CH, a.V, cbase, cthr, [&](float xt, float) {
-        return __builtin_amdgcn_exp2f(fmaf(xt, cc_, -Mp));
-    });
-    if (lane == 0) out[acc] = y;
-}
-
-// ---------------------------------------------------------------------------
-// verify_residual
-// ---------------------------------------------------------------------------
-
 // Residual mass of one chunk of a row pair, one 16-byte vector (or group of
 // scalars) at a time so that few values are live at once.
 template <int DT, bool VEC>
 __device__ __forceinline__ float chunk_residual_mass(const Raw<DT, VEC>& rt, const Raw<DT, VEC>& rd, int beg, int V,
-                                                     int lane, float c, float4 st, float ip, float iq) {
+                                                     int lane, float c, float lp, float lq) {
     using RW = Raw<DT, VEC>;
     constexpr int GW = RW::kVec;
     const bool full = beg + chunk_elems(GW) <= V;
@@ -614,94 +438,200 @@ __device__ __forceinline__ float chunk_residual_mass(const Raw<DT, VEC>& rt, con
         if (ok) {
 #pragma unroll
             for (int e = 0; e < GW; ++e)
-                s[e & 1] += xt[e] == -INFINITY ? 0.f : residual_weight(xt[e], xd[e], c, st, ip, iq);
+                s[e & 1] += residual_weight(xt[e], xd[e], c, lp, lq);
         }
     }
     return wave_sum_dpp(s[0] + s[1]);
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void verify_residual(VerifyArgs a) {
+// Softmax state (M, S) of a row from its chunk partials, or (argmax value,
+// lowest index) in greedy mode: one wavefront, the first 4 * 64 partials
+// loaded in one round.
+template <bool SAMPLE>
+__device__ __forceinline__ float2 merge_partials(const float2* part, int C, int lane) {
+    constexpr int kPre = 4;
+    float2 v[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int cc = lane + u * kWave;
+        v[u] = cc < C ? part[cc] : (SAMPLE ? make_float2(-INFINITY, 0.f) : make_float2(-INFINITY, __int_as_float(INT_MAX)));
+    }
+    float m = -INFINITY, z = 0.f;
+    int gi = INT_MAX;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        if (SAMPLE) lse_merge(m, z, v[u].x, v[u].y);
+        else argmax_merge(m, gi, v[u].x, __float_as_int(v[u].y));
+    }
+    for (int cc = lane + kPre * kWave; cc < C; cc += kWave) {
+        const float2 p = part[cc];
+        if (SAMPLE) lse_merge(m, z, p.x, p.y);
+        else argmax_merge(m, gi, p.x, __float_as_int(p.y));
+    }
+    if (SAMPLE) {
+        const float M = wave_max_dpp(m);
+        const float zs = wave_sum_dpp(m == -INFINITY ? 0.f : z * exp2f(m - M));
+        return make_float2(M, zs);
+    }
+    wave_argmax_dpp(m, gi);
+    return make_float2(m, __int_as_float(gi));
+}
+
+// One workgroup per request. Phase 1: wavefront j merges the partials of row
+// j of the request, decides it, and the first rejection a_r follows. Phase 2
+// (sampling): a request with a_r < L_r streams its rejected row pair, all
+// wavefronts together, into per-chunk residual masses in LDS; wavefront 0 then
+// draws by the inverse CDF (chunk, then position in the chunk). With every row
+// kept, wavefront 0 draws the bonus token from p of the bonus row, chunk masses
+// taken from the partials.
+template <int DT, int MODE, bool VEC>
+__global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
     using RW = Raw<DT, VEC>;
     using T = typename RW::T;
-    const int lane = threadIdx.x & (kWave - 1);
-    const long nw = long(gridDim.x) * kWaves;
-    const long w = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    const int C = a.C, CH = a.CH, V = a.V;
-    const int nres = min(int(a.hdr->count), a.R);
-    const long items = long(nres) * C;             // (residual request, chunk)
-    const float c = a.c;
-    long i = items * w / nw;
-    const long iend = items * (w + 1) / nw;
-    while (i < iend) {
-        // one run: the chunks of one residual request in this wavefront's share
-        const int q = int(i / C);
-        const int ch0 = int(i % C);
-        const int n = int(min<long>(iend - i, C - ch0));
-        i += n;
-        const int r = a.rs_list[q];
-        const int4 rw = a.rs_row[r];
-        const float4 st = a.rs_stat[r];
-        const int j = rw.y;
-        const T* trow = static_cast<const T*>(a.target) + (long(r) * (a.k + 1) + j) * long(V);
-        const T* drow = static_cast<const T*>(a.draft) + (long(r) * a.k + j) * long(V);
-        const float ip = 1.f / st.y, iq = 1.f / st.w;
-        auto issue = [&](RW& rt, RW& rd, int ch) {
-            const int beg = ch * CH;
-            const bool full = beg + CH <= V;
-            rt.load(trow, beg, V, lane, full);
-            rd.load(drow, beg, V, lane, full);
-        };
-        RW t0, d0, t1, d1;
-        issue(t0, d0, ch0);
-        for (int m = 0; m < n; m += 2) {
-            if (m + 1 < n) issue(t1, d1, ch0 + m + 1);
-            const float m0 = chunk_residual_mass(t0, d0, (ch0 + m) * CH, V, lane, c, st, ip, iq);
-            if (lane == 0) put(&a.mass[long(r) * C + ch0 + m], m0);
-            if (m + 1 >= n) break;
-            if (m + 2 < n) issue(t0, d0, ch0 + m + 2);
-            const float m1 = chunk_residual_mass(t1, d1, (ch0 + m + 1) * CH, V, lane, c, st, ip, iq);
-            if (lane == 0) put(&a.mass[long(r) * C + ch0 + m + 1], m1);
+    constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
+    constexpr int kW = kDecideThreads / kWave;
+    __shared__ int keep_s[SPECV_MAX_K + 1];
+    __shared__ int g_s[SPECV_MAX_K + 1];
+    __shared__ float4 st_s[SPECV_MAX_K + 1];
+    __shared__ float mass_s[SAMPLE ? kMaxChunks : 1];
+    __shared__ int bad_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = blockIdx.x;
+    const int k = a.k, C = a.C, CH = a.CH, V = a.V;
+    const int nrows = min(max(*a.n_rows, 0), a.Bmax);
+    const int N = a.cu_rows[a.R];
+    const int base = a.cu_rows[r];
+    const int L = a.cu_rows[r + 1] - base;
+    const float ub = SAMPLE ? a.uniforms[long(r) * (k + 1) + k] : 0.f;
+    int32_t* out = a.out_tokens + long(r) * (k + 1);
+    if (tid == 0) bad_s = L < 0 || L > k || base < 0 || base + L > N || N < 0 || N + r >= nrows;
+    __syncthreads();
+
+    if (!bad_s) {
+        for (int j = wave; j <= L; j += kW) {
+            const bool verified = j < L;
+            const int t = verified ? base + j : N + r;
+            // independent loads first: one round of latency with the partials
+            const int tag_r = a.tags[2 * t], tag_j = a.tags[2 * t + 1];
+            const int x = verified ? a.tokens[long(r) * k + j] : 0;
+            float uj = 0.f;
+            RowRec rc{0.f, 0.f};
+            if (SAMPLE && verified) {
+                uj = a.uniforms[long(r) * (k + 1) + j];
+                rc = a.rec[t];
+            }
+            const float2 P = merge_partials<SAMPLE>(a.part_p + long(t) * C, C, lane);
+            float2 Q = make_float2(-INFINITY, 0.f);
+            if (SAMPLE && verified) Q = merge_partials<true>(a.part_q + long(t) * C, C, lane);
+            if (lane != 0) continue;               // lane 0 decides the row
+            if (tag_r != r || tag_j != j) bad_s = 1;
+            const bool xok = x >= 0 && x < V;
+            if (verified && !xok) atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TOKEN);
+            bool keep = false;
+            if (!SAMPLE) {
+                const int gi = __float_as_int(P.y);
+                const int y = gi == INT_MAX ? 0 : gi;
+                keep = verified && x == y;
+                g_s[j] = y;
+                if (a.diag)
+                    reinterpret_cast<float4*>(a.diag)[t] =
+                        make_float4(float(y), P.x, 0.f, verified ? (keep ? 1.f : 0.f) : -1.f);
+            } else {
+                st_s[j] = make_float4(P.x, P.y, Q.x, Q.y);
+                float px = 0.f, qx = 0.f, ratio = 0.f;
+                if (verified && xok) {
+                    px = exp2f(fmaf(rc.ax, a.c, -P.x)) / P.y;
+                    qx = exp2f(fmaf(rc.bx, a.c, -Q.x)) / Q.y;
+                    ratio = qx > 0.f ? px / qx : INFINITY;
+                    keep = uj < fminf(1.f, ratio);
+                }
+                if (a.diag)
+                    reinterpret_cast<float4*>(a.diag)[t] =
+                        verified ? make_float4(px, qx, ratio, keep ? 1.f : 0.f) : make_float4(0.f, 0.f, 0.f, -1.f);
+            }
+            keep_s[j] = keep;
         }
-        int last = 0;
-        if (lane == 0) {
-            publish();
-            last = bump(&a.rctr[r], n) + n == C;
+    }
+    __syncthreads();
+    if (bad_s) {
+        if (tid == 0) {
+            atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TAG);
+            a.acc_len[r] = 0;
         }
-        last = __shfl(last, 0, kWave);
-        if (!last) continue;
-        // every chunk of this request is in: draw from the residual (from p when
-        // the residual has no mass), then reset the counter for the next call
-        auto mass_of = [&](int cc) { return get(&a.mass[long(r) * C + cc]); };
+        if (tid <= k) out[tid] = -1;
+        return;
+    }
+    int acc = L;
+    for (int j = 0; j < L; ++j)
+        if (!keep_s[j]) { acc = j; break; }
+    if (tid <= k) {
+        int v = -1;
+        if (tid < acc) v = a.tokens[long(r) * k + tid];
+        else if (tid == acc && !SAMPLE) v = g_s[acc];
+        out[tid] = v;
+    }
+    if (tid == 0) a.acc_len[r] = acc;
+    if constexpr (SAMPLE) {
+        const float4 st = st_s[acc];
+        const float c = a.c, lp = st.x + log2f(st.y), lq = st.z + log2f(st.w);
+        const T* trow = static_cast<const T*>(a.target) + (long(r) * (k + 1) + acc) * long(V);
+        const T* drow = static_cast<const T*>(a.draft) + (long(r) * k + min(acc, k - 1)) * long(V);
+        const bool rejected = acc < L;
+        if (rejected) {
+            // the rejected row pair, chunk w, w + kW, ... per wavefront, two in flight
+            auto issue = [&](RW& rt, RW& rd, int ch) {
+                const int beg = ch * CH;
+                const bool full = beg + CH <= V;
+                rt.load(trow, beg, V, lane, full);
+                rd.load(drow, beg, V, lane, full);
+            };
+            RW t0, d0;
+            if constexpr (!VEC) {                  // scalar rows: one chunk at a time (registers)
+                for (int ch = wave; ch < C; ch += kW) {
+                    issue(t0, d0, ch);
+                    const float m0 = chunk_residual_mass(t0, d0, ch * CH, V, lane, c, lp, lq);
+                    if (lane == 0) mass_s[ch] = m0;
+                }
+            }
+            RW t1, d1;
+            int ch = VEC ? wave : C;
+            if (ch < C) issue(t0, d0, ch);
+            while (ch < C) {
+                const int c1 = ch + kW;
+                if (c1 < C) issue(t1, d1, c1);
+                const float m0 = chunk_residual_mass(t0, d0, ch * CH, V, lane, c, lp, lq);
+                if (lane == 0) mass_s[ch] = m0;
+                if (c1 >= C) break;
+                const int c2 = c1 + kW;
+                if (c2 < C) issue(t0, d0, c2);
+                const float m1 = chunk_residual_mass(t1, d1, c1 * CH, V, lane, c, lp, lq);
+                if (lane == 0) mass_s[c1] = m1;
+                ch = c2;
+            }
+        }
+        __syncthreads();
+        if (wave != 0) return;
         float total = 0.f;
-        for (int c0 = 0; c0 < C; c0 += kWave) total += wave_sum(c0 + lane < C ? mass_of(c0 + lane) : 0.f);
-        const bool residual = total > 0.f;
-        const float u = a.uniforms[long(r) * (a.k + 1) + a.k];
+        if (rejected)
+            for (int c0 = 0; c0 < C; c0 += kWave) total += wave_sum_dpp(c0 + lane < C ? mass_s[c0 + lane] : 0.f);
         float cbase, cthr;
-        int cs;
-        if (residual) {
-            cs = wave_find_chunk(C, u, mass_of, cbase, cthr);
-        } else {
-            const int t = rw.x;
-            cs = wave_find_chunk(C, u, [&](int cc) {
-                const float2 p = a.part_p[long(t) * C + cc];
-                return p.x == -INFINITY ? 0.f : p.y * exp2f(p.x - st.x);
-            }, cbase, cthr);
-        }
-        const int b2 = cs * CH;
         int y;
-        if (residual)
-            y = chunk_pick<DT, VEC, true>(trow, drow, b2, V, cbase, cthr, [&](float xt_, float xd_) {
-                return residual_weight(xt_, xd_, c, st, ip, iq);
+        if (total > 0.f) {                         // residual max(0, p - q) of row a_r
+            const int cs = wave_find_chunk(C, ub, [&](int cc) { return mass_s[cc]; }, cbase, cthr);
+            y = chunk_pick<DT, VEC, true>(trow, drow, cs * CH, V, cbase, cthr, [&](float xt_, float xd_) {
+                return residual_weight(xt_, xd_, c, lp, lq);
             });
-        else
-            y = chunk_pick<DT, VEC, false>(trow, nullptr, b2, V, cbase, cthr, [&](float xt_, float) {
+        } else {                                   // p of row a_r: the bonus row, or a residual without mass
+            const float2* pp = a.part_p + long(rejected ? base + acc : N + r) * C;
+            const int cs = wave_find_chunk(C, ub, [&](int cc) {
+                const float2 q = pp[cc];
+                return q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
+            }, cbase, cthr);
+            y = chunk_pick<DT, VEC, false>(trow, nullptr, cs * CH, V, cbase, cthr, [&](float xt_, float) {
                 return __builtin_amdgcn_exp2f(fmaf(xt_, c, -st.x));
             });
-        if (lane == 0) {
-            a.out_tokens[long(r) * (a.k + 1) + j] = y;
-            __hip_atomic_store(&a.rctr[r], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        if (lane == 0) out[acc] = y;
     }
 }
 
@@ -745,9 +675,6 @@ static int launch_verify(int mode, VerifyArgs& a, hipStream_t s) {
     if (int e = persistent_grid(ks, 2L * a.Bmax * a.C, cus, G)) return e;
     SPECV_LAUNCH("verify_stream", ks, G, kThreads, 0, s, a);
     SPECV_LAUNCH("verify_decide", verify_decide<DT, SPECV_SAMPLE, VEC>, a.R, kDecideThreads, 0, s, a);
-    auto kr = verify_residual<DT, VEC>;
-    if (int e = persistent_grid(kr, long(a.R) * a.C, cus, G)) return e;
-    SPECV_LAUNCH("verify_residual", kr, G, kThreads, 0, s, a);
     return SPECV_OK;
 }
 
@@ -793,6 +720,9 @@ extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void*
 
     if (long(R) * (k + 1) * 2 * ((V + chunk_elems(4) - 1) / chunk_elems(4)) > INT_MAX)
         return fail(SPECV_EUNSUPPORTED, "spec_verify: R*(k+1)*V too large for one call");
+    if (mode == SPECV_SAMPLE && (V + chunk_len(dtype) - 1) / chunk_len(dtype) > kMaxChunks)
+        return fail(SPECV_EUNSUPPORTED, "spec_verify: sampling supports at most %d chunks of %d logits per row "
+                    "(V = %d)", kMaxChunks, chunk_len(dtype), V);
     const int esize = dtype == SPECV_BF16 ? 2 : 4;
     const int vecw = 16 / esize;
     const bool vec = (V % vecw) == 0 && aligned16(target_logits) &&
@@ -819,11 +749,6 @@ extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void*
     a.part_p = reinterpret_cast<float2*>(w + lay.part_p);
     a.part_q = reinterpret_cast<float2*>(w + lay.part_q);
     a.rec = reinterpret_cast<RowRec*>(w + lay.rec);
-    a.rs_stat = reinterpret_cast<float4*>(w + lay.rs_stat);
-    a.rs_row = reinterpret_cast<int4*>(w + lay.rs_row);
-    a.rs_list = reinterpret_cast<int*>(w + lay.rs_list);
-    a.mass = reinterpret_cast<float*>(w + lay.mass);
-    a.rctr = reinterpret_cast<int*>(w + lay.rctr);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == SPECV_BF16)
         return vec ? launch_verify<SPECV_BF16, true>(mode, a, s) : launch_verify<SPECV_BF16, false>(mode, a, s);

@@ -55,8 +55,7 @@ enum { SPECV_GREEDY = 0, SPECV_SAMPLE = 1 };  /* acceptance mode */
 /* status-word bits (specv_read_status) */
 enum {
     SPECV_STATUS_BAD_TOKEN = 1u, /* a draft token outside [0, V) */
-    SPECV_STATUS_BAD_TAG = 2u,   /* tags[] disagrees with cu_rows[] */
-    SPECV_STATUS_TIMEOUT = 4u    /* a bounded wait between workgroups expired */
+    SPECV_STATUS_BAD_TAG = 2u    /* tags[] disagrees with cu_rows[] */
 };
 
 /* Limits of the scheduler: all candidate keys of one call are held in the
@@ -179,16 +178,17 @@ int spec_flatten(int R, int k, const int32_t* len_in, int32_t* tags_out,
  *                    kept}. Bonus rows: sampling {0,0,0,-1}, greedy {argmax,
  *                    max logit, 0, -1}.
  *   ws, ws_bytes     workspace of at least spec_verify_workspace_bytes(mode,R,k,V)
- *                    bytes, 256-byte aligned, zero-filled before its first use;
- *                    every call leaves it ready for the next (its counters back
- *                    at zero), so it is filled once per allocation
- * Execution: one persistent kernel. In sampling mode the workgroups that share
- * a row wait for each other (bounded spin); the grid is sized to be resident at
- * once, so concurrent work on other streams can delay but not deadlock it. A
- * wait that exceeds its bound sets SPECV_STATUS_TIMEOUT instead of hanging.
+ *                    bytes, 256-byte aligned; its contents need no
+ *                    initialisation (chunk partials of the call in flight)
+ * Execution: two kernels on `stream`. A persistent grid streams every logit
+ * row of the batch once into per-chunk partials; then one workgroup per request
+ * decides its rows and, in sampling mode, re-reads the rejected row pair (or one
+ * chunk of the bonus row) to draw the extra token. No workgroup waits for
+ * another.
  * Errors: SPECV_EINVAL (NULL pointers, sizes, tau, small workspace),
- *         SPECV_EUNSUPPORTED (dtype; sampling with more than 1024 chunks of
- *         4096 logits per row, i.e. V > 4194304), SPECV_EDEVICE (launch failure).
+ *         SPECV_EUNSUPPORTED (dtype; R*(k+1)*V beyond 32-bit item counts;
+ *         sampling with more than 4096 chunks per row, i.e. V > 8388608 in
+ *         bf16 or V > 4194304 in f32), SPECV_EDEVICE (launch failure).
  */
 size_t spec_verify_workspace_bytes(int mode, int R, int k, int V);
 int spec_verify(int mode, int dtype, int R, int k, int V, const void* target_logits,

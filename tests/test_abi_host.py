@@ -55,7 +55,9 @@ def _verify(**kw):
     (dict(tau=-1.0), B.EINVAL, "temperature"),
     (dict(tau=float("nan")), B.EINVAL, "temperature"),
     (dict(ws=FAKE + 16), B.EINVAL, "aligned"),
-    (dict(wsb=1024), B.EINVAL, "workspace"),
+    (dict(wsb=512), B.EINVAL, "workspace"),
+    (dict(V=4096 * 2048 + 1), B.EUNSUPPORTED, "at most 4096 chunks"),
+    (dict(V=4096 * 1024 + 1, dtype=B.F32), B.EUNSUPPORTED, "at most 4096 chunks"),
 ])
 def test_verify_rejects(kw, code, msg):
     assert _verify(**kw) == code
