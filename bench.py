@@ -12,9 +12,11 @@ time) and the HBM bandwidth the verification kernel achieves against the
 8 TB/s peak of MI355X.
 
   python bench.py [--steps K] [--warmup W] [--config c2] [--mode sample]
-                  [--max-len k|-1] [--no-cpu] [--variants]
+                  [--max-len k|-1] [--no-cpu] [--variants] [--copies 3]
 
-Prints one JSON line. Inputs are resident in HBM before timing starts.
+Prints one JSON line. Inputs are resident in HBM before timing starts; the
+logits exist in `--copies` copies used in turn, so that no step is served from
+the Infinity Cache by the step before it.
 """
 from __future__ import annotations
 
@@ -45,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--variants", action="store_true",
                     help="also time greedy and verify-all variants of the workload")
+    ap.add_argument("--copies", type=int, default=3,
+                    help="input copies rotated over the steps (no step reads logits cached by the previous one)")
     ap.add_argument("--copy-probe", type=float, default=0.0,
                     help="only run a device copy of this many GiB (counter calibration) and exit")
     return ap.parse_args()
@@ -208,7 +212,7 @@ def main():
     B.lib()   # fail loudly if the HIP library is missing
     w = workloads.make(args.config)
     max_len = w.k if args.max_len == "k" else int(args.max_len)
-    d = DeviceStep(w)
+    d = DeviceStep(w, copies=args.copies)
     mode_c = B.SAMPLE if args.mode == "sample" else B.GREEDY
     main_res = run_variant(d, w, mode_c, args.mode, max_len, args.steps, args.warmup, B, torch)
 
@@ -256,6 +260,7 @@ def main():
             "R": w.R, "k": w.k, "V": w.V, "storage": w.dtype, "mode": args.mode,
             "tau": w.tau, "max_len": max_len, "verified_drafts_per_step": main_res["N"],
             "flattened_rows_per_step": main_res["rows"], "parallelism": "single GPU",
+            "input_copies": args.copies,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -15,9 +15,10 @@
 //   verify_stream    the HBM stream. Work item = one chunk of 64 * kNV 16-byte
 //                    vectors of one logit row. Items: the target chunks of all
 //                    rows, then (sampling) the draft chunks of the verified rows,
-//                    so every item costs the same; the item range is split into
-//                    one contiguous share per wavefront of a persistent grid.
-//                    Each wavefront loads item i+1 while it reduces item i to a
+//                    so every item costs the same. Wavefront w of the persistent
+//                    grid takes items w, w + nw, w + 2 nw, ... (at any moment the
+//                    grid reads one dense window of the item range). Each
+//                    wavefront loads item i+1 while it reduces item i to a
 //                    partial: (max, lowest index) in greedy mode, the base-2
 //                    softmax state (M, S) of the chunk in sampling mode (M = max
 //                    of logit * log2(e) / tau, S = sum of exp2(that - M)). No
@@ -202,14 +203,10 @@ __device__ __forceinline__ float2 chunk_argmax(const float (&x)[E], int beg, int
 // verify_stream
 // ---------------------------------------------------------------------------
 
-template <class T>
-struct RowMeta {
-    const T* row;
-    int t;                                  // flattened row
-    int x;                                  // draft token to capture, or -1
-    bool ok;                                // tag in range
-};
-
+// Grid-stride items: wave w processes items w, w + nw, w + 2 nw, ... Lane l of
+// the wave holds the description of the wave's item (batch + l): row pointer,
+// flattened row, chunk, captured token, tensor/ok flags; the loop reads them
+// back with readlane, so every address is wave-uniform.
 template <int DT, int MODE, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
     using RW = Raw<DT, VEC>;
@@ -219,91 +216,83 @@ __global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const long nw = long(gridDim.x) * kWaves;
     const long w = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr->status = 0u;   // verify_decide sets bits later
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr->status = 0u;
     const int nrows = min(max(*a.n_rows, 0), a.Bmax);
     const int nver = min(max(a.cu_rows[a.R], 0), nrows);
     const int C = a.C, CH = a.CH, V = a.V;
-    const long it_t = long(nrows) * C;                              // target items, then draft items
+    const long it_t = long(nrows) * C;
     const long items = it_t + (SAMPLE ? long(nver) * C : 0);
-    const long i0 = items * w / nw, i1 = items * (w + 1) / nw;
-    if (i0 >= i1) return;
-
-    // tensor 0 = target row t, 1 = draft row t (t < nver)
-    auto meta = [&](int t, int tensor) {
-        RowMeta<T> m;
-        const int r = a.tags[2 * t], j = a.tags[2 * t + 1];
-        m.t = t;
-        m.ok = r >= 0 && r < a.R && j >= 0 && j <= a.k && (tensor == 0 || j < a.k);
-        m.x = -1;
-        m.row = nullptr;
-        if (m.ok) {
-            m.row = tensor == 0 ? static_cast<const T*>(a.target) + (long(r) * (a.k + 1) + j) * long(V)
-                                : static_cast<const T*>(a.draft) + (long(r) * a.k + j) * long(V);
-            if (SAMPLE && t < nver && j < a.k) m.x = a.tokens[long(r) * a.k + j];
-        }
-        return m;
-    };
-
-    int tensor = i0 >= it_t ? 1 : 0;
-    const long rel = tensor ? i0 - it_t : i0;
-    int t = int(rel / C), ch = int(rel % C);
-    int left = int(i1 - i0);
-    // metadata of this row and of the row after it (loaded one run ahead)
-    auto next_row = [&](int& tt, int& tens) {
-        if (++tt == nrows && tens == 0) { tt = 0; tens = 1; }
-    };
-    RowMeta<T> cur = meta(t, tensor);
-    int tn = t, tensn = tensor;
-    next_row(tn, tensn);
-    RowMeta<T> nxt{};
-    if (left > C - ch) nxt = meta(tn, tensn);
-
+    if (w >= items) return;
+    const int mine = int((items - 1 - w) / nw) + 1;
     const float c = a.c;
-    auto issue = [&](RW& b, const RowMeta<T>& m, int chunk) {
-        if (!m.ok) return;
-        const int beg = chunk * CH;
-        b.load(m.row, beg, V, lane, beg + CH <= V);
-    };
-    auto process = [&](const RW& b) {
-        const int beg = ch * CH;
-        const bool full = beg + CH <= V;
-        float2 P = SAMPLE ? make_float2(-INFINITY, 0.f) : make_float2(-INFINITY, __int_as_float(INT_MAX));
-        if (cur.ok) {
-            float x[E];
-            b.widen(beg, V, lane, full, x);
-            P = SAMPLE ? chunk_softmax(x, c) : chunk_argmax<RW>(x, beg, lane);
-            if (SAMPLE && lane == 0 && cur.x >= beg && cur.x < beg + CH && cur.x < V) {
-                const float lx = Logit<DT>::load1(cur.row + cur.x);
-                if (tensor == 0) a.rec[cur.t].ax = lx; else a.rec[cur.t].bx = lx;
+
+    for (int b0 = 0; b0 < mine; b0 += kWave) {
+        const int nb = min(kWave, mine - b0);
+        // this lane's item
+        uint32_t plo = 0, phi = 0;
+        int t = 0, ch = 0, x = -1, fl = 0;                 // fl: bit 0 ok, bit 1 draft tensor
+        if (lane < nb) {
+            const long item = w + long(b0 + lane) * nw;
+            const int tensor = item >= it_t ? 1 : 0;
+            const long rel = tensor ? item - it_t : item;
+            t = int(rel / C);
+            ch = int(rel - long(t) * C);
+            const int r = a.tags[2 * t], j = a.tags[2 * t + 1];
+            const bool ok = r >= 0 && r < a.R && j >= 0 && j <= a.k && (tensor == 0 || j < a.k);
+            fl = (ok ? 1 : 0) | (tensor << 1);
+            if (ok) {
+                const T* row = tensor == 0 ? static_cast<const T*>(a.target) + (long(r) * (a.k + 1) + j) * long(V)
+                                           : static_cast<const T*>(a.draft) + (long(r) * a.k + j) * long(V);
+                const uint64_t pv = reinterpret_cast<uint64_t>(row);
+                plo = uint32_t(pv);
+                phi = uint32_t(pv >> 32);
+                if (SAMPLE && t < nver && j < a.k) {
+                    const int xx = a.tokens[long(r) * a.k + j];
+                    if (xx >= ch * CH && xx < ch * CH + CH && xx < V) x = xx;   // captured by this chunk
+                }
             }
         }
-        if (lane == 0) (tensor == 0 ? a.part_p : a.part_q)[long(cur.t) * C + ch] = P;
-    };
-    // item (cur, ch) from b while the next item is loaded into nb
-    auto step = [&](RW& b, RW& nb) {
-        const bool row_end = ch + 1 == C;
-        if (left > 1) issue(nb, row_end ? nxt : cur, row_end ? 0 : ch + 1);
-        process(b);
-        --left;
-        if (row_end) {
-            ch = 0;
-            t = tn;
-            tensor = tensn;
-            cur = nxt;
-            next_row(tn, tensn);
-            if (left > C) nxt = meta(tn, tensn);
-        } else {
-            ++ch;
+        auto row_of = [&](int i) {
+            const uint64_t pv = (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(phi), i))) << 32) |
+                                uint32_t(__builtin_amdgcn_readlane(int(plo), i));
+            return reinterpret_cast<const T*>(pv);
+        };
+        auto issue = [&](RW& buf, int i) {
+            if (__builtin_amdgcn_readlane(fl, i) & 1) {
+                const int beg = __builtin_amdgcn_readlane(ch, i) * CH;
+                buf.load(row_of(i), beg, V, lane, beg + CH <= V);
+            }
+        };
+        auto process = [&](const RW& buf, int i) {
+            const int f = __builtin_amdgcn_readlane(fl, i);
+            const int cc = __builtin_amdgcn_readlane(ch, i);
+            const int tt = __builtin_amdgcn_readlane(t, i);
+            const int beg = cc * CH;
+            const bool full = beg + CH <= V;
+            float2 P = SAMPLE ? make_float2(-INFINITY, 0.f) : make_float2(-INFINITY, __int_as_float(INT_MAX));
+            if (f & 1) {
+                float xv[E];
+                buf.widen(beg, V, lane, full, xv);
+                P = SAMPLE ? chunk_softmax(xv, c) : chunk_argmax<RW>(xv, beg, lane);
+                if (SAMPLE) {
+                    const int xx = __builtin_amdgcn_readlane(x, i);
+                    if (xx >= 0 && lane == 0) {
+                        const float lx = Logit<DT>::load1(row_of(i) + xx);
+                        if (f & 2) a.rec[tt].bx = lx; else a.rec[tt].ax = lx;
+                    }
+                }
+            }
+            if (lane == 0) ((f & 2) ? a.part_q : a.part_p)[long(tt) * C + cc] = P;
+        };
+        RW q0, q1;
+        issue(q0, 0);
+        for (int i = 0; i < nb; i += 2) {
+            if (i + 1 < nb) issue(q1, i + 1);
+            process(q0, i);
+            if (i + 1 >= nb) break;
+            if (i + 2 < nb) issue(q0, i + 2);
+            process(q1, i + 1);
         }
-    };
-
-    RW b0, b1;                                    // two named buffers: no dynamic indexing
-    issue(b0, cur, ch);
-    for (;;) {
-        step(b0, b1);
-        if (left == 0) break;
-        step(b1, b0);
-        if (left == 0) break;
     }
 }
 

@@ -20,7 +20,12 @@ def to_device(a: np.ndarray, device) -> torch.Tensor:
 
 
 class DeviceStep:
-    def __init__(self, w: Workload, device="cuda"):
+    """`copies` > 1 keeps that many copies of the large read-only inputs (target
+    logits, draft logits, Markov backbone logits) and moves to the next copy at
+    every step, so that no step finds the previous step's logits in the 256 MB
+    Infinity Cache."""
+
+    def __init__(self, w: Workload, device="cuda", copies: int = 1):
         self.w = w
         self.device = device
         R, k, V = w.R, w.k, w.V
@@ -39,6 +44,11 @@ class DeviceStep:
         self.emb = dev(w.emb)
         self.proj = dev(w.proj)
         self.prev = dev(w.prev_token)
+        big = ("target", "draft_in", "backbone")
+        self._copies = [{n: getattr(self, n) for n in big}]
+        for _ in range(max(1, int(copies)) - 1):
+            self._copies.append({n: None if getattr(self, n) is None else getattr(self, n).clone() for n in big})
+        self._turn = 0
         i32 = dict(dtype=torch.int32, device=device)
         self.lengths = torch.zeros(R, **i32)
         self.tags = torch.zeros(R * (k + 1), 2, **i32)
@@ -82,8 +92,15 @@ class DeviceStep:
                       self.acc_len, self.out_tokens, self.ws_verify, row_diag=self.diag if diag else None,
                       stream=stream)
 
+    def use_copy(self, i: int):
+        for n, t in self._copies[i % len(self._copies)].items():
+            setattr(self, n, t)
+
     def step(self, mode, max_len=None, diag=False, stream=None):
         """One pass of the hot path: (Markov draft,) schedule + flatten, verify."""
+        if len(self._copies) > 1:
+            self._turn += 1
+            self.use_copy(self._turn)
         if self.w.backbone is not None:
             self.markov(mode, stream=stream)
         self.schedule(max_len, stream=stream)
