@@ -167,6 +167,21 @@ __device__ __forceinline__ void wave_argmax_dpp(float& v, int& i) {
     i = __builtin_amdgcn_readlane(i, 63);
 }
 
+// Inclusive prefix sum of an int across the wave in lane order (all lanes
+// active): sums of 4 within each row of 16 lanes, then of 8 and 16 under bank
+// masks, then the two row broadcasts carry row totals forward.
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+    const int v0 = v;
+    v += __builtin_amdgcn_update_dpp(0, v0, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v0, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v0, 0x113, 0xf, 0xf, false);   // row_shr:3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xe, false);    // row_shr:4, lanes 4-15 of a row
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xc, false);    // row_shr:8, lanes 8-15 of a row
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);    // row_bcast:15 into rows 1 and 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);    // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 // Inclusive prefix sum across the wave in lane order.
 __device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
 #pragma unroll

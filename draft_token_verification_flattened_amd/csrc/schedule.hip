@@ -99,6 +99,51 @@ __device__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* sh, uint64_t&
     return res;
 }
 
+// Block-wide exclusive scan of one int per thread (DPP within each wave, wave
+// totals through LDS); returns the block total too. Totals stay below 2^31.
+__device__ int block_exclusive_scan_i32(int v, int* sh, int& total) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+    const int incl = wave_incl_scan_i32(v);
+    if (lane == 63) sh[w] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int q = 0; q < nw; ++q) {
+        const int t = sh[q];
+        tot += t;
+        if (q < w) before += t;
+    }
+    total = tot;
+    __syncthreads();
+    return before + incl - v;
+}
+
+// Wave maximum of a double (DPP on both halves), as a scalar.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_d(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(int(b), int(b), CTRL, ROW_MASK, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(int(b >> 32), int(b >> 32), CTRL, ROW_MASK, 0xf, false);
+    return __longlong_as_double((long long)(unsigned)lo | ((long long)hi << 32));
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+    v = fmax(v, dpp_d<0xb1>(v));
+    v = fmax(v, dpp_d<0x4e>(v));
+    v = fmax(v, dpp_d<0x141>(v));
+    v = fmax(v, dpp_d<0x140>(v));
+    v = fmax(v, dpp_d<0x142, 0xa>(v));
+    v = fmax(v, dpp_d<0x143, 0xc>(v));
+    const long long b = __double_as_longlong(v);
+    return __longlong_as_double(((long long)__builtin_amdgcn_readlane(int(b >> 32), 63) << 32) |
+                                (long long)(unsigned)__builtin_amdgcn_readlane(int(b), 63));
+}
+
+// Best prefix over the wave: the largest G, then the smallest M with it.
+__device__ __forceinline__ void wave_best_gm(double& g, int& m) {
+    const double gm = wave_max_f64(g);
+    m = wave_min_int_dpp(g == gm ? m : INT_MAX);
+    g = gm;
+}
+
 struct SchedArgs {
     int R, k, kk, max_len, n_tbl;
     const float* z;
@@ -135,15 +180,25 @@ struct SchedWs {
 // cu_rows[r] .. cu_rows[r+1]-1, tags (r, 0) .. (r, L_r - 1)), then one bonus row
 // per request at N + r with tag (r, L_r); N = cu_rows[R], n_rows = N + R.
 template <typename F>
-__device__ void flatten_block(const SchedArgs& a, int r0, int r1, F len_of, uint64_t* sh) {
-    uint64_t local = 0;
-    for (int r = r0; r < r1; ++r) local += uint64_t(len_of(r));
-    uint64_t total;
-    uint64_t off = block_exclusive_scan_u64(local, sh, total);
-    const int N = int(total);
+__device__ void flatten_block(const SchedArgs& a, int r0, int r1, F len_of, int* sh) {
+    constexpr int kKeep = 4;                    // lengths kept in registers; more are recomputed
+    int Lk[kKeep];
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < kKeep; ++q) {
+        Lk[q] = r0 + q < r1 ? len_of(r0 + q) : 0;
+        local += Lk[q];
+    }
+    for (int r = r0 + kKeep; r < r1; ++r) local += len_of(r);
+    int N;
+    int off = block_exclusive_scan_i32(local, sh, N);
     for (int r = r0; r < r1; ++r) {
-        const int L = len_of(r);
-        a.cu_rows[r] = int32_t(off);
+        int L = 0;
+#pragma unroll
+        for (int q = 0; q < kKeep; ++q)
+            if (r == r0 + q) L = Lk[q];
+        if (r >= r0 + kKeep) L = len_of(r);
+        a.cu_rows[r] = off;
         if (a.len_out) a.len_out[r] = L;
         for (int j = 0; j < L; ++j) {
             a.tags[2 * (off + j)] = r;
@@ -151,7 +206,7 @@ __device__ void flatten_block(const SchedArgs& a, int r0, int r1, F len_of, uint
         }
         a.tags[2 * (N + r)] = r;
         a.tags[2 * (N + r) + 1] = L;
-        off += uint64_t(L);
+        off += L;
     }
     if (threadIdx.x == 0) {
         a.cu_rows[a.R] = N;
@@ -175,7 +230,7 @@ __device__ void compute_keys(const SchedArgs& a, uint64_t* keys, bool write_surv
 
 // All lengths fixed (max_len < 0: all k; max_len == 0: none): survival and flatten.
 __global__ __launch_bounds__(kSchedThreads) void schedule_fixed(SchedArgs a) {
-    __shared__ uint64_t sh[64];
+    __shared__ int sh[64];
     const int tid = threadIdx.x, nt = blockDim.x;
     if (a.survival) {
         for (int r = tid; r < a.R; r += nt) {
@@ -229,8 +284,9 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_rank(SchedArgs a, int 
     __shared__ unsigned long long cnt_sh[64];                  // per local key (kw <= 64)
     __shared__ unsigned long long sum_sh[64];
     __shared__ uint64_t sh[64];
+    __shared__ int ish[64];
     __shared__ int last_sh;
-    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
+    const int tid = threadIdx.x, nt = blockDim.x;
     const int n = a.R * a.kk;
 
     // 1. table and all keys
@@ -309,15 +365,181 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_rank(SchedArgs a, int 
     const uint64_t kt = sh[62];
     const bool any = sh[63] > 0;
     __syncthreads();
-    // a request's keys increase with the position, so its selection is a prefix
+    // a request's keys increase with the position, so its selection is a prefix:
+    // its length is the number of its keys <= kt
     auto len_of = [&](int r) {
         int L = 0;
         if (any)
-            while (L < a.kk && keys[r * a.kk + L] <= kt) ++L;
+            for (int i = 0; i < a.kk; ++i) L += keys[r * a.kk + i] <= kt ? 1 : 0;
         return L;
     };
     const int per = (a.R + nt - 1) / nt;
     const int r0 = min(a.R, tid * per), r1 = min(a.R, r0 + per);
+    flatten_block(a, r0, r1, len_of, ish);
+}
+
+// ---------------------------------------------------------------------------
+// schedule_bucket: the same schedule from one workgroup, for R * k <= 4096.
+// The keys are sorted by a bucket pass on their leading bits (bucket order is
+// key order) followed by an exact rank inside each bucket; then the prefix
+// sums of Q in sorted order give P(M) for every M, and G(M) follows. No
+// workgroup waits for another. Inside a bucket every key compares itself with
+// every member, so a bucket of s keys costs s steps: many near-equal
+// survivals make it slower, never wrong.
+// ---------------------------------------------------------------------------
+
+constexpr int kBuckets = 4096;
+constexpr int kBucketItems = 4096;          // largest R * k for schedule_bucket
+
+// Bucket of a key: 2^32 - Q in steps of 2^20 (ascending bucket = descending Q).
+__device__ __forceinline__ int bucket_of(uint64_t key) {
+    const uint64_t d = (1ull << 32) - key_q(key);
+    return int(min(d >> 20, uint64_t(kBuckets - 1)));
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_bucket(SchedArgs a) {
+    extern __shared__ __align__(16) uint64_t lds[];   // keys [R*k] | grouped [n] | sorted [n] | cnt, off [kBuckets]
+    __shared__ int tb[kMaxTbl];
+    __shared__ double tt[kMaxTbl];
+    __shared__ double wg_sh[kSchedThreads / 64];
+    __shared__ int wm_sh[kSchedThreads / 64];
+    __shared__ int sh[64], sh2[64];
+    __shared__ uint64_t kt_sh;
+    __shared__ int any_sh;
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nwav = nt >> 6;
+    const int R = a.R, k = a.k, kk = a.kk, n = R * kk, Rk = R * k;
+    const bool surv = a.survival != nullptr;
+    const int kc = surv ? k : kk;
+    uint64_t* keys = lds;
+    uint64_t* grp = keys + Rk;
+    uint64_t* srt = grp + n;
+    int* cnt = reinterpret_cast<int*>(srt + n);
+    int* off = cnt + kBuckets;
+    double* sg = reinterpret_cast<double*>(keys);
+
+    // 1. table, empty histogram, one calibrated sigmoid per (request, position)
+    for (int i = tid; i < a.n_tbl; i += nt) { tb[i] = a.tbl_b[i]; tt[i] = a.tbl_t[i]; }
+    for (int b = tid; b < kBuckets; b += nt) cnt[b] = 0;
+    for (int e = tid; e < Rk; e += nt) {
+        const int i = e % k;
+        if (i < kc) sg[e] = survival_step(a.z[e], a.T[i]);
+    }
+    __syncthreads();
+
+    // this thread's prefix lengths M = p + 1, p in [p0, p1): their throughput
+    // does not depend on the keys
+    constexpr int kPosPer = kBucketItems / kSchedThreads;
+    const int per = (n + nt - 1) / nt;
+    const int p0 = min(n, tid * per), p1 = min(n, p0 + per);
+    double thr[kPosPer];
+#pragma unroll
+    for (int q = 0; q < kPosPer; ++q) thr[q] = p0 + q < p1 ? throughput(R + p0 + q + 1, tb, tt, a.n_tbl) : 0.0;
+
+    // 2. survival (running products in position order) and keys, in place;
+    //    positions >= kk get a key above every real one
+    for (int r = tid; r < R; r += nt) {
+        double S = 1.0;
+        for (int i = 0; i < k; ++i) {
+            const int e = r * k + i;
+            if (i < kc) {
+                S = S * sg[e];
+                if (surv) a.survival[long(r) * k + i] = S;
+            }
+            uint64_t key = ~0ull;
+            if (i < kk) {
+                key = make_key(quantise(S), i, r);
+                atomicAdd(&cnt[bucket_of(key)], 1);
+            }
+            keys[e] = key;
+        }
+    }
+    __syncthreads();
+
+    // 3. bucket offsets (exclusive scan), then every key into its bucket
+    {
+        constexpr int kPer = kBuckets / kSchedThreads;
+        int loc[kPer];
+        int sum = 0;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) { loc[q] = cnt[tid * kPer + q]; sum += loc[q]; }
+        int total;
+        int base = block_exclusive_scan_i32(sum, sh, total);
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) { off[tid * kPer + q] = base; base += loc[q]; }
+    }
+    __syncthreads();
+    for (int e = tid; e < Rk; e += nt) {
+        const uint64_t x = keys[e];
+        if (x != ~0ull) grp[atomicAdd(&off[bucket_of(x)], 1)] = x;
+    }
+    __syncthreads();
+
+    // 4. exact sorted position: bucket start + smaller keys of the same bucket
+    for (int e = tid; e < Rk; e += nt) {
+        const uint64_t x = keys[e];
+        if (x == ~0ull) continue;
+        const int b = bucket_of(x);
+        const int end = off[b], beg = end - cnt[b];
+        int rank = beg;
+        for (int m = beg; m < end; ++m) rank += grp[m] < x ? 1 : 0;
+        srt[rank] = x;
+    }
+    __syncthreads();
+
+    // 5. P(M) for every prefix length (contiguous positions per thread), G(M),
+    //    and the best prefix: largest G, then smallest M
+    //    Q <= 2^32 is scanned as two exact 32-bit sums of its 16-bit halves.
+    const uint64_t R32 = uint64_t(R) << 32;
+    int lo = 0, hi = 0;
+    for (int p = p0; p < p1; ++p) {
+        const uint64_t q = key_q(srt[p]);
+        lo += int(q & 0xffffu);
+        hi += int(q >> 16);
+    }
+    int tlo, thi;
+    const int elo = block_exclusive_scan_i32(lo, sh, tlo);
+    const int ehi = block_exclusive_scan_i32(hi, sh2, thi);
+    uint64_t P = (uint64_t(uint32_t(ehi)) << 16) + uint64_t(uint32_t(elo));
+    double g = -1.0;                                          // below every gain
+    int m = INT_MAX;
+#pragma unroll
+    for (int q = 0; q < kPosPer; ++q) {
+        if (p0 + q < p1) {
+            P += key_q(srt[p0 + q]);
+            const int M = p0 + q + 1, bt = R + M;
+            const double G = (double(R32 + P) * thr[q]) / double(bt);
+            if (G > g) { g = G; m = M; }                      // positions ascend: first M wins ties
+        }
+    }
+    if (tid == 0) {                                           // the empty prefix, M = 0
+        const double G0 = (double(R32) * throughput(R, tb, tt, a.n_tbl)) / double(R);
+        if (G0 >= g) { g = G0; m = 0; }
+    }
+    wave_best_gm(g, m);
+    if (lane == 0) { wg_sh[wave] = g; wm_sh[wave] = m; }
+    __syncthreads();
+    if (wave == 0) {
+        double gw = lane < nwav ? wg_sh[lane] : -1.0;
+        int mw = lane < nwav ? wm_sh[lane] : INT_MAX;
+        wave_best_gm(gw, mw);
+        if (lane == 0) {
+            any_sh = mw > 0;
+            kt_sh = mw > 0 ? srt[mw - 1] : 0ull;
+        }
+    }
+    __syncthreads();
+
+    // 6. lengths (a request's keys increase with the position) and the batch
+    const uint64_t kt = kt_sh;
+    const bool any = any_sh != 0;
+    auto len_of = [&](int r) {
+        int L = 0;
+        if (any)
+            for (int i = 0; i < kk; ++i) L += keys[r * k + i] <= kt ? 1 : 0;
+        return L;
+    };
+    const int rper = (R + nt - 1) / nt;
+    const int r0 = min(R, tid * rper), r1 = min(R, r0 + rper);
     flatten_block(a, r0, r1, len_of, sh);
 }
 
@@ -399,6 +621,16 @@ extern "C" int spec_schedule(int R, int k, const float* conf_logit, const float*
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (max_len < 0 || max_len == 0) {
         SPECV_LAUNCH("schedule", schedule_fixed, 1, kSchedThreads, 0, s, a);
+        return SPECV_OK;
+    }
+    if (long(R) * k <= kBucketItems) {
+        const size_t lds = size_t(R) * k * sizeof(uint64_t) + 2 * size_t(R) * a.kk * sizeof(uint64_t) +
+                           2 * size_t(kBuckets) * sizeof(int);
+        if (lds > 65536 &&
+            hipFuncSetAttribute(reinterpret_cast<const void*>(schedule_bucket),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
+            return fail(SPECV_EDEVICE, "spec_schedule: cannot reserve %zu bytes of LDS", lds);
+        SPECV_LAUNCH("schedule", schedule_bucket, 1, kSchedThreads, lds, s, a);
         return SPECV_OK;
     }
     // keys per workgroup: a power of two >= 16, enough for at most 256 workgroups

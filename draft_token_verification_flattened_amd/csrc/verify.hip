@@ -203,10 +203,16 @@ __device__ __forceinline__ float2 chunk_argmax(const float (&x)[E], int beg, int
 // verify_stream
 // ---------------------------------------------------------------------------
 
-// Grid-stride items: wave w processes items w, w + nw, w + 2 nw, ... Lane l of
-// the wave holds the description of the wave's item (batch + l): row pointer,
-// flattened row, chunk, captured token, tensor/ok flags; the loop reads them
-// back with readlane, so every address is wave-uniform.
+// Grid-stride item slots. The slot space is static: the target chunks of all
+// Bmax = R (k+1) possible rows, then (sampling) the draft chunks of all of
+// them; a slot is live when its row exists in this call's batch (target: row
+// < n_rows; draft: row < N, the verified rows). Wave w visits slots w, w + nw,
+// w + 2 nw, ... in batches of 64: lane l loads the tag of the batch's l-th
+// slot at once (no wait for n_rows first, and the next batch's tags are
+// fetched while this one streams), and the wave walks the live lanes of the
+// batch in order, reading each item's description back with readlane, so
+// every address is wave-uniform. Live slots are a prefix of each half of the
+// slot space, so every wave gets the same number of them, within one.
 template <int DT, int MODE, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
     using RW = Raw<DT, VEC>;
@@ -214,43 +220,60 @@ __global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
     constexpr int E = RW::kE;
     constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
     const int lane = threadIdx.x & (kWave - 1);
-    const long nw = long(gridDim.x) * kWaves;
-    const long w = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+    const uint32_t nw = gridDim.x * kWaves;
+    const uint32_t w = blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr->status = 0u;
-    const int nrows = min(max(*a.n_rows, 0), a.Bmax);
-    const int nver = min(max(a.cu_rows[a.R], 0), nrows);
-    const int C = a.C, CH = a.CH, V = a.V;
-    const long it_t = long(nrows) * C;
-    const long items = it_t + (SAMPLE ? long(nver) * C : 0);
-    if (w >= items) return;
-    const int mine = int((items - 1 - w) / nw) + 1;
+    const int C = a.C, CH = a.CH, V = a.V, K = a.k;
+    const uint32_t region = uint32_t(a.Bmax) * uint32_t(C);          // slots per tensor
+    const uint32_t slots = SAMPLE ? 2 * region : region;
+    if (w >= slots) return;
+    const uint32_t mine = (slots - 1 - w) / nw + 1;
+    const int nrows_in = *a.n_rows, nver_in = a.cu_rows[a.R];       // in flight with the first tags
     const float c = a.c;
 
-    for (int b0 = 0; b0 < mine; b0 += kWave) {
-        const int nb = min(kWave, mine - b0);
-        // this lane's item
+    // slot -> (tensor, row, chunk) and the row's tag, for batch b0 (lane < nb)
+    auto slot_of = [&](uint32_t b0, int& tensor, int& t, int& ch) {
+        const uint32_t slot = w + (b0 + uint32_t(lane)) * nw;
+        tensor = slot >= region ? 1 : 0;
+        const uint32_t rel = tensor ? slot - region : slot;
+        t = int(rel / uint32_t(C));
+        ch = int(rel - uint32_t(t) * uint32_t(C));
+    };
+    int tg_r = -1, tg_j = -1;                                        // tag of this lane's slot
+    {
+        int tensor, t, ch;
+        if (uint32_t(lane) < min(uint32_t(kWave), mine)) {
+            slot_of(0, tensor, t, ch);
+            tg_r = a.tags[2 * t];
+            tg_j = a.tags[2 * t + 1];
+        }
+    }
+    const int nrows = min(max(nrows_in, 0), a.Bmax);
+    const int nver = min(max(nver_in, 0), nrows);
+
+    for (uint32_t b0 = 0; b0 < mine; b0 += kWave) {
+        const uint32_t nb = min(uint32_t(kWave), mine - b0);
+        int tensor = 0, t = 0, ch = 0;
+        const bool in = uint32_t(lane) < nb;
+        if (in) slot_of(b0, tensor, t, ch);
+        const int r = tg_r, j = tg_j;
+        // the next batch's tags, fetched behind this batch's chunks
+        if (b0 + kWave < mine && uint32_t(lane) < min(uint32_t(kWave), mine - b0 - kWave)) {
+            int tn, ttn, chn;
+            slot_of(b0 + kWave, tn, ttn, chn);
+            tg_r = a.tags[2 * ttn];
+            tg_j = a.tags[2 * ttn + 1];
+        }
+        const bool live = in && t < (tensor ? nver : nrows);
+        const bool ok = live && r >= 0 && r < a.R && j >= 0 && j <= K && (tensor == 0 || j < K);
+        const int fl = (ok ? 1 : 0) | (tensor << 1);                  // bit 0 ok, bit 1 draft tensor
         uint32_t plo = 0, phi = 0;
-        int t = 0, ch = 0, x = -1, fl = 0;                 // fl: bit 0 ok, bit 1 draft tensor
-        if (lane < nb) {
-            const long item = w + long(b0 + lane) * nw;
-            const int tensor = item >= it_t ? 1 : 0;
-            const long rel = tensor ? item - it_t : item;
-            t = int(rel / C);
-            ch = int(rel - long(t) * C);
-            const int r = a.tags[2 * t], j = a.tags[2 * t + 1];
-            const bool ok = r >= 0 && r < a.R && j >= 0 && j <= a.k && (tensor == 0 || j < a.k);
-            fl = (ok ? 1 : 0) | (tensor << 1);
-            if (ok) {
-                const T* row = tensor == 0 ? static_cast<const T*>(a.target) + (long(r) * (a.k + 1) + j) * long(V)
-                                           : static_cast<const T*>(a.draft) + (long(r) * a.k + j) * long(V);
-                const uint64_t pv = reinterpret_cast<uint64_t>(row);
-                plo = uint32_t(pv);
-                phi = uint32_t(pv >> 32);
-                if (SAMPLE && t < nver && j < a.k) {
-                    const int xx = a.tokens[long(r) * a.k + j];
-                    if (xx >= ch * CH && xx < ch * CH + CH && xx < V) x = xx;   // captured by this chunk
-                }
-            }
+        if (ok) {
+            const T* row = tensor == 0 ? static_cast<const T*>(a.target) + (long(r) * (K + 1) + j) * long(V)
+                                       : static_cast<const T*>(a.draft) + (long(r) * K + j) * long(V);
+            const uint64_t pv = reinterpret_cast<uint64_t>(row);
+            plo = uint32_t(pv);
+            phi = uint32_t(pv >> 32);
         }
         auto row_of = [&](int i) {
             const uint64_t pv = (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(phi), i))) << 32) |
@@ -263,6 +286,23 @@ __global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
                 buf.load(row_of(i), beg, V, lane, beg + CH <= V);
             }
         };
+        uint64_t todo = __ballot(live);
+        auto next = [&]() {
+            if (!todo) return -1;
+            const int i = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            return i;
+        };
+        RW q0, q1;
+        int i0 = next();
+        if (i0 >= 0) issue(q0, i0);
+        // draft token of the row, if this item's chunk holds it (loaded after
+        // the first chunk is in flight)
+        int x = -1;
+        if (SAMPLE && ok && t < nver && j < K) {
+            const int xx = a.tokens[long(r) * K + j];
+            if (xx >= ch * CH && xx < ch * CH + CH && xx < V) x = xx;
+        }
         auto process = [&](const RW& buf, int i) {
             const int f = __builtin_amdgcn_readlane(fl, i);
             const int cc = __builtin_amdgcn_readlane(ch, i);
@@ -284,14 +324,14 @@ __global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
             }
             if (lane == 0) ((f & 2) ? a.part_q : a.part_p)[long(tt) * C + cc] = P;
         };
-        RW q0, q1;
-        issue(q0, 0);
-        for (int i = 0; i < nb; i += 2) {
-            if (i + 1 < nb) issue(q1, i + 1);
-            process(q0, i);
-            if (i + 1 >= nb) break;
-            if (i + 2 < nb) issue(q0, i + 2);
-            process(q1, i + 1);
+        while (i0 >= 0) {
+            const int i1 = next();
+            if (i1 >= 0) issue(q1, i1);
+            process(q0, i0);
+            if (i1 < 0) break;
+            i0 = next();
+            if (i0 >= 0) issue(q0, i0);
+            process(q1, i1);
         }
     }
 }

@@ -120,6 +120,41 @@ def test_schedule_limits(R, k):
     assert np.array_equal(tags.cpu().numpy()[:osched.n_rows(rc)], rt)
 
 
+@pytest.mark.parametrize("R,k", [(512, 8), (683, 6), (3, 5)])
+@pytest.mark.parametrize("pattern", ["equal", "saturated", "few"])
+def test_schedule_ties(R, k, pattern):
+    """Heavy ties in Q: identical confidences in every request ("equal"), all
+    survivals 1.0 ("saturated"), or confidences from four values ("few"). R*k =
+    4096 and 4098 sit on both sides of the single-workgroup size limit."""
+    g = np.random.Generator(np.random.Philox(R * 7 + k))
+    if pattern == "equal":
+        z = np.tile((g.standard_normal(k) + 1.5).astype(np.float32), (R, 1))
+    elif pattern == "saturated":
+        z = np.full((R, k), 60.0, np.float32)
+    else:
+        z = g.choice(np.array([-1.0, 0.5, 1.0, 2.0], np.float32), size=(R, k))
+    T = np.linspace(1, 2, k).astype(np.float32)
+    pts = np.array([max(1, R // 2), R, 2 * R, 4 * R, 8 * R, 33 * R], np.int32)
+    thr = np.array([p / (1.0 + 0.6 * max(0, p - R) / R) for p in pts])
+    say("schedule ties R", R, "k", k, pattern)
+    dev = lambda a: to_device(a, "cuda")   # noqa: E731
+    L = torch.zeros(R, dtype=torch.int32, device="cuda")
+    tags = torch.zeros(R * (k + 1), 2, dtype=torch.int32, device="cuda")
+    cu = torch.zeros(R + 1, dtype=torch.int32, device="cuda")
+    nr = torch.zeros(1, dtype=torch.int32, device="cuda")
+    surv = torch.zeros(R, k, dtype=torch.float64, device="cuda")
+    ws = B.workspace(B.schedule_workspace_bytes(R, k), "cuda")
+    for ml in (k, max(1, k // 2)):
+        B.spec_schedule(dev(z), dev(T), dev(pts), dev(thr), ml, L, tags, cu, nr, ws, survival_out=surv)
+        torch.cuda.synchronize()
+        ref = osched.schedule(z, T, pts, thr, ml)
+        assert np.array_equal(L.cpu().numpy(), ref["L"]), (pattern, ml)
+        rt, rc = osched.flatten(ref["L"])
+        assert np.array_equal(cu.cpu().numpy(), rc)
+        assert np.array_equal(tags.cpu().numpy()[:osched.n_rows(rc)], rt)
+        assert np.max(np.abs(surv.cpu().numpy() - ref["S"]) / ref["S"]) < 1e-14
+
+
 def test_flatten_matches_oracle():
     g = np.random.Generator(np.random.Philox(5))
     for R, k in [(1, 1), (7, 5), (100000, 4)]:
