@@ -182,6 +182,24 @@ __device__ __forceinline__ int wave_incl_scan_i32(int v) {
     return v;
 }
 
+// Block-wide exclusive scan of one int per thread (DPP within each wave, wave
+// totals through LDS); returns the block total too. Totals stay below 2^31.
+__device__ __forceinline__ int block_exclusive_scan_i32(int v, int* sh, int& total) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+    const int incl = wave_incl_scan_i32(v);
+    if (lane == 63) sh[w] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int q = 0; q < nw; ++q) {
+        const int t = sh[q];
+        tot += t;
+        if (q < w) before += t;
+    }
+    total = tot;
+    __syncthreads();
+    return before + incl - v;
+}
+
 // Inclusive prefix sum across the wave in lane order.
 __device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
 #pragma unroll

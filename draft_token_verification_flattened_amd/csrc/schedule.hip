@@ -99,24 +99,6 @@ __device__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* sh, uint64_t&
     return res;
 }
 
-// Block-wide exclusive scan of one int per thread (DPP within each wave, wave
-// totals through LDS); returns the block total too. Totals stay below 2^31.
-__device__ int block_exclusive_scan_i32(int v, int* sh, int& total) {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
-    const int incl = wave_incl_scan_i32(v);
-    if (lane == 63) sh[w] = incl;
-    __syncthreads();
-    int before = 0, tot = 0;
-    for (int q = 0; q < nw; ++q) {
-        const int t = sh[q];
-        tot += t;
-        if (q < w) before += t;
-    }
-    total = tot;
-    __syncthreads();
-    return before + incl - v;
-}
-
 // Wave maximum of a double (DPP on both halves), as a scalar.
 template <int CTRL, int ROW_MASK = 0xf>
 __device__ __forceinline__ double dpp_d(double v) {

@@ -40,8 +40,8 @@
 
 namespace specv {
 
-constexpr int kThreads = 256;               // 4 wavefronts per workgroup
-constexpr int kWaves = kThreads / kWave;
+constexpr int kStreamThreads = 1024;        // verify_stream: one workgroup per compute unit
+constexpr int kPhaseSlots = 2 * kStreamThreads;   // slots described in LDS at a time
 constexpr int kDecideThreads = 1024;        // verify_decide: 16 wavefronts per request
 constexpr int kMaxChunks = 4096;            // sampling: chunks per row (residual masses live in LDS)
 constexpr int kNV = 4;                      // 16-byte vectors per lane per item
@@ -203,136 +203,161 @@ __device__ __forceinline__ float2 chunk_argmax(const float (&x)[E], int beg, int
 // verify_stream
 // ---------------------------------------------------------------------------
 
-// Grid-stride item slots. The slot space is static: the target chunks of all
-// Bmax = R (k+1) possible rows, then (sampling) the draft chunks of all of
-// them; a slot is live when its row exists in this call's batch (target: row
-// < n_rows; draft: row < N, the verified rows). Wave w visits slots w, w + nw,
-// w + 2 nw, ... in batches of 64: lane l loads the tag of the batch's l-th
-// slot at once (no wait for n_rows first, and the next batch's tags are
-// fetched while this one streams), and the wave walks the live lanes of the
-// batch in order, reading each item's description back with readlane, so
-// every address is wave-uniform. Live slots are a prefix of each half of the
-// slot space, so every wave gets the same number of them, within one.
+// One workgroup of kStreamThreads per compute unit. The slot space is static:
+// the target chunks of all Bmax = R (k+1) possible rows, then (sampling) the
+// draft chunks of all of them; a slot is live when its row exists in this
+// call's batch (target: row < n_rows; draft: row < N, the verified rows).
+// Workgroup b owns slots b, b + G, b + 2G, ... (so the grid sweeps one dense
+// window of the slot space). It describes up to kPhaseSlots of them at a time
+// in LDS (tag -> row pointer, row, chunk, token index), live ones only, in slot
+// order; its wavefronts then take the items one at a time from an LDS counter,
+// so a wavefront that the compute unit serves faster simply takes more items
+// and all of them finish together. Each wavefront loads its next item while it
+// reduces the current one.
 template <int DT, int MODE, bool VEC>
-__global__ __launch_bounds__(kThreads) void verify_stream(VerifyArgs a) {
+__global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
     using RW = Raw<DT, VEC>;
     using T = typename RW::T;
     constexpr int E = RW::kE;
+    constexpr int GW = RW::kVec;
     constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t nw = gridDim.x * kWaves;
-    const uint32_t w = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr->status = 0u;
+    __shared__ uint64_t d_row[kPhaseSlots];
+    __shared__ int d_t[kPhaseSlots];                 // flattened row
+    __shared__ int d_cf[kPhaseSlots];                // chunk << 2 | draft << 1 | ok
+    __shared__ int d_tok[kPhaseSlots];               // index of the row's draft token, or -1
+    __shared__ float2 st_p[kPhaseSlots];             // the items' partials, written out after the phase
+    __shared__ float st_x[kPhaseSlots];              // logit at the draft token, if the item holds it
+    __shared__ unsigned char st_f[kPhaseSlots];
+    __shared__ int sh[64];
+    __shared__ int n_live, next_item;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const uint32_t G = gridDim.x, b = blockIdx.x;
+    if (b == 0 && tid == 0) a.hdr->status = 0u;
     const int C = a.C, CH = a.CH, V = a.V, K = a.k;
     const uint32_t region = uint32_t(a.Bmax) * uint32_t(C);          // slots per tensor
     const uint32_t slots = SAMPLE ? 2 * region : region;
-    if (w >= slots) return;
-    const uint32_t mine = (slots - 1 - w) / nw + 1;
-    const int nrows_in = *a.n_rows, nver_in = a.cu_rows[a.R];       // in flight with the first tags
+    if (b >= slots) return;
+    const uint32_t mine = (slots - 1 - b) / G + 1;                   // slots b + i G, i < mine
+    const int nrows = min(max(*a.n_rows, 0), a.Bmax);
+    const int nver = min(max(a.cu_rows[a.R], 0), nrows);
     const float c = a.c;
 
-    // slot -> (tensor, row, chunk) and the row's tag, for batch b0 (lane < nb)
-    auto slot_of = [&](uint32_t b0, int& tensor, int& t, int& ch) {
-        const uint32_t slot = w + (b0 + uint32_t(lane)) * nw;
-        tensor = slot >= region ? 1 : 0;
-        const uint32_t rel = tensor ? slot - region : slot;
-        t = int(rel / uint32_t(C));
-        ch = int(rel - uint32_t(t) * uint32_t(C));
-    };
-    int tg_r = -1, tg_j = -1;                                        // tag of this lane's slot
-    {
-        int tensor, t, ch;
-        if (uint32_t(lane) < min(uint32_t(kWave), mine)) {
-            slot_of(0, tensor, t, ch);
-            tg_r = a.tags[2 * t];
-            tg_j = a.tags[2 * t + 1];
+    for (uint32_t p0 = 0; p0 < mine; p0 += kPhaseSlots) {
+        const uint32_t np = min(uint32_t(kPhaseSlots), mine - p0);
+        // 1. describe this phase's slots; thread tid owns slots 2 tid and 2 tid + 1
+        uint64_t rp[2] = {0ull, 0ull};
+        int tt[2] = {0, 0}, cf[2] = {0, 0}, tk[2] = {-1, -1}, lv[2] = {0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t i = 2u * uint32_t(tid) + uint32_t(h);
+            if (i >= np) continue;
+            const uint32_t slot = b + (p0 + i) * G;
+            const int tensor = slot >= region ? 1 : 0;
+            const uint32_t rel = tensor ? slot - region : slot;
+            const int t = int(rel / uint32_t(C));
+            const int ch = int(rel - uint32_t(t) * uint32_t(C));
+            const int r = a.tags[2 * t], j = a.tags[2 * t + 1];      // t < Bmax: loaded with n_rows
+            if (t >= (tensor ? nver : nrows)) continue;
+            const bool ok = r >= 0 && r < a.R && j >= 0 && j <= K && (tensor == 0 || j < K);
+            lv[h] = 1;
+            tt[h] = t;
+            cf[h] = (ch << 2) | (tensor << 1) | (ok ? 1 : 0);
+            if (ok) {
+                const T* row = tensor == 0 ? static_cast<const T*>(a.target) + (long(r) * (K + 1) + j) * long(V)
+                                           : static_cast<const T*>(a.draft) + (long(r) * K + j) * long(V);
+                rp[h] = reinterpret_cast<uint64_t>(row);
+                if (SAMPLE && t < nver && j < K) tk[h] = r * K + j;
+            }
         }
-    }
-    const int nrows = min(max(nrows_in, 0), a.Bmax);
-    const int nver = min(max(nver_in, 0), nrows);
+        int nl;
+        const int pos = block_exclusive_scan_i32(lv[0] + lv[1], sh, nl);
+#pragma unroll
+        for (int h = 0, q = pos; h < 2; ++h) {
+            if (!lv[h]) continue;
+            d_row[q] = rp[h];
+            d_t[q] = tt[h];
+            d_cf[q] = cf[h];
+            d_tok[q] = tk[h];
+            st_f[q] = 0;
+            ++q;
+        }
+        if (tid == 0) next_item = 0;
+        __syncthreads();
 
-    for (uint32_t b0 = 0; b0 < mine; b0 += kWave) {
-        const uint32_t nb = min(uint32_t(kWave), mine - b0);
-        int tensor = 0, t = 0, ch = 0;
-        const bool in = uint32_t(lane) < nb;
-        if (in) slot_of(b0, tensor, t, ch);
-        const int r = tg_r, j = tg_j;
-        // the next batch's tags, fetched behind this batch's chunks
-        if (b0 + kWave < mine && uint32_t(lane) < min(uint32_t(kWave), mine - b0 - kWave)) {
-            int tn, ttn, chn;
-            slot_of(b0 + kWave, tn, ttn, chn);
-            tg_r = a.tags[2 * ttn];
-            tg_j = a.tags[2 * ttn + 1];
-        }
-        const bool live = in && t < (tensor ? nver : nrows);
-        const bool ok = live && r >= 0 && r < a.R && j >= 0 && j <= K && (tensor == 0 || j < K);
-        const int fl = (ok ? 1 : 0) | (tensor << 1);                  // bit 0 ok, bit 1 draft tensor
-        uint32_t plo = 0, phi = 0;
-        if (ok) {
-            const T* row = tensor == 0 ? static_cast<const T*>(a.target) + (long(r) * (K + 1) + j) * long(V)
-                                       : static_cast<const T*>(a.draft) + (long(r) * K + j) * long(V);
-            const uint64_t pv = reinterpret_cast<uint64_t>(row);
-            plo = uint32_t(pv);
-            phi = uint32_t(pv >> 32);
-        }
-        auto row_of = [&](int i) {
-            const uint64_t pv = (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(phi), i))) << 32) |
-                                uint32_t(__builtin_amdgcn_readlane(int(plo), i));
-            return reinterpret_cast<const T*>(pv);
+        // 2. stream the live items, one at a time per wavefront
+        auto grab = [&]() {
+            int i = 0;
+            if (lane == 0) i = atomicAdd(&next_item, 1);
+            return __builtin_amdgcn_readfirstlane(i);
         };
-        auto issue = [&](RW& buf, int i) {
-            if (__builtin_amdgcn_readlane(fl, i) & 1) {
-                const int beg = __builtin_amdgcn_readlane(ch, i) * CH;
-                buf.load(row_of(i), beg, V, lane, beg + CH <= V);
+        struct Cur {
+            const T* row;
+            int i, cf, x;
+        };
+        auto issue = [&](RW& buf, Cur& m, int i) {
+            m.i = i;
+            const uint64_t rw = d_row[i];
+            m.row = reinterpret_cast<const T*>(
+                (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(rw >> 32)))) << 32) |
+                uint32_t(__builtin_amdgcn_readfirstlane(int(rw))));
+            m.cf = __builtin_amdgcn_readfirstlane(d_cf[i]);
+            const int tok = __builtin_amdgcn_readfirstlane(d_tok[i]);
+            m.x = -1;
+            if (m.cf & 1) {
+                const int beg = (m.cf >> 2) * CH;
+                buf.load(m.row, beg, V, lane, beg + CH <= V);
+                if (SAMPLE && tok >= 0) m.x = a.tokens[tok];
             }
         };
-        uint64_t todo = __ballot(live);
-        auto next = [&]() {
-            if (!todo) return -1;
-            const int i = __builtin_ctzll(todo);
-            todo &= todo - 1;
-            return i;
-        };
-        RW q0, q1;
-        int i0 = next();
-        if (i0 >= 0) issue(q0, i0);
-        // draft token of the row, if this item's chunk holds it (loaded after
-        // the first chunk is in flight)
-        int x = -1;
-        if (SAMPLE && ok && t < nver && j < K) {
-            const int xx = a.tokens[long(r) * K + j];
-            if (xx >= ch * CH && xx < ch * CH + CH && xx < V) x = xx;
-        }
-        auto process = [&](const RW& buf, int i) {
-            const int f = __builtin_amdgcn_readlane(fl, i);
-            const int cc = __builtin_amdgcn_readlane(ch, i);
-            const int tt = __builtin_amdgcn_readlane(t, i);
-            const int beg = cc * CH;
+        auto process = [&](const RW& buf, const Cur& m) {
+            const int beg = (m.cf >> 2) * CH;
             const bool full = beg + CH <= V;
             float2 P = SAMPLE ? make_float2(-INFINITY, 0.f) : make_float2(-INFINITY, __int_as_float(INT_MAX));
-            if (f & 1) {
+            if (m.cf & 1) {
                 float xv[E];
                 buf.widen(beg, V, lane, full, xv);
                 P = SAMPLE ? chunk_softmax(xv, c) : chunk_argmax<RW>(xv, beg, lane);
-                if (SAMPLE) {
-                    const int xx = __builtin_amdgcn_readlane(x, i);
-                    if (xx >= 0 && lane == 0) {
-                        const float lx = Logit<DT>::load1(row_of(i) + xx);
-                        if (f & 2) a.rec[tt].bx = lx; else a.rec[tt].ax = lx;
+                if (SAMPLE && m.x >= beg && m.x < beg + CH && m.x < V) {
+                    // the draft token's logit, from the lane that holds it
+                    const int off = m.x - beg, vi = off / GW;
+                    const int qx = (vi >> 6) * GW + off % GW;
+                    if (lane == (vi & (kWave - 1))) {
+                        float lx = 0.f;
+#pragma unroll
+                        for (int q = 0; q < E; ++q)
+                            if (q == qx) lx = xv[q];
+                        st_x[m.i] = lx;
+                        st_f[m.i] = 1;
                     }
                 }
             }
-            if (lane == 0) ((f & 2) ? a.part_q : a.part_p)[long(tt) * C + cc] = P;
+            if (lane == 0) st_p[m.i] = P;
         };
-        while (i0 >= 0) {
-            const int i1 = next();
-            if (i1 >= 0) issue(q1, i1);
-            process(q0, i0);
-            if (i1 < 0) break;
-            i0 = next();
-            if (i0 >= 0) issue(q0, i0);
-            process(q1, i1);
+        RW q0, q1;
+        Cur m0, m1;
+        int i0 = grab();
+        if (i0 < nl) issue(q0, m0, i0);
+        while (i0 < nl) {
+            const int i1 = grab();
+            if (i1 < nl) issue(q1, m1, i1);
+            process(q0, m0);
+            if (i1 >= nl) break;
+            i0 = grab();
+            if (i0 < nl) issue(q0, m0, i0);
+            process(q1, m1);
         }
+        __syncthreads();
+
+        // 3. write the phase's results (no stores while the loads stream: a
+        //    store ahead of a load in the memory queue would delay its wait)
+        for (int i = tid; i < nl; i += kStreamThreads) {
+            const int t = d_t[i], cf = d_cf[i];
+            ((cf & 2) ? a.part_q : a.part_p)[long(t) * C + (cf >> 2)] = st_p[i];
+            if (st_f[i]) {
+                if (cf & 2) a.rec[t].bx = st_x[i]; else a.rec[t].ax = st_x[i];
+            }
+        }
+        __syncthreads();                             // the next phase rewrites the descriptions
     }
 }
 
@@ -676,15 +701,14 @@ static int device_cus(int& cus) {
     return SPECV_OK;
 }
 
-// Workgroups for a persistent kernel over `items` wave-sized work items: as
-// many as are resident at once, but no more than one wave per item.
+// verify_stream: as many kStreamThreads workgroups as are resident at once
+// (one per compute unit), no more than there are slots.
 template <class K>
-static int persistent_grid(K kernel, long items, int cus, int& G) {
+static int stream_grid(K kernel, long slots, int cus, int& G) {
     int per = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess || per < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kStreamThreads, 0) != hipSuccess || per < 1)
         return fail(SPECV_EDEVICE, "spec_verify: cannot query the occupancy");
-    const long waves_needed = std::max<long>(1, items);
-    G = int(std::min<long>(long(cus) * per, (waves_needed + kWaves - 1) / kWaves));
+    G = int(std::min<long>(long(cus) * per, std::max<long>(1, slots)));
     return SPECV_OK;
 }
 
@@ -695,14 +719,14 @@ static int launch_verify(int mode, VerifyArgs& a, hipStream_t s) {
     int G = 0;
     if (mode == SPECV_GREEDY) {
         auto ks = verify_stream<DT, SPECV_GREEDY, VEC>;
-        if (int e = persistent_grid(ks, long(a.Bmax) * a.C, cus, G)) return e;
-        SPECV_LAUNCH("verify_stream", ks, G, kThreads, 0, s, a);
+        if (int e = stream_grid(ks, long(a.Bmax) * a.C, cus, G)) return e;
+        SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
         SPECV_LAUNCH("verify_decide", verify_decide<DT, SPECV_GREEDY, VEC>, a.R, kDecideThreads, 0, s, a);
         return SPECV_OK;
     }
     auto ks = verify_stream<DT, SPECV_SAMPLE, VEC>;
-    if (int e = persistent_grid(ks, 2L * a.Bmax * a.C, cus, G)) return e;
-    SPECV_LAUNCH("verify_stream", ks, G, kThreads, 0, s, a);
+    if (int e = stream_grid(ks, 2L * a.Bmax * a.C, cus, G)) return e;
+    SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
     SPECV_LAUNCH("verify_decide", verify_decide<DT, SPECV_SAMPLE, VEC>, a.R, kDecideThreads, 0, s, a);
     return SPECV_OK;
 }
