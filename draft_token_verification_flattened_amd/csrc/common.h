@@ -182,6 +182,20 @@ __device__ __forceinline__ int wave_incl_scan_i32(int v) {
     return v;
 }
 
+// Inclusive prefix sum of a float across the wave in lane order (all lanes
+// active), same pattern as wave_incl_scan_i32.
+__device__ __forceinline__ float wave_incl_scan_f32(float v) {
+    const float v0 = v;
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v0), 0x111, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v0), 0x112, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v0), 0x113, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xe, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xc, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+    return v;
+}
+
 // Block-wide exclusive scan of one int per thread (DPP within each wave, wave
 // totals through LDS); returns the block total too. Totals stay below 2^31.
 __device__ __forceinline__ int block_exclusive_scan_i32(int v, int* sh, int& total) {

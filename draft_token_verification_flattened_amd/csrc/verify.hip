@@ -369,25 +369,27 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
 // row (and, for PAIR, of the draft row) is loaded in the stream layout; wt(xt,
 // xd) is an element's weight. Returns the first element whose running sum from
 // `base`, in index order, exceeds thr; else the last element with positive
-// weight (beg if none).
+// weight (beg if none). The chunk is kNV groups of 64 lanes x GW elements in
+// index order (lane-major inside a group): the group totals pick the group, a
+// scan of the lanes' sums picks the lane, and the lane scans its own elements.
 template <int DT, bool VEC, bool PAIR, class Wf>
 __device__ __forceinline__ int chunk_pick(const typename Logit<DT>::T* trow, const typename Logit<DT>::T* drow, int beg,
-                          int V, float base, float thr, Wf wt) {
+                                          int V, float base, float thr, Wf wt) {
     using RW = Raw<DT, VEC>;
     constexpr int GW = RW::kVec;
     const int lane = threadIdx.x & (kWave - 1);
     const bool full = beg + chunk_elems(GW) <= V;
     const int nv = VEC ? V / GW - beg / GW - lane : 0;
     RW rt, rd;
-    if constexpr (VEC) {                            // scalar rows load group by group below
+    if constexpr (VEC) {
         rt.load(trow, beg, V, lane, full);
         if constexpr (PAIR) rd.load(drow, beg, V, lane, full);
     }
-    float run = base;
+    float w[kNV][GW], ls[kNV], gt[kNV];
     int lastw = -1;
 #pragma unroll
-    for (int u = 0; u < kNV; ++u) {                 // groups of 64 * GW elements, in index order
-        float xt[GW], xd[GW], w[GW];
+    for (int u = 0; u < kNV; ++u) {
+        float xt[GW], xd[GW];
         if constexpr (VEC) {
             RW::LT::unpack(rt.v[u], xt);
             if constexpr (PAIR) RW::LT::unpack(rd.v[u], xd);
@@ -400,27 +402,39 @@ __device__ __forceinline__ int chunk_pick(const typename Logit<DT>::T* trow, con
             }
         }
         const bool ok = !VEC || full || u * kWave < nv;
-        float ls = 0.f;
+        ls[u] = 0.f;
 #pragma unroll
         for (int e = 0; e < GW; ++e) {
-            w[e] = ok && xt[e] != -INFINITY ? wt(xt[e], PAIR ? xd[e] : 0.f) : 0.f;
-            ls += w[e];
+            w[u][e] = ok && xt[e] != -INFINITY ? wt(xt[e], PAIR ? xd[e] : 0.f) : 0.f;
+            ls[u] += w[u][e];
+            if (w[u][e] > 0.f) lastw = beg + RW::offset(u * GW + e, lane);
         }
-        const float incl = wave_inclusive_scan(ls, lane);
-        float cum = run + (incl - ls);
-        int hit = INT_MAX;
-#pragma unroll
-        for (int e = 0; e < GW; ++e) {
-            const int off = beg + RW::offset(u * GW + e, lane);
-            cum += w[e];
-            if (w[e] > 0.f) lastw = max(lastw, off);
-            if (hit == INT_MAX && cum > thr) hit = off;
-        }
-        const int f = wave_min_int(hit);
-        if (f != INT_MAX) return f;
-        run += __shfl(incl, kWave - 1, kWave);
     }
-    const int lw = -wave_min_int(-lastw);
+#pragma unroll
+    for (int u = 0; u < kNV; ++u) gt[u] = wave_sum_dpp(ls[u]);
+    float run = base;
+#pragma unroll
+    for (int u = 0; u < kNV; ++u) {
+        if (run + gt[u] > thr) {                        // the crossing is in group u (or, by rounding, later)
+            const float incl = wave_incl_scan_f32(ls[u]);
+            const uint64_t hit = __ballot(run + incl > thr);
+            if (hit) {
+                const int l = __builtin_ctzll(hit);
+                float cum = run + (incl - ls[u]);
+                int f = -1, lp = GW - 1;                // first element of the lane past thr
+#pragma unroll
+                for (int e = 0; e < GW; ++e) {
+                    cum += w[u][e];
+                    if (f < 0 && cum > thr) f = e;
+                    if (w[u][e] > 0.f) lp = e;
+                }
+                const int fe = __builtin_amdgcn_readlane(f < 0 ? lp : f, l);
+                return beg + RW::offset(u * GW + fe, l);
+            }
+        }
+        run += gt[u];
+    }
+    const int lw = -wave_min_int_dpp(-lastw);
     return lw >= 0 ? lw : beg;
 }
 
@@ -432,25 +446,24 @@ template <class Mf>
 __device__ __forceinline__ int wave_find_chunk(int C, float u, Mf mass_of, float& base, float& cthr) {
     const int lane = threadIdx.x & (kWave - 1);
     float total = 0.f;
-    for (int c0 = 0; c0 < C; c0 += kWave) {
-        const int cc = c0 + lane;
-        total += __shfl(wave_inclusive_scan(cc < C ? mass_of(cc) : 0.f, lane), kWave - 1, kWave);
-    }
+    for (int c0 = 0; c0 < C; c0 += kWave) total += wave_sum_dpp(c0 + lane < C ? mass_of(c0 + lane) : 0.f);
     const float thr = u * total;
     float carry = 0.f;
     int last_pos = -1;
     for (int c0 = 0; c0 < C; c0 += kWave) {
         const int cc = c0 + lane;
         const float mc = cc < C ? mass_of(cc) : 0.f;
-        const float inc = wave_inclusive_scan(mc, lane) + carry;
-        const int cand = wave_min_int(cc < C && inc > thr ? cc : INT_MAX);
-        last_pos = max(last_pos, -wave_min_int(cc < C && mc > 0.f ? -cc : 1));
-        if (cand != INT_MAX) {
-            base = __shfl(inc - mc, cand - c0, kWave);
+        const float inc = wave_incl_scan_f32(mc) + carry;
+        const uint64_t hit = __ballot(cc < C && inc > thr);
+        const uint64_t pos = __ballot(cc < C && mc > 0.f);
+        if (pos) last_pos = c0 + 63 - __builtin_clzll(pos);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            base = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc - mc), l));
             cthr = thr;
-            return cand;
+            return c0 + l;
         }
-        carry = __shfl(inc, kWave - 1, kWave);
+        carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), 63));
     }
     base = 0.f;
     cthr = INFINITY;
@@ -548,7 +561,7 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
     __shared__ int g_s[SPECV_MAX_K + 1];
     __shared__ float4 st_s[SPECV_MAX_K + 1];
     __shared__ float mass_s[SAMPLE ? kMaxChunks : 1];
-    __shared__ int bad_s;
+    __shared__ int bad_s, rnext_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = blockIdx.x;
     const int k = a.k, C = a.C, CH = a.CH, V = a.V;
@@ -558,7 +571,10 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
     const int L = a.cu_rows[r + 1] - base;
     const float ub = SAMPLE ? a.uniforms[long(r) * (k + 1) + k] : 0.f;
     int32_t* out = a.out_tokens + long(r) * (k + 1);
-    if (tid == 0) bad_s = L < 0 || L > k || base < 0 || base + L > N || N < 0 || N + r >= nrows;
+    if (tid == 0) {
+        bad_s = L < 0 || L > k || base < 0 || base + L > N || N < 0 || N + r >= nrows;
+        rnext_s = 0;
+    }
     __syncthreads();
 
     if (!bad_s) {
@@ -632,35 +648,49 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
         const T* drow = static_cast<const T*>(a.draft) + (long(r) * k + min(acc, k - 1)) * long(V);
         const bool rejected = acc < L;
         if (rejected) {
-            // the rejected row pair, chunk w, w + kW, ... per wavefront, two in flight
+            // the rejected row pair: each wavefront takes the next chunk from an
+            // LDS counter (the compute unit serves its waves unevenly) and loads
+            // it while it reduces the previous one
             auto issue = [&](RW& rt, RW& rd, int ch) {
                 const int beg = ch * CH;
                 const bool full = beg + CH <= V;
                 rt.load(trow, beg, V, lane, full);
                 rd.load(drow, beg, V, lane, full);
             };
+            auto grab = [&]() {
+                int i = 0;
+                if (lane == 0) i = atomicAdd(&rnext_s, 1);
+                return __builtin_amdgcn_readfirstlane(i);
+            };
             RW t0, d0;
             if constexpr (!VEC) {                  // scalar rows: one chunk at a time (registers)
-                for (int ch = wave; ch < C; ch += kW) {
+                for (int ch = grab(); ch < C; ch = grab()) {
                     issue(t0, d0, ch);
                     const float m0 = chunk_residual_mass(t0, d0, ch * CH, V, lane, c, lp, lq);
                     if (lane == 0) mass_s[ch] = m0;
                 }
+            } else {
+                RW t1, d1;
+                int c0 = grab();
+                if (c0 < C) issue(t0, d0, c0);
+                while (c0 < C) {
+                    const int c1 = grab();
+                    if (c1 < C) issue(t1, d1, c1);
+                    const float m0 = chunk_residual_mass(t0, d0, c0 * CH, V, lane, c, lp, lq);
+                    if (lane == 0) mass_s[c0] = m0;
+                    if (c1 >= C) break;
+                    c0 = grab();
+                    if (c0 < C) issue(t0, d0, c0);
+                    const float m1 = chunk_residual_mass(t1, d1, c1 * CH, V, lane, c, lp, lq);
+                    if (lane == 0) mass_s[c1] = m1;
+                }
             }
-            RW t1, d1;
-            int ch = VEC ? wave : C;
-            if (ch < C) issue(t0, d0, ch);
-            while (ch < C) {
-                const int c1 = ch + kW;
-                if (c1 < C) issue(t1, d1, c1);
-                const float m0 = chunk_residual_mass(t0, d0, ch * CH, V, lane, c, lp, lq);
-                if (lane == 0) mass_s[ch] = m0;
-                if (c1 >= C) break;
-                const int c2 = c1 + kW;
-                if (c2 < C) issue(t0, d0, c2);
-                const float m1 = chunk_residual_mass(t1, d1, c1 * CH, V, lane, c, lp, lq);
-                if (lane == 0) mass_s[c1] = m1;
-                ch = c2;
+        } else {
+            // bonus row: chunk masses of p relative to Mp, from the partials
+            const float2* pp = a.part_p + long(N + r) * C;
+            for (int cc = tid; cc < C; cc += kDecideThreads) {
+                const float2 q = pp[cc];
+                mass_s[cc] = q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
             }
         }
         __syncthreads();
@@ -670,17 +700,23 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
             for (int c0 = 0; c0 < C; c0 += kWave) total += wave_sum_dpp(c0 + lane < C ? mass_s[c0 + lane] : 0.f);
         float cbase, cthr;
         int y;
-        if (total > 0.f) {                         // residual max(0, p - q) of row a_r
+        if (rejected && total > 0.f) {             // residual max(0, p - q) of row a_r
             const int cs = wave_find_chunk(C, ub, [&](int cc) { return mass_s[cc]; }, cbase, cthr);
             y = chunk_pick<DT, VEC, true>(trow, drow, cs * CH, V, cbase, cthr, [&](float xt_, float xd_) {
                 return residual_weight(xt_, xd_, c, lp, lq);
             });
         } else {                                   // p of row a_r: the bonus row, or a residual without mass
-            const float2* pp = a.part_p + long(rejected ? base + acc : N + r) * C;
-            const int cs = wave_find_chunk(C, ub, [&](int cc) {
-                const float2 q = pp[cc];
-                return q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
-            }, cbase, cthr);
+            if (rejected) {
+                const float2* pp = a.part_p + long(base + acc) * C;
+                for (int cc = lane; cc < C; cc += kWave) {
+                    const float2 q = pp[cc];
+                    mass_s[cc] = q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+            const int cs = wave_find_chunk(C, ub, [&](int cc) { return mass_s[cc]; }, cbase, cthr);
             y = chunk_pick<DT, VEC, false>(trow, nullptr, cs * CH, V, cbase, cthr, [&](float xt_, float) {
                 return __builtin_amdgcn_exp2f(fmaf(xt_, c, -st.x));
             });
