@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--variants", action="store_true",
                     help="also time greedy and verify-all variants of the workload")
+    ap.add_argument("--lagged", action="store_true",
+                    help="also time the lagged schedule (two streams, HIP graph) on rotating confidence rounds")
     ap.add_argument("--copies", type=int, default=3,
                     help="input copies rotated over the steps (no step reads logits cached by the previous one)")
     ap.add_argument("--copy-probe", type=float, default=0.0,
@@ -133,6 +135,106 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
                 verify_tokens_per_s=N / (verify_us * 1e-6) if verify_us else None,
                 algorithmic_bytes=nbytes, dominant_gbps=achieved / 1e9 if achieved else None,
                 dominant_frac=achieved / HBM_PEAK if achieved else None, kernels=kern)
+
+
+def run_lagged(d, w, mode_c, steps, warmup, B, torch, copies):
+    """Lagged scheduling over n_rounds rotating confidence rounds: round t
+    verifies lengths scheduled from round t-2's confidences, and the next
+    round's schedule runs inside round t's verify launches (spec_verify_ex).
+    Timed eagerly and as a replayed HIP graph, next to the synchronous
+    schedule-then-verify of the same rounds.
+    Goodput: expected emitted tokens per step (R + the current round's survival
+    summed over the verified drafts) per unit step time."""
+    import numpy as np
+    from draft_token_verification_flattened_amd import workloads
+    from draft_token_verification_flattened_amd.pipeline import LaggedStep, to_device
+    per = 2 * copies if copies % 2 else copies               # batch slots and input copies line up
+    n_rounds = per * max(1, 8 // per)                        # the graph replays this many rounds, in a cycle
+    n_long = 24                                              # the lag's effect, from a run without wrap-around
+    zlong = to_device(workloads.conf_rounds(w, n_long), "cuda")
+    zdev = zlong[:n_rounds].contiguous()
+    R, k = w.R, w.k
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+
+    # per-round lengths and current-round survival (for the goodput)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    L = torch.zeros(R, **i32)
+    tags = torch.zeros(R * (k + 1), 2, **i32)
+    cu = torch.zeros(R + 1, **i32)
+    nr = torch.zeros(1, **i32)
+    sv = torch.zeros(R, k, dtype=torch.float64, device="cuda")
+    Ls, Ss = [], []
+    for t in range(n_long):
+        B.spec_schedule(zlong[t], d.T, d.tbl_b, d.tbl_t, k, L, tags, cu, nr, d.ws_sched, sv)
+        torch.cuda.synchronize()
+        Ls.append(L.cpu().numpy().copy())
+        Ss.append(sv.cpu().numpy().copy())
+
+    def emitted(lengths, S):
+        m = np.arange(k)[None, :] < lengths[:, None]
+        return R + float((S * m).sum())
+
+    sync_n = [int(Ls[t].sum()) for t in range(n_rounds)]                 # the timed cycle
+    lag_n = [int(Ls[(t - 2) % n_rounds].sum()) for t in range(n_rounds)]
+    sync_e = [emitted(Ls[t], Ss[t]) for t in range(2, n_long)]
+    lag_e = [emitted(Ls[t - 2], Ss[t]) for t in range(2, n_long)]
+
+    # synchronous: schedule(t) then verify(t), one stream
+    def sync_step(t):
+        if len(d._copies) > 1:
+            d.use_copy(t)
+        B.spec_schedule(zdev[t % n_rounds], d.T, d.tbl_b, d.tbl_t, k, d.lengths, d.tags, d.cu_rows, d.n_rows,
+                        d.ws_sched, d.survival)
+        d.verify(mode_c, diag=False)
+    for t in range(warmup):
+        sync_step(t)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for t in range(steps):
+        sync_step(t)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_sync = ev0.elapsed_time(ev1) / steps
+
+    ls = LaggedStep(d, zdev)
+    ls.start(0)
+    for _ in range(warmup):
+        ls.step(mode_c)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        ls.step(mode_c)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_eager = ev0.elapsed_time(ev1) / steps
+
+    rounds = n_rounds
+    ls.start(0)
+    g = ls.capture(mode_c, rounds)
+    reps = max(1, steps // rounds)
+    for _ in range(2):
+        ls.start(0)
+        g.replay()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_graph = ev0.elapsed_time(ev1) / (reps * rounds)
+    mean = lambda v: float(np.mean(v))  # noqa: E731
+    return dict(
+        rounds_timed=n_rounds, rounds_goodput=n_long - 2, lag=2,
+        ms_per_step_sync=ms_sync, ms_per_step_lagged=ms_eager, ms_per_step_lagged_graph=ms_graph,
+        verified_per_step_sync=mean(sync_n), verified_per_step_lagged=mean(lag_n),
+        tokens_per_s_sync=mean(sync_n) / (ms_sync * 1e-3),
+        tokens_per_s_lagged_graph=mean(lag_n) / (ms_graph * 1e-3),
+        expected_emitted_per_step_sync=mean(sync_e), expected_emitted_per_step_lagged=mean(lag_e),
+        goodput_sync=mean(sync_e) / (ms_sync * 1e-3), goodput_lagged_graph=mean(lag_e) / (ms_graph * 1e-3),
+        emitted_lost_to_lag=1.0 - mean(lag_e) / mean(sync_e),
+    )
 
 
 def cpu_baseline(w, mode, max_len, min_seconds=10.0):
@@ -226,6 +328,10 @@ def main():
                 r = run_variant(d, w, mc, mode, ml, args.steps, args.warmup, B, torch)
                 extra[f"{mode}_{'scheduled' if ml == w.k else 'verify_all'}"] = r
 
+    lagged = None
+    if args.variants or args.lagged:
+        lagged = run_lagged(d, w, mode_c, args.steps, args.warmup, B, torch, args.copies)
+
     traffic, thash = committed_traffic()
     dom = main_res["kernels"].get(DOMINANT, {})
     roofline = {
@@ -271,6 +377,7 @@ def main():
                                                 "tokens_per_s", "verify_us", "verify_tokens_per_s",
                                                 "dominant_gbps", "dominant_frac")}
                      for k, v in extra.items()},
+        "lagged_schedule": lagged,
         "source_hash": source_hash(),
     }
     print(json.dumps(out))

@@ -27,6 +27,14 @@ MAX_K, MAX_SCHED_ITEMS = 32, 16384
 
 _c_int, _c_size, _c_ptr = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
+class ScheduleJob(ctypes.Structure):
+    """specv_schedule_job: spec_schedule's arguments for spec_verify_ex."""
+    _fields_ = [("R", _c_int), ("k", _c_int), ("conf_logit", _c_ptr), ("pos_temp", _c_ptr),
+                ("tbl_tokens", _c_ptr), ("tbl_thr", _c_ptr), ("n_tbl", _c_int), ("max_len", _c_int),
+                ("len_out", _c_ptr), ("tags_out", _c_ptr), ("cu_rows_out", _c_ptr), ("n_rows_out", _c_ptr),
+                ("survival_out", _c_ptr), ("ws", _c_ptr), ("ws_bytes", _c_size)]
+
+
 _SIGS = {
     "spec_schedule_workspace_bytes": (_c_size, [_c_int, _c_int]),
     "spec_schedule": (_c_int, [_c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
@@ -36,6 +44,9 @@ _SIGS = {
     "spec_verify": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                              _c_ptr, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                              _c_size, _c_ptr]),
+    "spec_verify_ex": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                _c_ptr, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                _c_size, ctypes.POINTER(ScheduleJob), _c_ptr]),
     "markov_draft_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "markov_draft": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
                               _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
@@ -119,6 +130,27 @@ def schedule_workspace_bytes(R: int, k: int) -> int:
     return int(lib().spec_schedule_workspace_bytes(R, k))
 
 
+def schedule_job(conf_logit, pos_temp, tbl_tokens, tbl_thr, max_len, len_out, tags_out, cu_rows_out,
+                 n_rows_out, ws, survival_out=None) -> ScheduleJob:
+    """A spec_schedule request to hand to spec_verify(..., next_job=...). The
+    tensors must stay alive until the call that uses it has run."""
+    R, k = conf_logit.shape
+    _dev(conf_logit, "conf_logit", (torch.float32,))
+    _dev(pos_temp, "pos_temp", (torch.float32,), (k,))
+    _dev(tbl_tokens, "tbl_tokens", (torch.int32,))
+    _dev(tbl_thr, "tbl_thr", (torch.float64,), tuple(tbl_tokens.shape))
+    _dev(len_out, "len_out", (torch.int32,), (R,))
+    _dev(tags_out, "tags_out", (torch.int32,), (R * (k + 1), 2))
+    _dev(cu_rows_out, "cu_rows_out", (torch.int32,), (R + 1,))
+    _dev(n_rows_out, "n_rows_out", (torch.int32,), (1,))
+    _dev(ws, "ws", (torch.uint8,))
+    if survival_out is not None:
+        _dev(survival_out, "survival_out", (torch.float64,), (R, k))
+    return ScheduleJob(R, k, _ptr(conf_logit), _ptr(pos_temp), _ptr(tbl_tokens), _ptr(tbl_thr), tbl_tokens.numel(),
+                       int(max_len), _ptr(len_out), _ptr(tags_out), _ptr(cu_rows_out), _ptr(n_rows_out),
+                       _ptr(survival_out), _ptr(ws), ws.numel())
+
+
 def spec_schedule(conf_logit, pos_temp, tbl_tokens, tbl_thr, max_len, len_out, tags_out, cu_rows_out,
                   n_rows_out, ws, survival_out=None, stream=None):
     R, k = conf_logit.shape
@@ -161,7 +193,9 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 
 def spec_verify(mode, target, draft, tokens, tags, cu_rows, n_rows, temperature, uniforms, accepted_len_out,
-                out_tokens, ws, row_diag=None, stream=None):
+                out_tokens, ws, row_diag=None, stream=None, next_job: Optional[ScheduleJob] = None):
+    """spec_verify; with next_job, spec_verify_ex (the job's schedule runs
+    beside this call's decisions)."""
     R, k1, V = target.shape
     k = k1 - 1
     dt = logit_dtype(target)
@@ -178,10 +212,14 @@ def spec_verify(mode, target, draft, tokens, tags, cu_rows, n_rows, temperature,
     _dev(ws, "ws", (torch.uint8,))
     if row_diag is not None:
         _dev(row_diag, "row_diag", (torch.float32,), (R * (k + 1), 4))
-    _check(lib().spec_verify(int(mode), dt, R, k, V, _ptr(target), _ptr(draft) if mode == SAMPLE else None,
-                             _ptr(tokens), _ptr(tags), _ptr(cu_rows), _ptr(n_rows), float(temperature),
-                             _ptr(uniforms) if mode == SAMPLE else None, _ptr(accepted_len_out),
-                             _ptr(out_tokens), _ptr(row_diag), _ptr(ws), ws.numel(), _stream(stream)))
+    args = (int(mode), dt, R, k, V, _ptr(target), _ptr(draft) if mode == SAMPLE else None,
+            _ptr(tokens), _ptr(tags), _ptr(cu_rows), _ptr(n_rows), float(temperature),
+            _ptr(uniforms) if mode == SAMPLE else None, _ptr(accepted_len_out),
+            _ptr(out_tokens), _ptr(row_diag), _ptr(ws), ws.numel())
+    if next_job is None:
+        _check(lib().spec_verify(*args, _stream(stream)))
+    else:
+        _check(lib().spec_verify_ex(*args, ctypes.byref(next_job), _stream(stream)))
 
 
 def markov_workspace_bytes(R: int, k: int, V: int, d_m: int) -> int:

@@ -28,7 +28,10 @@ int launch_kernel(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 bl
                   hipStream_t s, Args... args) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (timing_on()) timing_events(e0, e1);
-    hipExtLaunchKernelGGL(kernel, grid, block, static_cast<std::uint32_t>(shmem), s, e0, e1, 0u, args...);
+    if (e0 && e1)
+        hipExtLaunchKernelGGL(kernel, grid, block, static_cast<std::uint32_t>(shmem), s, e0, e1, 0u, args...);
+    else                                   // plain launch: also what stream capture records
+        hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
     const hipError_t e = hipGetLastError();
     if (e0 && e1) timing_record(name, e0, e1);
     if (e != hipSuccess) return fail(SPECV_EDEVICE, "%s: launch failed: %s", name, hipGetErrorString(e));

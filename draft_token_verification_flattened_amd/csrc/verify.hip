@@ -37,6 +37,7 @@
 
 #include "common.h"
 #include "host.h"
+#include "schedule_dev.h"
 
 namespace specv {
 
@@ -71,6 +72,8 @@ struct VerifyArgs {
     float2* part_p;                         // [Bmax * C] target chunk partials
     float2* part_q;                         // [Bmax * C] draft chunk partials (sampling)
     RowRec* rec;                            // [Bmax]
+    SchedArgs next;                         // the next round's schedule (spec_verify_ex)
+    int has_next;                           // 1: verify_decide runs `next` as workgroup R
 };
 
 struct Layout {
@@ -551,8 +554,15 @@ __device__ __forceinline__ float2 merge_partials(const float2* part, int C, int 
 // draws by the inverse CDF (chunk, then position in the chunk). With every row
 // kept, wavefront 0 draws the bonus token from p of the bonus row, chunk masses
 // taken from the partials.
+static_assert(kDecideThreads == kSchedThreads, "the next round's schedule runs in a decide workgroup");
+
 template <int DT, int MODE, bool VEC>
 __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
+    if (a.has_next && int(blockIdx.x) == a.R) {     // the next round's schedule, beside this round's decisions
+        extern __shared__ __align__(16) uint64_t sched_lds[];
+        schedule_bucket_body(a.next, sched_lds);
+        return;
+    }
     using RW = Raw<DT, VEC>;
     using T = typename RW::T;
     constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
@@ -748,8 +758,26 @@ static int stream_grid(K kernel, long slots, int cus, int& G) {
     return SPECV_OK;
 }
 
+// verify_decide, with the next round's schedule as one more workgroup when it
+// fits one (else launched after it, on the same stream).
+template <class K>
+static int launch_decide(K kernel, VerifyArgs& a, const SchedArgs* next, hipStream_t s) {
+    a.has_next = next && schedule_is_bucket(*next);
+    size_t lds = 0;
+    if (a.has_next) {
+        a.next = *next;
+        lds = schedule_bucket_lds(next->R, next->k, next->kk);
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                int(lds)) != hipSuccess)
+            return fail(SPECV_EDEVICE, "spec_verify: cannot reserve %zu bytes of LDS", lds);
+    }
+    SPECV_LAUNCH("verify_decide", kernel, a.R + (a.has_next ? 1 : 0), kDecideThreads, lds, s, a);
+    if (next && !a.has_next) return schedule_launch(*next, s);
+    return SPECV_OK;
+}
+
 template <int DT, bool VEC>
-static int launch_verify(int mode, VerifyArgs& a, hipStream_t s) {
+static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStream_t s) {
     int cus = 0;
     if (int e = device_cus(cus)) return e;
     int G = 0;
@@ -757,14 +785,12 @@ static int launch_verify(int mode, VerifyArgs& a, hipStream_t s) {
         auto ks = verify_stream<DT, SPECV_GREEDY, VEC>;
         if (int e = stream_grid(ks, long(a.Bmax) * a.C, cus, G)) return e;
         SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
-        SPECV_LAUNCH("verify_decide", verify_decide<DT, SPECV_GREEDY, VEC>, a.R, kDecideThreads, 0, s, a);
-        return SPECV_OK;
+        return launch_decide(verify_decide<DT, SPECV_GREEDY, VEC>, a, next, s);
     }
     auto ks = verify_stream<DT, SPECV_SAMPLE, VEC>;
     if (int e = stream_grid(ks, 2L * a.Bmax * a.C, cus, G)) return e;
     SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
-    SPECV_LAUNCH("verify_decide", verify_decide<DT, SPECV_SAMPLE, VEC>, a.R, kDecideThreads, 0, s, a);
-    return SPECV_OK;
+    return launch_decide(verify_decide<DT, SPECV_SAMPLE, VEC>, a, next, s);
 }
 
 }  // namespace specv
@@ -775,13 +801,12 @@ extern "C" size_t spec_verify_workspace_bytes(int mode, int R, int k, int V) {
     return specv::ws_layout(R, k, V).total;
 }
 
-extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void* target_logits,
-                           const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
-                           const int32_t* cu_rows, const int32_t* n_rows, float temperature,
-                           const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
-                           float* row_diag, void* ws, size_t ws_bytes, specv_stream stream) {
-    using namespace specv;
-    clear_error();
+namespace specv {
+
+static int verify_impl(int mode, int dtype, int R, int k, int V, const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, const int32_t* tags, const int32_t* cu_rows, const int32_t* n_rows,
+                       float temperature, const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
+                       float* row_diag, void* ws, size_t ws_bytes, const SchedArgs* next, specv_stream stream) {
     if (mode != SPECV_GREEDY && mode != SPECV_SAMPLE)
         return fail(SPECV_EINVAL, "spec_verify: mode %d is neither greedy (0) nor sample (1)", mode);
     if (dtype != SPECV_BF16 && dtype != SPECV_F32)
@@ -838,8 +863,46 @@ extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void*
     a.part_p = reinterpret_cast<float2*>(w + lay.part_p);
     a.part_q = reinterpret_cast<float2*>(w + lay.part_q);
     a.rec = reinterpret_cast<RowRec*>(w + lay.rec);
+    a.has_next = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == SPECV_BF16)
-        return vec ? launch_verify<SPECV_BF16, true>(mode, a, s) : launch_verify<SPECV_BF16, false>(mode, a, s);
-    return vec ? launch_verify<SPECV_F32, true>(mode, a, s) : launch_verify<SPECV_F32, false>(mode, a, s);
+        return vec ? launch_verify<SPECV_BF16, true>(mode, a, next, s)
+                   : launch_verify<SPECV_BF16, false>(mode, a, next, s);
+    return vec ? launch_verify<SPECV_F32, true>(mode, a, next, s) : launch_verify<SPECV_F32, false>(mode, a, next, s);
+}
+
+}  // namespace specv
+
+extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void* target_logits,
+                           const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
+                           const int32_t* cu_rows, const int32_t* n_rows, float temperature,
+                           const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
+                           float* row_diag, void* ws, size_t ws_bytes, specv_stream stream) {
+    specv::clear_error();
+    return specv::verify_impl(mode, dtype, R, k, V, target_logits, draft_logits, draft_tokens, tags, cu_rows, n_rows,
+                              temperature, uniforms, accepted_len_out, out_tokens, row_diag, ws, ws_bytes, nullptr,
+                              stream);
+}
+
+extern "C" int spec_verify_ex(int mode, int dtype, int R, int k, int V, const void* target_logits,
+                              const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
+                              const int32_t* cu_rows, const int32_t* n_rows, float temperature,
+                              const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
+                              float* row_diag, void* ws, size_t ws_bytes, const specv_schedule_job* next,
+                              specv_stream stream) {
+    using namespace specv;
+    clear_error();
+    SchedArgs na;
+    if (next) {
+        if (int e = schedule_prepare(next->R, next->k, next->conf_logit, next->pos_temp, next->tbl_tokens,
+                                     next->tbl_thr, next->n_tbl, next->max_len, next->len_out, next->tags_out,
+                                     next->cu_rows_out, next->n_rows_out, next->survival_out, next->ws,
+                                     next->ws_bytes, "spec_verify_ex (next)", na))
+            return e;
+        if (next->tags_out == tags || next->cu_rows_out == cu_rows || next->n_rows_out == n_rows)
+            return fail(SPECV_EINVAL, "spec_verify_ex: the next schedule must write a batch other than this one");
+    }
+    return verify_impl(mode, dtype, R, k, V, target_logits, draft_logits, draft_tokens, tags, cu_rows, n_rows,
+                       temperature, uniforms, accepted_len_out, out_tokens, row_diag, ws, ws_bytes,
+                       next ? &na : nullptr, stream);
 }

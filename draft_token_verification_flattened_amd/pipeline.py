@@ -109,3 +109,77 @@ class DeviceStep:
     # -- readback ------------------------------------------------------------
     def host(self, name) -> np.ndarray:
         return getattr(self, name).cpu().numpy()
+
+
+class LaggedStep:
+    """Asynchronous lagged scheduling over a run of rounds.
+
+    The lengths verified in round t come from the confidences of round
+    t - lag (lag = 2: the schedule for round t+1 is made while round t is
+    verified, from the confidences known before round t). Each round is one
+    spec_verify_ex call: it verifies round t from batch slot t % 2 and, as one
+    more workgroup of its decide launch, schedules round t+1 into slot
+    (t+1) % 2, so the schedule leaves the critical path without a second
+    stream or any event. Every launch has a fixed capacity (R (k+1) rows), so
+    a run of rounds can be captured into a HIP graph and replayed (capture()).
+    Marshalling only.
+    """
+
+    def __init__(self, d: DeviceStep, z_rounds: torch.Tensor, lag: int = 2):
+        self.d = d
+        self.z = z_rounds                     # f32 [n, R, k] on the device
+        self.n = int(z_rounds.shape[0])
+        self.lag = lag
+        w, dev = d.w, d.device
+        R, k = w.R, w.k
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.lengths = [torch.zeros(R, **i32) for _ in range(2)]
+        self.tags = [torch.zeros(R * (k + 1), 2, **i32) for _ in range(2)]
+        self.cu_rows = [torch.zeros(R + 1, **i32) for _ in range(2)]
+        self.n_rows = [torch.zeros(1, **i32) for _ in range(2)]
+        self.survival = [torch.zeros(R, k, dtype=torch.float64, device=dev) for _ in range(2)]
+        self.acc_len = [torch.zeros(R, **i32) for _ in range(2)]
+        self.out_tokens = [torch.zeros(R, k + 1, **i32) for _ in range(2)]
+        self.t = 0
+
+    def _job(self, slot: int, rnd: int):
+        d = self.d
+        return B.schedule_job(self.z[rnd % self.n], d.T, d.tbl_b, d.tbl_t, d.w.k, self.lengths[slot],
+                              self.tags[slot], self.cu_rows[slot], self.n_rows[slot], d.ws_sched,
+                              self.survival[slot])
+
+    def start(self, t0: int = 0):
+        """Schedule round t0 (from the confidences lag rounds before it); round
+        t0 is the next to verify."""
+        self.t = t0
+        d, s = self.d, t0 % 2
+        B.spec_schedule(self.z[(t0 - self.lag) % self.n], d.T, d.tbl_b, d.tbl_t, d.w.k, self.lengths[s],
+                        self.tags[s], self.cu_rows[s], self.n_rows[s], d.ws_sched, self.survival[s])
+
+    def step(self, mode, diag=False):
+        """Verify round t; schedule round t+1 in the same launches."""
+        d, t = self.d, self.t
+        s, o = t % 2, (t + 1) % 2
+        if len(d._copies) > 1:
+            d.use_copy(t)
+        if d.w.backbone is not None:
+            d.markov(mode)
+        dl, tk = d.drafts(mode)
+        B.spec_verify(mode, d.target, dl, tk, self.tags[s], self.cu_rows[s], self.n_rows[s], d.w.tau,
+                      d.u_verify, self.acc_len[s], self.out_tokens[s], d.ws_verify,
+                      row_diag=d.diag if diag else None, next_job=self._job(o, t + 1 - self.lag))
+        self.t = t + 1
+
+    def capture(self, mode, rounds: int):
+        """A HIP graph of `rounds` consecutive rounds (even, so the batch slots
+        line up on replay) starting at the current round; each round keeps its
+        own confidence round on every replay."""
+        assert rounds % 2 == 0
+        t0 = self.t
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(rounds):
+                self.step(mode)
+        self.t = t0
+        return g

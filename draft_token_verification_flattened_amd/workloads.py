@@ -266,3 +266,23 @@ def make(name: str, *, R: Optional[int] = None, V: Optional[int] = None) -> Work
     w["u_verify"] = _uniform24(g, (R_, k + 1))
     w["u_draft"] = _uniform24(g, (R_, k))
     return Workload(**w)
+
+
+def conf_rounds(w: Workload, n_rounds: int, rho: float = 0.8, sigma: float = 0.75,
+                seed: int = 99) -> np.ndarray:
+    """Confidence-head logits for n_rounds consecutive rounds of the same
+    requests, f32 [n_rounds, R, k]: round 0 is w.conf_logit, and each later
+    round adds a stationary AR(1) drift, d_t = rho d_(t-1) + sqrt(1 - rho^2)
+    sigma e_t (e standard normal, Philox keyed by the workload seed and `seed`),
+    so a schedule made from older confidences sees a different state than the
+    round it is used for."""
+    g = _stream(int(CONFIGS[w.name]["seed"]), seed, 0)
+    R, k = w.conf_logit.shape
+    out = np.empty((n_rounds, R, k), dtype=np.float32)
+    d = np.zeros((R, k), dtype=np.float64)
+    s = float(np.sqrt(1.0 - rho * rho)) * sigma
+    for t in range(n_rounds):
+        if t > 0:
+            d = rho * d + s * g.standard_normal((R, k))
+        out[t] = (w.conf_logit.astype(np.float64) + d).astype(np.float32)
+    return out

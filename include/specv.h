@@ -198,6 +198,51 @@ int spec_verify(int mode, int dtype, int R, int k, int V, const void* target_log
                 float* row_diag, void* ws, size_t ws_bytes, specv_stream stream);
 
 /* ------------------------------------------------------------------------ */
+/* spec_verify_ex: spec_verify with the next round's schedule riding along   */
+/* ------------------------------------------------------------------------ */
+/*
+ * The asynchronous lagged scheduler ([P1] section "2. 置信度调度验证": lengths
+ * for a round come from confidences of two rounds earlier, so the schedule
+ * leaves the critical path; fixed-capacity launches can be replayed as a
+ * graph). spec_verify_ex verifies this round exactly as spec_verify does and,
+ * in the same launch sequence on the same stream, computes the spec_schedule
+ * described by `next` (typically the next round's batch, from older
+ * confidences). When next->R * next->k <= 4096 and next->max_len >= 1 the
+ * schedule runs as one extra workgroup of the decide kernel, beside this
+ * round's decisions; otherwise it is launched after them on the same stream.
+ * Its results are those of spec_schedule with the same arguments, bit for bit.
+ *
+ * next: host pointer, or NULL (then spec_verify_ex is spec_verify). Its fields
+ *   are spec_schedule's arguments (device pointers as there). Its batch
+ *   (tags_out, cu_rows_out, n_rows_out) must be other buffers than this call's
+ *   tags, cu_rows and n_rows, and nothing else may use its workspace meanwhile.
+ * Errors: as spec_verify and spec_schedule (with "spec_verify_ex (next)" in the
+ *   message for the job); SPECV_EINVAL if the next batch is this one.
+ */
+typedef struct {
+    int R, k;
+    const float* conf_logit;        /* f32 [R,k] */
+    const float* pos_temp;          /* f32 [k] */
+    const int32_t* tbl_tokens;      /* i32 [n_tbl] */
+    const double* tbl_thr;          /* f64 [n_tbl] */
+    int n_tbl, max_len;
+    int32_t* len_out;               /* i32 [R] */
+    int32_t* tags_out;              /* i32 [R*(k+1),2] */
+    int32_t* cu_rows_out;           /* i32 [R+1] */
+    int32_t* n_rows_out;            /* i32 [1] */
+    double* survival_out;           /* f64 [R,k] or NULL */
+    void* ws;                       /* spec_schedule_workspace_bytes(R, k) bytes */
+    size_t ws_bytes;
+} specv_schedule_job;
+
+int spec_verify_ex(int mode, int dtype, int R, int k, int V, const void* target_logits,
+                   const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
+                   const int32_t* cu_rows, const int32_t* n_rows, float temperature,
+                   const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
+                   float* row_diag, void* ws, size_t ws_bytes, const specv_schedule_job* next,
+                   specv_stream stream);
+
+/* ------------------------------------------------------------------------ */
 /* markov_draft                                                              */
 /* ------------------------------------------------------------------------ */
 /*

@@ -114,3 +114,16 @@ def test_flatten_and_markov_reject():
 def test_timing_read_empty():
     B.timing_reset()
     assert B.timing_read("verify") == (0, 0.0)
+
+
+def test_verify_ex_rejects_job_writing_this_batch():
+    lib = B.lib()
+    job = B.ScheduleJob(4, 5, FAKE, FAKE, FAKE, FAKE, 4, 5, FAKE, FAKE + 256, FAKE + 512, FAKE + 768, None, FAKE,
+                        1 << 20)
+    args = (B.SAMPLE, B.BF16, 4, 5, 1024, FAKE, FAKE, FAKE, FAKE + 256, FAKE + 4096, FAKE + 8192,
+            ctypes.c_float(1.0), FAKE, FAKE, FAKE, None, FAKE, 1 << 30)
+    assert lib.spec_verify_ex(*args, ctypes.byref(job), None) == B.EINVAL
+    assert "other than this one" in B.last_error()
+    bad = B.ScheduleJob(4, 0, FAKE, FAKE, FAKE, FAKE, 4, 5, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20)
+    assert lib.spec_verify_ex(*args, ctypes.byref(bad), None) == B.EINVAL
+    assert "spec_verify_ex (next)" in B.last_error()
