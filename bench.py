@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--variants", action="store_true",
                     help="also time greedy and verify-all variants of the workload")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the load sweep over R = 1..512 and print its table as one JSON line")
     ap.add_argument("--lagged", action="store_true",
                     help="also time the lagged schedule (two streams, HIP graph) on rotating confidence rounds")
     ap.add_argument("--copies", type=int, default=3,
@@ -237,6 +239,66 @@ def run_lagged(d, w, mode_c, steps, warmup, B, torch, copies):
     )
 
 
+def run_sweep(args, B, torch):
+    """Load sweep: for R = 1, 2, 4, ..., 512 requests of the c2 recipe (the
+    first R requests of one R = 512 draw, so every R sees the same requests),
+    8 rounds of drifting confidences, each a synchronous schedule-then-verify.
+    Per R: mean verified length per request, mean step time, verified draft
+    tokens/s and expected emitted tokens/s (R + survival over the verified
+    drafts, per unit measured step time)."""
+    import dataclasses
+    import numpy as np
+    from draft_token_verification_flattened_amd import workloads
+    from draft_token_verification_flattened_amd.pipeline import DeviceStep, to_device
+    full = workloads.make("c2", R=512)
+    rounds = 8
+    rows = []
+    for R in [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]:
+        cut = lambda a: None if a is None else np.ascontiguousarray(a[:R])  # noqa: E731
+        w = dataclasses.replace(full, R=R, conf_logit=cut(full.conf_logit), target=cut(full.target),
+                                draft=cut(full.draft), tokens_sample=cut(full.tokens_sample),
+                                tokens_greedy=cut(full.tokens_greedy), u_verify=cut(full.u_verify))
+        d = DeviceStep(w)
+        z = to_device(workloads.conf_rounds(w, rounds), "cuda")
+        k = w.k
+        Ls, Ss = [], []
+        for t in range(rounds):                               # lengths and survival per round
+            B.spec_schedule(z[t], d.T, d.tbl_b, d.tbl_t, k, d.lengths, d.tags, d.cu_rows, d.n_rows, d.ws_sched,
+                            d.survival)
+            torch.cuda.synchronize()
+            Ls.append(d.host("lengths").copy())
+            Ss.append(d.host("survival").copy())
+
+        def step(t):
+            B.spec_schedule(z[t % rounds], d.T, d.tbl_b, d.tbl_t, k, d.lengths, d.tags, d.cu_rows, d.n_rows,
+                            d.ws_sched, d.survival)
+            d.verify(B.SAMPLE, diag=False)
+        for t in range(args.warmup):
+            step(t)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        n = max(rounds, args.steps // rounds * rounds)
+        e0.record()
+        for t in range(n):
+            step(t)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        meanL = float(np.mean([L.mean() for L in Ls]))
+        N = float(np.mean([L.sum() for L in Ls]))
+        emitted = float(np.mean([R + float((S * (np.arange(k)[None, :] < L[:, None])).sum())
+                                 for L, S in zip(Ls, Ss)]))
+        rows.append(dict(R=R, mean_verify_len=meanL, verified_per_step=N, us_per_step=ms * 1e3,
+                         verified_tokens_per_s=N / (ms * 1e-3), expected_emitted_per_step=emitted,
+                         goodput=emitted / (ms * 1e-3)))
+        print(json.dumps(dict(sweep_row=rows[-1])), file=sys.stderr, flush=True)
+        del d, z
+        torch.cuda.empty_cache()
+    print(json.dumps(dict(sweep="c2 recipe, first R of 512 requests, 8 drifting confidence rounds, sampling",
+                          rows=rows)))
+
+
 def cpu_baseline(w, mode, max_len, min_seconds=10.0):
     """The oracle, as it stands, on the same workload: whole steps repeated until
     at least `min_seconds` of CPU time have passed."""
@@ -312,6 +374,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     B.lib()   # fail loudly if the HIP library is missing
+    if args.sweep:
+        run_sweep(args, B, torch)
+        return
     w = workloads.make(args.config)
     max_len = w.k if args.max_len == "k" else int(args.max_len)
     d = DeviceStep(w, copies=args.copies)
