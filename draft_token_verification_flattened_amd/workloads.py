@@ -286,3 +286,53 @@ def conf_rounds(w: Workload, n_rounds: int, rho: float = 0.8, sigma: float = 0.7
             d = rho * d + s * g.standard_normal((R, k))
         out[t] = (w.conf_logit.astype(np.float64) + d).astype(np.float32)
     return out
+
+
+@dataclasses.dataclass
+class AttnInputs:
+    """Inputs of the tag-masked attention over a flattened batch."""
+    R: int
+    k: int
+    Hq: int
+    Hkv: int
+    D: int
+    page_size: int
+    lengths: np.ndarray             # i32 [R]   verified drafts per request (the batch to flatten)
+    ctx_len: np.ndarray             # i32 [R]   cached positions before the block
+    q: np.ndarray                   # bf16 bits [R*(k+1), Hq, D]   one query per flattened row
+    k_cache: np.ndarray             # bf16 bits [pages, page_size, Hkv, D]
+    v_cache: np.ndarray             # bf16 bits [pages, page_size, Hkv, D]
+    page_table: np.ndarray          # i32 [R, max_pages]
+
+
+def make_attention(R: int, k: int, *, Hq: int = 32, Hkv: int = 8, D: int = 128, page_size: int = 64,
+                   ctx_range=(1024, 3072), lengths: Optional[np.ndarray] = None, seed: int = 11) -> AttnInputs:
+    """Synthetic attention inputs: N(0, 1) queries, keys and values in bf16;
+    context lengths uniform in ctx_range; each request's pages drawn without
+    replacement from a shuffled pool with room for ctx + k + 1 positions; per
+    request verified lengths uniform in 0 .. k unless given."""
+    g = np.random.Generator(np.random.Philox(key=(int(seed) << 64) | 0xA77))
+    if lengths is None:
+        lengths = g.integers(0, k + 1, size=R).astype(np.int32)
+    ctx = g.integers(ctx_range[0], ctx_range[1] + 1, size=R).astype(np.int32)
+    need = (ctx.astype(np.int64) + k + 1 + page_size - 1) // page_size
+    max_pages = int(need.max())
+    n_pages = int(need.sum())
+    perm = g.permutation(n_pages).astype(np.int32)
+    table = np.zeros((R, max_pages), dtype=np.int32)
+    o = 0
+    for r in range(R):
+        table[r, :need[r]] = perm[o:o + need[r]]
+        o += int(need[r])
+    q = f32_to_bf16_bits(g.standard_normal((R * (k + 1), Hq, D), dtype=np.float32))
+
+    def pool(array_id):
+        out = np.empty((n_pages, page_size, Hkv, D), dtype=np.uint16)
+
+        def fill(b, lo, hi):
+            gg = _stream(seed, array_id, b)
+            out[lo:hi] = f32_to_bf16_bits(gg.standard_normal((hi - lo, page_size, Hkv, D), dtype=np.float32))
+        _parallel_blocks(n_pages, fill)
+        return out
+    return AttnInputs(R=R, k=k, Hq=Hq, Hkv=Hkv, D=D, page_size=page_size, lengths=lengths, ctx_len=ctx,
+                      q=q, k_cache=pool(40), v_cache=pool(41), page_table=table)
