@@ -51,6 +51,9 @@ def parse():
                     help="only run the load sweep over R = 1..512 and print its table as one JSON line")
     ap.add_argument("--lagged", action="store_true",
                     help="also time the lagged schedule (two streams, HIP graph) on rotating confidence rounds")
+    ap.add_argument("--attention", action="store_true",
+                    help="time spec_attention (tag-masked flattened attention over a paged KV cache) instead")
+    ap.add_argument("--split-keys", type=int, default=0, help="spec_attention keys per work item (0: automatic)")
     ap.add_argument("--copies", type=int, default=3,
                     help="input copies rotated over the steps (no step reads logits cached by the previous one)")
     ap.add_argument("--copy-probe", type=float, default=0.0,
@@ -299,6 +302,70 @@ def run_sweep(args, B, torch):
                           rows=rows)))
 
 
+def run_attention(args, B, torch):
+    """spec_attention at R = 256, k = 5 with Qwen3-4B-like heads (32 query heads
+    over 8 KV heads, D = 128), 64-key pages drawn from a shuffled pool, contexts
+    uniform in 1024..3072, verified lengths uniform in 0..5, flattened by
+    spec_flatten. Algorithmic bytes per call: every request's K and V over its
+    visible positions (ctx + L + 1 per KV head), the queries and the output."""
+    import numpy as np
+    from draft_token_verification_flattened_amd import workloads
+    from draft_token_verification_flattened_amd.pipeline import to_device
+    ai = workloads.make_attention(256, 5, seed=11)
+    dev = "cuda"
+    R, k = ai.R, ai.k
+    q, kc, vc = (to_device(x, dev) for x in (ai.q, ai.k_cache, ai.v_cache))
+    pt, ctx = to_device(ai.page_table, dev), to_device(ai.ctx_len, dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    tags = torch.zeros(R * (k + 1), 2, **i32)
+    cu = torch.zeros(R + 1, **i32)
+    nr = torch.zeros(1, **i32)
+    B.spec_flatten(to_device(ai.lengths, dev), k, tags, cu, nr)
+    out = torch.zeros(R * (k + 1), ai.Hq, ai.D, dtype=torch.float32, device=dev)
+    ws = B.workspace(B.attention_workspace_bytes(R, k, ai.Hq, ai.Hkv, ai.page_size, ai.page_table.shape[1],
+                                                 args.split_keys), dev)
+
+    def call():
+        B.spec_attention(k, ai.page_size, q, kc, vc, pt, ctx, tags, cu, nr, out, ws, split_keys=args.split_keys)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    B.timing_reset()
+    B.timing_enable(True)
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    B.timing_enable(False)
+    kern = {}
+    for name in ("attn_partial", "attn_combine"):
+        n, tot = B.timing_read(name)
+        if n:
+            kern[name] = dict(launches_per_call=n / args.steps, avg_us=1000.0 * tot / n)
+    B.timing_reset()
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    assert B.read_status(ws) == 0
+    L = ai.lengths.astype(np.int64)
+    rows = int(L.sum()) + R
+    kv = int(2 * ai.Hkv * ai.D * 2 * (ai.ctx_len.astype(np.int64) + L + 1).sum())
+    qo = rows * ai.Hq * ai.D * (2 + 4)
+    nbytes = kv + qo
+    part = kern["attn_partial"]["avg_us"]
+    print(json.dumps(dict(attention=dict(
+        workload="R=256, k=5, Hq=32, Hkv=8, D=128, page 64, ctx 1024..3072, L uniform 0..5",
+        rows=rows, us_per_call=us, rows_per_s=rows / (us * 1e-6), algorithmic_bytes=nbytes,
+        kv_bytes=kv, call_gbps=nbytes / (us * 1e-6) / 1e9,
+        roofline=dict(bound="hbm", kernel="attn_partial", achieved=nbytes / (part * 1e-6) / 1e9,
+                      peak=HBM_PEAK / 1e9, unit="GB/s", frac=nbytes / (part * 1e-6) / HBM_PEAK,
+                      avg_launch_us=part),
+        split_keys=args.split_keys, kernels=kern))))
+
+
 def cpu_baseline(w, mode, max_len, min_seconds=10.0):
     """The oracle, as it stands, on the same workload: whole steps repeated until
     at least `min_seconds` of CPU time have passed."""
@@ -376,6 +443,9 @@ def main():
     B.lib()   # fail loudly if the HIP library is missing
     if args.sweep:
         run_sweep(args, B, torch)
+        return
+    if args.attention:
+        run_attention(args, B, torch)
         return
     w = workloads.make(args.config)
     max_len = w.k if args.max_len == "k" else int(args.max_len)

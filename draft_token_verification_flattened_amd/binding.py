@@ -22,7 +22,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "specv.h")
 OK, EINVAL, EUNSUPPORTED, EDEVICE = 0, -1, -2, -3
 BF16, F32 = 0, 1
 GREEDY, SAMPLE = 0, 1
-STATUS_BAD_TOKEN, STATUS_BAD_TAG = 1, 2
+STATUS_BAD_TOKEN, STATUS_BAD_TAG, STATUS_BAD_PAGE = 1, 2, 4
 MAX_K, MAX_SCHED_ITEMS = 32, 16384
 
 _c_int, _c_size, _c_ptr = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
@@ -50,6 +50,8 @@ _SIGS = {
     "markov_draft_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "markov_draft": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
                               _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+    "spec_attention_workspace_bytes": (_c_size, [_c_int] * 7),
+    "spec_attention": (_c_int, [_c_int] * 9 + [_c_ptr] * 9 + [_c_ptr, _c_size, _c_ptr]),
     "specv_last_error": (ctypes.c_char_p, []),
     "specv_read_status": (_c_int, [_c_ptr, _c_ptr, ctypes.POINTER(ctypes.c_uint32)]),
     "specv_timing_enable": (_c_int, [_c_int]),
@@ -243,6 +245,37 @@ def markov_draft(mode, backbone, emb, proj, prev_token, temperature, uniforms, t
     _check(lib().markov_draft(int(mode), dt, R, k, V, d_m, _ptr(backbone), _ptr(emb), _ptr(proj),
                               _ptr(prev_token), float(temperature), _ptr(uniforms) if mode == SAMPLE else None,
                               _ptr(tokens_out), _ptr(logits_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def attention_workspace_bytes(R: int, k: int, Hq: int, Hkv: int, page_size: int, max_pages: int,
+                              split_keys: int = 0) -> int:
+    return int(lib().spec_attention_workspace_bytes(R, k, Hq, Hkv, page_size, max_pages, split_keys))
+
+
+def spec_attention(k, page_size, q, k_cache, v_cache, page_table, ctx_len, tags, cu_rows, n_rows, out, ws,
+                   split_keys=0, stream=None):
+    """q [R*(k+1), Hq, D] bf16; caches [pages, page_size, Hkv, D] bf16; page_table i32 [R, max_pages];
+    out f32 [R*(k+1), Hq, D]."""
+    R, max_pages = page_table.shape
+    rows, Hq, D = q.shape
+    num_pages, ps, Hkv, Dk = k_cache.shape
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    if rows != R * (k + 1) or ps != page_size or Dk != D:
+        raise ValueError("spec_attention: q, caches and page_table disagree on R, k, page_size or D")
+    _dev(q, "q", bf)
+    _dev(k_cache, "k_cache", bf)
+    _dev(v_cache, "v_cache", bf, tuple(k_cache.shape))
+    _dev(page_table, "page_table", (torch.int32,))
+    _dev(ctx_len, "ctx_len", (torch.int32,), (R,))
+    _dev(tags, "tags", (torch.int32,), (R * (k + 1), 2))
+    _dev(cu_rows, "cu_rows", (torch.int32,), (R + 1,))
+    _dev(n_rows, "n_rows", (torch.int32,), (1,))
+    _dev(out, "out", (torch.float32,), (rows, Hq, D))
+    _dev(ws, "ws", (torch.uint8,))
+    _check(lib().spec_attention(R, int(k), Hq, Hkv, D, int(page_size), num_pages, max_pages, int(split_keys),
+                                _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(ctx_len),
+                                _ptr(tags), _ptr(cu_rows), _ptr(n_rows), _ptr(out), _ptr(ws), ws.numel(),
+                                _stream(stream)))
 
 
 def read_status(ws, stream=None) -> int:

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libspecv.so")
 
-SOURCES = ["abi.cpp", "schedule.hip", "verify.hip", "markov.hip"]
+SOURCES = ["abi.cpp", "schedule.hip", "verify.hip", "markov.hip", "attention.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -55,7 +55,9 @@ enum { SPECV_GREEDY = 0, SPECV_SAMPLE = 1 };  /* acceptance mode */
 /* status-word bits (specv_read_status) */
 enum {
     SPECV_STATUS_BAD_TOKEN = 1u, /* a draft token outside [0, V) */
-    SPECV_STATUS_BAD_TAG = 2u    /* tags[] disagrees with cu_rows[] */
+    SPECV_STATUS_BAD_TAG = 2u,   /* tags[] disagrees with cu_rows[] */
+    SPECV_STATUS_BAD_PAGE = 4u   /* spec_attention: a page id outside [0, num_pages), or a
+                                    context length that is negative or overruns its page-table row */
 };
 
 /* Limits of the scheduler: all candidate keys of one call are held in the
@@ -279,14 +281,70 @@ int markov_draft(int mode, int dtype, int R, int k, int V, int d_m,
                  specv_stream stream);
 
 /* ------------------------------------------------------------------------ */
+/* spec_attention                                                            */
+/* ------------------------------------------------------------------------ */
+/*
+ * Attention of the flattened verification batch over a paged KV cache, masked
+ * by the tag tensor. [P1], engineering table, row "内核利用率暴跌": padded
+ * kernels lose their utilisation on dynamic, variable-length verification, so
+ * each token is flattened into an independent element and the sequence
+ * dependencies travel in a tag tensor (physically decoupled sparse attention).
+ *
+ * For every flattened row t < n_rows with tag (r, j) and every query head h:
+ *   out[t,h,:] = sum_p w_p V_r[p, h/G, :],  w = softmax_p(q[t,h,:] . K_r[p, h/G, :] / sqrt(D)),
+ * over request r's positions p = 0 .. ctx_len[r] + j (G = H_q / H_kv: grouped-
+ * query attention). Position p of request r is slot p % page_size of page
+ * page_table[r, p / page_size]. The verified tokens' own keys and values are
+ * expected in the cache already (positions ctx_len[r] .. ctx_len[r] + L_r).
+ * Arithmetic: scores and sums in float32 from exact bf16 products; the
+ * softmax weights enter the weighted sum of values rounded to bf16.
+ *
+ * Arguments (device pointers unless noted)
+ *   R, k            host ints: R >= 1, 1 <= k <= 32; the flattened batch has
+ *                   R*(k+1) row slots in the spec_flatten layout
+ *   Hq, Hkv, D      host ints: H_kv divides H_q; D == 128
+ *   page_size       host int, a multiple of 32
+ *   num_pages       host int: pages in each cache pool
+ *   max_pages       host int: columns of page_table; ctx_len[r] + k + 1 must
+ *                   fit in max_pages * page_size
+ *   split_keys      host int: keys per work item (a multiple of 32), or 0 to
+ *                   let the library choose; a tuning knob, results depend on
+ *                   it only through the float32 summation order
+ *   q               bf16 [R*(k+1), Hq, D] queries of the flattened rows
+ *   k_cache, v_cache bf16 [num_pages, page_size, Hkv, D]
+ *   page_table      i32 [R, max_pages];  ctx_len i32 [R] (>= 0)
+ *   tags, cu_rows, n_rows  as written by spec_schedule / spec_flatten
+ *   out             f32 [R*(k+1), Hq, D]; rows >= n_rows are not written
+ *   ws, ws_bytes    at least spec_attention_workspace_bytes(...) bytes with the
+ *                   same R, k, Hq, Hkv, page_size, max_pages, split_keys;
+ *                   256-byte aligned; no initialisation needed
+ *   q, caches, out  16-byte aligned
+ * Data errors (status word): a row whose tag disagrees with cu_rows is
+ * written as zeros (SPECV_STATUS_BAD_TAG; when cu_rows itself is inconsistent
+ * the request's rows are not written); a page id outside [0, num_pages) or a
+ * context length that is negative or overruns the page-table row makes the
+ * request's rows zeros (SPECV_STATUS_BAD_PAGE). No read leaves the pools.
+ * Errors: SPECV_EINVAL for bad sizes, NULL or misaligned pointers or a short
+ * workspace; SPECV_EUNSUPPORTED for D != 128, page sizes that are not a
+ * multiple of 32, or sizes beyond 32-bit grid and index ranges.
+ */
+size_t spec_attention_workspace_bytes(int R, int k, int Hq, int Hkv, int page_size, int max_pages,
+                                      int split_keys);
+int spec_attention(int R, int k, int Hq, int Hkv, int D, int page_size, int num_pages, int max_pages,
+                   int split_keys, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* page_table, const int32_t* ctx_len, const int32_t* tags,
+                   const int32_t* cu_rows, const int32_t* n_rows, float* out, void* ws, size_t ws_bytes,
+                   specv_stream stream);
+
+/* ------------------------------------------------------------------------ */
 /* diagnostics                                                               */
 /* ------------------------------------------------------------------------ */
 
 /* Message of the last failed call on this host thread ("" if none). */
 const char* specv_last_error(void);
 
-/* Read the workspace status word of the last spec_verify / markov_draft call
- * that used `ws` (synchronises `stream`). */
+/* Read the workspace status word of the last spec_verify / markov_draft /
+ * spec_attention call that used `ws` (synchronises `stream`). */
 int specv_read_status(const void* ws, specv_stream stream, uint32_t* status_out);
 
 /* Per-kernel timing with HIP events recorded on the launch stream around each

@@ -127,3 +127,41 @@ def test_verify_ex_rejects_job_writing_this_batch():
     bad = B.ScheduleJob(4, 0, FAKE, FAKE, FAKE, FAKE, 4, 5, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20)
     assert lib.spec_verify_ex(*args, ctypes.byref(bad), None) == B.EINVAL
     assert "spec_verify_ex (next)" in B.last_error()
+
+
+def _attention(**kw):
+    a = dict(R=4, k=5, Hq=32, Hkv=8, D=128, ps=64, pages=100, maxp=50, split=0, q=FAKE, kc=FAKE, vc=FAKE,
+             pt=FAKE, ctx=FAKE, tags=FAKE, cu=FAKE, nr=FAKE, out=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return B.lib().spec_attention(a["R"], a["k"], a["Hq"], a["Hkv"], a["D"], a["ps"], a["pages"], a["maxp"],
+                                  a["split"], a["q"], a["kc"], a["vc"], a["pt"], a["ctx"], a["tags"], a["cu"],
+                                  a["nr"], a["out"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(R=0), B.EINVAL, "R >= 1"),
+    (dict(k=33), B.EINVAL, "k <="),
+    (dict(Hq=12), B.EINVAL, "dividing"),
+    (dict(Hkv=0), B.EINVAL, "H_kv >= 1"),
+    (dict(pages=0), B.EINVAL, "num_pages"),
+    (dict(D=64), B.EUNSUPPORTED, "head dimension"),
+    (dict(ps=48), B.EUNSUPPORTED, "page size"),
+    (dict(split=40), B.EINVAL, "split_keys"),
+    (dict(ps=32, maxp=0), B.EINVAL, "max_pages"),
+    (dict(k=32, ps=32, maxp=1), B.EINVAL, "cannot hold"),
+    (dict(vc=None), B.EINVAL, "NULL"),
+    (dict(q=FAKE + 8), B.EINVAL, "16-byte"),
+    (dict(ws=FAKE + 16), B.EINVAL, "256-byte"),
+])
+def test_attention_rejects(kw, code, msg):
+    assert _attention(**kw) == code
+    assert msg in B.last_error()
+
+
+def test_attention_workspace_sizes():
+    a = B.attention_workspace_bytes(256, 5, 32, 8, 64, 49)
+    b = B.attention_workspace_bytes(256, 5, 32, 8, 64, 49, 64)
+    assert 0 < a and 0 < b and a % 256 == 0 and b % 256 == 0
+    assert b >= a                           # shorter splits: more partial records
+    assert B.attention_workspace_bytes(256, 5, 32, 8, 48, 49) == 0
+    assert B.attention_workspace_bytes(256, 5, 30, 8, 64, 49) == 0
