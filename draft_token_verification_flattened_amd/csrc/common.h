@@ -20,6 +20,15 @@ struct WsHeader {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// A pointer into device global memory, for loads through pointers the compiler
+// cannot trace to a kernel argument (read from LDS, say): without it they become
+// flat loads, which also count in lgkmcnt, so every later LDS wait would wait for
+// them as well.
+template <typename U>
+__device__ __forceinline__ const __attribute__((address_space(1))) U* as_global(const U* p) {
+    return (const __attribute__((address_space(1))) U*)(p);
+}
+
 // Storage traits: 16-byte vector of logits, widened to float.
 template <int DT> struct Logit;
 
@@ -27,7 +36,7 @@ template <> struct Logit<SPECV_BF16> {
     using T = uint16_t;
     static constexpr int kVec = 8;                 // elements per 16-byte load
     __device__ static __forceinline__ float load1(const T* p) {
-        return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+        return __uint_as_float(static_cast<uint32_t>(*as_global(p)) << 16);
     }
     __device__ static __forceinline__ void unpack(const uint4& v, float (&x)[8]) {
         x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
@@ -40,7 +49,7 @@ template <> struct Logit<SPECV_BF16> {
 template <> struct Logit<SPECV_F32> {
     using T = float;
     static constexpr int kVec = 4;
-    __device__ static __forceinline__ float load1(const T* p) { return *p; }
+    __device__ static __forceinline__ float load1(const T* p) { return *as_global(p); }
     __device__ static __forceinline__ void unpack(const uint4& v, float (&x)[4]) {
         x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
         x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);

@@ -117,23 +117,27 @@ struct Raw {
     }
 
     // Load the chunk starting at element `beg`; `full` = the whole chunk lies
-    // inside the row (else the elements past V are not read).
+    // inside the row (else the elements past V are read from the row's last
+    // position and masked by widen). Every call issues the same loads whatever
+    // the arguments, so the compiler's load counting stays exact across the
+    // streaming loop's branches (a path with fewer loads makes it wait for all).
     __device__ __forceinline__ void load(const T* row, int beg, int V, int lane, bool full) {
         if constexpr (VEC) {
-            const uint4* vr = reinterpret_cast<const uint4*>(row) + beg / kVec + lane;
-            if (full) {
+            using U4 = unsigned int __attribute__((ext_vector_type(4)));
+            const auto* vr = as_global(reinterpret_cast<const U4*>(row));
+            const int first = beg / kVec + lane, last = V / kVec - 1;
+            (void)full;
 #pragma unroll
-                for (int u = 0; u < kNV; ++u) v[u] = vr[u * kWave];
-            } else {
-                const int nv = V / kVec - beg / kVec - lane;
-#pragma unroll
-                for (int u = 0; u < kNV; ++u) v[u] = u * kWave < nv ? vr[u * kWave] : make_uint4(0u, 0u, 0u, 0u);
+            for (int u = 0; u < kNV; ++u) {
+                const U4 t = vr[min(first + u * kWave, last)];
+                v[u] = make_uint4(t.x, t.y, t.z, t.w);
             }
         } else {
 #pragma unroll
             for (int q = 0; q < kE; ++q) {
                 const int e = beg + offset(q, lane);
-                s[q] = e < V ? LT::load1(row + e) : -INFINITY;
+                const float t = LT::load1(row + min(e, V - 1));
+                s[q] = e < V ? t : -INFINITY;
             }
         }
     }
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
     __shared__ uint64_t d_row[kPhaseSlots];
     __shared__ int d_t[kPhaseSlots];                 // flattened row
     __shared__ int d_cf[kPhaseSlots];                // chunk << 2 | draft << 1 | ok
-    __shared__ int d_tok[kPhaseSlots];               // index of the row's draft token, or -1
+    __shared__ int d_tok[kPhaseSlots];               // the row's draft token (sampling, verified rows), or -1
     __shared__ float2 st_p[kPhaseSlots];             // the items' partials, written out after the phase
     __shared__ float st_x[kPhaseSlots];              // logit at the draft token, if the item holds it
     __shared__ unsigned char st_f[kPhaseSlots];
@@ -241,26 +245,44 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
     const uint32_t slots = SAMPLE ? 2 * region : region;
     if (b >= slots) return;
     const uint32_t mine = (slots - 1 - b) / G + 1;                   // slots b + i G, i < mine
-    const int nrows = min(max(*a.n_rows, 0), a.Bmax);
-    const int nver = min(max(a.cu_rows[a.R], 0), nrows);
     const float c = a.c;
 
     for (uint32_t p0 = 0; p0 < mine; p0 += kPhaseSlots) {
         const uint32_t np = min(uint32_t(kPhaseSlots), mine - p0);
-        // 1. describe this phase's slots; thread tid owns slots 2 tid and 2 tid + 1
-        uint64_t rp[2] = {0ull, 0ull};
+        // 1. describe this phase's slots; thread tid owns slots 2 tid and 2 tid + 1.
+        //    Both tag loads are unconditional (a past-the-end slot reads the phase's last
+        //    one), so they are in flight together with n_rows: one memory round trip
+        //    before the scan instead of a chain of three.
+        uint32_t sl[2];
+        int2 tg[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t i = min(2u * uint32_t(tid) + uint32_t(h), np - 1);
+            sl[h] = b + (p0 + i) * G;
+            const uint32_t rel = sl[h] >= region ? sl[h] - region : sl[h];
+            const int t = int(rel / uint32_t(C));                       // t < Bmax
+            tg[h] = make_int2(a.tags[2 * t], a.tags[2 * t + 1]);
+        }
+        // all six values at one point: the loads are issued ahead of it and waited for once
+        // (otherwise the compiler waits for n_rows first and sinks each tag load into its branch)
+        int nr = *a.n_rows, nv = a.cu_rows[a.R];
+        asm volatile("" : "+v"(nr), "+v"(nv) : "v"(tg[0].x), "v"(tg[0].y), "v"(tg[1].x), "v"(tg[1].y));
+        const int nrows = min(max(nr, 0), a.Bmax);
+        const int nver = min(max(nv, 0), nrows);
+        // items with a bad tag keep the first target row as a (harmless) load address
+        const uint64_t row0 = reinterpret_cast<uint64_t>(a.target);
+        uint64_t rp[2] = {row0, row0};
         int tt[2] = {0, 0}, cf[2] = {0, 0}, tk[2] = {-1, -1}, lv[2] = {0, 0};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t i = 2u * uint32_t(tid) + uint32_t(h);
-            if (i >= np) continue;
-            const uint32_t slot = b + (p0 + i) * G;
+            const uint32_t slot = sl[h];
             const int tensor = slot >= region ? 1 : 0;
             const uint32_t rel = tensor ? slot - region : slot;
             const int t = int(rel / uint32_t(C));
             const int ch = int(rel - uint32_t(t) * uint32_t(C));
-            const int r = a.tags[2 * t], j = a.tags[2 * t + 1];      // t < Bmax: loaded with n_rows
-            if (t >= (tensor ? nver : nrows)) continue;
+            const int r = tg[h].x, j = tg[h].y;
+            if (i >= np || t >= (tensor ? nver : nrows)) continue;
             const bool ok = r >= 0 && r < a.R && j >= 0 && j <= K && (tensor == 0 || j < K);
             lv[h] = 1;
             tt[h] = t;
@@ -272,6 +294,11 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
                 if (SAMPLE && t < nver && j < K) tk[h] = r * K + j;
             }
         }
+        // the draft tokens, loaded while the scan runs (no small loads in the streaming
+        // loop: a reused load destination there makes the compiler drain every load)
+        int tv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) tv[h] = tk[h] >= 0 ? a.tokens[tk[h]] : -1;
         int nl;
         const int pos = block_exclusive_scan_i32(lv[0] + lv[1], sh, nl);
 #pragma unroll
@@ -280,7 +307,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
             d_row[q] = rp[h];
             d_t[q] = tt[h];
             d_cf[q] = cf[h];
-            d_tok[q] = tk[h];
+            d_tok[q] = tv[h];
             st_f[q] = 0;
             ++q;
         }
@@ -304,13 +331,9 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
                 (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(rw >> 32)))) << 32) |
                 uint32_t(__builtin_amdgcn_readfirstlane(int(rw))));
             m.cf = __builtin_amdgcn_readfirstlane(d_cf[i]);
-            const int tok = __builtin_amdgcn_readfirstlane(d_tok[i]);
-            m.x = -1;
-            if (m.cf & 1) {
-                const int beg = (m.cf >> 2) * CH;
-                buf.load(m.row, beg, V, lane, beg + CH <= V);
-                if (SAMPLE && tok >= 0) m.x = a.tokens[tok];
-            }
+            m.x = __builtin_amdgcn_readfirstlane(d_tok[i]);
+            const int beg = (m.cf >> 2) * CH;
+            buf.load(m.row, beg, V, lane, beg + CH <= V);    // also for a bad tag: same loads on every path
         };
         auto process = [&](const RW& buf, const Cur& m) {
             const int beg = (m.cf >> 2) * CH;
@@ -336,18 +359,30 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
             }
             if (lane == 0) st_p[m.i] = P;
         };
+        // Two items per wavefront: the next one's loads are issued before the current
+        // one is reduced. The last item is handled on its own exit path, so that in
+        // the loop every issue is unconditional.
         RW q0, q1;
         Cur m0, m1;
         int i0 = grab();
-        if (i0 < nl) issue(q0, m0, i0);
-        while (i0 < nl) {
-            const int i1 = grab();
-            if (i1 < nl) issue(q1, m1, i1);
-            process(q0, m0);
-            if (i1 >= nl) break;
-            i0 = grab();
-            if (i0 < nl) issue(q0, m0, i0);
-            process(q1, m1);
+        if (i0 < nl) {
+            issue(q0, m0, i0);
+            while (true) {
+                const int i1 = grab();
+                if (i1 >= nl) {
+                    process(q0, m0);
+                    break;
+                }
+                issue(q1, m1, i1);
+                process(q0, m0);
+                i0 = grab();
+                if (i0 >= nl) {
+                    process(q1, m1);
+                    break;
+                }
+                issue(q0, m0, i0);
+                process(q1, m1);
+            }
         }
         __syncthreads();
 
