@@ -207,8 +207,13 @@ __device__ __forceinline__ float wave_incl_scan_f32(float v) {
 
 // Block-wide exclusive scan of one int per thread (DPP within each wave, wave
 // totals through LDS); returns the block total too. Totals stay below 2^31.
-__device__ __forceinline__ int block_exclusive_scan_i32(int v, int* sh, int& total) {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+// nw: wavefronts in the workgroup (0: from blockDim). A source built with
+// -mno-amdgpu-ieee cannot inline the device-library function behind blockDim, and
+// that call waits for every outstanding memory operation, so callers with loads
+// in flight pass nw.
+__device__ __forceinline__ int block_exclusive_scan_i32(int v, int* sh, int& total, int nw = 0) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (nw == 0) nw = blockDim.x >> 6;
     const int incl = wave_incl_scan_i32(v);
     if (lane == 63) sh[w] = incl;
     __syncthreads();

@@ -249,33 +249,38 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
 
     for (uint32_t p0 = 0; p0 < mine; p0 += kPhaseSlots) {
         const uint32_t np = min(uint32_t(kPhaseSlots), mine - p0);
-        // 1. describe this phase's slots; thread tid owns slots 2 tid and 2 tid + 1.
-        //    Both tag loads are unconditional (a past-the-end slot reads the phase's last
-        //    one), so they are in flight together with n_rows: one memory round trip
-        //    before the scan instead of a chain of three.
-        uint32_t sl[2];
-        int2 tg[2];
+        // 1. describe this phase's slots; thread tid owns slots 2 tid and 2 tid + 1, and
+        //    every thread of wavefront w also describes slot w: the first kWaves slots
+        //    are the wavefronts' first items, taken before the scan and kept out of the
+        //    shared list. All tag loads are unconditional (a past-the-end slot reads the
+        //    phase's last one), so they are in flight together with n_rows: one memory
+        //    round trip before the scan instead of a chain of three.
+        constexpr int kWaves = kStreamThreads / kWave;
+        const int wv = tid >> 6;
+        uint32_t sl[3];
+        int2 tg[3];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t i = min(2u * uint32_t(tid) + uint32_t(h), np - 1);
+        for (int h = 0; h < 3; ++h) {
+            const uint32_t i = min(h < 2 ? 2u * uint32_t(tid) + uint32_t(h) : uint32_t(wv), np - 1);
             sl[h] = b + (p0 + i) * G;
             const uint32_t rel = sl[h] >= region ? sl[h] - region : sl[h];
             const int t = int(rel / uint32_t(C));                       // t < Bmax
             tg[h] = make_int2(a.tags[2 * t], a.tags[2 * t + 1]);
         }
-        // all six values at one point: the loads are issued ahead of it and waited for once
+        // all values at one point: the loads are issued ahead of it and waited for once
         // (otherwise the compiler waits for n_rows first and sinks each tag load into its branch)
         int nr = *a.n_rows, nv = a.cu_rows[a.R];
-        asm volatile("" : "+v"(nr), "+v"(nv) : "v"(tg[0].x), "v"(tg[0].y), "v"(tg[1].x), "v"(tg[1].y));
+        asm volatile("" : "+v"(nr), "+v"(nv) : "v"(tg[0].x), "v"(tg[0].y), "v"(tg[1].x), "v"(tg[1].y),
+                     "v"(tg[2].x), "v"(tg[2].y));
         const int nrows = min(max(nr, 0), a.Bmax);
         const int nver = min(max(nv, 0), nrows);
         // items with a bad tag keep the first target row as a (harmless) load address
         const uint64_t row0 = reinterpret_cast<uint64_t>(a.target);
-        uint64_t rp[2] = {row0, row0};
-        int tt[2] = {0, 0}, cf[2] = {0, 0}, tk[2] = {-1, -1}, lv[2] = {0, 0};
+        uint64_t rp[3] = {row0, row0, row0};
+        int tt[3] = {0, 0, -1}, cf[3] = {0, 0, 0}, tk[3] = {-1, -1, -1}, lv[3] = {0, 0, 0};
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t i = 2u * uint32_t(tid) + uint32_t(h);
+        for (int h = 0; h < 3; ++h) {
+            const uint32_t i = h < 2 ? 2u * uint32_t(tid) + uint32_t(h) : uint32_t(wv);
             const uint32_t slot = sl[h];
             const int tensor = slot >= region ? 1 : 0;
             const uint32_t rel = tensor ? slot - region : slot;
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
             const int r = tg[h].x, j = tg[h].y;
             if (i >= np || t >= (tensor ? nver : nrows)) continue;
             const bool ok = r >= 0 && r < a.R && j >= 0 && j <= K && (tensor == 0 || j < K);
-            lv[h] = 1;
+            lv[h] = (h < 2 && i < uint32_t(kWaves)) ? 0 : 1;       // slots 0 .. kWaves-1: not listed
             tt[h] = t;
             cf[h] = (ch << 2) | (tensor << 1) | (ok ? 1 : 0);
             if (ok) {
@@ -296,11 +301,36 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
         }
         // the draft tokens, loaded while the scan runs (no small loads in the streaming
         // loop: a reused load destination there makes the compiler drain every load)
-        int tv[2];
+        int tv[3];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) tv[h] = tk[h] >= 0 ? a.tokens[tk[h]] : -1;
+        for (int h = 0; h < 3; ++h) tv[h] = tk[h] >= 0 ? a.tokens[tk[h]] : -1;
+
+        struct Cur {
+            const T* row;
+            int i, cf, x;
+        };
+        auto issue_at = [&](RW& buf, Cur& m, uint64_t rw, int cfv) {
+            m.row = reinterpret_cast<const T*>(
+                (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(rw >> 32)))) << 32) |
+                uint32_t(__builtin_amdgcn_readfirstlane(int(rw))));
+            m.cf = __builtin_amdgcn_readfirstlane(cfv);
+            const int beg = (m.cf >> 2) * CH;
+            buf.load(m.row, beg, V, lane, beg + CH <= V);    // also for a bad tag: same loads on every path
+        };
+        // The wavefront's first item (slot w, the same for all its lanes). If that slot is
+        // not live, one chunk of the first target row stands in (not reduced, not
+        // written; a different chunk per wavefront), so that every wavefront issues the
+        // same loads here and the loop below needs no other entry.
+        RW q0, q1;
+        Cur m0, m1;
+        const int pre = lv[2];
+        const int pre_t = pre ? tt[2] : -1;
+        const int pre_cf = pre ? cf[2] : int((uint32_t(b) * kWaves + uint32_t(wv)) % uint32_t(C)) << 2;
+        issue_at(q0, m0, rp[2], pre_cf);
+        m0.x = tv[2];
+
         int nl;
-        const int pos = block_exclusive_scan_i32(lv[0] + lv[1], sh, nl);
+        const int pos = block_exclusive_scan_i32(lv[0] + lv[1], sh, nl, kWaves);
 #pragma unroll
         for (int h = 0, q = pos; h < 2; ++h) {
             if (!lv[h]) continue;
@@ -311,6 +341,13 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
             st_f[q] = 0;
             ++q;
         }
+        // the wavefronts' first items are entries nl + w (row -1: none), for the write-out
+        m0.i = nl + wv;
+        if (lane == 0) {
+            d_t[nl + wv] = pre_t;
+            d_cf[nl + wv] = pre_cf;
+            st_f[nl + wv] = 0;
+        }
         if (tid == 0) next_item = 0;
         __syncthreads();
 
@@ -320,20 +357,10 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
             if (lane == 0) i = atomicAdd(&next_item, 1);
             return __builtin_amdgcn_readfirstlane(i);
         };
-        struct Cur {
-            const T* row;
-            int i, cf, x;
-        };
         auto issue = [&](RW& buf, Cur& m, int i) {
             m.i = i;
-            const uint64_t rw = d_row[i];
-            m.row = reinterpret_cast<const T*>(
-                (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(rw >> 32)))) << 32) |
-                uint32_t(__builtin_amdgcn_readfirstlane(int(rw))));
-            m.cf = __builtin_amdgcn_readfirstlane(d_cf[i]);
             m.x = __builtin_amdgcn_readfirstlane(d_tok[i]);
-            const int beg = (m.cf >> 2) * CH;
-            buf.load(m.row, beg, V, lane, beg + CH <= V);    // also for a bad tag: same loads on every path
+            issue_at(buf, m, d_row[i], d_cf[i]);
         };
         auto process = [&](const RW& buf, const Cur& m) {
             const int beg = (m.cf >> 2) * CH;
@@ -362,12 +389,8 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
         // Two items per wavefront: the next one's loads are issued before the current
         // one is reduced. The last item is handled on its own exit path, so that in
         // the loop every issue is unconditional.
-        RW q0, q1;
-        Cur m0, m1;
-        int i0 = grab();
-        if (i0 < nl) {
-            issue(q0, m0, i0);
-            while (true) {
+        {
+            while (true) {                         // q0 holds an issued item here
                 const int i1 = grab();
                 if (i1 >= nl) {
                     process(q0, m0);
@@ -375,7 +398,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
                 }
                 issue(q1, m1, i1);
                 process(q0, m0);
-                i0 = grab();
+                const int i0 = grab();
                 if (i0 >= nl) {
                     process(q1, m1);
                     break;
@@ -388,8 +411,9 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
 
         // 3. write the phase's results (no stores while the loads stream: a
         //    store ahead of a load in the memory queue would delay its wait)
-        for (int i = tid; i < nl; i += kStreamThreads) {
+        for (int i = tid; i < nl + kStreamThreads / kWave; i += kStreamThreads) {
             const int t = d_t[i], cf = d_cf[i];
+            if (t < 0) continue;
             ((cf & 2) ? a.part_q : a.part_p)[long(t) * C + (cf >> 2)] = st_p[i];
             if (st_f[i]) {
                 if (cf & 2) a.rec[t].bx = st_x[i]; else a.rec[t].ax = st_x[i];
