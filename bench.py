@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--attention", action="store_true",
                     help="time spec_attention (tag-masked flattened attention over a paged KV cache) instead")
     ap.add_argument("--split-keys", type=int, default=0, help="spec_attention keys per work item (0: automatic)")
+    ap.add_argument("--kv-layout", default="head", choices=["head", "position"],
+                    help="spec_attention page layout: head-major [Hkv, page, D] or position-major [page, Hkv, D]")
     ap.add_argument("--copies", type=int, default=3,
                     help="input copies rotated over the steps (no step reads logits cached by the previous one)")
     ap.add_argument("--copy-probe", type=float, default=0.0,
@@ -304,14 +306,16 @@ def run_sweep(args, B, torch):
 
 def run_attention(args, B, torch):
     """spec_attention at R = 256, k = 5 with Qwen3-4B-like heads (32 query heads
-    over 8 KV heads, D = 128), 64-key pages drawn from a shuffled pool, contexts
-    uniform in 1024..3072, verified lengths uniform in 0..5, flattened by
-    spec_flatten. Algorithmic bytes per call: every request's K and V over its
-    visible positions (ctx + L + 1 per KV head), the queries and the output."""
+    over 8 KV heads, D = 128), 64-key pages drawn from a shuffled pool (head-major
+    unless --kv-layout position), contexts uniform in 1024..3072, verified
+    lengths uniform in 0..5, flattened by spec_flatten. Algorithmic bytes per
+    call: every request's K and V over its visible positions (ctx + L + 1 per KV
+    head), the queries and the output."""
     import numpy as np
     from draft_token_verification_flattened_amd import workloads
     from draft_token_verification_flattened_amd.pipeline import to_device
-    ai = workloads.make_attention(256, 5, seed=11)
+    head = args.kv_layout == "head"
+    ai = workloads.make_attention(256, 5, seed=11, head_major=head)
     dev = "cuda"
     R, k = ai.R, ai.k
     q, kc, vc = (to_device(x, dev) for x in (ai.q, ai.k_cache, ai.v_cache))
@@ -326,7 +330,8 @@ def run_attention(args, B, torch):
                                                  args.split_keys), dev)
 
     def call():
-        B.spec_attention(k, ai.page_size, q, kc, vc, pt, ctx, tags, cu, nr, out, ws, split_keys=args.split_keys)
+        B.spec_attention(k, ai.page_size, q, kc, vc, pt, ctx, tags, cu, nr, out, ws,
+                         kv_layout=B.KV_HEAD_MAJOR if head else B.KV_POSITION_MAJOR, split_keys=args.split_keys)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -357,7 +362,7 @@ def run_attention(args, B, torch):
     nbytes = kv + qo
     part = kern["attn_partial"]["avg_us"]
     print(json.dumps(dict(attention=dict(
-        workload="R=256, k=5, Hq=32, Hkv=8, D=128, page 64, ctx 1024..3072, L uniform 0..5",
+        workload=f"R=256, k=5, Hq=32, Hkv=8, D=128, page 64 ({args.kv_layout}-major), ctx 1024..3072, L uniform 0..5",
         rows=rows, us_per_call=us, rows_per_s=rows / (us * 1e-6), algorithmic_bytes=nbytes,
         kv_bytes=kv, call_gbps=nbytes / (us * 1e-6) / 1e9,
         roofline=dict(bound="hbm", kernel="attn_partial", achieved=nbytes / (part * 1e-6) / 1e9,

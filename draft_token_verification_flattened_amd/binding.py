@@ -24,6 +24,7 @@ BF16, F32 = 0, 1
 GREEDY, SAMPLE = 0, 1
 STATUS_BAD_TOKEN, STATUS_BAD_TAG, STATUS_BAD_PAGE = 1, 2, 4
 MAX_K, MAX_SCHED_ITEMS = 32, 16384
+KV_POSITION_MAJOR, KV_HEAD_MAJOR = 0, 1
 
 _c_int, _c_size, _c_ptr = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
@@ -51,7 +52,7 @@ _SIGS = {
     "markov_draft": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
                               _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
     "spec_attention_workspace_bytes": (_c_size, [_c_int] * 7),
-    "spec_attention": (_c_int, [_c_int] * 9 + [_c_ptr] * 9 + [_c_ptr, _c_size, _c_ptr]),
+    "spec_attention": (_c_int, [_c_int] * 10 + [_c_ptr] * 9 + [_c_ptr, _c_size, _c_ptr]),
     "specv_last_error": (ctypes.c_char_p, []),
     "specv_read_status": (_c_int, [_c_ptr, _c_ptr, ctypes.POINTER(ctypes.c_uint32)]),
     "specv_timing_enable": (_c_int, [_c_int]),
@@ -253,12 +254,15 @@ def attention_workspace_bytes(R: int, k: int, Hq: int, Hkv: int, page_size: int,
 
 
 def spec_attention(k, page_size, q, k_cache, v_cache, page_table, ctx_len, tags, cu_rows, n_rows, out, ws,
-                   split_keys=0, stream=None):
-    """q [R*(k+1), Hq, D] bf16; caches [pages, page_size, Hkv, D] bf16; page_table i32 [R, max_pages];
-    out f32 [R*(k+1), Hq, D]."""
+                   kv_layout=KV_POSITION_MAJOR, split_keys=0, stream=None):
+    """q [R*(k+1), Hq, D] bf16; caches bf16 [pages, page_size, Hkv, D] (KV_POSITION_MAJOR) or
+    [pages, Hkv, page_size, D] (KV_HEAD_MAJOR); page_table i32 [R, max_pages]; out f32 [R*(k+1), Hq, D]."""
     R, max_pages = page_table.shape
     rows, Hq, D = q.shape
-    num_pages, ps, Hkv, Dk = k_cache.shape
+    if kv_layout == KV_HEAD_MAJOR:
+        num_pages, Hkv, ps, Dk = k_cache.shape
+    else:
+        num_pages, ps, Hkv, Dk = k_cache.shape
     bf = (torch.bfloat16, torch.int16, torch.uint16)
     if rows != R * (k + 1) or ps != page_size or Dk != D:
         raise ValueError("spec_attention: q, caches and page_table disagree on R, k, page_size or D")
@@ -272,10 +276,10 @@ def spec_attention(k, page_size, q, k_cache, v_cache, page_table, ctx_len, tags,
     _dev(n_rows, "n_rows", (torch.int32,), (1,))
     _dev(out, "out", (torch.float32,), (rows, Hq, D))
     _dev(ws, "ws", (torch.uint8,))
-    _check(lib().spec_attention(R, int(k), Hq, Hkv, D, int(page_size), num_pages, max_pages, int(split_keys),
-                                _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(ctx_len),
-                                _ptr(tags), _ptr(cu_rows), _ptr(n_rows), _ptr(out), _ptr(ws), ws.numel(),
-                                _stream(stream)))
+    _check(lib().spec_attention(R, int(k), Hq, Hkv, D, int(page_size), num_pages, max_pages, int(kv_layout),
+                                int(split_keys), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                                _ptr(ctx_len), _ptr(tags), _ptr(cu_rows), _ptr(n_rows), _ptr(out), _ptr(ws),
+                                ws.numel(), _stream(stream)))
 
 
 def read_status(ws, stream=None) -> int:

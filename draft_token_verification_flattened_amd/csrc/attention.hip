@@ -47,11 +47,12 @@ using f32x4 = __attribute__((__vector_size__(4 * sizeof(float)))) float;
 
 struct AttnArgs {
     int R, k, Hq, Hkv, G, page_size, num_pages, max_pages;
+    int head_major;                        // cache layout: 0 [pages, page_size, Hkv, D], 1 [pages, Hkv, page_size, D]
     int C;                                 // query chunks per (request, KV head)
     int split_tiles, Smax;                 // tiles per split; splits per request at most
     int Mmax;                              // (k+1) G: query vectors of a full request
     const uint16_t* q;                     // [R*(k+1), Hq, D]
-    const uint16_t* kc;                    // [num_pages, page_size, Hkv, D]
+    const uint16_t* kc;                    // [num_pages, page_size, Hkv, D] or [num_pages, Hkv, page_size, D]
     const uint16_t* vc;
     const int32_t* page_table;             // [R, max_pages]
     const int32_t* ctx_len;                // [R]
@@ -184,11 +185,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         const int p0 = tile * kTile;
         int page = a.page_table[long(r) * a.max_pages + p0 / a.page_size];
         if (page < 0 || page >= a.num_pages) { err |= SPECV_STATUS_BAD_PAGE; page = 0; }
-        const long slot0 = long(page) * a.page_size + p0 % a.page_size;
+        // element offset of (page, slot, head hk): position-major or head-major pages
+        const long slot0 = p0 % a.page_size;
+        const long pstride = a.head_major ? kD : long(a.Hkv) * kD;           // between positions
+        const long base = a.head_major ? ((long(page) * a.Hkv + hk) * a.page_size) * kD
+                                       : (long(page) * a.page_size * a.Hkv + hk) * kD;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const bool ok = p0 + 16 * kb + l16 < nkc;
-            const long off = ((slot0 + 16 * kb + l16) * a.Hkv + hk) * kD + 8 * g;
+            const long off = base + (slot0 + 16 * kb + l16) * pstride + 8 * g;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 kr[kb][ks] = ok ? *reinterpret_cast<const uint4*>(a.kc + off + 32 * ks) : make_uint4(0, 0, 0, 0);
@@ -371,7 +376,11 @@ int attn_plan(int R, int k, int Hq, int Hkv, int page_size, int max_pages, int s
     return SPECV_OK;
 }
 
-int attn_check(int R, int k, int Hq, int Hkv, int D, int page_size, int num_pages, int max_pages, int split_keys) {
+int attn_check(int R, int k, int Hq, int Hkv, int D, int page_size, int num_pages, int max_pages, int split_keys,
+               int kv_layout) {
+    if (kv_layout != SPECV_KV_POSITION_MAJOR && kv_layout != SPECV_KV_HEAD_MAJOR)
+        return fail(SPECV_EINVAL, "spec_attention: kv_layout %d is neither position-major (0) nor head-major (1)",
+                    kv_layout);
     if (R < 1 || k < 1 || k > SPECV_MAX_K || Hkv < 1 || Hq < Hkv || Hq % Hkv || num_pages < 1 || max_pages < 1)
         return fail(SPECV_EINVAL,
                     "spec_attention: need R >= 1, 1 <= k <= %d, H_kv >= 1 dividing H_q, num_pages >= 1, max_pages >= 1",
@@ -407,7 +416,7 @@ int device_cus(int& cus) {
 extern "C" size_t spec_attention_workspace_bytes(int R, int k, int Hq, int Hkv, int page_size, int max_pages,
                                                  int split_keys) {
     using namespace specv;
-    if (attn_check(R, k, Hq, Hkv, kD, page_size, 1, max_pages, split_keys)) return 0;
+    if (attn_check(R, k, Hq, Hkv, kD, page_size, 1, max_pages, split_keys, SPECV_KV_POSITION_MAJOR)) return 0;
     int cus = 0;
     if (device_cus(cus)) cus = 256;
     AttnPlan p;
@@ -416,13 +425,13 @@ extern "C" size_t spec_attention_workspace_bytes(int R, int k, int Hq, int Hkv, 
 }
 
 extern "C" int spec_attention(int R, int k, int Hq, int Hkv, int D, int page_size, int num_pages, int max_pages,
-                              int split_keys, const void* q, const void* k_cache, const void* v_cache,
+                              int kv_layout, int split_keys, const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* page_table, const int32_t* ctx_len, const int32_t* tags,
                               const int32_t* cu_rows, const int32_t* n_rows, float* out, void* ws, size_t ws_bytes,
                               specv_stream stream) {
     using namespace specv;
     clear_error();
-    if (int e = attn_check(R, k, Hq, Hkv, D, page_size, num_pages, max_pages, split_keys)) return e;
+    if (int e = attn_check(R, k, Hq, Hkv, D, page_size, num_pages, max_pages, split_keys, kv_layout)) return e;
     if (!q || !k_cache || !v_cache || !page_table || !ctx_len || !tags || !cu_rows || !n_rows || !out || !ws)
         return fail(SPECV_EINVAL, "spec_attention: NULL required pointer");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
@@ -441,6 +450,7 @@ extern "C" int spec_attention(int R, int k, int Hq, int Hkv, int D, int page_siz
     AttnArgs a;
     a.R = R; a.k = k; a.Hq = Hq; a.Hkv = Hkv; a.G = p.G;
     a.page_size = page_size; a.num_pages = num_pages; a.max_pages = max_pages;
+    a.head_major = kv_layout == SPECV_KV_HEAD_MAJOR;
     a.C = p.C; a.split_tiles = p.split_tiles; a.Smax = p.Smax; a.Mmax = p.Mmax;
     a.q = static_cast<const uint16_t*>(q);
     a.kc = static_cast<const uint16_t*>(k_cache);

@@ -303,14 +303,17 @@ class AttnInputs:
     k_cache: np.ndarray             # bf16 bits [pages, page_size, Hkv, D]
     v_cache: np.ndarray             # bf16 bits [pages, page_size, Hkv, D]
     page_table: np.ndarray          # i32 [R, max_pages]
+    head_major: bool = False        # pools [pages, Hkv, page_size, D] instead of [pages, page_size, Hkv, D]
 
 
 def make_attention(R: int, k: int, *, Hq: int = 32, Hkv: int = 8, D: int = 128, page_size: int = 64,
-                   ctx_range=(1024, 3072), lengths: Optional[np.ndarray] = None, seed: int = 11) -> AttnInputs:
+                   ctx_range=(1024, 3072), lengths: Optional[np.ndarray] = None, seed: int = 11,
+                   head_major: bool = False) -> AttnInputs:
     """Synthetic attention inputs: N(0, 1) queries, keys and values in bf16;
     context lengths uniform in ctx_range; each request's pages drawn without
     replacement from a shuffled pool with room for ctx + k + 1 positions; per
-    request verified lengths uniform in 0 .. k unless given."""
+    request verified lengths uniform in 0 .. k unless given. head_major: pools
+    [pages, Hkv, page_size, D] instead of [pages, page_size, Hkv, D]."""
     g = np.random.Generator(np.random.Philox(key=(int(seed) << 64) | 0xA77))
     if lengths is None:
         lengths = g.integers(0, k + 1, size=R).astype(np.int32)
@@ -327,12 +330,13 @@ def make_attention(R: int, k: int, *, Hq: int = 32, Hkv: int = 8, D: int = 128, 
     q = f32_to_bf16_bits(g.standard_normal((R * (k + 1), Hq, D), dtype=np.float32))
 
     def pool(array_id):
-        out = np.empty((n_pages, page_size, Hkv, D), dtype=np.uint16)
+        shape = (Hkv, page_size, D) if head_major else (page_size, Hkv, D)
+        out = np.empty((n_pages,) + shape, dtype=np.uint16)
 
         def fill(b, lo, hi):
             gg = _stream(seed, array_id, b)
-            out[lo:hi] = f32_to_bf16_bits(gg.standard_normal((hi - lo, page_size, Hkv, D), dtype=np.float32))
+            out[lo:hi] = f32_to_bf16_bits(gg.standard_normal((hi - lo,) + shape, dtype=np.float32))
         _parallel_blocks(n_pages, fill)
         return out
     return AttnInputs(R=R, k=k, Hq=Hq, Hkv=Hkv, D=D, page_size=page_size, lengths=lengths, ctx_len=ctx,
-                      q=q, k_cache=pool(40), v_cache=pool(41), page_table=table)
+                      q=q, k_cache=pool(40), v_cache=pool(41), page_table=table, head_major=head_major)

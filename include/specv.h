@@ -51,6 +51,7 @@ enum {
 
 enum { SPECV_BF16 = 0, SPECV_F32 = 1 };       /* logit storage type */
 enum { SPECV_GREEDY = 0, SPECV_SAMPLE = 1 };  /* acceptance mode */
+enum { SPECV_KV_POSITION_MAJOR = 0, SPECV_KV_HEAD_MAJOR = 1 };  /* spec_attention cache layout */
 
 /* status-word bits (specv_read_status) */
 enum {
@@ -307,11 +308,15 @@ int markov_draft(int mode, int dtype, int R, int k, int V, int d_m,
  *   num_pages       host int: pages in each cache pool
  *   max_pages       host int: columns of page_table; ctx_len[r] + k + 1 must
  *                   fit in max_pages * page_size
+ *   kv_layout       host int: SPECV_KV_POSITION_MAJOR, pages [page_size, Hkv, D]
+ *                   (a position's heads side by side), or SPECV_KV_HEAD_MAJOR,
+ *                   pages [Hkv, page_size, D] (each head's page_size x D block
+ *                   contiguous; the faster one to stream, ~12% at 64-key pages)
  *   split_keys      host int: keys per work item (a multiple of 32), or 0 to
  *                   let the library choose; a tuning knob, results depend on
  *                   it only through the float32 summation order
  *   q               bf16 [R*(k+1), Hq, D] queries of the flattened rows
- *   k_cache, v_cache bf16 [num_pages, page_size, Hkv, D]
+ *   k_cache, v_cache bf16 [num_pages, page_size, Hkv, D] or [num_pages, Hkv, page_size, D]
  *   page_table      i32 [R, max_pages];  ctx_len i32 [R] (>= 0)
  *   tags, cu_rows, n_rows  as written by spec_schedule / spec_flatten
  *   out             f32 [R*(k+1), Hq, D]; rows >= n_rows are not written
@@ -324,14 +329,14 @@ int markov_draft(int mode, int dtype, int R, int k, int V, int d_m,
  * the request's rows are not written); a page id outside [0, num_pages) or a
  * context length that is negative or overruns the page-table row makes the
  * request's rows zeros (SPECV_STATUS_BAD_PAGE). No read leaves the pools.
- * Errors: SPECV_EINVAL for bad sizes, NULL or misaligned pointers or a short
- * workspace; SPECV_EUNSUPPORTED for D != 128, page sizes that are not a
+ * Errors: SPECV_EINVAL for bad sizes or layout, NULL or misaligned pointers or a
+ * short workspace; SPECV_EUNSUPPORTED for D != 128, page sizes that are not a
  * multiple of 32, or sizes beyond 32-bit grid and index ranges.
  */
 size_t spec_attention_workspace_bytes(int R, int k, int Hq, int Hkv, int page_size, int max_pages,
                                       int split_keys);
 int spec_attention(int R, int k, int Hq, int Hkv, int D, int page_size, int num_pages, int max_pages,
-                   int split_keys, const void* q, const void* k_cache, const void* v_cache,
+                   int kv_layout, int split_keys, const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* page_table, const int32_t* ctx_len, const int32_t* tags,
                    const int32_t* cu_rows, const int32_t* n_rows, float* out, void* ws, size_t ws_bytes,
                    specv_stream stream);

@@ -19,7 +19,9 @@ notes):
                 block); other requests are never visible.
   cache         paged: position p of request r lives in page
                 page_table[r, p // page_size], slot p % page_size; the pool is
-                [pages, page_size, H_kv, D].
+                [pages, page_size, H_kv, D] (position-major) or
+                [pages, H_kv, page_size, D] (head-major): two storage orders of
+                the same cache.
   heads         grouped-query attention: query head h reads KV head
                 h // (H_q / H_kv).
   scale         1 / sqrt(D); softmax over the visible keys.
@@ -42,24 +44,28 @@ import numpy as np
 from .numerics import decode
 
 
-def gather_keys(cache: np.ndarray, page_table: np.ndarray, r: int, n: int, page_size: int, hk: int) -> np.ndarray:
+def gather_keys(cache: np.ndarray, page_table: np.ndarray, r: int, n: int, page_size: int, hk: int,
+                head_major: bool = False) -> np.ndarray:
     """Positions 0 .. n-1 of request r, KV head hk: float64 [n, D]."""
     p = np.arange(n)
     pages = page_table[r, p // page_size]
+    if head_major:
+        return cache[pages, hk, p % page_size, :].astype(np.float64)
     return cache[pages, p % page_size, hk, :].astype(np.float64)
 
 
-def flat_attention(q, k_cache, v_cache, page_table, ctx_len, tags, n_rows, page_size, dtype="bf16"):
+def flat_attention(q, k_cache, v_cache, page_table, ctx_len, tags, n_rows, page_size, dtype="bf16",
+                   head_major=False):
     """Output [n_rows, H_q, D] float64 for the flattened rows 0 .. n_rows-1.
 
     q [B, H_q, D], caches [pages, page_size, H_kv, D] (bf16 bit patterns or
     fp32), page_table [R, max_pages], ctx_len [R], tags [B, 2] (request,
-    position)."""
+    position). head_major: the caches are [pages, H_kv, page_size, D]."""
     Q = decode(q, dtype)
     K = decode(k_cache, dtype)
     Vc = decode(v_cache, dtype)
     Hq, D = Q.shape[1], Q.shape[2]
-    Hkv = K.shape[2]
+    Hkv = K.shape[1] if head_major else K.shape[2]
     G = Hq // Hkv
     scale = 1.0 / np.sqrt(float(D))
     out = np.zeros((n_rows, Hq, D), dtype=np.float64)
@@ -67,8 +73,8 @@ def flat_attention(q, k_cache, v_cache, page_table, ctx_len, tags, n_rows, page_
         r, j = int(tags[t, 0]), int(tags[t, 1])
         n = int(ctx_len[r]) + j + 1                   # visible positions
         for hk in range(Hkv):
-            Kr = gather_keys(K, page_table, r, n, page_size, hk)
-            Vr = gather_keys(Vc, page_table, r, n, page_size, hk)
+            Kr = gather_keys(K, page_table, r, n, page_size, hk, head_major)
+            Vr = gather_keys(Vc, page_table, r, n, page_size, hk, head_major)
             for h in range(hk * G, (hk + 1) * G):
                 s = (Kr @ Q[t, h]) * scale
                 w = np.exp(s - s.max())

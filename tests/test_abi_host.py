@@ -130,11 +130,11 @@ def test_verify_ex_rejects_job_writing_this_batch():
 
 
 def _attention(**kw):
-    a = dict(R=4, k=5, Hq=32, Hkv=8, D=128, ps=64, pages=100, maxp=50, split=0, q=FAKE, kc=FAKE, vc=FAKE,
+    a = dict(R=4, k=5, Hq=32, Hkv=8, D=128, ps=64, pages=100, maxp=50, layout=0, split=0, q=FAKE, kc=FAKE, vc=FAKE,
              pt=FAKE, ctx=FAKE, tags=FAKE, cu=FAKE, nr=FAKE, out=FAKE, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return B.lib().spec_attention(a["R"], a["k"], a["Hq"], a["Hkv"], a["D"], a["ps"], a["pages"], a["maxp"],
-                                  a["split"], a["q"], a["kc"], a["vc"], a["pt"], a["ctx"], a["tags"], a["cu"],
+                                  a["layout"], a["split"], a["q"], a["kc"], a["vc"], a["pt"], a["ctx"], a["tags"], a["cu"],
                                   a["nr"], a["out"], a["ws"], a["wsb"], None)
 
 
@@ -147,6 +147,7 @@ def _attention(**kw):
     (dict(D=64), B.EUNSUPPORTED, "head dimension"),
     (dict(ps=48), B.EUNSUPPORTED, "page size"),
     (dict(split=40), B.EINVAL, "split_keys"),
+    (dict(layout=2), B.EINVAL, "kv_layout"),
     (dict(ps=32, maxp=0), B.EINVAL, "max_pages"),
     (dict(k=32, ps=32, maxp=1), B.EINVAL, "cannot hold"),
     (dict(vc=None), B.EINVAL, "NULL"),

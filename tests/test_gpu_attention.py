@@ -43,7 +43,7 @@ def _run(ai, tags, cu, n, split_keys=0, page_table=None, ctx_len=None):
                                                  split_keys), dev)
     B.spec_attention(ai.k, ai.page_size, q, kc, vc, to_device(pt, dev), to_device(ctx, dev),
                      to_device(tags, dev), to_device(cu, dev), to_device(np.array([n], np.int32), dev), out, ws,
-                     split_keys=split_keys)
+                     kv_layout=B.KV_HEAD_MAJOR if ai.head_major else B.KV_POSITION_MAJOR, split_keys=split_keys)
     status = B.read_status(ws)
     return out.cpu().numpy().astype(np.float64), status
 
@@ -52,9 +52,10 @@ def _oracle(ai, tags, rows, ctx_len=None):
     ctx = ai.ctx_len if ctx_len is None else ctx_len
     q = ai.q[rows]
     t = tags[rows]
-    ref = oatt.flat_attention(q, ai.k_cache, ai.v_cache, ai.page_table, ctx, t, len(rows), ai.page_size)
+    ref = oatt.flat_attention(q, ai.k_cache, ai.v_cache, ai.page_table, ctx, t, len(rows), ai.page_size,
+                              head_major=ai.head_major)
     bound = oatt.flat_attention(q, ai.k_cache, ai.v_cache & np.uint16(0x7FFF), ai.page_table, ctx, t,
-                                len(rows), ai.page_size)
+                                len(rows), ai.page_size, head_major=ai.head_major)
     return ref, bound
 
 
@@ -77,11 +78,12 @@ CASES = {
 
 @pytest.mark.parametrize("name", sorted(CASES))
 @pytest.mark.parametrize("split_keys", [0, 32, 96])
-def test_attention_matches_oracle(name, split_keys):
+@pytest.mark.parametrize("head_major", [False, True])
+def test_attention_matches_oracle(name, split_keys, head_major):
     R, k, Hq, Hkv, ps, cr, lengths = CASES[name]
-    print(f"[gpu] spec_attention {name} split_keys={split_keys}", flush=True)
+    print(f"[gpu] spec_attention {name} split_keys={split_keys} head_major={head_major}", flush=True)
     ai = workloads.make_attention(R, k, Hq=Hq, Hkv=Hkv, page_size=ps, ctx_range=cr,
-                                  lengths=np.array(lengths, np.int32), seed=5)
+                                  lengths=np.array(lengths, np.int32), seed=5, head_major=head_major)
     ai.ctx_len[0] = 0                      # a row that sees one key only (L_0 = 0) or a short block
     tags, cu, n = _batch(ai, ai.lengths)
     got, status = _run(ai, tags, cu, n, split_keys)
@@ -91,12 +93,14 @@ def test_attention_matches_oracle(name, split_keys):
     assert np.isnan(got[n:]).all()         # rows past n_rows untouched
 
 
-def test_attention_bench_size_sampled():
+@pytest.mark.parametrize("head_major", [True, False])
+def test_attention_bench_size_sampled(head_major):
     """R = 256, k = 5, 32 query heads over 8 KV heads, D = 128, 64-key pages,
-    contexts 1024..3072: the launch configuration of the benchmark; sampled rows
-    against the oracle, every row finite, repeat calls bit-identical."""
-    print("[gpu] spec_attention bench size", flush=True)
-    ai = workloads.make_attention(256, 5, seed=11)
+    contexts 1024..3072: the launch configuration of the benchmark (head-major
+    pages); sampled rows against the oracle, every row finite, repeat calls
+    bit-identical."""
+    print(f"[gpu] spec_attention bench size head_major={head_major}", flush=True)
+    ai = workloads.make_attention(256, 5, seed=11, head_major=head_major)
     tags, cu, n = _batch(ai, ai.lengths)
     got, status = _run(ai, tags, cu, n)
     again, _ = _run(ai, tags, cu, n)

@@ -95,3 +95,21 @@ def test_tag_mask_hides_later_positions():
         kc[a.page_table[r, pos // a.page_size], pos % a.page_size] ^= np.uint16(0x4000)
         o2 = oatt.flat_attention(a.q, kc, a.v_cache, a.page_table, a.ctx_len, tags, nr, a.page_size)
         assert np.array_equal(o2[t], out[t]) != changes
+
+
+def test_head_major_storage_is_the_same_cache():
+    """The head-major pool holds the same cache as the position-major one, with
+    the head and position axes of each page swapped: the outputs agree bit for
+    bit (a wrong axis in either gather would mix heads and positions)."""
+    a, tags, nr = _small(seed=9, Hkv=2, Hq=4)
+    ref = oatt.flat_attention(a.q, a.k_cache, a.v_cache, a.page_table, a.ctx_len, tags, nr, a.page_size)
+    kh = np.ascontiguousarray(a.k_cache.transpose(0, 2, 1, 3))
+    vh = np.ascontiguousarray(a.v_cache.transpose(0, 2, 1, 3))
+    got = oatt.flat_attention(a.q, kh, vh, a.page_table, a.ctx_len, tags, nr, a.page_size, head_major=True)
+    assert np.array_equal(got, ref)
+    # and reading the head-major pool as position-major is a different cache
+    if a.page_size != a.Hkv:
+        wrong = oatt.flat_attention(a.q, np.ascontiguousarray(kh.reshape(a.k_cache.shape)),
+                                    np.ascontiguousarray(vh.reshape(a.v_cache.shape)), a.page_table,
+                                    a.ctx_len, tags, nr, a.page_size)
+        assert not np.allclose(wrong, ref)
