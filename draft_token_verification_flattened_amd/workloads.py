@@ -119,8 +119,18 @@ class Workload:
     emb: Optional[np.ndarray] = None            # [V,d_m]   previous-token embedding
     proj: Optional[np.ndarray] = None           # [V,d_m]   projection, one d_m row per vocab entry
     prev_token: Optional[np.ndarray] = None     # i32 [R]
+    rec: Optional[np.ndarray] = None            # [d_m,d_m] RNN-head recurrence A ((A h)_j = sum_k A[j,k] h_k)
     u_draft: Optional[np.ndarray] = None        # f32 [R,k]
     d_m: int = 0
+
+
+def _recurrence(seed: int, d_m: int, dtype: str) -> np.ndarray:
+    """RNN-head recurrence A [d_m, d_m]: N(0, (0.5 / sqrt(d_m))^2) entries (spectral
+    radius about 0.5, so the state neither dies out nor saturates over a block),
+    from a stream of its own so the workload's other arrays are unchanged."""
+    gr = _stream(seed, 3, 0)
+    a = np.float32(0.5 / np.sqrt(d_m)) * gr.standard_normal((d_m, d_m), dtype=np.float32)
+    return _enc(a, dtype)
 
 
 def _enc(x32: np.ndarray, dtype: str) -> np.ndarray:
@@ -199,7 +209,7 @@ def make(name: str, *, R: Optional[int] = None, V: Optional[int] = None) -> Work
         prev = g.integers(0, V_, size=R_, dtype=np.int64).astype(np.int32)
         z = (1.0 + g.standard_normal((R_, k), dtype=np.float32)).astype(np.float32)
         w.update(target=_enc(tl32, dt), backbone=_enc(bk32, dt), emb=emb, proj=proj,
-                 prev_token=prev, conf_logit=z, d_m=cfg["d_m"])
+                 prev_token=prev, conf_logit=z, d_m=cfg["d_m"], rec=_recurrence(seed, cfg["d_m"], dt))
     elif name in ("c1", "c2", "c3"):
         target = np.empty((R_, k + 1, V_), dtype=st)
         draft = np.empty((R_, k, V_), dtype=st)
@@ -259,7 +269,7 @@ def make(name: str, *, R: Optional[int] = None, V: Optional[int] = None) -> Work
         prev = g.integers(0, V_, size=R_, dtype=np.int64).astype(np.int32)
         z = (1.0 + g.standard_normal((R_, k), dtype=np.float32)).astype(np.float32)
         w.update(target=target, backbone=backbone, emb=emb, proj=proj, prev_token=prev,
-                 conf_logit=z, d_m=d_m)
+                 conf_logit=z, d_m=d_m, rec=_recurrence(seed, d_m, dt))
     else:
         raise KeyError(name)
 

@@ -31,7 +31,8 @@ Modules
   verify    the rule over a flattened batch, float64, vectorised over requests
   schedule  calibration, survival, the hardware-aware prefix scheduler, flatten
   markov    the Markov head of the semi-autoregressive drafter
+  rnn       the RNN head (recurrent state over the block's prefix)
   attention tag-masked attention of the flattened rows over a paged KV cache
 """
 
-from . import numerics, rule, verify, schedule, markov, attention  # noqa: F401
+from . import numerics, rule, verify, schedule, markov, rnn, attention  # noqa: F401
