@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--split-keys", type=int, default=0, help="spec_attention keys per work item (0: automatic)")
     ap.add_argument("--kv-layout", default="head", choices=["head", "position"],
                     help="spec_attention page layout: head-major [Hkv, page, D] or position-major [page, Hkv, D]")
+    ap.add_argument("--head", default="markov", choices=["markov", "rnn"],
+                    help="the drafter's sequential module for the semi-autoregressive workload (c4)")
     ap.add_argument("--copies", type=int, default=3,
                     help="input copies rotated over the steps (no step reads logits cached by the previous one)")
     ap.add_argument("--copy-probe", type=float, default=0.0,
@@ -118,7 +120,7 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
     B.timing_enable(False)
     ms_step = t0.elapsed_time(t1) / steps
     kern = {}
-    for name in ("markov_logits", "markov_pick", "schedule", "verify_stream", "verify_decide"):
+    for name in ("rnn_state", "markov_logits", "markov_pick", "schedule", "verify_stream", "verify_decide"):
         n, tot = B.timing_read(name)
         if n:
             kern[name] = dict(launches_per_step=n / steps, avg_us=1000.0 * tot / n)
@@ -454,7 +456,7 @@ def main():
         return
     w = workloads.make(args.config)
     max_len = w.k if args.max_len == "k" else int(args.max_len)
-    d = DeviceStep(w, copies=args.copies)
+    d = DeviceStep(w, copies=args.copies, head=args.head)
     mode_c = B.SAMPLE if args.mode == "sample" else B.GREEDY
     main_res = run_variant(d, w, mode_c, args.mode, max_len, args.steps, args.warmup, B, torch)
 
@@ -502,7 +504,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.config}: {workloads.CONFIGS[args.config]['desc']}",
+            "workload": f"{args.config}: {workloads.CONFIGS[args.config]['desc']}"
+                        + (", RNN head" if args.head == "rnn" and w.backbone is not None else ""),
             "R": w.R, "k": w.k, "V": w.V, "storage": w.dtype, "mode": args.mode,
             "tau": w.tau, "max_len": max_len, "verified_drafts_per_step": main_res["N"],
             "flattened_rows_per_step": main_res["rows"], "parallelism": "single GPU",

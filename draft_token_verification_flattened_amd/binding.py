@@ -53,6 +53,8 @@ _SIGS = {
                               _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
     "spec_attention_workspace_bytes": (_c_size, [_c_int] * 7),
     "spec_attention": (_c_int, [_c_int] * 10 + [_c_ptr] * 9 + [_c_ptr, _c_size, _c_ptr]),
+    "rnn_draft_workspace_bytes": (_c_size, [_c_int] * 4),
+    "rnn_draft": (_c_int, [_c_int] * 6 + [_c_ptr] * 5 + [ctypes.c_float] + [_c_ptr] * 5 + [_c_size, _c_ptr]),
     "specv_last_error": (ctypes.c_char_p, []),
     "specv_read_status": (_c_int, [_c_ptr, _c_ptr, ctypes.POINTER(ctypes.c_uint32)]),
     "specv_timing_enable": (_c_int, [_c_int]),
@@ -280,6 +282,33 @@ def spec_attention(k, page_size, q, k_cache, v_cache, page_table, ctx_len, tags,
                                 int(split_keys), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
                                 _ptr(ctx_len), _ptr(tags), _ptr(cu_rows), _ptr(n_rows), _ptr(out), _ptr(ws),
                                 ws.numel(), _stream(stream)))
+
+
+def rnn_workspace_bytes(R: int, k: int, V: int, d_m: int) -> int:
+    return int(lib().rnn_draft_workspace_bytes(R, k, V, d_m))
+
+
+def rnn_draft(mode, backbone, emb, rec, proj, prev_token, temperature, uniforms, tokens_out, logits_out, ws,
+              state_out=None, stream=None):
+    R, k, V = backbone.shape
+    d_m = emb.shape[1]
+    dt = logit_dtype(backbone)
+    _dev(backbone, "backbone", tuple(_LOGIT_TYPES))
+    _dev(emb, "emb", (backbone.dtype,), (V, d_m))
+    _dev(rec, "rec", (backbone.dtype,), (d_m, d_m))
+    _dev(proj, "proj", (backbone.dtype,), (V, d_m))
+    _dev(prev_token, "prev_token", (torch.int32,), (R,))
+    _dev(tokens_out, "tokens_out", (torch.int32,), (R, k))
+    _dev(logits_out, "logits_out", (backbone.dtype,), (R, k, V))
+    _dev(ws, "ws", (torch.uint8,))
+    if state_out is not None:
+        _dev(state_out, "state_out", (backbone.dtype,), (R, k, d_m))
+    if mode == SAMPLE:
+        _dev(uniforms, "uniforms", (torch.float32,), (R, k))
+    _check(lib().rnn_draft(int(mode), dt, R, k, V, d_m, _ptr(backbone), _ptr(emb), _ptr(rec), _ptr(proj),
+                           _ptr(prev_token), float(temperature), _ptr(uniforms) if mode == SAMPLE else None,
+                           _ptr(tokens_out), _ptr(logits_out), _ptr(state_out), _ptr(ws), ws.numel(),
+                           _stream(stream)))
 
 
 def read_status(ws, stream=None) -> int:

@@ -18,6 +18,15 @@
 //   markov_logits_fma (fp32)   the same with one lane per output and plain FMA.
 //   markov_pick                one wavefront per request: merges the partials;
 //       greedy argmax, or the two-level inverse-CDF draw over softmax(dl / tau).
+//
+// rnn_draft: the RNN head, the pages' other sequential module, which carries
+// the whole prefix of the block in a recurrent state (same sections). Read as
+// h_i = round(tanh(E[x_{i-1}] + A h_{i-1})), h_{-1} = 0, dl_i = bk_i + h_i . P^T:
+//   rnn_state                  one workgroup per request: h_i from h_{i-1} and
+//       the embedding row, float32 accumulation, tanh, rounded to the storage
+//       type (the operand of the projection);
+//   then the same logits and pick kernels, with the state rows in place of the
+//       gathered embedding rows.
 #include <climits>
 
 #include "common.h"
@@ -36,6 +45,8 @@ struct MarkovArgs {
     const void* emb;                // [V,d_m]
     const void* proj;               // [V,d_m]
     const int32_t* prev;            // [R]
+    const void* rec;                // RNN head: [d_m,d_m] recurrence A (NULL: Markov head)
+    void* state;                    // RNN head: [R,k,d_m] states, storage type
     const float* uniforms;          // [R,k]
     int32_t* tokens;                // [R,k]
     void* dl;                       // [R,k,V]
@@ -139,7 +150,8 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
             mok[b] = m < a.R;
             int p = mok[b] ? prev_token(a, m) : 0;
             if (p < 0 || p >= a.V) p = 0;             // reported by markov_pick
-            erow[b] = E + long(p) * dm;
+            erow[b] = a.state ? static_cast<const uint16_t*>(a.state) + (long(mok[b] ? m : 0) * a.k + a.pos) * dm
+                              : E + long(p) * dm;
         }
         for (int k0 = 0; k0 < dm; k0 += 32) {
             bf16x8 bfr[4], afr[4];
@@ -225,10 +237,12 @@ __global__ __launch_bounds__(256) void markov_logits_fma(MarkovArgs a) {
     if (a.pos == 0 && item == 0 && lane == 0) a.hdr->status = 0u;   // this kernel sets no bits
     int p = prev_token(a, m);
     if (p < 0 || p >= a.V) p = 0;                 // reported by markov_pick
+    const float* erow = a.state ? static_cast<const float*>(a.state) + (long(m) * a.k + a.pos) * a.d_m
+                                : E + long(p) * a.d_m;
     Part pp = part_empty(a.mode);
     if (n < a.V) {
         float acc = 0.f;
-        for (int d = 0; d < a.d_m; ++d) acc = fmaf(E[long(p) * a.d_m + d], P[long(n) * a.d_m + d], acc);
+        for (int d = 0; d < a.d_m; ++d) acc = fmaf(erow[d], P[long(n) * a.d_m + d], acc);
         const long off = (long(m) * a.k + a.pos) * long(a.V) + n;
         const float v = acc + bk[off];
         dl[off] = v;
@@ -242,6 +256,36 @@ __global__ __launch_bounds__(256) void markov_logits_fma(MarkovArgs a) {
         part_merge(a.mode, pp, q);
     }
     if (lane == 0) a.part[long(m) * a.S + sl] = make_float2(pp.a, pp.b);
+}
+
+// ---------------------------------------------------------------------------
+// RNN head: h_i = round(tanh(E[x_{i-1}] + A h_{i-1})), one workgroup per request
+// ---------------------------------------------------------------------------
+
+template <int DT>
+__global__ __launch_bounds__(256) void rnn_state(MarkovArgs a) {
+    using LT = Logit<DT>;
+    using T = typename LT::T;
+    __shared__ float h[512];
+    const int m = blockIdx.x, dm = a.d_m;
+    const T* A = static_cast<const T*>(a.rec);
+    const T* E = static_cast<const T*>(a.emb);
+    T* st = static_cast<T*>(a.state);
+    for (int q = threadIdx.x; q < dm; q += blockDim.x)
+        h[q] = a.pos == 0 ? 0.f : LT::load1(st + (long(m) * a.k + a.pos - 1) * dm + q);
+    int p = prev_token(a, m);
+    if (p < 0 || p >= a.V) p = 0;                 // reported by markov_pick
+    __syncthreads();
+    for (int j = threadIdx.x; j < dm; j += blockDim.x) {
+        float s = LT::load1(E + long(p) * dm + j);
+        const T* row = A + long(j) * dm;
+        for (int q = 0; q < dm; ++q) s = fmaf(LT::load1(row + q), h[q], s);
+        const float t = tanhf(s);
+        if constexpr (DT == SPECV_BF16)
+            st[(long(m) * a.k + a.pos) * dm + j] = uint16_t(f32_to_bf16_rne(t));
+        else
+            st[(long(m) * a.k + a.pos) * dm + j] = t;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -289,40 +333,44 @@ __global__ __launch_bounds__(256) void markov_pick(MarkovArgs a) {
 
 }  // namespace specv
 
-extern "C" size_t markov_draft_workspace_bytes(int R, int k, int V, int d_m) {
+namespace specv {
+namespace {
+
+size_t head_workspace_bytes(int R, int k, int V, int d_m, bool state) {
     if (R < 1 || k < 1 || k > SPECV_MAX_K || V < 1 || d_m < 1) return 0;
-    const size_t S = (size_t(V) + specv::kSlice - 1) / specv::kSlice;
-    return 256 + ((size_t(R) * S * sizeof(float2) + 255) & ~size_t(255));
+    const size_t S = (size_t(V) + kSlice - 1) / kSlice;
+    size_t n = 256 + ((size_t(R) * S * sizeof(float2) + 255) & ~size_t(255));
+    if (state) n += (size_t(R) * k * d_m * sizeof(float) + 255) & ~size_t(255);
+    return n;
 }
 
-extern "C" int markov_draft(int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
-                            const void* emb, const void* proj, const int32_t* prev_token,
-                            float temperature, const float* uniforms, int32_t* draft_tokens_out,
-                            void* draft_logits_out, void* ws, size_t ws_bytes, specv_stream stream) {
-    using namespace specv;
+// Markov head (rec == NULL) or RNN head: validation and the per-position launches.
+int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
+               const void* emb, const void* rec, const void* proj, const int32_t* prev_token, float temperature,
+               const float* uniforms, int32_t* draft_tokens_out, void* draft_logits_out, void* state_out, void* ws,
+               size_t ws_bytes, hipStream_t s) {
     clear_error();
+    const bool rnn = rec != nullptr;
     if (mode != SPECV_GREEDY && mode != SPECV_SAMPLE)
-        return fail(SPECV_EINVAL, "markov_draft: mode %d is neither greedy (0) nor sample (1)", mode);
-    if (dtype != SPECV_BF16 && dtype != SPECV_F32)
-        return fail(SPECV_EUNSUPPORTED, "markov_draft: dtype %d unsupported", dtype);
+        return fail(SPECV_EINVAL, "%s: mode %d is neither greedy (0) nor sample (1)", fn, mode);
+    if (dtype != SPECV_BF16 && dtype != SPECV_F32) return fail(SPECV_EUNSUPPORTED, "%s: dtype %d unsupported", fn, dtype);
     if (R < 1 || k < 1 || k > SPECV_MAX_K || V < 1 || d_m < 1)
-        return fail(SPECV_EINVAL, "markov_draft: need R >= 1, 1 <= k <= %d, V >= 1, d_m >= 1", SPECV_MAX_K);
+        return fail(SPECV_EINVAL, "%s: need R >= 1, 1 <= k <= %d, V >= 1, d_m >= 1", fn, SPECV_MAX_K);
     if (dtype == SPECV_BF16 && (d_m % 32 != 0 || d_m > 480))
-        return fail(SPECV_EUNSUPPORTED, "markov_draft: bf16 needs d_m %% 32 == 0 and d_m <= 480 (got %d)", d_m);
+        return fail(SPECV_EUNSUPPORTED, "%s: bf16 needs d_m %% 32 == 0 and d_m <= 480 (got %d)", fn, d_m);
+    if (rnn && d_m > 512) return fail(SPECV_EUNSUPPORTED, "%s: d_m %d above 512", fn, d_m);
     if (!backbone_logits || !emb || !proj || !prev_token || !draft_tokens_out || !draft_logits_out || !ws)
-        return fail(SPECV_EINVAL, "markov_draft: NULL required pointer");
+        return fail(SPECV_EINVAL, "%s: NULL required pointer", fn);
     if (mode == SPECV_SAMPLE) {
-        if (!uniforms) return fail(SPECV_EINVAL, "markov_draft: sampling needs uniforms");
+        if (!uniforms) return fail(SPECV_EINVAL, "%s: sampling needs uniforms", fn);
         if (!(temperature > 0.f) || !(temperature < INFINITY))
-            return fail(SPECV_EINVAL, "markov_draft: temperature must be finite and > 0");
+            return fail(SPECV_EINVAL, "%s: temperature must be finite and > 0", fn);
     }
-    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
-        return fail(SPECV_EINVAL, "markov_draft: workspace must be 256-byte aligned");
-    const size_t need = markov_draft_workspace_bytes(R, k, V, d_m);
-    if (ws_bytes < need)
-        return fail(SPECV_EINVAL, "markov_draft: workspace of %zu bytes, need %zu", ws_bytes, need);
-    if (dtype == SPECV_BF16 && (!aligned16(emb) || !aligned16(proj)))
-        return fail(SPECV_EINVAL, "markov_draft: emb and proj must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(SPECV_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+    const size_t need = head_workspace_bytes(R, k, V, d_m, rnn && !state_out);
+    if (ws_bytes < need) return fail(SPECV_EINVAL, "%s: workspace of %zu bytes, need %zu", fn, ws_bytes, need);
+    if (dtype == SPECV_BF16 && (!aligned16(emb) || !aligned16(proj) || (state_out && !aligned16(state_out))))
+        return fail(SPECV_EINVAL, "%s: emb, proj and state_out must be 16-byte aligned", fn);
 
     MarkovArgs a;
     a.R = R; a.k = k; a.V = V; a.d_m = d_m;
@@ -333,7 +381,10 @@ extern "C" int markov_draft(int mode, int dtype, int R, int k, int V, int d_m, c
     a.uniforms = uniforms; a.tokens = draft_tokens_out; a.dl = draft_logits_out;
     a.hdr = static_cast<WsHeader*>(ws);
     a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + 256);
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    a.rec = rec;
+    a.state = nullptr;
+    if (rnn)
+        a.state = state_out ? state_out : static_cast<char*>(ws) + head_workspace_bytes(R, k, V, d_m, false);
     const bool vec4 = (V % 4) == 0 && (reinterpret_cast<uintptr_t>(backbone_logits) & 7u) == 0 &&
                       (reinterpret_cast<uintptr_t>(draft_logits_out) & 7u) == 0;
     const size_t lds = size_t(kSlice) * size_t(d_m * 2 + 16);
@@ -342,16 +393,51 @@ extern "C" int markov_draft(int mode, int dtype, int R, int k, int V, int d_m, c
     for (int i = 0; i < k; ++i) {
         a.pos = i;
         if (dtype == SPECV_BF16) {
+            if (rnn) SPECV_LAUNCH("rnn_state", rnn_state<SPECV_BF16>, R, 256, 0, s, a);
             if (vec4)
                 SPECV_LAUNCH("markov_logits", markov_logits_mfma<true>, a.S, 256, lds, s, a);
             else
                 SPECV_LAUNCH("markov_logits", markov_logits_mfma<false>, a.S, 256, lds, s, a);
             SPECV_LAUNCH("markov_pick", markov_pick<SPECV_BF16>, (R + 3) / 4, 256, 0, s, a);
         } else {
+            if (rnn) SPECV_LAUNCH("rnn_state", rnn_state<SPECV_F32>, R, 256, 0, s, a);
             const long items = long(R) * a.S;
             SPECV_LAUNCH("markov_logits", markov_logits_fma, (items + 3) / 4, 256, 0, s, a);
             SPECV_LAUNCH("markov_pick", markov_pick<SPECV_F32>, (R + 3) / 4, 256, 0, s, a);
         }
     }
     return SPECV_OK;
+}
+
+}  // namespace
+}  // namespace specv
+
+extern "C" size_t markov_draft_workspace_bytes(int R, int k, int V, int d_m) {
+    return specv::head_workspace_bytes(R, k, V, d_m, false);
+}
+
+extern "C" int markov_draft(int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
+                            const void* emb, const void* proj, const int32_t* prev_token,
+                            float temperature, const float* uniforms, int32_t* draft_tokens_out,
+                            void* draft_logits_out, void* ws, size_t ws_bytes, specv_stream stream) {
+    return specv::head_draft("markov_draft", mode, dtype, R, k, V, d_m, backbone_logits, emb, nullptr, proj,
+                             prev_token, temperature, uniforms, draft_tokens_out, draft_logits_out, nullptr, ws,
+                             ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t rnn_draft_workspace_bytes(int R, int k, int V, int d_m) {
+    return specv::head_workspace_bytes(R, k, V, d_m, true);
+}
+
+extern "C" int rnn_draft(int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
+                         const void* emb, const void* rec, const void* proj, const int32_t* prev_token,
+                         float temperature, const float* uniforms, int32_t* draft_tokens_out, void* draft_logits_out,
+                         void* state_out, void* ws, size_t ws_bytes, specv_stream stream) {
+    if (!rec) {
+        specv::clear_error();
+        return specv::fail(SPECV_EINVAL, "rnn_draft: NULL required pointer (rec)");
+    }
+    return specv::head_draft("rnn_draft", mode, dtype, R, k, V, d_m, backbone_logits, emb, rec, proj, prev_token,
+                             temperature, uniforms, draft_tokens_out, draft_logits_out, state_out, ws, ws_bytes,
+                             static_cast<hipStream_t>(stream));
 }

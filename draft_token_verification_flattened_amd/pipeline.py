@@ -25,7 +25,7 @@ class DeviceStep:
     every step, so that no step finds the previous step's logits in the 256 MB
     Infinity Cache."""
 
-    def __init__(self, w: Workload, device="cuda", copies: int = 1):
+    def __init__(self, w: Workload, device="cuda", copies: int = 1, head: str = "markov"):
         self.w = w
         self.device = device
         R, k, V = w.R, w.k, w.V
@@ -44,6 +44,8 @@ class DeviceStep:
         self.emb = dev(w.emb)
         self.proj = dev(w.proj)
         self.prev = dev(w.prev_token)
+        self.head = head                                 # "markov" or "rnn": the sequential module
+        self.rec = dev(w.rec) if head == "rnn" else None
         big = ("target", "draft_in", "backbone")
         self._copies = [{n: getattr(self, n) for n in big}]
         for _ in range(max(1, int(copies)) - 1):
@@ -63,7 +65,8 @@ class DeviceStep:
         if w.backbone is not None:
             self.draft_tokens = torch.zeros(R, k, **i32)
             self.draft_logits = torch.zeros(R, k, V, dtype=self.backbone.dtype, device=device)
-            self.ws_markov = B.workspace(B.markov_workspace_bytes(R, k, V, w.d_m), device)
+            nbytes = (B.rnn_workspace_bytes if head == "rnn" else B.markov_workspace_bytes)(R, k, V, w.d_m)
+            self.ws_markov = B.workspace(nbytes, device)
 
     # -- calls ---------------------------------------------------------------
     def schedule(self, max_len=None, stream=None):
@@ -75,8 +78,13 @@ class DeviceStep:
         B.spec_flatten(lengths, self.w.k, self.tags, self.cu_rows, self.n_rows, stream=stream)
 
     def markov(self, mode, stream=None):
-        B.markov_draft(mode, self.backbone, self.emb, self.proj, self.prev, self.w.tau, self.u_draft,
-                       self.draft_tokens, self.draft_logits, self.ws_markov, stream=stream)
+        """The drafter's sequential module: the Markov head, or the RNN head."""
+        if self.head == "rnn":
+            B.rnn_draft(mode, self.backbone, self.emb, self.rec, self.proj, self.prev, self.w.tau, self.u_draft,
+                        self.draft_tokens, self.draft_logits, self.ws_markov, stream=stream)
+        else:
+            B.markov_draft(mode, self.backbone, self.emb, self.proj, self.prev, self.w.tau, self.u_draft,
+                           self.draft_tokens, self.draft_logits, self.ws_markov, stream=stream)
 
     def drafts(self, mode):
         """(draft logits, draft tokens) the verifier uses for this workload and mode."""

@@ -282,6 +282,34 @@ int markov_draft(int mode, int dtype, int R, int k, int V, int d_m,
                  specv_stream stream);
 
 /* ------------------------------------------------------------------------ */
+/* rnn_draft                                                                 */
+/* ------------------------------------------------------------------------ */
+/*
+ * The RNN head: the pages' other light sequential module, which carries the
+ * whole prefix of the block in a recurrent state instead of the previous token
+ * alone ([P1] "1. 半自回归生成"; [P2] 3.1: more of the block's history, small
+ * gain, more cost). Read as, for i = 0..k-1, with h_{-1} = 0 and
+ * x_{-1} = prev_token[r]:
+ *   h_i      = round(tanh(emb[x_{i-1},:] + rec . h_{i-1}))   ((rec . h)_j = sum_q rec[j,q] h_q;
+ *              float32 accumulation; rounded to dtype: the operand of the products)
+ *   dl[r,i,:] = round(backbone[r,i,:] + h_i . proj^T)          (as markov_draft)
+ *   x_i       drawn as markov_draft draws.
+ *
+ * Arguments: as markov_draft, plus
+ *   rec       [d_m,d_m] dtype   the recurrence
+ *   state_out optional [R,k,d_m] dtype: the states h_i (NULL: kept in the
+ *             workspace); 16-byte aligned for bf16
+ *   d_m       <= 512 (bf16: a multiple of 32, <= 480)
+ *   ws        at least rnn_draft_workspace_bytes(R,k,V,d_m)
+ * Errors: as markov_draft.
+ */
+size_t rnn_draft_workspace_bytes(int R, int k, int V, int d_m);
+int rnn_draft(int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
+              const void* emb, const void* rec, const void* proj, const int32_t* prev_token,
+              float temperature, const float* uniforms, int32_t* draft_tokens_out,
+              void* draft_logits_out, void* state_out, void* ws, size_t ws_bytes, specv_stream stream);
+
+/* ------------------------------------------------------------------------ */
 /* spec_attention                                                            */
 /* ------------------------------------------------------------------------ */
 /*
@@ -349,7 +377,7 @@ int spec_attention(int R, int k, int Hq, int Hkv, int D, int page_size, int num_
 const char* specv_last_error(void);
 
 /* Read the workspace status word of the last spec_verify / markov_draft /
- * spec_attention call that used `ws` (synchronises `stream`). */
+ * rnn_draft / spec_attention call that used `ws` (synchronises `stream`). */
 int specv_read_status(const void* ws, specv_stream stream, uint32_t* status_out);
 
 /* Per-kernel timing with HIP events recorded on the launch stream around each
