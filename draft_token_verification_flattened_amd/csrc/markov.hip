@@ -103,6 +103,41 @@ __device__ __forceinline__ Part part_empty(int mode) {
     return p;
 }
 
+// Partial of the 16 rounded logits one lane holds for one request (vocabulary
+// n_x + e for x, e in 0..3; entries at or past V excluded): the maximum first,
+// then one exp2 per value (sampling), or the first argmax (greedy).
+__device__ __forceinline__ Part lane_part(int mode, const float (&v)[4][4], const int (&n)[4], int V, float c) {
+    Part p = part_empty(mode);
+    if (mode == SPECV_GREEDY) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n[x] + e < V && (v[x][e] > p.a || __float_as_int(p.b) == INT_MAX)) {
+                    p.a = v[x][e];
+                    p.b = __int_as_float(n[x] + e);
+                }
+        return p;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n[x] + e < V) mx = fmaxf(mx, v[x][e]);
+    if (mx == -INFINITY) return p;
+    const float m = mx * c;
+    float sum = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n[x] + e < V) sum += __builtin_amdgcn_exp2f(fmaf(v[x][e], c, -m));
+    p.a = m;
+    p.b = sum;
+    return p;
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -141,7 +176,8 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
         for (int x = 0; x < 4; ++x)
 #pragma unroll
             for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // gathered embedding rows of this lane's four request columns
+        // gathered operand rows (embedding of the previous token, or the RNN state)
+        // of this lane's four request columns
         const uint16_t* erow[4];
         bool mok[4];
 #pragma unroll
@@ -153,13 +189,33 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
             erow[b] = a.state ? static_cast<const uint16_t*>(a.state) + (long(mok[b] ? m : 0) * a.k + a.pos) * dm
                               : E + long(p) * dm;
         }
-        for (int k0 = 0; k0 < dm; k0 += 32) {
-            bf16x8 bfr[4], afr[4];
+        // the epilogue's backbone values, loaded now so that they arrive during the
+        // products: lane holds vocab n0 + 16x + 4g + {0..3} of request mb + 16b + l16
+        uint2 bkw[4][4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int m = mb + 16 * b + l16;
+            const long rowoff = (long(mok[b] ? m : 0) * a.k + a.pos) * long(a.V);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int n = n0 + 16 * x + 4 * g;
+                bkw[b][x] = make_uint2(0u, 0u);
+                if (VEC4 && mok[b] && n + 3 < a.V) bkw[b][x] = *reinterpret_cast<const uint2*>(bk + rowoff + n);
+            }
+        }
+        // products, with the next k-step's operand rows in flight during this one
+        auto load_b = [&](bf16x8 (&f)[4], int k0) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                uint4 v = mok[b] ? *reinterpret_cast<const uint4*>(erow[b] + k0 + 8 * g) : make_uint4(0, 0, 0, 0);
-                bfr[b] = __builtin_bit_cast(bf16x8, v);
+                const uint4 v = mok[b] ? *reinterpret_cast<const uint4*>(erow[b] + k0 + 8 * g) : make_uint4(0, 0, 0, 0);
+                f[b] = __builtin_bit_cast(bf16x8, v);
             }
+        };
+        bf16x8 bfr[4], bnx[4];
+        load_b(bfr, 0);
+        for (int k0 = 0; k0 < dm; k0 += 32) {
+            if (k0 + 32 < dm) load_b(bnx, k0 + 32);
+            bf16x8 afr[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 uint4 v = *reinterpret_cast<const uint4*>(lds_raw + (16 * x + l16) * row_bytes + (k0 + 8 * g) * 2);
@@ -170,8 +226,10 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
                     acc[x][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[x], bfr[b], acc[x][b], 0, 0, 0);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) bfr[b] = bnx[b];
         }
-        // epilogue: lane holds vocab n0 + 16x + 4g + {0..3} of request mb + 16b + l16
+        // epilogue
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int m = mb + 16 * b + l16;
@@ -183,9 +241,8 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
                     const int n = n0 + 16 * x + 4 * g;
                     float bkv[4];
                     if (VEC4 && n + 3 < a.V) {
-                        uint2 w = *reinterpret_cast<const uint2*>(bk + rowoff + n);
-                        bkv[0] = bf16_lo(w.x); bkv[1] = bf16_hi(w.x);
-                        bkv[2] = bf16_lo(w.y); bkv[3] = bf16_hi(w.y);
+                        bkv[0] = bf16_lo(bkw[b][x].x); bkv[1] = bf16_hi(bkw[b][x].x);
+                        bkv[2] = bf16_lo(bkw[b][x].y); bkv[3] = bf16_hi(bkw[b][x].y);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
@@ -216,6 +273,152 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
                 part_merge(a.mode, pp, q);
             }
             if (g == 0 && m < a.R) a.part[long(m) * a.S + blockIdx.x] = make_float2(pp.a, pp.b);
+        }
+    }
+}
+
+// bf16, d_m <= 256: one 512-thread workgroup per 256-entry vocabulary tile. The
+// tile's 256 rows of P sit in LDS (135 KB at d_m = 256); each wavefront keeps
+// its 64 requests' operand rows in registers (d_m / 2 VGPRs) and sweeps the
+// tile's four 64-entry sub-slices, so the gathered rows are read once per 256
+// vocabulary entries instead of once per 64, and a workgroup's logits are 512
+// contiguous bytes per row. Partials stay per 64-entry sub-slice.
+constexpr int kTileN = 256;
+constexpr int kTileThreads = 512;
+
+template <bool VEC4, int KS>
+__global__ __launch_bounds__(kTileThreads) void markov_logits_tile(MarkovArgs a) {
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.x * kTileN;
+    constexpr int dm = KS * 32;
+    if (a.pos == 0 && blockIdx.x == 0 && tid == 0) a.hdr->status = 0u;   // this kernel sets no bits
+    constexpr int row_bytes = dm * 2 + 16;
+    const uint16_t* P = static_cast<const uint16_t*>(a.proj);
+    const uint16_t* E = static_cast<const uint16_t*>(a.emb);
+    constexpr int vec_per_row = dm / 8;
+    for (int q = tid; q < kTileN * vec_per_row; q += kTileThreads) {
+        const int rr = q / vec_per_row, cc = q % vec_per_row;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (t0 + rr < a.V) v = reinterpret_cast<const uint4*>(P + long(t0 + rr) * dm)[cc];
+        *reinterpret_cast<uint4*>(lds_raw + rr * row_bytes + cc * 16) = v;
+    }
+    __syncthreads();
+
+    const uint16_t* bk = static_cast<const uint16_t*>(a.bk);
+    uint16_t* dl = static_cast<uint16_t*>(a.dl);
+    const int g = lane >> 4, l16 = lane & 15;
+    constexpr int KB = 2;                        // 16-request blocks per wavefront
+    for (int mb = wave * 16 * KB; mb < a.R; mb += (kTileThreads / 64) * 16 * KB) {
+        bool mok[KB];
+        bf16x8 bfr[KS][KB];                      // this lane's operand rows, all of d_m
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            const int m = mb + 16 * b + l16;
+            mok[b] = m < a.R;
+            int p = mok[b] ? prev_token(a, m) : 0;
+            if (p < 0 || p >= a.V) p = 0;             // reported by markov_pick
+            const uint16_t* erow = a.state
+                ? static_cast<const uint16_t*>(a.state) + (long(mok[b] ? m : 0) * a.k + a.pos) * dm
+                : E + long(p) * dm;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint4 v = mok[b] ? *reinterpret_cast<const uint4*>(erow + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
+                bfr[ks][b] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+        // backbone values of a sub-slice (VEC4 path), one sub-slice ahead of its epilogue
+        auto load_bk = [&](uint2 (&w)[KB][4], int n0) {
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                const int m = mb + 16 * b + l16;
+                const long rowoff = (long(mok[b] ? m : 0) * a.k + a.pos) * long(a.V);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int n = n0 + 16 * x + 4 * g;
+                    w[b][x] = make_uint2(0u, 0u);
+                    if (VEC4 && mok[b] && n + 3 < a.V) w[b][x] = *reinterpret_cast<const uint2*>(bk + rowoff + n);
+                }
+            }
+        };
+        uint2 bkc[KB][4], bkn[KB][4];
+        load_bk(bkc, t0);
+        for (int sub = 0; sub < kTileN / kSlice; ++sub) {
+            const int n0 = t0 + sub * kSlice;
+            if (n0 >= a.V) break;
+            if (sub + 1 < kTileN / kSlice) load_bk(bkn, n0 + kSlice);
+            f32x4 acc[4][KB];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < KB; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 afr[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(
+                        lds_raw + (sub * kSlice + 16 * x + l16) * row_bytes + (32 * ks + 8 * g) * 2);
+                    afr[x] = __builtin_bit_cast(bf16x8, v);
+                }
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int b = 0; b < KB; ++b)
+                        acc[x][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[x], bfr[ks][b], acc[x][b], 0, 0, 0);
+            }
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                const int m = mb + 16 * b + l16;
+                Part pp = part_empty(a.mode);
+                if (m < a.R) {
+                    const long rowoff = (long(m) * a.k + a.pos) * long(a.V);
+                    float vals[4][4];
+                    int ns[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int n = n0 + 16 * x + 4 * g;
+                        ns[x] = n;
+                        float bkv[4];
+                        if (VEC4 && n + 3 < a.V) {
+                            const uint2 w = bkc[b][x];
+                            bkv[0] = bf16_lo(w.x); bkv[1] = bf16_hi(w.x);
+                            bkv[2] = bf16_lo(w.y); bkv[3] = bf16_hi(w.y);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                bkv[e] = n + e < a.V ? __uint_as_float(uint32_t(bk[rowoff + n + e]) << 16) : 0.f;
+                        }
+                        uint32_t hb[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            hb[e] = f32_to_bf16_rne(acc[x][b][e] + bkv[e]);
+                            vals[x][e] = __uint_as_float(hb[e] << 16);
+                        }
+                        if (VEC4 && n + 3 < a.V) {
+                            *reinterpret_cast<uint2*>(dl + rowoff + n) =
+                                make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < a.V) dl[rowoff + n + e] = uint16_t(hb[e]);
+                        }
+                    }
+                    pp = lane_part(a.mode, vals, ns, a.V, a.c);
+                }
+#pragma unroll
+                for (int o = 16; o <= 32; o <<= 1) {
+                    Part q;
+                    q.a = __shfl_xor(pp.a, o, 64);
+                    q.b = __shfl_xor(pp.b, o, 64);
+                    part_merge(a.mode, pp, q);
+                }
+                if (g == 0 && m < a.R) a.part[long(m) * a.S + n0 / kSlice] = make_float2(pp.a, pp.b);
+            }
+#pragma unroll
+            for (int b = 0; b < KB; ++b)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) bkc[b][x] = bkn[b][x];
         }
     }
 }
@@ -388,13 +591,28 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
     const bool vec4 = (V % 4) == 0 && (reinterpret_cast<uintptr_t>(backbone_logits) & 7u) == 0 &&
                       (reinterpret_cast<uintptr_t>(draft_logits_out) & 7u) == 0;
     const size_t lds = size_t(kSlice) * size_t(d_m * 2 + 16);
+    if (dtype == SPECV_BF16 && d_m == 256) {
+        const int tlds = int(size_t(kTileN) * size_t(d_m * 2 + 16));
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(markov_logits_tile<true, 8>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, tlds) != hipSuccess ||
+            hipFuncSetAttribute(reinterpret_cast<const void*>(markov_logits_tile<false, 8>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, tlds) != hipSuccess)
+            return fail(SPECV_EDEVICE, "%s: cannot raise the LDS limit of the projection kernel", fn);
+    }
     // The status word is cleared by position 0's logits kernel (which sets no
     // bits) and set by position 0's pick kernel, which checks prev_token.
     for (int i = 0; i < k; ++i) {
         a.pos = i;
         if (dtype == SPECV_BF16) {
             if (rnn) SPECV_LAUNCH("rnn_state", rnn_state<SPECV_BF16>, R, 256, 0, s, a);
-            if (vec4)
+            if (d_m == 256) {
+                const int tiles = (V + kTileN - 1) / kTileN;
+                const size_t tlds = size_t(kTileN) * size_t(d_m * 2 + 16);
+                if (vec4)
+                    SPECV_LAUNCH("markov_logits", (markov_logits_tile<true, 8>), tiles, kTileThreads, tlds, s, a);
+                else
+                    SPECV_LAUNCH("markov_logits", (markov_logits_tile<false, 8>), tiles, kTileThreads, tlds, s, a);
+            } else if (vec4)
                 SPECV_LAUNCH("markov_logits", markov_logits_mfma<true>, a.S, 256, lds, s, a);
             else
                 SPECV_LAUNCH("markov_logits", markov_logits_mfma<false>, a.S, 256, lds, s, a);
