@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified draft tokens/s at V=151936, k=5, 256 req; achieved HBM GB/s % peak"
 HBM_PEAK = 8.0e12
+MFMA_BF16_PEAK = 2.5e15   # dense bf16 MFMA, MI355X
 DOMINANT = "verify_stream"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_stream_c2_traffic.txt")
 
@@ -65,29 +66,52 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash() -> str:
+def source_hash(files=("common.h", "verify.hip")) -> str:
     h = hashlib.sha256()
-    for f in ("common.h", "verify.hip"):
+    for f in files:
         h.update(open(os.path.join(ROOT, "draft_token_verification_flattened_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic():
+# Counter summaries (profiles/) per dominant kernel: the file, the sources its
+# kernel is built from, and the workload the counters were taken on.
+TRAFFIC = {
+    "verify_stream": (os.path.join(ROOT, "profiles", "verify_stream_c2_traffic.txt"), ("common.h", "verify.hip")),
+    "markov_logits": (os.path.join(ROOT, "profiles", "markov_logits_c4_traffic.txt"), ("common.h", "markov.hip")),
+}
+
+
+def workload_key(args, max_len) -> str:
+    return f"{args.config} {args.mode} max_len={max_len} head={args.head}"
+
+
+def committed_traffic(kernel, wkey):
     """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, if it was taken on the current kernel source."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+    summary, if it was taken on the current kernel source and on this workload."""
+    path, files = TRAFFIC[kernel]
+    if not os.path.exists(path):
         return None, None
     vals = {}
-    for line in open(PROFILE_TRAFFIC):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_hash") != source_hash():
+    if vals.get("source_hash") != source_hash(files) or vals.get("workload") != wkey:
         return None, vals.get("source_hash")
     try:
         return float(vals["hbm_bytes_per_launch"]), vals.get("source_hash")
     except (KeyError, ValueError):
         return None, None
+
+
+def markov_bytes_flops(w):
+    """Per position: P read once (2 d_m V), the gathered operand rows
+    (2 R d_m), the backbone read and the draft logits written (2 R V each);
+    2 R d_m V flops."""
+    es = 2 if w.dtype == "bf16" else 4
+    d_m = w.emb.shape[1]
+    nbytes = es * (d_m * w.V + w.R * d_m + 2 * w.R * w.V)
+    return nbytes, 2.0 * w.R * d_m * w.V
 
 
 def algorithmic_bytes(w, mode, N, R):
@@ -474,19 +498,37 @@ def main():
     if args.variants or args.lagged:
         lagged = run_lagged(d, w, mode_c, args.steps, args.warmup, B, torch, args.copies)
 
-    traffic, thash = committed_traffic()
-    dom = main_res["kernels"].get(DOMINANT, {})
+    kern = main_res["kernels"]
+    ver = kern.get("verify_stream", {})
+    mk = kern.get("markov_logits")
     roofline = {
         "bound": "hbm",
         "achieved": main_res["dominant_gbps"],
         "peak": HBM_PEAK / 1e9,
         "unit": "GB/s",
         "frac": main_res["dominant_frac"],
-        "traffic": traffic,
-        "kernel": DOMINANT,
-        "avg_launch_us": dom.get("avg_us"),
+        "traffic": committed_traffic("verify_stream", workload_key(args, max_len))[0],
+        "kernel": "verify_stream",
+        "avg_launch_us": ver.get("avg_us"),
         "algorithmic_bytes_per_launch": main_res["algorithmic_bytes"],
     }
+    markov_roof = None
+    if mk and w.dtype == "bf16":
+        # the Markov projection: HBM-bound (about 102 flop per byte at d_m = 256,
+        # below the bf16 ridge of 2.5e15 / 8e12 = 312), MFMA use reported beside it
+        nb, fl = markov_bytes_flops(w)
+        t = mk["avg_us"] * 1e-6
+        markov_roof = {
+            "bound": "hbm", "achieved": nb / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": nb / t / HBM_PEAK,
+            "traffic": committed_traffic("markov_logits", workload_key(args, max_len))[0],
+            "kernel": "markov_logits", "avg_launch_us": mk["avg_us"], "algorithmic_bytes_per_launch": nb,
+            "mfma": {"achieved": fl / t / 1e12, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                     "frac": fl / t / MFMA_BF16_PEAK, "flops_per_launch": fl},
+        }
+        # the dominant kernel of the step is the one with the larger share of its time
+        if mk["avg_us"] * mk["launches_per_step"] > ver.get("avg_us", 0.0) * ver.get("launches_per_step", 0.0):
+            roofline, markov_roof = markov_roof, roofline
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, args.mode, max_len)
@@ -512,6 +554,7 @@ def main():
             "input_copies": args.copies,
         },
         "roofline": roofline,
+        "roofline_other": markov_roof,
         "cpu_baseline": cpu,
         "verify_only": {"us_per_step": main_res["verify_us"], "tokens_per_s": main_res["verify_tokens_per_s"]},
         "kernels": main_res["kernels"],

@@ -16,8 +16,10 @@
 //       stores the draft logits and emits per-(request, slice) softmax or
 //       argmax partials of the rounded values.
 //   markov_logits_fma (fp32)   the same with one lane per output and plain FMA.
-//   markov_pick                one wavefront per request: merges the partials;
-//       greedy argmax, or the two-level inverse-CDF draw over softmax(dl / tau).
+//   markov_pick_wg             one workgroup per request: merges the partials;
+//       greedy argmax, or the two-level inverse-CDF draw over softmax(dl / tau)
+//       (markov_pick, one wavefront per request, for rows of more than 4096
+//       slices).
 //
 // rnn_draft: the RNN head, the pages' other sequential module, which carries
 // the whole prefix of the block in a recurrent state (same sections). Read as
@@ -277,149 +279,218 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
     }
 }
 
-// bf16, d_m <= 256: one 512-thread workgroup per 256-entry vocabulary tile. The
-// tile's 256 rows of P sit in LDS (135 KB at d_m = 256); each wavefront keeps
-// its 64 requests' operand rows in registers (d_m / 2 VGPRs) and sweeps the
-// tile's four 64-entry sub-slices, so the gathered rows are read once per 256
-// vocabulary entries instead of once per 64, and a workgroup's logits are 512
-// contiguous bytes per row. Partials stay per 64-entry sub-slice.
-constexpr int kTileN = 256;
-constexpr int kTileThreads = 512;
+// bf16, d_m = 32 * KS (256 at KS = 8): a persistent grid of 512-thread
+// workgroups, one per compute unit. Workgroup (range, group) owns a contiguous
+// range of 64-entry vocabulary slices and a group of 256 requests; the groups
+// of one range are launched on the same XCD (blockIdx modulo 8), so the second
+// group's reads of P find the first group's in that XCD's L2. Each wavefront
+// keeps its 32 requests' operand rows in registers for the whole launch and
+// sweeps the range slice by slice:
+//   - P slices go through two LDS buffers: the next slice's rows are loaded
+//     into registers during the current slice and written to the other buffer
+//     after it, one barrier per slice. A slice's rows are stored permuted so
+//     that the MFMA output puts 16 consecutive vocabulary entries of one
+//     request in one lane: vocabulary entry v = 16q + 4x + r of the slice is
+//     row 4q + r of MFMA tile x, at LDS row 16x + 4q + r (conflict-free reads);
+//   - backbone values come in 16-byte loads one slice ahead of their epilogue;
+//   - the epilogue adds them, rounds to bf16 with the hardware conversion
+//     (nearest-even), stores 2 x 16 bytes per lane (4 lanes cover 128
+//     contiguous bytes of a request's row) and emits the per-(request, slice)
+//     partials.
+constexpr int kRunThreads = 512;             // 8 wavefronts
+constexpr int kRunGroup = 256;               // requests per workgroup: 8 x 32
 
-template <bool VEC4, int KS>
-__global__ __launch_bounds__(kTileThreads) void markov_logits_tile(MarkovArgs a) {
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// grid of the persistent projection for R requests and S slices: nr ranges
+// (a multiple of 8) times ng request groups
+__host__ __device__ inline void run_grid(int R, int S, int& ng, int& nr) {
+    ng = (R + kRunGroup - 1) / kRunGroup;
+    nr = (256 / ng) / 8 * 8;
+    if (nr < 8) nr = 8;
+    (void)S;
+}
+
+template <bool VEC, int KS>
+__global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, int ng, int nr) {
     extern __shared__ __align__(16) unsigned char lds_raw[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int t0 = blockIdx.x * kTileN;
     constexpr int dm = KS * 32;
+    constexpr int row_bytes = dm * 2 + 16;             // padded LDS row (bank spread)
+    constexpr int buf_bytes = kSlice * row_bytes;
+    constexpr int vpr = dm / 8;                        // 16-byte vectors per P row
+    constexpr int PT = kSlice * vpr / kRunThreads;     // P vectors per thread per slice
+    static_assert(PT * kRunThreads == kSlice * vpr, "P slice must split evenly over the threads");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (a.pos == 0 && blockIdx.x == 0 && tid == 0) a.hdr->status = 0u;   // this kernel sets no bits
-    constexpr int row_bytes = dm * 2 + 16;
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int range = (idx / ng) * 8 + xcd, grp = idx % ng;
+    const int S = a.S, V = a.V;
+    const int s_beg = int((long(range) * S) / nr), s_end = int((long(range + 1) * S) / nr);
+    if (s_beg >= s_end) return;
+
     const uint16_t* P = static_cast<const uint16_t*>(a.proj);
     const uint16_t* E = static_cast<const uint16_t*>(a.emb);
-    constexpr int vec_per_row = dm / 8;
-    for (int q = tid; q < kTileN * vec_per_row; q += kTileThreads) {
-        const int rr = q / vec_per_row, cc = q % vec_per_row;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (t0 + rr < a.V) v = reinterpret_cast<const uint4*>(P + long(t0 + rr) * dm)[cc];
-        *reinterpret_cast<uint4*>(lds_raw + rr * row_bytes + cc * 16) = v;
-    }
-    __syncthreads();
-
     const uint16_t* bk = static_cast<const uint16_t*>(a.bk);
     uint16_t* dl = static_cast<uint16_t*>(a.dl);
     const int g = lane >> 4, l16 = lane & 15;
-    constexpr int KB = 2;                        // 16-request blocks per wavefront
-    for (int mb = wave * 16 * KB; mb < a.R; mb += (kTileThreads / 64) * 16 * KB) {
-        bool mok[KB];
-        bf16x8 bfr[KS][KB];                      // this lane's operand rows, all of d_m
+
+    // P slice s: thread vectors q = tid + j * threads (row q / vpr, vector q % vpr)
+    auto load_p = [&](uint4 (&pr)[PT], int s) {
 #pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            const int m = mb + 16 * b + l16;
-            mok[b] = m < a.R;
-            int p = mok[b] ? prev_token(a, m) : 0;
-            if (p < 0 || p >= a.V) p = 0;             // reported by markov_pick
-            const uint16_t* erow = a.state
-                ? static_cast<const uint16_t*>(a.state) + (long(mok[b] ? m : 0) * a.k + a.pos) * dm
-                : E + long(p) * dm;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const uint4 v = mok[b] ? *reinterpret_cast<const uint4*>(erow + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
-                bfr[ks][b] = __builtin_bit_cast(bf16x8, v);
-            }
+        for (int j = 0; j < PT; ++j) {
+            const int q = tid + j * kRunThreads, row = q / vpr, cc = q % vpr;
+            const int v = s * kSlice + row;
+            pr[j] = v < V ? *reinterpret_cast<const uint4*>(P + long(v) * dm + cc * 8) : make_uint4(0, 0, 0, 0);
         }
-        // backbone values of a sub-slice (VEC4 path), one sub-slice ahead of its epilogue
-        auto load_bk = [&](uint2 (&w)[KB][4], int n0) {
+    };
+    auto store_p = [&](const uint4 (&pr)[PT], int buf) {
 #pragma unroll
-            for (int b = 0; b < KB; ++b) {
-                const int m = mb + 16 * b + l16;
-                const long rowoff = (long(mok[b] ? m : 0) * a.k + a.pos) * long(a.V);
+        for (int j = 0; j < PT; ++j) {
+            const int q = tid + j * kRunThreads, row = q / vpr, cc = q % vpr;
+            const int L = 16 * ((row >> 2) & 3) + 4 * (row >> 4) + (row & 3);
+            *reinterpret_cast<uint4*>(lds_raw + buf * buf_bytes + L * row_bytes + cc * 16) = pr[j];
+        }
+    };
+
+    // this wavefront's requests and their operand rows
+    int mreq[2];
+    bool mok[2];
+    bf16x8 bfr[KS][2];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int n = n0 + 16 * x + 4 * g;
-                    w[b][x] = make_uint2(0u, 0u);
-                    if (VEC4 && mok[b] && n + 3 < a.V) w[b][x] = *reinterpret_cast<const uint2*>(bk + rowoff + n);
-                }
+    for (int b = 0; b < 2; ++b) {
+        const int m = grp * kRunGroup + wave * 32 + 16 * b + l16;
+        mreq[b] = m;
+        mok[b] = m < a.R;
+        int p = mok[b] ? prev_token(a, m) : 0;
+        if (p < 0 || p >= V) p = 0;                    // reported by markov_pick
+        const uint16_t* erow = a.state
+            ? static_cast<const uint16_t*>(a.state) + (long(mok[b] ? m : 0) * a.k + a.pos) * dm
+            : E + long(p) * dm;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint4 v = mok[b] ? *reinterpret_cast<const uint4*>(erow + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
+            bfr[ks][b] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    long rowoff[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) rowoff[b] = (long(mok[b] ? mreq[b] : 0) * a.k + a.pos) * long(V);
+
+    // backbone values of slice s for this lane: entries 16g .. 16g + 15 of its two requests
+    auto load_bk = [&](uint4 (&w)[2][2], int s) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int n = s * kSlice + 16 * g + 8 * h;
+                w[b][h] = (VEC && mok[b] && n < V) ? *reinterpret_cast<const uint4*>(bk + rowoff[b] + n)
+                                                   : make_uint4(0, 0, 0, 0);
             }
-        };
-        uint2 bkc[KB][4], bkn[KB][4];
-        load_bk(bkc, t0);
-        for (int sub = 0; sub < kTileN / kSlice; ++sub) {
-            const int n0 = t0 + sub * kSlice;
-            if (n0 >= a.V) break;
-            if (sub + 1 < kTileN / kSlice) load_bk(bkn, n0 + kSlice);
-            f32x4 acc[4][KB];
+    };
+
+    uint4 pr[PT];
+    load_p(pr, s_beg);
+    store_p(pr, 0);
+    if (s_beg + 1 < s_end) load_p(pr, s_beg + 1);
+    uint4 bkc[2][2], bkn[2][2];
+    load_bk(bkc, s_beg);
+    __syncthreads();
+
+    for (int s = s_beg, it = 0; s < s_end; ++s, ++it) {
+        const int cur = it & 1;
+        if (s + 1 < s_end) load_bk(bkn, s + 1);
+        f32x4 acc[4][2];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) acc[x][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const unsigned char* buf = lds_raw + cur * buf_bytes;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 afr[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                afr[x] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const uint4*>(buf + (16 * x + l16) * row_bytes + (32 * ks + 8 * g) * 2));
 #pragma unroll
             for (int x = 0; x < 4; ++x)
 #pragma unroll
-                for (int y = 0; y < KB; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int b = 0; b < 2; ++b)
+                    acc[x][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[x], bfr[ks][b], acc[x][b], 0, 0, 0);
+        }
+        // epilogue: lane holds entries n16 + 4x + e (x, e < 4) of request mreq[b]
+        const int n16 = s * kSlice + 16 * g;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                bf16x8 afr[4];
+        for (int b = 0; b < 2; ++b) {
+            Part pp = part_empty(a.mode);
+            if (mok[b]) {
+                float bkv[16];
+                if constexpr (VEC) {
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(
-                        lds_raw + (sub * kSlice + 16 * x + l16) * row_bytes + (32 * ks + 8 * g) * 2);
-                    afr[x] = __builtin_bit_cast(bf16x8, v);
+                    for (int h = 0; h < 2; ++h) {
+                        const uint4 w = bkc[b][h];
+                        bkv[8 * h + 0] = bf16_lo(w.x); bkv[8 * h + 1] = bf16_hi(w.x);
+                        bkv[8 * h + 2] = bf16_lo(w.y); bkv[8 * h + 3] = bf16_hi(w.y);
+                        bkv[8 * h + 4] = bf16_lo(w.z); bkv[8 * h + 5] = bf16_hi(w.z);
+                        bkv[8 * h + 6] = bf16_lo(w.w); bkv[8 * h + 7] = bf16_hi(w.w);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        bkv[j] = n16 + j < V ? __uint_as_float(uint32_t(bk[rowoff[b] + n16 + j]) << 16) : 0.f;
                 }
+                uint32_t wd[8];
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
 #pragma unroll
-                    for (int b = 0; b < KB; ++b)
-                        acc[x][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[x], bfr[ks][b], acc[x][b], 0, 0, 0);
+                    for (int e = 0; e < 4; e += 2)
+                        wd[2 * x + e / 2] = pack_bf16_rne(acc[x][b][e] + bkv[4 * x + e], acc[x][b][e + 1] + bkv[4 * x + e + 1]);
+                float vals[4][4];
+                int ns[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    ns[x] = n16 + 4 * x;
+                    vals[x][0] = bf16_lo(wd[2 * x]);     vals[x][1] = bf16_hi(wd[2 * x]);
+                    vals[x][2] = bf16_lo(wd[2 * x + 1]); vals[x][3] = bf16_hi(wd[2 * x + 1]);
+                }
+                if (VEC && n16 + 16 <= V) {
+                    uint4* o = reinterpret_cast<uint4*>(dl + rowoff[b] + n16);
+                    o[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                    o[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+                } else if (VEC && n16 + 8 <= V) {
+                    *reinterpret_cast<uint4*>(dl + rowoff[b] + n16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                } else if (!VEC) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (n16 + j < V) dl[rowoff[b] + n16 + j] = uint16_t(wd[j / 2] >> (16 * (j & 1)));
+                }
+                pp = lane_part(a.mode, vals, ns, V, a.c);
             }
 #pragma unroll
-            for (int b = 0; b < KB; ++b) {
-                const int m = mb + 16 * b + l16;
-                Part pp = part_empty(a.mode);
-                if (m < a.R) {
-                    const long rowoff = (long(m) * a.k + a.pos) * long(a.V);
-                    float vals[4][4];
-                    int ns[4];
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const int n = n0 + 16 * x + 4 * g;
-                        ns[x] = n;
-                        float bkv[4];
-                        if (VEC4 && n + 3 < a.V) {
-                            const uint2 w = bkc[b][x];
-                            bkv[0] = bf16_lo(w.x); bkv[1] = bf16_hi(w.x);
-                            bkv[2] = bf16_lo(w.y); bkv[3] = bf16_hi(w.y);
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                bkv[e] = n + e < a.V ? __uint_as_float(uint32_t(bk[rowoff + n + e]) << 16) : 0.f;
-                        }
-                        uint32_t hb[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            hb[e] = f32_to_bf16_rne(acc[x][b][e] + bkv[e]);
-                            vals[x][e] = __uint_as_float(hb[e] << 16);
-                        }
-                        if (VEC4 && n + 3 < a.V) {
-                            *reinterpret_cast<uint2*>(dl + rowoff + n) =
-                                make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (n + e < a.V) dl[rowoff + n + e] = uint16_t(hb[e]);
-                        }
-                    }
-                    pp = lane_part(a.mode, vals, ns, a.V, a.c);
-                }
-#pragma unroll
-                for (int o = 16; o <= 32; o <<= 1) {
-                    Part q;
-                    q.a = __shfl_xor(pp.a, o, 64);
-                    q.b = __shfl_xor(pp.b, o, 64);
-                    part_merge(a.mode, pp, q);
-                }
-                if (g == 0 && m < a.R) a.part[long(m) * a.S + n0 / kSlice] = make_float2(pp.a, pp.b);
+            for (int o = 16; o <= 32; o <<= 1) {
+                Part q;
+                q.a = __shfl_xor(pp.a, o, 64);
+                q.b = __shfl_xor(pp.b, o, 64);
+                part_merge(a.mode, pp, q);
             }
-#pragma unroll
-            for (int b = 0; b < KB; ++b)
-#pragma unroll
-                for (int x = 0; x < 4; ++x) bkc[b][x] = bkn[b][x];
+            if (g == 0 && mok[b]) a.part[long(mreq[b]) * S + s] = make_float2(pp.a, pp.b);
         }
+        // the slice after next: the other buffer was last read before the previous barrier
+        if (s + 1 < s_end) {
+            store_p(pr, cur ^ 1);
+            if (s + 2 < s_end) load_p(pr, s + 2);
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) bkc[b][h] = bkn[b][h];
+        __syncthreads();
     }
 }
 
@@ -534,6 +605,127 @@ __global__ __launch_bounds__(256) void markov_pick(MarkovArgs a) {
     if (lane == 0) a.tokens[long(m) * a.k + a.pos] = y;
 }
 
+// The same draw by one 256-thread workgroup per request, for rows of at most
+// kPickThreads * kPickPer slices. Thread t holds the contiguous slices
+// [t J, t J + J), J = ceil(S / kPickThreads), in registers: one round trip for
+// all of a row's partials, a workgroup merge, then (sampling) the slice masses
+// exp2(M_s - M) S_s in slice order, a workgroup exclusive scan of the threads'
+// sums, each thread's walk over its own slices for the first running sum above
+// u Z, and one wavefront's scan of the chosen 64-entry slice.
+constexpr int kPickThreads = 256;
+constexpr int kPickPer = 16;
+
+template <int DT>
+__global__ __launch_bounds__(kPickThreads) void markov_pick_wg(MarkovArgs a) {
+    using LT = Logit<DT>;
+    using T = typename LT::T;
+    constexpr int NW = kPickThreads / kWave;
+    __shared__ float sh_a[NW], sh_b[NW];
+    __shared__ int sh_i[NW];
+    __shared__ float sh_base[NW];
+    __shared__ int sh_last[NW];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int m = blockIdx.x;
+    if (a.pos == 0 && tid == 0 && (a.prev[m] < 0 || a.prev[m] >= a.V)) set_status(a.hdr, SPECV_STATUS_BAD_TOKEN);
+    const int S = a.S;
+    const int J = (S + kPickThreads - 1) / kPickThreads;
+    const int beg = tid * J, end = min(S, beg + J);
+    const float2* pr = a.part + long(m) * S;
+    float2 q[kPickPer];
+#pragma unroll
+    for (int j = 0; j < kPickPer; ++j)
+        q[j] = (j < J && beg + j < end) ? pr[beg + j] : make_float2(-INFINITY, __int_as_float(INT_MAX));
+    Part tot = part_empty(a.mode);
+#pragma unroll
+    for (int j = 0; j < kPickPer; ++j) {
+        if (!(j < J && beg + j < end)) continue;
+        Part p;
+        p.a = q[j].x;
+        p.b = q[j].y;
+        part_merge(a.mode, tot, p);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        Part p;
+        p.a = __shfl_xor(tot.a, o, 64);
+        p.b = __shfl_xor(tot.b, o, 64);
+        part_merge(a.mode, tot, p);
+    }
+    if (lane == 0) { sh_a[w] = tot.a; sh_b[w] = tot.b; }
+    __syncthreads();
+    tot = part_empty(a.mode);
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        Part p;
+        p.a = sh_a[v];
+        p.b = sh_b[v];
+        part_merge(a.mode, tot, p);
+    }
+    if (a.mode == SPECV_GREEDY) {
+        if (tid == 0) a.tokens[long(m) * a.k + a.pos] = __float_as_int(tot.b);
+        return;
+    }
+    const float M = tot.a;
+    const float thr = a.uniforms[long(m) * a.k + a.pos] * tot.b;
+    float wm[kPickPer];
+    float lsum = 0.f;
+    int lastpos = -1;
+#pragma unroll
+    for (int j = 0; j < kPickPer; ++j) {
+        const bool in = j < J && beg + j < end;
+        wm[j] = (in && q[j].x != -INFINITY) ? q[j].y * exp2f(q[j].x - M) : 0.f;
+        lsum += wm[j];
+        if (wm[j] > 0.f) lastpos = beg + j;
+    }
+    // workgroup exclusive scan of the threads' sums (slice order = thread order)
+    const float incl = wave_incl_scan_f32(lsum);
+    __syncthreads();                                  // sh_a / sh_b reads are done
+    if (lane == 63) sh_a[w] = incl;
+    __syncthreads();
+    float before = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v)
+        if (v < w) before += sh_a[v];
+    float cum = before + (incl - lsum);
+    int hit = INT_MAX;
+    float base = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPickPer; ++j) {
+        const bool in = j < J && beg + j < end;
+        const float prev_cum = cum;
+        cum += wm[j];
+        if (hit == INT_MAX && in && cum > thr) { hit = beg + j; base = prev_cum; }
+    }
+    // first crossing over the workgroup, with its running sum before the slice
+    const int whit = wave_min_int(hit);
+    const int wlast = -wave_min_int(-lastpos);
+    if (hit == whit && whit != INT_MAX) { sh_i[w] = whit; sh_base[w] = base; }
+    if (lane == 0 && whit == INT_MAX) sh_i[w] = INT_MAX;
+    if (lane == 0) sh_last[w] = wlast;
+    __syncthreads();
+    if (w != 0) return;
+    int sel = INT_MAX, lastall = -1;
+    float sbase = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        if (sel == INT_MAX && sh_i[v] != INT_MAX) { sel = sh_i[v]; sbase = sh_base[v]; }
+        lastall = max(lastall, sh_last[v]);
+    }
+    if (sel == INT_MAX) {                             // rounding left no crossing: last slice with mass
+        sel = lastall < 0 ? 0 : lastall;
+        sbase = -INFINITY;
+    }
+    // the chosen slice: one entry per lane
+    const T* row = static_cast<const T*>(a.dl) + (long(m) * a.k + a.pos) * long(a.V);
+    const int e = sel * kSlice + lane;
+    const float we = e < a.V ? exp2f(fmaf(LT::load1(row + e), a.c, -M)) : 0.f;
+    const float run = sbase + wave_incl_scan_f32(we);
+    const int ehit = wave_min_int((e < a.V && run > thr) ? e : INT_MAX);
+    const int elast = -wave_min_int((we > 0.f) ? -e : 1);
+    const int y = ehit != INT_MAX ? ehit : (elast >= 0 ? elast : sel * kSlice);
+    if (lane == 0) a.tokens[long(m) * a.k + a.pos] = y;
+}
+
 }  // namespace specv
 
 namespace specv {
@@ -590,15 +782,20 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
         a.state = state_out ? state_out : static_cast<char*>(ws) + head_workspace_bytes(R, k, V, d_m, false);
     const bool vec4 = (V % 4) == 0 && (reinterpret_cast<uintptr_t>(backbone_logits) & 7u) == 0 &&
                       (reinterpret_cast<uintptr_t>(draft_logits_out) & 7u) == 0;
+    const bool vec8 = (V % 8) == 0 && (reinterpret_cast<uintptr_t>(backbone_logits) & 15u) == 0 &&
+                      (reinterpret_cast<uintptr_t>(draft_logits_out) & 15u) == 0;
     const size_t lds = size_t(kSlice) * size_t(d_m * 2 + 16);
+    const int run_lds = 2 * kSlice * (d_m * 2 + 16);
     if (dtype == SPECV_BF16 && d_m == 256) {
-        const int tlds = int(size_t(kTileN) * size_t(d_m * 2 + 16));
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(markov_logits_tile<true, 8>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, tlds) != hipSuccess ||
-            hipFuncSetAttribute(reinterpret_cast<const void*>(markov_logits_tile<false, 8>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, tlds) != hipSuccess)
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(markov_logits_run<true, 8>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, run_lds) != hipSuccess ||
+            hipFuncSetAttribute(reinterpret_cast<const void*>(markov_logits_run<false, 8>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, run_lds) != hipSuccess)
             return fail(SPECV_EDEVICE, "%s: cannot raise the LDS limit of the projection kernel", fn);
     }
+    int run_ng = 1, run_nr = 8;
+    run_grid(R, a.S, run_ng, run_nr);
+    const bool pick_wg = a.S <= kPickThreads * kPickPer;   // else one wavefront per request
     // The status word is cleared by position 0's logits kernel (which sets no
     // bits) and set by position 0's pick kernel, which checks prev_token.
     for (int i = 0; i < k; ++i) {
@@ -606,22 +803,28 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
         if (dtype == SPECV_BF16) {
             if (rnn) SPECV_LAUNCH("rnn_state", rnn_state<SPECV_BF16>, R, 256, 0, s, a);
             if (d_m == 256) {
-                const int tiles = (V + kTileN - 1) / kTileN;
-                const size_t tlds = size_t(kTileN) * size_t(d_m * 2 + 16);
-                if (vec4)
-                    SPECV_LAUNCH("markov_logits", (markov_logits_tile<true, 8>), tiles, kTileThreads, tlds, s, a);
+                if (vec8)
+                    SPECV_LAUNCH("markov_logits", (markov_logits_run<true, 8>), run_ng * run_nr, kRunThreads,
+                                 size_t(run_lds), s, a, run_ng, run_nr);
                 else
-                    SPECV_LAUNCH("markov_logits", (markov_logits_tile<false, 8>), tiles, kTileThreads, tlds, s, a);
+                    SPECV_LAUNCH("markov_logits", (markov_logits_run<false, 8>), run_ng * run_nr, kRunThreads,
+                                 size_t(run_lds), s, a, run_ng, run_nr);
             } else if (vec4)
                 SPECV_LAUNCH("markov_logits", markov_logits_mfma<true>, a.S, 256, lds, s, a);
             else
                 SPECV_LAUNCH("markov_logits", markov_logits_mfma<false>, a.S, 256, lds, s, a);
-            SPECV_LAUNCH("markov_pick", markov_pick<SPECV_BF16>, (R + 3) / 4, 256, 0, s, a);
+            if (pick_wg)
+                SPECV_LAUNCH("markov_pick", markov_pick_wg<SPECV_BF16>, R, kPickThreads, 0, s, a);
+            else
+                SPECV_LAUNCH("markov_pick", markov_pick<SPECV_BF16>, (R + 3) / 4, 256, 0, s, a);
         } else {
             if (rnn) SPECV_LAUNCH("rnn_state", rnn_state<SPECV_F32>, R, 256, 0, s, a);
             const long items = long(R) * a.S;
             SPECV_LAUNCH("markov_logits", markov_logits_fma, (items + 3) / 4, 256, 0, s, a);
-            SPECV_LAUNCH("markov_pick", markov_pick<SPECV_F32>, (R + 3) / 4, 256, 0, s, a);
+            if (pick_wg)
+                SPECV_LAUNCH("markov_pick", markov_pick_wg<SPECV_F32>, R, kPickThreads, 0, s, a);
+            else
+                SPECV_LAUNCH("markov_pick", markov_pick<SPECV_F32>, (R + 3) / 4, 256, 0, s, a);
         }
     }
     return SPECV_OK;

@@ -493,6 +493,10 @@ MARKOV_SMALL = [
     (70, 3, 1000, 64, "sample"),      # partial request block, V % 64 != 0
     (130, 2, 1001, 96, "greedy"),     # ragged V: scalar epilogue
     (64, 5, 5000, 256, "sample"),
+    (600, 2, 3000, 256, "greedy"),    # three request groups of the persistent projection
+    (40, 2, 2001, 256, "sample"),     # V % 8 != 0: scalar backbone loads and stores
+    (3, 2, 300000, 32, "sample"),     # more than 4096 slices: one wavefront per request picks
+    (2, 2, 270000, 32, "greedy"),
 ]
 
 
