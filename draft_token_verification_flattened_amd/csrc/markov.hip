@@ -140,6 +140,37 @@ __device__ __forceinline__ Part lane_part(int mode, const float (&v)[4][4], cons
     return p;
 }
 
+// lane_part for 16 values that all lie inside the row (no masks).
+__device__ __forceinline__ Part lane_part_full(int mode, const float (&v)[4][4], const int (&n)[4], float c) {
+    Part p;
+    if (mode == SPECV_GREEDY) {
+        p.a = v[0][0];
+        p.b = __int_as_float(n[0]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (v[x][e] > p.a) {
+                    p.a = v[x][e];
+                    p.b = __int_as_float(n[x] + e);
+                }
+        return p;
+    }
+    float mx = fmaxf(v[0][0], v[0][1]);
+#pragma unroll
+    for (int q = 2; q < 16; q += 2) mx = fmaxf(mx, fmaxf(v[q / 4][q % 4], v[q / 4][q % 4 + 1]));
+    const float m = mx * c;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; q += 2) {
+        s0 += __builtin_amdgcn_exp2f(fmaf(v[q / 4][q % 4], c, -m));
+        s1 += __builtin_amdgcn_exp2f(fmaf(v[q / 4][q % 4 + 1], c, -m));
+    }
+    p.a = m;
+    p.b = s0 + s1;
+    return p;
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -280,10 +311,11 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
 }
 
 // bf16, d_m = 32 * KS (256 at KS = 8): a persistent grid of 512-thread
-// workgroups, one per compute unit. Workgroup (range, group) owns a contiguous
-// range of 64-entry vocabulary slices and a group of 256 requests; the groups
-// of one range are launched on the same XCD (blockIdx modulo 8), so the second
-// group's reads of P find the first group's in that XCD's L2. Each wavefront
+// workgroups, one per compute unit. Workgroup (range, group) owns the 64-entry
+// vocabulary slices range, range + nr, range + 2 nr, ... (so the grid sweeps
+// each request's row as one dense window) and a group of 256 requests; the
+// groups of one range are launched on the same XCD (blockIdx modulo 8), so the
+// second group's reads of P find the first group's in that XCD's L2. Each wavefront
 // keeps its 32 requests' operand rows in registers for the whole launch and
 // sweeps the range slice by slice:
 //   - P slices go through two LDS buffers: the next slice's rows are loaded
@@ -292,7 +324,7 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
 //     that the MFMA output puts 16 consecutive vocabulary entries of one
 //     request in one lane: vocabulary entry v = 16q + 4x + r of the slice is
 //     row 4q + r of MFMA tile x, at LDS row 16x + 4q + r (conflict-free reads);
-//   - backbone values come in 16-byte loads one slice ahead of their epilogue;
+//   - backbone values come in 16-byte loads two slices ahead of their epilogue;
 //   - the epilogue adds them, rounds to bf16 with the hardware conversion
 //     (nearest-even), stores 2 x 16 bytes per lane (4 lanes cover 128
 //     contiguous bytes of a request's row) and emits the per-(request, slice)
@@ -301,6 +333,7 @@ constexpr int kRunThreads = 512;             // 8 wavefronts
 constexpr int kRunGroup = 256;               // requests per workgroup: 8 x 32
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
@@ -331,80 +364,88 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int range = (idx / ng) * 8 + xcd, grp = idx % ng;
     const int S = a.S, V = a.V;
-    const int s_beg = int((long(range) * S) / nr), s_end = int((long(range + 1) * S) / nr);
-    if (s_beg >= s_end) return;
+    // slices range, range + nr, range + 2 nr, ...: at any moment the grid works on
+    // one dense window of each request's row
+    if (range >= S) return;
+    const int s_last = range + (S - 1 - range) / nr * nr;
 
+    // Every load in the slice loop is issued on every path (addresses clamped
+    // into the tensors), so the compiler's count of outstanding memory
+    // operations stays exact and a wait for one slice's backbone values never
+    // waits for the next slice's.
     const uint16_t* P = static_cast<const uint16_t*>(a.proj);
     const uint16_t* E = static_cast<const uint16_t*>(a.emb);
     const uint16_t* bk = static_cast<const uint16_t*>(a.bk);
     uint16_t* dl = static_cast<uint16_t*>(a.dl);
     const int g = lane >> 4, l16 = lane & 15;
 
-    // P slice s: thread vectors q = tid + j * threads (row q / vpr, vector q % vpr)
-    auto load_p = [&](uint4 (&pr)[PT], int s) {
+    // P slice s: thread vectors q = tid + j * threads (row q / vpr, vector q % vpr);
+    // rows past V repeat row V - 1 (their outputs are never stored)
+    auto load_p = [&](u32x4 (&pr)[PT], int s) {
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
             const int q = tid + j * kRunThreads, row = q / vpr, cc = q % vpr;
-            const int v = s * kSlice + row;
-            pr[j] = v < V ? *reinterpret_cast<const uint4*>(P + long(v) * dm + cc * 8) : make_uint4(0, 0, 0, 0);
+            const int v = min(s * kSlice + row, V - 1);
+            pr[j] = *reinterpret_cast<const u32x4*>(P + long(v) * dm + cc * 8);
         }
     };
-    auto store_p = [&](const uint4 (&pr)[PT], int buf) {
+    auto store_p = [&](const u32x4 (&pr)[PT], int buf) {
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
             const int q = tid + j * kRunThreads, row = q / vpr, cc = q % vpr;
             const int L = 16 * ((row >> 2) & 3) + 4 * (row >> 4) + (row & 3);
-            *reinterpret_cast<uint4*>(lds_raw + buf * buf_bytes + L * row_bytes + cc * 16) = pr[j];
+            *reinterpret_cast<u32x4*>(lds_raw + buf * buf_bytes + L * row_bytes + cc * 16) = pr[j];
         }
     };
 
-    // this wavefront's requests and their operand rows
+    // this wavefront's requests (rows of absent requests read request 0's) and their operand rows
     int mreq[2];
     bool mok[2];
+    long rowoff[2];
     bf16x8 bfr[KS][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         const int m = grp * kRunGroup + wave * 32 + 16 * b + l16;
         mreq[b] = m;
         mok[b] = m < a.R;
-        int p = mok[b] ? prev_token(a, m) : 0;
+        const int mc = mok[b] ? m : 0;
+        rowoff[b] = (long(mc) * a.k + a.pos) * long(V);
+        int p = prev_token(a, mc);
         if (p < 0 || p >= V) p = 0;                    // reported by markov_pick
-        const uint16_t* erow = a.state
-            ? static_cast<const uint16_t*>(a.state) + (long(mok[b] ? m : 0) * a.k + a.pos) * dm
-            : E + long(p) * dm;
+        const uint16_t* erow = a.state ? static_cast<const uint16_t*>(a.state) + (long(mc) * a.k + a.pos) * dm
+                                       : E + long(p) * dm;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const uint4 v = mok[b] ? *reinterpret_cast<const uint4*>(erow + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
-            bfr[ks][b] = __builtin_bit_cast(bf16x8, v);
-        }
+        for (int ks = 0; ks < KS; ++ks)
+            bfr[ks][b] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(erow + 32 * ks + 8 * g));
     }
-    long rowoff[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) rowoff[b] = (long(mok[b] ? mreq[b] : 0) * a.k + a.pos) * long(V);
 
-    // backbone values of slice s for this lane: entries 16g .. 16g + 15 of its two requests
-    auto load_bk = [&](uint4 (&w)[2][2], int s) {
+    // backbone values of slice s for this lane: entries 16g .. 16g + 15 of its two
+    // requests (clamped into the row; entries past V are never stored)
+    auto load_bk = [&](u32x4 (&w)[2][2], int s) {
+        if constexpr (VEC) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int n = s * kSlice + 16 * g + 8 * h;
-                w[b][h] = (VEC && mok[b] && n < V) ? *reinterpret_cast<const uint4*>(bk + rowoff[b] + n)
-                                                   : make_uint4(0, 0, 0, 0);
-            }
+                for (int h = 0; h < 2; ++h) {
+                    const int n = min(s * kSlice + 16 * g + 8 * h, V - 8);
+                    w[b][h] = *reinterpret_cast<const u32x4*>(bk + rowoff[b] + n);
+                }
+        }
     };
 
-    uint4 pr[PT];
-    load_p(pr, s_beg);
+    u32x4 pr[PT];
+    load_p(pr, range);
     store_p(pr, 0);
-    if (s_beg + 1 < s_end) load_p(pr, s_beg + 1);
-    uint4 bkc[2][2], bkn[2][2];
-    load_bk(bkc, s_beg);
+    load_p(pr, min(range + nr, s_last));
+    // backbone values two slices ahead: bk0 (slice s), bk1 (s + 1), bk2 (s + 2)
+    u32x4 bk0[2][2], bk1[2][2], bk2[2][2];
+    load_bk(bk0, range);
+    load_bk(bk1, min(range + nr, s_last));
     __syncthreads();
 
-    for (int s = s_beg, it = 0; s < s_end; ++s, ++it) {
+    for (int s = range, it = 0; s <= s_last; s += nr, ++it) {
         const int cur = it & 1;
-        if (s + 1 < s_end) load_bk(bkn, s + 1);
+        load_bk(bk2, min(s + 2 * nr, s_last));
         f32x4 acc[4][2];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
@@ -428,50 +469,51 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
         const int n16 = s * kSlice + 16 * g;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            Part pp = part_empty(a.mode);
-            if (mok[b]) {
-                float bkv[16];
-                if constexpr (VEC) {
+            float bkv[16];
+            if constexpr (VEC) {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const uint4 w = bkc[b][h];
-                        bkv[8 * h + 0] = bf16_lo(w.x); bkv[8 * h + 1] = bf16_hi(w.x);
-                        bkv[8 * h + 2] = bf16_lo(w.y); bkv[8 * h + 3] = bf16_hi(w.y);
-                        bkv[8 * h + 4] = bf16_lo(w.z); bkv[8 * h + 5] = bf16_hi(w.z);
-                        bkv[8 * h + 6] = bf16_lo(w.w); bkv[8 * h + 7] = bf16_hi(w.w);
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        bkv[j] = n16 + j < V ? __uint_as_float(uint32_t(bk[rowoff[b] + n16 + j]) << 16) : 0.f;
+                for (int h = 0; h < 2; ++h) {
+                    const u32x4 w = bk0[b][h];
+                    bkv[8 * h + 0] = bf16_lo(w.x); bkv[8 * h + 1] = bf16_hi(w.x);
+                    bkv[8 * h + 2] = bf16_lo(w.y); bkv[8 * h + 3] = bf16_hi(w.y);
+                    bkv[8 * h + 4] = bf16_lo(w.z); bkv[8 * h + 5] = bf16_hi(w.z);
+                    bkv[8 * h + 6] = bf16_lo(w.w); bkv[8 * h + 7] = bf16_hi(w.w);
                 }
-                uint32_t wd[8];
+            } else {
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
-#pragma unroll
-                    for (int e = 0; e < 4; e += 2)
-                        wd[2 * x + e / 2] = pack_bf16_rne(acc[x][b][e] + bkv[4 * x + e], acc[x][b][e + 1] + bkv[4 * x + e + 1]);
-                float vals[4][4];
-                int ns[4];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    ns[x] = n16 + 4 * x;
-                    vals[x][0] = bf16_lo(wd[2 * x]);     vals[x][1] = bf16_hi(wd[2 * x]);
-                    vals[x][2] = bf16_lo(wd[2 * x + 1]); vals[x][3] = bf16_hi(wd[2 * x + 1]);
-                }
-                if (VEC && n16 + 16 <= V) {
-                    uint4* o = reinterpret_cast<uint4*>(dl + rowoff[b] + n16);
-                    o[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-                    o[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
-                } else if (VEC && n16 + 8 <= V) {
-                    *reinterpret_cast<uint4*>(dl + rowoff[b] + n16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-                } else if (!VEC) {
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        if (n16 + j < V) dl[rowoff[b] + n16 + j] = uint16_t(wd[j / 2] >> (16 * (j & 1)));
-                }
-                pp = lane_part(a.mode, vals, ns, V, a.c);
+                for (int j = 0; j < 16; ++j)
+                    bkv[j] = __uint_as_float(uint32_t(bk[rowoff[b] + min(n16 + j, V - 1)]) << 16);
             }
+            uint32_t wd[8];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int e = 0; e < 4; e += 2)
+                    wd[2 * x + e / 2] = pack_bf16_rne(acc[x][b][e] + bkv[4 * x + e], acc[x][b][e + 1] + bkv[4 * x + e + 1]);
+            float vals[4][4];
+            int ns[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                ns[x] = n16 + 4 * x;
+                vals[x][0] = bf16_lo(wd[2 * x]);     vals[x][1] = bf16_hi(wd[2 * x]);
+                vals[x][2] = bf16_lo(wd[2 * x + 1]); vals[x][3] = bf16_hi(wd[2 * x + 1]);
+            }
+            if constexpr (VEC) {
+                // V % 8 == 0: each 8-entry half is wholly inside the row or wholly past it
+                uint4* drow = reinterpret_cast<uint4*>(dl + rowoff[b] + n16);
+                if (mok[b] && n16 + 16 <= V) {
+                    drow[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                    drow[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+                } else if (mok[b] && n16 + 8 <= V) {
+                    drow[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (mok[b] && n16 + j < V) dl[rowoff[b] + n16 + j] = uint16_t(wd[j / 2] >> (16 * (j & 1)));
+            }
+            Part pp = (s + 1) * kSlice <= V ? lane_part_full(a.mode, vals, ns, a.c)
+                                            : lane_part(a.mode, vals, ns, V, a.c);
 #pragma unroll
             for (int o = 16; o <= 32; o <<= 1) {
                 Part q;
@@ -482,14 +524,15 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
             if (g == 0 && mok[b]) a.part[long(mreq[b]) * S + s] = make_float2(pp.a, pp.b);
         }
         // the slice after next: the other buffer was last read before the previous barrier
-        if (s + 1 < s_end) {
-            store_p(pr, cur ^ 1);
-            if (s + 2 < s_end) load_p(pr, s + 2);
-        }
+        store_p(pr, cur ^ 1);
+        load_p(pr, min(s + 2 * nr, s_last));
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) bkc[b][h] = bkn[b][h];
+            for (int h = 0; h < 2; ++h) {
+                bk0[b][h] = bk1[b][h];
+                bk1[b][h] = bk2[b][h];
+            }
         __syncthreads();
     }
 }
