@@ -191,11 +191,22 @@ __device__ __forceinline__ void flatten_block(const SchedArgs& a, int r0, int r1
 constexpr int kBuckets = 4096;
 constexpr int kBucketItems = 4096;          // largest R * k for schedule_bucket
 
-// Bucket of a key: 2^32 - Q in steps of 2^20 (ascending bucket = descending Q).
+// Bucket of a key; ascending bucket = descending Q, so bucket order is key
+// order. Survivals S = Q / 2^32 >= 1/4 take steps of 2^-12 in S (buckets
+// 0..3072). Smaller ones, which decaying confidences over a long block make
+// plentiful, go by octave: the leading one's position and the next six bits of
+// Q for S in [2^-10, 1/4) (64 buckets per octave, 3073..3584), the next four
+// bits below that (16 per octave, 3585..3936); Q = 0 is bucket 3937.
 __device__ __forceinline__ int bucket_of(uint64_t key) {
-    const uint64_t d = (1ull << 32) - key_q(key);
-    return int(min(d >> 20, uint64_t(kBuckets - 1)));
+    const uint64_t q = key_q(key);
+    if (q >= (1ull << 30)) return int(((1ull << 32) - q) >> 20);
+    if (q == 0) return 3937;
+    const int e = 63 - __builtin_clzll(q);                       // 0..29
+    if (e >= 22) return 3073 + (511 - ((e - 22) * 64 + int((q >> (e - 6)) & 63u)));
+    const int m = int((e >= 4 ? q >> (e - 4) : q << (4 - e)) & 15u);
+    return 3585 + (351 - (e * 16 + m));
 }
+static_assert(3937 < kBuckets, "bucket range");
 
 // The whole schedule by one workgroup of kSchedThreads threads; `lds` holds
 // schedule_bucket_lds(R, k, kk) bytes: keys [R*k] | grouped [n] | sorted [n] |
