@@ -310,14 +310,14 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
     }
 }
 
-// bf16, d_m = 32 * KS (256 at KS = 8): a persistent grid of 512-thread
+// bf16, d_m = 32 * KS (256 at KS = 8): a persistent grid of 1024-thread
 // workgroups, one per compute unit. Workgroup (range, group) owns the 64-entry
 // vocabulary slices range, range + nr, range + 2 nr, ... (so the grid sweeps
 // each request's row as one dense window) and a group of 256 requests; the
 // groups of one range are launched on the same XCD (blockIdx modulo 8), so the
-// second group's reads of P find the first group's in that XCD's L2. Each wavefront
-// keeps its 32 requests' operand rows in registers for the whole launch and
-// sweeps the range slice by slice:
+// second group's reads of P find the first group's in that XCD's L2. Each
+// wavefront keeps its 16 requests' operand rows in registers for the whole
+// launch and sweeps the range slice by slice:
 //   - P slices go through two LDS buffers: the next slice's rows are loaded
 //     into registers during the current slice and written to the other buffer
 //     after it, one barrier per slice. A slice's rows are stored permuted so
@@ -329,8 +329,10 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
 //     (nearest-even), stores 2 x 16 bytes per lane (4 lanes cover 128
 //     contiguous bytes of a request's row) and emits the per-(request, slice)
 //     partials.
-constexpr int kRunThreads = 512;             // 8 wavefronts
-constexpr int kRunGroup = 256;               // requests per workgroup: 8 x 32
+constexpr int kRunKB = 1;                    // 16-request blocks per wavefront (2: 8 wavefronts of
+                                             // 228 VGPRs, 5% slower than 16 of 120)
+constexpr int kRunThreads = 1024 / kRunKB;   // 16 / kRunKB wavefronts
+constexpr int kRunGroup = 256;               // requests per workgroup
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -399,13 +401,13 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
     };
 
     // this wavefront's requests (rows of absent requests read request 0's) and their operand rows
-    int mreq[2];
-    bool mok[2];
-    long rowoff[2];
-    bf16x8 bfr[KS][2];
+    int mreq[kRunKB];
+    bool mok[kRunKB];
+    long rowoff[kRunKB];
+    bf16x8 bfr[KS][kRunKB];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int m = grp * kRunGroup + wave * 32 + 16 * b + l16;
+    for (int b = 0; b < kRunKB; ++b) {
+        const int m = grp * kRunGroup + wave * 16 * kRunKB + 16 * b + l16;
         mreq[b] = m;
         mok[b] = m < a.R;
         const int mc = mok[b] ? m : 0;
@@ -421,10 +423,10 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
 
     // backbone values of slice s for this lane: entries 16g .. 16g + 15 of its two
     // requests (clamped into the row; entries past V are never stored)
-    auto load_bk = [&](u32x4 (&w)[2][2], int s) {
+    auto load_bk = [&](u32x4 (&w)[kRunKB][2], int s) {
         if constexpr (VEC) {
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < kRunKB; ++b)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int n = min(s * kSlice + 16 * g + 8 * h, V - 8);
@@ -438,7 +440,7 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
     store_p(pr, 0);
     load_p(pr, min(range + nr, s_last));
     // backbone values two slices ahead: bk0 (slice s), bk1 (s + 1), bk2 (s + 2)
-    u32x4 bk0[2][2], bk1[2][2], bk2[2][2];
+    u32x4 bk0[kRunKB][2], bk1[kRunKB][2], bk2[kRunKB][2];
     load_bk(bk0, range);
     load_bk(bk1, min(range + nr, s_last));
     __syncthreads();
@@ -446,11 +448,11 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
     for (int s = range, it = 0; s <= s_last; s += nr, ++it) {
         const int cur = it & 1;
         load_bk(bk2, min(s + 2 * nr, s_last));
-        f32x4 acc[4][2];
+        f32x4 acc[4][kRunKB];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
-            for (int b = 0; b < 2; ++b) acc[x][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int b = 0; b < kRunKB; ++b) acc[x][b] = f32x4{0.f, 0.f, 0.f, 0.f};
         const unsigned char* buf = lds_raw + cur * buf_bytes;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -462,13 +464,13 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
 #pragma unroll
             for (int x = 0; x < 4; ++x)
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < kRunKB; ++b)
                     acc[x][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[x], bfr[ks][b], acc[x][b], 0, 0, 0);
         }
         // epilogue: lane holds entries n16 + 4x + e (x, e < 4) of request mreq[b]
         const int n16 = s * kSlice + 16 * g;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < kRunKB; ++b) {
             float bkv[16];
             if constexpr (VEC) {
 #pragma unroll
@@ -527,7 +529,7 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
         store_p(pr, cur ^ 1);
         load_p(pr, min(s + 2 * nr, s_last));
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < kRunKB; ++b)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 bk0[b][h] = bk1[b][h];

@@ -194,19 +194,20 @@ constexpr int kBucketItems = 4096;          // largest R * k for schedule_bucket
 // Bucket of a key; ascending bucket = descending Q, so bucket order is key
 // order. Survivals S = Q / 2^32 >= 1/4 take steps of 2^-12 in S (buckets
 // 0..3072). Smaller ones, which decaying confidences over a long block make
-// plentiful, go by octave: the leading one's position and the next six bits of
-// Q for S in [2^-10, 1/4) (64 buckets per octave, 3073..3584), the next four
-// bits below that (16 per octave, 3585..3936); Q = 0 is bucket 3937.
+// plentiful, go by octave: the leading one's position and the next bits of Q,
+// 128 buckets per octave for S in [1/16, 1/4) (3073..3328), 64 per octave down
+// to 2^-10 (3329..3712), 16 per octave below (3713..4064); Q = 0 is bucket 4065.
 __device__ __forceinline__ int bucket_of(uint64_t key) {
     const uint64_t q = key_q(key);
     if (q >= (1ull << 30)) return int(((1ull << 32) - q) >> 20);
-    if (q == 0) return 3937;
+    if (q == 0) return 4065;
     const int e = 63 - __builtin_clzll(q);                       // 0..29
-    if (e >= 22) return 3073 + (511 - ((e - 22) * 64 + int((q >> (e - 6)) & 63u)));
+    if (e >= 28) return 3073 + (255 - ((e - 28) * 128 + int((q >> (e - 7)) & 127u)));
+    if (e >= 22) return 3329 + (383 - ((e - 22) * 64 + int((q >> (e - 6)) & 63u)));
     const int m = int((e >= 4 ? q >> (e - 4) : q << (4 - e)) & 15u);
-    return 3585 + (351 - (e * 16 + m));
+    return 3713 + (351 - (e * 16 + m));
 }
-static_assert(3937 < kBuckets, "bucket range");
+static_assert(4065 < kBuckets, "bucket range");
 
 // The whole schedule by one workgroup of kSchedThreads threads; `lds` holds
 // schedule_bucket_lds(R, k, kk) bytes: keys [R*k] | grouped [n] | sorted [n] |

@@ -121,16 +121,22 @@ def test_schedule_limits(R, k):
 
 
 @pytest.mark.parametrize("R,k", [(512, 8), (683, 6), (3, 5)])
-@pytest.mark.parametrize("pattern", ["equal", "saturated", "few"])
+@pytest.mark.parametrize("pattern", ["equal", "saturated", "few", "decay", "vanishing"])
 def test_schedule_ties(R, k, pattern):
     """Heavy ties in Q: identical confidences in every request ("equal"), all
-    survivals 1.0 ("saturated"), or confidences from four values ("few"). R*k =
-    4096 and 4098 sit on both sides of the single-workgroup size limit."""
+    survivals 1.0 ("saturated"), or confidences from four values ("few");
+    survivals falling through many octaves below 1/4 ("decay"), and survivals
+    that quantise to Q = 0 ("vanishing"). R*k = 4096 and 4098 sit on both sides
+    of the single-workgroup size limit."""
     g = np.random.Generator(np.random.Philox(R * 7 + k))
     if pattern == "equal":
         z = np.tile((g.standard_normal(k) + 1.5).astype(np.float32), (R, 1))
     elif pattern == "saturated":
         z = np.full((R, k), 60.0, np.float32)
+    elif pattern == "decay":
+        z = (np.linspace(3.0, -9.0, k)[None, :] + 0.5 * g.standard_normal((R, k))).astype(np.float32)
+    elif pattern == "vanishing":
+        z = np.full((R, k), -60.0, np.float32)
     else:
         z = g.choice(np.array([-1.0, 0.5, 1.0, 2.0], np.float32), size=(R, k))
     T = np.linspace(1, 2, k).astype(np.float32)
