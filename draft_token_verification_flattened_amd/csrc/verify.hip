@@ -23,16 +23,19 @@
 //                    softmax state (M, S) of the chunk in sampling mode (M = max
 //                    of logit * log2(e) / tau, S = sum of exp2(that - M)). No
 //                    atomics, no waits: all of the step's logit traffic is here.
-//   verify_decide    one 1024-thread workgroup per request: merges each row's
-//                    chunk partials, decides every verified row, finds the
-//                    first rejection a_r and writes the accepted length and
-//                    tokens. Greedy: complete. Sampling: a request with
-//                    a_r < L_r re-reads its rejected row pair with all 16
+//   verify_decide    one 1024-thread workgroup per request (sampling with
+//                    fewer requests than compute units: two or four): merges
+//                    each row's chunk partials, decides every verified row,
+//                    finds the first rejection a_r and writes the accepted
+//                    length and tokens. Greedy: complete. Sampling: a request
+//                    with a_r < L_r re-reads its rejected row pair with all 16
 //                    wavefronts for the chunk masses of max(0, p - q) (kept in
-//                    LDS) and draws the token by the inverse CDF; with every
-//                    row kept it draws the bonus token from p of the bonus row
-//                    (chunk masses from the partials). No cross-workgroup
-//                    exchange anywhere.
+//                    LDS; split over the request's workgroups, which exchange
+//                    their masses through device-scope stores and one arrival
+//                    counter, the last to arrive drawing) and draws the token by
+//                    the inverse CDF; with every row kept it draws the bonus
+//                    token from p of the bonus row (chunk masses from the
+//                    partials).
 #include <climits>
 
 #include "common.h"
@@ -72,12 +75,15 @@ struct VerifyArgs {
     float2* part_p;                         // [Bmax * C] target chunk partials
     float2* part_q;                         // [Bmax * C] draft chunk partials (sampling)
     RowRec* rec;                            // [Bmax]
+    float* res_mass;                        // [R * C] sampling: residual chunk masses shared by a request's decide workgroups
+    int* res_cnt;                           // [R] arrivals per request (zeroed by verify_stream)
+    int nsplit;                             // sampling: decide workgroups per request (1, 2 or 4)
     SchedArgs next;                         // the next round's schedule (spec_verify_ex)
     int has_next;                           // 1: verify_decide runs `next` as workgroup R
 };
 
 struct Layout {
-    size_t part_p, part_q, rec, total;
+    size_t part_p, part_q, rec, res_mass, res_cnt, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -90,6 +96,8 @@ static Layout ws_layout(int R, int k, int V) {
     l.part_p = off;  off = align256(off + B * C * sizeof(float2));
     l.part_q = off;  off = align256(off + B * C * sizeof(float2));
     l.rec = off;     off = align256(off + B * sizeof(RowRec));
+    l.res_mass = off; off = align256(off + size_t(R) * C * sizeof(float));
+    l.res_cnt = off; off = align256(off + size_t(R) * sizeof(int));
     l.total = off;
     return l;
 }
@@ -240,6 +248,8 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const uint32_t G = gridDim.x, b = blockIdx.x;
     if (b == 0 && tid == 0) a.hdr->status = 0u;
+    if (SAMPLE && b == 0 && a.nsplit > 1)            // verify_decide's per-request arrival counters
+        for (int i = tid; i < a.R; i += kStreamThreads) a.res_cnt[i] = 0;
     const int C = a.C, CH = a.CH, V = a.V, K = a.k;
     const uint32_t region = uint32_t(a.Bmax) * uint32_t(C);          // slots per tensor
     const uint32_t slots = SAMPLE ? 2 * region : region;
@@ -617,7 +627,8 @@ static_assert(kDecideThreads == kSchedThreads, "the next round's schedule runs i
 
 template <int DT, int MODE, bool VEC>
 __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
-    if (a.has_next && int(blockIdx.x) == a.R) {     // the next round's schedule, beside this round's decisions
+    const int nsplit = MODE == SPECV_SAMPLE ? a.nsplit : 1;
+    if (a.has_next && int(blockIdx.x) == nsplit * a.R) {    // the next round's schedule, beside this round's decisions
         extern __shared__ __align__(16) uint64_t sched_lds[];
         schedule_bucket_body(a.next, sched_lds);
         return;
@@ -630,9 +641,10 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
     __shared__ int g_s[SPECV_MAX_K + 1];
     __shared__ float4 st_s[SPECV_MAX_K + 1];
     __shared__ float mass_s[SAMPLE ? kMaxChunks : 1];
-    __shared__ int bad_s, rnext_s;
+    __shared__ int bad_s, rnext_s, last_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = blockIdx.x;
+    const int r = int(blockIdx.x) / nsplit, part = int(blockIdx.x) % nsplit;
+    const bool writer = part == 0;                 // the workgroup that writes the request's decisions
     const int k = a.k, C = a.C, CH = a.CH, V = a.V;
     const int nrows = min(max(*a.n_rows, 0), a.Bmax);
     const int N = a.cu_rows[a.R];
@@ -665,14 +677,14 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
             if (lane != 0) continue;               // lane 0 decides the row
             if (tag_r != r || tag_j != j) bad_s = 1;
             const bool xok = x >= 0 && x < V;
-            if (verified && !xok) atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TOKEN);
+            if (writer && verified && !xok) atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TOKEN);
             bool keep = false;
             if (!SAMPLE) {
                 const int gi = __float_as_int(P.y);
                 const int y = gi == INT_MAX ? 0 : gi;
                 keep = verified && x == y;
                 g_s[j] = y;
-                if (a.diag)
+                if (a.diag && writer)
                     reinterpret_cast<float4*>(a.diag)[t] =
                         make_float4(float(y), P.x, 0.f, verified ? (keep ? 1.f : 0.f) : -1.f);
             } else {
@@ -684,7 +696,7 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
                     ratio = qx > 0.f ? px / qx : INFINITY;
                     keep = uj < fminf(1.f, ratio);
                 }
-                if (a.diag)
+                if (a.diag && writer)
                     reinterpret_cast<float4*>(a.diag)[t] =
                         verified ? make_float4(px, qx, ratio, keep ? 1.f : 0.f) : make_float4(0.f, 0.f, 0.f, -1.f);
             }
@@ -693,6 +705,7 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
     }
     __syncthreads();
     if (bad_s) {
+        if (!writer) return;
         if (tid == 0) {
             atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TAG);
             a.acc_len[r] = 0;
@@ -703,19 +716,24 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
     int acc = L;
     for (int j = 0; j < L; ++j)
         if (!keep_s[j]) { acc = j; break; }
-    if (tid <= k) {
+    // the drawn token out[acc] (sampling) is written by the workgroup that draws it
+    if (writer && tid <= k && !(SAMPLE && tid == acc)) {
         int v = -1;
         if (tid < acc) v = a.tokens[long(r) * k + tid];
-        else if (tid == acc && !SAMPLE) v = g_s[acc];
+        else if (tid == acc) v = g_s[acc];
         out[tid] = v;
     }
-    if (tid == 0) a.acc_len[r] = acc;
+    if (writer && tid == 0) a.acc_len[r] = acc;
     if constexpr (SAMPLE) {
         const float4 st = st_s[acc];
         const float c = a.c, lp = st.x + log2f(st.y), lq = st.z + log2f(st.w);
         const T* trow = static_cast<const T*>(a.target) + (long(r) * (k + 1) + acc) * long(V);
         const T* drow = static_cast<const T*>(a.draft) + (long(r) * k + min(acc, k - 1)) * long(V);
         const bool rejected = acc < L;
+        if (!rejected && !writer) return;          // the bonus draw needs no re-read: one workgroup
+        // a rejected row pair is split between the request's nsplit workgroups: chunks [lo, hi)
+        const int Cs = (C + nsplit - 1) / nsplit;
+        const int lo = rejected ? min(C, part * Cs) : 0, hi = rejected ? min(C, lo + Cs) : C;
         if (rejected) {
             // the rejected row pair: each wavefront takes the next chunk from an
             // LDS counter (the compute unit serves its waves unevenly) and loads
@@ -729,11 +747,11 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
             auto grab = [&]() {
                 int i = 0;
                 if (lane == 0) i = atomicAdd(&rnext_s, 1);
-                return __builtin_amdgcn_readfirstlane(i);
+                return lo + __builtin_amdgcn_readfirstlane(i);
             };
             RW t0, d0;
             if constexpr (!VEC) {                  // scalar rows: one chunk at a time (registers)
-                for (int ch = grab(); ch < C; ch = grab()) {
+                for (int ch = grab(); ch < hi; ch = grab()) {
                     issue(t0, d0, ch);
                     const float m0 = chunk_residual_mass(t0, d0, ch * CH, V, lane, c, lp, lq);
                     if (lane == 0) mass_s[ch] = m0;
@@ -741,15 +759,15 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
             } else {
                 RW t1, d1;
                 int c0 = grab();
-                if (c0 < C) issue(t0, d0, c0);
-                while (c0 < C) {
+                if (c0 < hi) issue(t0, d0, c0);
+                while (c0 < hi) {
                     const int c1 = grab();
-                    if (c1 < C) issue(t1, d1, c1);
+                    if (c1 < hi) issue(t1, d1, c1);
                     const float m0 = chunk_residual_mass(t0, d0, c0 * CH, V, lane, c, lp, lq);
                     if (lane == 0) mass_s[c0] = m0;
-                    if (c1 >= C) break;
+                    if (c1 >= hi) break;
                     c0 = grab();
-                    if (c0 < C) issue(t0, d0, c0);
+                    if (c0 < hi) issue(t0, d0, c0);
                     const float m1 = chunk_residual_mass(t1, d1, c1 * CH, V, lane, c, lp, lq);
                     if (lane == 0) mass_s[c1] = m1;
                 }
@@ -763,6 +781,29 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
             }
         }
         __syncthreads();
+        if (rejected && nsplit > 1) {
+            // exchange the parts' chunk masses: device-scope stores (written through),
+            // their completion, then one arrival; the last to arrive draws the token
+            float* gm = a.res_mass + long(r) * C;
+            for (int cc = lo + tid; cc < hi; cc += kDecideThreads)
+                __hip_atomic_store(gm + cc, mass_s[cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __syncthreads();
+            if (tid == 0) {
+                last_s = __hip_atomic_fetch_add(a.res_cnt + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                         nsplit - 1;
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            }
+            __syncthreads();
+            if (!last_s) return;
+            for (int cc = tid; cc < C; cc += kDecideThreads)
+                if (cc < lo || cc >= hi)
+                    mass_s[cc] = __hip_atomic_load(gm + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0) __hip_atomic_store(a.res_cnt + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+        }
         if (wave != 0) return;
         float total = 0.f;
         if (rejected)
@@ -830,7 +871,7 @@ static int launch_decide(K kernel, VerifyArgs& a, const SchedArgs* next, hipStre
                                 int(lds)) != hipSuccess)
             return fail(SPECV_EDEVICE, "spec_verify: cannot reserve %zu bytes of LDS", lds);
     }
-    SPECV_LAUNCH("verify_decide", kernel, a.R + (a.has_next ? 1 : 0), kDecideThreads, lds, s, a);
+    SPECV_LAUNCH("verify_decide", kernel, a.nsplit * a.R + (a.has_next ? 1 : 0), kDecideThreads, lds, s, a);
     if (next && !a.has_next) return schedule_launch(*next, s);
     return SPECV_OK;
 }
@@ -848,6 +889,12 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
     }
     auto ks = verify_stream<DT, SPECV_SAMPLE, VEC>;
     if (int e = stream_grid(ks, 2L * a.Bmax * a.C, cus, G)) return e;
+    // With fewer requests than compute units, a rejected row pair is re-read by
+    // up to four workgroups (one decide workgroup fits per compute unit, so with
+    // more requests a split only adds rounds), each with at least a chunk per
+    // wavefront.
+    a.nsplit = a.R * 4 <= cus ? 4 : (a.R * 2 <= cus ? 2 : 1);
+    while (a.nsplit > 1 && a.C < a.nsplit * (kDecideThreads / kWave)) a.nsplit /= 2;
     SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
     return launch_decide(verify_decide<DT, SPECV_SAMPLE, VEC>, a, next, s);
 }
@@ -922,6 +969,9 @@ static int verify_impl(int mode, int dtype, int R, int k, int V, const void* tar
     a.part_p = reinterpret_cast<float2*>(w + lay.part_p);
     a.part_q = reinterpret_cast<float2*>(w + lay.part_q);
     a.rec = reinterpret_cast<RowRec*>(w + lay.rec);
+    a.res_mass = reinterpret_cast<float*>(w + lay.res_mass);
+    a.res_cnt = reinterpret_cast<int*>(w + lay.res_cnt);
+    a.nsplit = 1;
     a.has_next = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == SPECV_BF16)

@@ -186,8 +186,9 @@ int spec_flatten(int R, int k, const int32_t* len_in, int32_t* tags_out,
  * Execution: two kernels on `stream`. A persistent grid streams every logit
  * row of the batch once into per-chunk partials; then one workgroup per request
  * decides its rows and, in sampling mode, re-reads the rejected row pair (or one
- * chunk of the bonus row) to draw the extra token. No workgroup waits for
- * another.
+ * chunk of the bonus row) to draw the extra token. With fewer requests than
+ * compute units (sampling), two or four workgroups share a request's re-read
+ * and the last to finish draws; none ever waits for another.
  * Errors: SPECV_EINVAL (NULL pointers, sizes, tau, small workspace),
  *         SPECV_EUNSUPPORTED (dtype; R*(k+1)*V beyond 32-bit item counts;
  *         sampling with more than 4096 chunks per row, i.e. V > 8388608 in
