@@ -155,6 +155,15 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
     t1.record(stream)
     torch.cuda.synchronize()
     ms_plain = t0.elapsed_time(t1) / steps
+    # per-step spread: one event between consecutive steps (a pass of its own)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        d.step(mode_c, max_len)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(1000.0 * evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    pct = {f"p{q}": per[min(steps - 1, int(round(q / 100.0 * (steps - 1))))] for q in (10, 50, 90)}
     L = d.host("lengths")
     N = int(L.sum())
     R = w.R
@@ -167,7 +176,7 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
                 rows=int(d.host("n_rows")[0]), tokens_per_s=N / (ms_plain * 1e-3), verify_us=verify_us,
                 verify_tokens_per_s=N / (verify_us * 1e-6) if verify_us else None,
                 algorithmic_bytes=nbytes, dominant_gbps=achieved / 1e9 if achieved else None,
-                dominant_frac=achieved / HBM_PEAK if achieved else None, kernels=kern)
+                dominant_frac=achieved / HBM_PEAK if achieved else None, kernels=kern, step_us_percentiles=pct)
 
 
 def run_lagged(d, w, mode_c, steps, warmup, B, torch, copies):
@@ -559,6 +568,7 @@ def main():
         "verify_only": {"us_per_step": main_res["verify_us"], "tokens_per_s": main_res["verify_tokens_per_s"]},
         "kernels": main_res["kernels"],
         "ms_per_step_instrumented": main_res["ms_per_step_instrumented"],
+        "step_us_percentiles": main_res["step_us_percentiles"],
         "variants": {k: {kk: v[kk] for kk in ("ms_per_step", "ms_per_step_instrumented", "N", "rows",
                                                 "tokens_per_s", "verify_us", "verify_tokens_per_s",
                                                 "dominant_gbps", "dominant_frac")}

@@ -320,7 +320,10 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
 // launch and sweeps the range slice by slice:
 //   - P slices go through two LDS buffers: the next slice's rows are loaded
 //     into registers during the current slice and written to the other buffer
-//     after it, one barrier per slice. A slice's rows are stored permuted so
+//     after it, one barrier per slice. Rows are 512 bytes, unpadded; the
+//     16-byte chunk c of LDS row L is stored at position c ^ (L % 16), so the
+//     16 lanes that read one chunk of 16 consecutive rows hit 16 different
+//     bank groups. A slice's rows are stored permuted so
 //     that the MFMA output puts 16 consecutive vocabulary entries of one
 //     request in one lane: vocabulary entry v = 16q + 4x + r of the slice is
 //     row 4q + r of MFMA tile x, at LDS row 16x + 4q + r (conflict-free reads);
@@ -356,7 +359,7 @@ template <bool VEC, int KS>
 __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, int ng, int nr) {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     constexpr int dm = KS * 32;
-    constexpr int row_bytes = dm * 2 + 16;             // padded LDS row (bank spread)
+    constexpr int row_bytes = dm * 2;                  // LDS row; 16-byte chunk c of row L sits at c ^ (L % 16)
     constexpr int buf_bytes = kSlice * row_bytes;
     constexpr int vpr = dm / 8;                        // 16-byte vectors per P row
     constexpr int PT = kSlice * vpr / kRunThreads;     // P vectors per thread per slice
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
         for (int j = 0; j < PT; ++j) {
             const int q = tid + j * kRunThreads, row = q / vpr, cc = q % vpr;
             const int L = 16 * ((row >> 2) & 3) + 4 * (row >> 4) + (row & 3);
-            *reinterpret_cast<u32x4*>(lds_raw + buf * buf_bytes + L * row_bytes + cc * 16) = pr[j];
+            *reinterpret_cast<u32x4*>(lds_raw + buf * buf_bytes + L * row_bytes + ((cc ^ (L & 15)) * 16)) = pr[j];
         }
     };
 
@@ -460,7 +463,7 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
 #pragma unroll
             for (int x = 0; x < 4; ++x)
                 afr[x] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const uint4*>(buf + (16 * x + l16) * row_bytes + (32 * ks + 8 * g) * 2));
+                    bf16x8, *reinterpret_cast<const uint4*>(buf + (16 * x + l16) * row_bytes + (((4 * ks + g) ^ l16) * 16)));
 #pragma unroll
             for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -830,7 +833,7 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
     const bool vec8 = (V % 8) == 0 && (reinterpret_cast<uintptr_t>(backbone_logits) & 15u) == 0 &&
                       (reinterpret_cast<uintptr_t>(draft_logits_out) & 15u) == 0;
     const size_t lds = size_t(kSlice) * size_t(d_m * 2 + 16);
-    const int run_lds = 2 * kSlice * (d_m * 2 + 16);
+    const int run_lds = 2 * kSlice * (d_m * 2);
     if (dtype == SPECV_BF16 && d_m == 256) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(markov_logits_run<true, 8>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, run_lds) != hipSuccess ||
