@@ -505,12 +505,15 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
             }
             if constexpr (VEC) {
                 // V % 8 == 0: each 8-entry half is wholly inside the row or wholly past it
-                uint4* drow = reinterpret_cast<uint4*>(dl + rowoff[b] + n16);
+                // non-temporal stores: the logits go to HBM now, while this kernel leaves
+                // bandwidth spare, instead of sitting dirty in the Infinity Cache until
+                // the verify stream's reads evict them
+                u32x4* drow = reinterpret_cast<u32x4*>(dl + rowoff[b] + n16);
                 if (mok[b] && n16 + 16 <= V) {
-                    drow[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-                    drow[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+                    __builtin_nontemporal_store(u32x4{wd[0], wd[1], wd[2], wd[3]}, drow);
+                    __builtin_nontemporal_store(u32x4{wd[4], wd[5], wd[6], wd[7]}, drow + 1);
                 } else if (mok[b] && n16 + 8 <= V) {
-                    drow[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                    __builtin_nontemporal_store(u32x4{wd[0], wd[1], wd[2], wd[3]}, drow);
                 }
             } else {
 #pragma unroll

@@ -137,7 +137,9 @@ struct Raw {
             (void)full;
 #pragma unroll
             for (int u = 0; u < kNV; ++u) {
-                const U4 t = vr[min(first + u * kWave, last)];
+                // read once per call: non-temporal, so the stream does not fill the
+                // caches (and the Infinity Cache) with rows nothing reads again soon
+                const U4 t = __builtin_nontemporal_load(vr + min(first + u * kWave, last));
                 v[u] = make_uint4(t.x, t.y, t.z, t.w);
             }
         } else {
