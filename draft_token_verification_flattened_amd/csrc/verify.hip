@@ -46,7 +46,8 @@ namespace specv {
 
 constexpr int kStreamThreads = 1024;        // verify_stream: one workgroup per compute unit
 constexpr int kPhaseSlots = 2 * kStreamThreads;   // slots described in LDS at a time
-constexpr int kDecideThreads = 1024;        // verify_decide: 16 wavefronts per request
+constexpr int kDecideThreads = 1024;        // verify_decide: 16 wavefronts per workgroup, or
+constexpr int kDecideHalf = 512;            // 8 (two workgroups per compute unit)
 constexpr int kMaxChunks = 4096;            // sampling: chunks per row (residual masses live in LDS)
 constexpr int kNV = 4;                      // 16-byte vectors per lane per item
 constexpr int kChunkVecs = kWave * kNV;     // vectors per chunk
@@ -627,18 +628,20 @@ __device__ __forceinline__ float2 merge_partials(const float2* part, int C, int 
 // taken from the partials.
 static_assert(kDecideThreads == kSchedThreads, "the next round's schedule runs in a decide workgroup");
 
-template <int DT, int MODE, bool VEC>
-__global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
+template <int DT, int MODE, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
     const int nsplit = MODE == SPECV_SAMPLE ? a.nsplit : 1;
-    if (a.has_next && int(blockIdx.x) == nsplit * a.R) {    // the next round's schedule, beside this round's decisions
-        extern __shared__ __align__(16) uint64_t sched_lds[];
-        schedule_bucket_body(a.next, sched_lds);
-        return;
+    if constexpr (NT == kSchedThreads) {
+        if (a.has_next && int(blockIdx.x) == nsplit * a.R) {    // the next round's schedule, beside this round's decisions
+            extern __shared__ __align__(16) uint64_t sched_lds[];
+            schedule_bucket_body(a.next, sched_lds);
+            return;
+        }
     }
     using RW = Raw<DT, VEC>;
     using T = typename RW::T;
     constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
-    constexpr int kW = kDecideThreads / kWave;
+    constexpr int kW = NT / kWave;
     __shared__ int keep_s[SPECV_MAX_K + 1];
     __shared__ int g_s[SPECV_MAX_K + 1];
     __shared__ float4 st_s[SPECV_MAX_K + 1];
@@ -777,7 +780,7 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
         } else {
             // bonus row: chunk masses of p relative to Mp, from the partials
             const float2* pp = a.part_p + long(N + r) * C;
-            for (int cc = tid; cc < C; cc += kDecideThreads) {
+            for (int cc = tid; cc < C; cc += NT) {
                 const float2 q = pp[cc];
                 mass_s[cc] = q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
             }
@@ -787,7 +790,7 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
             // exchange the parts' chunk masses: device-scope stores (written through),
             // their completion, then one arrival; the last to arrive draws the token
             float* gm = a.res_mass + long(r) * C;
-            for (int cc = lo + tid; cc < hi; cc += kDecideThreads)
+            for (int cc = lo + tid; cc < hi; cc += NT)
                 __hip_atomic_store(gm + cc, mass_s[cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_s_waitcnt(0);
@@ -800,7 +803,7 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide(VerifyArgs a) {
             }
             __syncthreads();
             if (!last_s) return;
-            for (int cc = tid; cc < C; cc += kDecideThreads)
+            for (int cc = tid; cc < C; cc += NT)
                 if (cc < lo || cc >= hi)
                     mass_s[cc] = __hip_atomic_load(gm + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (tid == 0) __hip_atomic_store(a.res_cnt + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -863,8 +866,8 @@ static int stream_grid(K kernel, long slots, int cus, int& G) {
 // verify_decide, with the next round's schedule as one more workgroup when it
 // fits one (else launched after it, on the same stream).
 template <class K>
-static int launch_decide(K kernel, VerifyArgs& a, const SchedArgs* next, hipStream_t s) {
-    a.has_next = next && schedule_is_bucket(*next);
+static int launch_decide(K kernel, int threads, VerifyArgs& a, const SchedArgs* next, hipStream_t s) {
+    a.has_next = threads == kSchedThreads && next && schedule_is_bucket(*next);
     size_t lds = 0;
     if (a.has_next) {
         a.next = *next;
@@ -873,7 +876,7 @@ static int launch_decide(K kernel, VerifyArgs& a, const SchedArgs* next, hipStre
                                 int(lds)) != hipSuccess)
             return fail(SPECV_EDEVICE, "spec_verify: cannot reserve %zu bytes of LDS", lds);
     }
-    SPECV_LAUNCH("verify_decide", kernel, a.nsplit * a.R + (a.has_next ? 1 : 0), kDecideThreads, lds, s, a);
+    SPECV_LAUNCH("verify_decide", kernel, a.nsplit * a.R + (a.has_next ? 1 : 0), threads, lds, s, a);
     if (next && !a.has_next) return schedule_launch(*next, s);
     return SPECV_OK;
 }
@@ -887,18 +890,27 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
         auto ks = verify_stream<DT, SPECV_GREEDY, VEC>;
         if (int e = stream_grid(ks, long(a.Bmax) * a.C, cus, G)) return e;
         SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
-        return launch_decide(verify_decide<DT, SPECV_GREEDY, VEC>, a, next, s);
+        return launch_decide(verify_decide<DT, SPECV_GREEDY, VEC, kDecideThreads>, kDecideThreads, a, next, s);
     }
     auto ks = verify_stream<DT, SPECV_SAMPLE, VEC>;
     if (int e = stream_grid(ks, 2L * a.Bmax * a.C, cus, G)) return e;
-    // With fewer requests than compute units, a rejected row pair is re-read by
-    // up to four workgroups (one decide workgroup fits per compute unit, so with
-    // more requests a split only adds rounds), each with at least a chunk per
-    // wavefront.
-    a.nsplit = a.R * 4 <= cus ? 4 : (a.R * 2 <= cus ? 2 : 1);
-    while (a.nsplit > 1 && a.C < a.nsplit * (kDecideThreads / kWave)) a.nsplit /= 2;
+    // One 1024-thread decide workgroup fits per compute unit. With fewer requests
+    // than compute units a rejected row pair is re-read by up to four of them
+    // (each with at least a chunk per wavefront); with more requests than compute
+    // units (and no next-round schedule in the launch, which needs 1024 threads)
+    // the workgroups have 512 threads, two per compute unit, so that all are
+    // resident at once instead of running in two rounds.
+    const bool lagged = next && schedule_is_bucket(*next);
+    const int threads = (!lagged && a.R > cus) ? kDecideHalf : kDecideThreads;
+    a.nsplit = 1;
+    if (threads == kDecideThreads) {
+        a.nsplit = a.R * 4 <= cus ? 4 : (a.R * 2 <= cus ? 2 : 1);
+        while (a.nsplit > 1 && a.C < a.nsplit * (kDecideThreads / kWave)) a.nsplit /= 2;
+    }
     SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
-    return launch_decide(verify_decide<DT, SPECV_SAMPLE, VEC>, a, next, s);
+    if (threads == kDecideThreads)
+        return launch_decide(verify_decide<DT, SPECV_SAMPLE, VEC, kDecideThreads>, threads, a, next, s);
+    return launch_decide(verify_decide<DT, SPECV_SAMPLE, VEC, kDecideHalf>, threads, a, next, s);
 }
 
 }  // namespace specv
