@@ -24,7 +24,9 @@
 //                    of logit * log2(e) / tau, S = sum of exp2(that - M)). No
 //                    atomics, no waits: all of the step's logit traffic is here.
 //   verify_decide    one 1024-thread workgroup per request (sampling with
-//                    fewer requests than compute units: two or four): merges
+//                    fewer requests than compute units: two or four; with more
+//                    requests than compute units: 512 threads, two per unit,
+//                    so that all are resident at once): merges
 //                    each row's chunk partials, decides every verified row,
 //                    finds the first rejection a_r and writes the accepted
 //                    length and tokens. Greedy: complete. Sampling: a request
