@@ -367,9 +367,12 @@ int attn_plan(int R, int k, int Hq, int Hkv, int page_size, int max_pages, int s
     if (split_keys > 0) {
         p.split_tiles = split_keys / kTile;
     } else {
-        // about 24 wavefronts per compute unit if every request used its whole page-table row
+        // about one resident round, 8 wavefronts per compute unit (two per SIMD at this
+        // kernel's registers), if every request used its whole page-table row: in a
+        // sweep of fixed split lengths at 256 requests with 1-3 K contexts, fewer and
+        // longer splits ran fastest (no split 444 us per call, 33-tile splits 462 us)
         const long items = long(R) * Hkv * p.C * max_tiles;
-        p.split_tiles = int(std::max<long>(4, (items + 24L * cus - 1) / (24L * cus)));
+        p.split_tiles = int(std::max<long>(4, (items + 8L * cus - 1) / (8L * cus)));
     }
     p.split_tiles = int(std::min<long>(p.split_tiles, max_tiles));
     p.Smax = int((max_tiles + p.split_tiles - 1) / p.split_tiles);
