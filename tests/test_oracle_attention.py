@@ -92,7 +92,8 @@ def test_tag_mask_hides_later_positions():
     hidden, seen = int(a.ctx_len[r]) + 1, int(a.ctx_len[r])  # the position after the row, and the row itself
     for pos, changes in ((hidden, False), (seen, True)):
         kc = a.k_cache.copy()
-        kc[a.page_table[r, pos // a.page_size], pos % a.page_size] ^= np.uint16(0x4000)
+        # lowest exponent bit: every key value of that position doubles or halves (finite, nonzero)
+        kc[a.page_table[r, pos // a.page_size], pos % a.page_size] ^= np.uint16(0x0080)
         o2 = oatt.flat_attention(a.q, kc, a.v_cache, a.page_table, a.ctx_len, tags, nr, a.page_size)
         assert np.array_equal(o2[t], out[t]) != changes
 
