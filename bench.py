@@ -40,8 +40,8 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_stream_c2_traffic.txt")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--mode", default="sample", choices=["sample", "greedy"])
     ap.add_argument("--max-len", default="k")
