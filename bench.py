@@ -223,10 +223,13 @@ def run_lagged(d, w, mode_c, steps, warmup, B, torch, copies):
     sync_e = [emitted(Ls[t], Ss[t]) for t in range(2, n_long)]
     lag_e = [emitted(Ls[t - 2], Ss[t]) for t in range(2, n_long)]
 
-    # synchronous: schedule(t) then verify(t), one stream
+    # synchronous: [draft(t),] schedule(t) then verify(t), one stream; the same work
+    # as a lagged round, which drafts too when the workload has a sequential head
     def sync_step(t):
         if len(d._copies) > 1:
             d.use_copy(t)
+        if d.w.backbone is not None:
+            d.markov(mode_c)
         B.spec_schedule(zdev[t % n_rounds], d.T, d.tbl_b, d.tbl_t, k, d.lengths, d.tags, d.cu_rows, d.n_rows,
                         d.ws_sched, d.survival)
         d.verify(mode_c, diag=False)
