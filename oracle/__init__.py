@@ -27,6 +27,7 @@ definitions state. Nothing here is shared with the HIP sources.
 
 Modules
   numerics  decoding, bf16 rounding, softmax, argmax, inverse-CDF draw
+  philox    the counter-based generator (Philox4x64-10) behind every uniform
   rule      the acceptance rule for one request, in any exact or float arithmetic
   verify    the rule over a flattened batch, float64, vectorised over requests
   schedule  calibration, survival, the hardware-aware prefix scheduler, flatten
@@ -35,4 +36,4 @@ Modules
   attention tag-masked attention of the flattened rows over a paged KV cache
 """
 
-from . import numerics, rule, verify, schedule, markov, rnn, attention  # noqa: F401
+from . import numerics, philox, rule, verify, schedule, markov, rnn, attention  # noqa: F401

@@ -14,7 +14,8 @@ with E [V, d_m] the previous-token embedding and P [V, d_m] the projection (one
 d_m row per vocabulary entry). dl_i is computed in float64 and rounded once to
 the storage type (bf16 or fp32, nearest-even), and x_i is drawn from the
 rounded logits: greedy = first argmax; sampling = inverse-CDF draw from
-softmax(dl_i / tau) with uniform u[r, i]. The draft distribution q that the
+softmax(dl_i / tau) with uniform u[r, i] = U(seed, step, 2, r, i)
+(oracle.philox), or a given array. The draft distribution q that the
 verifier uses is the softmax of these same stored logits, so the draw and the
 verification see one distribution.
 
@@ -26,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import numerics
+from . import numerics, philox
 
 
 def head_exact(bk_row: np.ndarray, emb: np.ndarray, proj: np.ndarray, prev: np.ndarray,
@@ -46,35 +47,49 @@ def head_logits(bk_row: np.ndarray, emb: np.ndarray, proj: np.ndarray, prev: np.
     return numerics.round_f32(exact)
 
 
-def draw_position(dl_row: np.ndarray, dtype: str, mode: str, tau: float, u: np.ndarray):
-    """Next draft token per request from stored logits [R, V]; also the draw margins."""
+def draw_position(dl_row: np.ndarray, dtype: str, mode: str, tau: float, u: np.ndarray, near_eps: float = 0.0):
+    """Next draft token per request from stored logits [R, V]; also the draws'
+    near sets (oracle.verify.draw_rows; None in greedy mode)."""
     vals = numerics.decode(dl_row, dtype)
     if mode == "greedy":
         return numerics.argmax_first(vals).astype(np.int64), None
     from .verify import draw_rows
-    return draw_rows(numerics.softmax(vals, tau), np.asarray(u, dtype=np.float64))
+    return draw_rows(numerics.softmax(vals, tau), np.asarray(u, dtype=np.float64), near_eps)
+
+
+def draft_uniforms(u_draft, rng, R: int, k: int) -> np.ndarray:
+    """The head's sampling uniforms [R, k]: U(seed, step, 2, r, i) for
+    rng = (seed, step) (oracle.philox), else the given array."""
+    if rng is not None:
+        return philox.uniforms(rng[0], rng[1], philox.DRAFT, R, k)
+    return np.asarray(u_draft, dtype=np.float64)
 
 
 def markov_draft(mode: str, dtype: str, backbone: np.ndarray, emb: np.ndarray, proj: np.ndarray,
-                 prev_token: np.ndarray, tau: float, u_draft: np.ndarray, prev_override=None) -> dict:
+                 prev_token: np.ndarray, tau: float, u_draft=None, prev_override=None, rng=None,
+                 near_eps: float = 0.0) -> dict:
     """Run the head over the k positions.
 
-    prev_override (optional [R,k]): previous tokens to use at each position
-    instead of the head's own draws, so that one position can be checked
-    against another implementation's draws.
+    Sampling uniforms: U(seed, step, 2, r, i) for rng = (seed, step), else
+    u_draft [R, k]. prev_override (optional [R,k]): previous tokens to use at
+    each position instead of the head's own draws, so that one position can be
+    checked against another implementation's draws. draw_near[r][i]: the near
+    set of the draw at near_eps (oracle.verify.draw_rows).
     """
     R, k, V = backbone.shape
     x = np.zeros((R, k), dtype=np.int64)
     dl = np.zeros(backbone.shape, dtype=backbone.dtype)
-    margins = np.zeros((R, k))
+    near = [[np.zeros(0, dtype=np.int64)] * k for _ in range(R)]
+    u = draft_uniforms(u_draft, rng, R, k) if mode == "sample" else np.zeros((R, k))
     prev = np.asarray(prev_token, dtype=np.int64)
     for i in range(k):
         if prev_override is not None:
             prev = np.asarray(prev_override[:, i], dtype=np.int64)
         dl[:, i] = head_logits(backbone[:, i], emb, proj, prev, dtype)
-        xi, m = draw_position(dl[:, i], dtype, mode, tau, u_draft[:, i])
+        xi, nb = draw_position(dl[:, i], dtype, mode, tau, u[:, i], near_eps)
         x[:, i] = xi
-        if m is not None:
-            margins[:, i] = m
+        if nb is not None:
+            for r in range(R):
+                near[r][i] = nb[r]
         prev = xi
-    return dict(tokens=x, logits=dl, draw_margin=margins)
+    return dict(tokens=x, logits=dl, draw_near=near, u_draft=u)

@@ -29,7 +29,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import numerics
-from .markov import draw_position
+from .markov import draft_uniforms, draw_position
 
 
 def _round(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -60,8 +60,11 @@ def states(emb: np.ndarray, rec: np.ndarray, prev_tokens: np.ndarray, dtype: str
 
 
 def rnn_draft(mode: str, dtype: str, backbone: np.ndarray, emb: np.ndarray, rec: np.ndarray, proj: np.ndarray,
-              prev_token: np.ndarray, tau: float, u_draft: np.ndarray, prev_override=None, state_override=None) -> dict:
+              prev_token: np.ndarray, tau: float, u_draft=None, prev_override=None, state_override=None,
+              rng=None, near_eps: float = 0.0) -> dict:
     """Run the head over the k positions.
+
+    Uniforms and draw_near as oracle.markov.markov_draft.
 
     prev_override (optional [R,k]): previous tokens to use at each position
     instead of the head's own draws; state_override (optional [R,k,d_m],
@@ -73,7 +76,8 @@ def rnn_draft(mode: str, dtype: str, backbone: np.ndarray, emb: np.ndarray, rec:
     x = np.zeros((R, k), dtype=np.int64)
     dl = np.zeros(backbone.shape, dtype=backbone.dtype)
     hs = np.zeros((R, k, d_m), dtype=emb.dtype)
-    margins = np.zeros((R, k))
+    near = [[np.zeros(0, dtype=np.int64)] * k for _ in range(R)]
+    u = draft_uniforms(u_draft, rng, R, k) if mode == "sample" else np.zeros((R, k))
     prev = np.asarray(prev_token, dtype=np.int64)
     h = np.zeros((R, d_m))
     P = numerics.decode(proj, dtype)
@@ -86,9 +90,10 @@ def rnn_draft(mode: str, dtype: str, backbone: np.ndarray, emb: np.ndarray, rec:
         hs[:, i] = hr
         h = numerics.decode(hr, dtype)
         dl[:, i] = _round(numerics.decode(backbone[:, i], dtype) + h @ P.T, dtype)
-        xi, m = draw_position(dl[:, i], dtype, mode, tau, u_draft[:, i])
+        xi, nb = draw_position(dl[:, i], dtype, mode, tau, u[:, i], near_eps)
         x[:, i] = xi
-        if m is not None:
-            margins[:, i] = m
+        if nb is not None:
+            for r in range(R):
+                near[r][i] = nb[r]
         prev = xi
-    return dict(tokens=x, logits=dl, states=hs, draw_margin=margins)
+    return dict(tokens=x, logits=dl, states=hs, draw_near=near, u_draft=u)

@@ -17,8 +17,10 @@ Per verified row (the rule itself is oracle.rule):
 Per request: a_r = first j < L_r not kept, else L_r ([P2] section 一: resample
 after the first divergence). Emitted: x_0 .. x_{a_r - 1}, then
   greedy    the target argmax of row a_r;
-  sampling  a draw with u[r, k] from max(0, p - q) at row a_r when a_r < L_r
+  sampling  an inverse-CDF draw from max(0, p - q) at row a_r when a_r < L_r
             (from p when that residual has no mass), else from p of row L_r.
+The uniforms come from the counter-based generator (oracle.philox), or are
+given as an array (see verify()).
 
 The scalar definition in oracle.rule and this vectorised form must agree
 element for element on the same uniforms (tests/test_oracle_verify.py); the
@@ -31,7 +33,15 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import numerics
+from . import numerics, philox
+
+# Distance (a fraction of the draw's total weight W) within which the tokens a
+# draw could produce under rounding are reported (draw_rows' near sets): the
+# float32 draws of the GPU path keep t / W and each C(v) / W within this of the
+# exact values (relative errors of the weights from the scaled exponent, the
+# exponential and the normaliser, and the float32 running sums, each a few
+# times 2**-24 times the number of summation levels).
+DRAW_EPS = 1e-5
 
 
 def _first_false(acc: np.ndarray, L: np.ndarray) -> np.ndarray:
@@ -61,11 +71,17 @@ def decide(px: np.ndarray, qx: np.ndarray, u_acc: np.ndarray, L: np.ndarray):
     return acc, _first_false(acc, np.asarray(L)), ratio
 
 
-def draw_rows(w: np.ndarray, u: np.ndarray):
+def draw_rows(w: np.ndarray, u: np.ndarray, eps: float = 0.0):
     """Inverse-CDF draw per row of weights w [n,V] with uniforms u [n].
 
-    Returns (index [n], margin [n]) where margin is the distance of t = u * W to
-    the nearest CDF boundary, divided by W: how far the draw is from flipping.
+    W = sum of the row in index order, t = u * W, C(v) = w_0 + ... + w_v; the
+    draw is the smallest v with C(v) > t, else (rounding) the last v with
+    w_v > 0. Token v owns the interval [C(v-1), C(v)) of the CDF.
+
+    Returns (index [n], near [n]): near[i] holds, in increasing order, the
+    other tokens with positive weight whose interval lies within eps * W of t,
+    i.e. the tokens a perturbation of t or of the CDF by at most eps * W could
+    draw instead. With eps = 0 every near set is empty.
     """
     w = np.asarray(w, dtype=np.float64)
     c = np.cumsum(w, axis=1)
@@ -77,12 +93,16 @@ def draw_rows(w: np.ndarray, u: np.ndarray):
     if none.any():
         for i in np.nonzero(none)[0]:
             y[i] = np.nonzero(w[i] > 0)[0][-1]
-    n = w.shape[0]
-    hi = c[np.arange(n), y]
-    lo = np.where(y > 0, c[np.arange(n), np.maximum(y - 1, 0)], 0.0)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        margin = np.minimum(np.abs(hi - t), np.abs(t - lo)) / W
-    return y.astype(np.int64), margin
+    near = []
+    for i in range(w.shape[0]):
+        if eps <= 0.0:
+            near.append(np.zeros(0, dtype=np.int64))
+            continue
+        lo = np.concatenate(([0.0], c[i, :-1]))             # C(v - 1)
+        dist = np.maximum(np.maximum(lo - t[i], t[i] - c[i]), 0.0)
+        v = np.nonzero((w[i] > 0) & (dist <= eps * W[i]))[0]
+        near.append(v[v != y[i]].astype(np.int64))
+    return y.astype(np.int64), near
 
 
 def residual_rows(p: np.ndarray, q: np.ndarray) -> np.ndarray:
@@ -130,14 +150,22 @@ def lengths_from_cu(cu_rows: np.ndarray) -> np.ndarray:
 
 
 def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
-           tags: np.ndarray, cu_rows: np.ndarray, tau: float, u_verify: np.ndarray,
-           block_rows: int = 64) -> dict:
+           tags: np.ndarray, cu_rows: np.ndarray, tau: float, u_verify=None,
+           block_rows: int = 64, rng=None, near_eps: float = DRAW_EPS) -> dict:
     """Verify a flattened batch. Shapes: target [R,k+1,V], draft [R,k,V] (sampling
     only), tokens [R,k], tags [B,2] with B = cu_rows[R] + R, cu_rows [R+1]
-    (schedule.flatten), u_verify [R,k+1].
+    (schedule.flatten).
+
+    Uniforms (sampling): rng = (seed, step) takes them from the counter-based
+    generator (oracle.philox): U(seed, step, 0, r, j) keeps or rejects row j,
+    U(seed, step, 1, r, a_r) drives the draw. Without rng, u_verify [R,k+1]
+    gives them: column j < k keeps or rejects row j, column k drives the draw.
 
     Returns a dict with accepted_len [R], out_tokens [R,k+1] (-1 after the last
-    emitted token) and per-row and per-request diagnostics for parity tests.
+    emitted token) and per-row and per-request diagnostics for parity tests,
+    among them the uniforms used (u_accept [R,k], u_draw [R]), the residual
+    mass sum(max(0, p - q)) of each rejected row a_r (0 where every row was
+    kept) and draw_near (draw_rows' near sets at near_eps).
     """
     R, k1, V = target.shape
     k = k1 - 1
@@ -167,6 +195,11 @@ def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
 
     if mode != "sample":
         raise ValueError(mode)
+    if rng is not None:
+        seed, step = rng
+        u_acc = philox.uniforms(seed, step, philox.ACCEPT, R, k)
+    else:
+        u_acc = np.asarray(u_verify, dtype=np.float64)[:, :k]
     px = np.zeros((R, k), dtype=np.float64)
     qx = np.ones((R, k), dtype=np.float64)
     row_p = np.full(B, np.nan)
@@ -184,10 +217,14 @@ def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
         qx[r, j] = q[n, xt]
         row_p[t] = p[n, xt]
         row_q[t] = q[n, xt]
-    acc, a, ratio = decide(px, qx, u_verify[:, :k], L)
+    acc, a, ratio = decide(px, qx, u_acc, L)
+    if rng is not None:
+        u_draw = np.array([philox.uniform(seed, step, philox.DRAW, r, int(a[r])) for r in range(R)])
+    else:
+        u_draw = np.asarray(u_verify, dtype=np.float64)[:, k]
     # resample / bonus rows, recomputed one block at a time
     y = np.zeros(R, dtype=np.int64)
-    margin = np.zeros(R, dtype=np.float64)
+    near = [None] * R
     res_mass = np.zeros(R, dtype=np.float64)
     for s in range(0, R, block_rows):
         rs = np.arange(s, min(R, s + block_rows))
@@ -201,12 +238,14 @@ def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
             res_mass[rs[rej]] = wr.sum(axis=1)
             wr = residual_rows(p[rej], q)
             w[rej] = wr
-        y[rs], margin[rs] = draw_rows(w, u_verify[rs, k])
+        y[rs], nb = draw_rows(w, u_draw[rs], near_eps)
+        for n_, r_ in enumerate(rs):
+            near[r_] = nb[n_]
     row_ratio = np.full(B, np.nan)
     row_acc = np.zeros(B, dtype=bool)
     row_ratio[vidx] = ratio[tags[vidx, 0], tags[vidx, 1]]
     row_acc[vidx] = acc[tags[vidx, 0], tags[vidx, 1]]
     res.update(accepted_len=a, out_tokens=_emit(a, x, y, k), row_p=row_p, row_q=row_q,
-               row_ratio=row_ratio, row_accept=row_acc, accept=acc, draw_margin=margin,
-               residual_mass=res_mass, row_verified=ver)
+               row_ratio=row_ratio, row_accept=row_acc, accept=acc, draw_near=near,
+               residual_mass=res_mass, row_verified=ver, u_accept=u_acc, u_draw=u_draw)
     return res

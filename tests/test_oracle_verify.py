@@ -142,3 +142,68 @@ def test_chisquare_planted_mistakes_fail(logit_model, bad):
     seqs, pr = logit_model.target_probs(k + 1)
     counts = run_trials(logit_model, 1_000_000, k, seed=77, verify_fn=bad)
     assert chi2_pvalue(counts, pr) < 1e-9
+
+
+# ---------------------------------------------------------------------------
+# uniforms from the counter-based generator (rng = (seed, step))
+# ---------------------------------------------------------------------------
+
+def test_rng_uniforms_are_addressed_by_decision():
+    """verify(rng=(seed, step)) equals verify() on the array of the same
+    uniforms: U(seed, step, 0, r, j) for row j, U(seed, step, 1, r, a_r) for
+    the draw."""
+    from oracle import philox
+    g = np.random.Generator(np.random.Philox(31))
+    R, k, V = 40, 4, 24
+    tl = (2 * g.standard_normal((R, k + 1, V))).astype(np.float32)
+    dl = (tl[:, :k] + g.standard_normal((R, k, V))).astype(np.float32)
+    Qd = numerics.softmax(dl.astype(np.float64), 1.0)
+    x = np.array([[numerics.inv_cdf(Qd[r, j], g.random()) for j in range(k)] for r in range(R)])
+    L = g.integers(0, k + 1, size=R)
+    tags, cu = schedule.flatten(L)
+    res = verify.verify("sample", "f32", tl, dl, x, tags, cu, 1.0, rng=(7, 12))
+    u = np.zeros((R, k + 1))
+    for r in range(R):
+        for j in range(k):
+            u[r, j] = philox.uniform(7, 12, philox.ACCEPT, r, j)
+        u[r, k] = philox.uniform(7, 12, philox.DRAW, r, int(res["accepted_len"][r]))
+    ref = verify.verify("sample", "f32", tl, dl, x, tags, cu, 1.0, u)
+    assert np.array_equal(res["accepted_len"], ref["accepted_len"])
+    assert np.array_equal(res["out_tokens"], ref["out_tokens"])
+    assert np.array_equal(res["u_accept"], u[:, :k]) and np.array_equal(res["u_draw"], u[:, k])
+    # another step gives other decisions
+    other = verify.verify("sample", "f32", tl, dl, x, tags, cu, 1.0, rng=(7, 13))
+    assert not np.array_equal(other["u_accept"], res["u_accept"])
+
+
+def test_rng_chisquare_lossless(logit_model):
+    """Trials through verify(rng=(seed, step)), one step per round of the
+    harness: the first k+1 emitted tokens follow the target (V = 8, k = 2,
+    512 cells). A planted reuse of the keep uniform for the draw must fail."""
+    from oracle import philox
+    k = 2
+    seqs, pr = logit_model.target_probs(k + 1)
+    V = logit_model.V
+    calls = [0]
+
+    def via_rng(rows, x, L, u, reuse=False):
+        R = rows.shape[0]
+        tl = logit_model.tl[rows]
+        dl = logit_model.dl[rows[:, :k]]
+        tags, cu = schedule.flatten(L)
+        calls[0] += 1
+        if not reuse:
+            res = verify.verify("sample", "f32", tl, dl, x, tags, cu, 1.0, rng=(5, calls[0]))
+        else:
+            uu = np.zeros((R, k + 1))
+            uu[:, :k] = philox.uniforms(5, calls[0], philox.ACCEPT, R, k)
+            uu[:, k] = uu[:, 0]
+            res = verify.verify("sample", "f32", tl, dl, x, tags, cu, 1.0, uu)
+        return res["accepted_len"], res["out_tokens"]
+
+    counts = run_trials(logit_model, 60_000, k, seed=99, verify_fn=via_rng, batch=20_000, rows=True)
+    assert counts.sum() == 60_000
+    assert chi2_pvalue(counts, pr) > 1e-4
+    counts = run_trials(logit_model, 60_000, k, seed=98,
+                        verify_fn=lambda *a: via_rng(*a, reuse=True), batch=20_000, rows=True)
+    assert chi2_pvalue(counts, pr) < 1e-9
