@@ -226,6 +226,7 @@ def run_lagged(d, w, mode_c, steps, warmup, B, torch, copies):
     # synchronous: [draft(t),] schedule(t) then verify(t), one stream; the same work
     # as a lagged round, which drafts too when the workload has a sequential head
     def sync_step(t):
+        d.step_no = t
         if len(d._copies) > 1:
             d.use_copy(t)
         if d.w.backbone is not None:
@@ -409,45 +410,101 @@ def run_attention(args, B, torch):
         split_keys=args.split_keys, kernels=kern))))
 
 
-def cpu_baseline(w, mode, max_len, min_seconds=10.0):
-    """The oracle, as it stands, on the same workload: whole steps repeated until
-    at least `min_seconds` of CPU time have passed."""
+_CPU = {}
+
+
+def _oracle_share(job):
+    """One worker's share of an oracle step: (Markov head and) verification of
+    a contiguous range of requests, on the batch the parent scheduled. Runs in
+    a forked worker; the workload sits in _CPU, inherited from the parent."""
+    lo, hi, L = job
     import numpy as np
     from oracle import markov as omarkov
     from oracle import schedule as osched
     from oracle import verify as overify
+    w, mode = _CPU["w"], _CPU["mode"]
+    sl = slice(lo, hi)
+    if w.backbone is not None:
+        m = omarkov.markov_draft(mode, w.dtype, w.backbone[sl], w.emb, w.proj, w.prev_token[sl], w.tau,
+                                 w.u_draft[sl])
+        dl, tok = m["logits"], m["tokens"]
+    else:
+        dl = w.draft[sl] if mode == "sample" else None
+        tok = (w.tokens_sample if mode == "sample" else w.tokens_greedy)[sl]
+    tags, cu = osched.flatten(np.asarray(L[sl]))
+    r = overify.verify(mode, w.dtype, w.target[sl], dl, tok, tags, cu, w.tau, w.u_verify[sl])
+    return int(np.sum(r["accepted_len"]))
 
-    def one_step():
-        if w.backbone is not None:
-            m = omarkov.markov_draft(mode, w.dtype, w.backbone, w.emb, w.proj, w.prev_token, w.tau, w.u_draft)
-            dl, tok = m["logits"], m["tokens"]
-        else:
-            dl, tok = w.draft, (w.tokens_sample if mode == "sample" else w.tokens_greedy)
-        s = osched.schedule(w.conf_logit, w.pos_temp, w.tbl_tokens, w.tbl_thr, max_len)
-        tags, cu = osched.flatten(s["L"])
-        overify.verify(mode, w.dtype, w.target, dl if mode == "sample" else None, tok, tags, cu, w.tau,
-                       w.u_verify)
-        return int(np.sum(s["L"]))
 
-    threads = 1
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, mode, max_len, min_seconds=10.0):
+    """The oracle, as it stands, on the same workload and the host's cores.
+
+    Each step: the schedule (one process), then (the Markov head and)
+    verification split over requests among worker processes, one per core
+    (fork, before this process touches the GPU), whole steps repeated for at
+    least `min_seconds`. A single-core figure times whole steps in one
+    process, on a prefix of the requests when the batch is large (at least
+    `min_seconds` / 3). The per-request uniforms come from the workload's
+    arrays, so every share computes exactly what the whole batch would."""
+    import multiprocessing as mp
+    import numpy as np
+    from oracle import schedule as osched
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        if w.backbone is not None and info:        # only the Markov head calls BLAS
-            threads = max(i.get("num_threads", 1) for i in info)
+        limit = threadpoolctl.threadpool_limits(1)         # one BLAS thread per process (workers inherit it)
     except Exception:
-        pass
-    reps, N = 0, 0
-    t = time.perf_counter()
+        limit = None
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    _CPU.update(w=w, mode=mode)
+    R = w.R
+
+    def schedule():
+        return osched.schedule(w.conf_logit, w.pos_temp, w.tbl_tokens, w.tbl_thr, max_len)["L"]
+
+    # single core: whole steps over the first R1 requests (schedule of the whole batch)
+    R1 = min(R, 32)
+    reps1, t = 0, time.perf_counter()
     while True:
-        N = one_step()
-        reps += 1
-        dt = time.perf_counter() - t
-        if dt >= min_seconds:
+        L = schedule()
+        _oracle_share((0, R1, L))
+        reps1 += 1
+        dt1 = time.perf_counter() - t
+        if dt1 >= min_seconds / 3:
             break
-    return dict(value=N * reps / dt, unit="verified draft tokens/s", cores=threads, kind="oracle",
-                sample=f"{reps} full steps of the workload (R={w.R}, N={N} verified drafts per step), "
-                       f"{dt:.1f} s, one process")
+    N1 = int(np.sum(L[:R1]))
+    one_core = N1 * reps1 / dt1
+    # all cores: the batch split into `cores` request ranges
+    edges = np.linspace(0, R, cores + 1).astype(int)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        reps, t = 0, time.perf_counter()
+        while True:
+            L = schedule()
+            pool.map(_oracle_share, [(int(edges[i]), int(edges[i + 1]), L) for i in range(cores)
+                                     if edges[i + 1] > edges[i]])
+            reps += 1
+            dt = time.perf_counter() - t
+            if dt >= min_seconds:
+                break
+    if limit is not None:
+        limit.restore_original_limits()
+    N = int(np.sum(L))
+    return dict(value=N * reps / dt, unit="verified draft tokens/s", cores=cores, kind="oracle",
+                cpu_model=_cpu_model(), single_core_value=one_core,
+                sample=f"{reps} full steps of the workload (R={R}, N={N} verified drafts per step) in {dt:.1f} s: "
+                       f"the schedule in one process, then the requests split over {cores} worker processes; "
+                       f"single core: {reps1} steps over the first {R1} requests ({N1} verified drafts) in "
+                       f"{dt1:.1f} s")
 
 
 def copy_probe(gib):
@@ -480,19 +537,29 @@ def main():
     from draft_token_verification_flattened_amd import workloads
     from draft_token_verification_flattened_amd.pipeline import DeviceStep
 
-    if not torch.cuda.is_available():
+    if torch.cuda.device_count() < 1:          # counts devices without initialising one
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    B.lib()   # fail loudly if the HIP library is missing
+    if not os.path.exists(B.LIB_PATH):         # fail loudly if the HIP library is missing
+        raise RuntimeError(f"{B.LIB_PATH} is not built: run python -m draft_token_verification_flattened_amd.build")
     if args.sweep:
+        B.lib()
         run_sweep(args, B, torch)
         return
     if args.attention:
+        B.lib()
         run_attention(args, B, torch)
         return
     w = workloads.make(args.config)
     max_len = w.k if args.max_len == "k" else int(args.max_len)
-    d = DeviceStep(w, copies=args.copies, head=args.head)
+    # the oracle baseline first: its worker processes are forked before this
+    # process touches the GPU
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, args.mode, max_len)
+        print(json.dumps(dict(cpu_baseline=cpu)), file=sys.stderr, flush=True)
+    B.lib()
+    d = DeviceStep(w, copies=args.copies, head=args.head, rng=True)
     mode_c = B.SAMPLE if args.mode == "sample" else B.GREEDY
     main_res = run_variant(d, w, mode_c, args.mode, max_len, args.steps, args.warmup, B, torch)
 
@@ -541,9 +608,6 @@ def main():
         # the dominant kernel of the step is the one with the larger share of its time
         if mk["avg_us"] * mk["launches_per_step"] > ver.get("avg_us", 0.0) * ver.get("launches_per_step", 0.0):
             roofline, markov_roof = markov_roof, roofline
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(w, args.mode, max_len)
     out = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],
@@ -568,7 +632,10 @@ def main():
         "roofline": roofline,
         "roofline_other": markov_roof,
         "cpu_baseline": cpu,
-        "verify_only": {"us_per_step": main_res["verify_us"], "tokens_per_s": main_res["verify_tokens_per_s"]},
+        "verify_only": {"us_per_step": main_res["verify_us"], "tokens_per_s": main_res["verify_tokens_per_s"],
+                        "hbm_frac": (main_res["algorithmic_bytes"] / (main_res["verify_us"] * 1e-6) / HBM_PEAK
+                                     if main_res["verify_us"] else None),
+                        "kernels": ["verify_stream", "verify_decide"]},
         "kernels": main_res["kernels"],
         "ms_per_step_instrumented": main_res["ms_per_step_instrumented"],
         "step_us_percentiles": main_res["step_us_percentiles"],

@@ -22,11 +22,11 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "specv.h")
 OK, EINVAL, EUNSUPPORTED, EDEVICE = 0, -1, -2, -3
 BF16, F32 = 0, 1
 GREEDY, SAMPLE = 0, 1
-STATUS_BAD_TOKEN, STATUS_BAD_TAG, STATUS_BAD_PAGE = 1, 2, 4
+STATUS_BAD_TOKEN, STATUS_BAD_TAG, STATUS_BAD_PAGE, STATUS_NONFINITE = 1, 2, 4, 8
 MAX_K, MAX_SCHED_ITEMS = 32, 16384
 KV_POSITION_MAJOR, KV_HEAD_MAJOR = 0, 1
 
-_c_int, _c_size, _c_ptr = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+_c_int, _c_size, _c_ptr, _c_u64 = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_uint64
 
 class ScheduleJob(ctypes.Structure):
     """specv_schedule_job: spec_schedule's arguments for spec_verify_ex."""
@@ -41,20 +41,22 @@ _SIGS = {
     "spec_schedule": (_c_int, [_c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
                                _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
     "spec_flatten": (_c_int, [_c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
-    "spec_verify_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
+    "spec_verify_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "spec_verify": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
-                             _c_ptr, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
-                             _c_size, _c_ptr]),
+                             _c_ptr, _c_ptr, ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                             _c_ptr, _c_size, _c_ptr]),
     "spec_verify_ex": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
-                                _c_ptr, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
-                                _c_size, ctypes.POINTER(ScheduleJob), _c_ptr]),
+                                _c_ptr, _c_ptr, ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                _c_ptr, _c_size, ctypes.POINTER(ScheduleJob), _c_ptr]),
     "markov_draft_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "markov_draft": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
-                              _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+                              _c_ptr, ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size,
+                              _c_ptr]),
     "spec_attention_workspace_bytes": (_c_size, [_c_int] * 7),
     "spec_attention": (_c_int, [_c_int] * 10 + [_c_ptr] * 9 + [_c_ptr, _c_size, _c_ptr]),
     "rnn_draft_workspace_bytes": (_c_size, [_c_int] * 4),
-    "rnn_draft": (_c_int, [_c_int] * 6 + [_c_ptr] * 5 + [ctypes.c_float] + [_c_ptr] * 5 + [_c_size, _c_ptr]),
+    "rnn_draft": (_c_int, [_c_int] * 6 + [_c_ptr] * 5 + [ctypes.c_float, _c_u64, _c_u64] + [_c_ptr] * 5
+                  + [_c_size, _c_ptr]),
     "specv_last_error": (ctypes.c_char_p, []),
     "specv_read_status": (_c_int, [_c_ptr, _c_ptr, ctypes.POINTER(ctypes.c_uint32)]),
     "specv_timing_enable": (_c_int, [_c_int]),
@@ -186,28 +188,30 @@ def spec_flatten(len_in, k, tags_out, cu_rows_out, n_rows_out, stream=None):
                               _stream(stream)))
 
 
-def verify_workspace_bytes(mode: int, R: int, k: int, V: int) -> int:
-    return int(lib().spec_verify_workspace_bytes(mode, R, k, V))
+def verify_workspace_bytes(R: int, k: int, V: int) -> int:
+    return int(lib().spec_verify_workspace_bytes(R, k, V))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A zero-filled device byte buffer for a ws argument (torch allocations
-    are 256-byte aligned). spec_schedule needs its workspace zeroed before the
-    first call and leaves it zeroed; the other calls need no initialisation."""
+    """A device byte buffer for a ws argument (torch allocations are 256-byte
+    aligned); no call needs its workspace initialised."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def spec_verify(mode, target, draft, tokens, tags, cu_rows, n_rows, temperature, uniforms, accepted_len_out,
-                out_tokens, ws, row_diag=None, stream=None, next_job: Optional[ScheduleJob] = None):
+                out_tokens, ws, row_diag=None, stream=None, next_job: Optional[ScheduleJob] = None,
+                seed: int = 0, step: int = 0):
     """spec_verify; with next_job, spec_verify_ex (the job's schedule runs
-    beside this call's decisions)."""
+    beside this call's decisions). uniforms None: the library's counter-based
+    uniforms keyed by (seed, step)."""
     R, k1, V = target.shape
     k = k1 - 1
     dt = logit_dtype(target)
     _dev(target, "target", tuple(_LOGIT_TYPES))
     if mode == SAMPLE:
         _dev(draft, "draft", (target.dtype,), (R, k, V))
-        _dev(uniforms, "uniforms", (torch.float32,), (R, k + 1))
+        if uniforms is not None:
+            _dev(uniforms, "uniforms", (torch.float32,), (R, k + 1))
     _dev(tokens, "tokens", (torch.int32,), (R, k))
     _dev(tags, "tags", (torch.int32,), (R * (k + 1), 2))
     _dev(cu_rows, "cu_rows", (torch.int32,), (R + 1,))
@@ -218,7 +222,7 @@ def spec_verify(mode, target, draft, tokens, tags, cu_rows, n_rows, temperature,
     if row_diag is not None:
         _dev(row_diag, "row_diag", (torch.float32,), (R * (k + 1), 4))
     args = (int(mode), dt, R, k, V, _ptr(target), _ptr(draft) if mode == SAMPLE else None,
-            _ptr(tokens), _ptr(tags), _ptr(cu_rows), _ptr(n_rows), float(temperature),
+            _ptr(tokens), _ptr(tags), _ptr(cu_rows), _ptr(n_rows), float(temperature), int(seed), int(step),
             _ptr(uniforms) if mode == SAMPLE else None, _ptr(accepted_len_out),
             _ptr(out_tokens), _ptr(row_diag), _ptr(ws), ws.numel())
     if next_job is None:
@@ -232,7 +236,9 @@ def markov_workspace_bytes(R: int, k: int, V: int, d_m: int) -> int:
 
 
 def markov_draft(mode, backbone, emb, proj, prev_token, temperature, uniforms, tokens_out, logits_out, ws,
-                 stream=None):
+                 stream=None, seed: int = 0, step: int = 0):
+    """markov_draft; uniforms None: the library's counter-based uniforms keyed
+    by (seed, step)."""
     R, k, V = backbone.shape
     d_m = emb.shape[1]
     dt = logit_dtype(backbone)
@@ -243,10 +249,11 @@ def markov_draft(mode, backbone, emb, proj, prev_token, temperature, uniforms, t
     _dev(tokens_out, "tokens_out", (torch.int32,), (R, k))
     _dev(logits_out, "logits_out", (backbone.dtype,), (R, k, V))
     _dev(ws, "ws", (torch.uint8,))
-    if mode == SAMPLE:
+    if mode == SAMPLE and uniforms is not None:
         _dev(uniforms, "uniforms", (torch.float32,), (R, k))
     _check(lib().markov_draft(int(mode), dt, R, k, V, d_m, _ptr(backbone), _ptr(emb), _ptr(proj),
-                              _ptr(prev_token), float(temperature), _ptr(uniforms) if mode == SAMPLE else None,
+                              _ptr(prev_token), float(temperature), int(seed), int(step),
+                              _ptr(uniforms) if mode == SAMPLE else None,
                               _ptr(tokens_out), _ptr(logits_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
@@ -289,7 +296,9 @@ def rnn_workspace_bytes(R: int, k: int, V: int, d_m: int) -> int:
 
 
 def rnn_draft(mode, backbone, emb, rec, proj, prev_token, temperature, uniforms, tokens_out, logits_out, ws,
-              state_out=None, stream=None):
+              state_out=None, stream=None, seed: int = 0, step: int = 0):
+    """rnn_draft; uniforms None: the library's counter-based uniforms keyed by
+    (seed, step)."""
     R, k, V = backbone.shape
     d_m = emb.shape[1]
     dt = logit_dtype(backbone)
@@ -303,10 +312,11 @@ def rnn_draft(mode, backbone, emb, rec, proj, prev_token, temperature, uniforms,
     _dev(ws, "ws", (torch.uint8,))
     if state_out is not None:
         _dev(state_out, "state_out", (backbone.dtype,), (R, k, d_m))
-    if mode == SAMPLE:
+    if mode == SAMPLE and uniforms is not None:
         _dev(uniforms, "uniforms", (torch.float32,), (R, k))
     _check(lib().rnn_draft(int(mode), dt, R, k, V, d_m, _ptr(backbone), _ptr(emb), _ptr(rec), _ptr(proj),
-                           _ptr(prev_token), float(temperature), _ptr(uniforms) if mode == SAMPLE else None,
+                           _ptr(prev_token), float(temperature), int(seed), int(step),
+                           _ptr(uniforms) if mode == SAMPLE else None,
                            _ptr(tokens_out), _ptr(logits_out), _ptr(state_out), _ptr(ws), ws.numel(),
                            _stream(stream)))
 

@@ -1,10 +1,15 @@
 // libspecv host utilities: last-error message, status readback, kernel timing.
+//
+// The timing registry below is the library's only global mutable state: opt-in,
+// process-wide, guarded by one mutex, and it changes no result.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -20,7 +25,8 @@ struct Pending {
     hipEvent_t a, b;
 };
 
-bool g_timing = false;
+std::atomic<bool> g_timing{false};
+std::mutex g_mu;                          // guards everything below
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_free;
 std::map<std::string, std::pair<int, double>> g_done;
@@ -47,9 +53,10 @@ int fail(int code, const char* fmt, ...) {
 
 void clear_error() { g_err[0] = 0; }
 
-bool timing_on() { return g_timing; }
+bool timing_on() { return g_timing.load(std::memory_order_relaxed); }
 
 void timing_events(hipEvent_t& start, hipEvent_t& stop) {
+    std::lock_guard<std::mutex> lk(g_mu);
     start = take_event();
     stop = start ? take_event() : nullptr;
     if (start && !stop) {
@@ -59,6 +66,7 @@ void timing_events(hipEvent_t& start, hipEvent_t& stop) {
 }
 
 void timing_record(const char* name, hipEvent_t start, hipEvent_t stop) {
+    std::lock_guard<std::mutex> lk(g_mu);
     g_pending.push_back({name, start, stop});
 }
 
@@ -79,11 +87,12 @@ int specv_read_status(const void* ws, specv_stream stream, uint32_t* status_out)
 }
 
 int specv_timing_enable(int on) {
-    specv::g_timing = on != 0;
+    specv::g_timing.store(on != 0, std::memory_order_relaxed);
     return SPECV_OK;
 }
 
 int specv_timing_reset(void) {
+    std::lock_guard<std::mutex> lk(specv::g_mu);
     for (auto& p : specv::g_pending) {
         (void)hipEventSynchronize(p.b);
         specv::g_free.push_back(p.a);
@@ -97,6 +106,7 @@ int specv_timing_reset(void) {
 int specv_timing_read(const char* prefix, int* launches, double* total_ms) {
     if (!prefix || !launches || !total_ms)
         return specv::fail(SPECV_EINVAL, "specv_timing_read: NULL pointer");
+    std::lock_guard<std::mutex> lk(specv::g_mu);
     for (auto& p : specv::g_pending) {
         if (hipEventSynchronize(p.b) != hipSuccess)
             return specv::fail(SPECV_EDEVICE, "specv_timing_read: event synchronisation failed");

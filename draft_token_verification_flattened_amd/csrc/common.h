@@ -299,4 +299,61 @@ __device__ __forceinline__ void set_status(WsHeader* h, uint32_t bits) {
     atomicOr(&h->status, bits);
 }
 
+// Float classes from the bits, behind an empty asm statement so that the
+// optimiser cannot turn them back into floating-point class tests: sources
+// built with -fno-honor-nans may fold those to "no NaN".
+__device__ __forceinline__ uint32_t opaque_bits(float x) {
+    uint32_t b = __float_as_uint(x);
+    asm volatile("" : "+v"(b));
+    return b;
+}
+// finite (neither infinite nor NaN)
+__device__ __forceinline__ bool finite_bits(float x) { return (opaque_bits(x) & 0x7f800000u) != 0x7f800000u; }
+// NaN or +inf (-inf is a valid logit: a token that can never be drawn)
+__device__ __forceinline__ bool nan_or_posinf_bits(float x) {
+    const uint32_t b = opaque_bits(x);
+    return b == 0x7f800000u || (b & 0x7fffffffu) > 0x7f800000u;
+}
+
+// ---- counter-based uniforms --------------------------------------------------
+// Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC'11). A round multiplies counter words 0 and
+// 2 by two fixed 64-bit constants into 128-bit products; the new counter is
+// (hi(w2 * M1) ^ w1 ^ k0, lo(w2 * M1), hi(w0 * M0) ^ w3 ^ k1, lo(w0 * M0)); the
+// key is bumped by two Weyl constants before every round but the first. Only
+// word 0 of the block is used.
+//
+// Every uniform of the step is addressed by what it decides:
+//   U(seed, step, purpose, r, i) = (word 0 of the block at counter
+//       (i + 1, r, purpose, 0) under key (seed, step)) >> 40, times 2^-24,
+// a float multiple of 2^-24 in [0, 1), exact. Purposes below.
+enum : uint32_t { kPurposeAccept = 0, kPurposeDraw = 1, kPurposeDraft = 2 };
+
+__device__ __forceinline__ uint64_t philox4x64_10_word0(uint64_t w0, uint64_t w1, uint64_t w2, uint64_t w3,
+                                                        uint64_t k0, uint64_t k1) {
+    constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    constexpr uint64_t K0 = 0x9E3779B97F4A7C15ull, K1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int n = 0; n < 10; ++n) {
+        if (n > 0) {
+            k0 += K0;
+            k1 += K1;
+        }
+        const uint64_t hi0 = __umul64hi(M0, w0), lo0 = M0 * w0;
+        const uint64_t hi1 = __umul64hi(M1, w2), lo1 = M1 * w2;
+        const uint64_t n0 = hi1 ^ w1 ^ k0, n2 = hi0 ^ w3 ^ k1;
+        w0 = n0;
+        w1 = lo1;
+        w2 = n2;
+        w3 = lo0;
+    }
+    return w0;
+}
+
+__device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t step, uint32_t purpose, uint32_t r,
+                                                uint32_t i) {
+    const uint64_t w = philox4x64_10_word0(uint64_t(i) + 1u, r, purpose, 0u, seed, step);
+    return float(uint32_t(w >> 40)) * 0x1p-24f;
+}
+
 }  // namespace specv

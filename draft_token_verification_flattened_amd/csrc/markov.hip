@@ -49,12 +49,25 @@ struct MarkovArgs {
     const int32_t* prev;            // [R]
     const void* rec;                // RNN head: [d_m,d_m] recurrence A (NULL: Markov head)
     void* state;                    // RNN head: [R,k,d_m] states, storage type
-    const float* uniforms;          // [R,k]
+    const float* uniforms;          // [R,k], or NULL: counter-based uniforms (common.h)
+    uint64_t seed, step;            // their key
     int32_t* tokens;                // [R,k]
     void* dl;                       // [R,k,V]
     float2* part;                   // [R * S]
     WsHeader* hdr;
 };
+
+// The sampling uniform of request m at the current position.
+__device__ __forceinline__ float draft_uniform(const MarkovArgs& a, int m) {
+    return a.uniforms ? a.uniforms[long(m) * a.k + a.pos] : philox_uniform(a.seed, a.step, kPurposeDraft, m, a.pos);
+}
+
+// A merged (max, sum) state (sampling) or (max, index) (greedy) that is not
+// finite: a NaN or +inf draft logit (sampling also: a row of -inf only).
+__device__ __forceinline__ bool part_nonfinite(int mode, float a_, float b_) {
+    if (mode == SPECV_GREEDY) return __float_as_uint(a_) == 0x7f800000u;
+    return !(finite_bits(a_) && finite_bits(b_));
+}
 
 __device__ __forceinline__ int prev_token(const MarkovArgs& a, int m) {
     int p = a.pos == 0 ? a.prev[m] : a.tokens[long(m) * a.k + a.pos - 1];
@@ -644,12 +657,13 @@ __global__ __launch_bounds__(256) void markov_pick(MarkovArgs a) {
         q.b = __shfl_xor(tot.b, o, 64);
         part_merge(a.mode, tot, q);
     }
+    if (lane == 0 && part_nonfinite(a.mode, tot.a, tot.b)) set_status(a.hdr, SPECV_STATUS_NONFINITE);
     int y;
     if (a.mode == SPECV_GREEDY) {
         y = __float_as_int(tot.b);
     } else {
         const float M = tot.a;
-        const float thr = a.uniforms[long(m) * a.k + a.pos] * tot.b;
+        const float thr = draft_uniform(a, m) * tot.b;
         const T* row = static_cast<const T*>(a.dl) + (long(m) * a.k + a.pos) * long(a.V);
         const float c = a.c;
         y = inv_cdf_pick(
@@ -716,12 +730,13 @@ __global__ __launch_bounds__(kPickThreads) void markov_pick_wg(MarkovArgs a) {
         p.b = sh_b[v];
         part_merge(a.mode, tot, p);
     }
+    if (tid == 0 && part_nonfinite(a.mode, tot.a, tot.b)) set_status(a.hdr, SPECV_STATUS_NONFINITE);
     if (a.mode == SPECV_GREEDY) {
         if (tid == 0) a.tokens[long(m) * a.k + a.pos] = __float_as_int(tot.b);
         return;
     }
     const float M = tot.a;
-    const float thr = a.uniforms[long(m) * a.k + a.pos] * tot.b;
+    const float thr = draft_uniform(a, m) * tot.b;
     float wm[kPickPer];
     float lsum = 0.f;
     int lastpos = -1;
@@ -797,8 +812,8 @@ size_t head_workspace_bytes(int R, int k, int V, int d_m, bool state) {
 // Markov head (rec == NULL) or RNN head: validation and the per-position launches.
 int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
                const void* emb, const void* rec, const void* proj, const int32_t* prev_token, float temperature,
-               const float* uniforms, int32_t* draft_tokens_out, void* draft_logits_out, void* state_out, void* ws,
-               size_t ws_bytes, hipStream_t s) {
+               uint64_t seed, uint64_t step, const float* uniforms, int32_t* draft_tokens_out,
+               void* draft_logits_out, void* state_out, void* ws, size_t ws_bytes, hipStream_t s) {
     clear_error();
     const bool rnn = rec != nullptr;
     if (mode != SPECV_GREEDY && mode != SPECV_SAMPLE)
@@ -812,7 +827,6 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
     if (!backbone_logits || !emb || !proj || !prev_token || !draft_tokens_out || !draft_logits_out || !ws)
         return fail(SPECV_EINVAL, "%s: NULL required pointer", fn);
     if (mode == SPECV_SAMPLE) {
-        if (!uniforms) return fail(SPECV_EINVAL, "%s: sampling needs uniforms", fn);
         if (!(temperature > 0.f) || !(temperature < INFINITY))
             return fail(SPECV_EINVAL, "%s: temperature must be finite and > 0", fn);
     }
@@ -828,7 +842,8 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
     a.mode = mode;
     a.c = mode == SPECV_SAMPLE ? float(1.4426950408889634 / double(temperature)) : 1.f;
     a.bk = backbone_logits; a.emb = emb; a.proj = proj; a.prev = prev_token;
-    a.uniforms = uniforms; a.tokens = draft_tokens_out; a.dl = draft_logits_out;
+    a.uniforms = uniforms; a.seed = seed; a.step = step;
+    a.tokens = draft_tokens_out; a.dl = draft_logits_out;
     a.hdr = static_cast<WsHeader*>(ws);
     a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + 256);
     a.rec = rec;
@@ -893,12 +908,12 @@ extern "C" size_t markov_draft_workspace_bytes(int R, int k, int V, int d_m) {
 }
 
 extern "C" int markov_draft(int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
-                            const void* emb, const void* proj, const int32_t* prev_token,
-                            float temperature, const float* uniforms, int32_t* draft_tokens_out,
+                            const void* emb, const void* proj, const int32_t* prev_token, float temperature,
+                            uint64_t seed, uint64_t step, const float* uniforms, int32_t* draft_tokens_out,
                             void* draft_logits_out, void* ws, size_t ws_bytes, specv_stream stream) {
     return specv::head_draft("markov_draft", mode, dtype, R, k, V, d_m, backbone_logits, emb, nullptr, proj,
-                             prev_token, temperature, uniforms, draft_tokens_out, draft_logits_out, nullptr, ws,
-                             ws_bytes, static_cast<hipStream_t>(stream));
+                             prev_token, temperature, seed, step, uniforms, draft_tokens_out, draft_logits_out,
+                             nullptr, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 extern "C" size_t rnn_draft_workspace_bytes(int R, int k, int V, int d_m) {
@@ -907,13 +922,14 @@ extern "C" size_t rnn_draft_workspace_bytes(int R, int k, int V, int d_m) {
 
 extern "C" int rnn_draft(int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
                          const void* emb, const void* rec, const void* proj, const int32_t* prev_token,
-                         float temperature, const float* uniforms, int32_t* draft_tokens_out, void* draft_logits_out,
-                         void* state_out, void* ws, size_t ws_bytes, specv_stream stream) {
+                         float temperature, uint64_t seed, uint64_t step, const float* uniforms,
+                         int32_t* draft_tokens_out, void* draft_logits_out, void* state_out, void* ws,
+                         size_t ws_bytes, specv_stream stream) {
     if (!rec) {
         specv::clear_error();
         return specv::fail(SPECV_EINVAL, "rnn_draft: NULL required pointer (rec)");
     }
     return specv::head_draft("rnn_draft", mode, dtype, R, k, V, d_m, backbone_logits, emb, rec, proj, prev_token,
-                             temperature, uniforms, draft_tokens_out, draft_logits_out, state_out, ws, ws_bytes,
-                             static_cast<hipStream_t>(stream));
+                             temperature, seed, step, uniforms, draft_tokens_out, draft_logits_out, state_out, ws,
+                             ws_bytes, static_cast<hipStream_t>(stream));
 }

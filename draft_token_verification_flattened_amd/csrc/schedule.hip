@@ -104,6 +104,13 @@ __device__ __forceinline__ void wave_best(Best& b) {
     }
 }
 
+// Clears schedule_rank's arrival counter; launched ahead of it on the same
+// stream, so the workspace needs no initialisation and a counter left behind by
+// an earlier call (or any other contents) cannot hide the last arrival.
+__global__ __launch_bounds__(64) void schedule_ws_clear(SchedWs* ws) {
+    if (threadIdx.x == 0) ws->done = 0;
+}
+
 __global__ __launch_bounds__(kSchedThreads) void schedule_rank(SchedArgs a, int kw) {
     extern __shared__ __align__(16) uint64_t keys[];          // [R * kk]
     __shared__ int tb[kMaxTbl];
@@ -162,12 +169,10 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_rank(SchedArgs a, int 
             put64(reinterpret_cast<unsigned long long*>(&w->best[blockIdx.x].g), (unsigned long long)b.g);
             __hip_atomic_store(&w->best[blockIdx.x].m, b.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             put64(reinterpret_cast<unsigned long long*>(&w->best[blockIdx.x].key), b.key);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_s_waitcnt(0);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            last_sh = __hip_atomic_fetch_add(&w->done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            // release: this record is visible before the arrival; acquire: the
+            // last to arrive sees every record
+            last_sh = __hip_atomic_fetch_add(&w->done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
                       int(gridDim.x) - 1;
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
         }
     }
     __syncthreads();
@@ -185,7 +190,6 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_rank(SchedArgs a, int 
         if (tid == 0) {
             sh[62] = b.key;
             sh[63] = uint64_t(b.m);
-            __hip_atomic_store(&w->done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     __syncthreads();
@@ -306,6 +310,7 @@ int schedule_launch(const SchedArgs& a, hipStream_t s) {
         hipFuncSetAttribute(reinterpret_cast<const void*>(schedule_rank),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
         return fail(SPECV_EDEVICE, "spec_schedule: cannot reserve %zu bytes of LDS", lds);
+    SPECV_LAUNCH("sched_ws_clear", schedule_ws_clear, 1, 64, 0, s, a.ws);
     SPECV_LAUNCH("schedule", schedule_rank, groups, kSchedThreads, lds, s, a, kw);
     return SPECV_OK;
 }

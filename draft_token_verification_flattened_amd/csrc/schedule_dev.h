@@ -123,8 +123,9 @@ struct SchedArgs {
 };
 
 
-// Workspace of spec_schedule's multi-workgroup kernel: a finish counter (zero
-// between calls) and one best-prefix record per workgroup.
+// Workspace of spec_schedule's multi-workgroup kernel: an arrival counter
+// (cleared by schedule_ws_clear ahead of every launch on the same stream) and
+// one best-prefix record per workgroup.
 constexpr int kMaxSchedGroups = 256;
 struct SchedBest {
     long long g;

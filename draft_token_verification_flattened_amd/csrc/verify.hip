@@ -5,7 +5,7 @@
 // 创始人亲自下场写代码…", engineering table, row "内核利用率暴跌"); verified tokens
 // are kept and the first divergence is resampled ("DSpark 的 661% 提速，是真突破
 // 还是数字游戏？", section 一); rejection sampling keeps the target's distribution
-// ("DeepSeek服务器不再卡顿！…", section "DSpark的神奇之处").
+// ("DeepSeek服务器不再卡顿！…", section "成本与质量的考量").
 //
 // Batch layout (spec_schedule / spec_flatten): rows [0, N) are the verified rows,
 // request-major, request r's at [cu_rows[r], cu_rows[r+1]); rows [N, N + R) are
@@ -69,7 +69,8 @@ struct VerifyArgs {
     const int32_t* tags;
     const int32_t* cu_rows;
     const int32_t* n_rows;
-    const float* uniforms;
+    const float* uniforms;                  // [R, k+1], or NULL: counter-based uniforms (common.h)
+    uint64_t seed, step;                    // the key of those uniforms
     float c;                                // log2(e) / tau
     int32_t* acc_len;
     int32_t* out_tokens;
@@ -205,9 +206,17 @@ __device__ __forceinline__ float2 chunk_softmax(const float (&x)[E], float c) {
     return make_float2(M, wave_sum_dpp((acc[0] + acc[1]) + (acc[2] + acc[3])));
 }
 
-// (max, lowest index) of one chunk over the wave.
+// (max, lowest index) of one chunk over the wave. A chunk holding a NaN or +inf
+// gives (+inf, INT_MIN), which wins every merge: the row's maximum is then +inf,
+// the mark of a row that is not finite. Each logit is folded into a scaled sum,
+// in which any NaN or +inf survives and finite values cannot overflow (-inf
+// alone, a valid logit, leaves -inf).
 template <class RW, int E>
 __device__ __forceinline__ float2 chunk_argmax(const float (&x)[E], int beg, int lane) {
+    float fold = 0.f;
+#pragma unroll
+    for (int q = 0; q < E; ++q) fold = fmaf(x[q], 0x1p-64f, fold);
+    if (__ballot(nan_or_posinf_bits(fold))) return make_float2(INFINITY, __int_as_float(INT_MIN));
     const float lm = lane_max(x);
     const float M = wave_max_dpp(lm);
     int idx = INT_MAX;
@@ -648,7 +657,7 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
     __shared__ int g_s[SPECV_MAX_K + 1];
     __shared__ float4 st_s[SPECV_MAX_K + 1];
     __shared__ float mass_s[SAMPLE ? kMaxChunks : 1];
-    __shared__ int bad_s, rnext_s, last_s;
+    __shared__ int bad_s, nonfinite_s, rnext_s, last_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = int(blockIdx.x) / nsplit, part = int(blockIdx.x) % nsplit;
     const bool writer = part == 0;                 // the workgroup that writes the request's decisions
@@ -657,10 +666,10 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
     const int N = a.cu_rows[a.R];
     const int base = a.cu_rows[r];
     const int L = a.cu_rows[r + 1] - base;
-    const float ub = SAMPLE ? a.uniforms[long(r) * (k + 1) + k] : 0.f;
     int32_t* out = a.out_tokens + long(r) * (k + 1);
     if (tid == 0) {
         bad_s = L < 0 || L > k || base < 0 || base + L > N || N < 0 || N + r >= nrows;
+        nonfinite_s = 0;
         rnext_s = 0;
     }
     __syncthreads();
@@ -675,7 +684,7 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
             float uj = 0.f;
             RowRec rc{0.f, 0.f};
             if (SAMPLE && verified) {
-                uj = a.uniforms[long(r) * (k + 1) + j];
+                uj = a.uniforms ? a.uniforms[long(r) * (k + 1) + j] : philox_uniform(a.seed, a.step, kPurposeAccept, r, j);
                 rc = a.rec[t];
             }
             const float2 P = merge_partials<SAMPLE>(a.part_p + long(t) * C, C, lane);
@@ -683,6 +692,13 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
             if (SAMPLE && verified) Q = merge_partials<true>(a.part_q + long(t) * C, C, lane);
             if (lane != 0) continue;               // lane 0 decides the row
             if (tag_r != r || tag_j != j) bad_s = 1;
+            // a row with a NaN or +inf logit: a softmax state (M, S) that is not
+            // finite (an all -inf row too: no distribution), or in greedy mode the
+            // (+inf, INT_MIN) mark of verify_stream
+            const bool nf = SAMPLE ? !(finite_bits(P.x) && finite_bits(P.y) &&
+                                       (!verified || (finite_bits(Q.x) && finite_bits(Q.y))))
+                                   : __float_as_uint(P.x) == 0x7f800000u;
+            if (nf) nonfinite_s = 1;
             const bool xok = x >= 0 && x < V;
             if (writer && verified && !xok) atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TOKEN);
             bool keep = false;
@@ -703,18 +719,18 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
                     ratio = qx > 0.f ? px / qx : INFINITY;
                     keep = uj < fminf(1.f, ratio);
                 }
-                if (a.diag && writer)
-                    reinterpret_cast<float4*>(a.diag)[t] =
-                        verified ? make_float4(px, qx, ratio, keep ? 1.f : 0.f) : make_float4(0.f, 0.f, 0.f, -1.f);
+                if (a.diag && writer && verified)
+                    reinterpret_cast<float4*>(a.diag)[t] = make_float4(px, qx, ratio, uj);
             }
             keep_s[j] = keep;
         }
     }
     __syncthreads();
-    if (bad_s) {
+    if (bad_s || nonfinite_s) {
+        // a data error: the request's results are void (accepted length 0, no tokens)
         if (!writer) return;
         if (tid == 0) {
-            atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TAG);
+            atomicOr(&a.hdr->status, bad_s ? SPECV_STATUS_BAD_TAG : SPECV_STATUS_NONFINITE);
             a.acc_len[r] = 0;
         }
         if (tid <= k) out[tid] = -1;
@@ -812,6 +828,8 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
             __syncthreads();
         }
         if (wave != 0) return;
+        const float ub = a.uniforms ? a.uniforms[long(r) * (k + 1) + k]
+                                    : philox_uniform(a.seed, a.step, kPurposeDraw, r, acc);
         float total = 0.f;
         if (rejected)
             for (int c0 = 0; c0 < C; c0 += kWave) total += wave_sum_dpp(c0 + lane < C ? mass_s[c0 + lane] : 0.f);
@@ -838,7 +856,13 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
                 return __builtin_amdgcn_exp2f(fmaf(xt_, c, -st.x));
             });
         }
-        if (lane == 0) out[acc] = y;
+        if (lane == 0) {
+            out[acc] = y;
+            // the bonus row's record: residual mass sum(max(0, p - q)) at row a_r
+            // (0 when every row was kept), a_r, the drawn token, its uniform
+            if (a.diag) reinterpret_cast<float4*>(a.diag)[N + r] = make_float4(rejected ? total : 0.f, float(acc),
+                                                                               float(y), ub);
+        }
     }
 }
 
@@ -917,9 +941,8 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
 
 }  // namespace specv
 
-extern "C" size_t spec_verify_workspace_bytes(int mode, int R, int k, int V) {
-    if (R < 1 || k < 1 || k > SPECV_MAX_K || V < 1 || (mode != SPECV_GREEDY && mode != SPECV_SAMPLE))
-        return 0;
+extern "C" size_t spec_verify_workspace_bytes(int R, int k, int V) {
+    if (R < 1 || k < 1 || k > SPECV_MAX_K || V < 1) return 0;
     return specv::ws_layout(R, k, V).total;
 }
 
@@ -927,8 +950,9 @@ namespace specv {
 
 static int verify_impl(int mode, int dtype, int R, int k, int V, const void* target_logits, const void* draft_logits,
                        const int32_t* draft_tokens, const int32_t* tags, const int32_t* cu_rows, const int32_t* n_rows,
-                       float temperature, const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
-                       float* row_diag, void* ws, size_t ws_bytes, const SchedArgs* next, specv_stream stream) {
+                       float temperature, uint64_t seed, uint64_t step, const float* uniforms,
+                       int32_t* accepted_len_out, int32_t* out_tokens, float* row_diag, void* ws, size_t ws_bytes,
+                       const SchedArgs* next, specv_stream stream) {
     if (mode != SPECV_GREEDY && mode != SPECV_SAMPLE)
         return fail(SPECV_EINVAL, "spec_verify: mode %d is neither greedy (0) nor sample (1)", mode);
     if (dtype != SPECV_BF16 && dtype != SPECV_F32)
@@ -942,8 +966,7 @@ static int verify_impl(int mode, int dtype, int R, int k, int V, const void* tar
         !out_tokens || !ws)
         return fail(SPECV_EINVAL, "spec_verify: NULL required pointer");
     if (mode == SPECV_SAMPLE) {
-        if (!draft_logits || !uniforms)
-            return fail(SPECV_EINVAL, "spec_verify: sampling needs draft_logits and uniforms");
+        if (!draft_logits) return fail(SPECV_EINVAL, "spec_verify: sampling needs draft_logits");
         if (!(temperature > 0.f) || !(temperature < INFINITY))
             return fail(SPECV_EINVAL, "spec_verify: temperature must be finite and > 0 (got %g)",
                         double(temperature));
@@ -976,6 +999,8 @@ static int verify_impl(int mode, int dtype, int R, int k, int V, const void* tar
     a.cu_rows = cu_rows;
     a.n_rows = n_rows;
     a.uniforms = uniforms;
+    a.seed = seed;
+    a.step = step;
     a.c = mode == SPECV_SAMPLE ? float(1.4426950408889634 / double(temperature)) : 1.f;
     a.acc_len = accepted_len_out;
     a.out_tokens = out_tokens;
@@ -1000,19 +1025,19 @@ static int verify_impl(int mode, int dtype, int R, int k, int V, const void* tar
 
 extern "C" int spec_verify(int mode, int dtype, int R, int k, int V, const void* target_logits,
                            const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
-                           const int32_t* cu_rows, const int32_t* n_rows, float temperature,
-                           const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
+                           const int32_t* cu_rows, const int32_t* n_rows, float temperature, uint64_t seed,
+                           uint64_t step, const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
                            float* row_diag, void* ws, size_t ws_bytes, specv_stream stream) {
     specv::clear_error();
     return specv::verify_impl(mode, dtype, R, k, V, target_logits, draft_logits, draft_tokens, tags, cu_rows, n_rows,
-                              temperature, uniforms, accepted_len_out, out_tokens, row_diag, ws, ws_bytes, nullptr,
-                              stream);
+                              temperature, seed, step, uniforms, accepted_len_out, out_tokens, row_diag, ws, ws_bytes,
+                              nullptr, stream);
 }
 
 extern "C" int spec_verify_ex(int mode, int dtype, int R, int k, int V, const void* target_logits,
                               const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
-                              const int32_t* cu_rows, const int32_t* n_rows, float temperature,
-                              const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
+                              const int32_t* cu_rows, const int32_t* n_rows, float temperature, uint64_t seed,
+                              uint64_t step, const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
                               float* row_diag, void* ws, size_t ws_bytes, const specv_schedule_job* next,
                               specv_stream stream) {
     using namespace specv;
@@ -1028,6 +1053,6 @@ extern "C" int spec_verify_ex(int mode, int dtype, int R, int k, int V, const vo
             return fail(SPECV_EINVAL, "spec_verify_ex: the next schedule must write a batch other than this one");
     }
     return verify_impl(mode, dtype, R, k, V, target_logits, draft_logits, draft_tokens, tags, cu_rows, n_rows,
-                       temperature, uniforms, accepted_len_out, out_tokens, row_diag, ws, ws_bytes,
+                       temperature, seed, step, uniforms, accepted_len_out, out_tokens, row_diag, ws, ws_bytes,
                        next ? &na : nullptr, stream);
 }

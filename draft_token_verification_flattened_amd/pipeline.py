@@ -10,7 +10,7 @@ import numpy as np
 import torch
 
 from . import binding as B
-from .workloads import Workload
+from .workloads import CONFIGS, Workload
 
 
 def to_device(a: np.ndarray, device) -> torch.Tensor:
@@ -23,11 +23,19 @@ class DeviceStep:
     """`copies` > 1 keeps that many copies of the large read-only inputs (target
     logits, draft logits, Markov backbone logits) and moves to the next copy at
     every step, so that no step finds the previous step's logits in the 256 MB
-    Infinity Cache."""
+    Infinity Cache.
 
-    def __init__(self, w: Workload, device="cuda", copies: int = 1, head: str = "markov"):
+    rng=False: the calls take the workload's uniform arrays. rng=True: the
+    library draws its own counter-based uniforms keyed by (seed, step), seed =
+    the workload's seed and step = a counter that step() advances, so every
+    step makes fresh decisions."""
+
+    def __init__(self, w: Workload, device="cuda", copies: int = 1, head: str = "markov", rng: bool = False):
         self.w = w
         self.device = device
+        self.rng = rng
+        self.seed = int(CONFIGS[w.name]["seed"])
+        self.step_no = 0
         R, k, V = w.R, w.k, w.V
         dev = lambda a: None if a is None else to_device(a, device)   # noqa: E731
         self.target = dev(w.target)
@@ -60,7 +68,7 @@ class DeviceStep:
         self.acc_len = torch.zeros(R, **i32)
         self.out_tokens = torch.zeros(R, k + 1, **i32)
         self.diag = torch.zeros(R * (k + 1), 4, dtype=torch.float32, device=device)
-        self.ws_verify = B.workspace(B.verify_workspace_bytes(B.SAMPLE, R, k, V), device)
+        self.ws_verify = B.workspace(B.verify_workspace_bytes(R, k, V), device)
         self.ws_sched = B.workspace(B.schedule_workspace_bytes(R, k), device)
         if w.backbone is not None:
             self.draft_tokens = torch.zeros(R, k, **i32)
@@ -77,14 +85,24 @@ class DeviceStep:
     def flatten(self, lengths: torch.Tensor, stream=None):
         B.spec_flatten(lengths, self.w.k, self.tags, self.cu_rows, self.n_rows, stream=stream)
 
+    def uniforms(self, which):
+        """Keyword arguments that select the uniforms of a call: the workload's
+        array `which`, or (rng) the library's generator at (seed, step_no)."""
+        if self.rng:
+            return dict(uniforms=None, seed=self.seed, step=self.step_no)
+        return dict(uniforms=getattr(self, which), seed=self.seed, step=self.step_no)
+
     def markov(self, mode, stream=None):
         """The drafter's sequential module: the Markov head, or the RNN head."""
+        u = self.uniforms("u_draft")
         if self.head == "rnn":
-            B.rnn_draft(mode, self.backbone, self.emb, self.rec, self.proj, self.prev, self.w.tau, self.u_draft,
-                        self.draft_tokens, self.draft_logits, self.ws_markov, stream=stream)
+            B.rnn_draft(mode, self.backbone, self.emb, self.rec, self.proj, self.prev, self.w.tau, u["uniforms"],
+                        self.draft_tokens, self.draft_logits, self.ws_markov, stream=stream, seed=u["seed"],
+                        step=u["step"])
         else:
-            B.markov_draft(mode, self.backbone, self.emb, self.proj, self.prev, self.w.tau, self.u_draft,
-                           self.draft_tokens, self.draft_logits, self.ws_markov, stream=stream)
+            B.markov_draft(mode, self.backbone, self.emb, self.proj, self.prev, self.w.tau, u["uniforms"],
+                           self.draft_tokens, self.draft_logits, self.ws_markov, stream=stream, seed=u["seed"],
+                           step=u["step"])
 
     def drafts(self, mode):
         """(draft logits, draft tokens) the verifier uses for this workload and mode."""
@@ -96,9 +114,10 @@ class DeviceStep:
         d, t = self.drafts(mode)
         d = d if draft is None else draft
         t = t if tokens is None else tokens
-        B.spec_verify(mode, self.target, d, t, self.tags, self.cu_rows, self.n_rows, self.w.tau, self.u_verify,
+        u = self.uniforms("u_verify")
+        B.spec_verify(mode, self.target, d, t, self.tags, self.cu_rows, self.n_rows, self.w.tau, u["uniforms"],
                       self.acc_len, self.out_tokens, self.ws_verify, row_diag=self.diag if diag else None,
-                      stream=stream)
+                      stream=stream, seed=u["seed"], step=u["step"])
 
     def use_copy(self, i: int):
         for n, t in self._copies[i % len(self._copies)].items():
@@ -106,6 +125,7 @@ class DeviceStep:
 
     def step(self, mode, max_len=None, diag=False, stream=None):
         """One pass of the hot path: (Markov draft,) schedule + flatten, verify."""
+        self.step_no += 1
         if len(self._copies) > 1:
             self._turn += 1
             self.use_copy(self._turn)
@@ -170,12 +190,15 @@ class LaggedStep:
         s, o = t % 2, (t + 1) % 2
         if len(d._copies) > 1:
             d.use_copy(t)
+        d.step_no = t
         if d.w.backbone is not None:
             d.markov(mode)
         dl, tk = d.drafts(mode)
+        u = d.uniforms("u_verify")
         B.spec_verify(mode, d.target, dl, tk, self.tags[s], self.cu_rows[s], self.n_rows[s], d.w.tau,
-                      d.u_verify, self.acc_len[s], self.out_tokens[s], d.ws_verify,
-                      row_diag=d.diag if diag else None, next_job=self._job(o, t + 1 - self.lag))
+                      u["uniforms"], self.acc_len[s], self.out_tokens[s], d.ws_verify,
+                      row_diag=d.diag if diag else None, next_job=self._job(o, t + 1 - self.lag), seed=u["seed"],
+                      step=u["step"])
         self.t = t + 1
 
     def capture(self, mode, rounds: int):

@@ -9,7 +9,7 @@
  *   [P2] "DSpark 的 661% 提速，是真突破还是数字游戏？" (new-universe.cn),
  *        sections 一, 3.1 and 3.2.
  *   [P3] "DeepSeek服务器不再卡顿！DSpark加速60% - 80%，推理成本降40%"
- *        (qwbw.cn), section "DSpark的神奇之处".
+ *        (qwbw.cn), sections "DSpark的神奇之处" and "成本与质量的考量".
  *   [P4] aibuzzwire.news, "deepseek-dspark-speculative-decoding-85-percent-
  *        faster-llm-inference", section "置信度计划、负载感知验证".
  *
@@ -23,10 +23,26 @@
  *     SPECV_EUNSUPPORTED nothing was enqueued. specv_last_error() gives a
  *     message (per host thread).
  *   - Data errors found on the device (a draft token outside [0, V), a tag that
- *     disagrees with cu_rows) never fault: the offending row is treated as
- *     rejected and a bit is set in the workspace status word, readable with
- *     specv_read_status().
+ *     disagrees with cu_rows, a logit that is NaN or +inf) never fault: a bit
+ *     is set in the workspace status word, readable with specv_read_status(),
+ *     and the offending row or request is handled as each call states.
  *   - Calls that share a workspace must not run concurrently.
+ *   - Random numbers: every uniform a call consumes is
+ *       U(seed, step, purpose, r, i) = (word 0 of Philox4x64-10 at counter
+ *           (i + 1, r, purpose, 0) under key (seed, step)) >> 40, times 2^-24
+ *     (Philox: Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+ *     1, 2, 3", SC'11), a float multiple of 2^-24 in [0, 1), addressed by the
+ *     decision it drives (purpose 0: keep or reject the draft token at position i
+ *     of request r; 1: the extra token drawn at position i = a_r; 2: the draft
+ *     head's token at position i), so results depend on neither the schedule
+ *     nor the row order. A caller that advances `step` once per decoding step
+ *     gets fresh, reproducible randomness without any state in the library.
+ *     The pages name Philox-seeded trials only; the rest is this library's
+ *     reading. A caller may pass its own uniforms instead (the `uniforms`
+ *     arguments; NULL selects the generator).
+ *   - No global mutable state, with one opt-in exception: the timing hooks at
+ *     the end of this header (off by default, guarded by a mutex, meant for
+ *     benchmarks; they change no result).
  *   - Row-major layouts throughout. "bf16" arrays hold IEEE bfloat16 values
  *     (2 bytes each); "f32" arrays hold float.
  */
@@ -57,8 +73,10 @@ enum { SPECV_KV_POSITION_MAJOR = 0, SPECV_KV_HEAD_MAJOR = 1 };  /* spec_attentio
 enum {
     SPECV_STATUS_BAD_TOKEN = 1u, /* a draft token outside [0, V) */
     SPECV_STATUS_BAD_TAG = 2u,   /* tags[] disagrees with cu_rows[] */
-    SPECV_STATUS_BAD_PAGE = 4u   /* spec_attention: a page id outside [0, num_pages), or a
+    SPECV_STATUS_BAD_PAGE = 4u,  /* spec_attention: a page id outside [0, num_pages), or a
                                     context length that is negative or overruns its page-table row */
+    SPECV_STATUS_NONFINITE = 8u  /* a logit row with a NaN or +inf value (sampling: also a row
+                                    of -inf only, which has no distribution) */
 };
 
 /* Limits of the scheduler: all candidate keys of one call are held in the
@@ -109,11 +127,20 @@ enum {
  *   n_rows_out    i32 [1]
  *   survival_out  f64 [R,k] or NULL
  *   ws, ws_bytes  workspace of at least spec_schedule_workspace_bytes(R, k)
- *                 bytes, 256-byte aligned, zero-filled before its first use
- *                 (every call leaves it zeroed again)
- * Execution: up to 256 workgroups; each computes every key, counts for its
- *   share of keys how many keys are smaller (and their sum), and posts its best
- *   prefix; the last to finish picks the overall best and flattens. No sort.
+ *                 bytes, 256-byte aligned; needs no initialisation
+ * Execution (on `stream`; no sort):
+ *   - max_len -1 or 0: one workgroup writes the survival and flattens the fixed
+ *     lengths.
+ *   - R * k <= 4096: one 1024-thread workgroup does everything in
+ *     its local data share: the keys go into 4096 buckets ordered like the keys
+ *     (linear in S above 1/4, by octave below), each key's sorted position is its
+ *     bucket's start plus the smaller keys in its bucket, P(M) comes from exact
+ *     integer scans, then G(M) for every M, the best M, the lengths and the
+ *     flattened batch.
+ *   - larger: a one-wavefront kernel clears the workspace's arrival counter,
+ *     then up to 256 workgroups each compute every key, count for their share
+ *     of keys how many keys are smaller (and their sum) and post their best
+ *     prefix; the last to arrive picks the overall best and flattens.
  * Errors: SPECV_EINVAL for NULL required pointers, out-of-range sizes or a small
  *   workspace; SPECV_EDEVICE if the launch fails.
  */
@@ -161,8 +188,14 @@ int spec_flatten(int R, int k, const int32_t* len_in, int32_t* tags_out,
  *               a_r < L_r (from p when that residual has no mass), else from
  *               p_{L_r}: the smallest v with w_0 + .. + w_v > u * sum(w).
  *   out_tokens[r, a_r+1 .. k] = -1; accepted_len[r] = a_r.
+ * Uniforms: u[r,j] = U(seed, step, 0, r, j) and the draw's u = U(seed, step,
+ * 1, r, a_r) (see the conventions above), or the caller's `uniforms`.
  * Arithmetic is float32 (softmax statistics in base 2 with a pre-scaled
  * log2(e)/tau); greedy decisions are exact comparisons.
+ * Logits may be -inf (a token that cannot be drawn). A request with a NaN or
+ * +inf logit in any row this call reads for it (sampling: also a row of -inf
+ * only) gets accepted_len 0 and out_tokens all -1, and sets
+ * SPECV_STATUS_NONFINITE; the other requests are unaffected.
  *
  * Arguments (device pointers unless noted)
  *   mode, dtype     SPECV_GREEDY / SPECV_SAMPLE, SPECV_BF16 / SPECV_F32
@@ -172,15 +205,18 @@ int spec_flatten(int R, int k, const int32_t* len_in, int32_t* tags_out,
  *   draft_tokens    i32 [R,k]
  *   tags, cu_rows, n_rows   the flattened batch (spec_schedule / spec_flatten)
  *   temperature     host float tau > 0 (sampling); ignored in greedy
- *   uniforms        f32 [R,k+1] in [0,1): column j < k decides row j, column k
- *                   drives the resample / bonus draw (sampling; may be NULL in greedy)
+ *   seed, step      host uint64: the key of the uniforms (sampling)
+ *   uniforms        NULL (the generator), or f32 [R,k+1] in [0,1): column j < k
+ *                   decides row j, column k drives the resample / bonus draw
  *   accepted_len_out i32 [R]
  *   out_tokens       i32 [R,k+1]
  *   row_diag         f32 [R*(k+1),4] or NULL. Verified rows: sampling
- *                    {p(x), q(x), p(x)/q(x), kept}, greedy {argmax, max logit, 0,
- *                    kept}. Bonus rows: sampling {0,0,0,-1}, greedy {argmax,
- *                    max logit, 0, -1}.
- *   ws, ws_bytes     workspace of at least spec_verify_workspace_bytes(mode,R,k,V)
+ *                    {p(x), q(x), p(x)/q(x), u}, greedy {argmax, max logit, 0,
+ *                    kept}. Bonus row of request r (row N + r): sampling
+ *                    {sum(max(0, p - q)) at row a_r (0 when a_r = L_r), a_r,
+ *                    drawn token, u of the draw}, greedy {argmax, max logit, 0,
+ *                    -1}. Rows of a request with a data error: undefined.
+ *   ws, ws_bytes     workspace of at least spec_verify_workspace_bytes(R,k,V)
  *                    bytes, 256-byte aligned; its contents need no
  *                    initialisation (chunk partials of the call in flight)
  * Execution: two kernels on `stream`. A persistent grid streams every logit
@@ -194,11 +230,11 @@ int spec_flatten(int R, int k, const int32_t* len_in, int32_t* tags_out,
  *         sampling with more than 4096 chunks per row, i.e. V > 8388608 in
  *         bf16 or V > 4194304 in f32), SPECV_EDEVICE (launch failure).
  */
-size_t spec_verify_workspace_bytes(int mode, int R, int k, int V);
+size_t spec_verify_workspace_bytes(int R, int k, int V);
 int spec_verify(int mode, int dtype, int R, int k, int V, const void* target_logits,
                 const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
-                const int32_t* cu_rows, const int32_t* n_rows, float temperature,
-                const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
+                const int32_t* cu_rows, const int32_t* n_rows, float temperature, uint64_t seed,
+                uint64_t step, const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
                 float* row_diag, void* ws, size_t ws_bytes, specv_stream stream);
 
 /* ------------------------------------------------------------------------ */
@@ -241,8 +277,8 @@ typedef struct {
 
 int spec_verify_ex(int mode, int dtype, int R, int k, int V, const void* target_logits,
                    const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
-                   const int32_t* cu_rows, const int32_t* n_rows, float temperature,
-                   const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
+                   const int32_t* cu_rows, const int32_t* n_rows, float temperature, uint64_t seed,
+                   uint64_t step, const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
                    float* row_diag, void* ws, size_t ws_bytes, const specv_schedule_job* next,
                    specv_stream stream);
 
@@ -257,9 +293,12 @@ int spec_verify_ex(int mode, int dtype, int R, int k, int V, const void* target_
  *   dl[r,i,:] = round(backbone[r,i,:] + emb[x_{i-1},:] . proj^T)  (float32
  *               accumulation; one round-to-nearest-even to dtype)
  *   x_i = argmax dl[r,i,:] (greedy, lowest index) or the inverse-CDF draw from
- *         softmax(dl[r,i,:] / tau) with uniforms[r,i] (sampling).
+ *         softmax(dl[r,i,:] / tau) with u = U(seed, step, 2, r, i), or
+ *         uniforms[r,i] (sampling).
  * The rounded logits are written out: they are the draft distribution the
- * verifier must use.
+ * verifier must use. A row whose softmax state (sampling) or maximum (greedy:
+ * +inf) is not finite sets SPECV_STATUS_NONFINITE; its token is then
+ * unspecified (within [0, V)).
  *
  * Arguments (device pointers unless noted)
  *   mode, dtype     as spec_verify
@@ -268,9 +307,14 @@ int spec_verify_ex(int mode, int dtype, int R, int k, int V, const void* target_
  *   backbone_logits [R,k,V] dtype
  *   emb             [V,d_m] dtype   previous-token embedding
  *   proj            [V,d_m] dtype   projection, one d_m row per vocabulary entry
+ *                   (the transpose of a [d_m,V] weight: a 64-entry vocabulary
+ *                   slice of it is one contiguous 64 x d_m block, which the
+ *                   projection kernel stages into its local data share with
+ *                   plain linear loads)
  *   prev_token      i32 [R]          last committed token
  *   temperature     host float > 0 (sampling)
- *   uniforms        f32 [R,k] (sampling; may be NULL in greedy)
+ *   seed, step      host uint64: the key of the uniforms (sampling)
+ *   uniforms        NULL (the generator), or f32 [R,k] (sampling)
  *   draft_tokens_out i32 [R,k];  draft_logits_out [R,k,V] dtype
  *   ws, ws_bytes    at least markov_draft_workspace_bytes(R,k,V,d_m)
  * Errors: as spec_verify.
@@ -278,9 +322,9 @@ int spec_verify_ex(int mode, int dtype, int R, int k, int V, const void* target_
 size_t markov_draft_workspace_bytes(int R, int k, int V, int d_m);
 int markov_draft(int mode, int dtype, int R, int k, int V, int d_m,
                  const void* backbone_logits, const void* emb, const void* proj,
-                 const int32_t* prev_token, float temperature, const float* uniforms,
-                 int32_t* draft_tokens_out, void* draft_logits_out, void* ws, size_t ws_bytes,
-                 specv_stream stream);
+                 const int32_t* prev_token, float temperature, uint64_t seed, uint64_t step,
+                 const float* uniforms, int32_t* draft_tokens_out, void* draft_logits_out, void* ws,
+                 size_t ws_bytes, specv_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* rnn_draft                                                                 */
@@ -307,8 +351,9 @@ int markov_draft(int mode, int dtype, int R, int k, int V, int d_m,
 size_t rnn_draft_workspace_bytes(int R, int k, int V, int d_m);
 int rnn_draft(int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
               const void* emb, const void* rec, const void* proj, const int32_t* prev_token,
-              float temperature, const float* uniforms, int32_t* draft_tokens_out,
-              void* draft_logits_out, void* state_out, void* ws, size_t ws_bytes, specv_stream stream);
+              float temperature, uint64_t seed, uint64_t step, const float* uniforms,
+              int32_t* draft_tokens_out, void* draft_logits_out, void* state_out, void* ws,
+              size_t ws_bytes, specv_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* spec_attention                                                            */
@@ -381,11 +426,13 @@ const char* specv_last_error(void);
  * rnn_draft / spec_attention call that used `ws` (synchronises `stream`). */
 int specv_read_status(const void* ws, specv_stream stream, uint32_t* status_out);
 
-/* Per-kernel timing with HIP events recorded on the launch stream around each
- * kernel the library enqueues. Off by default; meant for benchmarks. Not
- * thread-safe. specv_timing_read synchronises the recorded events and returns
- * the number of launches and their summed duration for kernels whose name
- * starts with `prefix`. */
+/* Per-kernel timing with HIP events that the library attaches to each kernel
+ * it enqueues (hipExtLaunchKernel). Off by default; meant for benchmarks. This
+ * registry is the library's only global mutable state: it is process-wide,
+ * guarded by a mutex, and changes no result. A launch made while timing is on
+ * from one host thread is recorded with the others. specv_timing_read
+ * synchronises the recorded events and returns the number of launches and
+ * their summed duration for kernels whose name starts with `prefix`. */
 int specv_timing_enable(int on);
 int specv_timing_reset(void);
 int specv_timing_read(const char* prefix, int* launches, double* total_ms);

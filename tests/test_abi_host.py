@@ -21,11 +21,11 @@ def test_header_functions_exported():
 
 
 def test_workspace_sizes():
-    a = B.verify_workspace_bytes(B.GREEDY, 256, 5, 151936)
-    b = B.verify_workspace_bytes(B.SAMPLE, 256, 5, 151936)
-    assert 0 < a <= b and a % 256 == 0 and b % 256 == 0
-    assert B.verify_workspace_bytes(B.SAMPLE, 0, 5, 10) == 0
-    assert B.verify_workspace_bytes(7, 1, 5, 10) == 0
+    a = B.verify_workspace_bytes(256, 5, 151936)
+    assert 0 < a and a % 256 == 0
+    assert B.verify_workspace_bytes(0, 5, 10) == 0
+    assert B.verify_workspace_bytes(1, 0, 10) == 0
+    assert B.verify_workspace_bytes(1, 33, 10) == 0
     assert B.markov_workspace_bytes(512, 5, 151936, 256) > 0
     assert B.markov_workspace_bytes(1, 0, 10, 4) == 0
 
@@ -37,7 +37,7 @@ def _verify(**kw):
     args.update(kw)
     return B.lib().spec_verify(args["mode"], args["dtype"], args["R"], args["k"], args["V"], args["target"],
                                args["draft"], args["tokens"], args["tags"], args["cu"], args["nrows"],
-                               ctypes.c_float(args["tau"]), args["u"], args["acc"], args["out"], args["diag"],
+                               ctypes.c_float(args["tau"]), 7, 0, args["u"], args["acc"], args["out"], args["diag"],
                                args["ws"], args["wsb"], None)
 
 
@@ -50,7 +50,6 @@ def _verify(**kw):
     (dict(V=0), B.EINVAL, "V >= 1"),
     (dict(target=None), B.EINVAL, "NULL"),
     (dict(draft=None), B.EINVAL, "draft_logits"),
-    (dict(u=None), B.EINVAL, "uniforms"),
     (dict(tau=0.0), B.EINVAL, "temperature"),
     (dict(tau=-1.0), B.EINVAL, "temperature"),
     (dict(tau=float("nan")), B.EINVAL, "temperature"),
@@ -67,6 +66,12 @@ def test_verify_rejects(kw, code, msg):
 def test_greedy_needs_no_draft_or_uniforms_but_checks_rest():
     # validation passes the draft/uniform checks, then fails on the workspace size
     assert _verify(mode=B.GREEDY, draft=None, u=None, wsb=16) == B.EINVAL
+    assert "workspace" in B.last_error()
+
+
+def test_sampling_without_uniforms_uses_the_generator():
+    # NULL uniforms select the counter-based generator: validation goes on to the workspace
+    assert _verify(u=None, wsb=16) == B.EINVAL
     assert "workspace" in B.last_error()
 
 
@@ -101,12 +106,13 @@ def test_flatten_and_markov_reject():
     lib = B.lib()
     assert lib.spec_flatten(0, 5, FAKE, FAKE, FAKE, FAKE, None) == B.EINVAL
     assert lib.spec_flatten(4, 5, None, FAKE, FAKE, FAKE, None) == B.EINVAL
-    assert lib.markov_draft(B.SAMPLE, B.BF16, 4, 5, 64, 48, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE,
-                            FAKE, FAKE, FAKE, 1 << 30, None) == B.EUNSUPPORTED
+    assert lib.markov_draft(B.SAMPLE, B.BF16, 4, 5, 64, 48, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), 7, 0,
+                            FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == B.EUNSUPPORTED
     assert "d_m" in B.last_error()
-    assert lib.markov_draft(B.SAMPLE, B.F32, 4, 5, 64, 4, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), None,
+    assert lib.markov_draft(B.SAMPLE, B.F32, 4, 5, 64, 4, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.0), 7, 0, None,
                             FAKE, FAKE, FAKE, 1 << 30, None) == B.EINVAL
-    assert lib.markov_draft(B.GREEDY, B.F32, 4, 5, 64, 4, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), None,
+    assert "temperature" in B.last_error()
+    assert lib.markov_draft(B.GREEDY, B.F32, 4, 5, 64, 4, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), 7, 0, None,
                             FAKE, FAKE, FAKE, 16, None) == B.EINVAL
     assert "workspace" in B.last_error()
 
@@ -121,7 +127,7 @@ def test_verify_ex_rejects_job_writing_this_batch():
     job = B.ScheduleJob(4, 5, FAKE, FAKE, FAKE, FAKE, 4, 5, FAKE, FAKE + 256, FAKE + 512, FAKE + 768, None, FAKE,
                         1 << 20)
     args = (B.SAMPLE, B.BF16, 4, 5, 1024, FAKE, FAKE, FAKE, FAKE + 256, FAKE + 4096, FAKE + 8192,
-            ctypes.c_float(1.0), FAKE, FAKE, FAKE, None, FAKE, 1 << 30)
+            ctypes.c_float(1.0), 7, 0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30)
     assert lib.spec_verify_ex(*args, ctypes.byref(job), None) == B.EINVAL
     assert "other than this one" in B.last_error()
     bad = B.ScheduleJob(4, 0, FAKE, FAKE, FAKE, FAKE, 4, 5, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20)

@@ -64,7 +64,7 @@ def test_full_vocab_acceptance_and_first_token(name, R, steps):
     B.spec_flatten(torch.full((R,), k, **i32), k, tags, cu, nr)
     acc = torch.zeros(R, **i32)
     out = torch.zeros(R, k + 1, **i32)
-    ws = B.workspace(B.verify_workspace_bytes(B.SAMPLE, R, k, V), dev)
+    ws = B.workspace(B.verify_workspace_bytes(R, k, V), dev)
     acc_all = torch.zeros(steps, R, **i32)
     first_all = torch.zeros(steps, R, **i32)
     for t in range(steps):
