@@ -48,6 +48,9 @@ _SIGS = {
     "spec_verify_ex": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                 _c_ptr, _c_ptr, ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                 _c_ptr, _c_size, ctypes.POINTER(ScheduleJob), _c_ptr]),
+    "spec_verify_noalloc": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                     _c_ptr, _c_ptr, ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr,
+                                     _c_ptr, _c_ptr, _c_ptr]),
     "markov_draft_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "markov_draft": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
                               _c_ptr, ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size,
@@ -229,6 +232,40 @@ def spec_verify(mode, target, draft, tokens, tags, cu_rows, n_rows, temperature,
         _check(lib().spec_verify(*args, _stream(stream)))
     else:
         _check(lib().spec_verify_ex(*args, ctypes.byref(next_job), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def spec_verify_noalloc(mode, target, draft, tokens, tags, cu_rows, n_rows, temperature, uniforms,
+                        accepted_len_out, out_tokens, row_diag=None, status_out=None, stream=None,
+                        seed: int = 0, step: int = 0):
+    """spec_verify_noalloc: spec_verify with the library's static scratch in place
+    of a workspace. status_out: None or an int32/uint32 device tensor of one
+    element that receives the status word."""
+    R, k1, V = target.shape
+    k = k1 - 1
+    dt = logit_dtype(target)
+    _dev(target, "target", tuple(_LOGIT_TYPES))
+    if mode == SAMPLE:
+        _dev(draft, "draft", (target.dtype,), (R, k, V))
+        if uniforms is not None:
+            _dev(uniforms, "uniforms", (torch.float32,), (R, k + 1))
+    _dev(tokens, "tokens", (torch.int32,), (R, k))
+    _dev(tags, "tags", (torch.int32,), (R * (k + 1), 2))
+    _dev(cu_rows, "cu_rows", (torch.int32,), (R + 1,))
+    _dev(n_rows, "n_rows", (torch.int32,), (1,))
+    _dev(accepted_len_out, "accepted_len_out", (torch.int32,), (R,))
+    _dev(out_tokens, "out_tokens", (torch.int32,), (R, k + 1))
+    if row_diag is not None:
+        _dev(row_diag, "row_diag", (torch.float32,), (R * (k + 1), 4))
+    if status_out is not None:
+        _dev(status_out, "status_out", (torch.int32, torch.uint32), (1,))
+    _check(lib().spec_verify_noalloc(int(mode), dt, R, k, V, _ptr(target), _ptr(draft) if mode == SAMPLE else None,
+                                     _ptr(tokens), _ptr(tags), _ptr(cu_rows), _ptr(n_rows), float(temperature),
+                                     int(seed), int(step), _ptr(uniforms) if mode == SAMPLE else None,
+                                     _ptr(accepted_len_out), _ptr(out_tokens), _ptr(row_diag), _ptr(status_out),
+                                     _stream(stream)))
 
 
 def markov_workspace_bytes(R: int, k: int, V: int, d_m: int) -> int:

@@ -39,6 +39,7 @@
 //                    token from p of the bonus row (chunk masses from the
 //                    partials).
 #include <climits>
+#include <mutex>
 
 #include "common.h"
 #include "host.h"
@@ -952,7 +953,7 @@ static int verify_impl(int mode, int dtype, int R, int k, int V, const void* tar
                        const int32_t* draft_tokens, const int32_t* tags, const int32_t* cu_rows, const int32_t* n_rows,
                        float temperature, uint64_t seed, uint64_t step, const float* uniforms,
                        int32_t* accepted_len_out, int32_t* out_tokens, float* row_diag, void* ws, size_t ws_bytes,
-                       const SchedArgs* next, specv_stream stream) {
+                       const SchedArgs* next, specv_stream stream, uint32_t* status_word = nullptr) {
     if (mode != SPECV_GREEDY && mode != SPECV_SAMPLE)
         return fail(SPECV_EINVAL, "spec_verify: mode %d is neither greedy (0) nor sample (1)", mode);
     if (dtype != SPECV_BF16 && dtype != SPECV_F32)
@@ -1006,7 +1007,8 @@ static int verify_impl(int mode, int dtype, int R, int k, int V, const void* tar
     a.out_tokens = out_tokens;
     a.diag = row_diag;
     char* w = static_cast<char*>(ws);
-    a.hdr = reinterpret_cast<WsHeader*>(w);
+    // the kernels use only the header's first word, the status
+    a.hdr = status_word ? reinterpret_cast<WsHeader*>(status_word) : reinterpret_cast<WsHeader*>(w);
     a.part_p = reinterpret_cast<float2*>(w + lay.part_p);
     a.part_q = reinterpret_cast<float2*>(w + lay.part_q);
     a.rec = reinterpret_cast<RowRec*>(w + lay.rec);
@@ -1055,4 +1057,67 @@ extern "C" int spec_verify_ex(int mode, int dtype, int R, int k, int V, const vo
     return verify_impl(mode, dtype, R, k, V, target_logits, draft_logits, draft_tokens, tags, cu_rows, n_rows,
                        temperature, seed, step, uniforms, accepted_len_out, out_tokens, row_diag, ws, ws_bytes,
                        next ? &na : nullptr, stream);
+}
+
+// ---------------------------------------------------------------------------
+// spec_verify_noalloc: the workspace in a static device array
+// ---------------------------------------------------------------------------
+
+namespace specv {
+
+constexpr size_t kNoallocScratchBytes = size_t(SPECV_NOALLOC_SCRATCH_BYTES);
+constexpr int kMaxDevices = 64;
+
+// Every GPU the library runs on holds its own copy of this array until the
+// process ends. Host code never uses its name as an address: the per-device
+// address comes from hipGetSymbolAddress.
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with that device current) and kept.
+static int scratch_address(void*& ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(SPECV_EDEVICE, "spec_verify_noalloc: cannot query the current device");
+    if (dev >= kMaxDevices)
+        return fail(SPECV_EUNSUPPORTED, "spec_verify_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(SPECV_EDEVICE, "spec_verify_noalloc: hipGetSymbolAddress failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    ptr = g_scratch_ptr[dev];
+    return SPECV_OK;
+}
+
+}  // namespace specv
+
+extern "C" int spec_verify_noalloc(int mode, int dtype, int R, int k, int V, const void* target_logits,
+                                   const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
+                                   const int32_t* cu_rows, const int32_t* n_rows, float temperature, uint64_t seed,
+                                   uint64_t step, const float* uniforms, int32_t* accepted_len_out,
+                                   int32_t* out_tokens, float* row_diag, uint32_t* status_out, specv_stream stream) {
+    using namespace specv;
+    clear_error();
+    if (R < 1 || k < 1 || k > SPECV_MAX_K || V < 1)
+        return fail(SPECV_EINVAL, "spec_verify_noalloc: need R >= 1, 1 <= k <= %d, V >= 1 (got R=%d k=%d V=%d)",
+                    SPECV_MAX_K, R, k, V);
+    const size_t need = ws_layout(R, k, V).total;
+    if (need > kNoallocScratchBytes)
+        return fail(SPECV_EUNSUPPORTED,
+                    "spec_verify_noalloc: R=%d, k=%d, V=%d needs %zu bytes of scratch, above the static %zu "
+                    "(SPECV_NOALLOC_SCRATCH_BYTES); use spec_verify with a workspace",
+                    R, k, V, need, kNoallocScratchBytes);
+    void* ws = nullptr;
+    if (int e = scratch_address(ws)) return e;
+    return verify_impl(mode, dtype, R, k, V, target_logits, draft_logits, draft_tokens, tags, cu_rows, n_rows,
+                       temperature, seed, step, uniforms, accepted_len_out, out_tokens, row_diag, ws,
+                       kNoallocScratchBytes, nullptr, stream, status_out);
 }

@@ -283,6 +283,39 @@ int spec_verify_ex(int mode, int dtype, int R, int k, int V, const void* target_
                    specv_stream stream);
 
 /* ------------------------------------------------------------------------ */
+/* spec_verify_noalloc: spec_verify without a workspace                      */
+/* ------------------------------------------------------------------------ */
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. It computes
+ * exactly what spec_verify computes (same kernels), but its chunk partials
+ * live in one static device array of SPECV_NOALLOC_SCRATCH_BYTES inside the
+ * library, which each GPU the library runs on holds until the process ends.
+ * The call allocates nothing: it looks the array's address up once per device
+ * (on its first call there) and then only enqueues kernels.
+ *
+ * Arguments: as spec_verify, without ws and ws_bytes, plus
+ *   status_out  NULL, or a device u32 that receives the status word (0 or
+ *               SPECV_STATUS_* bits) when the call's kernels have run; with
+ *               NULL the status word stays inside the library.
+ * Limit: spec_verify_workspace_bytes(R, k, V) <= SPECV_NOALLOC_SCRATCH_BYTES
+ *   (e.g. R = 512, k = 5, V = 151936 needs 7.7 MB); larger batches return
+ *   SPECV_EUNSUPPORTED with the sizes in the message.
+ * Every call on one GPU uses that GPU's one array and leaves its contents
+ * behind (the kernels clear what must start at zero): calls that may overlap
+ * on one GPU, on different streams or from different host threads, race and
+ * must be serialised by the caller. Not usable with spec_verify_ex's
+ * next-round schedule.
+ * Errors: as spec_verify.
+ */
+#define SPECV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int spec_verify_noalloc(int mode, int dtype, int R, int k, int V, const void* target_logits,
+                        const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
+                        const int32_t* cu_rows, const int32_t* n_rows, float temperature, uint64_t seed,
+                        uint64_t step, const float* uniforms, int32_t* accepted_len_out,
+                        int32_t* out_tokens, float* row_diag, uint32_t* status_out, specv_stream stream);
+
+/* ------------------------------------------------------------------------ */
 /* markov_draft                                                              */
 /* ------------------------------------------------------------------------ */
 /*
