@@ -1,9 +1,12 @@
 """Build libspecv.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m draft_token_verification_flattened_amd.build
+    python -m draft_token_verification_flattened_amd.build [--sanitized-check]
 
 The library is written next to this file so that it travels with the source
-tree; every call recompiles.
+tree; every call recompiles. build_sanitized_check() compiles the same sources
+and tests/abi_sanitized_check.cpp into one host executable with
+AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (device
+code is built as usual), for the C ABI's argument validation and host state.
 """
 from __future__ import annotations
 
@@ -81,5 +84,54 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host code only: each sanitizer flag goes to the host compilation and link.
+SANITIZE = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+SAN_DIR = os.path.join(OBJDIR, "sanitized")
+SAN_CHECK = os.path.join(SAN_DIR, "abi_sanitized_check")
+SAN_DRIVER = os.path.join(ROOT, "tests", "abi_sanitized_check.cpp")
+
+
+def build_sanitized_check(verbose: bool = False, planted: bool = False) -> str:
+    """The sanitized host check executable (see the module docstring).
+    planted=True builds a copy whose driver ends with a heap overflow, the
+    control that shows the sanitizers are active (it must abort)."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    hipcc = _hipcc()
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g"] + SANITIZE
+    if planted:
+        flags.append("-DSPECV_PLANTED_OVERFLOW")
+    tag = "_planted" if planted else ""
+
+    def one(src):
+        path = src if os.path.isabs(src) else os.path.join(CSRC, src)
+        obj = os.path.join(SAN_DIR, os.path.splitext(os.path.basename(src))[0] + tag + ".o")
+        cmd = [hipcc, "-xhip", *flags, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", path, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
+        return obj
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(one, SOURCES + [SAN_DRIVER]))
+    exe = SAN_CHECK + tag
+    cmd = [hipcc, f"--offload-arch={ARCH}", *SANITIZE, "-o", exe, *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    return exe
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitized-check" in sys.argv:
+        print(build_sanitized_check(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))
