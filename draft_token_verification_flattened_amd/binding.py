@@ -22,7 +22,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "specv.h")
 OK, EINVAL, EUNSUPPORTED, EDEVICE = 0, -1, -2, -3
 BF16, F32 = 0, 1
 GREEDY, SAMPLE = 0, 1
-STATUS_BAD_TOKEN, STATUS_BAD_TAG, STATUS_BAD_PAGE, STATUS_NONFINITE = 1, 2, 4, 8
+STATUS_BAD_TOKEN, STATUS_BAD_TAG, STATUS_BAD_PAGE, STATUS_NONFINITE, STATUS_BAD_STATS = 1, 2, 4, 8, 16
+DRAFT_STAT_WORDS = 8        # specv_draft_stat: m, z, x_logit, c (float), token, 3 pad (int32)
 MAX_K, MAX_SCHED_ITEMS = 32, 16384
 KV_POSITION_MAJOR, KV_HEAD_MAJOR = 0, 1
 
@@ -47,18 +48,18 @@ _SIGS = {
                              _c_ptr, _c_size, _c_ptr]),
     "spec_verify_ex": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                 _c_ptr, _c_ptr, ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
-                                _c_ptr, _c_size, ctypes.POINTER(ScheduleJob), _c_ptr]),
+                                _c_ptr, _c_size, _c_ptr, ctypes.POINTER(ScheduleJob), _c_ptr]),
     "spec_verify_noalloc": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                      _c_ptr, _c_ptr, ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr,
                                      _c_ptr, _c_ptr, _c_ptr]),
     "markov_draft_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "markov_draft": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
-                              _c_ptr, ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size,
-                              _c_ptr]),
+                              _c_ptr, ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                              _c_size, _c_ptr]),
     "spec_attention_workspace_bytes": (_c_size, [_c_int] * 7),
     "spec_attention": (_c_int, [_c_int] * 10 + [_c_ptr] * 9 + [_c_ptr, _c_size, _c_ptr]),
     "rnn_draft_workspace_bytes": (_c_size, [_c_int] * 4),
-    "rnn_draft": (_c_int, [_c_int] * 6 + [_c_ptr] * 5 + [ctypes.c_float, _c_u64, _c_u64] + [_c_ptr] * 5
+    "rnn_draft": (_c_int, [_c_int] * 6 + [_c_ptr] * 5 + [ctypes.c_float, _c_u64, _c_u64] + [_c_ptr] * 6
                   + [_c_size, _c_ptr]),
     "specv_last_error": (ctypes.c_char_p, []),
     "specv_read_status": (_c_int, [_c_ptr, _c_ptr, ctypes.POINTER(ctypes.c_uint32)]),
@@ -203,10 +204,12 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 def spec_verify(mode, target, draft, tokens, tags, cu_rows, n_rows, temperature, uniforms, accepted_len_out,
                 out_tokens, ws, row_diag=None, stream=None, next_job: Optional[ScheduleJob] = None,
-                seed: int = 0, step: int = 0):
-    """spec_verify; with next_job, spec_verify_ex (the job's schedule runs
-    beside this call's decisions). uniforms None: the library's counter-based
-    uniforms keyed by (seed, step)."""
+                seed: int = 0, step: int = 0, draft_stats=None):
+    """spec_verify; with next_job or draft_stats, spec_verify_ex (the job's
+    schedule runs beside this call's decisions; the draft head's statistics
+    replace the pass over the draft rows). uniforms None: the library's
+    counter-based uniforms keyed by (seed, step). draft_stats: a float32
+    device tensor [R, k, 8] holding specv_draft_stat records."""
     R, k1, V = target.shape
     k = k1 - 1
     dt = logit_dtype(target)
@@ -224,14 +227,17 @@ def spec_verify(mode, target, draft, tokens, tags, cu_rows, n_rows, temperature,
     _dev(ws, "ws", (torch.uint8,))
     if row_diag is not None:
         _dev(row_diag, "row_diag", (torch.float32,), (R * (k + 1), 4))
+    if draft_stats is not None:
+        _dev(draft_stats, "draft_stats", (torch.float32,), (R, k, DRAFT_STAT_WORDS))
     args = (int(mode), dt, R, k, V, _ptr(target), _ptr(draft) if mode == SAMPLE else None,
             _ptr(tokens), _ptr(tags), _ptr(cu_rows), _ptr(n_rows), float(temperature), int(seed), int(step),
             _ptr(uniforms) if mode == SAMPLE else None, _ptr(accepted_len_out),
             _ptr(out_tokens), _ptr(row_diag), _ptr(ws), ws.numel())
-    if next_job is None:
+    if next_job is None and draft_stats is None:
         _check(lib().spec_verify(*args, _stream(stream)))
     else:
-        _check(lib().spec_verify_ex(*args, ctypes.byref(next_job), _stream(stream)))
+        _check(lib().spec_verify_ex(*args, _ptr(draft_stats), ctypes.byref(next_job) if next_job is not None else None,
+                                    _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -273,9 +279,10 @@ def markov_workspace_bytes(R: int, k: int, V: int, d_m: int) -> int:
 
 
 def markov_draft(mode, backbone, emb, proj, prev_token, temperature, uniforms, tokens_out, logits_out, ws,
-                 stream=None, seed: int = 0, step: int = 0):
+                 stream=None, seed: int = 0, step: int = 0, stats_out=None):
     """markov_draft; uniforms None: the library's counter-based uniforms keyed
-    by (seed, step)."""
+    by (seed, step). stats_out: None or a float32 device tensor [R, k, 8] for
+    the specv_draft_stat records (sampling)."""
     R, k, V = backbone.shape
     d_m = emb.shape[1]
     dt = logit_dtype(backbone)
@@ -288,10 +295,13 @@ def markov_draft(mode, backbone, emb, proj, prev_token, temperature, uniforms, t
     _dev(ws, "ws", (torch.uint8,))
     if mode == SAMPLE and uniforms is not None:
         _dev(uniforms, "uniforms", (torch.float32,), (R, k))
+    if stats_out is not None:
+        _dev(stats_out, "stats_out", (torch.float32,), (R, k, DRAFT_STAT_WORDS))
     _check(lib().markov_draft(int(mode), dt, R, k, V, d_m, _ptr(backbone), _ptr(emb), _ptr(proj),
                               _ptr(prev_token), float(temperature), int(seed), int(step),
                               _ptr(uniforms) if mode == SAMPLE else None,
-                              _ptr(tokens_out), _ptr(logits_out), _ptr(ws), ws.numel(), _stream(stream)))
+                              _ptr(tokens_out), _ptr(logits_out), _ptr(stats_out), _ptr(ws), ws.numel(),
+                              _stream(stream)))
 
 
 def attention_workspace_bytes(R: int, k: int, Hq: int, Hkv: int, page_size: int, max_pages: int,
@@ -333,9 +343,9 @@ def rnn_workspace_bytes(R: int, k: int, V: int, d_m: int) -> int:
 
 
 def rnn_draft(mode, backbone, emb, rec, proj, prev_token, temperature, uniforms, tokens_out, logits_out, ws,
-              state_out=None, stream=None, seed: int = 0, step: int = 0):
+              state_out=None, stream=None, seed: int = 0, step: int = 0, stats_out=None):
     """rnn_draft; uniforms None: the library's counter-based uniforms keyed by
-    (seed, step)."""
+    (seed, step); stats_out as markov_draft."""
     R, k, V = backbone.shape
     d_m = emb.shape[1]
     dt = logit_dtype(backbone)
@@ -351,10 +361,12 @@ def rnn_draft(mode, backbone, emb, rec, proj, prev_token, temperature, uniforms,
         _dev(state_out, "state_out", (backbone.dtype,), (R, k, d_m))
     if mode == SAMPLE and uniforms is not None:
         _dev(uniforms, "uniforms", (torch.float32,), (R, k))
+    if stats_out is not None:
+        _dev(stats_out, "stats_out", (torch.float32,), (R, k, DRAFT_STAT_WORDS))
     _check(lib().rnn_draft(int(mode), dt, R, k, V, d_m, _ptr(backbone), _ptr(emb), _ptr(rec), _ptr(proj),
                            _ptr(prev_token), float(temperature), int(seed), int(step),
                            _ptr(uniforms) if mode == SAMPLE else None,
-                           _ptr(tokens_out), _ptr(logits_out), _ptr(state_out), _ptr(ws), ws.numel(),
+                           _ptr(tokens_out), _ptr(logits_out), _ptr(stats_out), _ptr(state_out), _ptr(ws), ws.numel(),
                            _stream(stream)))
 
 

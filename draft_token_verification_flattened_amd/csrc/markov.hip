@@ -53,6 +53,7 @@ struct MarkovArgs {
     uint64_t seed, step;            // their key
     int32_t* tokens;                // [R,k]
     void* dl;                       // [R,k,V]
+    specv_draft_stat* stats;        // [R,k] or NULL (sampling): the rows' softmax states for verification
     float2* part;                   // [R * S]
     WsHeader* hdr;
 };
@@ -670,6 +671,8 @@ __global__ __launch_bounds__(256) void markov_pick(MarkovArgs a) {
             a.S, a.V, kSlice, thr,
             [&](int s) { float2 q = pr[s]; return q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - M); },
             [&](int e) { return exp2f(fmaf(LT::load1(row + e), c, -M)); }, lane);
+        if (a.stats && lane == 0)
+            a.stats[long(m) * a.k + a.pos] = specv_draft_stat{M, tot.b, LT::load1(row + y), c, y, {0, 0, 0}};
     }
     if (lane == 0) a.tokens[long(m) * a.k + a.pos] = y;
 }
@@ -793,7 +796,11 @@ __global__ __launch_bounds__(kPickThreads) void markov_pick_wg(MarkovArgs a) {
     const int ehit = wave_min_int((e < a.V && run > thr) ? e : INT_MAX);
     const int elast = -wave_min_int((we > 0.f) ? -e : 1);
     const int y = ehit != INT_MAX ? ehit : (elast >= 0 ? elast : sel * kSlice);
-    if (lane == 0) a.tokens[long(m) * a.k + a.pos] = y;
+    if (lane == 0) {
+        a.tokens[long(m) * a.k + a.pos] = y;
+        if (a.stats)     // the row's softmax state and the drawn token's stored logit, for verification
+            a.stats[long(m) * a.k + a.pos] = specv_draft_stat{M, tot.b, LT::load1(row + y), a.c, y, {0, 0, 0}};
+    }
 }
 
 }  // namespace specv
@@ -813,7 +820,8 @@ size_t head_workspace_bytes(int R, int k, int V, int d_m, bool state) {
 int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
                const void* emb, const void* rec, const void* proj, const int32_t* prev_token, float temperature,
                uint64_t seed, uint64_t step, const float* uniforms, int32_t* draft_tokens_out,
-               void* draft_logits_out, void* state_out, void* ws, size_t ws_bytes, hipStream_t s) {
+               void* draft_logits_out, specv_draft_stat* stats_out, void* state_out, void* ws, size_t ws_bytes,
+               hipStream_t s) {
     clear_error();
     const bool rnn = rec != nullptr;
     if (mode != SPECV_GREEDY && mode != SPECV_SAMPLE)
@@ -844,6 +852,7 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
     a.bk = backbone_logits; a.emb = emb; a.proj = proj; a.prev = prev_token;
     a.uniforms = uniforms; a.seed = seed; a.step = step;
     a.tokens = draft_tokens_out; a.dl = draft_logits_out;
+    a.stats = mode == SPECV_SAMPLE ? stats_out : nullptr;
     a.hdr = static_cast<WsHeader*>(ws);
     a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + 256);
     a.rec = rec;
@@ -910,10 +919,11 @@ extern "C" size_t markov_draft_workspace_bytes(int R, int k, int V, int d_m) {
 extern "C" int markov_draft(int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
                             const void* emb, const void* proj, const int32_t* prev_token, float temperature,
                             uint64_t seed, uint64_t step, const float* uniforms, int32_t* draft_tokens_out,
-                            void* draft_logits_out, void* ws, size_t ws_bytes, specv_stream stream) {
+                            void* draft_logits_out, specv_draft_stat* draft_stats_out, void* ws, size_t ws_bytes,
+                            specv_stream stream) {
     return specv::head_draft("markov_draft", mode, dtype, R, k, V, d_m, backbone_logits, emb, nullptr, proj,
                              prev_token, temperature, seed, step, uniforms, draft_tokens_out, draft_logits_out,
-                             nullptr, ws, ws_bytes, static_cast<hipStream_t>(stream));
+                             draft_stats_out, nullptr, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 extern "C" size_t rnn_draft_workspace_bytes(int R, int k, int V, int d_m) {
@@ -923,13 +933,13 @@ extern "C" size_t rnn_draft_workspace_bytes(int R, int k, int V, int d_m) {
 extern "C" int rnn_draft(int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
                          const void* emb, const void* rec, const void* proj, const int32_t* prev_token,
                          float temperature, uint64_t seed, uint64_t step, const float* uniforms,
-                         int32_t* draft_tokens_out, void* draft_logits_out, void* state_out, void* ws,
-                         size_t ws_bytes, specv_stream stream) {
+                         int32_t* draft_tokens_out, void* draft_logits_out, specv_draft_stat* draft_stats_out,
+                         void* state_out, void* ws, size_t ws_bytes, specv_stream stream) {
     if (!rec) {
         specv::clear_error();
         return specv::fail(SPECV_EINVAL, "rnn_draft: NULL required pointer (rec)");
     }
     return specv::head_draft("rnn_draft", mode, dtype, R, k, V, d_m, backbone_logits, emb, rec, proj, prev_token,
-                             temperature, seed, step, uniforms, draft_tokens_out, draft_logits_out, state_out, ws,
-                             ws_bytes, static_cast<hipStream_t>(stream));
+                             temperature, seed, step, uniforms, draft_tokens_out, draft_logits_out, draft_stats_out,
+                             state_out, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }

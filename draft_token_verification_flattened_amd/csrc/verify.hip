@@ -71,6 +71,7 @@ struct VerifyArgs {
     const int32_t* cu_rows;
     const int32_t* n_rows;
     const float* uniforms;                  // [R, k+1], or NULL: counter-based uniforms (common.h)
+    const specv_draft_stat* stats;          // [R, k] or NULL (sampling): q's state per draft row; no draft items
     uint64_t seed, step;                    // the key of those uniforms
     float c;                                // log2(e) / tau
     int32_t* acc_len;
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
         for (int i = tid; i < a.R; i += kStreamThreads) a.res_cnt[i] = 0;
     const int C = a.C, CH = a.CH, V = a.V, K = a.k;
     const uint32_t region = uint32_t(a.Bmax) * uint32_t(C);          // slots per tensor
-    const uint32_t slots = SAMPLE ? 2 * region : region;
+    const uint32_t slots = (SAMPLE && !a.stats) ? 2 * region : region;
     if (b >= slots) return;
     const uint32_t mine = (slots - 1 - b) / G + 1;                   // slots b + i G, i < mine
     const float c = a.c;
@@ -658,7 +659,7 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
     __shared__ int g_s[SPECV_MAX_K + 1];
     __shared__ float4 st_s[SPECV_MAX_K + 1];
     __shared__ float mass_s[SAMPLE ? kMaxChunks : 1];
-    __shared__ int bad_s, nonfinite_s, rnext_s, last_s;
+    __shared__ int bad_s, nonfinite_s, stats_bad_s, rnext_s, last_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = int(blockIdx.x) / nsplit, part = int(blockIdx.x) % nsplit;
     const bool writer = part == 0;                 // the workgroup that writes the request's decisions
@@ -671,6 +672,7 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
     if (tid == 0) {
         bad_s = L < 0 || L > k || base < 0 || base + L > N || N < 0 || N + r >= nrows;
         nonfinite_s = 0;
+        stats_bad_s = 0;
         rnext_s = 0;
     }
     __syncthreads();
@@ -688,11 +690,22 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
                 uj = a.uniforms ? a.uniforms[long(r) * (k + 1) + j] : philox_uniform(a.seed, a.step, kPurposeAccept, r, j);
                 rc = a.rec[t];
             }
+            specv_draft_stat ds{};
+            if (SAMPLE && verified && a.stats) ds = a.stats[long(r) * k + j];
             const float2 P = merge_partials<SAMPLE>(a.part_p + long(t) * C, C, lane);
             float2 Q = make_float2(-INFINITY, 0.f);
-            if (SAMPLE && verified) Q = merge_partials<true>(a.part_q + long(t) * C, C, lane);
+            if (SAMPLE && verified) {
+                if (a.stats) {                     // q's state and q(x) from the draft head
+                    Q = make_float2(ds.m, ds.z);
+                    rc.bx = ds.x_logit;
+                } else {
+                    Q = merge_partials<true>(a.part_q + long(t) * C, C, lane);
+                }
+            }
             if (lane != 0) continue;               // lane 0 decides the row
             if (tag_r != r || tag_j != j) bad_s = 1;
+            if (SAMPLE && verified && a.stats && (__float_as_uint(ds.c) != __float_as_uint(a.c) || ds.token != x))
+                stats_bad_s = 1;
             // a row with a NaN or +inf logit: a softmax state (M, S) that is not
             // finite (an all -inf row too: no distribution), or in greedy mode the
             // (+inf, INT_MIN) mark of verify_stream
@@ -727,11 +740,12 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
         }
     }
     __syncthreads();
-    if (bad_s || nonfinite_s) {
+    if (bad_s || nonfinite_s || stats_bad_s) {
         // a data error: the request's results are void (accepted length 0, no tokens)
         if (!writer) return;
         if (tid == 0) {
-            atomicOr(&a.hdr->status, bad_s ? SPECV_STATUS_BAD_TAG : SPECV_STATUS_NONFINITE);
+            atomicOr(&a.hdr->status, bad_s ? SPECV_STATUS_BAD_TAG
+                                           : (stats_bad_s ? SPECV_STATUS_BAD_STATS : SPECV_STATUS_NONFINITE));
             a.acc_len[r] = 0;
         }
         if (tid <= k) out[tid] = -1;
@@ -920,7 +934,7 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
         return launch_decide(verify_decide<DT, SPECV_GREEDY, VEC, kDecideThreads>, kDecideThreads, a, next, s);
     }
     auto ks = verify_stream<DT, SPECV_SAMPLE, VEC>;
-    if (int e = stream_grid(ks, 2L * a.Bmax * a.C, cus, G)) return e;
+    if (int e = stream_grid(ks, (a.stats ? 1L : 2L) * a.Bmax * a.C, cus, G)) return e;
     // One 1024-thread decide workgroup fits per compute unit. With fewer requests
     // than compute units a rejected row pair is re-read by up to four of them
     // (each with at least a chunk per wavefront); with more requests than compute
@@ -953,7 +967,8 @@ static int verify_impl(int mode, int dtype, int R, int k, int V, const void* tar
                        const int32_t* draft_tokens, const int32_t* tags, const int32_t* cu_rows, const int32_t* n_rows,
                        float temperature, uint64_t seed, uint64_t step, const float* uniforms,
                        int32_t* accepted_len_out, int32_t* out_tokens, float* row_diag, void* ws, size_t ws_bytes,
-                       const SchedArgs* next, specv_stream stream, uint32_t* status_word = nullptr) {
+                       const SchedArgs* next, specv_stream stream, uint32_t* status_word = nullptr,
+                       const specv_draft_stat* draft_stats = nullptr) {
     if (mode != SPECV_GREEDY && mode != SPECV_SAMPLE)
         return fail(SPECV_EINVAL, "spec_verify: mode %d is neither greedy (0) nor sample (1)", mode);
     if (dtype != SPECV_BF16 && dtype != SPECV_F32)
@@ -1000,6 +1015,7 @@ static int verify_impl(int mode, int dtype, int R, int k, int V, const void* tar
     a.cu_rows = cu_rows;
     a.n_rows = n_rows;
     a.uniforms = uniforms;
+    a.stats = mode == SPECV_SAMPLE ? draft_stats : nullptr;
     a.seed = seed;
     a.step = step;
     a.c = mode == SPECV_SAMPLE ? float(1.4426950408889634 / double(temperature)) : 1.f;
@@ -1040,8 +1056,8 @@ extern "C" int spec_verify_ex(int mode, int dtype, int R, int k, int V, const vo
                               const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
                               const int32_t* cu_rows, const int32_t* n_rows, float temperature, uint64_t seed,
                               uint64_t step, const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
-                              float* row_diag, void* ws, size_t ws_bytes, const specv_schedule_job* next,
-                              specv_stream stream) {
+                              float* row_diag, void* ws, size_t ws_bytes, const specv_draft_stat* draft_stats,
+                              const specv_schedule_job* next, specv_stream stream) {
     using namespace specv;
     clear_error();
     SchedArgs na;
@@ -1056,7 +1072,7 @@ extern "C" int spec_verify_ex(int mode, int dtype, int R, int k, int V, const vo
     }
     return verify_impl(mode, dtype, R, k, V, target_logits, draft_logits, draft_tokens, tags, cu_rows, n_rows,
                        temperature, seed, step, uniforms, accepted_len_out, out_tokens, row_diag, ws, ws_bytes,
-                       next ? &na : nullptr, stream);
+                       next ? &na : nullptr, stream, nullptr, draft_stats);
 }
 
 // ---------------------------------------------------------------------------

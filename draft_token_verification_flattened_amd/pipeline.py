@@ -70,9 +70,14 @@ class DeviceStep:
         self.diag = torch.zeros(R * (k + 1), 4, dtype=torch.float32, device=device)
         self.ws_verify = B.workspace(B.verify_workspace_bytes(R, k, V), device)
         self.ws_sched = B.workspace(B.schedule_workspace_bytes(R, k), device)
+        # the draft head's per-row softmax states (sampling): spec_verify_ex then
+        # skips the pass over the draft rows (use_stats)
+        self.use_stats = True
+        self.draft_stats = None
         if w.backbone is not None:
             self.draft_tokens = torch.zeros(R, k, **i32)
             self.draft_logits = torch.zeros(R, k, V, dtype=self.backbone.dtype, device=device)
+            self.draft_stats = torch.zeros(R, k, B.DRAFT_STAT_WORDS, dtype=torch.float32, device=device)
             nbytes = (B.rnn_workspace_bytes if head == "rnn" else B.markov_workspace_bytes)(R, k, V, w.d_m)
             self.ws_markov = B.workspace(nbytes, device)
 
@@ -98,11 +103,18 @@ class DeviceStep:
         if self.head == "rnn":
             B.rnn_draft(mode, self.backbone, self.emb, self.rec, self.proj, self.prev, self.w.tau, u["uniforms"],
                         self.draft_tokens, self.draft_logits, self.ws_markov, stream=stream, seed=u["seed"],
-                        step=u["step"])
+                        step=u["step"], stats_out=self.draft_stats)
         else:
             B.markov_draft(mode, self.backbone, self.emb, self.proj, self.prev, self.w.tau, u["uniforms"],
                            self.draft_tokens, self.draft_logits, self.ws_markov, stream=stream, seed=u["seed"],
-                           step=u["step"])
+                           step=u["step"], stats_out=self.draft_stats)
+
+    def stats_for(self, mode, draft=None, tokens=None):
+        """The draft statistics to hand to verification: the head's, when it
+        verifies the head's own drafts in sampling mode and use_stats is on."""
+        if mode == B.SAMPLE and self.use_stats and self.draft_stats is not None and draft is None and tokens is None:
+            return self.draft_stats
+        return None
 
     def drafts(self, mode):
         """(draft logits, draft tokens) the verifier uses for this workload and mode."""
@@ -112,12 +124,13 @@ class DeviceStep:
 
     def verify(self, mode, draft=None, tokens=None, diag=True, stream=None):
         d, t = self.drafts(mode)
+        st = self.stats_for(mode, draft, tokens)
         d = d if draft is None else draft
         t = t if tokens is None else tokens
         u = self.uniforms("u_verify")
         B.spec_verify(mode, self.target, d, t, self.tags, self.cu_rows, self.n_rows, self.w.tau, u["uniforms"],
                       self.acc_len, self.out_tokens, self.ws_verify, row_diag=self.diag if diag else None,
-                      stream=stream, seed=u["seed"], step=u["step"])
+                      stream=stream, seed=u["seed"], step=u["step"], draft_stats=st)
 
     def use_copy(self, i: int):
         for n, t in self._copies[i % len(self._copies)].items():
@@ -198,7 +211,7 @@ class LaggedStep:
         B.spec_verify(mode, d.target, dl, tk, self.tags[s], self.cu_rows[s], self.n_rows[s], d.w.tau,
                       u["uniforms"], self.acc_len[s], self.out_tokens[s], d.ws_verify,
                       row_diag=d.diag if diag else None, next_job=self._job(o, t + 1 - self.lag), seed=u["seed"],
-                      step=u["step"])
+                      step=u["step"], draft_stats=d.stats_for(mode))
         self.t = t + 1
 
     def capture(self, mode, rounds: int):

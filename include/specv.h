@@ -75,9 +75,24 @@ enum {
     SPECV_STATUS_BAD_TAG = 2u,   /* tags[] disagrees with cu_rows[] */
     SPECV_STATUS_BAD_PAGE = 4u,  /* spec_attention: a page id outside [0, num_pages), or a
                                     context length that is negative or overruns its page-table row */
-    SPECV_STATUS_NONFINITE = 8u  /* a logit row with a NaN or +inf value (sampling: also a row
+    SPECV_STATUS_NONFINITE = 8u, /* a logit row with a NaN or +inf value (sampling: also a row
                                     of -inf only, which has no distribution) */
+    SPECV_STATUS_BAD_STATS = 16u /* spec_verify_ex: a draft statistic made at another temperature
+                                    or for another token than the one verified */
 };
+
+/* The draft head's statistics of one draft row (r, i), written by markov_draft
+ * and rnn_draft in sampling mode, read by spec_verify_ex: the base-2 softmax
+ * state of the stored draft logits, so that verification needs no pass over
+ * the draft rows. */
+typedef struct {
+    float m;          /* max over the row of logit * c */
+    float z;          /* sum over the row of exp2(logit * c - m) */
+    float x_logit;    /* the stored logit of the drawn token */
+    float c;          /* log2(e) / temperature, the scale used */
+    int32_t token;    /* the drawn token */
+    int32_t pad[3];
+} specv_draft_stat;
 
 /* Limits of the scheduler: all candidate keys of one call are held in the
  * local data share of each of its workgroups. */
@@ -256,6 +271,14 @@ int spec_verify(int mode, int dtype, int R, int k, int V, const void* target_log
  *   are spec_schedule's arguments (device pointers as there). Its batch
  *   (tags_out, cu_rows_out, n_rows_out) must be other buffers than this call's
  *   tags, cu_rows and n_rows, and nothing else may use its workspace meanwhile.
+ *
+ * draft_stats: NULL, or (sampling) the draft head's specv_draft_stat [R,k] for
+ *   these draft rows (markov_draft / rnn_draft, same temperature). q's
+ *   normaliser and q(x) then come from them and the verification pass reads
+ *   no draft row; the draft logits are still read for the rejected rows'
+ *   residuals. A statistic whose scale c is not log2(e)/temperature, or whose
+ *   token is not draft_tokens[r,i], voids its request and sets
+ *   SPECV_STATUS_BAD_STATS. Ignored in greedy mode.
  * Errors: as spec_verify and spec_schedule (with "spec_verify_ex (next)" in the
  *   message for the job); SPECV_EINVAL if the next batch is this one.
  */
@@ -279,8 +302,8 @@ int spec_verify_ex(int mode, int dtype, int R, int k, int V, const void* target_
                    const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
                    const int32_t* cu_rows, const int32_t* n_rows, float temperature, uint64_t seed,
                    uint64_t step, const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
-                   float* row_diag, void* ws, size_t ws_bytes, const specv_schedule_job* next,
-                   specv_stream stream);
+                   float* row_diag, void* ws, size_t ws_bytes, const specv_draft_stat* draft_stats,
+                   const specv_schedule_job* next, specv_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* spec_verify_noalloc: spec_verify without a workspace                      */
@@ -329,7 +352,9 @@ int spec_verify_noalloc(int mode, int dtype, int R, int k, int V, const void* ta
  *         softmax(dl[r,i,:] / tau) with u = U(seed, step, 2, r, i), or
  *         uniforms[r,i] (sampling).
  * The rounded logits are written out: they are the draft distribution the
- * verifier must use. A row whose softmax state (sampling) or maximum (greedy:
+ * verifier must use. In sampling mode the call can also write each draft row's
+ * specv_draft_stat (draft_stats_out), which lets spec_verify_ex skip the pass
+ * over the draft rows. A row whose softmax state (sampling) or maximum (greedy:
  * +inf) is not finite sets SPECV_STATUS_NONFINITE; its token is then
  * unspecified (within [0, V)).
  *
@@ -349,6 +374,7 @@ int spec_verify_noalloc(int mode, int dtype, int R, int k, int V, const void* ta
  *   seed, step      host uint64: the key of the uniforms (sampling)
  *   uniforms        NULL (the generator), or f32 [R,k] (sampling)
  *   draft_tokens_out i32 [R,k];  draft_logits_out [R,k,V] dtype
+ *   draft_stats_out  NULL, or specv_draft_stat [R,k] (written in sampling mode)
  *   ws, ws_bytes    at least markov_draft_workspace_bytes(R,k,V,d_m)
  * Errors: as spec_verify.
  */
@@ -356,8 +382,8 @@ size_t markov_draft_workspace_bytes(int R, int k, int V, int d_m);
 int markov_draft(int mode, int dtype, int R, int k, int V, int d_m,
                  const void* backbone_logits, const void* emb, const void* proj,
                  const int32_t* prev_token, float temperature, uint64_t seed, uint64_t step,
-                 const float* uniforms, int32_t* draft_tokens_out, void* draft_logits_out, void* ws,
-                 size_t ws_bytes, specv_stream stream);
+                 const float* uniforms, int32_t* draft_tokens_out, void* draft_logits_out,
+                 specv_draft_stat* draft_stats_out, void* ws, size_t ws_bytes, specv_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* rnn_draft                                                                 */
@@ -385,8 +411,8 @@ size_t rnn_draft_workspace_bytes(int R, int k, int V, int d_m);
 int rnn_draft(int mode, int dtype, int R, int k, int V, int d_m, const void* backbone_logits,
               const void* emb, const void* rec, const void* proj, const int32_t* prev_token,
               float temperature, uint64_t seed, uint64_t step, const float* uniforms,
-              int32_t* draft_tokens_out, void* draft_logits_out, void* state_out, void* ws,
-              size_t ws_bytes, specv_stream stream);
+              int32_t* draft_tokens_out, void* draft_logits_out, specv_draft_stat* draft_stats_out,
+              void* state_out, void* ws, size_t ws_bytes, specv_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* spec_attention                                                            */

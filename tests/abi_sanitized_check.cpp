@@ -98,7 +98,7 @@ int main() {
     job.n_rows_out = fake<int32_t>(768); job.ws = FAKE; job.ws_bytes = size_t(1) << 20;
     expect_code(spec_verify_ex(SPECV_SAMPLE, SPECV_BF16, 4, 5, 1024, FAKE, FAKE, fake<int32_t>(), fake<int32_t>(256),
                                fake<int32_t>(4096), fake<int32_t>(8192), 1.f, 7, 0, nullptr, fake<int32_t>(),
-                               fake<int32_t>(), nullptr, FAKE, big, &job, nullptr),
+                               fake<int32_t>(), nullptr, FAKE, big, nullptr, &job, nullptr),
                 SPECV_EINVAL, "other than this one", "verify_ex same batch");
 
     // spec_schedule / spec_flatten
@@ -118,13 +118,13 @@ int main() {
 
     // the draft heads
     expect_code(markov_draft(SPECV_SAMPLE, SPECV_BF16, 4, 5, 64, 48, FAKE, FAKE, FAKE, fake<int32_t>(), 1.f, 7, 0,
-                             nullptr, fake<int32_t>(), FAKE, FAKE, big, nullptr),
+                             nullptr, fake<int32_t>(), FAKE, nullptr, FAKE, big, nullptr),
                 SPECV_EUNSUPPORTED, "d_m", "markov d_m");
     expect_code(markov_draft(SPECV_SAMPLE, SPECV_F32, 4, 5, 64, 4, FAKE, FAKE, FAKE, fake<int32_t>(), 0.f, 7, 0,
-                             nullptr, fake<int32_t>(), FAKE, FAKE, big, nullptr),
+                             nullptr, fake<int32_t>(), FAKE, nullptr, FAKE, big, nullptr),
                 SPECV_EINVAL, "temperature", "markov tau");
     expect_code(rnn_draft(SPECV_SAMPLE, SPECV_F32, 4, 5, 64, 4, FAKE, FAKE, nullptr, FAKE, fake<int32_t>(), 1.f, 7, 0,
-                          nullptr, fake<int32_t>(), FAKE, nullptr, FAKE, big, nullptr),
+                          nullptr, fake<int32_t>(), FAKE, nullptr, nullptr, FAKE, big, nullptr),
                 SPECV_EINVAL, "rec", "rnn rec");
 
     // spec_attention

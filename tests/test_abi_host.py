@@ -107,13 +107,13 @@ def test_flatten_and_markov_reject():
     assert lib.spec_flatten(0, 5, FAKE, FAKE, FAKE, FAKE, None) == B.EINVAL
     assert lib.spec_flatten(4, 5, None, FAKE, FAKE, FAKE, None) == B.EINVAL
     assert lib.markov_draft(B.SAMPLE, B.BF16, 4, 5, 64, 48, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), 7, 0,
-                            FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == B.EUNSUPPORTED
+                            FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == B.EUNSUPPORTED
     assert "d_m" in B.last_error()
     assert lib.markov_draft(B.SAMPLE, B.F32, 4, 5, 64, 4, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.0), 7, 0, None,
-                            FAKE, FAKE, FAKE, 1 << 30, None) == B.EINVAL
+                            FAKE, FAKE, None, FAKE, 1 << 30, None) == B.EINVAL
     assert "temperature" in B.last_error()
     assert lib.markov_draft(B.GREEDY, B.F32, 4, 5, 64, 4, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), 7, 0, None,
-                            FAKE, FAKE, FAKE, 16, None) == B.EINVAL
+                            FAKE, FAKE, None, FAKE, 16, None) == B.EINVAL
     assert "workspace" in B.last_error()
 
 
@@ -128,10 +128,10 @@ def test_verify_ex_rejects_job_writing_this_batch():
                         1 << 20)
     args = (B.SAMPLE, B.BF16, 4, 5, 1024, FAKE, FAKE, FAKE, FAKE + 256, FAKE + 4096, FAKE + 8192,
             ctypes.c_float(1.0), 7, 0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30)
-    assert lib.spec_verify_ex(*args, ctypes.byref(job), None) == B.EINVAL
+    assert lib.spec_verify_ex(*args, None, ctypes.byref(job), None) == B.EINVAL
     assert "other than this one" in B.last_error()
     bad = B.ScheduleJob(4, 0, FAKE, FAKE, FAKE, FAKE, 4, 5, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20)
-    assert lib.spec_verify_ex(*args, ctypes.byref(bad), None) == B.EINVAL
+    assert lib.spec_verify_ex(*args, None, ctypes.byref(bad), None) == B.EINVAL
     assert "spec_verify_ex (next)" in B.last_error()
 
 

@@ -787,3 +787,100 @@ def test_gpu_chisquare_1e7_trials_philox():
     p = chi2_pvalue(counts, pr)
     say("gpu chi-square (device Philox) p =", p)
     assert p > 1e-4
+
+
+# ---------------------------------------------------------------------------
+# the draft head's statistics in place of the pass over the draft rows
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,head", [("c0", "markov"), ("c4", "markov"), ("c4", "rnn")])
+def test_draft_stats_route(name, head):
+    """spec_verify_ex with the draft head's statistics against spec_verify on
+    the same drafts (the logits route, which the tests above pin to the
+    oracle). The statistics must describe the stored draft rows: the drawn
+    token and its stored logit exactly, the scale c = log2(e) / tau bit for
+    bit, z 2^m = sum of exp2(logit c) within 1e-5 relative. The two routes
+    must give p(x), q(x), p/q within 1e-5 relative, the same uniforms, the same
+    keep decisions except where |u - min(1, p/q)| < 1e-6, and the same tokens
+    except for at most DRAW_EXEMPT_LIMIT draws (the residual's normaliser comes
+    from a different float32 summation order)."""
+    w = W(name)
+    d = D(name) if head == "markov" else DeviceStep(w, head="rnn")
+    say("draft stats route", name, head)
+    d.rng, d.step_no = True, 5
+    d.markov(B.SAMPLE)
+    d.schedule(w.k)
+    d.use_stats = False
+    d.verify(B.SAMPLE)
+    torch.cuda.synchronize()
+    assert B.read_status(d.ws_verify) == 0
+    a1, o1, g1 = d.host("acc_len"), d.host("out_tokens"), d.host("diag").copy()
+    d.use_stats = True
+    d.verify(B.SAMPLE)
+    torch.cuda.synchronize()
+    assert B.read_status(d.ws_verify) == 0
+    a2, o2, g2 = d.host("acc_len"), d.host("out_tokens"), d.host("diag").copy()
+    d.rng = False
+    R, k = w.R, w.k
+    # the statistics
+    st = d.draft_stats.cpu().numpy()
+    tok = st[..., 4].copy().view(np.int32)
+    x = d.host("draft_tokens")
+    assert np.array_equal(tok, x)
+    assert np.all(st[..., 3] == np.float32(1.4426950408889634 / w.tau))
+    dl = d.draft_logits.cpu().numpy()
+    if dl.dtype == np.int16:
+        dl = dl.view(np.uint16)
+    c = float(np.float32(1.4426950408889634 / w.tau))
+    worst = 0.0
+    for i in range(k):
+        row = numerics.decode(dl[:, i], w.dtype)
+        assert np.array_equal(st[:, i, 2].astype(np.float64), row[np.arange(R), x[:, i]])
+        a = row * c
+        m = a.max(axis=1)
+        ztrue = np.exp2(a - m[:, None]).sum(axis=1)
+        zgot = st[:, i, 1].astype(np.float64) * np.exp2(st[:, i, 0].astype(np.float64) - m)
+        worst = max(worst, float(np.max(np.abs(zgot - ztrue) / ztrue)))
+    assert worst < 1e-5, worst
+    # the two routes
+    N = int(d.host("cu_rows")[-1])
+    ver = slice(0, N)
+    for col in range(3):
+        rel = np.abs(g2[ver, col].astype(np.float64) - g1[ver, col]) / np.abs(g1[ver, col].astype(np.float64))
+        assert rel.max(initial=0) < 1e-5, (col, rel.max())
+    assert np.array_equal(g1[ver, 3], g2[ver, 3])
+    near = np.abs(g1[ver, 3].astype(np.float64) - np.minimum(1.0, g1[ver, 2].astype(np.float64))) < 1e-6
+    tags = d.host("tags")[:N]
+    near_req = np.zeros(R, dtype=bool)
+    near_req[tags[near, 0]] = True
+    assert np.array_equal(a1[~near_req], a2[~near_req])
+    same = a1 == a2
+    diff_draw = int((o1[same] != o2[same]).any(axis=1).sum())
+    assert diff_draw <= DRAW_EXEMPT_LIMIT(int(same.sum())), diff_draw
+    parity_log.record("stats", f"{name} {head}", rows=N, near_keep=int(near.sum()), draws=int(same.sum()),
+                      draw_diffs=diff_draw, worst_z=worst)
+
+
+def test_draft_stats_must_match_the_call():
+    """Statistics made at another temperature, or for another token than the
+    one verified, void their requests and set SPECV_STATUS_BAD_STATS."""
+    w = W("c0")
+    d = D("c0")
+    say("draft stats mismatch")
+    d.rng, d.step_no = True, 6
+    d.markov(B.SAMPLE)
+    d.schedule(-1)                              # every request verifies all k rows
+    d.rng = False
+    acc = torch.zeros(w.R, dtype=torch.int32, device="cuda")
+    out = torch.zeros(w.R, w.k + 1, dtype=torch.int32, device="cuda")
+    B.spec_verify(B.SAMPLE, d.target, d.draft_logits, d.draft_tokens, d.tags, d.cu_rows, d.n_rows, 0.9, None, acc,
+                  out, d.ws_verify, seed=0, step=6, draft_stats=d.draft_stats)
+    assert B.read_status(d.ws_verify) & B.STATUS_BAD_STATS
+    assert (acc.cpu().numpy() == 0).all() and (out.cpu().numpy() == -1).all()
+    toks = d.draft_tokens.clone()
+    toks[1, 2] = (toks[1, 2] + 1) % w.V
+    B.spec_verify(B.SAMPLE, d.target, d.draft_logits, toks, d.tags, d.cu_rows, d.n_rows, w.tau, None, acc, out,
+                  d.ws_verify, seed=0, step=6, draft_stats=d.draft_stats)
+    assert B.read_status(d.ws_verify) == B.STATUS_BAD_STATS
+    a = acc.cpu().numpy()
+    assert a[1] == 0 and (out.cpu().numpy()[1] == -1).all()
