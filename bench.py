@@ -114,13 +114,25 @@ def markov_bytes_flops(w):
     return nbytes, 2.0 * w.R * d_m * w.V
 
 
-def algorithmic_bytes(w, mode, N, R):
-    """Logit bytes the verification pass must read once: every target row of
-    the flattened batch (N verified + R bonus), plus the N draft rows when
-    sampling."""
+def algorithmic_bytes(w, mode, N, R, draft_rows=True):
+    """Logit bytes the verification must read once: every target row of the
+    flattened batch (N verified + R bonus), plus the N draft rows when
+    sampling, unless the draft head hands over their softmax states
+    (draft_rows=False)."""
     esize = 2 if w.dtype == "bf16" else 4
-    rows = (2 * N + R) if mode == "sample" else (N + R)
+    rows = (2 * N + R) if (mode == "sample" and draft_rows) else (N + R)
     return rows * w.V * esize
+
+
+def verify_kernel_bytes(w, mode, N, R, draft_rows, fused):
+    """Algorithmic bytes per launch of the verification's streaming kernels.
+    fused (spec_step): verify_prefetch0 reads the target row (r, 0) of every
+    request beside the schedule, verify_stream the other rows."""
+    total = algorithmic_bytes(w, mode, N, R, draft_rows)
+    row0 = R * w.V * (2 if w.dtype == "bf16" else 4)
+    if fused:
+        return {"verify_prefetch0": row0, "verify_stream": total - row0}
+    return {"verify_stream": total}
 
 
 def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
@@ -144,7 +156,8 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
     B.timing_enable(False)
     ms_step = t0.elapsed_time(t1) / steps
     kern = {}
-    for name in ("rnn_state", "markov_logits", "markov_pick", "schedule", "verify_stream", "verify_decide"):
+    for name in ("rnn_state", "markov_logits", "markov_pick", "schedule", "verify_prefetch0", "verify_stream",
+                 "verify_decide"):
         n, tot = B.timing_read(name)
         if n:
             kern[name] = dict(launches_per_step=n / steps, avg_us=1000.0 * tot / n)
@@ -167,15 +180,25 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
     L = d.host("lengths")
     N = int(L.sum())
     R = w.R
-    nbytes = algorithmic_bytes(w, mode, N, R)
+    draft_rows = d.stats_for(mode_c) is None
+    fused = "verify_prefetch0" in kern
+    nbytes = algorithmic_bytes(w, mode, N, R, draft_rows)
+    per_kernel = verify_kernel_bytes(w, mode, N, R, draft_rows, fused)
     dom = kern.get(DOMINANT)
-    achieved = nbytes / (dom["avg_us"] * 1e-6) if dom else None
+    achieved = per_kernel[DOMINANT] / (dom["avg_us"] * 1e-6) if dom else None
+    for name, nb in per_kernel.items():
+        if name in kern:
+            kern[name]["algorithmic_bytes"] = nb
+            kern[name]["hbm_frac"] = nb / (kern[name]["avg_us"] * 1e-6) / HBM_PEAK
+    # the verification's time: its kernels (with spec_step, the first launch
+    # also holds the schedule, so the fraction is a lower bound)
     verify_us = sum(kern[k]["avg_us"] * kern[k]["launches_per_step"]
-                    for k in ("verify_stream", "verify_decide") if k in kern)
+                    for k in ("verify_prefetch0", "verify_stream", "verify_decide") if k in kern)
     return dict(mode=mode, max_len=max_len, ms_per_step=ms_plain, ms_per_step_instrumented=ms_step, N=N,
                 rows=int(d.host("n_rows")[0]), tokens_per_s=N / (ms_plain * 1e-3), verify_us=verify_us,
                 verify_tokens_per_s=N / (verify_us * 1e-6) if verify_us else None,
-                algorithmic_bytes=nbytes, dominant_gbps=achieved / 1e9 if achieved else None,
+                algorithmic_bytes=nbytes, dominant_bytes=per_kernel[DOMINANT], fused_schedule=fused,
+                draft_rows_read=draft_rows, dominant_gbps=achieved / 1e9 if achieved else None,
                 dominant_frac=achieved / HBM_PEAK if achieved else None, kernels=kern, step_us_percentiles=pct)
 
 
@@ -231,9 +254,7 @@ def run_lagged(d, w, mode_c, steps, warmup, B, torch, copies):
             d.use_copy(t)
         if d.w.backbone is not None:
             d.markov(mode_c)
-        B.spec_schedule(zdev[t % n_rounds], d.T, d.tbl_b, d.tbl_t, k, d.lengths, d.tags, d.cu_rows, d.n_rows,
-                        d.ws_sched, d.survival)
-        d.verify(mode_c, diag=False)
+        d.schedule_verify(mode_c, z=zdev[t % n_rounds])
     for t in range(warmup):
         sync_step(t)
     torch.cuda.synchronize()
@@ -589,7 +610,7 @@ def main():
         "traffic": committed_traffic("verify_stream", workload_key(args, max_len))[0],
         "kernel": "verify_stream",
         "avg_launch_us": ver.get("avg_us"),
-        "algorithmic_bytes_per_launch": main_res["algorithmic_bytes"],
+        "algorithmic_bytes_per_launch": main_res["dominant_bytes"],
     }
     markov_roof = None
     if mk and w.dtype == "bf16":
@@ -635,7 +656,9 @@ def main():
         "verify_only": {"us_per_step": main_res["verify_us"], "tokens_per_s": main_res["verify_tokens_per_s"],
                         "hbm_frac": (main_res["algorithmic_bytes"] / (main_res["verify_us"] * 1e-6) / HBM_PEAK
                                      if main_res["verify_us"] else None),
-                        "kernels": ["verify_stream", "verify_decide"]},
+                        "algorithmic_bytes": main_res["algorithmic_bytes"],
+                        "kernels": [k for k in ("verify_prefetch0", "verify_stream", "verify_decide")
+                                    if k in main_res["kernels"]]},
         "kernels": main_res["kernels"],
         "ms_per_step_instrumented": main_res["ms_per_step_instrumented"],
         "step_us_percentiles": main_res["step_us_percentiles"],

@@ -49,6 +49,9 @@ _SIGS = {
     "spec_verify_ex": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                 _c_ptr, _c_ptr, ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                 _c_ptr, _c_size, _c_ptr, ctypes.POINTER(ScheduleJob), _c_ptr]),
+    "spec_step": (_c_int, [ctypes.POINTER(ScheduleJob), _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
+                           ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size,
+                           _c_ptr]),
     "spec_verify_noalloc": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                      _c_ptr, _c_ptr, ctypes.c_float, _c_u64, _c_u64, _c_ptr, _c_ptr, _c_ptr,
                                      _c_ptr, _c_ptr, _c_ptr]),
@@ -238,6 +241,35 @@ def spec_verify(mode, target, draft, tokens, tags, cu_rows, n_rows, temperature,
     else:
         _check(lib().spec_verify_ex(*args, _ptr(draft_stats), ctypes.byref(next_job) if next_job is not None else None,
                                     _stream(stream)))
+
+
+def spec_step(job: ScheduleJob, mode, target, draft, tokens, temperature, uniforms, accepted_len_out, out_tokens,
+              ws, row_diag=None, stream=None, seed: int = 0, step: int = 0, draft_stats=None):
+    """spec_step: the schedule `job` (schedule_job(...)), then the verification
+    of the batch it writes. The job's tensors must stay alive until the call has
+    run; its batch buffers are the verification's tags, cu_rows and n_rows."""
+    R, k = job.R, job.k
+    Rt, k1, V = target.shape
+    if Rt != R or k1 != k + 1:
+        raise ValueError("spec_step: target logits disagree with the job's R and k")
+    dt = logit_dtype(target)
+    _dev(target, "target", tuple(_LOGIT_TYPES))
+    if mode == SAMPLE:
+        _dev(draft, "draft", (target.dtype,), (R, k, V))
+        if uniforms is not None:
+            _dev(uniforms, "uniforms", (torch.float32,), (R, k + 1))
+    _dev(tokens, "tokens", (torch.int32,), (R, k))
+    _dev(accepted_len_out, "accepted_len_out", (torch.int32,), (R,))
+    _dev(out_tokens, "out_tokens", (torch.int32,), (R, k + 1))
+    _dev(ws, "ws", (torch.uint8,))
+    if row_diag is not None:
+        _dev(row_diag, "row_diag", (torch.float32,), (R * (k + 1), 4))
+    if draft_stats is not None:
+        _dev(draft_stats, "draft_stats", (torch.float32,), (R, k, DRAFT_STAT_WORDS))
+    _check(lib().spec_step(ctypes.byref(job), int(mode), dt, V, _ptr(target), _ptr(draft) if mode == SAMPLE else None,
+                           _ptr(tokens), float(temperature), int(seed), int(step),
+                           _ptr(uniforms) if mode == SAMPLE else None, _ptr(accepted_len_out), _ptr(out_tokens),
+                           _ptr(row_diag), _ptr(draft_stats), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 16 << 20

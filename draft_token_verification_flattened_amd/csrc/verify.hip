@@ -86,10 +86,14 @@ struct VerifyArgs {
     int nsplit;                             // sampling: decide workgroups per request (1, 2 or 4)
     SchedArgs next;                         // the next round's schedule (spec_verify_ex)
     int has_next;                           // 1: verify_decide runs `next` as workgroup R
+    int pre0;                               // 1: target row (r, 0) of every request was streamed by
+                                            //    verify_prefetch0 into part0 / ax0 (spec_step)
+    float2* part0;                          // [R * C] target chunk partials of row (r, 0)
+    float* ax0;                             // [R] target logit at draft token (r, 0)
 };
 
 struct Layout {
-    size_t part_p, part_q, rec, res_mass, res_cnt, total;
+    size_t part_p, part_q, rec, res_mass, res_cnt, part0, ax0, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -104,6 +108,8 @@ static Layout ws_layout(int R, int k, int V) {
     l.rec = off;     off = align256(off + B * sizeof(RowRec));
     l.res_mass = off; off = align256(off + size_t(R) * C * sizeof(float));
     l.res_cnt = off; off = align256(off + size_t(R) * sizeof(int));
+    l.part0 = off;   off = align256(off + size_t(R) * C * sizeof(float2));
+    l.ax0 = off;     off = align256(off + size_t(R) * sizeof(float));
     l.total = off;
     return l;
 }
@@ -314,6 +320,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
             const int ch = int(rel - uint32_t(t) * uint32_t(C));
             const int r = tg[h].x, j = tg[h].y;
             if (i >= np || t >= (tensor ? nver : nrows)) continue;
+            if (a.pre0 && tensor == 0 && j == 0) continue;     // streamed beside the schedule (spec_step)
             const bool ok = r >= 0 && r < a.R && j >= 0 && j <= K && (tensor == 0 || j < K);
             lv[h] = (h < 2 && i < uint32_t(kWaves)) ? 0 : 1;       // slots 0 .. kWaves-1: not listed
             tt[h] = t;
@@ -446,6 +453,109 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
             }
         }
         __syncthreads();                             // the next phase rewrites the descriptions
+    }
+}
+
+// ---------------------------------------------------------------------------
+// verify_prefetch0 (spec_step)
+// ---------------------------------------------------------------------------
+
+// spec_step's first launch, one workgroup per compute unit. Workgroup 0 runs
+// this round's schedule (the single-workgroup bucket schedule, `a.next`), a
+// latency-bound job that keeps one compute unit busy for ~10 us. The others
+// meanwhile stream the target row (r, 0) of every request, which the batch
+// holds whatever lengths the schedule picks (verified row 0 when L_r > 0, the
+// bonus row when L_r = 0), into part0 (and ax0, the logit at draft token
+// (r, 0)); verify_stream then skips those rows. Work items are (request,
+// chunk) pairs, taken grid-stride by the streaming wavefronts in batches of at
+// most kPreBatch. A wavefront has only a few items (about five at 256
+// requests), so the loads go through a ring of kPreRing buffers: the first
+// kPreRing are issued at once, and each later one as soon as a buffer is free.
+// Every batch size is its own unrolled instance, so the compiler counts the
+// loads in flight exactly. The batch's results are stored after its last load.
+constexpr int kPreBatch = 5;
+constexpr int kPreRing = 3;          // 16-byte loads; scalar rows (kE floats per buffer) use one buffer
+
+template <int DT, int MODE, bool VEC, int NB>
+__device__ __forceinline__ void prefetch0_batch(const VerifyArgs& a, uint32_t i0, uint32_t nw, int lane) {
+    using RW = Raw<DT, VEC>;
+    using T = typename RW::T;
+    constexpr int E = RW::kE;
+    constexpr int GW = RW::kVec;
+    constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
+    const int C = a.C, CH = a.CH, V = a.V, K = a.k;
+    constexpr int kRing = VEC ? kPreRing : 1;
+    int xt[NB];
+    // the draft tokens of the batch's rows first: a small load issued after
+    // the chunk loads would make its wait drain them
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        xt[b] = SAMPLE ? a.tokens[long((i0 + uint32_t(b) * nw) / uint32_t(C)) * K] : -1;
+    auto issue = [&](RW& buf, int b) {
+        const uint32_t it = i0 + uint32_t(b) * nw;
+        const int r = int(it / uint32_t(C)), beg = int(it % uint32_t(C)) * CH;
+        buf.load(static_cast<const T*>(a.target) + long(r) * (K + 1) * long(V), beg, V, lane, beg + CH <= V);
+    };
+    RW ring[kRing];
+#pragma unroll
+    for (int b = 0; b < NB && b < kRing; ++b) issue(ring[b], b);
+    float2 res[NB];
+    float xv[NB];
+    bool xf[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const uint32_t it = i0 + uint32_t(b) * nw;
+        const int beg = int(it % uint32_t(C)) * CH;
+        float x[E];
+        ring[b % kRing].widen(beg, V, lane, beg + CH <= V, x);
+        if (b + kRing < NB) issue(ring[b % kRing], b + kRing);      // the buffer is free again
+        res[b] = SAMPLE ? chunk_softmax(x, a.c) : chunk_argmax<RW>(x, beg, lane);
+        xf[b] = false;
+        xv[b] = 0.f;
+        if (SAMPLE) {
+            const int xb = __builtin_amdgcn_readfirstlane(xt[b]);
+            if (xb >= beg && xb < beg + CH && xb < V) {
+                const int off = xb - beg, vi = off / GW;
+                const int qx = (vi >> 6) * GW + off % GW;
+                if (lane == (vi & (kWave - 1))) {
+#pragma unroll
+                    for (int q = 0; q < E; ++q)
+                        if (q == qx) xv[b] = x[q];
+                    xf[b] = true;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const uint32_t it = i0 + uint32_t(b) * nw;
+        if (lane == 0) a.part0[it] = res[b];                    // part0[r * C + ch]
+        if (xf[b]) a.ax0[it / uint32_t(C)] = xv[b];
+    }
+}
+
+template <int DT, int MODE, bool VEC>
+__global__ __launch_bounds__(kStreamThreads) void verify_prefetch0(VerifyArgs a) {
+    if (blockIdx.x == 0) {
+        extern __shared__ __align__(16) uint64_t sched_lds[];
+        schedule_bucket_body(a.next, sched_lds);
+        return;
+    }
+    constexpr int kWaves = kStreamThreads / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t nw = (gridDim.x - 1) * kWaves;
+    const uint32_t gw = (blockIdx.x - 1) * kWaves + (threadIdx.x >> 6);
+    const uint32_t items = uint32_t(a.R) * uint32_t(a.C);
+    for (uint32_t i0 = gw; i0 < items; i0 += kPreBatch * nw) {
+        const int nb = int(min(uint32_t(kPreBatch), (items - 1 - i0) / nw + 1));   // items of this batch
+        static_assert(kPreBatch == 5, "one case per batch size");
+        switch (nb) {
+            case 1: prefetch0_batch<DT, MODE, VEC, 1>(a, i0, nw, lane); break;
+            case 2: prefetch0_batch<DT, MODE, VEC, 2>(a, i0, nw, lane); break;
+            case 3: prefetch0_batch<DT, MODE, VEC, 3>(a, i0, nw, lane); break;
+            case 4: prefetch0_batch<DT, MODE, VEC, 4>(a, i0, nw, lane); break;
+            default: prefetch0_batch<DT, MODE, VEC, 5>(a, i0, nw, lane); break;
+        }
     }
 }
 
@@ -692,7 +802,9 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
             }
             specv_draft_stat ds{};
             if (SAMPLE && verified && a.stats) ds = a.stats[long(r) * k + j];
-            const float2 P = merge_partials<SAMPLE>(a.part_p + long(t) * C, C, lane);
+            const bool row0 = a.pre0 && j == 0;       // streamed beside the schedule (spec_step)
+            if (SAMPLE && verified && row0) rc.ax = a.ax0[r];
+            const float2 P = merge_partials<SAMPLE>(row0 ? a.part0 + long(r) * C : a.part_p + long(t) * C, C, lane);
             float2 Q = make_float2(-INFINITY, 0.f);
             if (SAMPLE && verified) {
                 if (a.stats) {                     // q's state and q(x) from the draft head
@@ -812,7 +924,7 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
             }
         } else {
             // bonus row: chunk masses of p relative to Mp, from the partials
-            const float2* pp = a.part_p + long(N + r) * C;
+            const float2* pp = (a.pre0 && L == 0) ? a.part0 + long(r) * C : a.part_p + long(N + r) * C;
             for (int cc = tid; cc < C; cc += NT) {
                 const float2 q = pp[cc];
                 mass_s[cc] = q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
@@ -857,7 +969,7 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
             });
         } else {                                   // p of row a_r: the bonus row, or a residual without mass
             if (rejected) {
-                const float2* pp = a.part_p + long(base + acc) * C;
+                const float2* pp = (a.pre0 && acc == 0) ? a.part0 + long(r) * C : a.part_p + long(base + acc) * C;
                 for (int cc = lane; cc < C; cc += kWave) {
                     const float2 q = pp[cc];
                     mass_s[cc] = q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
@@ -922,10 +1034,30 @@ static int launch_decide(K kernel, int threads, VerifyArgs& a, const SchedArgs* 
     return SPECV_OK;
 }
 
+// spec_step's first launch: this round's schedule in workgroup 0, the rows
+// (r, 0) in the others (verify_prefetch0).
+template <class K>
+static int launch_prefetch0(K kernel, VerifyArgs& a, const SchedArgs& first, int cus, hipStream_t s) {
+    a.next = first;
+    a.pre0 = 1;
+    const size_t lds = schedule_bucket_lds(first.R, first.k, first.kk);
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            int(lds)) != hipSuccess)
+        return fail(SPECV_EDEVICE, "spec_step: cannot reserve %zu bytes of LDS", lds);
+    SPECV_LAUNCH("verify_prefetch0", kernel, std::max(2, cus), kStreamThreads, lds, s, a);
+    return SPECV_OK;
+}
+
 template <int DT, bool VEC>
-static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStream_t s) {
+static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStream_t s,
+                         const SchedArgs* first = nullptr) {
     int cus = 0;
     if (int e = device_cus(cus)) return e;
+    if (first) {
+        if (int e = mode == SPECV_GREEDY ? launch_prefetch0(verify_prefetch0<DT, SPECV_GREEDY, VEC>, a, *first, cus, s)
+                                         : launch_prefetch0(verify_prefetch0<DT, SPECV_SAMPLE, VEC>, a, *first, cus, s))
+            return e;
+    }
     int G = 0;
     if (mode == SPECV_GREEDY) {
         auto ks = verify_stream<DT, SPECV_GREEDY, VEC>;
@@ -963,12 +1095,13 @@ extern "C" size_t spec_verify_workspace_bytes(int R, int k, int V) {
 
 namespace specv {
 
-static int verify_impl(int mode, int dtype, int R, int k, int V, const void* target_logits, const void* draft_logits,
-                       const int32_t* draft_tokens, const int32_t* tags, const int32_t* cu_rows, const int32_t* n_rows,
-                       float temperature, uint64_t seed, uint64_t step, const float* uniforms,
-                       int32_t* accepted_len_out, int32_t* out_tokens, float* row_diag, void* ws, size_t ws_bytes,
-                       const SchedArgs* next, specv_stream stream, uint32_t* status_word = nullptr,
-                       const specv_draft_stat* draft_stats = nullptr) {
+// Argument checks and the kernels' arguments; nothing is enqueued.
+static int verify_prepare(int mode, int dtype, int R, int k, int V, const void* target_logits,
+                          const void* draft_logits, const int32_t* draft_tokens, const int32_t* tags,
+                          const int32_t* cu_rows, const int32_t* n_rows, float temperature, uint64_t seed,
+                          uint64_t step, const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
+                          float* row_diag, void* ws, size_t ws_bytes, uint32_t* status_word,
+                          const specv_draft_stat* draft_stats, VerifyArgs& a, bool& vec) {
     if (mode != SPECV_GREEDY && mode != SPECV_SAMPLE)
         return fail(SPECV_EINVAL, "spec_verify: mode %d is neither greedy (0) nor sample (1)", mode);
     if (dtype != SPECV_BF16 && dtype != SPECV_F32)
@@ -1000,10 +1133,8 @@ static int verify_impl(int mode, int dtype, int R, int k, int V, const void* tar
                     "(V = %d)", kMaxChunks, chunk_len(dtype), V);
     const int esize = dtype == SPECV_BF16 ? 2 : 4;
     const int vecw = 16 / esize;
-    const bool vec = (V % vecw) == 0 && aligned16(target_logits) &&
-                     (mode == SPECV_GREEDY || aligned16(draft_logits));
+    vec = (V % vecw) == 0 && aligned16(target_logits) && (mode == SPECV_GREEDY || aligned16(draft_logits));
 
-    VerifyArgs a;
     a.R = R; a.k = k; a.V = V;
     a.CH = chunk_len(dtype);
     a.C = (V + a.CH - 1) / a.CH;
@@ -1030,13 +1161,39 @@ static int verify_impl(int mode, int dtype, int R, int k, int V, const void* tar
     a.rec = reinterpret_cast<RowRec*>(w + lay.rec);
     a.res_mass = reinterpret_cast<float*>(w + lay.res_mass);
     a.res_cnt = reinterpret_cast<int*>(w + lay.res_cnt);
+    a.part0 = reinterpret_cast<float2*>(w + lay.part0);
+    a.ax0 = reinterpret_cast<float*>(w + lay.ax0);
+    a.pre0 = 0;
     a.nsplit = 1;
     a.has_next = 0;
+    return SPECV_OK;
+}
+
+// Enqueue the kernels of a prepared call; `first`: this round's schedule, run
+// beside the rows (r, 0) (spec_step); `next`: the next round's (spec_verify_ex).
+static int verify_launch(int mode, int dtype, bool vec, VerifyArgs& a, const SchedArgs* next,
+                         const SchedArgs* first, specv_stream stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == SPECV_BF16)
-        return vec ? launch_verify<SPECV_BF16, true>(mode, a, next, s)
-                   : launch_verify<SPECV_BF16, false>(mode, a, next, s);
-    return vec ? launch_verify<SPECV_F32, true>(mode, a, next, s) : launch_verify<SPECV_F32, false>(mode, a, next, s);
+        return vec ? launch_verify<SPECV_BF16, true>(mode, a, next, s, first)
+                   : launch_verify<SPECV_BF16, false>(mode, a, next, s, first);
+    return vec ? launch_verify<SPECV_F32, true>(mode, a, next, s, first)
+               : launch_verify<SPECV_F32, false>(mode, a, next, s, first);
+}
+
+static int verify_impl(int mode, int dtype, int R, int k, int V, const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, const int32_t* tags, const int32_t* cu_rows, const int32_t* n_rows,
+                       float temperature, uint64_t seed, uint64_t step, const float* uniforms,
+                       int32_t* accepted_len_out, int32_t* out_tokens, float* row_diag, void* ws, size_t ws_bytes,
+                       const SchedArgs* next, specv_stream stream, uint32_t* status_word = nullptr,
+                       const specv_draft_stat* draft_stats = nullptr) {
+    VerifyArgs a;
+    bool vec = false;
+    if (int e = verify_prepare(mode, dtype, R, k, V, target_logits, draft_logits, draft_tokens, tags, cu_rows, n_rows,
+                               temperature, seed, step, uniforms, accepted_len_out, out_tokens, row_diag, ws, ws_bytes,
+                               status_word, draft_stats, a, vec))
+        return e;
+    return verify_launch(mode, dtype, vec, a, next, nullptr, stream);
 }
 
 }  // namespace specv
@@ -1073,6 +1230,38 @@ extern "C" int spec_verify_ex(int mode, int dtype, int R, int k, int V, const vo
     return verify_impl(mode, dtype, R, k, V, target_logits, draft_logits, draft_tokens, tags, cu_rows, n_rows,
                        temperature, seed, step, uniforms, accepted_len_out, out_tokens, row_diag, ws, ws_bytes,
                        next ? &na : nullptr, stream, nullptr, draft_stats);
+}
+
+// ---------------------------------------------------------------------------
+// spec_step: this round's schedule, then its verification
+// ---------------------------------------------------------------------------
+
+extern "C" int spec_step(const specv_schedule_job* sched, int mode, int dtype, int V, const void* target_logits,
+                         const void* draft_logits, const int32_t* draft_tokens, float temperature, uint64_t seed,
+                         uint64_t step, const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
+                         float* row_diag, const specv_draft_stat* draft_stats, void* ws, size_t ws_bytes,
+                         specv_stream stream) {
+    using namespace specv;
+    clear_error();
+    if (!sched) return fail(SPECV_EINVAL, "spec_step: NULL schedule job");
+    SchedArgs sa;
+    if (int e = schedule_prepare(sched->R, sched->k, sched->conf_logit, sched->pos_temp, sched->tbl_tokens,
+                                 sched->tbl_thr, sched->n_tbl, sched->max_len, sched->len_out, sched->tags_out,
+                                 sched->cu_rows_out, sched->n_rows_out, sched->survival_out, sched->ws, sched->ws_bytes,
+                                 "spec_step (schedule)", sa))
+        return e;
+    VerifyArgs a;
+    bool vec = false;
+    if (int e = verify_prepare(mode, dtype, sched->R, sched->k, V, target_logits, draft_logits, draft_tokens,
+                               sched->tags_out, sched->cu_rows_out, sched->n_rows_out, temperature, seed, step,
+                               uniforms, accepted_len_out, out_tokens, row_diag, ws, ws_bytes, nullptr, draft_stats, a,
+                               vec))
+        return e;
+    if (!schedule_is_bucket(sa)) {             // fixed lengths, or a schedule beyond one workgroup: in sequence
+        if (int e = schedule_launch(sa, static_cast<hipStream_t>(stream))) return e;
+        return verify_launch(mode, dtype, vec, a, nullptr, nullptr, stream);
+    }
+    return verify_launch(mode, dtype, vec, a, nullptr, &sa, stream);
 }
 
 // ---------------------------------------------------------------------------

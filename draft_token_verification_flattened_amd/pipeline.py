@@ -34,6 +34,7 @@ class DeviceStep:
         self.w = w
         self.device = device
         self.rng = rng
+        self.fused = True                   # step(): schedule and verification in one spec_step call
         self.seed = int(CONFIGS[w.name]["seed"])
         self.step_no = 0
         R, k, V = w.R, w.k, w.V
@@ -136,16 +137,34 @@ class DeviceStep:
         for n, t in self._copies[i % len(self._copies)].items():
             setattr(self, n, t)
 
+    def schedule_verify(self, mode, max_len=None, diag=False, stream=None, z=None):
+        """This round's schedule (from the confidence logits z, default the
+        workload's), then its verification, in one spec_step call (the schedule
+        beside the stream of the rows (r, 0))."""
+        max_len = self.w.k if max_len is None else max_len
+        job = B.schedule_job(self.z if z is None else z, self.T, self.tbl_b, self.tbl_t, max_len, self.lengths, self.tags, self.cu_rows,
+                             self.n_rows, self.ws_sched, self.survival)
+        d, t = self.drafts(mode)
+        u = self.uniforms("u_verify")
+        B.spec_step(job, mode, self.target, d, t, self.w.tau, u["uniforms"], self.acc_len, self.out_tokens,
+                    self.ws_verify, row_diag=self.diag if diag else None, stream=stream, seed=u["seed"],
+                    step=u["step"], draft_stats=self.stats_for(mode))
+
     def step(self, mode, max_len=None, diag=False, stream=None):
-        """One pass of the hot path: (Markov draft,) schedule + flatten, verify."""
+        """One pass of the hot path: (Markov draft,) schedule + flatten, verify;
+        with fused (the default) the schedule and the verification are one
+        spec_step call."""
         self.step_no += 1
         if len(self._copies) > 1:
             self._turn += 1
             self.use_copy(self._turn)
         if self.w.backbone is not None:
             self.markov(mode, stream=stream)
-        self.schedule(max_len, stream=stream)
-        self.verify(mode, diag=diag, stream=stream)
+        if self.fused:
+            self.schedule_verify(mode, max_len, diag=diag, stream=stream)
+        else:
+            self.schedule(max_len, stream=stream)
+            self.verify(mode, diag=diag, stream=stream)
 
     # -- readback ------------------------------------------------------------
     def host(self, name) -> np.ndarray:

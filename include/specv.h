@@ -306,6 +306,34 @@ int spec_verify_ex(int mode, int dtype, int R, int k, int V, const void* target_
                    const specv_schedule_job* next, specv_stream stream);
 
 /* ------------------------------------------------------------------------ */
+/* spec_step: this round's schedule, then its verification                   */
+/* ------------------------------------------------------------------------ */
+/*
+ * spec_schedule of the job `sched` (this round's confidences) followed by
+ * spec_verify of the batch it writes (its tags_out, cu_rows_out, n_rows_out),
+ * with the same results bit for bit: the synchronous step of [P2] 3.2 and
+ * [P3] "DSpark的神奇之处" (schedule from the current confidences, then verify).
+ * When the schedule fits one workgroup (R * k <= 4096, max_len >= 1) it runs
+ * in the first launch, on one compute unit, while the others stream every
+ * request's target row (r, 0): the batch holds that row whatever lengths the
+ * schedule picks (verified row 0, or the bonus row when L_r = 0). The
+ * verification pass then streams the other rows, so the latency-bound
+ * schedule hides behind reads the step needs anyway. Otherwise the two run
+ * one after the other.
+ * Arguments: sched as spec_verify_ex's `next` (a host pointer; device
+ *   pointers inside; its workspace separate from `ws`); the others as
+ *   spec_verify_ex, with R and k taken from sched.
+ * Errors: as spec_schedule and spec_verify ("spec_step (schedule)" in the
+ *   message for the job); all arguments are checked before anything is
+ *   enqueued.
+ */
+int spec_step(const specv_schedule_job* sched, int mode, int dtype, int V, const void* target_logits,
+              const void* draft_logits, const int32_t* draft_tokens, float temperature, uint64_t seed,
+              uint64_t step, const float* uniforms, int32_t* accepted_len_out, int32_t* out_tokens,
+              float* row_diag, const specv_draft_stat* draft_stats, void* ws, size_t ws_bytes,
+              specv_stream stream);
+
+/* ------------------------------------------------------------------------ */
 /* spec_verify_noalloc: spec_verify without a workspace                      */
 /* ------------------------------------------------------------------------ */
 /*

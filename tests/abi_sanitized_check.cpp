@@ -101,6 +101,20 @@ int main() {
                                fake<int32_t>(), nullptr, FAKE, big, nullptr, &job, nullptr),
                 SPECV_EINVAL, "other than this one", "verify_ex same batch");
 
+    // spec_step: the job's checks, then the verification's, before anything is enqueued
+    expect_code(spec_step(nullptr, SPECV_SAMPLE, SPECV_BF16, 1024, FAKE, FAKE, fake<int32_t>(), 1.f, 0, 0, nullptr,
+                          fake<int32_t>(), fake<int32_t>(), nullptr, nullptr, FAKE, big, nullptr),
+                SPECV_EINVAL, "NULL schedule job", "step without a job");
+    specv_schedule_job sj = job;
+    sj.max_len = 9;
+    expect_code(spec_step(&sj, SPECV_SAMPLE, SPECV_BF16, 1024, FAKE, FAKE, fake<int32_t>(), 1.f, 0, 0, nullptr,
+                          fake<int32_t>(), fake<int32_t>(), nullptr, nullptr, FAKE, big, nullptr),
+                SPECV_EINVAL, "spec_step (schedule)", "step with a bad job");
+    sj.max_len = 5;
+    expect_code(spec_step(&sj, SPECV_SAMPLE, SPECV_BF16, 1024, FAKE, FAKE, fake<int32_t>(), 0.f, 0, 0, nullptr,
+                          fake<int32_t>(), fake<int32_t>(), nullptr, nullptr, FAKE, big, nullptr),
+                SPECV_EINVAL, "temperature", "step with a bad temperature");
+
     // spec_schedule / spec_flatten
     auto sched = [&](int R, int k, int n, int max_len, void* ws, size_t wsb, const float* z) {
         return spec_schedule(R, k, z, fake<float>(), fake<int32_t>(), fake<double>(), n, max_len, fake<int32_t>(),

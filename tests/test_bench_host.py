@@ -62,3 +62,15 @@ def test_workload_configs_match_the_recipes():
     assert (c2["R"], c2["k"], c2["V"]) == (256, 5, 151936)
     c4 = workloads.CONFIGS["c4"]
     assert (c4["R"], c4["k"], c4["V"], c4["d_m"]) == (512, 5, 151936, 256)
+
+
+def test_verify_kernel_bytes_split():
+    # spec_step: the rows (r, 0) go to the first launch, the rest to the stream
+    w = types.SimpleNamespace(V=151936, dtype="bf16")
+    per = bench.verify_kernel_bytes(w, "sample", 512, 256, True, True)
+    assert per["verify_prefetch0"] == 2 * 151936 * 256
+    assert per["verify_prefetch0"] + per["verify_stream"] == bench.algorithmic_bytes(w, "sample", 512, 256)
+    assert bench.verify_kernel_bytes(w, "greedy", 512, 256, True, False) == {
+        "verify_stream": 2 * 151936 * (512 + 256)}
+    # the draft head's statistics: no draft rows
+    assert bench.algorithmic_bytes(w, "sample", 512, 256, draft_rows=False) == 2 * 151936 * (512 + 256)
