@@ -70,6 +70,16 @@ __device__ __forceinline__ bool part_nonfinite(int mode, float a_, float b_) {
     return !(finite_bits(a_) && finite_bits(b_));
 }
 
+// The partial of (request m, slice s) sits at part[((m / 16) * S + s) * 16 + m % 16]:
+// the 16 requests of one MFMA tile write one contiguous 128-byte record per
+// slice (a request-major layout scatters 8-byte stores 19 KB apart, each
+// costing the memory a whole sector), and request m's partials are 16 entries
+// apart.
+constexpr int kPartBlock = 16;
+__host__ __device__ __forceinline__ long part_at(int m, int s, int S) {
+    return (long(m / kPartBlock) * S + s) * kPartBlock + m % kPartBlock;
+}
+
 __device__ __forceinline__ int prev_token(const MarkovArgs& a, int m) {
     int p = a.pos == 0 ? a.prev[m] : a.tokens[long(m) * a.k + a.pos - 1];
     return p;
@@ -319,7 +329,7 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
                 q.b = __shfl_xor(pp.b, o, 64);
                 part_merge(a.mode, pp, q);
             }
-            if (g == 0 && m < a.R) a.part[long(m) * a.S + blockIdx.x] = make_float2(pp.a, pp.b);
+            if (g == 0 && m < a.R) a.part[part_at(m, blockIdx.x, a.S)] = make_float2(pp.a, pp.b);
         }
     }
 }
@@ -343,9 +353,13 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
 //     row 4q + r of MFMA tile x, at LDS row 16x + 4q + r (conflict-free reads);
 //   - backbone values come in 16-byte loads two slices ahead of their epilogue;
 //   - the epilogue adds them, rounds to bf16 with the hardware conversion
-//     (nearest-even), stores 2 x 16 bytes per lane (4 lanes cover 128
-//     contiguous bytes of a request's row) and emits the per-(request, slice)
-//     partials.
+//     (nearest-even), emits the per-(request, slice) partials and stores the
+//     logits through a per-wavefront LDS tile, so that each store instruction
+//     writes whole 128-byte lines (8 lanes per request row): non-temporal
+//     stores that cover half of each line per instruction move 1.43 times the
+//     bytes at half the rate.
+constexpr int kTileRow = 144;                // LDS row of the store tile: 128 bytes + 16 of padding
+constexpr int kTileBytes = 16 * kTileRow;    // one wavefront's 16 requests x 64 entries, bf16
 constexpr int kRunKB = 1;                    // 16-request blocks per wavefront (2: 8 wavefronts of
                                              // 228 VGPRs, 5% slower than 16 of 120)
 constexpr int kRunThreads = 1024 / kRunKB;   // 16 / kRunKB wavefronts
@@ -417,6 +431,18 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
         }
     };
 
+    // the store tile: lane (row, q) = (lane / 8 + 8 j, lane % 8) stores bytes 16 q .. 16 q + 15
+    // of request row's 128-byte segment, for j = 0, 1
+    unsigned char* tile = lds_raw + 2 * buf_bytes + wave * kTileBytes;
+    long strow[2];
+    bool stok[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = grp * kRunGroup + wave * 16 + 8 * j + (lane >> 3);
+        stok[j] = m < a.R;
+        strow[j] = (long(stok[j] ? m : 0) * a.k + a.pos) * long(V);
+    }
+
     // this wavefront's requests (rows of absent requests read request 0's) and their operand rows
     int mreq[kRunKB];
     bool mok[kRunKB];
@@ -456,21 +482,24 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
     load_p(pr, range);
     store_p(pr, 0);
     load_p(pr, min(range + nr, s_last));
-    // backbone values two slices ahead: bk0 (slice s), bk1 (s + 1), bk2 (s + 2)
-    u32x4 bk0[kRunKB][2], bk1[kRunKB][2], bk2[kRunKB][2];
-    load_bk(bk0, range);
-    load_bk(bk1, min(range + nr, s_last));
+    // backbone values one slice ahead, in two buffers whose roles alternate
+    // with the slice (as the two LDS buffers of P do); the loop below is
+    // unrolled twice so that every role is fixed at compile time: a rotation
+    // by register moves would make each slice wait for every load in flight,
+    // the next P slice included
+    u32x4 bkA[kRunKB][2], bkB[kRunKB][2];
+    load_bk(bkA, range);
     __syncthreads();
 
-    for (int s = range, it = 0; s <= s_last; s += nr, ++it) {
-        const int cur = it & 1;
-        load_bk(bk2, min(s + 2 * nr, s_last));
+    // one slice: cur holds slice s's backbone values, ahead receives slice s + 1's
+    auto slice = [&](int s, int lb, const u32x4 (&cur)[kRunKB][2], u32x4 (&ahead)[kRunKB][2]) {
+        load_bk(ahead, min(s + nr, s_last));
         f32x4 acc[4][kRunKB];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
             for (int b = 0; b < kRunKB; ++b) acc[x][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const unsigned char* buf = lds_raw + cur * buf_bytes;
+        const unsigned char* buf = lds_raw + lb * buf_bytes;
         // the MFMA phase issues ahead of other wavefronts' epilogues on the same SIMD
         // (raised wave priority; about 0.6% per launch at R = 512)
         __builtin_amdgcn_s_setprio(1);
@@ -496,7 +525,7 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
             if constexpr (VEC) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const u32x4 w = bk0[b][h];
+                    const u32x4 w = cur[b][h];
                     bkv[8 * h + 0] = bf16_lo(w.x); bkv[8 * h + 1] = bf16_hi(w.x);
                     bkv[8 * h + 2] = bf16_lo(w.y); bkv[8 * h + 3] = bf16_hi(w.y);
                     bkv[8 * h + 4] = bf16_lo(w.z); bkv[8 * h + 5] = bf16_hi(w.z);
@@ -522,16 +551,23 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
                 vals[x][2] = bf16_lo(wd[2 * x + 1]); vals[x][3] = bf16_hi(wd[2 * x + 1]);
             }
             if constexpr (VEC) {
-                // V % 8 == 0: each 8-entry half is wholly inside the row or wholly past it
-                // non-temporal stores: the logits go to HBM now, while this kernel leaves
+                // through the tile: this lane's 32 bytes in, then 16 bytes of each of two rows out.
+                // V % 8 == 0: each 8-entry piece is wholly inside the row or wholly past it.
+                // Non-temporal stores: the logits go to HBM now, while this kernel leaves
                 // bandwidth spare, instead of sitting dirty in the Infinity Cache until
                 // the verify stream's reads evict them
-                u32x4* drow = reinterpret_cast<u32x4*>(dl + rowoff[b] + n16);
-                if (mok[b] && n16 + 16 <= V) {
-                    __builtin_nontemporal_store(u32x4{wd[0], wd[1], wd[2], wd[3]}, drow);
-                    __builtin_nontemporal_store(u32x4{wd[4], wd[5], wd[6], wd[7]}, drow + 1);
-                } else if (mok[b] && n16 + 8 <= V) {
-                    __builtin_nontemporal_store(u32x4{wd[0], wd[1], wd[2], wd[3]}, drow);
+                u32x4* tw = reinterpret_cast<u32x4*>(tile + l16 * kTileRow + 32 * g);
+                tw[0] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+                tw[1] = u32x4{wd[4], wd[5], wd[6], wd[7]};
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const int q = lane & 7, nq = s * kSlice + 8 * q;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(tile + (8 * j + (lane >> 3)) * kTileRow + 16 * q);
+                    if (stok[j] && nq + 8 <= V)
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dl + strow[j] + nq));
                 }
             } else {
 #pragma unroll
@@ -547,19 +583,20 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
                 q.b = __shfl_xor(pp.b, o, 64);
                 part_merge(a.mode, pp, q);
             }
-            if (g == 0 && mok[b]) a.part[long(mreq[b]) * S + s] = make_float2(pp.a, pp.b);
+            if (g == 0 && mok[b]) a.part[part_at(mreq[b], s, S)] = make_float2(pp.a, pp.b);
         }
         // the slice after next: the other buffer was last read before the previous barrier
-        store_p(pr, cur ^ 1);
+        store_p(pr, lb ^ 1);
         load_p(pr, min(s + 2 * nr, s_last));
-#pragma unroll
-        for (int b = 0; b < kRunKB; ++b)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                bk0[b][h] = bk1[b][h];
-                bk1[b][h] = bk2[b][h];
-            }
         __syncthreads();
+    };
+
+    for (int s = range; s <= s_last;) {
+        slice(s, 0, bkA, bkB);
+        s += nr;
+        if (s > s_last) break;
+        slice(s, 1, bkB, bkA);
+        s += nr;
     }
 }
 
@@ -598,7 +635,7 @@ __global__ __launch_bounds__(256) void markov_logits_fma(MarkovArgs a) {
         q.b = __shfl_xor(pp.b, o, 64);
         part_merge(a.mode, pp, q);
     }
-    if (lane == 0) a.part[long(m) * a.S + sl] = make_float2(pp.a, pp.b);
+    if (lane == 0) a.part[part_at(m, sl, a.S)] = make_float2(pp.a, pp.b);
 }
 
 // ---------------------------------------------------------------------------
@@ -643,12 +680,12 @@ __global__ __launch_bounds__(256) void markov_pick(MarkovArgs a) {
     const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= a.R) return;
     if (a.pos == 0 && lane == 0 && (a.prev[m] < 0 || a.prev[m] >= a.V)) set_status(a.hdr, SPECV_STATUS_BAD_TOKEN);
-    const float2* pr = a.part + long(m) * a.S;
+    const float2* pr = a.part + part_at(m, 0, a.S);      // slice s at pr[kPartBlock * s]
     Part tot = part_empty(a.mode);
     for (int s = lane; s < a.S; s += 64) {
         Part q;
-        q.a = pr[s].x;
-        q.b = pr[s].y;
+        q.a = pr[kPartBlock * s].x;
+        q.b = pr[kPartBlock * s].y;
         part_merge(a.mode, tot, q);
     }
 #pragma unroll
@@ -669,7 +706,7 @@ __global__ __launch_bounds__(256) void markov_pick(MarkovArgs a) {
         const float c = a.c;
         y = inv_cdf_pick(
             a.S, a.V, kSlice, thr,
-            [&](int s) { float2 q = pr[s]; return q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - M); },
+            [&](int s) { float2 q = pr[kPartBlock * s]; return q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - M); },
             [&](int e) { return exp2f(fmaf(LT::load1(row + e), c, -M)); }, lane);
         if (a.stats && lane == 0)
             a.stats[long(m) * a.k + a.pos] = specv_draft_stat{M, tot.b, LT::load1(row + y), c, y, {0, 0, 0}};
@@ -686,6 +723,20 @@ __global__ __launch_bounds__(256) void markov_pick(MarkovArgs a) {
 // u Z, and one wavefront's scan of the chosen 64-entry slice.
 constexpr int kPickThreads = 256;
 constexpr int kPickPer = 16;
+constexpr int kXcds = 8;                     // workgroups are dealt to the XCDs round-robin
+
+// Workgroup b of the pick grid takes request pick_request(b): the 16 requests
+// of one partial block (part_at) go to workgroups b, b + 8, ... of one XCD, so
+// that XCD's L2 fetches each 128-byte record of the block once instead of up
+// to eight L2s fetching it. The grid has pick_grid(R) workgroups; those past R
+// return at once.
+__host__ __device__ inline int pick_grid(int R) {
+    return (R + kXcds * kPartBlock - 1) / (kXcds * kPartBlock) * (kXcds * kPartBlock);
+}
+__device__ __forceinline__ int pick_request(int b) {
+    const int xcd = b % kXcds, i = b / kXcds;
+    return (xcd + kXcds * (i / kPartBlock)) * kPartBlock + i % kPartBlock;
+}
 
 template <int DT>
 __global__ __launch_bounds__(kPickThreads) void markov_pick_wg(MarkovArgs a) {
@@ -697,16 +748,17 @@ __global__ __launch_bounds__(kPickThreads) void markov_pick_wg(MarkovArgs a) {
     __shared__ float sh_base[NW];
     __shared__ int sh_last[NW];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int m = blockIdx.x;
+    const int m = pick_request(int(blockIdx.x));
+    if (m >= a.R) return;
     if (a.pos == 0 && tid == 0 && (a.prev[m] < 0 || a.prev[m] >= a.V)) set_status(a.hdr, SPECV_STATUS_BAD_TOKEN);
     const int S = a.S;
     const int J = (S + kPickThreads - 1) / kPickThreads;
     const int beg = tid * J, end = min(S, beg + J);
-    const float2* pr = a.part + long(m) * S;
+    const float2* pr = a.part + part_at(m, 0, S);         // slice s at pr[kPartBlock * s]
     float2 q[kPickPer];
 #pragma unroll
     for (int j = 0; j < kPickPer; ++j)
-        q[j] = (j < J && beg + j < end) ? pr[beg + j] : make_float2(-INFINITY, __int_as_float(INT_MAX));
+        q[j] = (j < J && beg + j < end) ? pr[kPartBlock * (beg + j)] : make_float2(-INFINITY, __int_as_float(INT_MAX));
     Part tot = part_empty(a.mode);
 #pragma unroll
     for (int j = 0; j < kPickPer; ++j) {
@@ -811,7 +863,8 @@ namespace {
 size_t head_workspace_bytes(int R, int k, int V, int d_m, bool state) {
     if (R < 1 || k < 1 || k > SPECV_MAX_K || V < 1 || d_m < 1) return 0;
     const size_t S = (size_t(V) + kSlice - 1) / kSlice;
-    size_t n = 256 + ((size_t(R) * S * sizeof(float2) + 255) & ~size_t(255));
+    const size_t Rb = (size_t(R) + kPartBlock - 1) / kPartBlock * kPartBlock;     // part_at's blocks
+    size_t n = 256 + ((Rb * S * sizeof(float2) + 255) & ~size_t(255));
     if (state) n += (size_t(R) * k * d_m * sizeof(float) + 255) & ~size_t(255);
     return n;
 }
@@ -864,7 +917,7 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
     const bool vec8 = (V % 8) == 0 && (reinterpret_cast<uintptr_t>(backbone_logits) & 15u) == 0 &&
                       (reinterpret_cast<uintptr_t>(draft_logits_out) & 15u) == 0;
     const size_t lds = size_t(kSlice) * size_t(d_m * 2 + 16);
-    const int run_lds = 2 * kSlice * (d_m * 2);
+    const int run_lds = 2 * kSlice * (d_m * 2) + (kRunThreads / kWave) * kTileBytes;
     if (dtype == SPECV_BF16 && d_m == 256) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(markov_logits_run<true, 8>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, run_lds) != hipSuccess ||
@@ -893,7 +946,7 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
             else
                 SPECV_LAUNCH("markov_logits", markov_logits_mfma<false>, a.S, 256, lds, s, a);
             if (pick_wg)
-                SPECV_LAUNCH("markov_pick", markov_pick_wg<SPECV_BF16>, R, kPickThreads, 0, s, a);
+                SPECV_LAUNCH("markov_pick", markov_pick_wg<SPECV_BF16>, pick_grid(R), kPickThreads, 0, s, a);
             else
                 SPECV_LAUNCH("markov_pick", markov_pick<SPECV_BF16>, (R + 3) / 4, 256, 0, s, a);
         } else {
@@ -901,7 +954,7 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
             const long items = long(R) * a.S;
             SPECV_LAUNCH("markov_logits", markov_logits_fma, (items + 3) / 4, 256, 0, s, a);
             if (pick_wg)
-                SPECV_LAUNCH("markov_pick", markov_pick_wg<SPECV_F32>, R, kPickThreads, 0, s, a);
+                SPECV_LAUNCH("markov_pick", markov_pick_wg<SPECV_F32>, pick_grid(R), kPickThreads, 0, s, a);
             else
                 SPECV_LAUNCH("markov_pick", markov_pick<SPECV_F32>, (R + 3) / 4, 256, 0, s, a);
         }
