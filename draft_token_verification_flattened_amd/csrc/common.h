@@ -329,8 +329,9 @@ __device__ __forceinline__ bool nan_or_posinf_bits(float x) {
 // a float multiple of 2^-24 in [0, 1), exact. Purposes below.
 enum : uint32_t { kPurposeAccept = 0, kPurposeDraw = 1, kPurposeDraft = 2 };
 
-__device__ __forceinline__ uint64_t philox4x64_10_word0(uint64_t w0, uint64_t w1, uint64_t w2, uint64_t w3,
-                                                        uint64_t k0, uint64_t k1) {
+// The block of counter (w0, w1, w2, w3) under key (k0, k1), in place.
+__device__ __forceinline__ void philox4x64_10(uint64_t& w0, uint64_t& w1, uint64_t& w2, uint64_t& w3, uint64_t k0,
+                                              uint64_t k1) {
     constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
     constexpr uint64_t K0 = 0x9E3779B97F4A7C15ull, K1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
@@ -347,13 +348,24 @@ __device__ __forceinline__ uint64_t philox4x64_10_word0(uint64_t w0, uint64_t w1
         w2 = n2;
         w3 = lo0;
     }
-    return w0;
 }
 
 __device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t step, uint32_t purpose, uint32_t r,
                                                 uint32_t i) {
-    const uint64_t w = philox4x64_10_word0(uint64_t(i) + 1u, r, purpose, 0u, seed, step);
-    return float(uint32_t(w >> 40)) * 0x1p-24f;
+    uint64_t w0 = uint64_t(i) + 1u, w1 = r, w2 = purpose, w3 = 0u;
+    philox4x64_10(w0, w1, w2, w3, seed, step);
+    return float(uint32_t(w0 >> 40)) * 0x1p-24f;
+}
+
+// The two uniforms of trial t of the residual draw at position i of request r:
+// words 0 and 1 of the block at counter (i + 1, r, 1, t), each >> 40 and times
+// 2^-24 (trial 0's first uniform is U(seed, step, 1, r, i)).
+__device__ __forceinline__ void philox_trial(uint64_t seed, uint64_t step, uint32_t r, uint32_t i, uint32_t t,
+                                             float& u1, float& u2) {
+    uint64_t w0 = uint64_t(i) + 1u, w1 = r, w2 = kPurposeDraw, w3 = t;
+    philox4x64_10(w0, w1, w2, w3, seed, step);
+    u1 = float(uint32_t(w0 >> 40)) * 0x1p-24f;
+    u2 = float(uint32_t(w1 >> 40)) * 0x1p-24f;
 }
 
 }  // namespace specv

@@ -30,12 +30,16 @@
 //                    each row's chunk partials, decides every verified row,
 //                    finds the first rejection a_r and writes the accepted
 //                    length and tokens. Greedy: complete. Sampling: a request
-//                    with a_r < L_r re-reads its rejected row pair with all 16
-//                    wavefronts for the chunk masses of max(0, p - q) (kept in
+//                    with a_r < L_r draws from max(0, p - q). With the library's
+//                    uniforms its wavefronts run rejection trials from p side by
+//                    side (chunk masses from the partials, one chunk read per
+//                    trial); with the caller's uniforms, or when all trials are
+//                    rejected, it re-reads its rejected row pair with all its
+//                    wavefronts for the chunk masses of the residual (kept in
 //                    LDS; split over the request's workgroups, which exchange
 //                    their masses through device-scope stores and one arrival
 //                    counter, the last to arrive drawing) and draws the token by
-//                    the inverse CDF; with every row kept it draws the bonus
+//                    the inverse CDF. With every row kept it draws the bonus
 //                    token from p of the bonus row (chunk masses from the
 //                    partials).
 #include <climits>
@@ -52,6 +56,7 @@ constexpr int kPhaseSlots = 2 * kStreamThreads;   // slots described in LDS at a
 constexpr int kDecideThreads = 1024;        // verify_decide: 16 wavefronts per workgroup, or
 constexpr int kDecideHalf = 512;            // 8 (two workgroups per compute unit)
 constexpr int kMaxChunks = 4096;            // sampling: chunks per row (residual masses live in LDS)
+constexpr int kResidualTrials = 16;         // counter-based uniforms: rejection trials of the residual draw
 constexpr int kNV = 4;                      // 16-byte vectors per lane per item
 constexpr int kChunkVecs = kWave * kNV;     // vectors per chunk
 
@@ -744,11 +749,13 @@ __device__ __forceinline__ float2 merge_partials(const float2* part, int C, int 
 
 // One workgroup per request. Phase 1: wavefront j merges the partials of row
 // j of the request, decides it, and the first rejection a_r follows. Phase 2
-// (sampling): a request with a_r < L_r streams its rejected row pair, all
-// wavefronts together, into per-chunk residual masses in LDS; wavefront 0 then
-// draws by the inverse CDF (chunk, then position in the chunk). With every row
-// kept, wavefront 0 draws the bonus token from p of the bonus row, chunk masses
-// taken from the partials.
+// (sampling): a request with a_r < L_r draws from the residual of its rejected
+// row pair. With counter-based uniforms the wavefronts first run rejection
+// trials from p (no re-read of the rows); with caller uniforms, or when every
+// trial is rejected, all wavefronts stream the row pair into per-chunk residual
+// masses in LDS and wavefront 0 draws by the inverse CDF (chunk, then position
+// in the chunk). With every row kept, wavefront 0 draws the bonus token from p
+// of the bonus row, chunk masses taken from the partials.
 static_assert(kDecideThreads == kSchedThreads, "the next round's schedule runs in a decide workgroup");
 
 template <int DT, int MODE, bool VEC, int NT>
@@ -769,7 +776,8 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
     __shared__ int g_s[SPECV_MAX_K + 1];
     __shared__ float4 st_s[SPECV_MAX_K + 1];
     __shared__ float mass_s[SAMPLE ? kMaxChunks : 1];
-    __shared__ int bad_s, nonfinite_s, stats_bad_s, rnext_s, last_s;
+    __shared__ int trial_y_s[SAMPLE ? kResidualTrials : 1];
+    __shared__ int bad_s, nonfinite_s, stats_bad_s, rnext_s, last_s, win_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = int(blockIdx.x) / nsplit, part = int(blockIdx.x) % nsplit;
     const bool writer = part == 0;                 // the workgroup that writes the request's decisions
@@ -881,6 +889,56 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
         const T* drow = static_cast<const T*>(a.draft) + (long(r) * k + min(acc, k - 1)) * long(V);
         const bool rejected = acc < L;
         if (!rejected && !writer) return;          // the bonus draw needs no re-read: one workgroup
+        if (rejected && !a.uniforms) {
+            // Counter-based uniforms: the residual by rejection from p. Trial t
+            // draws y ~ p of row a_r (chunk masses from the partials) with its
+            // first uniform and keeps y iff its second lies below 1 - q(y) / p(y),
+            // so a kept y has probability max(0, p(y) - q(y)) per trial: the
+            // normalised residual. The trials are independent, so the wavefronts
+            // run them side by side and the lowest kept one gives the token; a
+            // wavefront stops once a lower trial than its next one was kept.
+            // Every workgroup of the request runs them and reaches the same
+            // result; with none kept the draw falls back to the residual's
+            // inverse CDF (the re-read below) with the uniform of trial
+            // kResidualTrials.
+            const float2* pp = (a.pre0 && acc == 0) ? a.part0 + long(r) * C : a.part_p + long(base + acc) * C;
+            for (int cc = tid; cc < C; cc += NT) {
+                const float2 q = pp[cc];
+                mass_s[cc] = q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
+            }
+            if (tid == 0) win_s = INT_MAX;
+            __syncthreads();
+            for (int t = wave; t < kResidualTrials; t += kW) {
+                if (__hip_atomic_load(&win_s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < t) break;
+                float u1, u2;
+                philox_trial(a.seed, a.step, uint32_t(r), uint32_t(acc), uint32_t(t), u1, u2);
+                float cb, cth;
+                const int cs = wave_find_chunk(C, u1, [&](int cc) { return mass_s[cc]; }, cb, cth);
+                const int yy = chunk_pick<DT, VEC, false>(trow, nullptr, cs * CH, V, cb, cth, [&](float xt_, float) {
+                    return __builtin_amdgcn_exp2f(fmaf(xt_, c, -st.x));
+                });
+                const float py = exp2f(fmaf(RW::LT::load1(trow + yy), c, -st.x)) / st.y;
+                const float qy = exp2f(fmaf(RW::LT::load1(drow + yy), c, -st.z)) / st.w;
+                if (lane == 0 && py > 0.f && u2 < 1.f - qy / py) {
+                    trial_y_s[t] = yy;
+                    atomicMin(&win_s, t);
+                }
+            }
+            __syncthreads();
+            const int win = win_s;
+            if (win != INT_MAX) {
+                if (writer && tid == 0) {
+                    const int y = trial_y_s[win];
+                    out[acc] = y;
+                    // the bonus row's record: -(kept trial + 1), a_r, the token, the trial's first uniform
+                    float u1, u2;
+                    philox_trial(a.seed, a.step, uint32_t(r), uint32_t(acc), uint32_t(win), u1, u2);
+                    if (a.diag)
+                        reinterpret_cast<float4*>(a.diag)[N + r] = make_float4(-float(win + 1), float(acc), float(y), u1);
+                }
+                return;
+            }
+        }
         // a rejected row pair is split between the request's nsplit workgroups: chunks [lo, hi)
         const int Cs = (C + nsplit - 1) / nsplit;
         const int lo = rejected ? min(C, part * Cs) : 0, hi = rejected ? min(C, lo + Cs) : C;
@@ -955,8 +1013,15 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
             __syncthreads();
         }
         if (wave != 0) return;
-        const float ub = a.uniforms ? a.uniforms[long(r) * (k + 1) + k]
-                                    : philox_uniform(a.seed, a.step, kPurposeDraw, r, acc);
+        float ub;
+        if (a.uniforms) {
+            ub = a.uniforms[long(r) * (k + 1) + k];
+        } else if (rejected) {                     // the fallback after kResidualTrials rejected trials
+            float u2;
+            philox_trial(a.seed, a.step, uint32_t(r), uint32_t(acc), uint32_t(kResidualTrials), ub, u2);
+        } else {
+            ub = philox_uniform(a.seed, a.step, kPurposeDraw, r, acc);
+        }
         float total = 0.f;
         if (rejected)
             for (int c0 = 0; c0 < C; c0 += kWave) total += wave_sum_dpp(c0 + lane < C ? mass_s[c0 + lane] : 0.f);

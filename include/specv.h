@@ -35,7 +35,9 @@
  *     decision it drives (purpose 0: keep or reject the draft token at position i
  *     of request r; 1: the extra token drawn at position i = a_r; 2: the draft
  *     head's token at position i), so results depend on neither the schedule
- *     nor the row order. A caller that advances `step` once per decoding step
+ *     nor the row order (the residual draw's rejection trials use words 0 and 1
+ *     of the blocks at counters (a_r + 1, r, 1, t), t = 0 .. 16; spec_verify
+ *     states how). A caller that advances `step` once per decoding step
  *     gets fresh, reproducible randomness without any state in the library.
  *     The pages name Philox-seeded trials only; the rest is this library's
  *     reading. A caller may pass its own uniforms instead (the `uniforms`
@@ -199,12 +201,21 @@ int spec_flatten(int R, int k, const int32_t* len_in, int32_t* tags_out,
  *   a_r = first j < L_r not kept, else L_r.
  *   out_tokens[r,0..a_r-1] = x[r,0..a_r-1]; out_tokens[r,a_r] =
  *     greedy:   g_{a_r};
- *     sampling: inverse-CDF draw with u[r,k] from max(0, p - q) at row a_r when
- *               a_r < L_r (from p when that residual has no mass), else from
- *               p_{L_r}: the smallest v with w_0 + .. + w_v > u * sum(w).
+ *     sampling, a_r = L_r: the bonus token, an inverse-CDF draw from p_{L_r}
+ *               with u = U(seed, step, 1, r, a_r) or the caller's u[r,k]: the
+ *               smallest v with w_0 + .. + w_v > u * sum(w);
+ *     sampling, a_r < L_r: a draw from max(0, p - q) at row a_r (from p when
+ *               that residual has no mass). With the caller's uniforms: the
+ *               inverse-CDF draw with u[r,k]. With the generator: rejection
+ *               from p, trial t = 0, 1, .. 15 taking (u1, u2) = words 0 and 1
+ *               of the block at counter (a_r + 1, r, 1, t), each >> 40 times
+ *               2^-24: y = the inverse-CDF draw from p with u1, kept iff
+ *               u2 < 1 - q(y) / p(y); the first kept y is the token (exactly
+ *               residual-distributed). With all 16 rejected: the inverse-CDF
+ *               draw from the residual with u1 of trial 16.
  *   out_tokens[r, a_r+1 .. k] = -1; accepted_len[r] = a_r.
- * Uniforms: u[r,j] = U(seed, step, 0, r, j) and the draw's u = U(seed, step,
- * 1, r, a_r) (see the conventions above), or the caller's `uniforms`.
+ * Uniforms: u[r,j] = U(seed, step, 0, r, j) and the draws' above (see the
+ * conventions), or the caller's `uniforms`.
  * Arithmetic is float32 (softmax statistics in base 2 with a pre-scaled
  * log2(e)/tau); greedy decisions are exact comparisons.
  * Logits may be -inf (a token that cannot be drawn). A request with a NaN or
@@ -228,18 +239,22 @@ int spec_flatten(int R, int k, const int32_t* len_in, int32_t* tags_out,
  *   row_diag         f32 [R*(k+1),4] or NULL. Verified rows: sampling
  *                    {p(x), q(x), p(x)/q(x), u}, greedy {argmax, max logit, 0,
  *                    kept}. Bonus row of request r (row N + r): sampling
- *                    {sum(max(0, p - q)) at row a_r (0 when a_r = L_r), a_r,
- *                    drawn token, u of the draw}, greedy {argmax, max logit, 0,
- *                    -1}. Rows of a request with a data error: undefined.
+ *                    {m, a_r, drawn token, u of the draw (the kept trial's u1)}
+ *                    with m = -(t + 1) for a draw kept at trial t, else
+ *                    sum(max(0, p - q)) at row a_r (0 when a_r = L_r); greedy
+ *                    {argmax, max logit, 0, -1}. Rows of a request with a data
+ *                    error: undefined.
  *   ws, ws_bytes     workspace of at least spec_verify_workspace_bytes(R,k,V)
  *                    bytes, 256-byte aligned; its contents need no
  *                    initialisation (chunk partials of the call in flight)
  * Execution: two kernels on `stream`. A persistent grid streams every logit
  * row of the batch once into per-chunk partials; then one workgroup per request
- * decides its rows and, in sampling mode, re-reads the rejected row pair (or one
- * chunk of the bonus row) to draw the extra token. With fewer requests than
- * compute units (sampling), two or four workgroups share a request's re-read
- * and the last to finish draws; none ever waits for another.
+ * decides its rows and, in sampling mode, draws the extra token: the bonus
+ * draw and the rejection trials read one chunk of a row per draw; the
+ * inverse-CDF residual draw (caller uniforms, or all trials rejected) re-reads
+ * the rejected row pair. With fewer requests than compute units (sampling),
+ * two or four workgroups share a request's re-read and the last to finish
+ * draws; none ever waits for another.
  * Errors: SPECV_EINVAL (NULL pointers, sizes, tau, small workspace),
  *         SPECV_EUNSUPPORTED (dtype; R*(k+1)*V beyond 32-bit item counts;
  *         sampling with more than 4096 chunks per row, i.e. V > 8388608 in

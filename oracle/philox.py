@@ -58,6 +58,14 @@ def uniform(seed: int, step: int, purpose: int, r: int, i: int) -> float:
     return float(w0 >> 40) * 2.0 ** -24
 
 
+def trial_uniforms(seed: int, step: int, r: int, i: int, t: int):
+    """The two uniforms of trial t of the residual draw at position i of request
+    r: words 0 and 1 of the block at counter (i + 1, r, 1, t), each >> 40 and
+    times 2**-24. Trial 0's first uniform is U(seed, step, 1, r, i)."""
+    w = block((i + 1, r, DRAW, t), (seed, step))
+    return float(w[0] >> 40) * 2.0 ** -24, float(w[1] >> 40) * 2.0 ** -24
+
+
 def uniforms(seed: int, step: int, purpose: int, R: int, n: int) -> np.ndarray:
     """U(seed, step, purpose, r, i) for r < R, i < n: float64 [R, n] (every value
     is a float32)."""

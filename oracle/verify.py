@@ -105,6 +105,50 @@ def draw_rows(w: np.ndarray, u: np.ndarray, eps: float = 0.0):
     return y.astype(np.int64), near
 
 
+# Trials of the rejection draw from the residual before the inverse-CDF fallback.
+RESIDUAL_TRIALS = 16
+
+
+def residual_draw_rejection(p: np.ndarray, q: np.ndarray, trial_u, trials: int = RESIDUAL_TRIALS,
+                            near_eps: float = 0.0):
+    """One draw from max(0, p - q) / sum(max(0, p - q)) for one row (p, q [V]).
+
+    Trial t takes y ~ p by the inverse CDF with its first uniform u1 and keeps
+    it iff its second uniform u2 < 1 - q(y) / p(y); the first kept trial gives
+    the token. A proposal from p kept with probability max(0, p - q) / p has
+    probability max(0, p(y) - q(y)) of being kept as y, so the kept token has
+    exactly the normalised residual's distribution. If all `trials` trials are
+    rejected, the token is the inverse-CDF draw from the residual itself (from
+    p if it has no mass) with the uniform trial_u(trials)[0]: exact too, since
+    that draw does not depend on the rejected trials. trial_u(t) -> (u1, u2).
+
+    Returns (token, kept trial or -1, near): near lists what rounding could
+    change on the way: ("draw", t, tokens) for a trial whose proposal has
+    other tokens within near_eps (draw_rows' near sets), ("keep", t) for a
+    trial with |u2 - (1 - q(y) / p(y))| < 1e-6, ("fallback", tokens) for the
+    fallback draw.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    near = []
+    for t in range(trials):
+        u1, u2 = trial_u(t)
+        y, nb = draw_rows(p[None, :], np.array([u1]), near_eps)
+        y = int(y[0])
+        if len(nb[0]):
+            near.append(("draw", t, nb[0]))
+        bound = 1.0 - q[y] / p[y]
+        if abs(u2 - bound) < 1e-6:
+            near.append(("keep", t))
+        if u2 < bound:
+            return y, t, near
+    w = residual_rows(p[None, :], q[None, :])
+    y, nb = draw_rows(w, np.array([trial_u(trials)[0]]), near_eps)
+    if len(nb[0]):
+        near.append(("fallback", nb[0]))
+    return int(y[0]), -1, near
+
+
 def residual_rows(p: np.ndarray, q: np.ndarray) -> np.ndarray:
     """max(0, p - q) per row; p itself for rows where that has no mass."""
     w = np.maximum(p - q, 0.0)
@@ -157,15 +201,22 @@ def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
     (schedule.flatten).
 
     Uniforms (sampling): rng = (seed, step) takes them from the counter-based
-    generator (oracle.philox): U(seed, step, 0, r, j) keeps or rejects row j,
-    U(seed, step, 1, r, a_r) drives the draw. Without rng, u_verify [R,k+1]
-    gives them: column j < k keeps or rejects row j, column k drives the draw.
+    generator (oracle.philox): U(seed, step, 0, r, j) keeps or rejects row j;
+    the draw at a_r is the bonus draw with U(seed, step, 1, r, a_r) when every
+    row was kept, else the residual's rejection draw with the trial uniforms
+    of (r, a_r) (residual_draw_rejection). Without rng, u_verify [R,k+1]
+    gives them: column j < k keeps or rejects row j, column k drives an
+    inverse-CDF draw (from the residual, or from p for the bonus row).
 
     Returns a dict with accepted_len [R], out_tokens [R,k+1] (-1 after the last
     emitted token) and per-row and per-request diagnostics for parity tests,
-    among them the uniforms used (u_accept [R,k], u_draw [R]), the residual
-    mass sum(max(0, p - q)) of each rejected row a_r (0 where every row was
-    kept) and draw_near (draw_rows' near sets at near_eps).
+    among them the uniforms used (u_accept [R,k], u_draw [R]: the inverse-CDF
+    draw's uniform, or the kept trial's first one), the residual mass
+    sum(max(0, p - q)) of each rejected row a_r (0 where every row was kept),
+    draw_trial [R] (the kept trial of a rejection draw; -1: fallback or no
+    rejection draw), draw_by_trials [R] (the draw was a rejection draw) and
+    draw_near (draw_rows' near sets at near_eps; for a rejection draw,
+    residual_draw_rejection's list).
     """
     R, k1, V = target.shape
     k = k1 - 1
@@ -226,12 +277,15 @@ def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
     y = np.zeros(R, dtype=np.int64)
     near = [None] * R
     res_mass = np.zeros(R, dtype=np.float64)
+    trial = np.full(R, -1, dtype=np.int64)
+    by_trials = np.zeros(R, dtype=bool)
     for s in range(0, R, block_rows):
         rs = np.arange(s, min(R, s + block_rows))
         ar = a[rs]
         p = numerics.softmax(numerics.decode(target[rs, ar], dtype), tau)
         w = p.copy()
         rej = ar < L[rs]
+        q = None
         if rej.any():
             q = numerics.softmax(numerics.decode(draft[rs[rej], ar[rej]], dtype), tau)
             wr = np.maximum(p[rej] - q, 0.0)
@@ -241,11 +295,21 @@ def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
         y[rs], nb = draw_rows(w, u_draw[rs], near_eps)
         for n_, r_ in enumerate(rs):
             near[r_] = nb[n_]
+        if rng is not None and rej.any():
+            # the residual by rejection from p (the counter-based uniforms' draw)
+            for n_, r_ in enumerate(rs[rej]):
+                i_ = int(a[r_])
+                yy, tt, nn = residual_draw_rejection(
+                    p[np.nonzero(rej)[0][n_]], q[n_],
+                    lambda t, r_=r_, i_=i_: philox.trial_uniforms(seed, step, int(r_), i_, t), near_eps=near_eps)
+                y[r_], trial[r_], near[r_], by_trials[r_] = yy, tt, nn, True
+                u_draw[r_] = philox.trial_uniforms(seed, step, int(r_), i_, tt if tt >= 0 else RESIDUAL_TRIALS)[0]
     row_ratio = np.full(B, np.nan)
     row_acc = np.zeros(B, dtype=bool)
     row_ratio[vidx] = ratio[tags[vidx, 0], tags[vidx, 1]]
     row_acc[vidx] = acc[tags[vidx, 0], tags[vidx, 1]]
     res.update(accepted_len=a, out_tokens=_emit(a, x, y, k), row_p=row_p, row_q=row_q,
                row_ratio=row_ratio, row_accept=row_acc, accept=acc, draw_near=near,
-               residual_mass=res_mass, row_verified=ver, u_accept=u_acc, u_draw=u_draw)
+               residual_mass=res_mass, row_verified=ver, u_accept=u_acc, u_draw=u_draw, draw_trial=trial,
+               draw_by_trials=by_trials)
     return res

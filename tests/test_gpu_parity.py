@@ -11,8 +11,12 @@ Tolerances:
                 cancellation in p - q); keep decisions identical except where
                 |u - p/q| < 1e-6; resampled / bonus tokens identical except
                 where the kernel's token is in the oracle's near set (its CDF
-                interval within 1e-5 * W of t = u W, oracle.verify.draw_rows),
-                at most DRAW_EXEMPT_LIMIT of them per case.
+                interval within 1e-5 * W of t = u W, oracle.verify.draw_rows);
+                residual draws by rejection trials (the library's uniforms):
+                the same kept trial and token, except where the oracle marked
+                a trial at or before the earlier side's last one as near (a
+                proposal near set, or |u2 - (1 - q/p)| < 1e-6); at most
+                DRAW_EXEMPT_LIMIT excused draws per case.
   Markov head   stored logits within the float32 accumulation bound plus half
                 a storage spacing of the exact value (check_markov); tokens
                 identical except where rounding differences can move them.
@@ -247,9 +251,24 @@ def _first_false(keep, L):
     return a
 
 
-def check_sampling(d, ref, tags, cu, case, tol=1e-5):
+def _trials_explain(near, T, tok_g):
+    """A rejection draw that differs between the kernel and the oracle (token or
+    kept trial) is excused iff the oracle saw a rounding-sensitive step at or
+    before T = the earlier of the two sides' last trials (16 for a fallback):
+    a proposal or keep decision of trial <= T, or the fallback draw with the
+    kernel's token in its near set."""
+    for e in near:
+        if e[0] in ("draw", "keep") and e[1] <= T:
+            return True
+        if e[0] == "fallback" and T == overify.RESIDUAL_TRIALS and tok_g in e[1]:
+            return True
+    return False
+
+
+def check_sampling(d, ref, tags, cu, case, tol=1e-5, rng=None):
     """Sampling-mode parity (see the module docstring); records and returns the
-    exemption counts."""
+    exemption counts. rng = (seed, step) of the counter-based uniforms when the
+    kernel drew them."""
     Bn = osched.n_rows(cu)
     R = len(cu) - 1
     N = int(cu[-1])
@@ -288,15 +307,39 @@ def check_sampling(d, ref, tags, cu, case, tol=1e-5):
     n_exempt = 0
     worst_res = 0.0
     n_res = 0
+    n_trials = 0
+    trials_used = 0
+    NT = overify.RESIDUAL_TRIALS
     for r in np.nonzero(same)[0]:
         a = int(a_o[r])
         assert np.array_equal(out_g[r, :a], out_o[r, :a])
         assert (out_g[r, a + 1:] == -1).all()
-        assert bon[r, 3] == ref["u_draw"][r], ("draw uniform", r)
         assert int(bon[r, 1]) == a and int(bon[r, 2]) == out_g[r, a], ("bonus record", r)
-        if out_g[r, a] != out_o[r, a]:
-            assert out_g[r, a] in ref["draw_near"][r], (r, out_g[r, a], out_o[r, a], ref["draw_near"][r])
-            n_exempt += 1
+        if ref["draw_by_trials"][r]:
+            # the residual by rejection trials: the kernel's kept trial (-(t+1) in
+            # column 0; a mass >= 0 there: the fallback) and token against the oracle's
+            t_g = int(-bon[r, 0]) - 1 if bon[r, 0] < 0 else -1
+            t_o = int(ref["draw_trial"][r])
+            if t_g >= 0:
+                n_trials += 1
+                trials_used += t_g + 1
+            if t_g == t_o and out_g[r, a] == out_o[r, a]:
+                assert bon[r, 3] == ref["u_draw"][r], ("draw uniform", r)
+            else:
+                T = min(t_g if t_g >= 0 else NT, t_o if t_o >= 0 else NT)
+                assert _trials_explain(ref["draw_near"][r], T, int(out_g[r, a])), \
+                    (r, t_g, t_o, out_g[r, a], out_o[r, a], ref["draw_near"][r])
+                assert rng is not None
+                want = ophilox.trial_uniforms(rng[0], rng[1], int(r), a, t_g if t_g >= 0 else NT)[0]
+                assert bon[r, 3] == want, ("draw uniform", r)
+                n_exempt += 1
+            if t_g >= 0:
+                continue
+        else:
+            assert bon[r, 3] == ref["u_draw"][r], ("draw uniform", r)
+            if out_g[r, a] != out_o[r, a]:
+                assert out_g[r, a] in ref["draw_near"][r], (r, out_g[r, a], out_o[r, a], ref["draw_near"][r])
+                n_exempt += 1
         if a < L[r]:
             m_o, m_g = ref["residual_mass"][r], bon[r, 0]
             assert abs(m_g - m_o) <= tol * m_o + 2e-6, ("residual mass", r, m_g, m_o)
@@ -309,7 +352,9 @@ def check_sampling(d, ref, tags, cu, case, tol=1e-5):
     assert n_exempt <= DRAW_EXEMPT_LIMIT(draws), (n_exempt, draws)
     rec = parity_log.record("verify", case, rows=int(ver.sum()), near_keep=int(near.sum()),
                             keep_flips=int(flips.sum()), draws=draws, draw_exempt=n_exempt,
-                            residual_rows=n_res, worst_p=worst["row_p"], worst_q=worst["row_q"],
+                            residual_rows=n_res, trial_draws=n_trials,
+                            mean_trials=trials_used / n_trials if n_trials else 0.0,
+                            worst_p=worst["row_p"], worst_q=worst["row_q"],
                             worst_ratio=worst["row_ratio"], worst_residual=worst_res)
     say("parity", rec)
     return rec
@@ -323,14 +368,16 @@ SAMPLE_CASES = [("c0", 5), ("c1", 5), ("c2", 5), ("c2", -1), ("c3", 16), ("c3", 
 def test_verify_sampling_within_tolerance(name, max_len, source):
     rng = (int(workloads.CONFIGS[name]["seed"]), 3) if source == "philox" else None
     d, ref, tags, cu = _run_verify(name, "sample", max_len, rng=rng)
-    check_sampling(d, ref, tags, cu, f"{name} max_len={max_len} {source}")
+    check_sampling(d, ref, tags, cu, f"{name} max_len={max_len} {source}", rng=rng)
 
 
 @pytest.mark.parametrize("seed,step", [(0, 0), (7, 1), ((1 << 64) - 1, (1 << 63) + 11), (12345, (1 << 32) + 7)])
 def test_philox_uniforms_bit_exact(seed, step):
-    """The kernel's uniforms: U(seed, step, 0, r, j) for every verified row and
-    U(seed, step, 1, r, a_r) for every draw, bit for bit the oracle's Philox
-    (pinned to numpy.random.Philox), at 64-bit keys too."""
+    """The kernel's uniforms: U(seed, step, 0, r, j) for every verified row,
+    U(seed, step, 1, r, a_r) for every bonus draw and the kept trial's (or the
+    fallback's) first uniform for every residual draw, bit for bit the oracle's
+    Philox (pinned to numpy.random.Philox), at 64-bit keys too; and the whole
+    result against the oracle with those uniforms."""
     R, k, V = 48, 6, 3000
     tl, dl, x, _, L = _small(R, k, V, "bf16", seed=41)
     L[:] = k
@@ -342,8 +389,17 @@ def test_philox_uniforms_bit_exact(seed, step):
     assert np.array_equal(rows[:, :, 3].astype(np.float64), want)
     bonus = diag[R * k:R * k + R]
     for r in range(R):
-        assert int(bonus[r, 1]) == acc[r]
-        assert float(bonus[r, 3]) == ophilox.uniform(seed, step, ophilox.DRAW, r, int(acc[r]))
+        a = int(acc[r])
+        assert int(bonus[r, 1]) == a
+        if a == k:
+            assert float(bonus[r, 3]) == ophilox.uniform(seed, step, ophilox.DRAW, r, a)
+        else:
+            t = int(-bonus[r, 0]) - 1 if bonus[r, 0] < 0 else overify.RESIDUAL_TRIALS
+            assert float(bonus[r, 3]) == ophilox.trial_uniforms(seed, step, r, a, t)[0]
+    tags, cu = osched.flatten(L)
+    ref = overify.verify("sample", "bf16", tl, dl, x, tags, cu, 1.0, rng=(seed, step), near_eps=overify.DRAW_EPS)
+    check_sampling(_Res(acc, out, diag), ref, tags, cu, f"philox uniforms seed={seed} step={step}",
+                   rng=(seed, step))
 
 
 def test_verify_deterministic():

@@ -84,7 +84,7 @@ def test_sweep_schedule_and_verify(full):
         assert B.read_status(d.ws_verify) == 0
         ref = overify.verify("sample", w.dtype, w.target, w.draft, w.tokens_sample, tags, cu, w.tau,
                              rng=(d.seed, 9))
-        check_sampling(d, ref, tags, cu, f"sweep R={R} V=4096 philox")
+        check_sampling(d, ref, tags, cu, f"sweep R={R} V=4096 philox", rng=(d.seed, 9))
         del d
         torch.cuda.empty_cache()
     say("sweep mean lengths", dict(zip(LOADS, means)))

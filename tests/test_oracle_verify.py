@@ -149,9 +149,10 @@ def test_chisquare_planted_mistakes_fail(logit_model, bad):
 # ---------------------------------------------------------------------------
 
 def test_rng_uniforms_are_addressed_by_decision():
-    """verify(rng=(seed, step)) equals verify() on the array of the same
-    uniforms: U(seed, step, 0, r, j) for row j, U(seed, step, 1, r, a_r) for
-    the draw."""
+    """verify(rng=(seed, step)): the keep decisions use U(seed, step, 0, r, j)
+    (the same as an array holding them), the bonus draw U(seed, step, 1, r, L_r),
+    and the residual draw of a rejecting request is residual_draw_rejection
+    with that request's trial uniforms."""
     from oracle import philox
     g = np.random.Generator(np.random.Philox(31))
     R, k, V = 40, 4, 24
@@ -169,11 +170,97 @@ def test_rng_uniforms_are_addressed_by_decision():
         u[r, k] = philox.uniform(7, 12, philox.DRAW, r, int(res["accepted_len"][r]))
     ref = verify.verify("sample", "f32", tl, dl, x, tags, cu, 1.0, u)
     assert np.array_equal(res["accepted_len"], ref["accepted_len"])
-    assert np.array_equal(res["out_tokens"], ref["out_tokens"])
-    assert np.array_equal(res["u_accept"], u[:, :k]) and np.array_equal(res["u_draw"], u[:, k])
+    assert np.array_equal(res["u_accept"], u[:, :k])
+    a = res["accepted_len"]
+    bonus = a == L
+    assert bonus.any() and (~bonus).any()
+    assert np.array_equal(res["out_tokens"][bonus], ref["out_tokens"][bonus])
+    P = numerics.softmax(tl.astype(np.float64), 1.0)
+    for r in np.nonzero(~bonus)[0]:
+        assert np.array_equal(res["out_tokens"][r, :a[r]], x[r, :a[r]])
+        yy, tt, _ = verify.residual_draw_rejection(P[r, a[r]], Qd[r, a[r]],
+                                                   lambda t, r=r: philox.trial_uniforms(7, 12, r, int(a[r]), t))
+        assert res["out_tokens"][r, a[r]] == yy and res["draw_trial"][r] == tt
     # another step gives other decisions
     other = verify.verify("sample", "f32", tl, dl, x, tags, cu, 1.0, rng=(7, 13))
     assert not np.array_equal(other["u_accept"], res["u_accept"])
+
+
+def _residual_dists(g, V):
+    p = g.gamma(1.0, size=V)
+    p /= p.sum()
+    q = g.gamma(1.0, size=V)
+    q /= q.sum()
+    res = np.maximum(p - q, 0.0)
+    return p, q, res / res.sum()
+
+
+def _chi2_p(counts, expected):
+    """Chi-square p-value; a count in a cell of expected 0 gives 0."""
+    from scipy import stats
+    zero = expected == 0
+    if counts[zero].sum() > 0:
+        return 0.0
+    return stats.chisquare(counts[~zero], expected[~zero]).pvalue
+
+
+def test_residual_rejection_draw_is_exact():
+    """The rejection draw's tokens follow max(0, p - q) normalised: a
+    chi-square on 2e5 draws (V = 8) against it, with few trials so that the
+    fallback is exercised too. Planted mistakes fail: keeping with probability
+    q / p, keeping every proposal, and a fallback from p."""
+    g = np.random.Generator(np.random.Philox(77))
+    V = 8
+    p, q, res = _residual_dists(g, V)
+    n = 100_000
+    uu = g.random((n, 4, 2))
+
+    def run(draw, trials):
+        ys = np.array([draw(p, q, lambda t, i=i: (uu[i, min(t, 3), 0], uu[i, min(t, 3), 1]), trials)[0]
+                       for i in range(n)])
+        return np.bincount(ys, minlength=V)
+
+    counts = run(lambda p_, q_, f, T: verify.residual_draw_rejection(p_, q_, f, T), 2)
+    assert _chi2_p(counts, res * n) > 1e-4
+
+    def keep_q_over_p(p_, q_, f, T):
+        orig = verify.residual_draw_rejection
+        for t in range(T):
+            u1, u2 = f(t)
+            y = int(verify.draw_rows(p_[None, :], np.array([u1]))[0][0])
+            if u2 < min(1.0, q_[y] / p_[y]):
+                return y, t, []
+        return orig(p_, q_, f, 0)
+
+    def keep_all(p_, q_, f, T):
+        return int(verify.draw_rows(p_[None, :], np.array([f(0)[0]]))[0][0]), 0, []
+
+    def fallback_from_p(p_, q_, f, T):
+        y, t, nn = verify.residual_draw_rejection(p_, q_, f, T)
+        if t < 0:
+            y = int(verify.draw_rows(p_[None, :], np.array([f(T)[0]]))[0][0])
+        return y, t, nn
+    for bad in (keep_q_over_p, keep_all):
+        assert _chi2_p(run(bad, 2), res * n) < 1e-9
+    # the fallback alone (no trials) is the inverse-CDF draw from the residual
+    assert _chi2_p(run(lambda p_, q_, f, T: verify.residual_draw_rejection(p_, q_, f, 0), 0), res * n) > 1e-4
+    assert _chi2_p(run(fallback_from_p, 0), res * n) < 1e-9
+
+
+def test_residual_rejection_draw_fallback_and_empty_residual():
+    # p == q: no trial can keep; the fallback draws from p
+    p = np.array([0.5, 0.25, 0.125, 0.125])
+    y, t, near = verify.residual_draw_rejection(p, p.copy(), lambda t: (0.6, 0.0), 16)
+    assert t == -1 and y == 1                 # C = [0.5, 0.75, ...]: t = 0.6 falls in token 1
+    # a trial keeps iff u2 < 1 - q(y) / p(y)
+    q = np.array([0.25, 0.25, 0.25, 0.25])
+    y, t, _ = verify.residual_draw_rejection(p, q, lambda t: (0.1, 0.49), 16)   # y = 0: 1 - q/p = 0.5
+    assert (y, t) == (0, 0)
+    seq = iter([(0.1, 0.51), (0.1, 0.49)])
+    y, t, _ = verify.residual_draw_rejection(p, q, lambda t: next(seq), 16)
+    assert (y, t) == (0, 1)
+    y, t, near = verify.residual_draw_rejection(p, q, lambda t: (0.1, 0.5 - 1e-7), 16)
+    assert (y, t) == (0, 0) and ("keep", 0) in near
 
 
 def test_rng_chisquare_lossless(logit_model):
