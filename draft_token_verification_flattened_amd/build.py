@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -53,18 +54,51 @@ def _hipcc() -> str:
 SOURCE_FLAGS = {"verify.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
+# Kernels must not spill VGPRs. The compiler can place a spill store inside a
+# lane-divergent block (an `if (lane == 0)` region), where it saves only the
+# active lanes, and reload the value later with every lane active: the other
+# lanes then read stale scratch memory (for an address, a wild access). Every
+# kernel is kept within its register budget, and the build refuses one that is
+# not.
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+_REMARK_NAME = re.compile(r"remark:\s+Function Name: (\S+)")
+_REMARK_SPILL = re.compile(r"remark:\s+VGPRs Spill: (\d+)")
+
+
+def vgpr_spills(remarks: str) -> dict:
+    """{kernel: spilled VGPRs} for every kernel with spills in the compiler's
+    kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for line in remarks.splitlines():
+        m = _REMARK_NAME.search(line)
+        if m:
+            cur = m.group(1)
+            continue
+        m = _REMARK_SPILL.search(line)
+        if m and cur is not None and int(m.group(1)) > 0:
+            out[cur] = int(m.group(1))
+    return out
+
+
 def _compile(src: str, hipcc: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
+    else:
+        cmd += RESOURCE_REMARKS
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
-    if verbose and res.stderr.strip():
-        print(res.stderr, file=sys.stderr)
+    spills = vgpr_spills(res.stderr)
+    if spills:
+        raise RuntimeError(f"{src}: kernels spill VGPRs (refused): {spills}")
+    if verbose:
+        rest = "\n".join(l for l in res.stderr.splitlines() if "remark:" not in l).strip()
+        if rest:
+            print(rest, file=sys.stderr)
     return obj
 
 

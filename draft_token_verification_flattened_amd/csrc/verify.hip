@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
     __shared__ float st_x[kPhaseSlots];              // logit at the draft token, if the item holds it
     __shared__ unsigned char st_f[kPhaseSlots];
     __shared__ int sh[64];
-    __shared__ int n_live, next_item;
+    __shared__ int next_item;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const uint32_t G = gridDim.x, b = blockIdx.x;
     if (b == 0 && tid == 0) a.hdr->status = 0u;
@@ -426,8 +426,16 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
         };
         // Two items per wavefront: the next one's loads are issued before the current
         // one is reduced. The last item is handled on its own exit path, so that in
-        // the loop every issue is unconditional.
-        {
+        // the loop every issue is unconditional. Scalar rows: one item at a time
+        // (their loads fill twice the registers).
+        if constexpr (!VEC) {
+            while (true) {                         // q0 holds an issued item here
+                process(q0, m0);
+                const int i0 = grab();
+                if (i0 >= nl) break;
+                issue(q0, m0, i0);
+            }
+        } else {
             while (true) {                         // q0 holds an issued item here
                 const int i1 = grab();
                 if (i1 >= nl) {
@@ -473,7 +481,8 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
 // bonus row when L_r = 0), into part0 (and ax0, the logit at draft token
 // (r, 0)); verify_stream then skips those rows. Work items are (request,
 // chunk) pairs, taken grid-stride by the streaming wavefronts in batches of at
-// most kPreBatch. A wavefront has only a few items (about five at 256
+// most kPreBatch (one fewer in sampling mode; scalar rows: one item at a time,
+// so that no registers spill). A wavefront has only a few items (about five at 256
 // requests), so the loads go through a ring of kPreRing buffers: the first
 // kPreRing are issued at once, and each later one as soon as a buffer is free.
 // Every batch size is its own unrolled instance, so the compiler counts the
@@ -551,15 +560,23 @@ __global__ __launch_bounds__(kStreamThreads) void verify_prefetch0(VerifyArgs a)
     const uint32_t nw = (gridDim.x - 1) * kWaves;
     const uint32_t gw = (blockIdx.x - 1) * kWaves + (threadIdx.x >> 6);
     const uint32_t items = uint32_t(a.R) * uint32_t(a.C);
-    for (uint32_t i0 = gw; i0 < items; i0 += kPreBatch * nw) {
-        const int nb = int(min(uint32_t(kPreBatch), (items - 1 - i0) / nw + 1));   // items of this batch
-        static_assert(kPreBatch == 5, "one case per batch size");
+    if constexpr (!VEC) {                 // scalar rows: one item at a time (registers)
+        for (uint32_t i0 = gw; i0 < items; i0 += nw) prefetch0_batch<DT, MODE, VEC, 1>(a, i0, nw, lane);
+        return;
+    }
+    // sampling keeps the draft token's logit per item too: one item fewer per batch (registers)
+    constexpr int kB = MODE == SPECV_SAMPLE ? kPreBatch - 1 : kPreBatch;
+    static_assert(kPreBatch == 5, "one case per batch size");
+    for (uint32_t i0 = gw; i0 < items; i0 += kB * nw) {
+        const int nb = int(min(uint32_t(kB), (items - 1 - i0) / nw + 1));   // items of this batch
         switch (nb) {
             case 1: prefetch0_batch<DT, MODE, VEC, 1>(a, i0, nw, lane); break;
             case 2: prefetch0_batch<DT, MODE, VEC, 2>(a, i0, nw, lane); break;
             case 3: prefetch0_batch<DT, MODE, VEC, 3>(a, i0, nw, lane); break;
             case 4: prefetch0_batch<DT, MODE, VEC, 4>(a, i0, nw, lane); break;
-            default: prefetch0_batch<DT, MODE, VEC, 5>(a, i0, nw, lane); break;
+            default:
+                if constexpr (kB >= 5) prefetch0_batch<DT, MODE, VEC, 5>(a, i0, nw, lane);
+                break;
         }
     }
 }
@@ -570,26 +587,40 @@ __global__ __launch_bounds__(kStreamThreads) void verify_prefetch0(VerifyArgs a)
 
 // In-chunk inverse CDF. The chunk of CH logits starting at `beg` of the target
 // row (and, for PAIR, of the draft row) is loaded in the stream layout; wt(xt,
-// xd) is an element's weight. Returns the first element whose running sum from
+// xd) is an element's weight, 0 for a target logit of -inf (exp2 of -inf; the
+// elements past V read as -inf). Returns the first element whose running sum from
 // `base`, in index order, exceeds thr; else the last element with positive
 // weight (beg if none). The chunk is kNV groups of 64 lanes x GW elements in
 // index order (lane-major inside a group): the group totals pick the group, a
 // scan of the lanes' sums picks the lane, and the lane scans its own elements.
+// With `vals`, also the target and (PAIR) draft logits at the returned element,
+// from the registers where the chunk was loaded in vector form.
 template <int DT, bool VEC, bool PAIR, class Wf>
 __device__ __forceinline__ int chunk_pick(const typename Logit<DT>::T* trow, const typename Logit<DT>::T* drow, int beg,
-                                          int V, float base, float thr, Wf wt) {
+                                          int V, float base, float thr, Wf wt, float2* vals = nullptr) {
     using RW = Raw<DT, VEC>;
     constexpr int GW = RW::kVec;
     const int lane = threadIdx.x & (kWave - 1);
     const bool full = beg + chunk_elems(GW) <= V;
     const int nv = VEC ? V / GW - beg / GW - lane : 0;
+    // scalar rows: group u's logits of the lane, -inf past V; loaded group by
+    // group (pass 1 keeps only the group sums, the crossing group is reloaded),
+    // so that few loads are in flight at once
+    auto scalar_group = [&](int u, float (&xt)[GW], float (&xd)[GW]) {
+#pragma unroll
+        for (int e = 0; e < GW; ++e) {
+            const int x = beg + RW::offset(u * GW + e, lane);
+            xt[e] = x < V ? RW::LT::load1(trow + x) : -INFINITY;
+            if constexpr (PAIR) xd[e] = x < V ? RW::LT::load1(drow + x) : -INFINITY;
+        }
+    };
     RW rt, rd;
     if constexpr (VEC) {
         rt.load(trow, beg, V, lane, full);
         if constexpr (PAIR) rd.load(drow, beg, V, lane, full);
     }
-    float w[kNV][GW], ls[kNV], gt[kNV];
-    int lastw = -1;
+    // VEC: all weights stay in registers; scalar rows keep none
+    float w[VEC ? kNV : 1][GW], ls[kNV], gt[kNV];
 #pragma unroll
     for (int u = 0; u < kNV; ++u) {
         float xt[GW], xd[GW];
@@ -597,22 +628,29 @@ __device__ __forceinline__ int chunk_pick(const typename Logit<DT>::T* trow, con
             RW::LT::unpack(rt.v[u], xt);
             if constexpr (PAIR) RW::LT::unpack(rd.v[u], xd);
         } else {
-#pragma unroll
-            for (int e = 0; e < GW; ++e) {
-                const int x = beg + RW::offset(u * GW + e, lane);
-                xt[e] = x < V ? RW::LT::load1(trow + x) : -INFINITY;
-                if constexpr (PAIR) xd[e] = x < V ? RW::LT::load1(drow + x) : -INFINITY;
-            }
+            scalar_group(u, xt, xd);
         }
         const bool ok = !VEC || full || u * kWave < nv;
         ls[u] = 0.f;
 #pragma unroll
         for (int e = 0; e < GW; ++e) {
-            w[u][e] = ok && xt[e] != -INFINITY ? wt(xt[e], PAIR ? xd[e] : 0.f) : 0.f;
-            ls[u] += w[u][e];
-            if (w[u][e] > 0.f) lastw = beg + RW::offset(u * GW + e, lane);
+            const float we = ok ? wt(xt[e], PAIR ? xd[e] : 0.f) : 0.f;
+            if constexpr (VEC) w[u][e] = we;
+            ls[u] += we;
         }
+        if constexpr (!VEC) __builtin_amdgcn_sched_barrier(0);
     }
+    // weights of group u (VEC: kept; scalar rows: reloaded and recomputed, the same values)
+    auto group_w = [&](int u, float (&wu)[GW], float (&xt)[GW], float (&xd)[GW]) {
+        if constexpr (VEC) {
+#pragma unroll
+            for (int e = 0; e < GW; ++e) wu[e] = w[u][e];
+        } else {
+            scalar_group(u, xt, xd);
+#pragma unroll
+            for (int e = 0; e < GW; ++e) wu[e] = wt(xt[e], PAIR ? xd[e] : 0.f);
+        }
+    };
 #pragma unroll
     for (int u = 0; u < kNV; ++u) gt[u] = wave_sum_dpp(ls[u]);
     float run = base;
@@ -623,22 +661,56 @@ __device__ __forceinline__ int chunk_pick(const typename Logit<DT>::T* trow, con
             const uint64_t hit = __ballot(run + incl > thr);
             if (hit) {
                 const int l = __builtin_ctzll(hit);
+                float wu[GW], xt[GW], xd[GW];
+                group_w(u, wu, xt, xd);
                 float cum = run + (incl - ls[u]);
                 int f = -1, lp = GW - 1;                // first element of the lane past thr
 #pragma unroll
                 for (int e = 0; e < GW; ++e) {
-                    cum += w[u][e];
+                    cum += wu[e];
                     if (f < 0 && cum > thr) f = e;
-                    if (w[u][e] > 0.f) lp = e;
+                    if (wu[e] > 0.f) lp = e;
                 }
-                const int fe = __builtin_amdgcn_readlane(f < 0 ? lp : f, l);
-                return beg + RW::offset(u * GW + fe, l);
+                const int fs = f < 0 ? lp : f;
+                const int fe = __builtin_amdgcn_readlane(fs, l);
+                const int y = beg + RW::offset(u * GW + fe, l);
+                if (vals) {
+                    if constexpr (VEC) {
+                        float tv[GW], dv[GW];
+                        RW::LT::unpack(rt.v[u], tv);
+                        if constexpr (PAIR) RW::LT::unpack(rd.v[u], dv);
+                        float st = tv[0], sd = PAIR ? dv[0] : 0.f;
+#pragma unroll
+                        for (int e = 1; e < GW; ++e)
+                            if (fs == e) {
+                                st = tv[e];
+                                if constexpr (PAIR) sd = dv[e];
+                            }
+                        *vals = make_float2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(st), l)),
+                                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sd), l)));
+                    } else {
+                        *vals = make_float2(RW::LT::load1(trow + y), PAIR ? RW::LT::load1(drow + y) : 0.f);
+                    }
+                }
+                return y;
             }
         }
         run += gt[u];
     }
+    // no crossing (rounding): the last element with positive weight
+    int lastw = -1;
+#pragma unroll
+    for (int u = 0; u < kNV; ++u) {
+        float wu[GW], xt[GW], xd[GW];
+        group_w(u, wu, xt, xd);
+#pragma unroll
+        for (int e = 0; e < GW; ++e)
+            if (wu[e] > 0.f) lastw = beg + RW::offset(u * GW + e, lane);
+    }
     const int lw = -wave_min_int_dpp(-lastw);
-    return lw >= 0 ? lw : beg;
+    const int y = lw >= 0 ? lw : beg;
+    if (vals) *vals = make_float2(RW::LT::load1(trow + y), PAIR ? RW::LT::load1(drow + y) : 0.f);
+    return y;
 }
 
 // Chunk holding the draw among C chunk masses, in chunk order: the first chunk
@@ -686,6 +758,29 @@ __device__ __forceinline__ float residual_weight(float xt, float xd, float c, fl
 
 // Residual mass of one chunk of a row pair, one 16-byte vector (or group of
 // scalars) at a time so that few values are live at once.
+// Scalar rows: the same sum with the chunk read group by group (kVec logits per
+// lane of each row at a time), so that few loads are in flight at once.
+template <int DT>
+__device__ __forceinline__ float scalar_chunk_residual_mass(const typename Logit<DT>::T* trow,
+                                                            const typename Logit<DT>::T* drow, int beg, int V,
+                                                            int lane, float c, float lp, float lq) {
+    using RW = Raw<DT, false>;
+    constexpr int GW = RW::kVec;
+    float s[2] = {0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kNV; ++u) {
+#pragma unroll
+        for (int e = 0; e < GW; ++e) {
+            const int x = beg + RW::offset(u * GW + e, lane);
+            const float xt = x < V ? RW::LT::load1(trow + x) : -INFINITY;
+            const float xd = x < V ? RW::LT::load1(drow + x) : -INFINITY;
+            s[e & 1] += residual_weight(xt, xd, c, lp, lq);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return wave_sum_dpp(s[0] + s[1]);
+}
+
 template <int DT, bool VEC>
 __device__ __forceinline__ float chunk_residual_mass(const Raw<DT, VEC>& rt, const Raw<DT, VEC>& rd, int beg, int V,
                                                      int lane, float c, float lp, float lq) {
@@ -715,17 +810,23 @@ __device__ __forceinline__ float chunk_residual_mass(const Raw<DT, VEC>& rt, con
 }
 
 // Softmax state (M, S) of a row from its chunk partials, or (argmax value,
-// lowest index) in greedy mode: one wavefront, the first 4 * 64 partials
-// loaded in one round.
+// lowest index) in greedy mode: one wavefront. load_partials issues the first
+// kMergePre * 64 partials in one round (lane's partials lane + u * 64, left in
+// v); reduce_partials merges them and the rest.
+constexpr int kMergePre = 4;
+
 template <bool SAMPLE>
-__device__ __forceinline__ float2 merge_partials(const float2* part, int C, int lane) {
-    constexpr int kPre = 4;
-    float2 v[kPre];
+__device__ __forceinline__ void load_partials(const float2* part, int C, int lane, float2 (&v)[kMergePre]) {
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) {
+    for (int u = 0; u < kMergePre; ++u) {
         const int cc = lane + u * kWave;
         v[u] = cc < C ? part[cc] : (SAMPLE ? make_float2(-INFINITY, 0.f) : make_float2(-INFINITY, __int_as_float(INT_MAX)));
     }
+}
+
+template <bool SAMPLE>
+__device__ __forceinline__ float2 reduce_partials(const float2* part, int C, int lane, const float2 (&v)[kMergePre]) {
+    constexpr int kPre = kMergePre;
     float m = -INFINITY, z = 0.f;
     int gi = INT_MAX;
 #pragma unroll
@@ -747,6 +848,35 @@ __device__ __forceinline__ float2 merge_partials(const float2* part, int C, int 
     return make_float2(m, __int_as_float(gi));
 }
 
+// Chunk holding the draw among C chunks given the inclusive prefix sums `pre`
+// of their masses (in LDS): the first chunk whose prefix exceeds
+// thr = u * pre[C-1], with the prefix before it in `base`; without one
+// (rounding), the last chunk with positive mass and an in-chunk threshold of
+// +inf.
+__device__ __forceinline__ int wave_find_chunk_prefix(int C, float u, const float* pre, float& base, float& cthr) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const float thr = u * pre[C - 1];
+    for (int c0 = 0; c0 < C; c0 += kWave) {
+        const int cc = c0 + lane;
+        const uint64_t hit = __ballot(cc < C && pre[min(cc, C - 1)] > thr);
+        if (hit) {
+            const int ch = c0 + __builtin_ctzll(hit);
+            base = ch > 0 ? pre[ch - 1] : 0.f;
+            cthr = thr;
+            return ch;
+        }
+    }
+    int last_pos = -1;
+    for (int c0 = 0; c0 < C; c0 += kWave) {
+        const int cc = c0 + lane;
+        const uint64_t pos = __ballot(cc < C && pre[min(cc, C - 1)] > (cc > 0 ? pre[max(cc - 1, 0)] : 0.f));
+        if (pos) last_pos = c0 + 63 - __builtin_clzll(pos);
+    }
+    base = 0.f;
+    cthr = INFINITY;
+    return last_pos < 0 ? 0 : last_pos;
+}
+
 // One workgroup per request. Phase 1: wavefront j merges the partials of row
 // j of the request, decides it, and the first rejection a_r follows. Phase 2
 // (sampling): a request with a_r < L_r draws from the residual of its rejected
@@ -759,7 +889,10 @@ __device__ __forceinline__ float2 merge_partials(const float2* part, int C, int 
 static_assert(kDecideThreads == kSchedThreads, "the next round's schedule runs in a decide workgroup");
 
 template <int DT, int MODE, bool VEC, int NT>
-__global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
+// Four wavefronts per SIMD: a 1024-thread workgroup, or two 512-thread ones per
+// compute unit (every request resident at once with up to twice as many
+// requests as units), so at most 128 VGPRs.
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void verify_decide(VerifyArgs a) {
     const int nsplit = MODE == SPECV_SAMPLE ? a.nsplit : 1;
     if constexpr (NT == kSchedThreads) {
         if (a.has_next && int(blockIdx.x) == nsplit * a.R) {    // the next round's schedule, beside this round's decisions
@@ -777,6 +910,12 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
     __shared__ float4 st_s[SPECV_MAX_K + 1];
     __shared__ float mass_s[SAMPLE ? kMaxChunks : 1];
     __shared__ int trial_y_s[SAMPLE ? kResidualTrials : 1];
+    // counter-based uniforms, computed in phase 1: (u1, u2) of trial t at position i
+    // in tu_s[t * kTuStride + i] (trial 0's u1 is also the bonus draw's uniform),
+    // the acceptance uniform of row j in ua_s[j]
+    constexpr int kTuStride = SPECV_MAX_K + 1;
+    __shared__ float2 tu_s[SAMPLE ? kResidualTrials * kTuStride : 1];
+    __shared__ float ua_s[SAMPLE ? SPECV_MAX_K : 1];
     __shared__ int bad_s, nonfinite_s, stats_bad_s, rnext_s, last_s, win_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = int(blockIdx.x) / nsplit, part = int(blockIdx.x) % nsplit;
@@ -786,40 +925,108 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
     const int N = a.cu_rows[a.R];
     const int base = a.cu_rows[r];
     const int L = a.cu_rows[r + 1] - base;
+    // sampling: every row's chunk masses of p stay in LDS from phase 1 (as inclusive
+    // prefix sums in chunk order) when they fit
+    const bool keep_mass = L >= 0 && L <= k && (L + 1) * C <= kMaxChunks;
+    const bool gen = SAMPLE && !a.uniforms;        // the library's own uniforms
     int32_t* out = a.out_tokens + long(r) * (k + 1);
     if (tid == 0) {
         bad_s = L < 0 || L > k || base < 0 || base + L > N || N < 0 || N + r >= nrows;
         nonfinite_s = 0;
         stats_bad_s = 0;
         rnext_s = 0;
+        win_s = INT_MAX;
     }
     __syncthreads();
 
     if (!bad_s) {
+        // This wavefront's counter-based uniforms, one Philox block per lane: its
+        // trials t = wave, wave + kW, .. at every position 0..L, and the
+        // acceptance uniforms of its rows j = wave, wave + kW, .. < L. Computed
+        // while the partials are in flight; only this wavefront reads ua_s before
+        // the workgroup barrier.
+        auto philox_slots = [&]() {
+            if constexpr (SAMPLE) {
+                const int npos = L + 1;
+                const int nt = (kResidualTrials - 1 - wave) / kW + 1;
+                const int na = wave < L ? (L - 1 - wave) / kW + 1 : 0;
+                const int ntp = nt * npos, ns = ntp + na;
+                for (int s0 = 0; s0 < ns; s0 += kWave) {
+                    const int sl = s0 + lane;
+                    const bool trial = sl < ntp;
+                    const int t = wave + (sl / npos) * kW, i = sl % npos;
+                    const int j = wave + (sl - ntp) * kW;
+                    uint64_t w0 = uint64_t(trial ? i : j) + 1u, w1 = uint64_t(r);
+                    uint64_t w2 = trial ? kPurposeDraw : kPurposeAccept, w3 = trial ? uint64_t(t) : 0u;
+                    philox4x64_10(w0, w1, w2, w3, a.seed, a.step);
+                    const float u1 = float(uint32_t(w0 >> 40)) * 0x1p-24f;
+                    const float u2 = float(uint32_t(w1 >> 40)) * 0x1p-24f;
+                    if (trial) tu_s[t * kTuStride + i] = make_float2(u1, u2);
+                    else if (sl < ns) ua_s[j] = u1;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        };
+        bool slots_done = !gen;
         for (int j = wave; j <= L; j += kW) {
             const bool verified = j < L;
             const int t = verified ? base + j : N + r;
             // independent loads first: one round of latency with the partials
             const int tag_r = a.tags[2 * t], tag_j = a.tags[2 * t + 1];
             const int x = verified ? a.tokens[long(r) * k + j] : 0;
-            float uj = 0.f;
             RowRec rc{0.f, 0.f};
-            if (SAMPLE && verified) {
-                uj = a.uniforms ? a.uniforms[long(r) * (k + 1) + j] : philox_uniform(a.seed, a.step, kPurposeAccept, r, j);
-                rc = a.rec[t];
-            }
+            if (SAMPLE && verified) rc = a.rec[t];
             specv_draft_stat ds{};
             if (SAMPLE && verified && a.stats) ds = a.stats[long(r) * k + j];
             const bool row0 = a.pre0 && j == 0;       // streamed beside the schedule (spec_step)
             if (SAMPLE && verified && row0) rc.ax = a.ax0[r];
-            const float2 P = merge_partials<SAMPLE>(row0 ? a.part0 + long(r) * C : a.part_p + long(t) * C, C, lane);
+            const float2* pp = row0 ? a.part0 + long(r) * C : a.part_p + long(t) * C;
+            float2 pv[kMergePre], qv[kMergePre];
+            load_partials<SAMPLE>(pp, C, lane, pv);
+            if (SAMPLE && verified && !a.stats) load_partials<true>(a.part_q + long(t) * C, C, lane, qv);
+            if (!slots_done) {
+                philox_slots();
+                slots_done = true;
+            }
+            float uj = 0.f;
+            if (SAMPLE && verified) uj = a.uniforms ? a.uniforms[long(r) * (k + 1) + j] : ua_s[j];
+            const float2 P = reduce_partials<SAMPLE>(pp, C, lane, pv);
             float2 Q = make_float2(-INFINITY, 0.f);
             if (SAMPLE && verified) {
                 if (a.stats) {                     // q's state and q(x) from the draft head
                     Q = make_float2(ds.m, ds.z);
                     rc.bx = ds.x_logit;
                 } else {
-                    Q = merge_partials<true>(a.part_q + long(t) * C, C, lane);
+                    Q = reduce_partials<true>(a.part_q + long(t) * C, C, lane, qv);
+                }
+            }
+            if (SAMPLE && keep_mass) {
+                // the row's chunk masses of p relative to its max as inclusive prefix
+                // sums, for a draw from p at this row
+                float* mrow = mass_s + j * C;
+                float carry = 0.f;
+#pragma unroll
+                for (int u = 0; u < kMergePre; ++u) {
+                    if (u * kWave < C) {
+                        const int cc = lane + u * kWave;
+                        const float m = cc < C && pv[u].x != -INFINITY ? pv[u].y * exp2f(pv[u].x - P.x) : 0.f;
+                        const float inc = wave_incl_scan_f32(m) + carry;
+                        if (cc < C) mrow[cc] = inc;
+                        carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), 63));
+                    }
+                }
+                for (int c0 = kMergePre * kWave; c0 < C; c0 += kWave) {
+                    const int cc = c0 + lane;
+                    float m = 0.f;
+                    if (cc < C) {
+                        const float2 q = pp[cc];
+                        m = q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - P.x);
+                    }
+                    const float inc = wave_incl_scan_f32(m) + carry;
+                    if (cc < C) mrow[cc] = inc;
+                    carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), 63));
                 }
             }
             if (lane != 0) continue;               // lane 0 decides the row
@@ -858,6 +1065,7 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
             }
             keep_s[j] = keep;
         }
+        if (!slots_done) philox_slots();           // a wavefront without rows
     }
     __syncthreads();
     if (bad_s || nonfinite_s || stats_bad_s) {
@@ -901,24 +1109,33 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
             // result; with none kept the draw falls back to the residual's
             // inverse CDF (the re-read below) with the uniform of trial
             // kResidualTrials.
-            const float2* pp = (a.pre0 && acc == 0) ? a.part0 + long(r) * C : a.part_p + long(base + acc) * C;
-            for (int cc = tid; cc < C; cc += NT) {
-                const float2 q = pp[cc];
-                mass_s[cc] = q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
+            const float* pm = mass_s + (keep_mass ? acc * C : 0);
+            if (!keep_mass) {
+                const float2* pp = (a.pre0 && acc == 0) ? a.part0 + long(r) * C : a.part_p + long(base + acc) * C;
+                for (int cc = tid; cc < C; cc += NT) {
+                    const float2 q = pp[cc];
+                    mass_s[cc] = q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
+                }
+                __syncthreads();
             }
-            if (tid == 0) win_s = INT_MAX;
-            __syncthreads();
             for (int t = wave; t < kResidualTrials; t += kW) {
                 if (__hip_atomic_load(&win_s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < t) break;
-                float u1, u2;
-                philox_trial(a.seed, a.step, uint32_t(r), uint32_t(acc), uint32_t(t), u1, u2);
+                const float2 uu = tu_s[t * kTuStride + acc];
+                const float u2 = uu.y;
                 float cb, cth;
-                const int cs = wave_find_chunk(C, u1, [&](int cc) { return mass_s[cc]; }, cb, cth);
-                const int yy = chunk_pick<DT, VEC, false>(trow, nullptr, cs * CH, V, cb, cth, [&](float xt_, float) {
+                const int cs = keep_mass ? wave_find_chunk_prefix(C, uu.x, pm, cb, cth)
+                                         : wave_find_chunk(C, uu.x, [&](int cc) { return pm[cc]; }, cb, cth);
+                // the draft chunk rides along (q(y) without another round trip) in
+                // 1024-thread workgroups; 512-thread ones load q's logit after the
+                // pick (registers)
+                constexpr bool kPair = NT == kDecideThreads;
+                float2 xy;
+                const int yy = chunk_pick<DT, VEC, kPair>(trow, drow, cs * CH, V, cb, cth, [&](float xt_, float) {
                     return __builtin_amdgcn_exp2f(fmaf(xt_, c, -st.x));
-                });
-                const float py = exp2f(fmaf(RW::LT::load1(trow + yy), c, -st.x)) / st.y;
-                const float qy = exp2f(fmaf(RW::LT::load1(drow + yy), c, -st.z)) / st.w;
+                }, &xy);
+                if (!kPair) xy.y = RW::LT::load1(drow + yy);
+                const float py = exp2f(fmaf(xy.x, c, -st.x)) / st.y;
+                const float qy = exp2f(fmaf(xy.y, c, -st.z)) / st.w;
                 if (lane == 0 && py > 0.f && u2 < 1.f - qy / py) {
                     trial_y_s[t] = yy;
                     atomicMin(&win_s, t);
@@ -931,10 +1148,9 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
                     const int y = trial_y_s[win];
                     out[acc] = y;
                     // the bonus row's record: -(kept trial + 1), a_r, the token, the trial's first uniform
-                    float u1, u2;
-                    philox_trial(a.seed, a.step, uint32_t(r), uint32_t(acc), uint32_t(win), u1, u2);
                     if (a.diag)
-                        reinterpret_cast<float4*>(a.diag)[N + r] = make_float4(-float(win + 1), float(acc), float(y), u1);
+                        reinterpret_cast<float4*>(a.diag)[N + r] =
+                            make_float4(-float(win + 1), float(acc), float(y), tu_s[win * kTuStride + acc].x);
                 }
                 return;
             }
@@ -957,15 +1173,13 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
                 if (lane == 0) i = atomicAdd(&rnext_s, 1);
                 return lo + __builtin_amdgcn_readfirstlane(i);
             };
-            RW t0, d0;
             if constexpr (!VEC) {                  // scalar rows: one chunk at a time (registers)
                 for (int ch = grab(); ch < hi; ch = grab()) {
-                    issue(t0, d0, ch);
-                    const float m0 = chunk_residual_mass(t0, d0, ch * CH, V, lane, c, lp, lq);
+                    const float m0 = scalar_chunk_residual_mass<DT>(trow, drow, ch * CH, V, lane, c, lp, lq);
                     if (lane == 0) mass_s[ch] = m0;
                 }
             } else {
-                RW t1, d1;
+                RW t0, d0, t1, d1;
                 int c0 = grab();
                 if (c0 < hi) issue(t0, d0, c0);
                 while (c0 < hi) {
@@ -980,7 +1194,7 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
                     if (lane == 0) mass_s[c1] = m1;
                 }
             }
-        } else {
+        } else if (!keep_mass) {
             // bonus row: chunk masses of p relative to Mp, from the partials
             const float2* pp = (a.pre0 && L == 0) ? a.part0 + long(r) * C : a.part_p + long(N + r) * C;
             for (int cc = tid; cc < C; cc += NT) {
@@ -1020,7 +1234,7 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
             float u2;
             philox_trial(a.seed, a.step, uint32_t(r), uint32_t(acc), uint32_t(kResidualTrials), ub, u2);
         } else {
-            ub = philox_uniform(a.seed, a.step, kPurposeDraw, r, acc);
+            ub = tu_s[acc].x;                      // U(seed, step, 1, r, a_r): trial 0's first uniform
         }
         float total = 0.f;
         if (rejected)
@@ -1043,7 +1257,9 @@ __global__ __launch_bounds__(NT) void verify_decide(VerifyArgs a) {
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
-            const int cs = wave_find_chunk(C, ub, [&](int cc) { return mass_s[cc]; }, cbase, cthr);
+            const int cs = !rejected && keep_mass
+                               ? wave_find_chunk_prefix(C, ub, mass_s + L * C, cbase, cthr)
+                               : wave_find_chunk(C, ub, [&](int cc) { return mass_s[cc]; }, cbase, cthr);
             y = chunk_pick<DT, VEC, false>(trow, nullptr, cs * CH, V, cbase, cthr, [&](float xt_, float) {
                 return __builtin_amdgcn_exp2f(fmaf(xt_, c, -st.x));
             });
