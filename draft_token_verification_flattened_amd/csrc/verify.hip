@@ -907,7 +907,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
     constexpr int kW = NT / kWave;
     __shared__ int keep_s[SPECV_MAX_K + 1];
     __shared__ int g_s[SPECV_MAX_K + 1];
+    __shared__ int x_s[SPECV_MAX_K + 1];           // the draft tokens of the request's rows
     __shared__ float4 st_s[SPECV_MAX_K + 1];
+    __shared__ float4 prq_s[SAMPLE ? SPECV_MAX_K : 1];   // sampling: p(x), q(x), p(x)/q(x) per verified row
     __shared__ float mass_s[SAMPLE ? kMaxChunks : 1];
     __shared__ int trial_y_s[SAMPLE ? kResidualTrials : 1];
     // counter-based uniforms, computed in phase 1: (u1, u2) of trial t at position i
@@ -940,33 +942,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
     __syncthreads();
 
     if (!bad_s) {
-        // This wavefront's counter-based uniforms, one Philox block per lane: its
-        // trials t = wave, wave + kW, .. at every position 0..L, and the
-        // acceptance uniforms of its rows j = wave, wave + kW, .. < L. Computed
-        // while the partials are in flight; only this wavefront reads ua_s before
-        // the workgroup barrier.
+        // The counter-based uniforms, one Philox block per thread, counted from the
+        // workgroup's last thread (wavefronts without rows first): slot s < 16 (L+1)
+        // is trial s / (L+1) at position s % (L+1), the next L slots the acceptance
+        // uniforms of rows 0..L-1. Computed while the partials are in flight; read
+        // after the workgroup barrier.
         auto philox_slots = [&]() {
             if constexpr (SAMPLE) {
-                const int npos = L + 1;
-                const int nt = (kResidualTrials - 1 - wave) / kW + 1;
-                const int na = wave < L ? (L - 1 - wave) / kW + 1 : 0;
-                const int ntp = nt * npos, ns = ntp + na;
-                for (int s0 = 0; s0 < ns; s0 += kWave) {
-                    const int sl = s0 + lane;
+                const int npos = L + 1, ntp = kResidualTrials * npos, ns = ntp + L;
+                for (int sl = NT - 1 - tid; sl < ns; sl += NT) {
                     const bool trial = sl < ntp;
-                    const int t = wave + (sl / npos) * kW, i = sl % npos;
-                    const int j = wave + (sl - ntp) * kW;
+                    const int t = sl / npos, i = sl % npos, j = sl - ntp;
                     uint64_t w0 = uint64_t(trial ? i : j) + 1u, w1 = uint64_t(r);
                     uint64_t w2 = trial ? kPurposeDraw : kPurposeAccept, w3 = trial ? uint64_t(t) : 0u;
                     philox4x64_10(w0, w1, w2, w3, a.seed, a.step);
                     const float u1 = float(uint32_t(w0 >> 40)) * 0x1p-24f;
                     const float u2 = float(uint32_t(w1 >> 40)) * 0x1p-24f;
                     if (trial) tu_s[t * kTuStride + i] = make_float2(u1, u2);
-                    else if (sl < ns) ua_s[j] = u1;
+                    else ua_s[j] = u1;
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
         };
         bool slots_done = !gen;
@@ -986,12 +980,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
             float2 pv[kMergePre], qv[kMergePre];
             load_partials<SAMPLE>(pp, C, lane, pv);
             if (SAMPLE && verified && !a.stats) load_partials<true>(a.part_q + long(t) * C, C, lane, qv);
+            float uj = 0.f;
+            if (SAMPLE && verified && !gen) uj = a.uniforms[long(r) * (k + 1) + j];
             if (!slots_done) {
                 philox_slots();
                 slots_done = true;
             }
-            float uj = 0.f;
-            if (SAMPLE && verified) uj = a.uniforms ? a.uniforms[long(r) * (k + 1) + j] : ua_s[j];
             const float2 P = reduce_partials<SAMPLE>(pp, C, lane, pv);
             float2 Q = make_float2(-INFINITY, 0.f);
             if (SAMPLE && verified) {
@@ -1042,28 +1036,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
             if (nf) nonfinite_s = 1;
             const bool xok = x >= 0 && x < V;
             if (writer && verified && !xok) atomicOr(&a.hdr->status, SPECV_STATUS_BAD_TOKEN);
-            bool keep = false;
+            x_s[j] = x;
             if (!SAMPLE) {
                 const int gi = __float_as_int(P.y);
                 const int y = gi == INT_MAX ? 0 : gi;
-                keep = verified && x == y;
+                const bool keep = verified && x == y;
                 g_s[j] = y;
+                keep_s[j] = keep;
                 if (a.diag && writer)
                     reinterpret_cast<float4*>(a.diag)[t] =
                         make_float4(float(y), P.x, 0.f, verified ? (keep ? 1.f : 0.f) : -1.f);
             } else {
+                // the keep decision u < min(1, p(x) / q(x)) follows the barrier, when
+                // every row's uniform is there (a token outside [0, V): ratio 0, rejected)
                 st_s[j] = make_float4(P.x, P.y, Q.x, Q.y);
                 float px = 0.f, qx = 0.f, ratio = 0.f;
                 if (verified && xok) {
                     px = exp2f(fmaf(rc.ax, a.c, -P.x)) / P.y;
                     qx = exp2f(fmaf(rc.bx, a.c, -Q.x)) / Q.y;
                     ratio = qx > 0.f ? px / qx : INFINITY;
-                    keep = uj < fminf(1.f, ratio);
                 }
-                if (a.diag && writer && verified)
-                    reinterpret_cast<float4*>(a.diag)[t] = make_float4(px, qx, ratio, uj);
+                if (verified) {
+                    prq_s[j] = make_float4(px, qx, ratio, 0.f);
+                    if (!gen) ua_s[j] = uj;
+                }
             }
-            keep_s[j] = keep;
         }
         if (!slots_done) philox_slots();           // a wavefront without rows
     }
@@ -1080,16 +1077,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
         return;
     }
     int acc = L;
-    for (int j = 0; j < L; ++j)
-        if (!keep_s[j]) { acc = j; break; }
-    // the drawn token out[acc] (sampling) is written by the workgroup that draws it
-    if (writer && tid <= k && !(SAMPLE && tid == acc)) {
-        int v = -1;
-        if (tid < acc) v = a.tokens[long(r) * k + tid];
-        else if (tid == acc) v = g_s[acc];
-        out[tid] = v;
+    if constexpr (SAMPLE) {
+        // every wavefront decides the rows (lane j: row j) and finds a_r itself
+        const bool kp = lane < L ? ua_s[lane] < fminf(1.f, prq_s[lane].z) : true;
+        const uint64_t rej = __ballot(!kp);
+        acc = rej ? __builtin_ctzll(rej) : L;
+    } else {
+        for (int j = 0; j < L; ++j)
+            if (!keep_s[j]) { acc = j; break; }
     }
-    if (writer && tid == 0) a.acc_len[r] = acc;
+    // the request's results, by the last wavefront (the first ones start the draw):
+    // the accepted length, the kept tokens and -1 after the extra one (the drawn
+    // token out[acc] is written by the workgroup that draws it), the rows' records
+    if (writer && wave == kW - 1) {
+        if (lane <= k && !(SAMPLE && lane == acc)) out[lane] = lane < acc ? x_s[lane] : (lane == acc ? g_s[acc] : -1);
+        if (lane == 0) a.acc_len[r] = acc;
+        if (SAMPLE && a.diag && lane < L) {
+            const float4 q = prq_s[lane];
+            reinterpret_cast<float4*>(a.diag)[base + lane] = make_float4(q.x, q.y, q.z, ua_s[lane]);
+        }
+    }
     if constexpr (SAMPLE) {
         const float4 st = st_s[acc];
         const float c = a.c, lp = st.x + log2f(st.y), lq = st.z + log2f(st.w);
