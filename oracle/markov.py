@@ -58,10 +58,12 @@ def draw_position(dl_row: np.ndarray, dtype: str, mode: str, tau: float, u: np.n
 
 
 def draft_uniforms(u_draft, rng, R: int, k: int) -> np.ndarray:
-    """The head's sampling uniforms [R, k]: U(seed, step, 2, r, i) for
-    rng = (seed, step) (oracle.philox), else the given array."""
+    """The head's sampling uniforms [R, k]: U(seed, step, 2, r0 + r, i) for
+    rng = (seed, step) or (seed, step, r0) (oracle.philox; r0 addresses a slice
+    of a larger batch's requests), else the given array."""
     if rng is not None:
-        return philox.uniforms(rng[0], rng[1], philox.DRAFT, R, k)
+        seed, step, r0 = (tuple(rng) + (0,))[:3]
+        return philox.uniforms(seed, step, philox.DRAFT, R, k, r0)
     return np.asarray(u_draft, dtype=np.float64)
 
 

@@ -66,11 +66,11 @@ def trial_uniforms(seed: int, step: int, r: int, i: int, t: int):
     return float(w[0] >> 40) * 2.0 ** -24, float(w[1] >> 40) * 2.0 ** -24
 
 
-def uniforms(seed: int, step: int, purpose: int, R: int, n: int) -> np.ndarray:
-    """U(seed, step, purpose, r, i) for r < R, i < n: float64 [R, n] (every value
-    is a float32)."""
+def uniforms(seed: int, step: int, purpose: int, R: int, n: int, r0: int = 0) -> np.ndarray:
+    """U(seed, step, purpose, r0 + r, i) for r < R, i < n: float64 [R, n] (every
+    value is a float32). r0 addresses a slice of a larger batch's requests."""
     out = np.empty((R, n), dtype=np.float64)
     for r in range(R):
         for i in range(n):
-            out[r, i] = uniform(seed, step, purpose, r, i)
+            out[r, i] = uniform(seed, step, purpose, r0 + r, i)
     return out

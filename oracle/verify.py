@@ -204,7 +204,9 @@ def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
     generator (oracle.philox): U(seed, step, 0, r, j) keeps or rejects row j;
     the draw at a_r is the bonus draw with U(seed, step, 1, r, a_r) when every
     row was kept, else the residual's rejection draw with the trial uniforms
-    of (r, a_r) (residual_draw_rejection). Without rng, u_verify [R,k+1]
+    of (r, a_r) (residual_draw_rejection). rng = (seed, step, r0) addresses
+    the requests as r0 + r: a slice of a larger batch gets the uniforms the
+    whole batch would. Without rng, u_verify [R,k+1]
     gives them: column j < k keeps or rejects row j, column k drives an
     inverse-CDF draw (from the residual, or from p for the bonus row).
 
@@ -247,8 +249,8 @@ def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
     if mode != "sample":
         raise ValueError(mode)
     if rng is not None:
-        seed, step = rng
-        u_acc = philox.uniforms(seed, step, philox.ACCEPT, R, k)
+        seed, step, r0 = (tuple(rng) + (0,))[:3]
+        u_acc = philox.uniforms(seed, step, philox.ACCEPT, R, k, r0)
     else:
         u_acc = np.asarray(u_verify, dtype=np.float64)[:, :k]
     px = np.zeros((R, k), dtype=np.float64)
@@ -270,7 +272,7 @@ def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
         row_q[t] = q[n, xt]
     acc, a, ratio = decide(px, qx, u_acc, L)
     if rng is not None:
-        u_draw = np.array([philox.uniform(seed, step, philox.DRAW, r, int(a[r])) for r in range(R)])
+        u_draw = np.array([philox.uniform(seed, step, philox.DRAW, r0 + r, int(a[r])) for r in range(R)])
     else:
         u_draw = np.asarray(u_verify, dtype=np.float64)[:, k]
     # resample / bonus rows, recomputed one block at a time
@@ -301,9 +303,9 @@ def verify(mode: str, dtype: str, target: np.ndarray, draft, tokens: np.ndarray,
                 i_ = int(a[r_])
                 yy, tt, nn = residual_draw_rejection(
                     p[np.nonzero(rej)[0][n_]], q[n_],
-                    lambda t, r_=r_, i_=i_: philox.trial_uniforms(seed, step, int(r_), i_, t), near_eps=near_eps)
+                    lambda t, r_=r_, i_=i_: philox.trial_uniforms(seed, step, r0 + int(r_), i_, t), near_eps=near_eps)
                 y[r_], trial[r_], near[r_], by_trials[r_] = yy, tt, nn, True
-                u_draw[r_] = philox.trial_uniforms(seed, step, int(r_), i_, tt if tt >= 0 else RESIDUAL_TRIALS)[0]
+                u_draw[r_] = philox.trial_uniforms(seed, step, r0 + int(r_), i_, tt if tt >= 0 else RESIDUAL_TRIALS)[0]
     row_ratio = np.full(B, np.nan)
     row_acc = np.zeros(B, dtype=bool)
     row_ratio[vidx] = ratio[tags[vidx, 0], tags[vidx, 1]]

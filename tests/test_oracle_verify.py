@@ -294,3 +294,26 @@ def test_rng_chisquare_lossless(logit_model):
     counts = run_trials(logit_model, 60_000, k, seed=98,
                         verify_fn=lambda *a: via_rng(*a, reuse=True), batch=20_000, rows=True)
     assert chi2_pvalue(counts, pr) < 1e-9
+
+
+def test_rng_request_offset_addresses_a_slice():
+    """rng = (seed, step, r0): a slice of requests lo..hi verified on its own
+    gets exactly the whole batch's uniforms, decisions and tokens."""
+    g = np.random.Generator(np.random.Philox(77))
+    R, k, V = 9, 3, 40
+    tl = (2.0 * g.standard_normal((R, k + 1, V))).astype(np.float32)
+    dl = (tl[:, :k] + g.standard_normal((R, k, V))).astype(np.float32)
+    x = g.integers(0, V, size=(R, k))
+    L = g.integers(0, k + 1, size=R)
+    tags, cu = schedule.flatten(L)
+    whole = verify.verify("sample", "f32", tl, dl, x, tags, cu, 1.0, rng=(5, 2))
+    lo, hi = 3, 8
+    t2, c2 = schedule.flatten(L[lo:hi])
+    part = verify.verify("sample", "f32", tl[lo:hi], dl[lo:hi], x[lo:hi], t2, c2, 1.0, rng=(5, 2, lo))
+    assert np.array_equal(part["u_accept"], whole["u_accept"][lo:hi])
+    assert np.array_equal(part["u_draw"], whole["u_draw"][lo:hi])
+    assert np.array_equal(part["accepted_len"], whole["accepted_len"][lo:hi])
+    assert np.array_equal(part["out_tokens"], whole["out_tokens"][lo:hi])
+    # without the offset the slice would draw other numbers
+    other = verify.verify("sample", "f32", tl[lo:hi], dl[lo:hi], x[lo:hi], t2, c2, 1.0, rng=(5, 2))
+    assert not np.array_equal(other["u_accept"], whole["u_accept"][lo:hi])
