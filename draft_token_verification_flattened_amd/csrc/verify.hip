@@ -1211,8 +1211,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
         }
         __syncthreads();
         if (rejected && nsplit > 1) {
-            // exchange the parts' chunk masses: device-scope stores (written through),
-            // their completion, then one arrival; the last to arrive draws the token
+            // exchange the parts' chunk masses: device-scope stores, then one arrival
+            // per part, an acquire-release RMW at agent scope; the part that arrives
+            // last reads the others' masses and draws the token. A workgroup barrier
+            // orders the other wavefronts' stores at workgroup scope only (it does
+            // not wait for them to reach the device), so each wavefront first waits
+            // for its own stores to complete.
             float* gm = a.res_mass + long(r) * C;
             for (int cc = lo + tid; cc < hi; cc += NT)
                 __hip_atomic_store(gm + cc, mass_s[cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1220,11 +1224,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
             __builtin_amdgcn_s_waitcnt(0);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __syncthreads();
-            if (tid == 0) {
-                last_s = __hip_atomic_fetch_add(a.res_cnt + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            if (tid == 0)
+                last_s = __hip_atomic_fetch_add(a.res_cnt + r, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
                          nsplit - 1;
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            }
             __syncthreads();
             if (!last_s) return;
             for (int cc = tid; cc < C; cc += NT)
