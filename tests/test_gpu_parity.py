@@ -402,6 +402,32 @@ def test_philox_uniforms_bit_exact(seed, step):
                    rng=(seed, step))
 
 
+def test_philox_residual_fallback():
+    """Rows whose q is close to p (residual mass about 0.1) so that for some
+    requests all 16 rejection trials fail: the fallback, an inverse-CDF draw
+    from the residual with the first uniform of trial 16, against the oracle
+    over 40 steps (fp32 rows, V = 600); at least 8 fallbacks are seen."""
+    R, k, V = 16, 3, 600
+    g = np.random.Generator(np.random.Philox(5))
+    tl = (2.0 * g.standard_normal((R, k + 1, V))).astype(np.float32)
+    dl = (tl[:, :k] + 0.35 * g.standard_normal((R, k, V))).astype(np.float32)
+    x = g.integers(0, V, size=(R, k)).astype(np.int32)
+    L = np.full(R, k, np.int32)
+    tags, cu = osched.flatten(L)
+    N = int(cu[-1])
+    fallbacks = 0
+    say("philox residual fallback")
+    for step in range(40):
+        acc, out, diag, st = _gpu_verify(B.SAMPLE, tl, dl, x, None, L, 1.0, seed=11, step=step)
+        assert st == 0
+        ref = overify.verify("sample", "f32", tl, dl, x, tags, cu, 1.0, rng=(11, step), near_eps=overify.DRAW_EPS)
+        check_sampling(_Res(acc, out, diag), ref, tags, cu, f"fallback seed=11 step={step}", rng=(11, step))
+        bon = diag[N:N + R]
+        fallbacks += int(((acc < L) & (bon[:, 0] >= 0)).sum())
+    say("fallbacks", fallbacks)
+    assert fallbacks >= 8, fallbacks
+
+
 def test_verify_deterministic():
     d, ref, tags, cu = _run_verify("c2", "sample", -1, rng=(2, 5))
     a1, o1, g1 = d.host("acc_len"), d.host("out_tokens"), d.host("diag")
