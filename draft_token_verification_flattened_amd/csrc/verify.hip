@@ -1362,12 +1362,15 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
     // (each with at least a chunk per wavefront); with more requests than compute
     // units (and no next-round schedule in the launch, which needs 1024 threads)
     // the workgroups have 512 threads, two per compute unit, so that all are
-    // resident at once instead of running in two rounds.
+    // resident at once instead of running in two rounds. With counter-based
+    // uniforms the re-read is the rare fallback after the residual trials, which
+    // every workgroup of the request runs in full, so at most two share a request.
     const bool lagged = next && schedule_is_bucket(*next);
     const int threads = (!lagged && a.R > cus) ? kDecideHalf : kDecideThreads;
     a.nsplit = 1;
     if (threads == kDecideThreads) {
         a.nsplit = a.R * 4 <= cus ? 4 : (a.R * 2 <= cus ? 2 : 1);
+        if (!a.uniforms && a.nsplit > 2) a.nsplit = 2;
         while (a.nsplit > 1 && a.C < a.nsplit * (kDecideThreads / kWave)) a.nsplit /= 2;
     }
     SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
