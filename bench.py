@@ -33,8 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "verified draft tokens/s at V=151936, k=5, 256 req; achieved HBM GB/s % peak"
 HBM_PEAK = 8.0e12
 MFMA_BF16_PEAK = 2.5e15   # dense bf16 MFMA, MI355X
-DOMINANT = "verify_stream"
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_stream_c2_traffic.txt")
+DOMINANT = "verify_stream"              # spec_verify; spec_step's is verify_step_stream
 
 
 def parse():
@@ -76,7 +75,8 @@ def source_hash(files=("common.h", "verify.hip")) -> str:
 # Counter summaries (profiles/) per dominant kernel: the file, the sources its
 # kernel is built from, and the workload the counters were taken on.
 TRAFFIC = {
-    "verify_stream": (os.path.join(ROOT, "profiles", "verify_stream_c2_traffic.txt"), ("common.h", "verify.hip")),
+    "verify_step_stream": (os.path.join(ROOT, "profiles", "verify_step_stream_c2_traffic.txt"),
+                           ("common.h", "verify.hip")),
     "markov_logits": (os.path.join(ROOT, "profiles", "markov_logits_c4_traffic.txt"), ("common.h", "markov.hip")),
 }
 
@@ -88,6 +88,8 @@ def workload_key(args, max_len) -> str:
 def committed_traffic(kernel, wkey):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, if it was taken on the current kernel source and on this workload."""
+    if kernel not in TRAFFIC:
+        return None, None
     path, files = TRAFFIC[kernel]
     if not os.path.exists(path):
         return None, None
@@ -125,14 +127,10 @@ def algorithmic_bytes(w, mode, N, R, draft_rows=True):
 
 
 def verify_kernel_bytes(w, mode, N, R, draft_rows, fused):
-    """Algorithmic bytes per launch of the verification's streaming kernels.
-    fused (spec_step): verify_prefetch0 reads the target row (r, 0) of every
-    request beside the schedule, verify_stream the other rows."""
-    total = algorithmic_bytes(w, mode, N, R, draft_rows)
-    row0 = R * w.V * (2 if w.dtype == "bf16" else 4)
-    if fused:
-        return {"verify_prefetch0": row0, "verify_stream": total - row0}
-    return {"verify_stream": total}
+    """Algorithmic bytes per launch of the verification's streaming kernel:
+    verify_step_stream (spec_step: the schedule beside the target rows (r, 0),
+    then the other rows) or verify_stream (spec_verify)."""
+    return {("verify_step_stream" if fused else "verify_stream"): algorithmic_bytes(w, mode, N, R, draft_rows)}
 
 
 def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
@@ -156,7 +154,7 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
     B.timing_enable(False)
     ms_step = t0.elapsed_time(t1) / steps
     kern = {}
-    for name in ("rnn_state", "markov_logits", "markov_pick", "schedule", "verify_prefetch0", "verify_stream",
+    for name in ("rnn_state", "markov_logits", "markov_pick", "schedule", "verify_step_stream", "verify_stream",
                  "verify_decide"):
         n, tot = B.timing_read(name)
         if n:
@@ -181,23 +179,25 @@ def run_variant(d, w, mode_c, mode, max_len, steps, warmup, B, torch):
     N = int(L.sum())
     R = w.R
     draft_rows = d.stats_for(mode_c) is None
-    fused = "verify_prefetch0" in kern
+    fused = "verify_step_stream" in kern
+    dom_name = "verify_step_stream" if fused else DOMINANT
     nbytes = algorithmic_bytes(w, mode, N, R, draft_rows)
     per_kernel = verify_kernel_bytes(w, mode, N, R, draft_rows, fused)
-    dom = kern.get(DOMINANT)
-    achieved = per_kernel[DOMINANT] / (dom["avg_us"] * 1e-6) if dom else None
+    dom = kern.get(dom_name)
+    achieved = per_kernel[dom_name] / (dom["avg_us"] * 1e-6) if dom else None
     for name, nb in per_kernel.items():
         if name in kern:
             kern[name]["algorithmic_bytes"] = nb
             kern[name]["hbm_frac"] = nb / (kern[name]["avg_us"] * 1e-6) / HBM_PEAK
-    # the verification's time: its kernels (with spec_step, the first launch
+    # the verification's time: its kernels (with spec_step, the streaming launch
     # also holds the schedule, so the fraction is a lower bound)
     verify_us = sum(kern[k]["avg_us"] * kern[k]["launches_per_step"]
-                    for k in ("verify_prefetch0", "verify_stream", "verify_decide") if k in kern)
+                    for k in ("verify_step_stream", "verify_stream", "verify_decide") if k in kern)
     return dict(mode=mode, max_len=max_len, ms_per_step=ms_plain, ms_per_step_instrumented=ms_step, N=N,
                 rows=int(d.host("n_rows")[0]), tokens_per_s=N / (ms_plain * 1e-3), verify_us=verify_us,
                 verify_tokens_per_s=N / (verify_us * 1e-6) if verify_us else None,
-                algorithmic_bytes=nbytes, dominant_bytes=per_kernel[DOMINANT], fused_schedule=fused,
+                algorithmic_bytes=nbytes, dominant_kernel=dom_name, dominant_bytes=per_kernel[dom_name],
+                fused_schedule=fused,
                 draft_rows_read=draft_rows, dominant_gbps=achieved / 1e9 if achieved else None,
                 dominant_frac=achieved / HBM_PEAK if achieved else None, kernels=kern, step_us_percentiles=pct)
 
@@ -608,7 +608,8 @@ def main():
         lagged = run_lagged(d, w, mode_c, args.steps, args.warmup, B, torch, args.copies)
 
     kern = main_res["kernels"]
-    ver = kern.get("verify_stream", {})
+    dom_name = main_res["dominant_kernel"]
+    ver = kern.get(dom_name, {})
     mk = kern.get("markov_logits")
     roofline = {
         "bound": "hbm",
@@ -616,8 +617,8 @@ def main():
         "peak": HBM_PEAK / 1e9,
         "unit": "GB/s",
         "frac": main_res["dominant_frac"],
-        "traffic": committed_traffic("verify_stream", workload_key(args, max_len))[0],
-        "kernel": "verify_stream",
+        "traffic": committed_traffic(dom_name, workload_key(args, max_len))[0],
+        "kernel": dom_name,
         "avg_launch_us": ver.get("avg_us"),
         "algorithmic_bytes_per_launch": main_res["dominant_bytes"],
     }
@@ -666,7 +667,7 @@ def main():
                         "hbm_frac": (main_res["algorithmic_bytes"] / (main_res["verify_us"] * 1e-6) / HBM_PEAK
                                      if main_res["verify_us"] else None),
                         "algorithmic_bytes": main_res["algorithmic_bytes"],
-                        "kernels": [k for k in ("verify_prefetch0", "verify_stream", "verify_decide")
+                        "kernels": [k for k in ("verify_step_stream", "verify_stream", "verify_decide")
                                     if k in main_res["kernels"]]},
         "kernels": main_res["kernels"],
         "ms_per_step_instrumented": main_res["ms_per_step_instrumented"],

@@ -23,6 +23,7 @@ OK, EINVAL, EUNSUPPORTED, EDEVICE = 0, -1, -2, -3
 BF16, F32 = 0, 1
 GREEDY, SAMPLE = 0, 1
 STATUS_BAD_TOKEN, STATUS_BAD_TAG, STATUS_BAD_PAGE, STATUS_NONFINITE, STATUS_BAD_STATS = 1, 2, 4, 8, 16
+STATUS_LATE_SCHEDULE = 32
 DRAFT_STAT_WORDS = 8        # specv_draft_stat: m, z, x_logit, c (float), token, 3 pad (int32)
 MAX_K, MAX_SCHED_ITEMS = 32, 16384
 KV_POSITION_MAJOR, KV_HEAD_MAJOR = 0, 1

@@ -50,6 +50,27 @@ __device__ __forceinline__ double throughput(int bt, const int* tb, const double
     return tt[lo] + (tt[hi] - tt[lo]) * frac;
 }
 
+// throughput() at increasing bt: `lo` (start at -1) keeps the segment of the
+// previous call, so that only the first in-table lookup searches.
+__device__ __forceinline__ double throughput_next(int bt, const int* tb, const double* tt, int n, int& lo) {
+#pragma clang fp contract(off)
+    if (bt < tb[0]) return (tt[0] * double(bt)) / double(tb[0]);
+    if (bt >= tb[n - 1]) return tt[n - 1];
+    if (lo < 0) {
+        int l = 0, h = n - 1;               // tb[l] <= bt < tb[h]
+        while (h - l > 1) {
+            const int mid = (l + h) >> 1;
+            if (tb[mid] <= bt) l = mid; else h = mid;
+        }
+        lo = l;
+    } else {
+        while (tb[lo + 1] <= bt) ++lo;      // bt < tb[n - 1]: stops at n - 2 at most
+    }
+    const int hi = lo + 1;
+    const double frac = double(bt - tb[lo]) / double(tb[hi] - tb[lo]);
+    return tt[lo] + (tt[hi] - tt[lo]) * frac;
+}
+
 // Block-wide exclusive scan of one 64-bit value per thread; returns the total too.
 __device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* sh, uint64_t& total) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -179,6 +200,64 @@ __device__ __forceinline__ void flatten_block(const SchedArgs& a, int r0, int r1
     }
 }
 
+// flatten_block for a single workgroup with LDS to spare: each request marks
+// its rows in `rowmap` (N + R entries: request << 6 | position), then one
+// thread per flattened row writes its tag, so that a wavefront's tag stores
+// cover one contiguous range (8 bytes per row when the tags are 8-byte aligned).
+// The batch is written with device-scope atomic stores, which the memory keeps
+// coherent across the chip's L2 caches without a cache write-back: spec_step's
+// streaming workgroups read it while this workgroup's kernel still runs.
+__device__ __forceinline__ void store_dev(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename F>
+__device__ __forceinline__ void flatten_rows_lds(const SchedArgs& a, int r0, int r1, F len_of, int* sh,
+                                                 int* rowmap) {
+    constexpr int kKeep = 4;                    // lengths kept in registers; more are recomputed
+    int Lk[kKeep];
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < kKeep; ++q) {
+        Lk[q] = r0 + q < r1 ? len_of(r0 + q) : 0;
+        local += Lk[q];
+    }
+    for (int r = r0 + kKeep; r < r1; ++r) local += len_of(r);
+    int N;
+    int off = block_exclusive_scan_i32(local, sh, N);
+    for (int r = r0; r < r1; ++r) {
+        int L = 0;
+#pragma unroll
+        for (int q = 0; q < kKeep; ++q)
+            if (r == r0 + q) L = Lk[q];
+        if (r >= r0 + kKeep) L = len_of(r);
+        store_dev(a.cu_rows + r, off);
+        if (a.len_out) a.len_out[r] = L;
+        for (int j = 0; j < L; ++j) rowmap[off + j] = (r << 6) | j;
+        rowmap[N + r] = (r << 6) | L;
+        off += L;
+    }
+    if (threadIdx.x == 0) {
+        store_dev(a.cu_rows + a.R, N);
+        store_dev(a.n_rows, N + a.R);
+    }
+    __syncthreads();
+    const int rows = N + a.R;
+    if ((reinterpret_cast<uintptr_t>(a.tags) & 7u) == 0) {
+        uint64_t* t2 = reinterpret_cast<uint64_t*>(a.tags);     // (request, position): request in the low word
+        for (int t = threadIdx.x; t < rows; t += blockDim.x) {
+            const int v = rowmap[t];
+            __hip_atomic_store(t2 + t, (uint64_t(uint32_t(v & 63)) << 32) | uint32_t(v >> 6), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        for (int t = threadIdx.x; t < rows; t += blockDim.x) {
+            const int v = rowmap[t];
+            store_dev(a.tags + 2 * t, v >> 6);
+            store_dev(a.tags + 2 * t + 1, v & 63);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // schedule_bucket: the same schedule from one workgroup, for R * k <= 4096.
 // The keys are sorted by a bucket pass on their leading bits (bucket order is
@@ -247,8 +326,12 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
     const int per = (n + nt - 1) / nt;
     const int p0 = min(n, tid * per), p1 = min(n, p0 + per);
     double thr[kPosPer];
+    {
+        int seg = -1;
 #pragma unroll
-    for (int q = 0; q < kPosPer; ++q) thr[q] = p0 + q < p1 ? throughput(R + p0 + q + 1, tb, tt, a.n_tbl) : 0.0;
+        for (int q = 0; q < kPosPer; ++q)
+            thr[q] = p0 + q < p1 ? throughput_next(R + p0 + q + 1, tb, tt, a.n_tbl, seg) : 0.0;
+    }
 
     // 2. survival (running products in position order) and keys, in place;
     //    positions >= kk get a key above every real one
@@ -311,9 +394,18 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
         lo += int(q & 0xffffu);
         hi += int(q >> 16);
     }
-    int tlo, thi;
-    const int elo = block_exclusive_scan_i32(lo, sh, tlo);
-    const int ehi = block_exclusive_scan_i32(hi, sh2, thi);
+    // both exclusive scans at once; sh and sh2 are not written again before the
+    // barrier that follows the gains
+    int elo, ehi;
+    {
+        const int ilo = wave_incl_scan_i32(lo), ihi = wave_incl_scan_i32(hi);
+        if (lane == 63) { sh[wave] = ilo; sh2[wave] = ihi; }
+        __syncthreads();
+        int blo = 0, bhi = 0;
+        for (int q = 0; q < wave; ++q) { blo += sh[q]; bhi += sh2[q]; }
+        elo = blo + ilo - lo;
+        ehi = bhi + ihi - hi;
+    }
     uint64_t P = (uint64_t(uint32_t(ehi)) << 16) + uint64_t(uint32_t(elo));
     double g = -1.0;                                          // below every gain
     int m = INT_MAX;
@@ -355,7 +447,8 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
     };
     const int rper = (R + nt - 1) / nt;
     const int r0 = min(R, tid * rper), r1 = min(R, r0 + rper);
-    flatten_block(a, r0, r1, len_of, sh);
+    // grouped keys are no longer needed: their space holds the row map
+    flatten_rows_lds(a, r0, r1, len_of, sh, reinterpret_cast<int*>(grp));
 }
 
 __host__ __device__ inline size_t schedule_bucket_lds(int R, int k, int kk) {

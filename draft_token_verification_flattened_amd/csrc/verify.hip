@@ -12,7 +12,11 @@
 // the bonus rows, request r's at N + r. N = cu_rows[R]; n_rows = N + R.
 //
 // Kernels, in stream order:
-//   verify_stream    the HBM stream. Work item = one chunk of 64 * kNV 16-byte
+//   verify_stream    (spec_verify; under spec_step verify_step_stream, which
+//                    runs this round's schedule in its workgroup 0 and streams
+//                    the rows (r, 0) in the others meanwhile, then streams the
+//                    batch like verify_stream in all of them)
+//                    the HBM stream. Work item = one chunk of 64 * kNV 16-byte
 //                    vectors of one logit row. Items: the target chunks of all
 //                    rows, then (sampling) the draft chunks of the verified rows,
 //                    so every item costs the same. Wavefront w of the persistent
@@ -42,8 +46,11 @@
 //                    the inverse CDF. With every row kept it draws the bonus
 //                    token from p of the bonus row (chunk masses from the
 //                    partials).
+#include <atomic>
+#include <chrono>
 #include <climits>
 #include <mutex>
+#include <random>
 
 #include "common.h"
 #include "host.h"
@@ -91,14 +98,16 @@ struct VerifyArgs {
     int nsplit;                             // sampling: decide workgroups per request (1, 2 or 4)
     SchedArgs next;                         // the next round's schedule (spec_verify_ex)
     int has_next;                           // 1: verify_decide runs `next` as workgroup R
-    int pre0;                               // 1: target row (r, 0) of every request was streamed by
-                                            //    verify_prefetch0 into part0 / ax0 (spec_step)
+    int pre0;                               // 1: target row (r, 0) of every request was streamed
+                                            //    beside the schedule into part0 / ax0 (spec_step)
     float2* part0;                          // [R * C] target chunk partials of row (r, 0)
     float* ax0;                             // [R] target logit at draft token (r, 0)
+    uint64_t* flag;                         // spec_step: [0] the schedule's completion mark, [1] a late waiter's
+    uint64_t token;                         // spec_step: this call's mark (unique per call, never 0)
 };
 
 struct Layout {
-    size_t part_p, part_q, rec, res_mass, res_cnt, part0, ax0, total;
+    size_t part_p, part_q, rec, res_mass, res_cnt, part0, ax0, flag, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -115,6 +124,7 @@ static Layout ws_layout(int R, int k, int V) {
     l.res_cnt = off; off = align256(off + size_t(R) * sizeof(int));
     l.part0 = off;   off = align256(off + size_t(R) * C * sizeof(float2));
     l.ax0 = off;     off = align256(off + size_t(R) * sizeof(float));
+    l.flag = off;    off = align256(off + 2 * sizeof(uint64_t));
     l.total = off;
     return l;
 }
@@ -256,22 +266,61 @@ __device__ __forceinline__ float2 chunk_argmax(const float (&x)[E], int beg, int
 // so a wavefront that the compute unit serves faster simply takes more items
 // and all of them finish together. Each wavefront loads its next item while it
 // reduces the current one.
+//
+// The slot descriptions and results of a phase live in LDS (StreamLds, carved
+// from one byte range): verify_stream declares it, verify_step_stream reuses
+// the schedule's dynamic LDS for it.
+struct StreamLds {
+    uint64_t* d_row;         // row pointer
+    float2* st_p;            // the items' partials, written out after the phase
+    int* d_t;                // flattened row
+    int* d_cf;               // chunk << 2 | draft << 1 | ok
+    int* d_tok;              // the row's draft token (sampling, verified rows), or -1
+    float* st_x;             // logit at the draft token, if the item holds it
+    int* sh;                 // [64] scan scratch
+    int* next_item;          // the phase's item counter
+    unsigned char* st_f;     // 1: st_x holds the item's value
+};
+constexpr size_t kStreamLdsBytes = size_t(kPhaseSlots) * (8 + 8 + 4 + 4 + 4 + 4 + 1) + 64 * 4 + 16;
+
+__device__ __forceinline__ StreamLds stream_lds_at(unsigned char* p) {
+    StreamLds l;
+    l.d_row = reinterpret_cast<uint64_t*>(p);
+    l.st_p = reinterpret_cast<float2*>(p + 8 * kPhaseSlots);
+    l.d_t = reinterpret_cast<int*>(p + 16 * kPhaseSlots);
+    l.d_cf = reinterpret_cast<int*>(p + 20 * kPhaseSlots);
+    l.d_tok = reinterpret_cast<int*>(p + 24 * kPhaseSlots);
+    l.st_x = reinterpret_cast<float*>(p + 28 * kPhaseSlots);
+    l.sh = reinterpret_cast<int*>(p + 32 * kPhaseSlots);
+    l.next_item = reinterpret_cast<int*>(p + 32 * kPhaseSlots + 64 * 4);
+    l.st_f = p + 32 * kPhaseSlots + 64 * 4 + 16;
+    return l;
+}
+
+// The batch (tags, cu_rows, n_rows) is read with device-scope atomic loads:
+// under spec_step it is written by another workgroup of the same launch
+// (device-scope atomic stores), and such loads see it without invalidating
+// any cache.
+__device__ __forceinline__ int load_dev(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int DT, int MODE, bool VEC>
-__global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
+__device__ __forceinline__ void stream_slots(const VerifyArgs& a, const StreamLds& lds) {
     using RW = Raw<DT, VEC>;
     using T = typename RW::T;
     constexpr int E = RW::kE;
     constexpr int GW = RW::kVec;
     constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
-    __shared__ uint64_t d_row[kPhaseSlots];
-    __shared__ int d_t[kPhaseSlots];                 // flattened row
-    __shared__ int d_cf[kPhaseSlots];                // chunk << 2 | draft << 1 | ok
-    __shared__ int d_tok[kPhaseSlots];               // the row's draft token (sampling, verified rows), or -1
-    __shared__ float2 st_p[kPhaseSlots];             // the items' partials, written out after the phase
-    __shared__ float st_x[kPhaseSlots];              // logit at the draft token, if the item holds it
-    __shared__ unsigned char st_f[kPhaseSlots];
-    __shared__ int sh[64];
-    __shared__ int next_item;
+    uint64_t* const d_row = lds.d_row;
+    int* const d_t = lds.d_t;
+    int* const d_cf = lds.d_cf;
+    int* const d_tok = lds.d_tok;
+    float2* const st_p = lds.st_p;
+    float* const st_x = lds.st_x;
+    unsigned char* const st_f = lds.st_f;
+    int* const sh = lds.sh;
+    int& next_item = *lds.next_item;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const uint32_t G = gridDim.x, b = blockIdx.x;
     if (b == 0 && tid == 0) a.hdr->status = 0u;
@@ -302,11 +351,11 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
             sl[h] = b + (p0 + i) * G;
             const uint32_t rel = sl[h] >= region ? sl[h] - region : sl[h];
             const int t = int(rel / uint32_t(C));                       // t < Bmax
-            tg[h] = make_int2(a.tags[2 * t], a.tags[2 * t + 1]);
+            tg[h] = make_int2(load_dev(a.tags + 2 * t), load_dev(a.tags + 2 * t + 1));
         }
         // all values at one point: the loads are issued ahead of it and waited for once
         // (otherwise the compiler waits for n_rows first and sinks each tag load into its branch)
-        int nr = *a.n_rows, nv = a.cu_rows[a.R];
+        int nr = load_dev(a.n_rows), nv = load_dev(a.cu_rows + a.R);
         asm volatile("" : "+v"(nr), "+v"(nv) : "v"(tg[0].x), "v"(tg[0].y), "v"(tg[1].x), "v"(tg[1].y),
                      "v"(tg[2].x), "v"(tg[2].y));
         const int nrows = min(max(nr, 0), a.Bmax);
@@ -469,36 +518,48 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
     }
 }
 
+template <int DT, int MODE, bool VEC>
+__global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
+    __shared__ __align__(16) unsigned char lds[kStreamLdsBytes];
+    stream_slots<DT, MODE, VEC>(a, stream_lds_at(lds));
+}
+
 // ---------------------------------------------------------------------------
-// verify_prefetch0 (spec_step)
+// verify_step_stream (spec_step)
 // ---------------------------------------------------------------------------
 
-// spec_step's first launch, one workgroup per compute unit. Workgroup 0 runs
-// this round's schedule (the single-workgroup bucket schedule, `a.next`), a
-// latency-bound job that keeps one compute unit busy for ~10 us. The others
-// meanwhile stream the target row (r, 0) of every request, which the batch
-// holds whatever lengths the schedule picks (verified row 0 when L_r > 0, the
-// bonus row when L_r = 0), into part0 (and ax0, the logit at draft token
-// (r, 0)); verify_stream then skips those rows. Work items are (request,
-// chunk) pairs, taken grid-stride by the streaming wavefronts in batches of at
-// most kPreBatch (one fewer in sampling mode; scalar rows: one item at a time,
-// so that no registers spill). A wavefront has only a few items (about five at 256
-// requests), so the loads go through a ring of kPreRing buffers: the first
-// kPreRing are issued at once, and each later one as soon as a buffer is free.
-// Every batch size is its own unrolled instance, so the compiler counts the
-// loads in flight exactly. The batch's results are stored after its last load.
-constexpr int kPreBatch = 5;
-constexpr int kPreRing = 3;          // 16-byte loads; scalar rows (kE floats per buffer) use one buffer
+// spec_step's streaming launch, one workgroup per compute unit. Workgroup 0
+// runs this round's schedule (the single-workgroup bucket schedule, `a.next`),
+// a latency-bound job that keeps one compute unit busy for ~10 us, and
+// publishes its completion. The others meanwhile stream the target row (r, 0)
+// of every request, which the batch holds whatever lengths the schedule picks
+// (verified row 0 when L_r > 0, the bonus row when L_r = 0), into part0 (and
+// ax0, the logit at draft token (r, 0)). Then every workgroup, the schedule's
+// included, streams its slots of the batch's other rows as verify_stream
+// does; the others start once the schedule is published, which it normally is
+// by the time their rows (r, 0) are done. One launch instead of two: the grid
+// does not drain between the rows (r, 0) and the rest.
+//
+// Rows (r, 0): work items are (request, chunk) pairs, taken grid-stride by the
+// streaming wavefronts in batches of at most kRow0Batch (scalar rows: one item
+// at a time, so that no registers spill). A
+// wavefront has only a few items (about five at 256 requests), so the loads go
+// through a ring of kRow0Ring buffers: the first kRow0Ring are issued at once,
+// and each later one as soon as a buffer is free. Every batch size is its own
+// unrolled instance, so the compiler counts the loads in flight exactly. The
+// batch's results are stored after its last load.
+constexpr int kRow0Batch = 3;        // (more spill registers beside the stream's code)
+constexpr int kRow0Ring = 3;         // 16-byte loads; scalar rows (kE floats per buffer) use one buffer
 
 template <int DT, int MODE, bool VEC, int NB>
-__device__ __forceinline__ void prefetch0_batch(const VerifyArgs& a, uint32_t i0, uint32_t nw, int lane) {
+__device__ __forceinline__ void row0_batch(const VerifyArgs& a, uint32_t i0, uint32_t nw, int lane) {
     using RW = Raw<DT, VEC>;
     using T = typename RW::T;
     constexpr int E = RW::kE;
     constexpr int GW = RW::kVec;
     constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
     const int C = a.C, CH = a.CH, V = a.V, K = a.k;
-    constexpr int kRing = VEC ? kPreRing : 1;
+    constexpr int kRing = VEC ? kRow0Ring : 1;
     int xt[NB];
     // the draft tokens of the batch's rows first: a small load issued after
     // the chunk loads would make its wait drain them
@@ -548,37 +609,67 @@ __device__ __forceinline__ void prefetch0_batch(const VerifyArgs& a, uint32_t i0
     }
 }
 
+// Streaming wavefront gw of nw: the (request, chunk) items of the rows (r, 0).
 template <int DT, int MODE, bool VEC>
-__global__ __launch_bounds__(kStreamThreads) void verify_prefetch0(VerifyArgs a) {
-    if (blockIdx.x == 0) {
-        extern __shared__ __align__(16) uint64_t sched_lds[];
-        schedule_bucket_body(a.next, sched_lds);
-        return;
-    }
-    constexpr int kWaves = kStreamThreads / kWave;
+__device__ __forceinline__ void row0_items(const VerifyArgs& a, uint32_t gw, uint32_t nw) {
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t nw = (gridDim.x - 1) * kWaves;
-    const uint32_t gw = (blockIdx.x - 1) * kWaves + (threadIdx.x >> 6);
     const uint32_t items = uint32_t(a.R) * uint32_t(a.C);
     if constexpr (!VEC) {                 // scalar rows: one item at a time (registers)
-        for (uint32_t i0 = gw; i0 < items; i0 += nw) prefetch0_batch<DT, MODE, VEC, 1>(a, i0, nw, lane);
+        for (uint32_t i0 = gw; i0 < items; i0 += nw) row0_batch<DT, MODE, VEC, 1>(a, i0, nw, lane);
         return;
     }
-    // sampling keeps the draft token's logit per item too: one item fewer per batch (registers)
-    constexpr int kB = MODE == SPECV_SAMPLE ? kPreBatch - 1 : kPreBatch;
-    static_assert(kPreBatch == 5, "one case per batch size");
-    for (uint32_t i0 = gw; i0 < items; i0 += kB * nw) {
-        const int nb = int(min(uint32_t(kB), (items - 1 - i0) / nw + 1));   // items of this batch
+    static_assert(kRow0Batch == 3, "one case per batch size");
+    for (uint32_t i0 = gw; i0 < items; i0 += kRow0Batch * nw) {
+        const int nb = int(min(uint32_t(kRow0Batch), (items - 1 - i0) / nw + 1));   // items of this batch
         switch (nb) {
-            case 1: prefetch0_batch<DT, MODE, VEC, 1>(a, i0, nw, lane); break;
-            case 2: prefetch0_batch<DT, MODE, VEC, 2>(a, i0, nw, lane); break;
-            case 3: prefetch0_batch<DT, MODE, VEC, 3>(a, i0, nw, lane); break;
-            case 4: prefetch0_batch<DT, MODE, VEC, 4>(a, i0, nw, lane); break;
-            default:
-                if constexpr (kB >= 5) prefetch0_batch<DT, MODE, VEC, 5>(a, i0, nw, lane);
-                break;
+            case 1: row0_batch<DT, MODE, VEC, 1>(a, i0, nw, lane); break;
+            case 2: row0_batch<DT, MODE, VEC, 2>(a, i0, nw, lane); break;
+            default: row0_batch<DT, MODE, VEC, 3>(a, i0, nw, lane); break;
         }
     }
+}
+
+// The wait for the schedule gives up after this long (100 MHz clock ticks):
+// only a workgroup 0 kept off the device by other work can take that long.
+constexpr uint64_t kScheduleWaitTicks = 100000000ull;    // one second
+
+template <int DT, int MODE, bool VEC>
+__global__ __launch_bounds__(kStreamThreads) void verify_step_stream(VerifyArgs a) {
+    extern __shared__ __align__(16) uint64_t step_lds[];
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0) {
+        schedule_bucket_body(a.next, step_lds);
+        // publish the batch. Its tags, offsets and row count went out as
+        // device-scope atomic stores (coherent across the L2 caches without a
+        // write-back, which would take microseconds under the stream's load);
+        // each wavefront waits for its own to complete (a workgroup barrier
+        // alone orders them at workgroup scope only), then the mark follows
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(a.flag, a.token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();                                  // the stream reuses the schedule's LDS
+    } else {
+        constexpr uint32_t kWaves = kStreamThreads / kWave;
+        row0_items<DT, MODE, VEC>(a, (blockIdx.x - 1) * kWaves + (threadIdx.x >> 6), (gridDim.x - 1) * kWaves);
+        // one thread waits for the mark; the stream reads the batch with
+        // device-scope atomic loads (no cache invalidation, which would stall the
+        // streaming compute units around), after the barrier
+        if (tid == 0) {
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            while (__hip_atomic_load(a.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.token) {
+                __builtin_amdgcn_s_sleep(2);
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kScheduleWaitTicks) {
+                    // reported by verify_decide; the stream goes on with what the batch holds
+                    __hip_atomic_store(a.flag + 1, a.token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    stream_slots<DT, MODE, VEC>(a, stream_lds_at(reinterpret_cast<unsigned char*>(step_lds)));
 }
 
 // ---------------------------------------------------------------------------
@@ -932,6 +1023,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
     const bool keep_mass = L >= 0 && L <= k && (L + 1) * C <= kMaxChunks;
     const bool gen = SAMPLE && !a.uniforms;        // the library's own uniforms
     int32_t* out = a.out_tokens + long(r) * (k + 1);
+    if (a.pre0 && blockIdx.x == 0 && tid == 0) {
+        // spec_step: a streaming workgroup that gave up waiting for the schedule
+        // voids the call; the mark is cleared for the next call (a replayed graph
+        // repeats this call's mark)
+        if (a.flag[1] == a.token) atomicOr(&a.hdr->status, SPECV_STATUS_LATE_SCHEDULE);
+        a.flag[0] = 0;
+    }
     if (tid == 0) {
         bad_s = L < 0 || L > k || base < 0 || base + L > N || N < 0 || N + r >= nrows;
         nonfinite_s = 0;
@@ -1324,17 +1422,31 @@ static int launch_decide(K kernel, int threads, VerifyArgs& a, const SchedArgs* 
     return SPECV_OK;
 }
 
-// spec_step's first launch: this round's schedule in workgroup 0, the rows
-// (r, 0) in the others (verify_prefetch0).
+// spec_step's schedule mark: unique per call in this process (a counter from a
+// random start) and never 0, so that neither an earlier call's mark nor
+// whatever a new workspace holds passes for this call's.
+static uint64_t call_token() {
+    static std::atomic<uint64_t> next{[] {
+        std::random_device rd;
+        return ((uint64_t(rd()) << 32) | rd()) ^ uint64_t(std::chrono::steady_clock::now().time_since_epoch().count());
+    }()};
+    uint64_t t = 0;
+    while (t == 0) t = next.fetch_add(1, std::memory_order_relaxed);
+    return t;
+}
+
+// spec_step's streaming launch (verify_step_stream): this round's schedule in
+// workgroup 0, the rows (r, 0) in the others, then the batch's other rows in all.
 template <class K>
-static int launch_prefetch0(K kernel, VerifyArgs& a, const SchedArgs& first, int cus, hipStream_t s) {
+static int launch_step_stream(K kernel, VerifyArgs& a, const SchedArgs& first, int cus, hipStream_t s) {
     a.next = first;
     a.pre0 = 1;
-    const size_t lds = schedule_bucket_lds(first.R, first.k, first.kk);
+    a.token = call_token();
+    const size_t lds = std::max(schedule_bucket_lds(first.R, first.k, first.kk), kStreamLdsBytes);
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                             int(lds)) != hipSuccess)
         return fail(SPECV_EDEVICE, "spec_step: cannot reserve %zu bytes of LDS", lds);
-    SPECV_LAUNCH("verify_prefetch0", kernel, std::max(2, cus), kStreamThreads, lds, s, a);
+    SPECV_LAUNCH("verify_step_stream", kernel, std::max(2, cus), kStreamThreads, lds, s, a);
     return SPECV_OK;
 }
 
@@ -1343,20 +1455,17 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
                          const SchedArgs* first = nullptr) {
     int cus = 0;
     if (int e = device_cus(cus)) return e;
-    if (first) {
-        if (int e = mode == SPECV_GREEDY ? launch_prefetch0(verify_prefetch0<DT, SPECV_GREEDY, VEC>, a, *first, cus, s)
-                                         : launch_prefetch0(verify_prefetch0<DT, SPECV_SAMPLE, VEC>, a, *first, cus, s))
-            return e;
-    }
     int G = 0;
     if (mode == SPECV_GREEDY) {
-        auto ks = verify_stream<DT, SPECV_GREEDY, VEC>;
-        if (int e = stream_grid(ks, long(a.Bmax) * a.C, cus, G)) return e;
-        SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
+        if (first) {
+            if (int e = launch_step_stream(verify_step_stream<DT, SPECV_GREEDY, VEC>, a, *first, cus, s)) return e;
+        } else {
+            auto ks = verify_stream<DT, SPECV_GREEDY, VEC>;
+            if (int e = stream_grid(ks, long(a.Bmax) * a.C, cus, G)) return e;
+            SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
+        }
         return launch_decide(verify_decide<DT, SPECV_GREEDY, VEC, kDecideThreads>, kDecideThreads, a, next, s);
     }
-    auto ks = verify_stream<DT, SPECV_SAMPLE, VEC>;
-    if (int e = stream_grid(ks, (a.stats ? 1L : 2L) * a.Bmax * a.C, cus, G)) return e;
     // One 1024-thread decide workgroup fits per compute unit. With fewer requests
     // than compute units a rejected row pair is re-read by up to four of them
     // (each with at least a chunk per wavefront); with more requests than compute
@@ -1373,7 +1482,13 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
         if (!a.uniforms && a.nsplit > 2) a.nsplit = 2;
         while (a.nsplit > 1 && a.C < a.nsplit * (kDecideThreads / kWave)) a.nsplit /= 2;
     }
-    SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
+    if (first) {
+        if (int e = launch_step_stream(verify_step_stream<DT, SPECV_SAMPLE, VEC>, a, *first, cus, s)) return e;
+    } else {
+        auto ks = verify_stream<DT, SPECV_SAMPLE, VEC>;
+        if (int e = stream_grid(ks, (a.stats ? 1L : 2L) * a.Bmax * a.C, cus, G)) return e;
+        SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
+    }
     if (threads == kDecideThreads)
         return launch_decide(verify_decide<DT, SPECV_SAMPLE, VEC, kDecideThreads>, threads, a, next, s);
     return launch_decide(verify_decide<DT, SPECV_SAMPLE, VEC, kDecideHalf>, threads, a, next, s);
@@ -1456,6 +1571,8 @@ static int verify_prepare(int mode, int dtype, int R, int k, int V, const void* 
     a.res_cnt = reinterpret_cast<int*>(w + lay.res_cnt);
     a.part0 = reinterpret_cast<float2*>(w + lay.part0);
     a.ax0 = reinterpret_cast<float*>(w + lay.ax0);
+    a.flag = reinterpret_cast<uint64_t*>(w + lay.flag);
+    a.token = 0;
     a.pre0 = 0;
     a.nsplit = 1;
     a.has_next = 0;

@@ -140,7 +140,7 @@ class DeviceStep:
     def schedule_verify(self, mode, max_len=None, diag=False, stream=None, z=None):
         """This round's schedule (from the confidence logits z, default the
         workload's), then its verification, in one spec_step call (the schedule
-        beside the stream of the rows (r, 0))."""
+        beside the stream of the rows (r, 0), in the same launch)."""
         max_len = self.w.k if max_len is None else max_len
         job = B.schedule_job(self.z if z is None else z, self.T, self.tbl_b, self.tbl_t, max_len, self.lengths, self.tags, self.cu_rows,
                              self.n_rows, self.ws_sched, self.survival)

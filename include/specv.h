@@ -79,8 +79,11 @@ enum {
                                     context length that is negative or overruns its page-table row */
     SPECV_STATUS_NONFINITE = 8u, /* a logit row with a NaN or +inf value (sampling: also a row
                                     of -inf only, which has no distribution) */
-    SPECV_STATUS_BAD_STATS = 16u /* spec_verify_ex: a draft statistic made at another temperature
-                                    or for another token than the one verified */
+    SPECV_STATUS_BAD_STATS = 16u, /* spec_verify_ex: a draft statistic made at another temperature
+                                     or for another token than the one verified */
+    SPECV_STATUS_LATE_SCHEDULE = 32u /* spec_step: the verification pass stopped waiting for the
+                                        schedule (one second; only other work holding the device
+                                        can delay it so long): every result of the call is void */
 };
 
 /* The draft head's statistics of one draft row (r, i), written by markov_draft
@@ -328,13 +331,19 @@ int spec_verify_ex(int mode, int dtype, int R, int k, int V, const void* target_
  * spec_verify of the batch it writes (its tags_out, cu_rows_out, n_rows_out),
  * with the same results bit for bit: the synchronous step of [P2] 3.2 and
  * [P3] "DSpark的神奇之处" (schedule from the current confidences, then verify).
- * When the schedule fits one workgroup (R * k <= 4096, max_len >= 1) it runs
- * in the first launch, on one compute unit, while the others stream every
- * request's target row (r, 0): the batch holds that row whatever lengths the
- * schedule picks (verified row 0, or the bonus row when L_r = 0). The
- * verification pass then streams the other rows, so the latency-bound
- * schedule hides behind reads the step needs anyway. Otherwise the two run
- * one after the other.
+ * When the schedule fits one workgroup (R * k <= 4096, max_len >= 1), one
+ * launch holds both the schedule and the verification pass: the schedule runs
+ * on one compute unit while the others stream every request's target row
+ * (r, 0), which the batch holds whatever lengths the schedule picks (verified
+ * row 0, or the bonus row when L_r = 0); the schedule writes the batch with
+ * device-scope atomic stores and then a completion mark unique to the call,
+ * and the other workgroups, once the mark is there, stream the batch's other
+ * rows. The latency-bound schedule hides behind reads the step needs anyway,
+ * and the grid does not drain between the two. A streaming workgroup that
+ * waits a second for the mark (only other work holding the device can delay
+ * the schedule so long) goes on and sets SPECV_STATUS_LATE_SCHEDULE: the
+ * call's results are then void. Otherwise the schedule and the verification
+ * run one after the other.
  * Arguments: sched as spec_verify_ex's `next` (a host pointer; device
  *   pointers inside; its workspace separate from `ws`); the others as
  *   spec_verify_ex, with R and k taken from sched.

@@ -65,11 +65,11 @@ def test_workload_configs_match_the_recipes():
 
 
 def test_verify_kernel_bytes_split():
-    # spec_step: the rows (r, 0) go to the first launch, the rest to the stream
+    # spec_step: one streaming launch reads every row, the rows (r, 0) included
     w = types.SimpleNamespace(V=151936, dtype="bf16")
     per = bench.verify_kernel_bytes(w, "sample", 512, 256, True, True)
-    assert per["verify_prefetch0"] == 2 * 151936 * 256
-    assert per["verify_prefetch0"] + per["verify_stream"] == bench.algorithmic_bytes(w, "sample", 512, 256)
+    assert per == {"verify_step_stream": 2 * 151936 * (2 * 512 + 256)}
+    assert per["verify_step_stream"] == bench.algorithmic_bytes(w, "sample", 512, 256)
     assert bench.verify_kernel_bytes(w, "greedy", 512, 256, True, False) == {
         "verify_stream": 2 * 151936 * (512 + 256)}
     # the draft head's statistics: no draft rows

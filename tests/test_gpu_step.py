@@ -75,6 +75,59 @@ def test_spec_step_equals_schedule_then_verify(name, mode, max_len):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("mode", ["sample", "greedy"])
+def test_spec_step_any_workspace_contents_and_graph_replays(mode):
+    """The streaming launch waits for the schedule's completion mark, which is
+    unique per call: a workspace full of arbitrary bytes gives the same results,
+    and so does every replay of a captured spec_step (each call's decisions
+    clear the mark for the next one), with eager work between the replays."""
+    w = W("c2")
+    d = DeviceStep(w, rng=True)
+    mc = B.SAMPLE if mode == "sample" else B.GREEDY
+    d.step_no = 5
+    say("spec_step eager", mode)
+    _clear(d)
+    d.schedule_verify(mc, diag=True)
+    torch.cuda.synchronize()
+    assert B.read_status(d.ws_verify) == 0
+    ref = _outputs(d)
+    for fill in (0xFF, None):
+        say("spec_step on a workspace of", "0xff bytes" if fill is not None else "random bytes")
+        if fill is None:
+            g = torch.Generator(device="cpu").manual_seed(3)
+            d.ws_verify.copy_(torch.randint(0, 256, d.ws_verify.shape, generator=g, dtype=torch.uint8))
+        else:
+            d.ws_verify.fill_(fill)
+        _clear(d)
+        d.schedule_verify(mc, diag=True)
+        torch.cuda.synchronize()
+        assert B.read_status(d.ws_verify) == 0
+        got = _outputs(d)
+        for key in NAMES:
+            assert np.array_equal(got[key], ref[key]), key
+    say("spec_step graph capture", mode)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            d.schedule_verify(mc, diag=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _clear(d)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say("replay", rep)
+        assert B.read_status(d.ws_verify) == 0
+        got = _outputs(d)
+        for key in NAMES:
+            assert np.array_equal(got[key], ref[key]), (rep, key)
+    del graph, d
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("R,k,V,dtype", [(1, 5, 151936, "bf16"), (7, 3, 1001, "bf16"), (40, 6, 5000, "f32"),
                                          (1024, 8, 256, "bf16")])
 def test_spec_step_small_and_beyond_one_workgroup(R, k, V, dtype):
