@@ -307,7 +307,8 @@ def run_lagged(d, w, mode_c, steps, warmup, B, torch, copies):
 def run_sweep(args, B, torch):
     """Load sweep: for R = 1, 2, 4, ..., 512 requests of the c2 recipe (the
     first R requests of one R = 512 draw, so every R sees the same requests),
-    8 rounds of drifting confidences, each a synchronous schedule-then-verify.
+    8 rounds of drifting confidences, each a synchronous schedule-then-verify
+    (spec_step, with the library's counter-based uniforms).
     Per R: mean verified length per request, mean step time, verified draft
     tokens/s and expected emitted tokens/s (R + survival over the verified
     drafts, per unit measured step time)."""
@@ -323,7 +324,7 @@ def run_sweep(args, B, torch):
         w = dataclasses.replace(full, R=R, conf_logit=cut(full.conf_logit), target=cut(full.target),
                                 draft=cut(full.draft), tokens_sample=cut(full.tokens_sample),
                                 tokens_greedy=cut(full.tokens_greedy), u_verify=cut(full.u_verify))
-        d = DeviceStep(w)
+        d = DeviceStep(w, rng=True)
         z = to_device(workloads.conf_rounds(w, rounds), "cuda")
         k = w.k
         Ls, Ss = [], []
@@ -335,9 +336,8 @@ def run_sweep(args, B, torch):
             Ss.append(d.host("survival").copy())
 
         def step(t):
-            B.spec_schedule(z[t % rounds], d.T, d.tbl_b, d.tbl_t, k, d.lengths, d.tags, d.cu_rows, d.n_rows,
-                            d.ws_sched, d.survival)
-            d.verify(B.SAMPLE, diag=False)
+            d.step_no += 1
+            d.schedule_verify(B.SAMPLE, z=z[t % rounds])
         for t in range(args.warmup):
             step(t)
         torch.cuda.synchronize()
