@@ -244,12 +244,15 @@ __device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
 // element's; the chunk totals select the chunk, an in-order scan of its
 // elements selects the index. When rounding leaves no crossing, the last index
 // with positive weight (in the last chunk with mass) is returned.
+// With c0 > 0 the search covers chunks [c0, C) only, its running sum starting
+// at carry0 (the mass before chunk c0; -inf: no crossing, the last positive
+// weight of those chunks).
 template <class ChunkMass, class Weight>
 __device__ int inv_cdf_pick(int C, int V, int chunk_len, float thr, ChunkMass chunk_mass, Weight weight,
-                            int lane) {
-    float carry = 0.f, base = 0.f;
+                            int lane, int c0 = 0, float carry0 = 0.f) {
+    float carry = carry0, base = 0.f;
     int sel = -1, last_pos = -1;
-    for (int ch0 = 0; ch0 < C && sel < 0; ch0 += kWave) {
+    for (int ch0 = c0; ch0 < C && sel < 0; ch0 += kWave) {
         const int ch = ch0 + lane;
         const float mch = ch < C ? chunk_mass(ch) : 0.f;
         const float inc = wave_inclusive_scan(mch, lane) + carry;

@@ -15,11 +15,16 @@
 //       epilogue adds the backbone logits, rounds to bf16 (nearest-even),
 //       stores the draft logits and emits per-(request, slice) softmax or
 //       argmax partials of the rounded values.
+//   markov_logits_run (bf16, d_m = 256)  the persistent projection (below); it
+//       also leaves each request's partial merged over each contiguous range of
+//       slices.
 //   markov_logits_fma (fp32)   the same with one lane per output and plain FMA.
-//   markov_pick_wg             one workgroup per request: merges the partials;
-//       greedy argmax, or the two-level inverse-CDF draw over softmax(dl / tau)
-//       (markov_pick, one wavefront per request, for rows of more than 4096
-//       slices).
+//   markov_pick_ranges         after markov_logits_run: one wavefront per
+//       request, the draw in three levels (range, slice, entry).
+//   markov_pick_wg             otherwise one workgroup per request: merges the
+//       partials; greedy argmax, or the two-level inverse-CDF draw over
+//       softmax(dl / tau) (markov_pick, one wavefront per request, for rows of
+//       more than 4096 slices).
 //
 // rnn_draft: the RNN head, the pages' other sequential module, which carries
 // the whole prefix of the block in a recurrent state (same sections). Read as
@@ -55,6 +60,8 @@ struct MarkovArgs {
     void* dl;                       // [R,k,V]
     specv_draft_stat* stats;        // [R,k] or NULL (sampling): the rows' softmax states for verification
     float2* part;                   // [R * S]
+    float2* part_rng;               // [R * nr] the projection's merged partial per (request, slice range)
+    int nr;                         // slice ranges (markov_logits_run's grid)
     WsHeader* hdr;
 };
 
@@ -336,8 +343,9 @@ __global__ __launch_bounds__(256) void markov_logits_mfma(MarkovArgs a) {
 
 // bf16, d_m = 32 * KS (256 at KS = 8): a persistent grid of 1024-thread
 // workgroups, one per compute unit. Workgroup (range, group) owns the 64-entry
-// vocabulary slices range, range + nr, range + 2 nr, ... (so the grid sweeps
-// each request's row as one dense window) and a group of 256 requests; the
+// vocabulary slices [range S / nr, (range + 1) S / nr) and a group of 256
+// requests (it also leaves each request's partial merged over its slices, in
+// vocabulary order, for the pick's first level); the
 // groups of one range are launched on the same XCD (blockIdx modulo 8), so the
 // second group's reads of P find the first group's in that XCD's L2. Each
 // wavefront keeps its 16 requests' operand rows in registers for the whole
@@ -397,10 +405,8 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int range = (idx / ng) * 8 + xcd, grp = idx % ng;
     const int S = a.S, V = a.V;
-    // slices range, range + nr, range + 2 nr, ...: at any moment the grid works on
-    // one dense window of each request's row
-    if (range >= S) return;
-    const int s_last = range + (S - 1 - range) / nr * nr;
+    // a contiguous run of slices [s_first, s_last]
+    const int s_first = int(long(range) * S / nr), s_last = int(long(range + 1) * S / nr) - 1;
 
     // Every load in the slice loop is issued on every path (addresses clamped
     // into the tensors), so the compiler's count of outstanding memory
@@ -478,22 +484,35 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
         }
     };
 
+    if (s_first > s_last) {
+        // a range without slices (a row of fewer slices than ranges): empty partials, no loads
+#pragma unroll
+        for (int b = 0; b < kRunKB; ++b)
+            if (g == 0 && mok[b]) {
+                const Part e = part_empty(a.mode);
+                a.part_rng[long(mreq[b]) * nr + range] = make_float2(e.a, e.b);
+            }
+        return;
+    }
     u32x4 pr[PT];
-    load_p(pr, range);
+    load_p(pr, s_first);
     store_p(pr, 0);
-    load_p(pr, min(range + nr, s_last));
+    load_p(pr, min(s_first + 1, s_last));
     // backbone values one slice ahead, in two buffers whose roles alternate
     // with the slice (as the two LDS buffers of P do); the loop below is
     // unrolled twice so that every role is fixed at compile time: a rotation
     // by register moves would make each slice wait for every load in flight,
     // the next P slice included
     u32x4 bkA[kRunKB][2], bkB[kRunKB][2];
-    load_bk(bkA, range);
+    load_bk(bkA, s_first);
+    Part run[kRunKB];
+#pragma unroll
+    for (int b = 0; b < kRunKB; ++b) run[b] = part_empty(a.mode);
     __syncthreads();
 
     // one slice: cur holds slice s's backbone values, ahead receives slice s + 1's
     auto slice = [&](int s, int lb, const u32x4 (&cur)[kRunKB][2], u32x4 (&ahead)[kRunKB][2]) {
-        load_bk(ahead, min(s + nr, s_last));
+        load_bk(ahead, min(s + 1, s_last));
         f32x4 acc[4][kRunKB];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
@@ -584,20 +603,25 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
                 part_merge(a.mode, pp, q);
             }
             if (g == 0 && mok[b]) a.part[part_at(mreq[b], s, S)] = make_float2(pp.a, pp.b);
+            part_merge(a.mode, run[b], pp);
         }
         // the slice after next: the other buffer was last read before the previous barrier
         store_p(pr, lb ^ 1);
-        load_p(pr, min(s + 2 * nr, s_last));
+        load_p(pr, min(s + 2, s_last));
         __syncthreads();
     };
 
-    for (int s = range; s <= s_last;) {
+    for (int s = s_first; s <= s_last;) {
         slice(s, 0, bkA, bkB);
-        s += nr;
+        s += 1;
         if (s > s_last) break;
         slice(s, 1, bkB, bkA);
-        s += nr;
+        s += 1;
     }
+    // the requests' partials merged over this workgroup's slices
+#pragma unroll
+    for (int b = 0; b < kRunKB; ++b)
+        if (g == 0 && mok[b]) a.part_rng[long(mreq[b]) * nr + range] = make_float2(run[b].a, run[b].b);
 }
 
 // ---------------------------------------------------------------------------
@@ -712,6 +736,97 @@ __global__ __launch_bounds__(256) void markov_pick(MarkovArgs a) {
             a.stats[long(m) * a.k + a.pos] = specv_draft_stat{M, tot.b, LT::load1(row + y), c, y, {0, 0, 0}};
     }
     if (lane == 0) a.tokens[long(m) * a.k + a.pos] = y;
+}
+
+// The draw from markov_logits_run's range partials, one wavefront per request,
+// in three levels, each in vocabulary order: the request's nr range partials
+// (one contiguous record; range p covers slices [p S / nr, (p + 1) S / nr))
+// give the row's state (M, Z) and the first range where the running mass
+// exceeds u Z; that range's slice partials give the slice; the slice's 64
+// logits give the token. When rounding leaves no crossing at a level, the
+// last range, slice or entry with positive weight is taken. Greedy: the merged
+// (max, first index) of the range partials is the token.
+constexpr int kRangePer = 4;                 // range partials per lane: nr <= 256
+static_assert(kRangePer * kWave >= 256, "run_grid makes at most 256 ranges");
+
+template <int DT>
+__global__ __launch_bounds__(256) void markov_pick_ranges(MarkovArgs a) {
+    using LT = Logit<DT>;
+    using T = typename LT::T;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= a.R) return;
+    if (a.pos == 0 && lane == 0 && (a.prev[m] < 0 || a.prev[m] >= a.V)) set_status(a.hdr, SPECV_STATUS_BAD_TOKEN);
+    const int nr = a.nr, S = a.S;
+    const float2* pr = a.part_rng + long(m) * nr;
+    // lane holds ranges [lane kRangePer, lane kRangePer + kRangePer)
+    float2 q[kRangePer];
+    Part tot = part_empty(a.mode);
+#pragma unroll
+    for (int i = 0; i < kRangePer; ++i) {
+        const int rr = lane * kRangePer + i;
+        q[i] = rr < nr ? pr[rr] : make_float2(-INFINITY, a.mode == SPECV_GREEDY ? __int_as_float(INT_MAX) : 0.f);
+        Part p;
+        p.a = q[i].x;
+        p.b = q[i].y;
+        if (rr < nr) part_merge(a.mode, tot, p);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        Part p;
+        p.a = __shfl_xor(tot.a, o, 64);
+        p.b = __shfl_xor(tot.b, o, 64);
+        part_merge(a.mode, tot, p);
+    }
+    if (lane == 0 && part_nonfinite(a.mode, tot.a, tot.b)) set_status(a.hdr, SPECV_STATUS_NONFINITE);
+    if (a.mode == SPECV_GREEDY) {
+        if (lane == 0) a.tokens[long(m) * a.k + a.pos] = __float_as_int(tot.b);
+        return;
+    }
+    const float M = tot.a;
+    const float thr = draft_uniform(a, m) * tot.b;
+    // level 1: the range
+    float w[kRangePer], lsum = 0.f;
+    int lastpos = -1;
+#pragma unroll
+    for (int i = 0; i < kRangePer; ++i) {
+        const int rr = lane * kRangePer + i;
+        w[i] = (rr < nr && q[i].x != -INFINITY) ? q[i].y * exp2f(q[i].x - M) : 0.f;
+        lsum += w[i];
+        if (w[i] > 0.f) lastpos = rr;
+    }
+    const float incl = wave_inclusive_scan(lsum, lane);
+    float cum = incl - lsum, base = 0.f;
+    int hit = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < kRangePer; ++i) {
+        const float prev = cum;
+        cum += w[i];
+        if (hit == INT_MAX && lane * kRangePer + i < nr && cum > thr) {
+            hit = lane * kRangePer + i;
+            base = prev;
+        }
+    }
+    int rsel = wave_min_int(hit);
+    if (rsel != INT_MAX) {
+        base = __shfl(base, rsel / kRangePer, kWave);
+    } else {                                  // no crossing: the last range with mass
+        rsel = max(0, -wave_min_int(-lastpos));
+        base = -INFINITY;
+    }
+    // levels 2 and 3: the slice inside the range, then the entry
+    const int s0 = int(long(rsel) * S / nr), s1 = int(long(rsel + 1) * S / nr);
+    const float2* ps = a.part + part_at(m, 0, S);        // slice s at ps[kPartBlock * s]
+    const T* row = static_cast<const T*>(a.dl) + (long(m) * a.k + a.pos) * long(a.V);
+    const float c = a.c;
+    const int y = inv_cdf_pick(
+        s1, a.V, kSlice, thr,
+        [&](int s) { const float2 p = ps[kPartBlock * s]; return p.x == -INFINITY ? 0.f : p.y * exp2f(p.x - M); },
+        [&](int e) { return exp2f(fmaf(LT::load1(row + e), c, -M)); }, lane, s0, base);
+    if (lane == 0) {
+        a.tokens[long(m) * a.k + a.pos] = y;
+        if (a.stats) a.stats[long(m) * a.k + a.pos] = specv_draft_stat{M, tot.b, LT::load1(row + y), c, y, {0, 0, 0}};
+    }
 }
 
 // The same draw by one 256-thread workgroup per request, for rows of at most
@@ -865,6 +980,7 @@ size_t head_workspace_bytes(int R, int k, int V, int d_m, bool state) {
     const size_t S = (size_t(V) + kSlice - 1) / kSlice;
     const size_t Rb = (size_t(R) + kPartBlock - 1) / kPartBlock * kPartBlock;     // part_at's blocks
     size_t n = 256 + ((Rb * S * sizeof(float2) + 255) & ~size_t(255));
+    n += (size_t(R) * 256 * sizeof(float2) + 255) & ~size_t(255);          // range partials (nr <= 256)
     if (state) n += (size_t(R) * k * d_m * sizeof(float) + 255) & ~size_t(255);
     return n;
 }
@@ -908,6 +1024,10 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
     a.stats = mode == SPECV_SAMPLE ? stats_out : nullptr;
     a.hdr = static_cast<WsHeader*>(ws);
     a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + 256);
+    {
+        const size_t S = size_t(a.S), Rb = (size_t(R) + kPartBlock - 1) / kPartBlock * kPartBlock;
+        a.part_rng = reinterpret_cast<float2*>(static_cast<char*>(ws) + 256 + ((Rb * S * sizeof(float2) + 255) & ~size_t(255)));
+    }
     a.rec = rec;
     a.state = nullptr;
     if (rnn)
@@ -927,6 +1047,7 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
     }
     int run_ng = 1, run_nr = 8;
     run_grid(R, a.S, run_ng, run_nr);
+    a.nr = run_nr;
     const bool pick_wg = a.S <= kPickThreads * kPickPer;   // else one wavefront per request
     // The status word is cleared by position 0's logits kernel (which sets no
     // bits) and set by position 0's pick kernel, which checks prev_token.
@@ -945,7 +1066,9 @@ int head_draft(const char* fn, int mode, int dtype, int R, int k, int V, int d_m
                 SPECV_LAUNCH("markov_logits", markov_logits_mfma<true>, a.S, 256, lds, s, a);
             else
                 SPECV_LAUNCH("markov_logits", markov_logits_mfma<false>, a.S, 256, lds, s, a);
-            if (pick_wg)
+            if (d_m == 256)                      // markov_logits_run left range partials
+                SPECV_LAUNCH("markov_pick", markov_pick_ranges<SPECV_BF16>, (R + 3) / 4, 256, 0, s, a);
+            else if (pick_wg)
                 SPECV_LAUNCH("markov_pick", markov_pick_wg<SPECV_BF16>, pick_grid(R), kPickThreads, 0, s, a);
             else
                 SPECV_LAUNCH("markov_pick", markov_pick<SPECV_BF16>, (R + 3) / 4, 256, 0, s, a);
