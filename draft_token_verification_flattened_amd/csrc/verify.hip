@@ -1230,15 +1230,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
                 float cb, cth;
                 const int cs = keep_mass ? wave_find_chunk_prefix(C, uu.x, pm, cb, cth)
                                          : wave_find_chunk(C, uu.x, [&](int cc) { return pm[cc]; }, cb, cth);
-                // the draft chunk rides along (q(y) without another round trip) in
-                // 1024-thread workgroups; 512-thread ones load q's logit after the
-                // pick (registers)
-                constexpr bool kPair = NT == kDecideThreads;
+                // only the target chunk is loaded, q's logit at y after the pick:
+                // the draft chunk along with it (no second round trip) doubled the
+                // round's burst of loads (16 pairs of 8 KiB per rejecting request at
+                // once), 0.7 us slower at 256 requests
                 float2 xy;
-                const int yy = chunk_pick<DT, VEC, kPair>(trow, drow, cs * CH, V, cb, cth, [&](float xt_, float) {
+                const int yy = chunk_pick<DT, VEC, false>(trow, drow, cs * CH, V, cb, cth, [&](float xt_, float) {
                     return __builtin_amdgcn_exp2f(fmaf(xt_, c, -st.x));
                 }, &xy);
-                if (!kPair) xy.y = RW::LT::load1(drow + yy);
+                xy.y = RW::LT::load1(drow + yy);
                 const float py = exp2f(fmaf(xy.x, c, -st.x)) / st.y;
                 const float qy = exp2f(fmaf(xy.y, c, -st.z)) / st.w;
                 if (lane == 0 && py > 0.f && u2 < 1.f - qy / py) {
