@@ -333,23 +333,37 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
             thr[q] = p0 + q < p1 ? throughput_next(R + p0 + q + 1, tb, tt, a.n_tbl, seg) : 0.0;
     }
 
-    // 2. survival (running products in position order) and keys, in place;
-    //    positions >= kk get a key above every real one
+    // 2. survival: the running products in position order, one thread per
+    //    request doing only the chain (its sigmoids read eight at a time) and
+    //    writing each product over its sigmoid; then every thread turns its
+    //    (request, position) elements into keys and bucket counts and stores the
+    //    survival (contiguous). Positions >= kk get a key above every real one.
+    constexpr int kSgBatch = 8;
     for (int r = tid; r < R; r += nt) {
         double S = 1.0;
-        for (int i = 0; i < k; ++i) {
-            const int e = r * k + i;
-            if (i < kc) {
-                S = S * sg[e];
-                if (surv) a.survival[long(r) * k + i] = S;
-            }
-            uint64_t key = ~0ull;
-            if (i < kk) {
-                key = make_key(quantise(S), i, r);
-                atomicAdd(&cnt[bucket_of(key)], 1);
-            }
-            keys[e] = key;
+        for (int i0 = 0; i0 < kc; i0 += kSgBatch) {
+            double sv[kSgBatch];
+#pragma unroll
+            for (int q = 0; q < kSgBatch; ++q) sv[q] = i0 + q < kc ? sg[r * k + i0 + q] : 1.0;
+#pragma unroll
+            for (int q = 0; q < kSgBatch; ++q)
+                if (i0 + q < kc) {
+                    S = S * sv[q];
+                    sg[r * k + i0 + q] = S;
+                }
         }
+    }
+    __syncthreads();
+    for (int e = tid; e < Rk; e += nt) {
+        const int r = e / k, i = e - r * k;
+        const double S = i < kc ? sg[e] : 0.0;
+        if (surv && i < kc) a.survival[e] = S;
+        uint64_t key = ~0ull;
+        if (i < kk) {
+            key = make_key(quantise(S), i, r);
+            atomicAdd(&cnt[bucket_of(key)], 1);
+        }
+        keys[e] = key;                         // over the product just read
     }
     __syncthreads();
 
