@@ -200,10 +200,11 @@ __device__ __forceinline__ void flatten_block(const SchedArgs& a, int r0, int r1
     }
 }
 
-// flatten_block for a single workgroup with LDS to spare: each request marks
-// its rows in `rowmap` (N + R entries: request << 6 | position), then one
-// thread per flattened row writes its tag, so that a wavefront's tag stores
-// cover one contiguous range (8 bytes per row when the tags are 8-byte aligned).
+// flatten_block for the bucket scheduler's single workgroup of kSchedThreads
+// threads, with LDS to spare: each request marks its rows in `rowmap` (N + R
+// entries: request << 6 | position), then one thread per flattened row writes
+// its tag, so that a wavefront's tag stores cover one contiguous range (8 bytes
+// per row when the tags are 8-byte aligned).
 // The batch is written with device-scope atomic stores, which the memory keeps
 // coherent across the chip's L2 caches without a cache write-back: spec_step's
 // streaming workgroups read it while this workgroup's kernel still runs.
@@ -223,7 +224,7 @@ __device__ __forceinline__ void flatten_rows_lds(const SchedArgs& a, int r0, int
     }
     for (int r = r0 + kKeep; r < r1; ++r) local += len_of(r);
     int N;
-    int off = block_exclusive_scan_i32(local, sh, N);
+    int off = block_exclusive_scan_i32(local, sh, N, kSchedThreads / 64);
     for (int r = r0; r < r1; ++r) {
         int L = 0;
 #pragma unroll
@@ -244,13 +245,13 @@ __device__ __forceinline__ void flatten_rows_lds(const SchedArgs& a, int r0, int
     const int rows = N + a.R;
     if ((reinterpret_cast<uintptr_t>(a.tags) & 7u) == 0) {
         uint64_t* t2 = reinterpret_cast<uint64_t*>(a.tags);     // (request, position): request in the low word
-        for (int t = threadIdx.x; t < rows; t += blockDim.x) {
+        for (int t = threadIdx.x; t < rows; t += kSchedThreads) {
             const int v = rowmap[t];
             __hip_atomic_store(t2 + t, (uint64_t(uint32_t(v & 63)) << 32) | uint32_t(v >> 6), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     } else {
-        for (int t = threadIdx.x; t < rows; t += blockDim.x) {
+        for (int t = threadIdx.x; t < rows; t += kSchedThreads) {
             const int v = rowmap[t];
             store_dev(a.tags + 2 * t, v >> 6);
             store_dev(a.tags + 2 * t + 1, v & 63);
@@ -299,8 +300,9 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
     __shared__ int wm_sh[kSchedThreads / 64];
     __shared__ int sh[64], sh2[64];
     __shared__ uint64_t kt_sh;
-    __shared__ int any_sh;
-    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nwav = nt >> 6;
+    // kSchedThreads threads (a constant: in a source built with -mno-amdgpu-ieee
+    // blockDim is a device-library call that waits on memory)
+    const int tid = threadIdx.x, nt = kSchedThreads, lane = tid & 63, wave = tid >> 6, nwav = nt >> 6;
     const int R = a.R, k = a.k, kk = a.kk, n = R * kk, Rk = R * k;
     const bool surv = a.survival != nullptr;
     const int kc = surv ? k : kk;
@@ -311,12 +313,36 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
     int* off = cnt + kBuckets;
     double* sg = reinterpret_cast<double*>(keys);
 
-    // 1. table, empty histogram, one calibrated sigmoid per (request, position)
-    for (int i = tid; i < a.n_tbl; i += nt) { tb[i] = a.tbl_b[i]; tt[i] = a.tbl_t[i]; }
+    // The sigmoids and the running products sit at a stride of ks = k | 1
+    // doubles per request: the thread that walks one request's positions then
+    // reads and writes its own bank pair at every step (an even stride such as
+    // 16 doubles would put all 64 lanes on one bank). R * ks doubles fit in the
+    // keys and grouped regions (kk >= 1).
+    const int ks = k | 1;
+
+    // 1. table, empty histogram, one calibrated sigmoid per (request, position);
+    //    every global load is issued before the first use, so they take one
+    //    round trip together
+    constexpr int kElPer = kBucketItems / kSchedThreads;
+    float zv[kElPer], Tv[kElPer];
+#pragma unroll
+    for (int j = 0; j < kElPer; ++j) {
+        const int e = tid + j * nt;
+        zv[j] = 0.f; Tv[j] = 1.f;
+        if (e < Rk && e % k < kc) { zv[j] = a.z[e]; Tv[j] = a.T[e % k]; }
+    }
+    int tbv = 0;
+    double ttv = 0.0;
+    if (tid < a.n_tbl) { tbv = a.tbl_b[tid]; ttv = a.tbl_t[tid]; }          // n_tbl <= kMaxTbl <= nt
     for (int b = tid; b < kBuckets; b += nt) cnt[b] = 0;
-    for (int e = tid; e < Rk; e += nt) {
-        const int i = e % k;
-        if (i < kc) sg[e] = survival_step(a.z[e], a.T[i]);
+    if (tid < a.n_tbl) { tb[tid] = tbv; tt[tid] = ttv; }
+#pragma unroll
+    for (int j = 0; j < kElPer; ++j) {
+        const int e = tid + j * nt;
+        if (e < Rk) {
+            const int r = e / k, i = e - r * k;
+            if (i < kc) sg[r * ks + i] = survival_step(zv[j], Tv[j]);
+        }
     }
     __syncthreads();
 
@@ -344,27 +370,35 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
         for (int i0 = 0; i0 < kc; i0 += kSgBatch) {
             double sv[kSgBatch];
 #pragma unroll
-            for (int q = 0; q < kSgBatch; ++q) sv[q] = i0 + q < kc ? sg[r * k + i0 + q] : 1.0;
+            for (int q = 0; q < kSgBatch; ++q) sv[q] = i0 + q < kc ? sg[r * ks + i0 + q] : 1.0;
 #pragma unroll
             for (int q = 0; q < kSgBatch; ++q)
                 if (i0 + q < kc) {
                     S = S * sv[q];
-                    sg[r * k + i0 + q] = S;
+                    sg[r * ks + i0 + q] = S;
                 }
         }
     }
     __syncthreads();
-    for (int e = tid; e < Rk; e += nt) {
-        const int r = e / k, i = e - r * k;
-        const double S = i < kc ? sg[e] : 0.0;
-        if (surv && i < kc) a.survival[e] = S;
-        uint64_t key = ~0ull;
-        if (i < kk) {
-            key = make_key(quantise(S), i, r);
-            atomicAdd(&cnt[bucket_of(key)], 1);
+    uint64_t kv[kElPer];
+#pragma unroll
+    for (int j = 0; j < kElPer; ++j) {
+        const int e = tid + j * nt;
+        kv[j] = ~0ull;
+        if (e < Rk) {
+            const int r = e / k, i = e - r * k;
+            const double S = i < kc ? sg[r * ks + i] : 0.0;
+            if (surv && i < kc) a.survival[e] = S;
+            if (i < kk) {
+                kv[j] = make_key(quantise(S), i, r);
+                atomicAdd(&cnt[bucket_of(kv[j])], 1);
+            }
         }
-        keys[e] = key;                         // over the product just read
     }
+    __syncthreads();                           // the keys go over the products
+#pragma unroll
+    for (int j = 0; j < kElPer; ++j)
+        if (tid + j * nt < Rk) keys[tid + j * nt] = kv[j];
     __syncthreads();
 
     // 3. bucket offsets (exclusive scan), then every key into its bucket
@@ -375,25 +409,35 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
 #pragma unroll
         for (int q = 0; q < kPer; ++q) { loc[q] = cnt[tid * kPer + q]; sum += loc[q]; }
         int total;
-        int base = block_exclusive_scan_i32(sum, sh, total);
+        int base = block_exclusive_scan_i32(sum, sh, total, nwav);
 #pragma unroll
         for (int q = 0; q < kPer; ++q) { off[tid * kPer + q] = base; base += loc[q]; }
     }
     __syncthreads();
-    for (int e = tid; e < Rk; e += nt) {
-        const uint64_t x = keys[e];
-        if (x != ~0ull) grp[atomicAdd(&off[bucket_of(x)], 1)] = x;
+    // this thread's keys stay in registers (kv) from here on, with their buckets
+    int bk[kElPer];
+#pragma unroll
+    for (int j = 0; j < kElPer; ++j) {
+        bk[j] = kv[j] != ~0ull ? bucket_of(kv[j]) : 0;
+        if (kv[j] != ~0ull) grp[atomicAdd(&off[bk[j]], 1)] = kv[j];
     }
     __syncthreads();
 
-    // 4. exact sorted position: bucket start + smaller keys of the same bucket
-    for (int e = tid; e < Rk; e += nt) {
-        const uint64_t x = keys[e];
+    // 4. exact sorted position: bucket start + smaller keys of the same bucket,
+    //    compared four at a time
+#pragma unroll
+    for (int j = 0; j < kElPer; ++j) {
+        const uint64_t x = kv[j];
         if (x == ~0ull) continue;
-        const int b = bucket_of(x);
-        const int end = off[b], beg = end - cnt[b];
+        const int end = off[bk[j]], beg = end - cnt[bk[j]];
         int rank = beg;
-        for (int m = beg; m < end; ++m) rank += grp[m] < x ? 1 : 0;
+        for (int m = beg; m < end; m += 4) {
+            const uint64_t g0 = grp[m];
+            const uint64_t g1 = m + 1 < end ? grp[m + 1] : ~0ull;
+            const uint64_t g2 = m + 2 < end ? grp[m + 2] : ~0ull;
+            const uint64_t g3 = m + 3 < end ? grp[m + 3] : ~0ull;
+            rank += int(g0 < x) + int(g1 < x) + int(g2 < x) + int(g3 < x);
+        }
         srt[rank] = x;
     }
     __syncthreads();
@@ -402,11 +446,13 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
     //    and the best prefix: largest G, then smallest M
     //    Q <= 2^32 is scanned as two exact 32-bit sums of its 16-bit halves.
     const uint64_t R32 = uint64_t(R) << 32;
+    uint64_t qv[kPosPer];
     int lo = 0, hi = 0;
-    for (int p = p0; p < p1; ++p) {
-        const uint64_t q = key_q(srt[p]);
-        lo += int(q & 0xffffu);
-        hi += int(q >> 16);
+#pragma unroll
+    for (int q = 0; q < kPosPer; ++q) {
+        qv[q] = p0 + q < p1 ? key_q(srt[p0 + q]) : 0ull;
+        lo += int(qv[q] & 0xffffu);
+        hi += int(qv[q] >> 16);
     }
     // both exclusive scans at once; sh and sh2 are not written again before the
     // barrier that follows the gains
@@ -426,7 +472,7 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
 #pragma unroll
     for (int q = 0; q < kPosPer; ++q) {
         if (p0 + q < p1) {
-            P += key_q(srt[p0 + q]);
+            P += qv[q];
             const int M = p0 + q + 1, bt = R + M;
             const double G = (double(R32 + P) * thr[q]) / double(bt);
             if (G > g) { g = G; m = M; }                      // positions ascend: first M wins ties
@@ -444,21 +490,33 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
         int mw = lane < nwav ? wm_sh[lane] : INT_MAX;
         wave_best_gm(gw, mw);
         if (lane == 0) {
-            any_sh = mw > 0;
-            kt_sh = mw > 0 ? srt[mw - 1] : 0ull;
+            kt_sh = mw > 0 ? srt[mw - 1] : 0ull;          // 0: below every key
         }
     }
     __syncthreads();
 
-    // 6. lengths (a request's keys increase with the position) and the batch
+    // 6. lengths and the batch. A request's keys increase with the position, so
+    //    the keys <= kt are its first L; the element at L - 1 (the last one in)
+    //    writes L, or the element at 0 writes 0 when none is in (also when the
+    //    best prefix is empty: every key is above 0). The sorted keys are no
+    //    longer needed: their space holds the lengths.
     const uint64_t kt = kt_sh;
-    const bool any = any_sh != 0;
-    auto len_of = [&](int r) {
-        int L = 0;
-        if (any)
-            for (int i = 0; i < kk; ++i) L += keys[r * k + i] <= kt ? 1 : 0;
-        return L;
-    };
+    int* len_sh = reinterpret_cast<int*>(srt);
+#pragma unroll
+    for (int j = 0; j < kElPer; ++j) {
+        const int e = tid + j * nt;
+        if (e < Rk) {
+            const int r = e / k, i = e - r * k;
+            if (i < kk) {
+                const bool in = kv[j] <= kt;
+                const bool next_in = i + 1 < kk && keys[e + 1] <= kt;
+                if (in && !next_in) len_sh[r] = i + 1;
+                if (i == 0 && !in) len_sh[r] = 0;
+            }
+        }
+    }
+    __syncthreads();
+    auto len_of = [&](int r) { return len_sh[r]; };
     const int rper = (R + nt - 1) / nt;
     const int r0 = min(R, tid * rper), r1 = min(R, r0 + rper);
     // grouped keys are no longer needed: their space holds the row map

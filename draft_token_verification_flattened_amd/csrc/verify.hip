@@ -104,6 +104,8 @@ struct VerifyArgs {
     float* ax0;                             // [R] target logit at draft token (r, 0)
     uint64_t* flag;                         // spec_step: [0] the schedule's completion mark, [1] a late waiter's
     uint64_t token;                         // spec_step: this call's mark (unique per call, never 0)
+    int grid;                               // workgroups of the streaming launch (gridDim.x, which this
+                                            // source would read through a call and a memory round trip)
 };
 
 struct Layout {
@@ -322,7 +324,7 @@ __device__ __forceinline__ void stream_slots(const VerifyArgs& a, const StreamLd
     int* const sh = lds.sh;
     int& next_item = *lds.next_item;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    const uint32_t G = gridDim.x, b = blockIdx.x;
+    const uint32_t G = uint32_t(a.grid), b = blockIdx.x;
     if (b == 0 && tid == 0) a.hdr->status = 0u;
     if (SAMPLE && b == 0 && a.nsplit > 1)            // verify_decide's per-request arrival counters
         for (int i = tid; i < a.R; i += kStreamThreads) a.res_cnt[i] = 0;
@@ -652,7 +654,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_step_stream(VerifyArgs 
         __syncthreads();                                  // the stream reuses the schedule's LDS
     } else {
         constexpr uint32_t kWaves = kStreamThreads / kWave;
-        row0_items<DT, MODE, VEC>(a, (blockIdx.x - 1) * kWaves + (threadIdx.x >> 6), (gridDim.x - 1) * kWaves);
+        row0_items<DT, MODE, VEC>(a, (blockIdx.x - 1) * kWaves + (threadIdx.x >> 6), (a.grid - 1) * kWaves);
         // one thread waits for the mark; the stream reads the batch with
         // device-scope atomic loads (no cache invalidation, which would stall the
         // streaming compute units around), after the barrier
@@ -1446,7 +1448,8 @@ static int launch_step_stream(K kernel, VerifyArgs& a, const SchedArgs& first, i
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                             int(lds)) != hipSuccess)
         return fail(SPECV_EDEVICE, "spec_step: cannot reserve %zu bytes of LDS", lds);
-    SPECV_LAUNCH("verify_step_stream", kernel, std::max(2, cus), kStreamThreads, lds, s, a);
+    a.grid = std::max(2, cus);
+    SPECV_LAUNCH("verify_step_stream", kernel, a.grid, kStreamThreads, lds, s, a);
     return SPECV_OK;
 }
 
@@ -1462,6 +1465,7 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
         } else {
             auto ks = verify_stream<DT, SPECV_GREEDY, VEC>;
             if (int e = stream_grid(ks, long(a.Bmax) * a.C, cus, G)) return e;
+            a.grid = G;
             SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
         }
         return launch_decide(verify_decide<DT, SPECV_GREEDY, VEC, kDecideThreads>, kDecideThreads, a, next, s);
@@ -1487,6 +1491,7 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
     } else {
         auto ks = verify_stream<DT, SPECV_SAMPLE, VEC>;
         if (int e = stream_grid(ks, (a.stats ? 1L : 2L) * a.Bmax * a.C, cus, G)) return e;
+        a.grid = G;
         SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
     }
     if (threads == kDecideThreads)
