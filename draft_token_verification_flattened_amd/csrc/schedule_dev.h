@@ -32,7 +32,9 @@ __device__ __forceinline__ double survival_step(float z, float T) {
 }
 
 __device__ __forceinline__ uint64_t quantise(double S) {
-    return uint64_t(floor(S * 4294967296.0 + 0.5));
+    // S in [0, 1]: x in [0, 2^32], an integer; only x = 2^32 needs more than 32 bits
+    const double x = floor(S * 4294967296.0 + 0.5);
+    return x >= 4294967296.0 ? (1ull << 32) : uint64_t(uint32_t(x));
 }
 
 // Table lookup: linear interpolation on the segment [B_j, B_j+1) holding bt
@@ -272,21 +274,24 @@ __device__ __forceinline__ void flatten_rows_lds(const SchedArgs& a, int r0, int
 constexpr int kBuckets = 4096;
 constexpr int kBucketItems = 4096;          // largest R * k for schedule_bucket
 
-// Bucket of a key; ascending bucket = descending Q, so bucket order is key
-// order. Survivals S = Q / 2^32 >= 1/4 take steps of 2^-12 in S (buckets
+// Bucket of a key, from its Q; ascending bucket = descending Q, so bucket order
+// is key order. Survivals S = Q / 2^32 >= 1/4 take steps of 2^-12 in S (buckets
 // 0..3072). Smaller ones, which decaying confidences over a long block make
 // plentiful, go by octave: the leading one's position and the next bits of Q,
 // 128 buckets per octave for S in [1/16, 1/4) (3073..3328), 64 per octave down
 // to 2^-10 (3329..3712), 16 per octave below (3713..4064); Q = 0 is bucket 4065.
-__device__ __forceinline__ int bucket_of(uint64_t key) {
-    const uint64_t q = key_q(key);
-    if (q >= (1ull << 30)) return int(((1ull << 32) - q) >> 20);
-    if (q == 0) return 4065;
-    const int e = 63 - __builtin_clzll(q);                       // 0..29
-    if (e >= 28) return 3073 + (255 - ((e - 28) * 128 + int((q >> (e - 7)) & 127u)));
-    if (e >= 22) return 3329 + (383 - ((e - 22) * 64 + int((q >> (e - 6)) & 63u)));
-    const int m = int((e >= 4 ? q >> (e - 4) : q << (4 - e)) & 15u);
-    return 3713 + (351 - (e * 16 + m));
+//
+// Below 2^30 the octave bucket is base - (e << nb) - m, with e the leading
+// one's position, nb the bits taken after it (7, 6 or 4) and m those bits,
+// read from q shifted so that the leading one is bit 31; no branches.
+__device__ __forceinline__ int bucket_of_q(uint64_t q) {
+    const uint32_t q32 = uint32_t(q);                            // q < 2^30 where used
+    const int lz = __builtin_clz(q32 | 1u), e = 31 - lz;         // q32 = 0 is handled below
+    const int nb = e >= 28 ? 7 : (e >= 22 ? 6 : 4);
+    const int base = e >= 28 ? 3073 + 255 + 28 * 128 : (e >= 22 ? 3329 + 383 + 22 * 64 : 3713 + 351);
+    const int m = int(((q32 << lz) >> (31 - nb)) & ((1u << nb) - 1u));
+    const int low = q32 == 0 ? 4065 : base - (e << nb) - m;
+    return q >= (1ull << 30) ? int(((1ull << 32) - q) >> 20) : low;
 }
 static_assert(4065 < kBuckets, "bucket range");
 
@@ -319,6 +324,10 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
     // 16 doubles would put all 64 lanes on one bank). R * ks doubles fit in the
     // keys and grouped regions (kk >= 1).
     const int ks = k | 1;
+    // e / k for e < 4096 and k <= 32 as (e * mk) >> 20, mk = ceil(2^20 / k):
+    // exact, since e * (mk * k - 2^20) < 4096 * k < 2^20
+    const uint32_t mk = ((1u << 20) + uint32_t(k) - 1u) / uint32_t(k);
+    auto div_k = [&](int e) { return int((uint32_t(e) * mk) >> 20); };
 
     // 1. table, empty histogram, one calibrated sigmoid per (request, position);
     //    every global load is issued before the first use, so they take one
@@ -327,9 +336,9 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
     float zv[kElPer], Tv[kElPer];
 #pragma unroll
     for (int j = 0; j < kElPer; ++j) {
-        const int e = tid + j * nt;
+        const int e = tid + j * nt, i = e - div_k(e) * k;
         zv[j] = 0.f; Tv[j] = 1.f;
-        if (e < Rk && e % k < kc) { zv[j] = a.z[e]; Tv[j] = a.T[e % k]; }
+        if (e < Rk && i < kc) { zv[j] = a.z[e]; Tv[j] = a.T[i]; }
     }
     int tbv = 0;
     double ttv = 0.0;
@@ -340,7 +349,7 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
     for (int j = 0; j < kElPer; ++j) {
         const int e = tid + j * nt;
         if (e < Rk) {
-            const int r = e / k, i = e - r * k;
+            const int r = div_k(e), i = e - r * k;
             if (i < kc) sg[r * ks + i] = survival_step(zv[j], Tv[j]);
         }
     }
@@ -380,18 +389,23 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
         }
     }
     __syncthreads();
+    // this thread's keys stay in registers (kv) from here on, with their buckets
     uint64_t kv[kElPer];
+    int bk[kElPer];
 #pragma unroll
     for (int j = 0; j < kElPer; ++j) {
         const int e = tid + j * nt;
         kv[j] = ~0ull;
+        bk[j] = 0;
         if (e < Rk) {
-            const int r = e / k, i = e - r * k;
+            const int r = div_k(e), i = e - r * k;
             const double S = i < kc ? sg[r * ks + i] : 0.0;
             if (surv && i < kc) a.survival[e] = S;
             if (i < kk) {
-                kv[j] = make_key(quantise(S), i, r);
-                atomicAdd(&cnt[bucket_of(kv[j])], 1);
+                const uint64_t Q = quantise(S);
+                kv[j] = make_key(Q, i, r);
+                bk[j] = bucket_of_q(Q);
+                atomicAdd(&cnt[bk[j]], 1);
             }
         }
     }
@@ -414,13 +428,9 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
         for (int q = 0; q < kPer; ++q) { off[tid * kPer + q] = base; base += loc[q]; }
     }
     __syncthreads();
-    // this thread's keys stay in registers (kv) from here on, with their buckets
-    int bk[kElPer];
 #pragma unroll
-    for (int j = 0; j < kElPer; ++j) {
-        bk[j] = kv[j] != ~0ull ? bucket_of(kv[j]) : 0;
+    for (int j = 0; j < kElPer; ++j)
         if (kv[j] != ~0ull) grp[atomicAdd(&off[bk[j]], 1)] = kv[j];
-    }
     __syncthreads();
 
     // 4. exact sorted position: bucket start + smaller keys of the same bucket,
@@ -506,7 +516,7 @@ __device__ __forceinline__ void schedule_bucket_body(const SchedArgs& a, uint64_
     for (int j = 0; j < kElPer; ++j) {
         const int e = tid + j * nt;
         if (e < Rk) {
-            const int r = e / k, i = e - r * k;
+            const int r = div_k(e), i = e - r * k;
             if (i < kk) {
                 const bool in = kv[j] <= kt;
                 const bool next_in = i + 1 < kk && keys[e + 1] <= kt;
