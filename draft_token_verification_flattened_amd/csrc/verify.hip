@@ -63,7 +63,9 @@ constexpr int kPhaseSlots = 2 * kStreamThreads;   // slots described in LDS at a
 constexpr int kDecideThreads = 1024;        // verify_decide: 16 wavefronts per workgroup, or
 constexpr int kDecideHalf = 512;            // 8 (two workgroups per compute unit)
 constexpr int kMaxChunks = 4096;            // sampling: chunks per row (residual masses live in LDS)
-constexpr int kResidualTrials = 16;         // counter-based uniforms: rejection trials of the residual draw
+constexpr int kResidualTrials = 16;         // counter-based uniforms: rejection trials of the residual draw per
+                                            // round (the first round's uniforms are tabled in phase 1)
+constexpr int kTrialsMax = 64;              // trials before the inverse-CDF fallback (at most four rounds)
 constexpr int kNV = 4;                      // 16-byte vectors per lane per item
 constexpr int kChunkVecs = kWave * kNV;     // vectors per chunk
 
@@ -981,14 +983,41 @@ __device__ __forceinline__ int wave_find_chunk_prefix(int C, float u, const floa
 // of the bonus row, chunk masses taken from the partials.
 static_assert(kDecideThreads == kSchedThreads, "the next round's schedule runs in a decide workgroup");
 
-template <int DT, int MODE, bool VEC, int NT>
+// One rejection trial of the residual draw at row a_r (see verify_decide):
+// y ~ p by the inverse CDF with u1 (chunk masses of p in pm, plain or as prefix
+// sums), kept iff u2 < 1 - q(y) / p(y); returns y, or -1 if it was rejected.
+// Only the target chunk is loaded, q's logit at y after the pick: the draft
+// chunk along with it (no second round trip) doubled the round's burst of loads
+// (16 pairs of 8 KiB per rejecting request at once), 0.7 us slower at 256 requests.
+template <int DT, bool VEC>
+__device__ __forceinline__ int residual_trial(const typename Logit<DT>::T* trow, const typename Logit<DT>::T* drow,
+                                              int C, int CH, int V, bool keep_mass, const float* pm, float4 st, float c,
+                                              float u1, float u2) {
+    using RW = Raw<DT, VEC>;
+    float cb, cth;
+    const int cs = keep_mass ? wave_find_chunk_prefix(C, u1, pm, cb, cth)
+                             : wave_find_chunk(C, u1, [&](int cc) { return pm[cc]; }, cb, cth);
+    float2 xy;
+    const int yy = chunk_pick<DT, VEC, false>(trow, drow, cs * CH, V, cb, cth, [&](float xt_, float) {
+        return __builtin_amdgcn_exp2f(fmaf(xt_, c, -st.x));
+    }, &xy);
+    xy.y = RW::LT::load1(drow + yy);
+    const float py = exp2f(fmaf(xy.x, c, -st.x)) / st.y;
+    const float qy = exp2f(fmaf(xy.y, c, -st.z)) / st.w;
+    return py > 0.f && u2 < 1.f - qy / py ? yy : -1;
+}
+
+template <int DT, int MODE, bool VEC, int NT, bool NEXT>
 // Four wavefronts per SIMD: a 1024-thread workgroup, or two 512-thread ones per
 // compute unit (every request resident at once with up to twice as many
-// requests as units), so at most 128 VGPRs.
+// requests as units), so at most 128 VGPRs. NEXT: the launch also runs the next
+// round's schedule (a separate instantiation, so that the schedule's register
+// pressure stays out of the decisions' code when there is none).
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void verify_decide(VerifyArgs a) {
     const int nsplit = MODE == SPECV_SAMPLE ? a.nsplit : 1;
-    if constexpr (NT == kSchedThreads) {
-        if (a.has_next && int(blockIdx.x) == nsplit * a.R) {    // the next round's schedule, beside this round's decisions
+    if constexpr (NEXT) {
+        static_assert(NT == kSchedThreads, "the next round's schedule runs in a 1024-thread workgroup");
+        if (int(blockIdx.x) == nsplit * a.R) {                  // the next round's schedule, beside this round's decisions
             extern __shared__ __align__(16) uint64_t sched_lds[];
             schedule_bucket_body(a.next, sched_lds);
             return;
@@ -1210,12 +1239,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
             // first uniform and keeps y iff its second lies below 1 - q(y) / p(y),
             // so a kept y has probability max(0, p(y) - q(y)) per trial: the
             // normalised residual. The trials are independent, so the wavefronts
-            // run them side by side and the lowest kept one gives the token; a
-            // wavefront stops once a lower trial than its next one was kept.
-            // Every workgroup of the request runs them and reaches the same
-            // result; with none kept the draw falls back to the residual's
-            // inverse CDF (the re-read below) with the uniform of trial
-            // kResidualTrials.
+            // run them side by side, kResidualTrials at a time, and the lowest
+            // kept one gives the token; a wavefront stops once a lower trial than
+            // its next one was kept. A further round runs only when every trial
+            // of the previous ones was rejected (where p and q nearly agree), its
+            // uniforms computed by the wavefront that needs them. Every workgroup
+            // of the request runs them and reaches the same result; with none of
+            // kTrialsMax kept the draw falls back to the residual's inverse CDF
+            // (the re-read below) with the uniform of trial kTrialsMax.
             const float* pm = mass_s + (keep_mass ? acc * C : 0);
             if (!keep_mass) {
                 const float2* pp = (a.pre0 && acc == 0) ? a.part0 + long(r) * C : a.part_p + long(base + acc) * C;
@@ -1225,40 +1256,63 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
                 }
                 __syncthreads();
             }
-            for (int t = wave; t < kResidualTrials; t += kW) {
+            // the kept trial's token (the round that kept it left its token and
+            // uniforms at index win % 16) and the bonus row's record: -(kept trial + 1),
+            // a_r, the token, the trial's first uniform
+            auto emit_kept = [&](int win) {
+                if (writer && tid == 0) {
+                    const int w16 = win % kResidualTrials;
+                    const int y = trial_y_s[w16];
+                    out[acc] = y;
+                    if (a.diag)
+                        reinterpret_cast<float4*>(a.diag)[N + r] =
+                            make_float4(-float(win + 1), float(acc), float(y), tu_s[w16 * kTuStride + acc].x);
+                }
+            };
+            for (int t = wave; t < kResidualTrials; t += kW) {                 // the first round
                 if (__hip_atomic_load(&win_s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < t) break;
                 const float2 uu = tu_s[t * kTuStride + acc];
-                const float u2 = uu.y;
-                float cb, cth;
-                const int cs = keep_mass ? wave_find_chunk_prefix(C, uu.x, pm, cb, cth)
-                                         : wave_find_chunk(C, uu.x, [&](int cc) { return pm[cc]; }, cb, cth);
-                // only the target chunk is loaded, q's logit at y after the pick:
-                // the draft chunk along with it (no second round trip) doubled the
-                // round's burst of loads (16 pairs of 8 KiB per rejecting request at
-                // once), 0.7 us slower at 256 requests
-                float2 xy;
-                const int yy = chunk_pick<DT, VEC, false>(trow, drow, cs * CH, V, cb, cth, [&](float xt_, float) {
-                    return __builtin_amdgcn_exp2f(fmaf(xt_, c, -st.x));
-                }, &xy);
-                xy.y = RW::LT::load1(drow + yy);
-                const float py = exp2f(fmaf(xy.x, c, -st.x)) / st.y;
-                const float qy = exp2f(fmaf(xy.y, c, -st.z)) / st.w;
-                if (lane == 0 && py > 0.f && u2 < 1.f - qy / py) {
-                    trial_y_s[t] = yy;
+                const int y = residual_trial<DT, VEC>(trow, drow, C, CH, V, keep_mass, pm, st, c, uu.x, uu.y);
+                if (lane == 0 && y >= 0) {
+                    trial_y_s[t] = y;
                     atomicMin(&win_s, t);
                 }
             }
             __syncthreads();
             const int win = win_s;
             if (win != INT_MAX) {
-                if (writer && tid == 0) {
-                    const int y = trial_y_s[win];
-                    out[acc] = y;
-                    // the bonus row's record: -(kept trial + 1), a_r, the token, the trial's first uniform
-                    if (a.diag)
-                        reinterpret_cast<float4*>(a.diag)[N + r] =
-                            make_float4(-float(win + 1), float(acc), float(y), tu_s[win * kTuStride + acc].x);
+                emit_kept(win);
+                return;
+            }
+            // Later rounds, only when every earlier trial was rejected (placed after
+            // the first round's exit, so that the common path's code keeps its
+            // shape). Round t0 runs trials t0 .. t0 + 15 with their uniforms
+            // computed into column a_r of the table (the previous round's being
+            // spent); a kept trial leaves its token at index t - t0. Every wavefront
+            // decides alike whether to run a round: a round keeps only trials >= its
+            // first, so the value read after the barrier is at least t0 for all
+            // wavefronts or for none.
+            for (int t0 = kResidualTrials; t0 < kTrialsMax; t0 += kResidualTrials) {
+                if (__hip_atomic_load(&win_s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < t0) break;
+                if (tid < kResidualTrials) {
+                    float u1, u2;
+                    philox_trial(a.seed, a.step, uint32_t(r), uint32_t(acc), uint32_t(t0 + tid), u1, u2);
+                    tu_s[tid * kTuStride + acc] = make_float2(u1, u2);
                 }
+                __syncthreads();
+                for (int t = wave; t < kResidualTrials; t += kW) {
+                    if (__hip_atomic_load(&win_s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < t0 + t) break;
+                    const float2 uu = tu_s[t * kTuStride + acc];
+                    const int y = residual_trial<DT, VEC>(trow, drow, C, CH, V, keep_mass, pm, st, c, uu.x, uu.y);
+                    if (lane == 0 && y >= 0) {
+                        trial_y_s[t] = y;
+                        atomicMin(&win_s, t0 + t);
+                    }
+                }
+                __syncthreads();
+            }
+            if (win_s != INT_MAX) {
+                emit_kept(win_s);
                 return;
             }
         }
@@ -1339,9 +1393,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
         float ub;
         if (a.uniforms) {
             ub = a.uniforms[long(r) * (k + 1) + k];
-        } else if (rejected) {                     // the fallback after kResidualTrials rejected trials
+        } else if (rejected) {                     // the fallback after kTrialsMax rejected trials
             float u2;
-            philox_trial(a.seed, a.step, uint32_t(r), uint32_t(acc), uint32_t(kResidualTrials), ub, u2);
+            philox_trial(a.seed, a.step, uint32_t(r), uint32_t(acc), uint32_t(kTrialsMax), ub, u2);
         } else {
             ub = tu_s[acc].x;                      // U(seed, step, 1, r, a_r): trial 0's first uniform
         }
@@ -1408,19 +1462,23 @@ static int stream_grid(K kernel, long slots, int cus, int& G) {
 
 // verify_decide, with the next round's schedule as one more workgroup when it
 // fits one (else launched after it, on the same stream).
-template <class K>
-static int launch_decide(K kernel, int threads, VerifyArgs& a, const SchedArgs* next, hipStream_t s) {
-    a.has_next = threads == kSchedThreads && next && schedule_is_bucket(*next);
-    size_t lds = 0;
-    if (a.has_next) {
-        a.next = *next;
-        lds = schedule_bucket_lds(next->R, next->k, next->kk);
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                int(lds)) != hipSuccess)
-            return fail(SPECV_EDEVICE, "spec_verify: cannot reserve %zu bytes of LDS", lds);
+template <int DT, int MODE, bool VEC, int NT>
+static int launch_decide(VerifyArgs& a, const SchedArgs* next, hipStream_t s) {
+    a.has_next = NT == kSchedThreads && next && schedule_is_bucket(*next);
+    if constexpr (NT == kSchedThreads) {
+        if (a.has_next) {
+            auto kernel = verify_decide<DT, MODE, VEC, NT, true>;
+            a.next = *next;
+            const size_t lds = schedule_bucket_lds(next->R, next->k, next->kk);
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    int(lds)) != hipSuccess)
+                return fail(SPECV_EDEVICE, "spec_verify: cannot reserve %zu bytes of LDS", lds);
+            SPECV_LAUNCH("verify_decide", kernel, a.nsplit * a.R + 1, NT, lds, s, a);
+            return SPECV_OK;
+        }
     }
-    SPECV_LAUNCH("verify_decide", kernel, a.nsplit * a.R + (a.has_next ? 1 : 0), threads, lds, s, a);
-    if (next && !a.has_next) return schedule_launch(*next, s);
+    SPECV_LAUNCH("verify_decide", (verify_decide<DT, MODE, VEC, NT, false>), a.nsplit * a.R, NT, 0, s, a);
+    if (next) return schedule_launch(*next, s);
     return SPECV_OK;
 }
 
@@ -1468,7 +1526,7 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
             a.grid = G;
             SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
         }
-        return launch_decide(verify_decide<DT, SPECV_GREEDY, VEC, kDecideThreads>, kDecideThreads, a, next, s);
+        return launch_decide<DT, SPECV_GREEDY, VEC, kDecideThreads>(a, next, s);
     }
     // One 1024-thread decide workgroup fits per compute unit. With fewer requests
     // than compute units a rejected row pair is re-read by up to four of them
@@ -1495,8 +1553,8 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
         SPECV_LAUNCH("verify_stream", ks, G, kStreamThreads, 0, s, a);
     }
     if (threads == kDecideThreads)
-        return launch_decide(verify_decide<DT, SPECV_SAMPLE, VEC, kDecideThreads>, threads, a, next, s);
-    return launch_decide(verify_decide<DT, SPECV_SAMPLE, VEC, kDecideHalf>, threads, a, next, s);
+        return launch_decide<DT, SPECV_SAMPLE, VEC, kDecideThreads>(a, next, s);
+    return launch_decide<DT, SPECV_SAMPLE, VEC, kDecideHalf>(a, next, s);
 }
 
 }  // namespace specv

@@ -210,12 +210,12 @@ int spec_flatten(int R, int k, const int32_t* len_in, int32_t* tags_out,
  *     sampling, a_r < L_r: a draw from max(0, p - q) at row a_r (from p when
  *               that residual has no mass). With the caller's uniforms: the
  *               inverse-CDF draw with u[r,k]. With the generator: rejection
- *               from p, trial t = 0, 1, .. 15 taking (u1, u2) = words 0 and 1
+ *               from p, trial t = 0, 1, .. 63 taking (u1, u2) = words 0 and 1
  *               of the block at counter (a_r + 1, r, 1, t), each >> 40 times
  *               2^-24: y = the inverse-CDF draw from p with u1, kept iff
  *               u2 < 1 - q(y) / p(y); the first kept y is the token (exactly
- *               residual-distributed). With all 16 rejected: the inverse-CDF
- *               draw from the residual with u1 of trial 16.
+ *               residual-distributed). With all 64 rejected: the inverse-CDF
+ *               draw from the residual with u1 of trial 64.
  *   out_tokens[r, a_r+1 .. k] = -1; accepted_len[r] = a_r.
  * Uniforms: u[r,j] = U(seed, step, 0, r, j) and the draws' above (see the
  * conventions), or the caller's `uniforms`.

@@ -106,7 +106,9 @@ def draw_rows(w: np.ndarray, u: np.ndarray, eps: float = 0.0):
 
 
 # Trials of the rejection draw from the residual before the inverse-CDF fallback.
-RESIDUAL_TRIALS = 16
+# All of them are rejected with probability (1 - TV)^64, TV = sum(max(0, p - q)):
+# rare even where the draft nearly agrees with the target (TV ~ 0.1).
+RESIDUAL_TRIALS = 64
 
 
 def residual_draw_rejection(p: np.ndarray, q: np.ndarray, trial_u, trials: int = RESIDUAL_TRIALS,

@@ -254,9 +254,9 @@ def _first_false(keep, L):
 def _trials_explain(near, T, tok_g):
     """A rejection draw that differs between the kernel and the oracle (token or
     kept trial) is excused iff the oracle saw a rounding-sensitive step at or
-    before T = the earlier of the two sides' last trials (16 for a fallback):
-    a proposal or keep decision of trial <= T, or the fallback draw with the
-    kernel's token in its near set."""
+    before T = the earlier of the two sides' last trials (RESIDUAL_TRIALS for a
+    fallback): a proposal or keep decision of trial <= T, or the fallback draw
+    with the kernel's token in its near set."""
     for e in near:
         if e[0] in ("draw", "keep") and e[1] <= T:
             return True
@@ -403,19 +403,21 @@ def test_philox_uniforms_bit_exact(seed, step):
 
 
 def test_philox_residual_fallback():
-    """Rows whose q is close to p (residual mass about 0.1) so that for some
-    requests all 16 rejection trials fail: the fallback, an inverse-CDF draw
-    from the residual with the first uniform of trial 16, against the oracle
-    over 40 steps (fp32 rows, V = 600); at least 8 fallbacks are seen."""
+    """Rows whose q is close to p (residual mass about 0.04) and draft tokens
+    that q overrates, so that rejections are frequent and the rejection trials
+    often need more than one round of 16 and for some requests all 64 fail: the
+    later rounds and the fallback, an inverse-CDF draw from the residual with
+    the first uniform of trial 64, against the oracle over 40 steps (fp32 rows,
+    V = 600); at least 8 fallbacks and 8 draws kept after the first round."""
     R, k, V = 16, 3, 600
     g = np.random.Generator(np.random.Philox(5))
     tl = (2.0 * g.standard_normal((R, k + 1, V))).astype(np.float32)
-    dl = (tl[:, :k] + 0.35 * g.standard_normal((R, k, V))).astype(np.float32)
-    x = g.integers(0, V, size=(R, k)).astype(np.int32)
+    dl = (tl[:, :k] + 0.1 * g.standard_normal((R, k, V))).astype(np.float32)
+    x = np.argmax(dl - tl[:, :k], axis=2).astype(np.int32)
     L = np.full(R, k, np.int32)
     tags, cu = osched.flatten(L)
     N = int(cu[-1])
-    fallbacks = 0
+    fallbacks = late = 0
     say("philox residual fallback")
     for step in range(40):
         acc, out, diag, st = _gpu_verify(B.SAMPLE, tl, dl, x, None, L, 1.0, seed=11, step=step)
@@ -424,8 +426,10 @@ def test_philox_residual_fallback():
         check_sampling(_Res(acc, out, diag), ref, tags, cu, f"fallback seed=11 step={step}", rng=(11, step))
         bon = diag[N:N + R]
         fallbacks += int(((acc < L) & (bon[:, 0] >= 0)).sum())
-    say("fallbacks", fallbacks)
+        late += int(((acc < L) & (bon[:, 0] <= -17)).sum())
+    say("fallbacks", fallbacks, "kept after the first round", late)
     assert fallbacks >= 8, fallbacks
+    assert late >= 8, late
 
 
 def test_verify_deterministic():
