@@ -747,6 +747,95 @@ __global__ __launch_bounds__(256) void markov_pick(MarkovArgs a) {
 // last range, slice or entry with positive weight is taken. Greedy: the merged
 // (max, first index) of the range partials is the token.
 constexpr int kRangePer = 4;                 // range partials per lane: nr <= 256
+
+// Levels 2 and 3 of markov_pick_ranges for a range of at most kPrefetchSlices
+// slices of a bf16 row with V % 8 == 0, with every load in one round trip: the
+// range's slice partials (one per lane) and all its logits (16-byte vectors,
+// four per lane) are loaded together, the slice is chosen from the partials,
+// and the chosen slice's eight vectors move by lane shuffles to lanes 0..7,
+// where the entry is chosen. The arithmetic, its order and the no-crossing
+// fallbacks are inv_cdf_pick's for chunks [s0, s1) from carry `base`; the
+// drawn token's logit for the statistics comes from the same registers.
+// Returns false, having stored nothing, when no slice of the range has mass
+// (inv_cdf_pick then falls back to slice 0, outside the loaded range).
+constexpr int kPrefetchSlices = 32;          // 32 x 8 vectors = 4 per lane
+__device__ __forceinline__ bool pick_in_range(const MarkovArgs& a, int m, const uint16_t* row, const float2* ps,
+                                              int s0, int s1, float thr, float M, float base, float Z) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int V = a.V, ns = s1 - s0, nvec = min(ns * (kSlice / 8), (V - s0 * kSlice) / 8);
+    const float c = a.c;
+    const float2 sp = lane < ns ? ps[kPartBlock * (s0 + lane)] : make_float2(-INFINITY, 0.f);
+    uint4 vec[kPrefetchSlices * (kSlice / 8) / kWave];
+#pragma unroll
+    for (int i = 0; i < kPrefetchSlices * (kSlice / 8) / kWave; ++i) {
+        const int j = lane + kWave * i;
+        vec[i] = j < nvec ? *reinterpret_cast<const uint4*>(row + long(s0) * kSlice + 8 * j) : uint4{0, 0, 0, 0};
+    }
+    // level 2: the slice, from the partials (inv_cdf_pick's chunk level, one window)
+    const float mch = lane < ns ? (sp.x == -INFINITY ? 0.f : sp.y * exp2f(sp.x - M)) : 0.f;
+    const float inc = wave_inclusive_scan(mch, lane) + base;
+    int cand = (lane < ns && inc > thr) ? s0 + lane : 0x7fffffff;
+    const int pos = (lane < ns && mch > 0.f) ? s0 + lane : -1;
+    cand = wave_min_int(cand);
+    const int last_pos = max(-1, -wave_min_int(-pos));
+    if (cand == 0x7fffffff && last_pos < 0) return false;
+    int sel;
+    float run;
+    if (cand != 0x7fffffff) {
+        sel = cand;
+        run = __shfl(inc - mch, cand - s0, kWave);
+    } else {
+        sel = last_pos;
+        run = -INFINITY;
+    }
+    // level 3: lane t < 8 takes entries beg + 8t .. beg + 8t + 7 of the slice
+    const int beg = sel * kSlice, end = min(V, beg + kSlice);
+    const int j0 = (sel - s0) * (kSlice / 8);                  // its first vector: slot j0 / 64, lanes j0 % 64 ..
+    const int slot = j0 / kWave, src = (j0 % kWave) + (lane & 7);
+    uint4 mine = vec[0];
+#pragma unroll
+    for (int i = 1; i < kPrefetchSlices * (kSlice / 8) / kWave; ++i)
+        if (slot == i) mine = vec[i];
+    uint4 v;
+    v.x = __shfl(mine.x, src, kWave);
+    v.y = __shfl(mine.y, src, kWave);
+    v.z = __shfl(mine.z, src, kWave);
+    v.w = __shfl(mine.w, src, kWave);
+    float x[8];
+    Logit<SPECV_BF16>::unpack(v, x);
+    const int my = beg + lane * 8;
+    float w[8], lsum = 0.f;
+    int lastw = -1;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        w[q] = (lane < 8 && my + q < end) ? exp2f(fmaf(x[q], c, -M)) : 0.f;
+        lsum += w[q];
+        if (w[q] > 0.f) lastw = max(lastw, my + q);
+    }
+    const float incl = wave_inclusive_scan(lsum, lane);
+    float cum = run + (incl - lsum);
+    int hit = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        cum += w[q];
+        if (hit == 0x7fffffff && lane < 8 && my + q < end && cum > thr) hit = my + q;
+    }
+    const int found = wave_min_int(hit);
+    lastw = -wave_min_int(-lastw);
+    const int y = found != 0x7fffffff ? found : (lastw >= 0 ? lastw : beg);
+    // y's logit from the lane that holds it
+    const int yl = (y - beg) >> 3, yq = (y - beg) & 7;
+    float xy = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        if (q == yq) xy = x[q];
+    xy = __shfl(xy, yl, kWave);
+    if (lane == 0) {
+        a.tokens[long(m) * a.k + a.pos] = y;
+        if (a.stats) a.stats[long(m) * a.k + a.pos] = specv_draft_stat{M, Z, xy, c, y, {0, 0, 0}};
+    }
+    return true;
+}
 static_assert(kRangePer * kWave >= 256, "run_grid makes at most 256 ranges");
 
 template <int DT>
@@ -819,6 +908,11 @@ __global__ __launch_bounds__(256) void markov_pick_ranges(MarkovArgs a) {
     const float2* ps = a.part + part_at(m, 0, S);        // slice s at ps[kPartBlock * s]
     const T* row = static_cast<const T*>(a.dl) + (long(m) * a.k + a.pos) * long(a.V);
     const float c = a.c;
+    if constexpr (DT == SPECV_BF16) {
+        if (s1 - s0 <= kPrefetchSlices && a.V % 8 == 0 && (reinterpret_cast<uintptr_t>(row) & 15u) == 0 &&
+            pick_in_range(a, m, row, ps, s0, s1, thr, M, base, tot.b))
+            return;
+    }
     const int y = inv_cdf_pick(
         s1, a.V, kSlice, thr,
         [&](int s) { const float2 p = ps[kPartBlock * s]; return p.x == -INFINITY ? 0.f : p.y * exp2f(p.x - M); },
