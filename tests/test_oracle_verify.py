@@ -263,6 +263,22 @@ def test_residual_rejection_draw_fallback_and_empty_residual():
     assert (y, t) == (0, 0) and ("keep", 0) in near
 
 
+def test_residual_rejection_default_cap():
+    """With p == q no trial can keep: the default draw runs RESIDUAL_TRIALS = 64
+    trials, in order, then the fallback takes the first uniform of trial 64."""
+    assert verify.RESIDUAL_TRIALS == 64
+    p = np.array([0.5, 0.25, 0.125, 0.125])
+    seen = []
+
+    def tu(t):
+        seen.append(t)
+        return (0.6, 0.0)
+
+    y, t, _ = verify.residual_draw_rejection(p, p.copy(), tu)
+    assert (y, t) == (1, -1)
+    assert seen == list(range(64)) + [64]
+
+
 def test_rng_chisquare_lossless(logit_model):
     """Trials through verify(rng=(seed, step)), one step per round of the
     harness: the first k+1 emitted tokens follow the target (V = 8, k = 2,
