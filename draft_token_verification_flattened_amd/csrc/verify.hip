@@ -100,10 +100,11 @@ struct VerifyArgs {
     int nsplit;                             // sampling: decide workgroups per request (1, 2 or 4)
     SchedArgs next;                         // the next round's schedule (spec_verify_ex)
     int has_next;                           // 1: verify_decide runs `next` as workgroup R
-    int pre0;                               // 1: target row (r, 0) of every request was streamed
-                                            //    beside the schedule into part0 / ax0 (spec_step)
-    float2* part0;                          // [R * C] target chunk partials of row (r, 0)
-    float* ax0;                             // [R] target logit at draft token (r, 0)
+    int pre0;                               // 1: rows streamed beside the schedule (spec_step): npre kinds
+    int npre;                               //    of row per request, kind 0 target (r, 0), kind 1 target
+                                            //    (r, 1), kind 2 draft (r, 0), into part0 / ax0
+    float2* part0;                          // [npre * R * C] chunk partials of those rows (kind-major)
+    float* ax0;                             // [npre * R] their logits at draft tokens x[r, 0], x[r, 1], x[r, 0]
     uint64_t* flag;                         // spec_step: [0] the schedule's completion mark, [1] a late waiter's
     uint64_t token;                         // spec_step: this call's mark (unique per call, never 0)
     int grid;                               // workgroups of the streaming launch (gridDim.x, which this
@@ -126,8 +127,8 @@ static Layout ws_layout(int R, int k, int V) {
     l.rec = off;     off = align256(off + B * sizeof(RowRec));
     l.res_mass = off; off = align256(off + size_t(R) * C * sizeof(float));
     l.res_cnt = off; off = align256(off + size_t(R) * sizeof(int));
-    l.part0 = off;   off = align256(off + size_t(R) * C * sizeof(float2));
-    l.ax0 = off;     off = align256(off + size_t(R) * sizeof(float));
+    l.part0 = off;   off = align256(off + 3 * size_t(R) * C * sizeof(float2));
+    l.ax0 = off;     off = align256(off + 3 * size_t(R) * sizeof(float));
     l.flag = off;    off = align256(off + 2 * sizeof(uint64_t));
     l.total = off;
     return l;
@@ -309,7 +310,7 @@ __device__ __forceinline__ int load_dev(const int32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int DT, int MODE, bool VEC>
+template <int DT, int MODE, bool VEC, bool PRE = false>
 __device__ __forceinline__ void stream_slots(const VerifyArgs& a, const StreamLds& lds) {
     using RW = Raw<DT, VEC>;
     using T = typename RW::T;
@@ -331,6 +332,9 @@ __device__ __forceinline__ void stream_slots(const VerifyArgs& a, const StreamLd
     if (SAMPLE && b == 0 && a.nsplit > 1)            // verify_decide's per-request arrival counters
         for (int i = tid; i < a.R; i += kStreamThreads) a.res_cnt[i] = 0;
     const int C = a.C, CH = a.CH, V = a.V, K = a.k;
+    // rows streamed beside the schedule (spec_step): the target rows (r, 0); with PRE
+    // also target (r, 1) and, if npre > 2, draft (r, 0)
+    const bool pre_d0 = PRE && a.npre > 2;
     const uint32_t region = uint32_t(a.Bmax) * uint32_t(C);          // slots per tensor
     const uint32_t slots = (SAMPLE && !a.stats) ? 2 * region : region;
     if (b >= slots) return;
@@ -378,7 +382,8 @@ __device__ __forceinline__ void stream_slots(const VerifyArgs& a, const StreamLd
             const int ch = int(rel - uint32_t(t) * uint32_t(C));
             const int r = tg[h].x, j = tg[h].y;
             if (i >= np || t >= (tensor ? nver : nrows)) continue;
-            if (a.pre0 && tensor == 0 && j == 0) continue;     // streamed beside the schedule (spec_step)
+            if (a.pre0 && j == 0 && (tensor == 0 || pre_d0)) continue;   // streamed beside the schedule
+            if (PRE && tensor == 0 && j == 1) continue;
             const bool ok = r >= 0 && r < a.R && j >= 0 && j <= K && (tensor == 0 || j < K);
             lv[h] = (h < 2 && i < uint32_t(kWaves)) ? 0 : 1;       // slots 0 .. kWaves-1: not listed
             tt[h] = t;
@@ -538,15 +543,18 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
 // publishes its completion. The others meanwhile stream the target row (r, 0)
 // of every request, which the batch holds whatever lengths the schedule picks
 // (verified row 0 when L_r > 0, the bonus row when L_r = 0), into part0 (and
-// ax0, the logit at draft token (r, 0)). Then every workgroup, the schedule's
-// included, streams its slots of the batch's other rows as verify_stream
-// does; the others start once the schedule is published, which it normally is
-// by the time their rows (r, 0) are done. One launch instead of two: the grid
-// does not drain between the rows (r, 0) and the rest.
+// ax0, the logit at draft token (r, 0)); when those rows alone would be done
+// well before the schedule (PRE, npre > 1: light loads, long blocks), also
+// the target rows (r, 1) and the draft rows (r, 0), which every request with
+// L_r > 0 needs. Then every workgroup, the schedule's included, streams its
+// slots of the batch's other rows as verify_stream does; the others start once
+// the schedule is published, which it normally is by the time those rows are
+// done. One launch instead of two: the grid does not drain between the rows
+// streamed beside the schedule and the rest.
 //
-// Rows (r, 0): work items are (request, chunk) pairs, taken grid-stride by the
-// streaming wavefronts in batches of at most kRow0Batch (scalar rows: one item
-// at a time, so that no registers spill). A
+// Rows beside the schedule: work items are (kind, request, chunk) triples,
+// taken grid-stride by the streaming wavefronts in batches of at most
+// kRow0Batch (scalar rows: one item at a time, so that no registers spill). A
 // wavefront has only a few items (about five at 256 requests), so the loads go
 // through a ring of kRow0Ring buffers: the first kRow0Ring are issued at once,
 // and each later one as soon as a buffer is free. Every batch size is its own
@@ -555,7 +563,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_stream(VerifyArgs a) {
 constexpr int kRow0Batch = 3;        // (more spill registers beside the stream's code)
 constexpr int kRow0Ring = 3;         // 16-byte loads; scalar rows (kE floats per buffer) use one buffer
 
-template <int DT, int MODE, bool VEC, int NB>
+template <int DT, int MODE, bool VEC, int NB, bool PRE>
 __device__ __forceinline__ void row0_batch(const VerifyArgs& a, uint32_t i0, uint32_t nw, int lane) {
     using RW = Raw<DT, VEC>;
     using T = typename RW::T;
@@ -564,16 +572,29 @@ __device__ __forceinline__ void row0_batch(const VerifyArgs& a, uint32_t i0, uin
     constexpr bool SAMPLE = MODE == SPECV_SAMPLE;
     const int C = a.C, CH = a.CH, V = a.V, K = a.k;
     constexpr int kRing = VEC ? kRow0Ring : 1;
+    // item it: kind it / (R C), request (it % (R C)) / C, chunk it % C; the kind's
+    // row and the draft token its logit is taken at (kind 1 with k = 1: none)
+    const uint32_t RC = uint32_t(a.R) * uint32_t(C);
+    auto kind_of = [&](uint32_t it) { return !PRE || it < RC ? 0u : (it < 2 * RC ? 1u : 2u); };
+    auto row_of = [&](uint32_t it) {
+        const uint32_t kind = kind_of(it);
+        const long r = long((it - kind * RC) / uint32_t(C));
+        return kind < 2 ? static_cast<const T*>(a.target) + (r * (K + 1) + kind) * long(V)
+                        : static_cast<const T*>(a.draft) + r * K * long(V);
+    };
     int xt[NB];
     // the draft tokens of the batch's rows first: a small load issued after
     // the chunk loads would make its wait drain them
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-        xt[b] = SAMPLE ? a.tokens[long((i0 + uint32_t(b) * nw) / uint32_t(C)) * K] : -1;
+    for (int b = 0; b < NB; ++b) {
+        const uint32_t it = i0 + uint32_t(b) * nw, kind = kind_of(it);
+        const int j = kind == 1 ? 1 : 0;
+        xt[b] = (SAMPLE && j < K) ? a.tokens[long((it - kind * RC) / uint32_t(C)) * K + j] : -1;
+    }
     auto issue = [&](RW& buf, int b) {
         const uint32_t it = i0 + uint32_t(b) * nw;
-        const int r = int(it / uint32_t(C)), beg = int(it % uint32_t(C)) * CH;
-        buf.load(static_cast<const T*>(a.target) + long(r) * (K + 1) * long(V), beg, V, lane, beg + CH <= V);
+        const int beg = int(it % uint32_t(C)) * CH;
+        buf.load(row_of(it), beg, V, lane, beg + CH <= V);
     };
     RW ring[kRing];
 #pragma unroll
@@ -593,7 +614,7 @@ __device__ __forceinline__ void row0_batch(const VerifyArgs& a, uint32_t i0, uin
         xv[b] = 0.f;
         if (SAMPLE) {
             const int xb = __builtin_amdgcn_readfirstlane(xt[b]);
-            if (xb >= beg && xb < beg + CH && xb < V) {
+            if (xb >= 0 && xb >= beg && xb < beg + CH && xb < V) {
                 const int off = xb - beg, vi = off / GW;
                 const int qx = (vi >> 6) * GW + off % GW;
                 if (lane == (vi & (kWave - 1))) {
@@ -608,27 +629,28 @@ __device__ __forceinline__ void row0_batch(const VerifyArgs& a, uint32_t i0, uin
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const uint32_t it = i0 + uint32_t(b) * nw;
-        if (lane == 0) a.part0[it] = res[b];                    // part0[r * C + ch]
-        if (xf[b]) a.ax0[it / uint32_t(C)] = xv[b];
+        if (lane == 0) a.part0[it] = res[b];                    // part0[(kind R + r) C + ch]
+        if (xf[b]) a.ax0[it / uint32_t(C)] = xv[b];              // ax0[kind R + r]
     }
 }
 
-// Streaming wavefront gw of nw: the (request, chunk) items of the rows (r, 0).
-template <int DT, int MODE, bool VEC>
+// Streaming wavefront gw of nw: the (kind, request, chunk) items of the rows
+// streamed beside the schedule.
+template <int DT, int MODE, bool VEC, bool PRE>
 __device__ __forceinline__ void row0_items(const VerifyArgs& a, uint32_t gw, uint32_t nw) {
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t items = uint32_t(a.R) * uint32_t(a.C);
+    const uint32_t items = uint32_t(PRE ? a.npre : 1) * uint32_t(a.R) * uint32_t(a.C);
     if constexpr (!VEC) {                 // scalar rows: one item at a time (registers)
-        for (uint32_t i0 = gw; i0 < items; i0 += nw) row0_batch<DT, MODE, VEC, 1>(a, i0, nw, lane);
+        for (uint32_t i0 = gw; i0 < items; i0 += nw) row0_batch<DT, MODE, VEC, 1, PRE>(a, i0, nw, lane);
         return;
     }
     static_assert(kRow0Batch == 3, "one case per batch size");
     for (uint32_t i0 = gw; i0 < items; i0 += kRow0Batch * nw) {
         const int nb = int(min(uint32_t(kRow0Batch), (items - 1 - i0) / nw + 1));   // items of this batch
         switch (nb) {
-            case 1: row0_batch<DT, MODE, VEC, 1>(a, i0, nw, lane); break;
-            case 2: row0_batch<DT, MODE, VEC, 2>(a, i0, nw, lane); break;
-            default: row0_batch<DT, MODE, VEC, 3>(a, i0, nw, lane); break;
+            case 1: row0_batch<DT, MODE, VEC, 1, PRE>(a, i0, nw, lane); break;
+            case 2: row0_batch<DT, MODE, VEC, 2, PRE>(a, i0, nw, lane); break;
+            default: row0_batch<DT, MODE, VEC, 3, PRE>(a, i0, nw, lane); break;
         }
     }
 }
@@ -637,7 +659,7 @@ __device__ __forceinline__ void row0_items(const VerifyArgs& a, uint32_t gw, uin
 // only a workgroup 0 kept off the device by other work can take that long.
 constexpr uint64_t kScheduleWaitTicks = 100000000ull;    // one second
 
-template <int DT, int MODE, bool VEC>
+template <int DT, int MODE, bool VEC, bool PRE>
 __global__ __launch_bounds__(kStreamThreads) void verify_step_stream(VerifyArgs a) {
     extern __shared__ __align__(16) uint64_t step_lds[];
     const int tid = threadIdx.x;
@@ -656,7 +678,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_step_stream(VerifyArgs 
         __syncthreads();                                  // the stream reuses the schedule's LDS
     } else {
         constexpr uint32_t kWaves = kStreamThreads / kWave;
-        row0_items<DT, MODE, VEC>(a, (blockIdx.x - 1) * kWaves + (threadIdx.x >> 6), (a.grid - 1) * kWaves);
+        row0_items<DT, MODE, VEC, PRE>(a, (blockIdx.x - 1) * kWaves + (threadIdx.x >> 6), (a.grid - 1) * kWaves);
         // one thread waits for the mark; the stream reads the batch with
         // device-scope atomic loads (no cache invalidation, which would stall the
         // streaming compute units around), after the barrier
@@ -673,7 +695,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_step_stream(VerifyArgs 
         }
         __syncthreads();
     }
-    stream_slots<DT, MODE, VEC>(a, stream_lds_at(reinterpret_cast<unsigned char*>(step_lds)));
+    stream_slots<DT, MODE, VEC, PRE>(a, stream_lds_at(reinterpret_cast<unsigned char*>(step_lds)));
 }
 
 // ---------------------------------------------------------------------------
@@ -1007,12 +1029,13 @@ __device__ __forceinline__ int residual_trial(const typename Logit<DT>::T* trow,
     return py > 0.f && u2 < 1.f - qy / py ? yy : -1;
 }
 
-template <int DT, int MODE, bool VEC, int NT, bool NEXT>
+template <int DT, int MODE, bool VEC, int NT, bool NEXT, bool PRE>
 // Four wavefronts per SIMD: a 1024-thread workgroup, or two 512-thread ones per
 // compute unit (every request resident at once with up to twice as many
 // requests as units), so at most 128 VGPRs. NEXT: the launch also runs the next
 // round's schedule (a separate instantiation, so that the schedule's register
-// pressure stays out of the decisions' code when there is none).
+// pressure stays out of the decisions' code when there is none). PRE: spec_step
+// streamed rows of npre > 1 kinds beside the schedule (verify_step_stream).
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void verify_decide(VerifyArgs a) {
     const int nsplit = MODE == SPECV_SAMPLE ? a.nsplit : 1;
     if constexpr (NEXT) {
@@ -1054,6 +1077,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
     const bool keep_mass = L >= 0 && L <= k && (L + 1) * C <= kMaxChunks;
     const bool gen = SAMPLE && !a.uniforms;        // the library's own uniforms
     int32_t* out = a.out_tokens + long(r) * (k + 1);
+    // Chunk partials of this request's row j (batch row t): the rows streamed
+    // beside the schedule (spec_step) are in part0, the others in part_p /
+    // part_q; ax0 holds those rows' logits at the draft token.
+    const int npt = PRE ? 2 : (a.pre0 ? 1 : 0);                 // target rows (r, 0 .. npt - 1)
+    const bool pre_d0 = PRE && a.npre > 2;                      // draft row (r, 0)
+    auto p_parts = [&](int j, int t) {
+        if constexpr (PRE) return j < 2 ? a.part0 + (long(j) * a.R + r) * C : a.part_p + long(t) * C;
+        return (a.pre0 && j == 0) ? a.part0 + long(r) * C : a.part_p + long(t) * C;
+    };
+    auto q_parts = [&](int j, int t) {
+        return (PRE && j == 0 && pre_d0) ? a.part0 + (2L * a.R + r) * C : a.part_q + long(t) * C;
+    };
     if (a.pre0 && blockIdx.x == 0 && tid == 0) {
         // spec_step: a streaming workgroup that gave up waiting for the schedule
         // voids the call; the mark is cleared for the next call (a replayed graph
@@ -1103,12 +1138,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
             if (SAMPLE && verified) rc = a.rec[t];
             specv_draft_stat ds{};
             if (SAMPLE && verified && a.stats) ds = a.stats[long(r) * k + j];
-            const bool row0 = a.pre0 && j == 0;       // streamed beside the schedule (spec_step)
-            if (SAMPLE && verified && row0) rc.ax = a.ax0[r];
-            const float2* pp = row0 ? a.part0 + long(r) * C : a.part_p + long(t) * C;
+            if (SAMPLE && verified && j < npt) rc.ax = a.ax0[long(j) * a.R + r];   // streamed beside the schedule
+            if (PRE && SAMPLE && verified && j == 0 && pre_d0) rc.bx = a.ax0[2L * a.R + r];
+            const float2* pp = p_parts(j, t);
+            const float2* pq = q_parts(j, t);
             float2 pv[kMergePre], qv[kMergePre];
             load_partials<SAMPLE>(pp, C, lane, pv);
-            if (SAMPLE && verified && !a.stats) load_partials<true>(a.part_q + long(t) * C, C, lane, qv);
+            if (SAMPLE && verified && !a.stats) load_partials<true>(pq, C, lane, qv);
             float uj = 0.f;
             if (SAMPLE && verified && !gen) uj = a.uniforms[long(r) * (k + 1) + j];
             if (!slots_done) {
@@ -1122,7 +1158,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
                     Q = make_float2(ds.m, ds.z);
                     rc.bx = ds.x_logit;
                 } else {
-                    Q = reduce_partials<true>(a.part_q + long(t) * C, C, lane, qv);
+                    Q = reduce_partials<true>(pq, C, lane, qv);
                 }
             }
             if (SAMPLE && keep_mass) {
@@ -1249,7 +1285,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
             // (the re-read below) with the uniform of trial kTrialsMax.
             const float* pm = mass_s + (keep_mass ? acc * C : 0);
             if (!keep_mass) {
-                const float2* pp = (a.pre0 && acc == 0) ? a.part0 + long(r) * C : a.part_p + long(base + acc) * C;
+                const float2* pp = p_parts(acc, base + acc);
                 for (int cc = tid; cc < C; cc += NT) {
                     const float2 q = pp[cc];
                     mass_s[cc] = q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
@@ -1357,7 +1393,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
             }
         } else if (!keep_mass) {
             // bonus row: chunk masses of p relative to Mp, from the partials
-            const float2* pp = (a.pre0 && L == 0) ? a.part0 + long(r) * C : a.part_p + long(N + r) * C;
+            const float2* pp = p_parts(L, N + r);
             for (int cc = tid; cc < C; cc += NT) {
                 const float2 q = pp[cc];
                 mass_s[cc] = q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
@@ -1411,7 +1447,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
             });
         } else {                                   // p of row a_r: the bonus row, or a residual without mass
             if (rejected) {
-                const float2* pp = (a.pre0 && acc == 0) ? a.part0 + long(r) * C : a.part_p + long(base + acc) * C;
+                const float2* pp = p_parts(acc, base + acc);
                 for (int cc = lane; cc < C; cc += kWave) {
                     const float2 q = pp[cc];
                     mass_s[cc] = q.x == -INFINITY ? 0.f : q.y * exp2f(q.x - st.x);
@@ -1466,8 +1502,8 @@ template <int DT, int MODE, bool VEC, int NT>
 static int launch_decide(VerifyArgs& a, const SchedArgs* next, hipStream_t s) {
     a.has_next = NT == kSchedThreads && next && schedule_is_bucket(*next);
     if constexpr (NT == kSchedThreads) {
-        if (a.has_next) {
-            auto kernel = verify_decide<DT, MODE, VEC, NT, true>;
+        if (a.has_next) {                       // spec_verify_ex: no rows streamed beside a schedule
+            auto kernel = verify_decide<DT, MODE, VEC, NT, true, false>;
             a.next = *next;
             const size_t lds = schedule_bucket_lds(next->R, next->k, next->kk);
             if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1477,7 +1513,10 @@ static int launch_decide(VerifyArgs& a, const SchedArgs* next, hipStream_t s) {
             return SPECV_OK;
         }
     }
-    SPECV_LAUNCH("verify_decide", (verify_decide<DT, MODE, VEC, NT, false>), a.nsplit * a.R, NT, 0, s, a);
+    if (a.pre0 && a.npre > 1)
+        SPECV_LAUNCH("verify_decide", (verify_decide<DT, MODE, VEC, NT, false, true>), a.nsplit * a.R, NT, 0, s, a);
+    else
+        SPECV_LAUNCH("verify_decide", (verify_decide<DT, MODE, VEC, NT, false, false>), a.nsplit * a.R, NT, 0, s, a);
     if (next) return schedule_launch(*next, s);
     return SPECV_OK;
 }
@@ -1495,8 +1534,23 @@ static uint64_t call_token() {
     return t;
 }
 
+// Kinds of row streamed beside spec_step's schedule: the target rows (r, 0)
+// always (the batch holds them whatever the lengths). When those alone would be
+// done well before the schedule (light loads, long blocks: the streaming
+// workgroups would wait for it), also the rows that every request with
+// L_r >= 1 needs: target (r, 1) and, if the draft rows are read, draft (r, 0).
+// Estimates: the schedule takes ~6.3 us + 3.2 ns per (request, position) under
+// the stream's load; rows stream at ~6 TB/s.
+static int pre_row_kinds(const VerifyArgs& a, const SchedArgs& first, int elem_bytes, bool draft_rows) {
+    const double rows_us = double(a.R) * double(a.V) * elem_bytes / 6.0e6;
+    const double sched_us = 6.3 + 0.0032 * double(first.R) * double(first.k);
+    if (rows_us >= sched_us) return 1;
+    return draft_rows ? 3 : 2;
+}
+
 // spec_step's streaming launch (verify_step_stream): this round's schedule in
-// workgroup 0, the rows (r, 0) in the others, then the batch's other rows in all.
+// workgroup 0, the rows of a.npre kinds (pre_row_kinds) in the others, then the
+// batch's other rows in all.
 template <class K>
 static int launch_step_stream(K kernel, VerifyArgs& a, const SchedArgs& first, int cus, hipStream_t s) {
     a.next = first;
@@ -1519,7 +1573,11 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
     int G = 0;
     if (mode == SPECV_GREEDY) {
         if (first) {
-            if (int e = launch_step_stream(verify_step_stream<DT, SPECV_GREEDY, VEC>, a, *first, cus, s)) return e;
+            a.npre = pre_row_kinds(a, *first, DT == SPECV_BF16 ? 2 : 4, false);
+            const int e = a.npre > 1
+                              ? launch_step_stream(verify_step_stream<DT, SPECV_GREEDY, VEC, true>, a, *first, cus, s)
+                              : launch_step_stream(verify_step_stream<DT, SPECV_GREEDY, VEC, false>, a, *first, cus, s);
+            if (e) return e;
         } else {
             auto ks = verify_stream<DT, SPECV_GREEDY, VEC>;
             if (int e = stream_grid(ks, long(a.Bmax) * a.C, cus, G)) return e;
@@ -1545,7 +1603,11 @@ static int launch_verify(int mode, VerifyArgs& a, const SchedArgs* next, hipStre
         while (a.nsplit > 1 && a.C < a.nsplit * (kDecideThreads / kWave)) a.nsplit /= 2;
     }
     if (first) {
-        if (int e = launch_step_stream(verify_step_stream<DT, SPECV_SAMPLE, VEC>, a, *first, cus, s)) return e;
+        a.npre = pre_row_kinds(a, *first, DT == SPECV_BF16 ? 2 : 4, !a.stats);
+        const int e = a.npre > 1
+                          ? launch_step_stream(verify_step_stream<DT, SPECV_SAMPLE, VEC, true>, a, *first, cus, s)
+                          : launch_step_stream(verify_step_stream<DT, SPECV_SAMPLE, VEC, false>, a, *first, cus, s);
+        if (e) return e;
     } else {
         auto ks = verify_stream<DT, SPECV_SAMPLE, VEC>;
         if (int e = stream_grid(ks, (a.stats ? 1L : 2L) * a.Bmax * a.C, cus, G)) return e;
@@ -1637,6 +1699,7 @@ static int verify_prepare(int mode, int dtype, int R, int k, int V, const void* 
     a.flag = reinterpret_cast<uint64_t*>(w + lay.flag);
     a.token = 0;
     a.pre0 = 0;
+    a.npre = 1;
     a.nsplit = 1;
     a.has_next = 0;
     return SPECV_OK;

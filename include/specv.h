@@ -335,7 +335,11 @@ int spec_verify_ex(int mode, int dtype, int R, int k, int V, const void* target_
  * launch holds both the schedule and the verification pass: the schedule runs
  * on one compute unit while the others stream every request's target row
  * (r, 0), which the batch holds whatever lengths the schedule picks (verified
- * row 0, or the bonus row when L_r = 0); the schedule writes the batch with
+ * row 0, or the bonus row when L_r = 0), and, when those rows alone would be
+ * read well before the schedule is done (few requests for their positions),
+ * also the target rows (r, 1) and draft rows (r, 0), which every request with
+ * L_r > 0 needs (those of requests with L_r = 0 are read for nothing); the
+ * schedule writes the batch with
  * device-scope atomic stores and then a completion mark unique to the call,
  * and the other workgroups, once the mark is there, stream the batch's other
  * rows. The latency-bound schedule hides behind reads the step needs anyway,
