@@ -440,15 +440,17 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
     // the store tile: lane (row, q) = (lane / 8 + 8 j, lane % 8) stores bytes 16 q .. 16 q + 15
     // of request row's 128-byte segment, for j = 0, 1
     unsigned char* tile = lds_raw + 2 * buf_bytes + wave * kTileBytes;
-    long strow[2];
+    // (row j = 1 is request m + 8, eight rows of k V further than row 0; it is
+    // stored only when present, and then so is row 0)
     bool stok[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int m = grp * kRunGroup + wave * 16 + 8 * j + (lane >> 3);
-        stok[j] = m < a.R;
-        strow[j] = (long(stok[j] ? m : 0) * a.k + a.pos) * long(V);
-    }
+    for (int j = 0; j < 2; ++j) stok[j] = grp * kRunGroup + wave * 16 + 8 * j + (lane >> 3) < a.R;
+    const int m_st = grp * kRunGroup + wave * 16 + (lane >> 3);
+    const long strow0 = (long(stok[0] ? m_st : 0) * a.k + a.pos) * long(V);
+    const long strow_step = 8L * a.k * long(V);
 
+    // this wavefront's first request, in a scalar register
+    const int m_wave = __builtin_amdgcn_readfirstlane(grp * kRunGroup + wave * 16 * kRunKB);
     // this wavefront's requests (rows of absent requests read request 0's) and their operand rows
     int mreq[kRunKB];
     bool mok[kRunKB];
@@ -494,10 +496,15 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
             }
         return;
     }
-    u32x4 pr[PT];
-    load_p(pr, s_first);
-    store_p(pr, 0);
-    load_p(pr, min(s_first + 1, s_last));
+    // P slices ahead in registers: vector rows two (sets prA / prB hold slices
+    // s + 1 and s + 2 while slice s is computed, roles alternating with the
+    // slice), scalar rows one (prA only: their epilogue needs the registers)
+    constexpr int kPAhead = VEC ? 2 : 1;
+    u32x4 prA[PT], prB[PT];
+    load_p(prA, s_first);
+    store_p(prA, 0);
+    load_p(prA, min(s_first + 1, s_last));
+    if constexpr (VEC) load_p(prB, min(s_first + 2, s_last));
     // backbone values one slice ahead, in two buffers whose roles alternate
     // with the slice (as the two LDS buffers of P do); the loop below is
     // unrolled twice so that every role is fixed at compile time: a rotation
@@ -511,7 +518,7 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
     __syncthreads();
 
     // one slice: cur holds slice s's backbone values, ahead receives slice s + 1's
-    auto slice = [&](int s, int lb, const u32x4 (&cur)[kRunKB][2], u32x4 (&ahead)[kRunKB][2]) {
+    auto slice = [&](int s, int lb, const u32x4 (&cur)[kRunKB][2], u32x4 (&ahead)[kRunKB][2], u32x4 (&pr)[PT]) {
         load_bk(ahead, min(s + 1, s_last));
         f32x4 acc[4][kRunKB];
 #pragma unroll
@@ -524,16 +531,14 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 afr[4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
-                afr[x] = __builtin_bit_cast(
+            for (int x = 0; x < 4; ++x) {
+                const bf16x8 afr = __builtin_bit_cast(
                     bf16x8, *reinterpret_cast<const uint4*>(buf + (16 * x + l16) * row_bytes + (((4 * ks + g) ^ l16) * 16)));
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
-#pragma unroll
                 for (int b = 0; b < kRunKB; ++b)
-                    acc[x][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[x], bfr[ks][b], acc[x][b], 0, 0, 0);
+                    acc[x][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[ks][b], acc[x][b], 0, 0, 0);
+            }
         }
         __builtin_amdgcn_s_setprio(0);
         // epilogue: lane holds entries n16 + 4x + e (x, e < 4) of request mreq[b]
@@ -586,7 +591,7 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
                 for (int j = 0; j < 2; ++j) {
                     const u32x4 v = *reinterpret_cast<const u32x4*>(tile + (8 * j + (lane >> 3)) * kTileRow + 16 * q);
                     if (stok[j] && nq + 8 <= V)
-                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dl + strow[j] + nq));
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dl + strow0 + j * strow_step + nq));
                 }
             } else {
 #pragma unroll
@@ -605,23 +610,33 @@ __global__ __launch_bounds__(kRunThreads) void markov_logits_run(MarkovArgs a, i
             if (g == 0 && mok[b]) a.part[part_at(mreq[b], s, S)] = make_float2(pp.a, pp.b);
             part_merge(a.mode, run[b], pp);
         }
-        // the slice after next: the other buffer was last read before the previous barrier
+        // the next slice into the other buffer (last read before the previous
+        // barrier); its registers then take slice s + 1 + kPAhead
         store_p(pr, lb ^ 1);
-        load_p(pr, min(s + 2, s_last));
+        load_p(pr, min(s + 1 + kPAhead, s_last));
         __syncthreads();
     };
 
     for (int s = s_first; s <= s_last;) {
-        slice(s, 0, bkA, bkB);
+        slice(s, 0, bkA, bkB, prA);
         s += 1;
         if (s > s_last) break;
-        slice(s, 1, bkB, bkA);
+        if constexpr (VEC) slice(s, 1, bkB, bkA, prB);
+        else slice(s, 1, bkB, bkA, prA);
         s += 1;
     }
     // the requests' partials merged over this workgroup's slices
 #pragma unroll
     for (int b = 0; b < kRunKB; ++b)
-        if (g == 0 && mok[b]) a.part_rng[long(mreq[b]) * nr + range] = make_float2(run[b].a, run[b].b);
+        if (g == 0 && mok[b]) {
+            // the request recomputed here (the lane count in an asm statement, which
+            // the compiler cannot merge with the earlier one), so that no vector
+            // register has to hold it across the loop
+            int l;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+            const int m = m_wave + 16 * b + (l & 15);
+            a.part_rng[long(m) * nr + range] = make_float2(run[b].a, run[b].b);
+        }
 }
 
 // ---------------------------------------------------------------------------
