@@ -36,7 +36,7 @@
  *     of request r; 1: the extra token drawn at position i = a_r; 2: the draft
  *     head's token at position i), so results depend on neither the schedule
  *     nor the row order (the residual draw's rejection trials use words 0 and 1
- *     of the blocks at counters (a_r + 1, r, 1, t), t = 0 .. 16; spec_verify
+ *     of the blocks at counters (a_r + 1, r, 1, t), t = 0 .. 64; spec_verify
  *     states how). A caller that advances `step` once per decoding step
  *     gets fresh, reproducible randomness without any state in the library.
  *     The pages name Philox-seeded trials only; the rest is this library's
