@@ -129,10 +129,12 @@ def test_spec_step_any_workspace_contents_and_graph_replays(mode):
 
 
 @pytest.mark.parametrize("R,k,V,dtype", [(1, 5, 151936, "bf16"), (7, 3, 1001, "bf16"), (40, 6, 5000, "f32"),
-                                         (1024, 8, 256, "bf16")])
+                                         (16, 1, 3000, "bf16"), (1024, 8, 256, "bf16")])
 def test_spec_step_small_and_beyond_one_workgroup(R, k, V, dtype):
-    """One request at full V; ragged V (scalar loads); fp32; and R * k = 8192,
-    whose schedule needs the multi-workgroup kernel (sequential path)."""
+    """One request at full V; ragged V (scalar loads); fp32; one draft per
+    request (the target rows (r, 1) streamed beside the schedule are bonus rows
+    only); and R * k = 8192, whose schedule needs the multi-workgroup kernel
+    (sequential path)."""
     g = np.random.Generator(np.random.Philox(R * 31 + V))
     tl = (3 * g.standard_normal((R, k + 1, V))).astype(np.float32)
     dl = (tl[:, :k] + 1.5 * g.standard_normal((R, k, V))).astype(np.float32)
