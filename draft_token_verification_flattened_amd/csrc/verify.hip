@@ -1538,14 +1538,18 @@ static uint64_t call_token() {
 // always (the batch holds them whatever the lengths). When those alone would be
 // done well before the schedule (light loads, long blocks: the streaming
 // workgroups would wait for it), also the rows that every request with
-// L_r >= 1 needs: target (r, 1) and, if the draft rows are read, draft (r, 0).
-// Estimates: the schedule takes ~6.3 us + 3.2 ns per (request, position) under
-// the stream's load; rows stream at ~6 TB/s.
+// L_r >= 1 needs: target (r, 1) and, if the draft rows are read, draft (r, 0);
+// as many kinds as it takes to cover the schedule, no more (rows streamed
+// beside it go at a lower rate than the batch's own stream). Estimates: the
+// schedule takes ~6.3 us + 3.2 ns per (request, position) under the stream's
+// load; one kind of row streams at ~6 TB/s.
 static int pre_row_kinds(const VerifyArgs& a, const SchedArgs& first, int elem_bytes, bool draft_rows) {
-    const double rows_us = double(a.R) * double(a.V) * elem_bytes / 6.0e6;
+    const double kind_us = double(a.R) * double(a.V) * elem_bytes / 6.0e6;
     const double sched_us = 6.3 + 0.0032 * double(first.R) * double(first.k);
-    if (rows_us >= sched_us) return 1;
-    return draft_rows ? 3 : 2;
+    const int most = draft_rows ? 3 : 2;
+    int n = 1;
+    while (n < most && n * kind_us < sched_us) ++n;
+    return n;
 }
 
 // spec_step's streaming launch (verify_step_stream): this round's schedule in
