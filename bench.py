@@ -72,13 +72,16 @@ def source_hash(files=("common.h", "verify.hip")) -> str:
     return h.hexdigest()[:16]
 
 
-# Counter summaries (profiles/) per dominant kernel: the file, the sources its
-# kernel is built from, and the workload the counters were taken on.
+# Counter summaries (profiles/) per dominant kernel and workload: the file and
+# the sources its kernel is built from (the workload the counters were taken on
+# is recorded in the file).
+_VERIFY_SRC = ("common.h", "verify.hip")
 TRAFFIC = {
-    "verify_step_stream": (os.path.join(ROOT, "profiles", "verify_step_stream_c2_traffic.txt"),
-                           ("common.h", "verify.hip")),
-    "markov_logits": (os.path.join(ROOT, "profiles", "markov_logits_c4_traffic.txt"), ("common.h", "markov.hip")),
+    ("verify_step_stream", cfg): (os.path.join(ROOT, "profiles", f"verify_step_stream_{cfg}_traffic.txt"), _VERIFY_SRC)
+    for cfg in ("c1", "c2", "c3")
 }
+TRAFFIC[("markov_logits", "c4")] = (os.path.join(ROOT, "profiles", "markov_logits_c4_traffic.txt"),
+                                    ("common.h", "markov.hip"))
 
 
 def workload_key(args, max_len) -> str:
@@ -88,9 +91,10 @@ def workload_key(args, max_len) -> str:
 def committed_traffic(kernel, wkey):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, if it was taken on the current kernel source and on this workload."""
-    if kernel not in TRAFFIC:
+    key = (kernel, wkey.split()[0])
+    if key not in TRAFFIC:
         return None, None
-    path, files = TRAFFIC[kernel]
+    path, files = TRAFFIC[key]
     if not os.path.exists(path):
         return None, None
     vals = {}

@@ -42,7 +42,7 @@ def test_markov_bytes_and_flops_per_position():
 
 
 def test_counter_summaries_parse_and_are_keyed_by_workload():
-    for kernel, (path, _files) in bench.TRAFFIC.items():
+    for (kernel, cfg), (path, _files) in bench.TRAFFIC.items():
         assert os.path.exists(path), path
         vals = {}
         for line in open(path):
@@ -52,9 +52,14 @@ def test_counter_summaries_parse_and_are_keyed_by_workload():
         for key in ("fetch_scale", "write_scale", "hbm_bytes_per_launch", "source_hash", "workload"):
             assert key in vals, (path, key)
         assert float(vals["hbm_bytes_per_launch"]) > 0
-        # never quoted for another workload
-        other = types.SimpleNamespace(config="c1", mode="greedy", head="markov")
+        assert vals["workload"].split()[0] == cfg, path
+        # never quoted for another workload: another mode of the same configuration,
+        # or the same mode of another one
+        other = types.SimpleNamespace(config=cfg, mode="greedy", head="markov")
         assert bench.committed_traffic(kernel, bench.workload_key(other, 5))[0] is None
+        wk = vals["workload"].split()
+        other = types.SimpleNamespace(config="c0", mode=wk[1], head=wk[3].split("=")[1])
+        assert bench.committed_traffic(kernel, bench.workload_key(other, int(wk[2].split("=")[1])))[0] is None
 
 
 def test_workload_configs_match_the_recipes():
